@@ -1,0 +1,286 @@
+"""Seeded synthetic workloads for the CommunityKV decode step.
+
+This module only draws inputs: planted community labels, keys, values and
+the per-step queries and new tokens.  It holds none of the method's
+arithmetic (no centroids, scores, selection, attention or assignment), so
+that both the HIP path and the CPU oracle can consume exactly the same
+tensors without sharing any computation.
+
+The planted partition stands in for the prefill-time Leiden partition that
+the CommunityKV page (Figure 1, panel 2) computes from the top-kappa token
+graph: tokens of one community are noisy copies of one random centre, so
+keys of a community are close to each other and far from other centres.
+
+Every tensor is a deterministic function of (workload, seed, layer, batch
+row, kv head, step) through numpy's SeedSequence spawn keys, so any slice can
+be regenerated on its own.  Float data is drawn in fp32 and then rounded to
+the workload's storage dtype (bf16 rounding is round-to-nearest-even, done by
+torch); the oracle reads those rounded values exactly.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+# stream tags for SeedSequence spawn keys
+_T_PART, _T_KEY, _T_VAL, _T_STEP, _T_LEN = 1, 2, 3, 4, 5
+
+PER_HEAD = "per_head"
+GROUP = "group"
+
+
+@dataclass(frozen=True)
+class Workload:
+    """Shape and distribution of one synthetic decode workload."""
+
+    name: str
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str                 # storage dtype of K/V/q: "f32" or "bf16"
+    n_ctx: int                 # prefill length (upper bound when lengths vary)
+    n_sinks: int
+    mode: str                  # PER_HEAD (one graph per query head) or GROUP (one per kv head)
+    budget: int                # token budget for the selected communities (sinks not counted)
+    max_comm: int              # cap on the number of selected communities (0 = no cap)
+    kappa: int
+    steps: int
+    sm_scale: float            # softmax scale applied to q.k
+    key_scale: float           # keys are (centre + noise) * key_scale
+    noise: float               # std of the per-token noise around a centre
+    partition: str             # "iid" (uniform labels) or "geometric"
+    n_components: int = 0      # for partition == "iid"
+    mean_size: int = 16        # for partition == "geometric"
+    min_size: int = 4
+    max_size: int = 64
+    n_layers: int = 1
+    min_ctx: int = 0           # > 0: per-sequence lengths uniform in [min_ctx, n_ctx]
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def n_graphs(self) -> int:
+        per = self.n_q_heads if self.mode == PER_HEAD else self.n_kv_heads
+        return self.batch * per
+
+    @property
+    def heads_per_graph(self) -> int:
+        return 1 if self.mode == PER_HEAD else self.group
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def graph_of(self, b: int, qh: int) -> int:
+        """Graph id that query head qh of sequence b reads."""
+        if self.mode == PER_HEAD:
+            return b * self.n_q_heads + qh
+        return b * self.n_kv_heads + qh // self.group
+
+    def graph_coords(self, g: int):
+        """(sequence, kv head, first query head, number of query heads) of graph g."""
+        if self.mode == PER_HEAD:
+            b, qh = divmod(g, self.n_q_heads)
+            return b, qh // self.group, qh, 1
+        b, kh = divmod(g, self.n_kv_heads)
+        return b, kh, kh * self.group, self.group
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads.  Names describe the shape, not a model checkpoint: no
+# weights are involved, only the attention-layer geometry.
+PRESETS = {
+    "tiny": Workload(
+        name="tiny", batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, dtype="f32",
+        n_ctx=1024, n_sinks=4, mode=PER_HEAD, budget=1 << 30, max_comm=4, kappa=4,
+        steps=16, sm_scale=1.0 / 8.0, key_scale=1.0, noise=0.3, partition="iid",
+        n_components=32),
+    "qwen3_8b_32k": Workload(
+        name="qwen3_8b_32k", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        dtype="bf16", n_ctx=32768, n_sinks=4, mode=PER_HEAD, budget=2048, max_comm=0,
+        kappa=8, steps=64, sm_scale=1.0, key_scale=1.0 / math.sqrt(128), noise=0.25,
+        partition="geometric"),
+    "llama31_8b_128k": Workload(
+        name="llama31_8b_128k", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        dtype="bf16", n_ctx=131072, n_sinks=4, mode=PER_HEAD, budget=4096, max_comm=0,
+        kappa=8, steps=128, sm_scale=1.0, key_scale=1.0 / math.sqrt(128), noise=0.25,
+        partition="geometric"),
+    "llama31_8b_128k_group_b8": Workload(
+        name="llama31_8b_128k_group_b8", batch=8, n_q_heads=32, n_kv_heads=8,
+        head_dim=128, dtype="bf16", n_ctx=131072, n_sinks=4, mode=GROUP, budget=4096,
+        max_comm=0, kappa=8, steps=128, sm_scale=1.0, key_scale=1.0 / math.sqrt(128),
+        noise=0.25, partition="geometric"),
+    "qwen3_8b_stream_36l": Workload(
+        name="qwen3_8b_stream_36l", batch=8, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        dtype="bf16", n_ctx=131072, min_ctx=16384, n_sinks=4, mode=GROUP, budget=4096,
+        max_comm=0, kappa=8, steps=256, sm_scale=1.0, key_scale=1.0 / math.sqrt(128),
+        noise=0.25, partition="geometric", n_layers=36),
+}
+
+
+def preset(name: str) -> Workload:
+    return PRESETS[name]
+
+
+def _rng(seed: int, tag: int, *key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence(entropy=seed, spawn_key=(tag,) + tuple(key)))
+
+
+def _to_storage(x: np.ndarray, w: Workload) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t if w.dtype == "f32" else t.to(torch.bfloat16)
+
+
+def seq_lengths(w: Workload, seed: int, layer: int = 0) -> List[int]:
+    """Prefill length of each sequence (all equal unless min_ctx > 0)."""
+    if w.min_ctx <= 0:
+        return [w.n_ctx] * w.batch
+    r = _rng(seed, _T_LEN)
+    return [int(x) for x in r.integers(w.min_ctx, w.n_ctx + 1, size=w.batch)]
+
+
+@dataclass
+class Partition:
+    """Planted partition of one (layer, sequence, kv head) slice."""
+
+    centers: np.ndarray   # [C][d] float32, unscaled
+    labels: np.ndarray    # [n] int32, -1 for sinks
+    n_comm: int
+
+
+def gen_partition(w: Workload, seed: int, layer: int, b: int, kh: int, n: int) -> Partition:
+    """Draw centres and labels for positions 0..n-1 (0..n_sinks-1 are sinks)."""
+    r = _rng(seed, _T_PART, layer, b, kh)
+    d = w.head_dim
+    labels = np.full(n, -1, dtype=np.int32)
+    m = n - w.n_sinks
+    if w.partition == "iid":
+        C = w.n_components
+        centers = r.standard_normal((C, d), dtype=np.float32)
+        labels[w.n_sinks:] = r.integers(0, C, size=m, dtype=np.int32)
+        return Partition(centers, labels, C)
+    # geometric sizes on {1,2,...} with the given mean, clamped, drawn until
+    # they cover the non-sink positions; the last run takes the remainder.
+    p = 1.0 / w.mean_size
+    sizes: List[int] = []
+    total = 0
+    while total < m:
+        chunk = np.clip(r.geometric(p, size=max(16, (m - total) // w.mean_size + 16)),
+                        w.min_size, w.max_size)
+        for s in chunk:
+            s = int(min(s, m - total))
+            sizes.append(s)
+            total += s
+            if total >= m:
+                break
+    C = len(sizes)
+    perm = r.permutation(np.arange(w.n_sinks, n, dtype=np.int32))
+    lab = np.repeat(np.arange(C, dtype=np.int32), sizes)
+    labels[perm] = lab
+    centers = r.standard_normal((C, d), dtype=np.float32)
+    return Partition(centers, labels, C)
+
+
+def gen_kv(w: Workload, seed: int, layer: int, b: int, kh: int, part: Partition):
+    """Keys and values [n][d] in the storage dtype for one slice."""
+    n = part.labels.shape[0]
+    d = w.head_dim
+    rk = _rng(seed, _T_KEY, layer, b, kh)
+    rv = _rng(seed, _T_VAL, layer, b, kh)
+    noise = rk.standard_normal((n, d), dtype=np.float32)
+    k = np.empty((n, d), dtype=np.float32)
+    s = w.n_sinks
+    k[:s] = noise[:s]
+    k[s:] = part.centers[part.labels[s:]] + np.float32(w.noise) * noise[s:]
+    k *= np.float32(w.key_scale)
+    v = rv.standard_normal((n, d), dtype=np.float32)
+    return _to_storage(k, w), _to_storage(v, w)
+
+
+@dataclass
+class Slice:
+    b: int
+    kh: int
+    part: Partition
+    k: torch.Tensor  # [n][d] storage dtype (CPU)
+    v: torch.Tensor
+
+
+def gen_layer(w: Workload, seed: int, layer: int = 0, with_kv: bool = True) -> List[List[Slice]]:
+    """All (sequence, kv head) slices of one layer: result[b][kh]."""
+    lens = seq_lengths(w, seed)
+    out = []
+    for b in range(w.batch):
+        row = []
+        for kh in range(w.n_kv_heads):
+            part = gen_partition(w, seed, layer, b, kh, lens[b])
+            if with_kv:
+                k, v = gen_kv(w, seed, layer, b, kh, part)
+            else:
+                k = v = None
+            row.append(Slice(b, kh, part, k, v))
+        out.append(row)
+    return out
+
+
+def graph_labels(w: Workload, slices: List[List[Slice]]) -> List[np.ndarray]:
+    """Initial labels of every graph (query heads of one kv head share the kv
+    head's planted partition in per-head mode)."""
+    res = []
+    for g in range(w.n_graphs):
+        b, kh, _, _ = w.graph_coords(g)
+        res.append(slices[b][kh].part.labels)
+    return res
+
+
+def graph_n_comm(w: Workload, slices: List[List[Slice]]) -> List[int]:
+    return [slices[w.graph_coords(g)[0]][w.graph_coords(g)[1]].part.n_comm for g in range(w.n_graphs)]
+
+
+@dataclass
+class StepInput:
+    q: torch.Tensor      # [B][Hq][d] storage dtype
+    k_new: torch.Tensor  # [B][Hkv][d]
+    v_new: torch.Tensor  # [B][Hkv][d]
+    target: np.ndarray   # [B][Hq] planted community each query head was drawn around
+
+
+def gen_step(w: Workload, seed: int, step: int, slices: List[List[Slice]], layer: int = 0) -> StepInput:
+    """Query, new key and new value for decode step `step`.
+
+    Each query head is a planted centre of its kv head plus noise.  In
+    per-head mode every query head picks its own centre; in group mode the
+    heads of a group share one.  The new key is drawn around the centre of
+    the group's first query head, scaled like the prefill keys.
+    """
+    B, Hq, Hkv, d, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    q = np.empty((B, Hq, d), dtype=np.float32)
+    kn = np.empty((B, Hkv, d), dtype=np.float32)
+    vn = np.empty((B, Hkv, d), dtype=np.float32)
+    tgt = np.empty((B, Hq), dtype=np.int32)
+    for b in range(B):
+        for kh in range(Hkv):
+            part = slices[b][kh].part
+            r = _rng(seed, _T_STEP, layer, b, kh, step)
+            if w.mode == PER_HEAD:
+                cs = r.integers(0, part.n_comm, size=G)
+            else:
+                cs = np.repeat(r.integers(0, part.n_comm, size=1), G)
+            qn = r.standard_normal((G, d), dtype=np.float32)
+            for j in range(G):
+                q[b, kh * G + j] = part.centers[cs[j]] + np.float32(w.noise) * qn[j]
+                tgt[b, kh * G + j] = cs[j]
+            kk = r.standard_normal(d, dtype=np.float32)
+            kn[b, kh] = (part.centers[cs[0]] + np.float32(w.noise) * kk) * np.float32(w.key_scale)
+            vn[b, kh] = r.standard_normal(d, dtype=np.float32)
+    return StepInput(_to_storage(q, w), _to_storage(kn, w), _to_storage(vn, w), tgt)

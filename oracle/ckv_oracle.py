@@ -1,0 +1,359 @@
+"""CPU oracle for the CommunityKV sparse decode step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this
+module: only the tests, the smoke check and the benchmark's CPU-baseline leg
+use it.  It shares no code with the HIP library; the two meet only in the
+seeded inputs.
+
+Source: "CommunityKV: Efficient Long-Context Decoding via Graph Partitioning"
+(McKenna, Alexandridis, Susanj, Liu), Figure 1 caption, panel (3)
+"Incremental Update": at each decoding step the query is scored against the
+community centroids, a candidate subset is retrieved, exact attention runs on
+that subset together with the sink tokens, and the top-kappa attended keys
+become the new token's edges, which assign it to a community in constant
+time.  Table 1 gives the per-step update as O(d) and the retrieval as a pass
+over the centroids.  Table 6 fixes the defaults (kappa = 8, per-head graphs,
+sinks excluded from the top-kappa pool).
+
+Everything is computed in float64 with plain numpy, one graph at a time, in
+the order the caption describes.  Where the page leaves a step open, the
+reading taken is stated at the function that implements it.
+
+Decision precision.  Two integer decisions rest on floating point:
+  * community selection compares centroid scores.  The centroid table is held
+    in float32 (the mean of the members' keys, computed exactly in float64,
+    rounded once to float32); a score is the float64 dot product of the
+    aggregated query with that float32 centroid, rounded once to float32.
+    Ties of the float32 score go to the lower community id.
+  * the top-kappa edge choice compares attention weights, computed here in
+    float64; ties go to the lower token position.
+A checker compares a device decision with these under a 1e-6 tie window.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+NEG_INF32 = np.float32(-np.inf)
+
+
+# --------------------------------------------------------------------------
+# Centroids (Figure 1, panel (2): one centroid, drawn as a star, per community)
+# --------------------------------------------------------------------------
+
+def community_sums(keys: np.ndarray, labels: np.ndarray, n_comm: int):
+    """Exact float64 key sum and member count of every community.
+
+    keys: [n][d]; labels: [n] with -1 for tokens in no community (sinks).
+    Sums of bf16/fp32 keys in float64 are exact for these magnitudes.
+    """
+    keys = np.asarray(keys, dtype=np.float64)
+    labels = np.asarray(labels)
+    d = keys.shape[1]
+    m = labels >= 0
+    sums = np.zeros((n_comm, d), dtype=np.float64)
+    np.add.at(sums, labels[m], keys[m])
+    counts = np.bincount(labels[m], minlength=n_comm).astype(np.int64)
+    return sums, counts
+
+
+def community_means(sums: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """float64 centroid = mean of the members' keys (0 for an empty community)."""
+    out = np.zeros_like(sums)
+    nz = counts > 0
+    out[nz] = sums[nz] / counts[nz, None].astype(np.float64)
+    return out
+
+
+def scoring_centroids(sums: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """The centroid table as stored for scoring: the float64 mean rounded once to float32."""
+    return community_means(sums, counts).astype(np.float32)
+
+
+# --------------------------------------------------------------------------
+# Retrieval (Figure 1, panel (3): score the query against community centroids
+# and retrieve a candidate subset under a token budget)
+# --------------------------------------------------------------------------
+
+def aggregate_query(q_heads: np.ndarray) -> np.ndarray:
+    """Query vector a graph scores with.
+
+    One graph per query head: the head's own query.  Query-group graphs (the
+    page's "query group" aggregation, Table 5 / Table 6): the score of a
+    community is the sum over the group's heads of q_h . centroid, which by
+    linearity is (sum_h q_h) . centroid.
+    """
+    q = np.asarray(q_heads, dtype=np.float64).reshape(-1, np.shape(q_heads)[-1])
+    return q.sum(axis=0)
+
+
+def score_communities(qbar: np.ndarray, cent32: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """s[c] = qbar . centroid[c] (float64 sum, rounded to float32); -inf for empty c."""
+    s = (cent32.astype(np.float64) @ np.asarray(qbar, dtype=np.float64)).astype(np.float32)
+    s[np.asarray(counts) <= 0] = NEG_INF32
+    return s
+
+
+def rank_communities(scores: np.ndarray, counts: np.ndarray) -> np.ndarray:
+    """Non-empty communities ordered by score, highest first; ties: lower id first."""
+    ids = np.nonzero(np.asarray(counts) > 0)[0]
+    order = np.lexsort((ids, -scores[ids].astype(np.float64)))
+    return ids[order]
+
+
+def select_communities(scores: np.ndarray, counts: np.ndarray, budget: int,
+                       max_comm: int = 0) -> np.ndarray:
+    """Communities retrieved for attention, as ascending ids.
+
+    Reading of "retrieve a candidate subset" under a token budget: walk the
+    communities from the best score down and keep each one while the running
+    member count stays within the budget; the first community that would
+    exceed it ends the walk (no skipping ahead to smaller ones).  Sink tokens
+    are not counted against the budget.  With max_comm > 0 the walk also stops
+    after max_comm communities (the tiny workload's fixed top-4).
+    """
+    taken: List[int] = []
+    total = 0
+    for c in rank_communities(scores, counts):
+        if max_comm > 0 and len(taken) == max_comm:
+            break
+        if total + int(counts[c]) > budget:
+            break
+        taken.append(int(c))
+        total += int(counts[c])
+    return np.array(sorted(taken), dtype=np.int64)
+
+
+def attended_positions(labels: np.ndarray, n_sinks: int, selected: np.ndarray) -> np.ndarray:
+    """Token set of the exact attention: the sinks plus every member of a
+    selected community, as ascending positions.  `labels` covers exactly the
+    tokens already in the cache (the new token is not among them)."""
+    labels = np.asarray(labels)
+    members = np.nonzero(np.isin(labels, np.asarray(selected)) & (labels >= 0))[0]
+    sinks = np.arange(min(n_sinks, labels.shape[0]))
+    return np.union1d(sinks, members)
+
+
+# --------------------------------------------------------------------------
+# Exact attention on the subset (Figure 1, panel (3))
+# --------------------------------------------------------------------------
+
+def attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: float):
+    """Softmax attention of each query head over the given keys and values.
+
+    Returns (out [h][d], probs [h][T], logits [h][T]) with
+    logits = sm_scale * q . k, probs = softmax(logits) per head, out = probs @ V.
+    """
+    q = np.asarray(q_heads, dtype=np.float64).reshape(-1, np.shape(q_heads)[-1])
+    K = np.asarray(keys, dtype=np.float64)
+    V = np.asarray(values, dtype=np.float64)
+    z = float(sm_scale) * (q @ K.T)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    return p @ V, p, z
+
+
+def dense_attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: float,
+                 chunk: int = 1 << 15) -> np.ndarray:
+    """Full attention over every cached token, in float64 (chunked so large
+    contexts fit in memory; the chunks merge exactly by rescaling)."""
+    q = np.asarray(q_heads, dtype=np.float64).reshape(-1, np.shape(q_heads)[-1])
+    n = keys.shape[0]
+    z = np.concatenate([float(sm_scale) * (q @ np.asarray(keys[i:i + chunk], dtype=np.float64).T)
+                        for i in range(0, n, chunk)], axis=1)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    out = np.zeros((q.shape[0], values.shape[1]))
+    for i in range(0, n, chunk):
+        out += e[:, i:i + chunk] @ np.asarray(values[i:i + chunk], dtype=np.float64)
+    return out / e.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------
+# Incremental update (Figure 1, panel (3); Table 1 "Per-step Update O(d)")
+# --------------------------------------------------------------------------
+
+def edge_weights(probs: np.ndarray) -> np.ndarray:
+    """Attention weight of each attended token for the graph.
+
+    One graph per query head: that head's softmax probability.  Query-group
+    graphs: the sum of the group's per-head probabilities (reading: the group
+    graph's edge weight is the summed attention of its heads).
+    """
+    return np.asarray(probs, dtype=np.float64).reshape(-1, np.shape(probs)[-1]).sum(axis=0)
+
+
+def top_kappa(weights: np.ndarray, positions: np.ndarray, kappa: int, n_sinks: int) -> np.ndarray:
+    """The new token's edges: the kappa attended tokens of largest weight.
+
+    Sinks are excluded from the pool (Figure 1, panel (1); Table 6 "sinks
+    excluded").  Ties go to the lower position.  Fewer than kappa candidates:
+    all of them.  Returned in rank order.
+    """
+    positions = np.asarray(positions)
+    pool = positions >= n_sinks
+    w = np.asarray(weights, dtype=np.float64)[pool]
+    pos = positions[pool]
+    order = np.lexsort((pos, -w))
+    return pos[order[:kappa]]
+
+
+def majority_vote(edge_labels: Sequence[int]) -> int:
+    """Community holding most of the edges; ties go to the lowest id.
+    Returns -1 when there are no labelled edges."""
+    lab = np.asarray([x for x in edge_labels if x >= 0], dtype=np.int64)
+    if lab.size == 0:
+        return -1
+    vals, cnt = np.unique(lab, return_counts=True)
+    return int(vals[np.argmax(cnt)])  # unique() sorts ids, argmax takes the first maximum
+
+
+# --------------------------------------------------------------------------
+# Whole-step driver over many graphs
+# --------------------------------------------------------------------------
+
+@dataclass
+class GraphState:
+    """Community state of one graph."""
+
+    b: int                   # sequence
+    kh: int                  # kv head whose keys the graph indexes
+    qh0: int                 # first query head of the graph
+    nh: int                  # query heads of the graph
+    labels: np.ndarray       # [cap] int64, -1 = sink / not yet cached
+    sums: np.ndarray         # [C][d] float64
+    counts: np.ndarray       # [C] int64
+
+
+@dataclass
+class GraphStep:
+    scores: np.ndarray
+    selected: np.ndarray
+    positions: np.ndarray
+    out: np.ndarray          # [nh][d]
+    probs: np.ndarray        # [nh][T]
+    logits: np.ndarray       # [nh][T]
+    weights: np.ndarray      # [T] (graph edge weight of every attended token)
+    edges: np.ndarray
+    assign: int
+    top: int                 # best-scoring community
+
+
+class Oracle:
+    """Decode-step oracle for a set of graphs of one layer.
+
+    shape: any object with batch, n_q_heads, n_kv_heads, head_dim, n_sinks,
+    mode ("per_head" | "group"), budget, max_comm, kappa, sm_scale.
+    kv[b][kh] = (keys [n_b][d], values [n_b][d]) as float32-representable
+    arrays (bf16 and fp32 storage both read exactly).
+    graphs: which graphs to track (default: all).
+    """
+
+    def __init__(self, shape, kv, labels: Dict[int, np.ndarray], n_comm: Dict[int, int],
+                 graphs: Optional[Sequence[int]] = None, extra: int = 1024):
+        self.w = shape
+        B, Hq, Hkv = shape.batch, shape.n_q_heads, shape.n_kv_heads
+        self.group = Hq // Hkv
+        per_head = shape.mode == "per_head"
+        self.n_graphs = B * (Hq if per_head else Hkv)
+        self.graph_ids = list(range(self.n_graphs)) if graphs is None else list(graphs)
+        self.len: Dict[int, int] = {}
+        self.K: Dict[tuple, np.ndarray] = {}
+        self.V: Dict[tuple, np.ndarray] = {}
+        self.g: Dict[int, GraphState] = {}
+        for gid in self.graph_ids:
+            if per_head:
+                b, qh = divmod(gid, Hq)
+                kh, qh0, nh = qh // self.group, qh, 1
+            else:
+                b, kh = divmod(gid, Hkv)
+                qh0, nh = kh * self.group, self.group
+            if (b, kh) not in self.K:
+                k, v = kv[b][kh]
+                n = k.shape[0]
+                self.len[b] = n
+                self.K[(b, kh)] = np.zeros((n + extra, k.shape[1]), dtype=np.float32)
+                self.V[(b, kh)] = np.zeros((n + extra, v.shape[1]), dtype=np.float32)
+                self.K[(b, kh)][:n] = np.asarray(k, dtype=np.float32)
+                self.V[(b, kh)][:n] = np.asarray(v, dtype=np.float32)
+            n = self.len[b]
+            lab = np.full(n + extra, -1, dtype=np.int64)
+            lab[:n] = labels[gid]
+            sums, counts = community_sums(self.K[(b, kh)][:n], lab[:n], n_comm[gid])
+            self.g[gid] = GraphState(b, kh, qh0, nh, lab, sums, counts)
+
+    # -- pieces a checker may call on their own -----------------------------
+    def centroids32(self, gid: int) -> np.ndarray:
+        st = self.g[gid]
+        return scoring_centroids(st.sums, st.counts)
+
+    def graph_query(self, gid: int, q: np.ndarray) -> np.ndarray:
+        st = self.g[gid]
+        return np.asarray(q[st.b, st.qh0:st.qh0 + st.nh], dtype=np.float64)
+
+    def step_graph(self, gid: int, q: np.ndarray, force_sel=None, force_edges=None) -> GraphStep:
+        """Retrieval, attention and edge choice for one graph (no state change)."""
+        w, st = self.w, self.g[gid]
+        n = self.len[st.b]
+        qh = self.graph_query(gid, q)
+        scores = score_communities(aggregate_query(qh), self.centroids32(gid), st.counts)
+        ranked = rank_communities(scores, st.counts)
+        top = int(ranked[0]) if ranked.size else -1
+        sel = select_communities(scores, st.counts, w.budget, w.max_comm)
+        if force_sel is not None:
+            sel = np.array(sorted(int(c) for c in force_sel), dtype=np.int64)
+        pos = attended_positions(st.labels[:n], w.n_sinks, sel)
+        K = self.K[(st.b, st.kh)][pos]
+        V = self.V[(st.b, st.kh)][pos]
+        out, p, z = attend(qh, K, V, w.sm_scale)
+        wts = edge_weights(p)
+        edges = top_kappa(wts, pos, w.kappa, w.n_sinks)
+        if force_edges is not None:
+            edges = np.asarray(force_edges, dtype=np.int64)
+        a = majority_vote(st.labels[edges])
+        if a < 0:
+            a = top  # no attended non-sink token: fall back to the best-scoring community
+        return GraphStep(scores, sel, pos, out, p, z, wts, edges, a, top)
+
+    def apply_update(self, gid: int, assign: int, k_new: np.ndarray):
+        """label[P] = a, member count and key sum of a grow by the new token
+        (so the centroid becomes the running mean (n*mu + k)/(n + 1))."""
+        st = self.g[gid]
+        P = self.len[st.b]
+        if assign < 0:
+            return
+        st.labels[P] = assign
+        st.sums[assign] += np.asarray(k_new, dtype=np.float64)
+        st.counts[assign] += 1
+
+    def step(self, q, k_new, v_new, force_sel: Optional[Dict[int, Sequence[int]]] = None,
+             force_edges: Optional[Dict[int, Sequence[int]]] = None) -> Dict[int, GraphStep]:
+        """One decode step for every tracked graph, then append the new token.
+
+        q: [B][Hq][d]; k_new, v_new: [B][Hkv][d] (any float dtype).
+        force_sel / force_edges: per-graph decisions to adopt in place of the
+        oracle's own (used after a near-tie was accepted).
+        """
+        q = np.asarray(q, dtype=np.float64)
+        res = {}
+        for gid in self.graph_ids:
+            res[gid] = self.step_graph(gid, q, (force_sel or {}).get(gid), (force_edges or {}).get(gid))
+        for gid in self.graph_ids:
+            st = self.g[gid]
+            self.apply_update(gid, res[gid].assign, k_new[st.b][st.kh])
+        for (b, kh) in self.K:
+            P = self.len[b]
+            self.K[(b, kh)][P] = np.asarray(k_new[b][kh], dtype=np.float32)
+            self.V[(b, kh)][P] = np.asarray(v_new[b][kh], dtype=np.float32)
+        for b in {b for (b, _) in self.K}:
+            self.len[b] += 1
+        return res
+
+    def dense(self, q, b: int, kh: int) -> np.ndarray:
+        """Dense attention of kv head kh's query heads over all cached tokens of sequence b."""
+        n = self.len[b]
+        qh = np.asarray(q, dtype=np.float64)[b, kh * self.group:(kh + 1) * self.group]
+        return dense_attend(qh, self.K[(b, kh)][:n], self.V[(b, kh)][:n], self.w.sm_scale)

@@ -1,0 +1,222 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each mutant below plants one mistake into a copy of an oracle function (a
+dropped term, a wrong sign, a flipped comparison, a swapped operand, a wrong
+tie rule).  The pin suite is then run against the mutated oracle on the CPU
+and at least one pin has to fail.
+"""
+import numpy as np
+import pytest
+
+from oracle import ckv_oracle as O
+from tests import test_oracle_pins as P
+
+
+def _pins():
+    """The pin checks, called directly (parametrised ones over a few params)."""
+    fx = P._hand()
+    checks = [lambda c=c["name"]: P.test_hand_fixture_case(c) for c in fx["cases"]]
+    checks += [P.test_hand_fixture_sequence, P.test_centroid_brute_force_means,
+               P.test_centroid_zero_noise_is_center, P.test_score_exact_small_integers,
+               P.test_score_brute_force_fsum, P.test_group_score_is_sum_of_head_scores,
+               P.test_select_no_skip_ahead, P.test_select_everything_under_large_budget,
+               P.test_select_top_k_cap_matches_heap, P.test_attend_two_tokens_closed_form,
+               P.test_attend_matches_torch_sdpa_float64, P.test_dense_chunking_is_exact,
+               P.test_attended_positions_brute_force,
+               P.test_top_kappa_excludes_sinks_and_takes_all_when_short,
+               P.test_group_weights_explicit_loop, P.test_budget_walk_invariants_on_workload]
+    checks += [lambda s=s: P.test_select_matches_definition(s) for s in range(40)]
+    checks += [lambda s=s: P.test_top_kappa_matches_heap(s) for s in range(20)]
+    checks += [lambda s=s: P.test_vote_matches_counter(s) for s in range(20)]
+    checks += [lambda m=m: P.test_centroid_stays_member_mean(m) for m in ("per_head", "group")]
+    checks += [lambda m=m: P.test_full_budget_equals_dense(m) for m in ("per_head", "group")]
+    return checks
+
+
+def _failures(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    failed = 0
+    for chk in _pins():
+        try:
+            chk()
+        except Exception:
+            failed += 1
+    return failed
+
+
+_orig = {k: getattr(O, k) for k in dir(O) if not k.startswith("_")}
+
+
+def m_score_sign(qbar, cent32, counts):
+    return -_orig["score_communities"](qbar, cent32, counts)
+
+
+def m_score_no_empty_mask(qbar, cent32, counts):
+    return (cent32.astype(np.float64) @ np.asarray(qbar, np.float64)).astype(np.float32)
+
+
+def m_select_overflow_included(scores, counts, budget, max_comm=0):
+    taken, total = [], 0
+    for c in O.rank_communities(scores, counts):
+        if max_comm > 0 and len(taken) == max_comm:
+            break
+        taken.append(int(c))
+        total += int(counts[c])
+        if total > budget:
+            break
+    return np.array(sorted(taken), dtype=np.int64)
+
+
+def m_select_skip_ahead(scores, counts, budget, max_comm=0):
+    taken, total = [], 0
+    for c in O.rank_communities(scores, counts):
+        if max_comm > 0 and len(taken) == max_comm:
+            break
+        if total + int(counts[c]) > budget:
+            continue
+        taken.append(int(c))
+        total += int(counts[c])
+    return np.array(sorted(taken), dtype=np.int64)
+
+
+def m_rank_tie_high_id(scores, counts):
+    ids = np.nonzero(np.asarray(counts) > 0)[0]
+    order = np.lexsort((-ids, -scores[ids].astype(np.float64)))
+    return ids[order]
+
+
+def m_rank_ascending(scores, counts):
+    return _orig["rank_communities"](scores, counts)[::-1]
+
+
+def m_attend_no_norm(q_heads, keys, values, sm_scale):
+    q = np.asarray(q_heads, np.float64).reshape(-1, np.shape(q_heads)[-1])
+    z = sm_scale * (q @ np.asarray(keys, np.float64).T)
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return e @ np.asarray(values, np.float64), e, z
+
+
+def m_attend_no_scale(q_heads, keys, values, sm_scale):
+    return _orig["attend"](q_heads, keys, values, 1.0)
+
+
+def m_attend_kv_swapped(q_heads, keys, values, sm_scale):
+    return _orig["attend"](q_heads, values, keys, sm_scale)
+
+
+def m_attend_transposed_q(q_heads, keys, values, sm_scale):
+    q = np.asarray(q_heads, np.float64).reshape(-1, np.shape(q_heads)[-1])
+    return _orig["attend"](q[:, ::-1], keys, values, sm_scale)
+
+
+def m_positions_no_sinks(labels, n_sinks, selected):
+    return _orig["attended_positions"](labels, 0, selected)
+
+
+def m_topk_with_sinks(weights, positions, kappa, n_sinks):
+    return _orig["top_kappa"](weights, positions, kappa, 0)
+
+
+def m_topk_smallest(weights, positions, kappa, n_sinks):
+    return _orig["top_kappa"](-np.asarray(weights), positions, kappa, n_sinks)
+
+
+def m_topk_tie_high_pos(weights, positions, kappa, n_sinks):
+    positions = np.asarray(positions)
+    pool = positions >= n_sinks
+    w, pos = np.asarray(weights)[pool], positions[pool]
+    return pos[np.lexsort((-pos, -w))[:kappa]]
+
+
+def m_topk_off_by_one(weights, positions, kappa, n_sinks):
+    return _orig["top_kappa"](weights, positions, kappa + 1, n_sinks)
+
+
+def m_vote_high_id(edge_labels):
+    lab = np.asarray([x for x in edge_labels if x >= 0])
+    if lab.size == 0:
+        return -1
+    vals, cnt = np.unique(lab, return_counts=True)
+    return int(vals[::-1][np.argmax(cnt[::-1])])
+
+
+def m_vote_first_edge(edge_labels):
+    lab = [x for x in edge_labels if x >= 0]
+    return int(lab[0]) if lab else -1
+
+
+def m_weights_max(probs):
+    return np.asarray(probs, np.float64).reshape(-1, np.shape(probs)[-1]).max(axis=0)
+
+
+def m_agg_mean(q_heads):
+    q = np.asarray(q_heads, np.float64).reshape(-1, np.shape(q_heads)[-1])
+    return q.mean(axis=0)
+
+
+def m_means_off_by_one(sums, counts):
+    out = np.zeros_like(sums)
+    nz = counts > 0
+    out[nz] = sums[nz] / (counts[nz, None] + 1.0)
+    return out
+
+
+def m_sums_skip_first(keys, labels, n_comm):
+    keys = np.asarray(keys, np.float64)
+    labels = np.asarray(labels).copy()
+    first = np.nonzero(labels >= 0)[0]
+    if first.size:
+        labels[first[0]] = -1
+    return _orig["community_sums"](keys, labels, n_comm)
+
+
+def m_dense_last_chunk_only(q_heads, keys, values, sm_scale, chunk=1 << 15):
+    n = keys.shape[0]
+    lo = max(0, n - 1 - ((n - 1) % chunk)) if n > chunk else 0
+    return _orig["attend"](q_heads, keys[lo:], values[lo:], sm_scale)[0]
+
+
+MUTANTS = {
+    "score_communities": [m_score_sign, m_score_no_empty_mask],
+    "select_communities": [m_select_overflow_included, m_select_skip_ahead],
+    "rank_communities": [m_rank_tie_high_id, m_rank_ascending],
+    "attend": [m_attend_no_norm, m_attend_no_scale, m_attend_kv_swapped, m_attend_transposed_q],
+    "attended_positions": [m_positions_no_sinks],
+    "top_kappa": [m_topk_with_sinks, m_topk_smallest, m_topk_tie_high_pos, m_topk_off_by_one],
+    "majority_vote": [m_vote_high_id, m_vote_first_edge],
+    "edge_weights": [m_weights_max],
+    "aggregate_query": [m_agg_mean],
+    "community_means": [m_means_off_by_one],
+    "community_sums": [m_sums_skip_first],
+    "dense_attend": [m_dense_last_chunk_only],
+}
+
+
+@pytest.mark.parametrize("name,mutant", [(k, f) for k, fs in MUTANTS.items() for f in fs],
+                         ids=[f.__name__ for fs in MUTANTS.values() for f in fs])
+def test_pins_catch_mutant(monkeypatch, name, mutant):
+    assert _failures(monkeypatch, name, mutant) > 0
+
+
+def test_apply_update_mutant_caught(monkeypatch):
+    def bad(self, gid, assign, k_new):  # overwrite instead of accumulate
+        st = self.g[gid]
+        P_ = self.len[st.b]
+        if assign < 0:
+            return
+        st.labels[P_] = assign
+        st.sums[assign] = np.asarray(k_new, np.float64) * st.counts[assign]
+        st.counts[assign] += 1
+    monkeypatch.setattr(O.Oracle, "apply_update", bad)
+    failed = 0
+    for chk in _pins():
+        try:
+            chk()
+        except Exception:
+            failed += 1
+    assert failed > 0
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for chk in _pins():
+        chk()
