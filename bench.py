@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""CommunityKV decode-step benchmark on one MI355X.
+
+A step is one pass of the whole decode path over the layer: centroid scoring,
+budgeted community selection, gather + exact attention, top-kappa edges with
+assignment and centroid update (four C-ABI calls, all HIP kernels).  The
+default workload is the Llama-3.1-8B-shaped layer at 131072 tokens of context
+(batch 1, 32 query heads over 8 kv heads, head_dim 128, bf16 K/V, one graph
+per query head, token budget 4096, kappa 8), drawn synthetically.
+
+Inputs for every step are generated and copied to the GPU before timing.
+Timed passes restore the same starting state, so every pass runs the same
+steps.  Output: one JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s + gathered-KV HBM GB/s (% roofline) at 128K ctx, budget 4096"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama31_8b_128k")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--profile", action="store_true", help="only warm-up + timed steps (for rocprofv3 runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the CommunityKV step runs on a single MI355X "
+              "(multi-GPU sharding is described in the design notes, not launched)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from community_kv_retrieval_amd import ckv, runner, synth
+
+    torch.cuda.set_device(0)
+    w = synth.preset(args.workload)
+    W, K = args.warmup, args.steps
+    total = W + K
+    log(f"[bench] workload {w.name}: generating")
+    t0 = time.time()
+    slices = synth.gen_layer(w, args.seed)
+    layer = runner.load_layer(w, args.seed, extra=total + 1, slices=slices)
+    dec, buf, idx, kv = layer.dec, layer.dec.buf, layer.idx, layer.kv
+    steps_in = [synth.gen_step(w, args.seed, t, slices) for t in range(total)]
+    Q = torch.stack([s.q for s in steps_in]).cuda()
+    KN = torch.stack([s.k_new for s in steps_in]).cuda()
+    VN = torch.stack([s.v_new for s in steps_in]).cuda()
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t0:.1f}s; G={idx.n_graphs} c_cap={idx.c_cap} t_cap={buf.t_cap}")
+
+    snap = (idx.state_dict(), kv.kv.clone(), kv.seq_len.clone())
+
+    def restore():
+        idx.load_state_dict(snap[0])
+        kv.kv.copy_(snap[1])
+        kv.seq_len.copy_(snap[2])
+        torch.cuda.synchronize()
+
+    # Accounting pass: tokens gathered per step (results are deterministic,
+    # so the timed passes below gather exactly these).
+    restore()
+    tok = []
+    for t in range(total):
+        dec.step(Q[t], KN[t], VN[t])
+        tok.append(buf.tok_n.clone())
+    torch.cuda.synchronize()
+    tok = torch.stack(tok).cpu().numpy().astype(np.int64)  # [total][G]
+    assert int(idx.status.item()) == 0, f"device status {int(idx.status.item())}"
+    esz = 2 if w.dtype == "bf16" else 4
+    row_bytes = 2 * w.head_dim * esz  # K row + V row
+    gathered = tok[W:].sum(axis=1) * row_bytes  # bytes per timed step
+    n_comm = np.array(synth.graph_n_comm(w, slices), dtype=np.int64)
+    score_bytes = int(n_comm.sum()) * w.head_dim * 4
+
+    # Headline pass: K steps back to back, bracketed by synchronisation.
+    restore()
+    for t in range(W):
+        dec.step(Q[t], KN[t], VN[t])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for t in range(W, total):
+        dec.step(Q[t], KN[t], VN[t])
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / K
+    if args.profile:
+        log(f"[bench] profile run: {ms_step * 1e3:.1f} us/step")
+        return
+
+    # Breakdown pass: the same steps with an event between the four calls.
+    restore()
+    for t in range(W):
+        dec.step(Q[t], KN[t], VN[t])
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    b = buf
+    for i, t in enumerate(range(W, total)):
+        q = Q[t]
+        ev[i][0].record()
+        ckv.ckv_score_centroids(kv, idx, q, b.scores)
+        ev[i][1].record()
+        ckv.ckv_select_communities(kv, idx, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
+                                   b.tok_list, b.tok_n)
+        ev[i][2].record()
+        ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, b.out, b.logits, b.ml, b.ws)
+        ev[i][3].record()
+        ckv.ckv_assign_update(kv, idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, dec.kappa, KN[t], VN[t],
+                              b.edges, b.assign, b.ws)
+        ev[i][4].record()
+    torch.cuda.synchronize()
+    dt = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)]) * 1e3  # us
+    names = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
+    gather_us = dt[:, 2]
+    gather_gbps = float(gathered.sum() / (gather_us.sum() * 1e-6) / 1e9)
+    score_gbps = float(score_bytes * K / (dt[:, 0].sum() * 1e-6) / 1e9)
+
+    # Cold pass: a 512 MB write between steps evicts the 256 MB MALL; only the
+    # step itself is timed.
+    restore()
+    for t in range(W):
+        dec.step(Q[t], KN[t], VN[t])
+    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    cold = []
+    for t in range(W, total):
+        flush.fill_(float(t))
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dec.step(Q[t], KN[t], VN[t])
+        c.record()
+        cold.append((a, c))
+    torch.cuda.synchronize()
+    cold_us = np.array([a.elapsed_time(c) for a, c in cold]) * 1e3
+    del flush
+
+    # Dense flash-decode over every cached token of the same state.
+    dense = None
+    if not args.no_dense:
+        restore()
+        out = torch.empty_like(buf.out)
+        for _ in range(3):
+            dec.dense(Q[W], out)
+        torch.cuda.synchronize()
+        reps = 20
+        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            dec.dense(Q[W], out)
+        c.record()
+        torch.cuda.synchronize()
+        d_us = a.elapsed_time(c) / reps * 1e3
+        d_bytes = int(kv.seq_len.sum().item()) * w.n_kv_heads * row_bytes
+        dense = {"us_per_call": round(d_us, 2), "bytes": d_bytes, "gbps": round(d_bytes / (d_us * 1e-6) / 1e9, 1),
+                 "frac_of_8tbps": round(d_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.seed, slices, steps_in, args.cpu_seconds)
+
+    avg_gather = float(gathered.mean())
+    res = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_step, 1),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "ctx": w.n_ctx, "budget": w.budget, "kappa": w.kappa,
+                   "graphs": "per_query_head" if w.mode == synth.PER_HEAD else "query_group",
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "kv_dtype": w.dtype, "n_graphs": idx.n_graphs, "seed": args.seed},
+        "gathered_kv_gbps": round(gather_gbps, 1),
+        "gathered_kv_frac_of_hbm": round(gather_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "gather_attend", "achieved": round(gather_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": int(avg_gather),
+                     "avg_launch_us": round(float(gather_us.mean()), 2)},
+        "score_roofline": {"bound": "hbm", "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": round(score_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": score_bytes,
+                           "avg_launch_us": round(float(dt[:, 0].mean()), 2)},
+        "breakdown_us": {n: round(float(dt[:, j].mean()), 2) for j, n in enumerate(names)},
+        "breakdown_step_us": round(float(dt.sum(axis=1).mean()), 2),
+        "cold_step_us": {"median": round(float(np.median(cold_us)), 2),
+                         "p10": round(float(np.percentile(cold_us, 10)), 2),
+                         "p90": round(float(np.percentile(cold_us, 90)), 2)},
+        "tokens_per_step": round(float(tok[W:].sum(axis=1).mean()), 1),
+        "dense_flash_decode": dense,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, seed, slices, steps_in, seconds):
+    """The CPU oracle, as it stands, on the first steps of the same workload."""
+    import numpy as np
+
+    from community_kv_retrieval_amd import synth
+    from oracle import ckv_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    kvh = [[(s.k.float().numpy(), s.v.float().numpy()) for s in row] for row in slices]
+    orc = O.Oracle(w, kvh, dict(enumerate(synth.graph_labels(w, slices))),
+                   dict(enumerate(synth.graph_n_comm(w, slices))), extra=len(steps_in) + 1)
+    n, t_used = 0, 0.0
+    while t_used < seconds and n < len(steps_in):
+        s = steps_in[n]
+        t0 = time.perf_counter()
+        orc.step(s.q.float().numpy(), s.k_new.float().numpy(), s.v_new.float().numpy())
+        t_used += time.perf_counter() - t0
+        n += 1
+    return {"value": round(n / t_used, 3), "unit": "decode steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} decode steps of the same workload, all {w.n_graphs} graphs, float64 numpy "
+                      f"({t_used:.1f}s of CPU time; setup not timed)"}
+
+
+if __name__ == "__main__":
+    main()

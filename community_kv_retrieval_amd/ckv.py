@@ -1,0 +1,331 @@
+"""ctypes binding of libckv.so (the C ABI in include/ckv.h).
+
+Every function here only marshals arguments: torch tensors supply device
+memory and the current HIP stream, and each call goes straight to the
+library's entry point of the same name.  There is no fallback: importing this
+module raises if the library has not been built, and every call raises
+CkvError when the library rejects its arguments.
+
+The helper classes (KVStore, CommunityIndex, DecodeBuffers, Decoder) only
+allocate the device buffers the entry points expect, with the shapes the
+header documents.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from ctypes import POINTER, c_float, c_int32, c_size_t, c_void_p
+from typing import List, Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libckv.so")
+
+CKV_OK, CKV_E_INVALID, CKV_E_UNSUPPORTED, CKV_E_WORKSPACE, CKV_E_HIP = 0, -1, -2, -3, -4
+CKV_ST_TAIL_FULL, CKV_ST_CAPACITY, CKV_ST_BAD_LABEL = 1, 2, 4
+CKV_DTYPE_F32, CKV_DTYPE_BF16 = 0, 1
+CKV_MODE_PER_HEAD, CKV_MODE_QUERY_GROUP = 0, 1
+CKV_MAX_KAPPA, CKV_MAX_C_CAP = 32, 16384
+
+EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_centroids",
+           "ckv_select_communities", "ckv_gather_attend", "ckv_assign_update", "ckv_dense_attend",
+           "ckv_status_str", "ckv_abi_version")
+
+
+class CkvError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {code} ({ckv_status_str(code)})")
+        self.code = code
+
+
+class CkvKV(ctypes.Structure):
+    _fields_ = [("kv", c_void_p), ("page_table", c_void_p), ("seq_len", c_void_p),
+                ("batch", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
+                ("head_dim", c_int32), ("page_size", c_int32), ("max_pages", c_int32),
+                ("n_pages", c_int32), ("dtype", c_int32)]
+
+
+class CkvIndex(ctypes.Structure):
+    _fields_ = [("mode", c_int32), ("n_graphs", c_int32), ("c_cap", c_int32), ("l_cap", c_int32),
+                ("tail_cap", c_int32), ("n_sinks", c_int32),
+                ("n_comm", c_void_p), ("size", c_void_p), ("offs", c_void_p), ("toks", c_void_p),
+                ("label", c_void_p), ("tail_pos", c_void_p), ("tail_comm", c_void_p),
+                ("tail_len", c_void_p), ("csum", c_void_p), ("cent", c_void_p), ("status", c_void_p)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m community_kv_retrieval_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    KVP, IXP = POINTER(CkvKV), POINTER(CkvIndex)
+    sig = {
+        "ckv_workspace_bytes": (c_size_t, [KVP, IXP, c_int32]),
+        "ckv_kv_write": (c_int32, [KVP, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+        "ckv_index_build": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_score_centroids": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p]),
+        "ckv_select_communities": (c_int32, [KVP, IXP, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+        "ckv_gather_attend": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
+                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_assign_update": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                        c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                        c_void_p]),
+        "ckv_dense_attend": (c_int32, [KVP, c_void_p, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_status_str": (ctypes.c_char_p, [c_int32]),
+        "ckv_abi_version": (c_int32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+LIB = _load()
+
+
+def ckv_status_str(code: int) -> str:
+    return LIB.ckv_status_str(code).decode()
+
+
+def _check(fn: str, code: int):
+    if code != CKV_OK:
+        raise CkvError(fn, code)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Sequence[int]):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous device {dtype} {tuple(shape)}, got {t.dtype} "
+                         f"{tuple(t.shape)} (contiguous={t.is_contiguous()}, device={t.device})")
+
+
+# ---------------------------------------------------------------------------
+# Device buffers the entry points work on
+# ---------------------------------------------------------------------------
+
+class KVStore:
+    """Paged K/V pool of one layer: [n_pages][n_kv_heads][page_size][2][head_dim]."""
+
+    def __init__(self, batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int, dtype: torch.dtype,
+                 capacity: int, page_size: int = 16, device="cuda", shuffle_pages: bool = True,
+                 seed: int = 0, seq_len: Optional[Sequence[int]] = None):
+        self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim = batch, n_q_heads, n_kv_heads, head_dim
+        self.dtype, self.page_size, self.capacity = dtype, page_size, capacity
+        self.max_pages = math.ceil(capacity / page_size)
+        self.n_pages = batch * self.max_pages
+        self.kv = torch.empty((self.n_pages, n_kv_heads, page_size, 2, head_dim), dtype=dtype, device=device)
+        ids = torch.arange(self.n_pages, dtype=torch.int32)
+        if shuffle_pages:
+            g = torch.Generator().manual_seed(seed)
+            ids = ids[torch.randperm(self.n_pages, generator=g)]
+        self.page_table = ids.view(batch, self.max_pages).contiguous().to(device)
+        lens = [0] * batch if seq_len is None else list(seq_len)
+        self.seq_len = torch.tensor(lens, dtype=torch.int32, device=device)
+        self.desc = CkvKV(self.kv.data_ptr(), self.page_table.data_ptr(), self.seq_len.data_ptr(), batch,
+                          n_q_heads, n_kv_heads, head_dim, page_size, self.max_pages, self.n_pages,
+                          CKV_DTYPE_F32 if dtype == torch.float32 else CKV_DTYPE_BF16)
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+
+class CommunityIndex:
+    """Community state of every graph of one layer (ckv_index)."""
+
+    def __init__(self, kv: KVStore, mode: int, n_comm: Sequence[int], l_cap: int, tail_cap: int,
+                 n_sinks: int, c_cap: Optional[int] = None, device="cuda"):
+        G = kv.batch * (kv.n_q_heads if mode == CKV_MODE_PER_HEAD else kv.n_kv_heads)
+        if c_cap is None:
+            c_cap = max(256, 256 * math.ceil(max(n_comm) / 256))
+        D = kv.head_dim
+        i32 = dict(dtype=torch.int32, device=device)
+        self.mode, self.n_graphs, self.c_cap, self.l_cap = mode, G, c_cap, l_cap
+        self.tail_cap, self.n_sinks = tail_cap, n_sinks
+        self.n_comm = torch.tensor(list(n_comm), **i32)
+        self.size = torch.zeros((G, c_cap), **i32)
+        self.offs = torch.zeros((G, c_cap + 1), **i32)
+        self.toks = torch.zeros((G, l_cap), **i32)
+        self.label = torch.full((G, l_cap), -1, **i32)
+        self.tail_pos = torch.zeros((G, tail_cap), **i32)
+        self.tail_comm = torch.zeros((G, tail_cap), **i32)
+        self.tail_len = torch.zeros((G,), **i32)
+        self.csum = torch.zeros((G, c_cap, D), dtype=torch.float64, device=device)
+        self.cent = torch.zeros((G, D, c_cap), dtype=torch.float32, device=device)
+        self.status = torch.zeros((1,), **i32)
+        self.desc = CkvIndex(mode, G, c_cap, l_cap, tail_cap, n_sinks, *[
+            t.data_ptr() for t in (self.n_comm, self.size, self.offs, self.toks, self.label, self.tail_pos,
+                                   self.tail_comm, self.tail_len, self.csum, self.cent, self.status)])
+
+    def heads_per_graph(self, kv: KVStore) -> int:
+        return 1 if self.mode == CKV_MODE_PER_HEAD else kv.group
+
+    STATE = ("size", "offs", "toks", "label", "tail_pos", "tail_comm", "tail_len", "csum", "cent", "status")
+
+    def state_dict(self):
+        return {k: getattr(self, k).clone() for k in self.STATE + ("n_comm",)}
+
+    def load_state_dict(self, sd):
+        for k in self.STATE + ("n_comm",):
+            getattr(self, k).copy_(sd[k])
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def ckv_workspace_bytes(kv: KVStore, idx: Optional[CommunityIndex], t_cap: int) -> int:
+    return int(LIB.ckv_workspace_bytes(ctypes.byref(kv.desc), ctypes.byref(idx.desc) if idx else None, t_cap))
+
+
+def ckv_kv_write(kv: KVStore, b: int, kv_head: int, pos0: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    n = k.shape[0]
+    _need(k, "k", kv.dtype, (n, kv.head_dim))
+    _need(v, "v", kv.dtype, (n, kv.head_dim))
+    _check("ckv_kv_write", LIB.ckv_kv_write(ctypes.byref(kv.desc), b, kv_head, pos0, n, _ptr(k), _ptr(v),
+                                            _stream(stream)))
+
+
+def ckv_index_build(kv: KVStore, idx: CommunityIndex, labels_in: torch.Tensor, ws: torch.Tensor, stream=None):
+    _need(labels_in, "labels_in", torch.int32, (idx.n_graphs, idx.l_cap))
+    _check("ckv_index_build", LIB.ckv_index_build(ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(labels_in),
+                                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def ckv_score_centroids(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, scores: torch.Tensor, stream=None):
+    _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
+    _need(scores, "scores", torch.float32, (idx.n_graphs, idx.c_cap))
+    _check("ckv_score_centroids", LIB.ckv_score_centroids(ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q),
+                                                          _ptr(scores), _stream(stream)))
+
+
+def ckv_select_communities(kv: KVStore, idx: CommunityIndex, scores: torch.Tensor, budget: int, max_comm: int,
+                           sel: torch.Tensor, sel_n: torch.Tensor, top: torch.Tensor, tok_list: torch.Tensor,
+                           tok_n: torch.Tensor, stream=None):
+    G = idx.n_graphs
+    _need(scores, "scores", torch.float32, (G, idx.c_cap))
+    _need(sel, "sel", torch.int32, (G, idx.c_cap))
+    for name, t in (("sel_n", sel_n), ("top", top), ("tok_n", tok_n)):
+        _need(t, name, torch.int32, (G,))
+    t_cap = tok_list.shape[1]
+    _need(tok_list, "tok_list", torch.int32, (G, t_cap))
+    _check("ckv_select_communities", LIB.ckv_select_communities(
+        ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(scores), budget, max_comm, t_cap, _ptr(sel),
+        _ptr(sel_n), _ptr(top), _ptr(tok_list), _ptr(tok_n), _stream(stream)))
+
+
+def ckv_gather_attend(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, tok_list: torch.Tensor,
+                      tok_n: torch.Tensor, sm_scale: float, out: torch.Tensor, logits: torch.Tensor,
+                      ml: torch.Tensor, ws: torch.Tensor, stream=None):
+    G, nh, t_cap = idx.n_graphs, idx.heads_per_graph(kv), tok_list.shape[1]
+    _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
+    _need(tok_list, "tok_list", torch.int32, (G, t_cap))
+    _need(tok_n, "tok_n", torch.int32, (G,))
+    _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
+    _need(logits, "logits", torch.float32, (G, nh, t_cap))
+    _need(ml, "ml", torch.float32, (G, nh, 2))
+    _check("ckv_gather_attend", LIB.ckv_gather_attend(
+        ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q), _ptr(tok_list), _ptr(tok_n), t_cap,
+        float(sm_scale), _ptr(out), _ptr(logits), _ptr(ml), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def ckv_assign_update(kv: KVStore, idx: CommunityIndex, tok_list: torch.Tensor, tok_n: torch.Tensor,
+                      logits: torch.Tensor, ml: torch.Tensor, top: torch.Tensor, kappa: int,
+                      k_new: torch.Tensor, v_new: torch.Tensor, edges: torch.Tensor, assign: torch.Tensor,
+                      ws: torch.Tensor, stream=None):
+    G, nh, t_cap = idx.n_graphs, idx.heads_per_graph(kv), tok_list.shape[1]
+    _need(tok_list, "tok_list", torch.int32, (G, t_cap))
+    _need(logits, "logits", torch.float32, (G, nh, t_cap))
+    _need(ml, "ml", torch.float32, (G, nh, 2))
+    for name, t in (("tok_n", tok_n), ("top", top), ("assign", assign)):
+        _need(t, name, torch.int32, (G,))
+    _need(k_new, "k_new", kv.dtype, (kv.batch, kv.n_kv_heads, kv.head_dim))
+    _need(v_new, "v_new", kv.dtype, (kv.batch, kv.n_kv_heads, kv.head_dim))
+    _need(edges, "edges", torch.int32, (G, kappa))
+    _check("ckv_assign_update", LIB.ckv_assign_update(
+        ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(tok_list), _ptr(tok_n), _ptr(logits), _ptr(ml),
+        t_cap, _ptr(top), kappa, _ptr(k_new), _ptr(v_new), _ptr(edges), _ptr(assign), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def ckv_dense_attend(kv: KVStore, q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor,
+                     stream=None):
+    _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
+    _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
+    _check("ckv_dense_attend", LIB.ckv_dense_attend(ctypes.byref(kv.desc), _ptr(q), float(sm_scale), _ptr(out),
+                                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# One decode step = the four calls in order
+# ---------------------------------------------------------------------------
+
+class DecodeBuffers:
+    """Per-step outputs of the four calls, sized for one layer."""
+
+    def __init__(self, kv: KVStore, idx: CommunityIndex, budget: int, kappa: int, device="cuda"):
+        G, nh = idx.n_graphs, idx.heads_per_graph(kv)
+        self.t_cap = idx.n_sinks + min(budget, idx.l_cap)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.scores = torch.empty((G, idx.c_cap), dtype=torch.float32, device=device)
+        self.sel = torch.empty((G, idx.c_cap), **i32)
+        self.sel_n = torch.empty((G,), **i32)
+        self.top = torch.empty((G,), **i32)
+        self.tok_list = torch.empty((G, self.t_cap), **i32)
+        self.tok_n = torch.empty((G,), **i32)
+        self.out = torch.empty((kv.batch, kv.n_q_heads, kv.head_dim), dtype=torch.float32, device=device)
+        self.logits = torch.empty((G, nh, self.t_cap), dtype=torch.float32, device=device)
+        self.ml = torch.empty((G, nh, 2), dtype=torch.float32, device=device)
+        self.edges = torch.empty((G, kappa), **i32)
+        self.assign = torch.empty((G,), **i32)
+        self.ws = torch.zeros((ckv_workspace_bytes(kv, idx, self.t_cap),), dtype=torch.uint8, device=device)
+
+
+class Decoder:
+    """Runs CommunityKV decode steps for one layer on the current stream."""
+
+    def __init__(self, kv: KVStore, idx: CommunityIndex, budget: int, max_comm: int, kappa: int,
+                 sm_scale: float, device="cuda"):
+        self.kv, self.idx = kv, idx
+        self.budget, self.max_comm, self.kappa, self.sm_scale = budget, max_comm, kappa, sm_scale
+        self.buf = DecodeBuffers(kv, idx, budget, kappa, device)
+
+    def build(self, labels_in: torch.Tensor, stream=None):
+        ckv_index_build(self.kv, self.idx, labels_in, self.buf.ws, stream)
+
+    def retrieve(self, q: torch.Tensor, stream=None):
+        b = self.buf
+        ckv_score_centroids(self.kv, self.idx, q, b.scores, stream)
+        ckv_select_communities(self.kv, self.idx, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
+                               b.tok_list, b.tok_n, stream)
+
+    def attend(self, q: torch.Tensor, stream=None):
+        b = self.buf
+        ckv_gather_attend(self.kv, self.idx, q, b.tok_list, b.tok_n, self.sm_scale, b.out, b.logits, b.ml, b.ws,
+                          stream)
+
+    def update(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+        b = self.buf
+        ckv_assign_update(self.kv, self.idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, self.kappa, k_new, v_new,
+                          b.edges, b.assign, b.ws, stream)
+
+    def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+        self.retrieve(q, stream)
+        self.attend(q, stream)
+        self.update(k_new, v_new, stream)
+        return self.buf.out
+
+    def dense(self, q: torch.Tensor, out: torch.Tensor, stream=None):
+        ckv_dense_attend(self.kv, q, self.sm_scale, out, self.buf.ws, stream)
+        return out

@@ -1,0 +1,351 @@
+// Exact softmax attention over a gathered token list (the CommunityKV page,
+// Figure 1 panel (3): exact attention on the retrieved subset together with
+// the sink tokens) and the dense flash-decode baseline over every cached token.
+//
+// One block of 256 threads (4 waves) attends a span of tokens of one unit (a
+// graph for the gather, a (sequence, kv head) for the dense baseline).  Each
+// token row [K | V] is read by 16 lanes, every lane loading one contiguous
+// slice of K and of V (16 B for bf16 d=128), so one wave instruction fetches
+// four 256-byte K rows.  All loads of a pass are issued before any arithmetic
+// to keep many row fetches in flight.  The q.k dot product is reduced inside
+// the 16-lane row with DPP; the softmax state (max, sum, accumulator) is kept
+// per lane in float32 and merged across token rows, waves and blocks with the
+// usual log-sum-exp rescaling.  The last block of a unit to finish (counted
+// with a device-scope atomic that it then resets) merges the per-block
+// partials, so the whole split-K attention is one launch.  Blocks of one unit
+// run on different XCDs, whose L2 caches are not coherent with each other:
+// partial records are padded to whole cache lines and written and read with
+// device-scope accesses, fenced on both sides of the counter.
+#include "ckv_device.h"
+#include "ckv_internal.h"
+
+namespace ckv {
+
+struct AttendParams {
+    const void *kv;
+    const int32_t *page_table;
+    const int32_t *seq_len;
+    int Hq, Hkv, ps_log2, max_pages;
+    const void *q;
+    const int32_t *tok_list;
+    const int32_t *tok_n;
+    int t_cap;
+    int mode;
+    float sm_scale;
+    float *out;
+    float *logits;
+    float *ml;
+    float *part;
+    int32_t *ctr;
+    int nchunk;  // blocks per unit
+};
+
+template <typename T, int D, int NH>
+constexpr int pick_u() {
+    return (NH >= 8 || RowSlice<T, D>::BYTES == 32) ? 4 : 8;
+}
+
+template <typename T, int D, int NH, int U, bool DENSE>
+__global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
+    using RS = RowSlice<T, D>;
+    constexpr int E = RS::E;
+    constexpr int SPAN = 16 * U;
+    constexpr int PER_BLOCK = DENSE ? kDenseTokens : kGatherTokens;
+    constexpr int ITERS = PER_BLOCK / SPAN;
+    constexpr int PS = part_stride(D);
+
+    __shared__ uint32_t s_row[PER_BLOCK];
+    __shared__ float s_q[NH][D];
+    __shared__ float s_wm[4][NH], s_wl[4][NH];
+    __shared__ float s_wacc[4][NH][D];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, ts = lane >> 4;
+    const int unit = blockIdx.x / a.nchunk;
+    const int chunk = blockIdx.x - unit * a.nchunk;
+
+    int b, kh, qh0, n;
+    if constexpr (DENSE) {
+        b = unit / a.Hkv;
+        kh = unit - b * a.Hkv;
+        qh0 = kh * NH;
+        n = a.seq_len[b];
+    } else {
+        const GraphCoords gc = graph_coords(unit, a.mode, a.Hq, a.Hkv);
+        b = gc.b;
+        kh = gc.kh;
+        qh0 = gc.qh0;
+        n = a.tok_n[unit];
+    }
+    const int start = chunk * PER_BLOCK;
+    if (n <= 0 && chunk == 0) {  // nothing to attend: zero output, empty softmax state
+        for (int i = tid; i < NH * D; i += 256) a.out[((size_t)b * a.Hq + qh0) * D + i] = 0.f;
+        if (!DENSE && tid < NH) {
+            a.ml[((size_t)unit * NH + tid) * 2] = kNegInf;
+            a.ml[((size_t)unit * NH + tid) * 2 + 1] = 0.f;
+        }
+        return;
+    }
+    if (start >= n) return;
+    const int nact = (n + PER_BLOCK - 1) / PER_BLOCK;
+    const int cnt = min(PER_BLOCK, n - start);
+
+    // Stage the row index of every token of the span (rows past the end
+    // repeat the span's first token and are masked below).
+    {
+        const int32_t *ptab = a.page_table + (size_t)b * a.max_pages;
+        const int32_t *tl = DENSE ? nullptr : a.tok_list + (size_t)unit * a.t_cap + start;
+        const uint32_t smask = (1u << a.ps_log2) - 1u;
+        for (int t = tid; t < PER_BLOCK; t += 256) {
+            const int tt = t < cnt ? t : 0;
+            const int pos = DENSE ? start + tt : tl[tt];
+            const int page = ptab[pos >> a.ps_log2];
+            s_row[t] = ((uint32_t)(page * a.Hkv + kh) << a.ps_log2) | ((uint32_t)pos & smask);
+        }
+        const T *qp = reinterpret_cast<const T *>(a.q) + ((size_t)b * a.Hq + qh0) * D;
+        for (int i = tid; i < NH * D; i += 256) s_q[i / D][i % D] = to_f32(qp[i]);
+    }
+    __syncthreads();
+
+    float qr[NH][E];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) qr[h][e] = s_q[h][l16 * E + e];
+
+    float m[NH], l[NH], acc[NH][E];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+
+    const T *kvb = reinterpret_cast<const T *>(a.kv);
+    for (int it = 0; it < ITERS; ++it) {
+        const int base = it * SPAN;
+        if (base >= cnt) break;
+        typename RS::F kf[U], vf[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = base + u * 16 + wave * 4 + ts;
+            const T *row = kvb + (size_t)s_row[t] * (2 * D) + l16 * E;
+            kf[u] = RS::load(row);
+            vf[u] = RS::load(row + D);
+        }
+        float z[NH][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float k[E];
+            RS::to_float(kf[u], k);
+            const int t = base + u * 16 + wave * 4 + ts;
+            const bool valid = t < cnt;
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                float d = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) d = fmaf(qr[h][e], k[e], d);
+                d = row16_sum(d);
+                z[h][u] = valid ? d * a.sm_scale : kNegInf;
+            }
+            if constexpr (!DENSE) {
+                if (l16 == 0 && valid) {
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        a.logits[((size_t)unit * NH + h) * a.t_cap + start + t] = z[h][u];
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            float mn = m[h];
+#pragma unroll
+            for (int u = 0; u < U; ++u) mn = fmaxf(mn, z[h][u]);
+            const float sc = (m[h] == kNegInf) ? 0.f : exp2f((m[h] - mn) * kLog2e);
+            l[h] *= sc;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] *= sc;
+            m[h] = mn;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float v[E];
+            RS::to_float(vf[u], v);
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const float p = (z[h][u] == kNegInf) ? 0.f : exp2f((z[h][u] - m[h]) * kLog2e);
+                l[h] += p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+            }
+        }
+    }
+
+    // Merge the four token rows of the wave (lanes l16, l16+16, l16+32, l16+48).
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int msk = 16; msk <= 32; msk <<= 1) {
+            const float mo = shfl_xor_f(m[h], msk), lo = shfl_xor_f(l[h], msk);
+            float M, s1, s2;
+            softmax_scales(m[h], mo, M, s1, s2);
+            l[h] = l[h] * s1 + lo * s2;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float ao = shfl_xor_f(acc[h][e], msk);
+                acc[h][e] = acc[h][e] * s1 + ao * s2;
+            }
+            m[h] = M;
+        }
+    }
+    if (ts == 0) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            if (l16 == 0) {
+                s_wm[wave][h] = m[h];
+                s_wl[wave][h] = l[h];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_wacc[wave][h][l16 * E + e] = acc[h][e];
+        }
+    }
+    __syncthreads();
+
+    // Block result per head: merge the four waves in a fixed order.
+    float *P = a.part + (size_t)unit * NH * a.nchunk * PS;
+    for (int i = tid; i < NH * D; i += 256) {
+        const int h = i / D, d = i - (i / D) * D;
+        float M = s_wm[0][h];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) M = fmaxf(M, s_wm[w][h]);
+        float o = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float s = (s_wm[w][h] == kNegInf) ? 0.f : exp2f((s_wm[w][h] - M) * kLog2e);
+            o += s_wacc[w][h][d] * s;
+            L += s_wl[w][h] * s;
+        }
+        if (nact == 1) {
+            a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = o / L;
+            if (!DENSE && d == 0) {
+                a.ml[((size_t)unit * NH + h) * 2] = M;
+                a.ml[((size_t)unit * NH + h) * 2 + 1] = L;
+            }
+        } else {
+            float *dst = P + ((size_t)h * a.nchunk + chunk) * PS;
+            __hip_atomic_store(dst + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == 0) {
+                __hip_atomic_store(dst + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(dst + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    if (nact == 1) return;
+
+    // The last block of the unit merges every block's partial.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(&a.ctr[unit], 1) == nact - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    for (int i = tid; i < NH * D; i += 256) {
+        const int h = i / D, d = i - (i / D) * D;
+        float *src = P + (size_t)h * a.nchunk * PS;
+        float M = kNegInf;
+        for (int c = 0; c < nact; ++c)
+            M = fmaxf(M, __hip_atomic_load(src + (size_t)c * PS + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        float L = 0.f, O = 0.f;
+        for (int c = 0; c < nact; ++c) {
+            float *pc = src + (size_t)c * PS;
+            const float mc = __hip_atomic_load(pc + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float s = (mc == kNegInf) ? 0.f : exp2f((mc - M) * kLog2e);
+            L += __hip_atomic_load(pc + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * s;
+            O += __hip_atomic_load(pc + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * s;
+        }
+        a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = O / L;
+        if (!DENSE && d == 0) {
+            a.ml[((size_t)unit * NH + h) * 2] = M;
+            a.ml[((size_t)unit * NH + h) * 2 + 1] = L;
+        }
+    }
+    if (tid == 0) a.ctr[unit] = 0;
+}
+
+template <typename T, int D, int NH, bool DENSE>
+static hipError_t launch_t(const AttendParams &p, int units, hipStream_t s) {
+    constexpr int U = pick_u<T, D, NH>();
+    hipLaunchKernelGGL((attend_kernel<T, D, NH, U, DENSE>), dim3(units * p.nchunk), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+template <bool DENSE>
+static hipError_t dispatch(const ckv_kv *kv, int nh, const AttendParams &p, int units, hipStream_t s) {
+    const bool bf = kv->dtype == CKV_DTYPE_BF16;
+    const int D = kv->head_dim;
+#define CKV_ATT(TT, DD, NN) \
+    if (D == DD && nh == NN) return launch_t<TT, DD, NN, DENSE>(p, units, s);
+#define CKV_ATT_T(TT)                                                                          \
+    CKV_ATT(TT, 64, 1) CKV_ATT(TT, 64, 2) CKV_ATT(TT, 64, 4) CKV_ATT(TT, 64, 8)                \
+    CKV_ATT(TT, 128, 1) CKV_ATT(TT, 128, 2) CKV_ATT(TT, 128, 4) CKV_ATT(TT, 128, 8)
+    if (bf) {
+        CKV_ATT_T(bf16_t)
+    } else {
+        CKV_ATT_T(float)
+    }
+#undef CKV_ATT_T
+#undef CKV_ATT
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                         const int32_t *tok_list, const int32_t *tok_n, int t_cap, float sm_scale,
+                         float *out, float *logits, float *ml, float *part, int32_t *ctr,
+                         hipStream_t s) {
+    AttendParams p{};
+    p.kv = kv->kv;
+    p.page_table = kv->page_table;
+    p.seq_len = kv->seq_len;
+    p.Hq = kv->n_q_heads;
+    p.Hkv = kv->n_kv_heads;
+    p.ps_log2 = __builtin_ctz((unsigned)kv->page_size);
+    p.max_pages = kv->max_pages;
+    p.q = q;
+    p.tok_list = tok_list;
+    p.tok_n = tok_n;
+    p.t_cap = t_cap;
+    p.mode = idx->mode;
+    p.sm_scale = sm_scale;
+    p.out = out;
+    p.logits = logits;
+    p.ml = ml;
+    p.part = part;
+    p.ctr = ctr;
+    p.nchunk = ceil_div(t_cap, kGatherTokens);
+    return dispatch<false>(kv, heads_per_graph(kv, idx), p, idx->n_graphs, s);
+}
+
+hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *part,
+                        int32_t *ctr, hipStream_t s) {
+    AttendParams p{};
+    p.kv = kv->kv;
+    p.page_table = kv->page_table;
+    p.seq_len = kv->seq_len;
+    p.Hq = kv->n_q_heads;
+    p.Hkv = kv->n_kv_heads;
+    p.ps_log2 = __builtin_ctz((unsigned)kv->page_size);
+    p.max_pages = kv->max_pages;
+    p.q = q;
+    p.t_cap = 0;
+    p.mode = CKV_MODE_QUERY_GROUP;
+    p.sm_scale = sm_scale;
+    p.out = out;
+    p.part = part;
+    p.ctr = ctr;
+    p.nchunk = ceil_div(ctx_cap(kv), kDenseTokens);
+    return dispatch<true>(kv, group_of(kv), p, kv->batch * kv->n_kv_heads, s);
+}
+
+}  // namespace ckv

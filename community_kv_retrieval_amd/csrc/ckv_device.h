@@ -1,0 +1,150 @@
+// Device helpers shared by the libckv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ckv.h"
+
+namespace ckv {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+
+// ---------------------------------------------------------------------------
+// One lane's slice of a K or V row.  A row of head_dim elements is spread over
+// 16 lanes; lane l16 holds elements [l16*E, l16*E+E), E = D/16.
+// ---------------------------------------------------------------------------
+template <int BYTES> struct Frag;
+template <> struct Frag<8> { uint2 w; };
+template <> struct Frag<16> { uint4 w; };
+template <> struct Frag<32> { uint4 w0, w1; };
+
+template <typename T, int D> struct RowSlice {
+    static constexpr int E = D / 16;
+    static constexpr int BYTES = E * (int)sizeof(T);
+    typedef Frag<BYTES> F;
+
+    __device__ __forceinline__ static F load(const T *p) {
+        F f;
+        if constexpr (BYTES == 8) {
+            f.w = *reinterpret_cast<const uint2 *>(p);
+        } else if constexpr (BYTES == 16) {
+            f.w = *reinterpret_cast<const uint4 *>(p);
+        } else {
+            f.w0 = reinterpret_cast<const uint4 *>(p)[0];
+            f.w1 = reinterpret_cast<const uint4 *>(p)[1];
+        }
+        return f;
+    }
+
+    __device__ __forceinline__ static void to_float(const F &f, float (&x)[E]) {
+        uint32_t w[BYTES / 4];
+        if constexpr (BYTES == 8) {
+            w[0] = f.w.x; w[1] = f.w.y;
+        } else if constexpr (BYTES == 16) {
+            w[0] = f.w.x; w[1] = f.w.y; w[2] = f.w.z; w[3] = f.w.w;
+        } else {
+            w[0] = f.w0.x; w[1] = f.w0.y; w[2] = f.w0.z; w[3] = f.w0.w;
+            w[4] = f.w1.x; w[5] = f.w1.y; w[6] = f.w1.z; w[7] = f.w1.w;
+        }
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = __uint_as_float(w[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < E / 2; ++e) {
+                x[2 * e] = __uint_as_float(w[e] << 16);
+                x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers.  Within a row of 16 lanes the butterfly uses DPP:
+// quad_perm swaps neighbours and pairs inside a quad, row_half_mirror pairs the
+// two quads of each half-row, row_mirror pairs the two half-rows.  After the
+// four steps every lane of the row holds the full row reduction.
+// ---------------------------------------------------------------------------
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<kQuadSwap1>(x);
+    x += dpp_f<kQuadSwap2>(x);
+    x += dpp_f<kRowHalfMirror>(x);
+    x += dpp_f<kRowMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
+
+// Merge two partial softmax states (max m, sum l, unnormalised accumulator).
+__device__ __forceinline__ void softmax_scales(float m1, float m2, float &M, float &s1, float &s2) {
+    M = fmaxf(m1, m2);
+    s1 = (m1 == kNegInf) ? 0.f : exp2f((m1 - M) * kLog2e);
+    s2 = (m2 == kNegInf) ? 0.f : exp2f((m2 - M) * kLog2e);
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x = NT, NT % 64 == 0).
+// `scratch` needs NT/64 + 1 ints of shared memory.  Returns the exclusive prefix;
+// *total receives the block sum.  Contains two barriers.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) scratch[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int acc = 0;
+        for (int w = 0; w < NT / 64; ++w) {
+            int t = scratch[w];
+            scratch[w] = acc;
+            acc += t;
+        }
+        scratch[NT / 64] = acc;
+    }
+    __syncthreads();
+    *total = scratch[NT / 64];
+    return scratch[wave] + x - v;
+}
+
+// Coordinates of graph g: sequence, kv head, first query head, query heads.
+struct GraphCoords {
+    int b, kh, qh0, nh;
+};
+__device__ __forceinline__ GraphCoords graph_coords(int g, int mode, int n_q_heads, int n_kv_heads) {
+    GraphCoords c;
+    const int grp = n_q_heads / n_kv_heads;
+    if (mode == CKV_MODE_PER_HEAD) {
+        c.b = g / n_q_heads;
+        const int qh = g - c.b * n_q_heads;
+        c.kh = qh / grp;
+        c.qh0 = qh;
+        c.nh = 1;
+    } else {
+        c.b = g / n_kv_heads;
+        c.kh = g - c.b * n_kv_heads;
+        c.qh0 = c.kh * grp;
+        c.nh = grp;
+    }
+    return c;
+}
+
+}  // namespace ckv

@@ -1,0 +1,94 @@
+// Host-side declarations shared by the libckv translation units: launch
+// shapes, workspace layout and the per-kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ckv.h"
+
+namespace ckv {
+
+// Tokens one gather block attends: 16 tokens per pass of its 256 threads
+// (4 waves x 4 rows of 16 lanes), kGatherU passes per block.
+constexpr int kGatherU = 8;
+constexpr int kGatherTokens = 16 * kGatherU;
+// The dense baseline walks kDenseIters such spans per block.
+constexpr int kDenseU = 8;
+constexpr int kDenseIters = 8;
+constexpr int kDenseTokens = 16 * kDenseU * kDenseIters;
+
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+// Floats of one split-K partial record (accumulator, max, sum), padded to whole
+// 128-byte cache lines so records written by different blocks never share a line.
+constexpr int part_stride(int d) { return ((d + 2 + 31) / 32) * 32; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int group_of(const ckv_kv *kv) { return kv->n_q_heads / kv->n_kv_heads; }
+inline int heads_per_graph(const ckv_kv *kv, const ckv_index *idx) {
+    return idx->mode == CKV_MODE_PER_HEAD ? 1 : group_of(kv);
+}
+inline int ctx_cap(const ckv_kv *kv) { return kv->max_pages * kv->page_size; }
+
+// Workspace layout.  The dense baseline's region comes first and depends only
+// on the K/V shape, so one workspace serves the dense baseline and the sparse
+// path alike.  Counters are self-resetting.
+struct WsLayout {
+    size_t ctr_dense, part_dense;              // dense baseline
+    size_t dense_total;                        // bytes the dense baseline needs
+    size_t ctr_gather, ctr_assign;             // int32 counters (byte offsets)
+    size_t part_gather;                        // float partials
+    size_t build_cursor;                       // int32 [G][c_cap]
+    size_t total;
+};
+
+// idx == nullptr: only the dense baseline's part.
+inline WsLayout ws_layout(const ckv_kv *kv, const ckv_index *idx, int t_cap) {
+    WsLayout L{};
+    const size_t units_dense = (size_t)kv->batch * kv->n_kv_heads;
+    const size_t D2 = (size_t)part_stride(kv->head_dim);
+    size_t off = 0;
+    L.ctr_dense = off;
+    off = align256(off + 4 * units_dense);
+    L.part_dense = off;
+    off += align256(4 * units_dense * group_of(kv) * (size_t)ceil_div(ctx_cap(kv), kDenseTokens) * D2);
+    L.dense_total = off;
+    if (!idx) {
+        L.total = off;
+        return L;
+    }
+    const size_t G = (size_t)idx->n_graphs;
+    L.ctr_gather = off;
+    L.ctr_assign = off + 4 * G;
+    off = align256(off + 4 * G + 4);
+    L.part_gather = off;
+    off += align256(4 * G * heads_per_graph(kv, idx) * (size_t)ceil_div(t_cap > 0 ? t_cap : 1, kGatherTokens) * D2);
+    L.build_cursor = off;
+    off += align256(4 * G * (size_t)idx->c_cap);
+    L.total = off;
+    return L;
+}
+
+// Launchers (each returns the hipError_t of its launches).
+hipError_t launch_kv_write(const ckv_kv *kv, int b, int kh, int pos0, int n, const void *k,
+                           const void *v, hipStream_t s);
+hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t *labels_in,
+                              int32_t *cursor, hipStream_t s);
+hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, float *scores,
+                        hipStream_t s);
+hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *scores, int budget,
+                         int max_comm, int t_cap, int32_t *sel, int32_t *sel_n, int32_t *top,
+                         int32_t *tok_list, int32_t *tok_n, hipStream_t s);
+hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                         const int32_t *tok_list, const int32_t *tok_n, int t_cap, float sm_scale,
+                         float *out, float *logits, float *ml, float *part, int32_t *ctr,
+                         hipStream_t s);
+hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *part,
+                        int32_t *ctr, hipStream_t s);
+hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
+                         const int32_t *tok_n, const float *logits, const float *ml, int t_cap,
+                         const int32_t *top, int kappa, const void *k_new, const void *v_new,
+                         int32_t *edges, int32_t *assign, int32_t *ctr, hipStream_t s);
+
+}  // namespace ckv

@@ -1,0 +1,210 @@
+/*
+ * ckv.h -- C ABI of libckv.so, the CommunityKV sparse decode step on AMD
+ * MI355X (gfx950).
+ *
+ * The method: "CommunityKV: Efficient Long-Context Decoding via Graph
+ * Partitioning" (McKenna, Alexandridis, Susanj, Liu).  Its Figure 1 caption,
+ * panel (3) "Incremental Update", defines one decode step: score the query
+ * against the community centroids, retrieve a candidate subset of
+ * communities, run exact attention over that subset together with the sink
+ * tokens, then use the top-kappa attended keys as the new token's edges and
+ * assign the token to a community in constant time.  Table 1 gives the
+ * per-step update as O(d).  Table 6 fixes kappa = 8, sinks excluded from the
+ * top-kappa pool, and one graph per query head as the default; Tables 5 and 6
+ * name query-group graphs (one graph per kv head, shared by its query heads)
+ * as the alternative aggregation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers inside the descriptors and all array arguments are DEVICE
+ *    pointers (memory the caller allocated on the GPU the stream belongs to),
+ *    except the descriptors themselves, which are host structs read during
+ *    the call only.
+ *  - The library allocates, frees and synchronises nothing.  Every call only
+ *    validates its arguments on the host and enqueues kernels on `stream`
+ *    (NULL = the null stream); it returns before the work runs.  Buffers must
+ *    stay alive until the stream work has finished.
+ *  - Host-side validation happens before any device call: a call that returns
+ *    an error has enqueued nothing.
+ *  - Outputs are overwritten, never accumulated.  Results are deterministic
+ *    (no floating-point atomics; every reduction has a fixed order).
+ *  - Conditions only the device can see (a full tail, a position beyond the
+ *    capacity, a bad label) set bits in idx->status[0]; they never fault.
+ *  - Calls that touch disjoint descriptors and workspaces may run on different
+ *    streams concurrently.  Two calls sharing a workspace must be ordered.
+ *
+ * Memory layout
+ * -------------
+ *  K/V pool: kv->kv holds n_pages pages; page p, kv head h, slot s holds one
+ *    token as [K row | V row], each head_dim elements of kv->dtype:
+ *      element (p, h, s, which, e) at ((((p * n_kv_heads + h) * page_size + s) * 2 + which) * head_dim + e)
+ *    which = 0 for K, 1 for V.  Position t of sequence b lives in page
+ *    page_table[b * max_pages + t / page_size], slot t % page_size.
+ *  Graphs: one per query head (CKV_MODE_PER_HEAD, G = batch * n_q_heads,
+ *    graph g = b * n_q_heads + qh, indexing kv head qh / (n_q_heads/n_kv_heads))
+ *    or one per kv head (CKV_MODE_QUERY_GROUP, G = batch * n_kv_heads,
+ *    graph g = b * n_kv_heads + kh, read by query heads kh*grp .. kh*grp+grp-1).
+ *  Positions 0 .. n_sinks-1 of every sequence are sink tokens: attended at
+ *    every step, in no community, never an edge.
+ */
+#ifndef CKV_H
+#define CKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *ckv_stream_t; /* a hipStream_t */
+
+typedef int32_t ckv_status;
+#define CKV_OK             0
+#define CKV_E_INVALID     -1 /* null pointer, bad size or shape */
+#define CKV_E_UNSUPPORTED -2 /* head_dim not 64/128, unknown dtype, heads per group not 1/2/4/8 */
+#define CKV_E_WORKSPACE   -3 /* workspace missing or smaller than ckv_workspace_bytes() */
+#define CKV_E_HIP         -4 /* a kernel launch failed (the HIP error is consumed) */
+
+/* bits of idx->status[0] (set by the device, cleared by ckv_index_build) */
+#define CKV_ST_TAIL_FULL   1 /* a new token found its graph's tail full: left unassigned */
+#define CKV_ST_CAPACITY    2 /* a new position reached l_cap or the page table's end: not stored */
+#define CKV_ST_BAD_LABEL   4 /* ckv_index_build met a label >= n_comm[g] (ignored) */
+
+#define CKV_DTYPE_F32  0
+#define CKV_DTYPE_BF16 1
+
+#define CKV_MODE_PER_HEAD    0
+#define CKV_MODE_QUERY_GROUP 1
+
+#define CKV_MAX_KAPPA 32
+#define CKV_MAX_C_CAP 16384
+
+/* The paged K/V store of one attention layer (layout above). */
+typedef struct ckv_kv {
+    void          *kv;          /* [n_pages][n_kv_heads][page_size][2][head_dim] of dtype */
+    const int32_t *page_table;  /* [batch][max_pages] page ids, each < n_pages */
+    int32_t       *seq_len;     /* [batch] tokens cached per sequence; ckv_assign_update adds one */
+    int32_t batch;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;         /* n_q_heads / n_kv_heads must be 1, 2, 4 or 8 */
+    int32_t head_dim;           /* 64 or 128 */
+    int32_t page_size;          /* power of two, 1 .. 1024 */
+    int32_t max_pages;          /* page-table entries per sequence */
+    int32_t n_pages;
+    int32_t dtype;              /* CKV_DTYPE_F32 or CKV_DTYPE_BF16 (also the dtype of q, k_new, v_new) */
+} ckv_kv;
+
+/* Community state of every graph of one layer.  Community ids of graph g are
+ * 0 .. n_comm[g]-1.  Members of community c are the base members
+ * toks[g][offs[g][c] .. offs[g][c+1]) (fixed by ckv_index_build) plus the
+ * tokens appended since, listed in the graph's tail. */
+typedef struct ckv_index {
+    int32_t  mode;       /* CKV_MODE_PER_HEAD or CKV_MODE_QUERY_GROUP */
+    int32_t  n_graphs;   /* G: batch*n_q_heads (per head) or batch*n_kv_heads (group) */
+    int32_t  c_cap;      /* community slots per graph: multiple of 256, <= CKV_MAX_C_CAP */
+    int32_t  l_cap;      /* positions per graph (label stride); new positions must stay below */
+    int32_t  tail_cap;   /* tokens a graph can take after the build, 1 .. 4096 */
+    int32_t  n_sinks;    /* leading sink positions, >= 0 */
+    int32_t *n_comm;     /* [G] communities in use, <= c_cap (set by the caller before the build) */
+    int32_t *size;       /* [G][c_cap] members per community (base + tail) */
+    int32_t *offs;       /* [G][c_cap+1] base CSR offsets into toks */
+    int32_t *toks;       /* [G][l_cap] base members, grouped by community, ascending position */
+    int32_t *label;      /* [G][l_cap] community of every position, -1 = sink / none */
+    int32_t *tail_pos;   /* [G][tail_cap] appended positions, in order */
+    int32_t *tail_comm;  /* [G][tail_cap] their communities */
+    int32_t *tail_len;   /* [G] */
+    double  *csum;       /* [G][c_cap][head_dim] exact float64 key sum of every community */
+    float   *cent;       /* [G][head_dim][c_cap] centroid = float32(csum / size), transposed */
+    int32_t *status;     /* [1] CKV_ST_* bits */
+} ckv_index;
+
+/* Bytes of workspace the calls below need for this layer shape and a token
+ * list capacity t_cap.  The workspace must be zero-filled once before its first
+ * use; the calls leave it zero-filled where it matters.  0 on bad arguments. */
+size_t ckv_workspace_bytes(const ckv_kv *kv, const ckv_index *idx, int32_t t_cap);
+
+/* Store n tokens of sequence b, kv head kv_head at positions pos0 .. pos0+n-1.
+ * k, v: [n][head_dim] of kv->dtype.  Does not change seq_len (setup helper for
+ * filling a prefill cache). */
+ckv_status ckv_kv_write(const ckv_kv *kv, int32_t b, int32_t kv_head, int32_t pos0, int32_t n,
+                        const void *k, const void *v, ckv_stream_t stream);
+
+/* Build the community index from a given partition (the page's prefill
+ * partition, Figure 1 panel (2); here any labelling the caller supplies).
+ * labels_in: [G][l_cap] community of each position < seq_len[b] (-1 = none;
+ * positions < n_sinks are always sinks).  idx->n_comm must hold each graph's
+ * community count.  Fills size, offs, toks, label, csum and cent (centroid =
+ * mean of the members' keys, Figure 1 panel (2) "a centroid per community"),
+ * empties the tails and clears status. */
+ckv_status ckv_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t *labels_in,
+                           void *ws, size_t ws_bytes, ckv_stream_t stream);
+
+/* Score every community against the query (Figure 1 panel (3): "score the
+ * query against community centroids").  q: [batch][n_q_heads][head_dim] of
+ * kv->dtype.  The graph's query is its head's q (per head) or the sum of its
+ * group's q (query group; the group's summed q.centroid).  scores: [G][c_cap]
+ * float32 = float32(sum_d qbar_d * cent_d) accumulated in float64; -inf for
+ * empty communities and ids >= n_comm[g]. */
+ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                               float *scores, ckv_stream_t stream);
+
+/* Retrieve communities under the token budget (Figure 1 panel (3): "retrieve
+ * a candidate subset").  Communities are ranked by score, higher first, ties to
+ * the lower id; the longest prefix of that ranking whose member count stays
+ * within `budget` (and, if max_comm > 0, holds at most max_comm communities)
+ * is taken: the first community that does not fit ends the walk.
+ * Outputs per graph: sel[G][c_cap] taken ids ascending, sel_n[G] their count,
+ * top[G] the best-ranked non-empty community (-1 if none), tok_list[G][t_cap]
+ * the attended positions (sinks first, then members of the taken communities)
+ * and tok_n[G] their count.  Requires t_cap >= n_sinks + min(budget, l_cap). */
+ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const float *scores,
+                                  int32_t budget, int32_t max_comm, int32_t t_cap,
+                                  int32_t *sel, int32_t *sel_n, int32_t *top,
+                                  int32_t *tok_list, int32_t *tok_n, ckv_stream_t stream);
+
+/* Exact softmax attention of each graph's query heads over its token list
+ * (Figure 1 panel (3): "run exact attention on this subset together with sink
+ * tokens").  z_j = sm_scale * q . k_j in float32 from the stored K; outputs:
+ * out[batch][n_q_heads][head_dim] float32 (every query head is written),
+ * logits[G][hpg][t_cap] the z_j of each slot < tok_n[g] (hpg = heads per graph),
+ * ml[G][hpg][2] = (max z, sum exp(z - max)). */
+ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                             const int32_t *tok_list, const int32_t *tok_n, int32_t t_cap,
+                             float sm_scale, float *out, float *logits, float *ml,
+                             void *ws, size_t ws_bytes, ckv_stream_t stream);
+
+/* Edges, assignment and update (Figure 1 panel (3): "use the resulting top-kappa
+ * keys to update the new token's edges and assign it to a community in
+ * constant time"; Table 1: per-step update O(d)).  For every graph: the kappa
+ * non-sink attended tokens of largest weight (per head: the head's attention
+ * probability; query group: the sum of its heads' probabilities), ties to the
+ * lower position, become edges[G][kappa] (-1 padded); the new token goes to the
+ * community holding most edges, ties to the lowest id (top[g] if there is no
+ * edge): assign[G].  Then, at P = seq_len[b]: label[P] = a, P joins a's tail,
+ * size[a] += 1, csum[a] += k_new, cent[a] = float32(csum[a] / size[a]); k_new,
+ * v_new ([batch][n_kv_heads][head_dim] of kv->dtype) are stored at P, and
+ * finally seq_len[b] += 1. */
+ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
+                             const int32_t *tok_n, const float *logits, const float *ml,
+                             int32_t t_cap, const int32_t *top, int32_t kappa,
+                             const void *k_new, const void *v_new, int32_t *edges,
+                             int32_t *assign, void *ws, size_t ws_bytes, ckv_stream_t stream);
+
+/* Dense flash-decode baseline: softmax attention of every query head over all
+ * seq_len[b] cached tokens of its kv head.  out[batch][n_q_heads][head_dim]. */
+ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out,
+                            void *ws, size_t ws_bytes, ckv_stream_t stream);
+
+/* Static description of a status code. */
+const char *ckv_status_str(ckv_status s);
+
+/* Library ABI version (bumped when a signature or layout changes). */
+int32_t ckv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CKV_H */

@@ -344,13 +344,18 @@ class Oracle:
         for gid in self.graph_ids:
             st = self.g[gid]
             self.apply_update(gid, res[gid].assign, k_new[st.b][st.kh])
+        self.append(k_new, v_new)
+        return res
+
+    def append(self, k_new, v_new):
+        """Store the new token's key and value at position P of every tracked
+        sequence and advance the cached length (after every graph's update)."""
         for (b, kh) in self.K:
             P = self.len[b]
             self.K[(b, kh)][P] = np.asarray(k_new[b][kh], dtype=np.float32)
             self.V[(b, kh)][P] = np.asarray(v_new[b][kh], dtype=np.float32)
         for b in {b for (b, _) in self.K}:
             self.len[b] += 1
-        return res
 
     def dense(self, q, b: int, kh: int) -> np.ndarray:
         """Dense attention of kv head kh's query heads over all cached tokens of sequence b."""

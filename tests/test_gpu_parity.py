@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Sizes span several kernel tiles (score tiles of 256 communities, gather
+blocks of 128 tokens, select blocks of 1024 threads) with ragged tails, plus
+the edge cases of the method: budget 0 (sinks only), a budget that takes
+every community (equals dense attention), fewer candidates than kappa, a
+community cap, empty communities, a full tail, page sizes 1..64, fp32 and
+bf16 storage at d = 64 and 128, one and several query heads per graph.
+"""
+import numpy as np
+import pytest
+import torch
+
+from community_kv_retrieval_amd import ckv, runner, synth
+from tests import parity as PY
+
+pytestmark = pytest.mark.gpu
+
+
+def small_per_head(**kw):
+    base = dict(name="small_per_head", n_ctx=9000, budget=600, steps=6)
+    base.update(kw)
+    return synth.preset("qwen3_8b_32k").replace(**base)
+
+
+def small_group(**kw):
+    base = dict(name="small_group", batch=3, n_ctx=7000, min_ctx=2500, budget=700, steps=6)
+    base.update(kw)
+    return synth.preset("llama31_8b_128k_group_b8").replace(**base)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_tiny_workload_16_steps(seed):
+    w = synth.preset("tiny")
+    PY.log(f"tiny seed={seed}")
+    st = PY.run_steps(w, seed, w.steps, check_dense=True)
+    PY.log(f"  near-tie selections {st.near_sel}, edges {st.near_edges}, max abs {st.max_abs:.2e}")
+    assert st.steps == 16
+
+
+def test_small_per_head():
+    w = small_per_head()
+    PY.log("small per-head")
+    st = PY.run_steps(w, 3, w.steps)
+    PY.log(f"  graphs {st.graphs} near {st.near_sel}/{st.near_edges} max abs {st.max_abs:.2e}")
+
+
+def test_small_group_mixed_lengths():
+    w = small_group()
+    PY.log("small group, mixed lengths")
+    st = PY.run_steps(w, 4, w.steps)
+    PY.log(f"  graphs {st.graphs} near {st.near_sel}/{st.near_edges} max abs {st.max_abs:.2e}")
+
+
+@pytest.mark.parametrize("mode", [synth.PER_HEAD, synth.GROUP])
+def test_budget_takes_everything_equals_dense(mode):
+    w = small_per_head(mode=mode, n_ctx=3000, budget=1 << 20, steps=3)
+    PY.log(f"full budget {mode}")
+    st = PY.run_steps(w, 5, w.steps, check_dense=True)
+    assert st.dense_equal == st.graphs
+
+
+@pytest.mark.parametrize("mode", [synth.PER_HEAD, synth.GROUP])
+def test_budget_zero_sinks_only(mode):
+    w = small_per_head(mode=mode, n_ctx=2000, budget=0, steps=3)
+    PY.log(f"budget 0 {mode}")
+    PY.run_steps(w, 6, w.steps)
+
+
+def test_fewer_candidates_than_kappa():
+    w = small_per_head(n_ctx=2000, budget=12, kappa=32, steps=3)
+    PY.log("budget 12, kappa 32")
+    PY.run_steps(w, 7, w.steps)
+
+
+def test_community_cap():
+    w = small_per_head(n_ctx=3000, budget=1 << 20, max_comm=5, steps=3)
+    PY.log("max_comm 5")
+    PY.run_steps(w, 8, w.steps)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 64), ("f32", 64)])
+def test_dtypes_and_head_dims(dtype, d):
+    w = small_group(dtype=dtype, head_dim=d, key_scale=1.0 / np.sqrt(d), batch=2, n_ctx=3000, min_ctx=0, steps=3)
+    PY.log(f"{dtype} d={d}")
+    PY.run_steps(w, 9, w.steps)
+
+
+@pytest.mark.parametrize("page_size", [1, 64])
+def test_page_sizes(page_size):
+    w = small_per_head(n_ctx=2500, steps=3)
+    PY.log(f"page size {page_size}")
+    PY.run_steps(w, 10, w.steps, layer_kw=dict(page_size=page_size))
+
+
+def test_group_of_two_and_eight():
+    for hq, hkv in ((16, 8), (32, 4)):
+        w = small_group(n_q_heads=hq, n_kv_heads=hkv, batch=2, n_ctx=3000, min_ctx=0, steps=2)
+        PY.log(f"group {hq // hkv}")
+        PY.run_steps(w, 11, w.steps)
+
+
+def test_empty_communities_never_selected():
+    w = small_per_head(n_ctx=3000, n_kv_heads=2, n_q_heads=8, steps=3)
+    sl = synth.gen_layer(w, 12)
+    for row in sl:
+        for s in row:  # spread ids over twice the range: every odd id is empty
+            lab = s.part.labels
+            lab[lab >= 0] *= 2
+            s.part.n_comm = 2 * s.part.n_comm
+            s.part.centers = np.repeat(s.part.centers, 2, axis=0)
+    PY.log("empty communities")
+    layer, orc = PY.make_pair(w, 12, 3, slices=sl)
+    PY.run_steps(w, 12, 3, pair=(layer, orc))
+    sel = layer.dec.buf.sel.cpu().numpy()
+    for g in range(w.n_graphs):
+        assert (sel[g, :layer.dec.buf.sel_n[g].item()] % 2 == 0).all()
+
+
+def test_tail_full_sets_status():
+    w = small_per_head(n_ctx=2000, n_kv_heads=1, n_q_heads=4, steps=3)
+    PY.log("tail full")
+    layer = runner.load_layer(w, 13, extra=4, tail_cap=1)
+    dec = layer.dec
+    for t in range(2):
+        inp = synth.gen_step(w, 13, t, layer.slices)
+        dec.step(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda())
+    torch.cuda.synchronize()
+    assert int(layer.idx.status.item()) & ckv.CKV_ST_TAIL_FULL
+    assert (layer.idx.tail_len.cpu().numpy() == 1).all()
+    assert layer.kv.seq_len.item() == 2002
+    lab = layer.idx.label.cpu().numpy()
+    assert (lab[:, 2000] >= 0).all() and (lab[:, 2001] == -1).all()
+
+
+def test_bad_label_sets_status():
+    w = small_per_head(n_ctx=1000, n_kv_heads=1, n_q_heads=4, steps=1)
+    sl = synth.gen_layer(w, 14)
+    sl[0][0].part.labels[10] = sl[0][0].part.n_comm + 3
+    PY.log("bad label")
+    layer = runner.load_layer(w, 14, extra=2, slices=sl)
+    torch.cuda.synchronize()
+    assert int(layer.idx.status.item()) & ckv.CKV_ST_BAD_LABEL
+    assert (layer.idx.label[:, 10].cpu().numpy() == -1).all()
+
+
+def test_deterministic_rerun():
+    w = small_group(batch=2, n_ctx=4000, min_ctx=0, steps=4)
+    outs = []
+    for rep in range(2):
+        PY.log(f"determinism rep {rep}")
+        layer = runner.load_layer(w, 15, extra=5)
+        rec = []
+        for t in range(4):
+            inp = synth.gen_step(w, 15, t, layer.slices)
+            layer.dec.step(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda())
+            b = layer.dec.buf
+            n = b.tok_n.cpu()
+            valid = [b.logits[g, :, :n[g]].cpu().clone() for g in range(n.numel())]
+            valid += [b.tok_list[g, :n[g]].cpu().clone() for g in range(n.numel())]
+            rec.append([x.cpu().clone() for x in (b.out, b.ml, b.edges, b.assign, b.tok_n)] + valid)
+        rec.append([layer.idx.cent.cpu().clone(), layer.idx.csum.cpu().clone()])
+        outs.append(rec)
+    for a, b in zip(outs[0], outs[1]):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
+def test_checkpoint_resume_bit_identical():
+    w = small_per_head(n_ctx=3000, n_kv_heads=2, n_q_heads=8, steps=6)
+    PY.log("checkpoint/resume")
+    ref = runner.load_layer(w, 16, extra=7)
+    for t in range(6):
+        inp = synth.gen_step(w, 16, t, ref.slices)
+        ref.dec.step(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda())
+    run = runner.load_layer(w, 16, extra=7)
+    for t in range(3):
+        inp = synth.gen_step(w, 16, t, run.slices)
+        run.dec.step(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda())
+    saved = (run.idx.state_dict(), run.kv.kv.clone(), run.kv.seq_len.clone())
+    res = runner.load_layer(w, 16, extra=7)
+    res.idx.load_state_dict(saved[0])
+    res.kv.kv.copy_(saved[1])
+    res.kv.seq_len.copy_(saved[2])
+    for t in range(3, 6):
+        inp = synth.gen_step(w, 16, t, res.slices)
+        res.dec.step(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(ref.dec.buf.out, res.dec.buf.out)
+    for k in ckv.CommunityIndex.STATE:
+        assert torch.equal(getattr(ref.idx, k), getattr(res.idx, k)), k
+
+
+def test_dense_baseline_matches_oracle():
+    w = synth.preset("qwen3_8b_32k").replace(n_ctx=20000, batch=2, min_ctx=9000)
+    PY.log("dense baseline")
+    layer, orc = PY.make_pair(w, 17, 1)
+    inp = synth.gen_step(w, 17, 0, layer.slices)
+    out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    layer.dec.dense(inp.q.cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(w.batch):
+        for kh in range(w.n_kv_heads):
+            ref = orc.dense(inp.q.float().numpy(), b, kh)
+            g = got[b, kh * 4:(kh + 1) * 4]
+            assert np.all(np.abs(g - ref) <= PY.ATOL + PY.RTOL * np.abs(ref))
