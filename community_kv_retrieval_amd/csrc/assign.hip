@@ -54,10 +54,9 @@ template <typename T, int D, int NH>
 __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     __shared__ float s_rw[4];
     __shared__ int s_rp[4];
-    __shared__ float s_ww;
-    __shared__ int s_wp;
     __shared__ int s_edges[CKV_MAX_KAPPA];
-    __shared__ int s_ne, s_a, s_newsize, s_last;
+    __shared__ int s_elab[CKV_MAX_KAPPA];
+    __shared__ int s_a, s_newsize;
 
     const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
@@ -83,19 +82,62 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         }
     };
 
+    // Candidate weights, computed once.  Up to kIpt per thread stay in
+    // registers; longer token lists re-read them from memory every round.
+    constexpr int kIpt = 24;
+    float cw[kIpt];
+    int cp[kIpt];
+    const bool inreg = n <= kIpt * 256;
+    {
+        // issue every load first, then compute the weights
+        float z[kIpt][NH];
+#pragma unroll
+        for (int i = 0; i < kIpt; ++i) {
+            const int j = tid + i * 256;
+            const bool ok = inreg && j < n;
+            cp[i] = ok ? tl[j] : 0x7fffffff;
+#pragma unroll
+            for (int h = 0; h < NH; ++h) z[i][h] = ok ? p.logits[((size_t)g * NH + h) * p.t_cap + j] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kIpt; ++i) {
+            if (cp[i] == 0x7fffffff || cp[i] < p.n_sinks) {
+                cp[i] = 0x7fffffff;
+                cw[i] = kNegInf;
+            } else if constexpr (NH == 1) {
+                cw[i] = z[i][0];
+            } else {
+                float w = 0.f;
+#pragma unroll
+                for (int h = 0; h < NH; ++h) w += exp2f((z[i][h] - M[h]) * kLog2e) * Linv[h];
+                cw[i] = w;
+            }
+        }
+    }
+
     float pw = __builtin_huge_valf();
     int pp = -1;
     int ne = 0;
     for (int r = 0; r < p.kappa; ++r) {
         float bw = kNegInf;
         int bp = 0x7fffffff;
-        for (int j = tid; j < n; j += 256) {
-            const int pos = tl[j];
-            if (pos < p.n_sinks) continue;
-            const float w = weight(j);
-            if (better(pw, pp, w, pos) && better(w, pos, bw, bp)) {
-                bw = w;
-                bp = pos;
+        if (inreg) {
+#pragma unroll
+            for (int i = 0; i < kIpt; ++i) {
+                if (cp[i] != 0x7fffffff && better(pw, pp, cw[i], cp[i]) && better(cw[i], cp[i], bw, bp)) {
+                    bw = cw[i];
+                    bp = cp[i];
+                }
+            }
+        } else {
+            for (int j = tid; j < n; j += 256) {
+                const int pos = tl[j];
+                if (pos < p.n_sinks) continue;
+                const float w = weight(j);
+                if (better(pw, pp, w, pos) && better(w, pos, bw, bp)) {
+                    bw = w;
+                    bp = pos;
+                }
             }
         }
 #pragma unroll
@@ -112,20 +154,18 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
             s_rp[wave] = bp;
         }
         __syncthreads();
-        if (tid == 0) {
+        {
             float w = s_rw[0];
             int q = s_rp[0];
+#pragma unroll
             for (int i = 1; i < 4; ++i)
                 if (better(s_rw[i], s_rp[i], w, q)) {
                     w = s_rw[i];
                     q = s_rp[i];
                 }
-            s_ww = w;
-            s_wp = q;
+            pw = w;
+            pp = q;
         }
-        __syncthreads();
-        pw = s_ww;
-        pp = s_wp;
         __syncthreads();
         if (pp == 0x7fffffff) break;
         if (tid == 0) s_edges[r] = pp;
@@ -134,13 +174,17 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
 
     const int cap = min(p.l_cap, p.max_pages << p.ps_log2);
     const bool room = P < cap;
+    __syncthreads();  // s_edges complete
+    if (tid < ne) s_elab[tid] = p.label[(size_t)g * p.l_cap + s_edges[tid]];
+    const int tn = p.tail_len[g];
+    __syncthreads();
     if (tid == 0) {
         int best = -1, bestc = 0;
         for (int r = 0; r < ne; ++r) {
-            const int c = p.label[(size_t)g * p.l_cap + s_edges[r]];
+            const int c = s_elab[r];
             if (c < 0) continue;
             int k = 0;
-            for (int r2 = 0; r2 < ne; ++r2) k += (p.label[(size_t)g * p.l_cap + s_edges[r2]] == c);
+            for (int r2 = 0; r2 < ne; ++r2) k += (s_elab[r2] == c);
             if (k > bestc || (k == bestc && c < best)) {
                 best = c;
                 bestc = k;
@@ -153,7 +197,6 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         if (!room) {
             atomicOr(p.status, CKV_ST_CAPACITY);
         } else if (a >= 0) {
-            const int tn = p.tail_len[g];
             if (tn < p.tail_cap) {
                 p.label[(size_t)g * p.l_cap + P] = a;
                 p.tail_pos[(size_t)g * p.tail_cap + tn] = P;
@@ -191,16 +234,14 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         for (int i = tid; i < 2 * D; i += 256) row[i] = i < D ? kn[i] : vn[i - D];
     }
 
-    // The last block advances every sequence with room by one token.
-    __threadfence();
+    // The last block advances every sequence with room by one token.  Every
+    // block read seq_len before it counts itself in, so the increment cannot
+    // race a read; the next kernel sees it across the kernel boundary.
     __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(p.ctr, 1) == p.G - 1);
-    __syncthreads();
-    if (s_last && tid == 0) {
-        __threadfence();
+    if (tid == 0 && arrive_last(p.ctr, p.G)) {
         for (int bb = 0; bb < p.B; ++bb)
             if (p.seq_len[bb] < cap) p.seq_len[bb] += 1;
-        *p.ctr = 0;
+        reset_counter(p.ctr);
     }
 }
 

@@ -15,7 +15,8 @@
 // partials, so the whole split-K attention is one launch.  Blocks of one unit
 // run on different XCDs, whose L2 caches are not coherent with each other:
 // partial records are padded to whole cache lines and written and read with
-// device-scope accesses, fenced on both sides of the counter.
+// device-scope accesses, and each block waits for its stores before it counts
+// itself in.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -45,6 +46,114 @@ constexpr int pick_u() {
     return (NH >= 8 || RowSlice<T, D>::BYTES == 32) ? 4 : 8;
 }
 
+// Block-wide reduction of NH values per thread (max or sum) over 256 threads;
+// every thread gets the results.  red: [4][NH] shared floats.
+template <int NH, bool MAX>
+__device__ __forceinline__ void block_reduce_nh(float (&v)[NH], float (*red)[NH]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float y = __shfl_xor(v[h], o, 64);
+            v[h] = MAX ? fmaxf(v[h], y) : v[h] + y;
+        }
+        if (lane == 0) red[wave][h] = v[h];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        float r = red[0][h];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) r = MAX ? fmaxf(r, red[w][h]) : r + red[w][h];
+        v[h] = r;
+    }
+    __syncthreads();
+}
+
+// Merge the nact partial records (accumulator[D], max, sum) of every head into
+// the final output.  Loads are batched so that many are in flight at once.
+template <int D, int NH, int PS>
+__device__ __forceinline__ void merge_partials(const float *P, int nchunk, int nact, float (*s_scale)[256],
+                                               float (*s_red)[NH], float *out, float *ml) {
+    const int tid = threadIdx.x;
+    float M[NH], L[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) M[h] = kNegInf;
+    for (int c = tid; c < nact; c += 256) {
+        float m[NH];
+#pragma unroll
+        for (int h = 0; h < NH; ++h) m[h] = ld_dev(P + ((size_t)h * nchunk + c) * PS + D);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) M[h] = fmaxf(M[h], m[h]);
+    }
+    block_reduce_nh<NH, true>(M, s_red);
+
+    constexpr int NP = (NH * D + 255) / 256;  // (head, dim) pairs per thread
+    float o[NP];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) L[h] = 0.f;
+    constexpr int B = 16;
+    for (int c0 = 0; c0 < nact; c0 += 256) {
+        const int tn = min(256, nact - c0);
+        if (tid < tn) {
+            float m[NH], l[NH];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                m[h] = ld_dev(P + ((size_t)h * nchunk + c0 + tid) * PS + D);
+                l[h] = ld_dev(P + ((size_t)h * nchunk + c0 + tid) * PS + D + 1);
+            }
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const float sc = (m[h] == kNegInf) ? 0.f : exp2f((m[h] - M[h]) * kLog2e);
+                s_scale[h][tid] = sc;
+                L[h] += l[h] * sc;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int pi = tid + i * 256;
+            if (pi < NH * D) {
+                const int h = pi / D, d = pi - (pi / D) * D;
+                const float *src = P + ((size_t)h * nchunk + c0) * PS + d;
+                for (int j0 = 0; j0 < tn; j0 += B) {
+                    float v[B];
+#pragma unroll
+                    for (int j = 0; j < B; ++j) v[j] = (j0 + j < tn) ? ld_dev(src + (size_t)(j0 + j) * PS) : 0.f;
+#pragma unroll
+                    for (int j = 0; j < B; ++j)
+                        if (j0 + j < tn) o[i] = fmaf(v[j], s_scale[h][j0 + j], o[i]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    block_reduce_nh<NH, false>(L, s_red);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        const int pi = tid + i * 256;
+        if (pi < NH * D) {
+            const int h = pi / D;
+            float Lh = L[0];
+#pragma unroll
+            for (int hh = 1; hh < NH; ++hh)
+                if (h == hh) Lh = L[hh];
+            out[pi] = o[i] / Lh;
+        }
+    }
+    if (ml) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            if (tid == h) {
+                ml[h * 2] = M[h];
+                ml[h * 2 + 1] = L[h];
+            }
+    }
+}
+
 template <typename T, int D, int NH, int U, bool DENSE>
 __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     using RS = RowSlice<T, D>;
@@ -58,6 +167,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     __shared__ float s_q[NH][D];
     __shared__ float s_wm[4][NH], s_wl[4][NH];
     __shared__ float s_wacc[4][NH][D];
+    __shared__ float s_scale[NH][256];
+    __shared__ float s_red[4][NH];
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,43 +346,25 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
             }
         } else {
             float *dst = P + ((size_t)h * a.nchunk + chunk) * PS;
-            __hip_atomic_store(dst + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            st_dev(dst + d, o);
             if (d == 0) {
-                __hip_atomic_store(dst + D, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(dst + D + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                st_dev(dst + D, M);
+                st_dev(dst + D + 1, L);
             }
         }
     }
     if (nact == 1) return;
 
     // The last block of the unit merges every block's partial.
-    __threadfence();
+    stores_done();
     __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&a.ctr[unit], 1) == nact - 1);
+    if (tid == 0) s_last = arrive_last(&a.ctr[unit], nact);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    for (int i = tid; i < NH * D; i += 256) {
-        const int h = i / D, d = i - (i / D) * D;
-        float *src = P + (size_t)h * a.nchunk * PS;
-        float M = kNegInf;
-        for (int c = 0; c < nact; ++c)
-            M = fmaxf(M, __hip_atomic_load(src + (size_t)c * PS + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        float L = 0.f, O = 0.f;
-        for (int c = 0; c < nact; ++c) {
-            float *pc = src + (size_t)c * PS;
-            const float mc = __hip_atomic_load(pc + D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float s = (mc == kNegInf) ? 0.f : exp2f((mc - M) * kLog2e);
-            L += __hip_atomic_load(pc + D + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * s;
-            O += __hip_atomic_load(pc + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) * s;
-        }
-        a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = O / L;
-        if (!DENSE && d == 0) {
-            a.ml[((size_t)unit * NH + h) * 2] = M;
-            a.ml[((size_t)unit * NH + h) * 2 + 1] = L;
-        }
-    }
-    if (tid == 0) a.ctr[unit] = 0;
+    merge_partials<D, NH, PS>(P, a.nchunk, nact, s_scale, s_red,
+                              a.out + ((size_t)b * a.Hq + qh0) * D,
+                              DENSE ? nullptr : a.ml + (size_t)unit * NH * 2);
+    if (tid == 0) reset_counter(&a.ctr[unit]);
 }
 
 template <typename T, int D, int NH, bool DENSE>

@@ -90,6 +90,32 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Cross-block hand-off inside one kernel.  Blocks of one kernel run on
+// different XCDs whose L2 caches are not coherent with each other.  Data meant
+// for another block is written and read with device-scope accesses (sc1), which
+// go to the device-coherent level.  Before a block announces its data on a
+// counter, it waits until its own stores are acknowledged; that is a release
+// for sc1 stores without __threadfence()'s write-back and invalidation of the
+// whole L2 (which, issued by every block, serialises on the cache).
+__device__ __forceinline__ void st_dev(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stores_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every prior load and store acknowledged
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Bump a device-scope counter; true for the block that completes `total`.
+__device__ __forceinline__ bool arrive_last(int32_t *ctr, int total) {
+    return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;
+}
+__device__ __forceinline__ void reset_counter(int32_t *ctr) {
+    __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Merge two partial softmax states (max m, sum l, unnormalised accumulator).
 __device__ __forceinline__ void softmax_scales(float m1, float m2, float &M, float &s1, float &s2) {
     M = fmaxf(m1, m2);

@@ -41,7 +41,14 @@ struct SelectParams {
     int32_t *tok_n;
 };
 
+// Taken communities whose copy runs block-wide out of LDS (more fall back to
+// one thread per community).
+constexpr int kSelLds = 4096;
+
 struct SelShared {
+    int sid[kSelLds];      // taken community
+    int soff[kSelLds];     // its first base member in toks
+    int spref[kSelLds + 1];  // its first slot in the token list (after the sinks)
     uint32_t hw[256];  // token weight per digit
     uint32_t hn[256];  // candidates per digit
     uint32_t bits[CKV_MAX_C_CAP / 32];
@@ -217,14 +224,49 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     int dst = ns + block_exclusive_scan<kSelThreads>(tokloc, sh.scan, &ntok);
     __syncthreads();
     const int32_t *toks = p.toks + (size_t)g * p.l_cap;
+    const bool staged = nsel <= kSelLds;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         if (key[j] > thr) {
             const int c = tid * EPT + j;
-            p.sel[(size_t)g * C + kpos++] = c;
+            p.sel[(size_t)g * C + kpos] = c;
             atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
             const int o = offs[c], e = offs[c + 1];
-            for (int i = o; i < e; ++i) tl[dst++] = toks[i];
+            if (staged) {
+                sh.sid[kpos] = c;
+                sh.soff[kpos] = o;
+                sh.spref[kpos] = dst - ns;
+            } else {
+                for (int i = o; i < e; ++i) tl[dst + i - o] = toks[i];
+            }
+            dst += e - o;
+            ++kpos;
+        }
+    }
+    if (staged) {
+        if (tid == 0) sh.spref[nsel] = ntok;
+        __syncthreads();
+        // slot j of the member part belongs to the last taken community whose
+        // first slot is <= j
+        for (int j0 = 0; j0 < ntok; j0 += 4 * kSelThreads) {
+            int v[4], at[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * kSelThreads + tid;
+                at[u] = j;
+                if (j < ntok) {
+                    int lo = 0, hi = nsel - 1;
+                    while (lo < hi) {
+                        const int mid = (lo + hi + 1) >> 1;
+                        if (sh.spref[mid] <= j) lo = mid;
+                        else hi = mid - 1;
+                    }
+                    v[u] = toks[sh.soff[lo] + (j - sh.spref[lo])];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (at[u] < ntok) tl[ns + at[u]] = v[u];
         }
     }
     for (int i = tid; i < ns; i += kSelThreads) tl[i] = i;
