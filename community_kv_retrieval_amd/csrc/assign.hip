@@ -6,10 +6,11 @@
 // One 256-thread block per graph.  The edge weight of an attended non-sink
 // token is its softmax probability (one head) or the sum of its heads'
 // probabilities (query group).  With one head the logit orders the tokens the
-// same way, so the logit itself is compared.  The kappa best tokens (larger
-// weight first, lower position on ties) are extracted one per round: each
-// round every thread proposes its best token ranked strictly below the
-// previous winner and a block reduction picks the best proposal.  Thread 0
+// same way, so the logit itself is compared.  Each candidate becomes a 64-bit
+// key (weight bits, then inverted position) so that one unsigned compare
+// ranks it.  The kappa best keys are found without sorting all of them: a
+// lower bound taken from the per-lane maxima leaves a few dozen candidates,
+// which one wave orders exactly with repeated DPP max reductions.  Thread 0
 // takes the majority label of the edges (lowest id on ties), then the block
 // appends the token to that community: label, tail entry, member count, the
 // exact float64 key sum and the float32 centroid column.  Graphs that own the
@@ -46,14 +47,17 @@ struct AssignParams {
     int32_t *ctr;
 };
 
-__device__ __forceinline__ bool better(float w1, int p1, float w2, int p2) {
-    return w1 > w2 || (w1 == w2 && p1 < p2);
+// Edge candidate key: larger weight first, then lower position (0 = none).
+__device__ __forceinline__ unsigned long long edge_key(float w, int pos) {
+    if (w == 0.f) w = 0.f;  // one key for +0 and -0
+    return ((unsigned long long)ordered_bits(w) << 32) | (0xFFFFFFFFu - (uint32_t)pos);
 }
 
 template <typename T, int D, int NH>
 __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
-    __shared__ float s_rw[4];
-    __shared__ int s_rp[4];
+    __shared__ unsigned long long s_tau[4];
+    __shared__ unsigned long long s_cand[64];
+    __shared__ int s_ncand, s_ne;
     __shared__ int s_edges[CKV_MAX_KAPPA];
     __shared__ int s_elab[CKV_MAX_KAPPA];
     __shared__ int s_a, s_newsize;
@@ -82,99 +86,107 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         }
     };
 
-    // Candidate weights, computed once.  Up to kIpt per thread stay in
-    // registers; longer token lists re-read them from memory every round.
+    // Candidates as 64-bit keys, (order-preserving bits of the weight) << 32 |
+    // ~position, so the larger key is the better edge (larger weight, then
+    // lower position).  Up to kIpt per thread stay in registers.
     constexpr int kIpt = 24;
-    float cw[kIpt];
-    int cp[kIpt];
+    unsigned long long ck[kIpt];
     const bool inreg = n <= kIpt * 256;
     {
-        // issue every load first, then compute the weights
+        int cp[kIpt];
         float z[kIpt][NH];
 #pragma unroll
-        for (int i = 0; i < kIpt; ++i) {
+        for (int i = 0; i < kIpt; ++i) {  // issue every load first
             const int j = tid + i * 256;
             const bool ok = inreg && j < n;
-            cp[i] = ok ? tl[j] : 0x7fffffff;
+            cp[i] = ok ? tl[j] : -1;
 #pragma unroll
             for (int h = 0; h < NH; ++h) z[i][h] = ok ? p.logits[((size_t)g * NH + h) * p.t_cap + j] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < kIpt; ++i) {
-            if (cp[i] == 0x7fffffff || cp[i] < p.n_sinks) {
-                cp[i] = 0x7fffffff;
-                cw[i] = kNegInf;
-            } else if constexpr (NH == 1) {
-                cw[i] = z[i][0];
+            float w;
+            if constexpr (NH == 1) {
+                w = z[i][0];
             } else {
-                float w = 0.f;
+                w = 0.f;
 #pragma unroll
                 for (int h = 0; h < NH; ++h) w += exp2f((z[i][h] - M[h]) * kLog2e) * Linv[h];
-                cw[i] = w;
             }
+            ck[i] = cp[i] >= p.n_sinks ? edge_key(w, cp[i]) : 0ull;
         }
     }
 
-    float pw = __builtin_huge_valf();
-    int pp = -1;
-    int ne = 0;
-    for (int r = 0; r < p.kappa; ++r) {
-        float bw = kNegInf;
-        int bp = 0x7fffffff;
-        if (inreg) {
+    // Lower bound on the kappa-th best key: in each wave, the kappa-th largest
+    // of the per-lane maxima (kappa keys of the wave reach it); the largest such
+    // bound of the four waves still has kappa keys at or above it.
+    const int kappa = p.kappa;
+    unsigned long long tau = 0ull;
+    if (inreg) {
+        unsigned long long lm = 0ull;
+#pragma unroll
+        for (int i = 0; i < kIpt; ++i) lm = umax64(lm, ck[i]);
+        unsigned long long tw = 0ull;
+        int got = 0;
+        for (int r = 0; r < kappa; ++r) {
+            const unsigned long long m = wave_max_u64(lm);
+            if (m == 0ull) break;
+            if (lm == m) lm = 0ull;
+            tw = m;
+            ++got;
+        }
+        if (lane == 0) s_tau[wave] = got == kappa ? tw : 0ull;
+        if (tid == 0) s_ncand = 0;
+        __syncthreads();
+        tau = umax64(umax64(s_tau[0], s_tau[1]), umax64(s_tau[2], s_tau[3]));
+        if (tau != 0ull) {
 #pragma unroll
             for (int i = 0; i < kIpt; ++i) {
-                if (cp[i] != 0x7fffffff && better(pw, pp, cw[i], cp[i]) && better(cw[i], cp[i], bw, bp)) {
-                    bw = cw[i];
-                    bp = cp[i];
+                if (ck[i] >= tau) {
+                    const int k = atomicAdd(&s_ncand, 1);
+                    if (k < 64) s_cand[k] = ck[i];
                 }
             }
-        } else {
-            for (int j = tid; j < n; j += 256) {
+        }
+        __syncthreads();
+    }
+    const bool fast = inreg && tau != 0ull && s_ncand <= 64;  // uniform
+
+    int ne = 0;
+    if (fast) {
+        if (wave == 0) {  // exact order among the few candidates, one per lane
+            unsigned long long c = lane < s_ncand ? s_cand[lane] : 0ull;
+            for (int r = 0; r < kappa; ++r) {
+                const unsigned long long m = wave_max_u64(c);
+                if (m == 0ull) break;
+                if (c == m) c = 0ull;
+                if (lane == 0) s_edges[r] = (int)(0xFFFFFFFFu - (uint32_t)m);
+                ++ne;
+            }
+        }
+    } else if (wave == 0) {  // long token lists or degenerate weights: rounds over all tokens
+        unsigned long long prev = ~0ull;
+        for (int r = 0; r < kappa; ++r) {
+            unsigned long long best = 0ull;
+            for (int j = lane; j < n; j += 64) {
                 const int pos = tl[j];
                 if (pos < p.n_sinks) continue;
-                const float w = weight(j);
-                if (better(pw, pp, w, pos) && better(w, pos, bw, bp)) {
-                    bw = w;
-                    bp = pos;
-                }
+                const unsigned long long k = edge_key(weight(j), pos);
+                if (k < prev && k > best) best = k;
             }
+            best = wave_max_u64(best);
+            if (best == 0ull) break;
+            if (lane == 0) s_edges[r] = (int)(0xFFFFFFFFu - (uint32_t)best);
+            prev = best;
+            ++ne;
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ow = __shfl_xor(bw, o, 64);
-            const int op = __shfl_xor(bp, o, 64);
-            if (better(ow, op, bw, bp)) {
-                bw = ow;
-                bp = op;
-            }
-        }
-        if (lane == 0) {
-            s_rw[wave] = bw;
-            s_rp[wave] = bp;
-        }
-        __syncthreads();
-        {
-            float w = s_rw[0];
-            int q = s_rp[0];
-#pragma unroll
-            for (int i = 1; i < 4; ++i)
-                if (better(s_rw[i], s_rp[i], w, q)) {
-                    w = s_rw[i];
-                    q = s_rp[i];
-                }
-            pw = w;
-            pp = q;
-        }
-        __syncthreads();
-        if (pp == 0x7fffffff) break;
-        if (tid == 0) s_edges[r] = pp;
-        ++ne;
     }
+    if (wave == 0 && lane == 0) s_ne = ne;
+    __syncthreads();
+    ne = s_ne;
 
     const int cap = min(p.l_cap, p.max_pages << p.ps_log2);
     const bool room = P < cap;
-    __syncthreads();  // s_edges complete
     if (tid < ne) s_elab[tid] = p.label[(size_t)g * p.l_cap + s_edges[tid]];
     const int tn = p.tail_len[g];
     __syncthreads();

@@ -90,6 +90,43 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// Wave-wide max of a 64-bit key, in every lane: the DPP butterfly inside each
+// row of 16 lanes, then the four row results read out with readlane.  Call with
+// all 64 lanes active.
+template <int CTRL> __device__ __forceinline__ unsigned long long dpp_u64(unsigned long long x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, true);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
+    return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long umin64(unsigned long long a, unsigned long long b) {
+    return a < b ? a : b;
+}
+__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long x, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+    return ((unsigned long long)hi << 32) | lo;
+}
+template <bool MAX>
+__device__ __forceinline__ unsigned long long wave_ext_u64(unsigned long long x) {
+    auto pick = [](unsigned long long a, unsigned long long b) { return MAX ? umax64(a, b) : umin64(a, b); };
+    x = pick(x, dpp_u64<kQuadSwap1>(x));
+    x = pick(x, dpp_u64<kQuadSwap2>(x));
+    x = pick(x, dpp_u64<kRowHalfMirror>(x));
+    x = pick(x, dpp_u64<kRowMirror>(x));
+    return pick(pick(readlane_u64(x, 0), readlane_u64(x, 16)), pick(readlane_u64(x, 32), readlane_u64(x, 48)));
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) { return wave_ext_u64<true>(x); }
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long x) { return wave_ext_u64<false>(x); }
+
+// Order-preserving map of a float32 onto uint32 (larger float, larger code).
+__device__ __forceinline__ uint32_t ordered_bits(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Cross-block hand-off inside one kernel.  Blocks of one kernel run on
 // different XCDs whose L2 caches are not coherent with each other.  Data meant
 // for another block is written and read with device-scope accesses (sc1), which
