@@ -58,6 +58,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_trace(verbose: bool = False) -> str:
+    """Profiling variant with per-phase time stamps (CKV_PHASE_TRACE), built as
+    one translation unit into _build/libckv_trace.so.  Not the product library."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    unity = os.path.join(BUILD, "ckv_trace_all.hip")
+    with open(unity, "w") as f:
+        for src in srcs:
+            f.write(f'#include "{src}"\n')
+    out = os.path.join(BUILD, "libckv_trace.so")
+    cmd = [HIPCC, *FLAGS, "-DCKV_PHASE_TRACE", "-shared", unity, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"trace build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {out}")
+    return out
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--trace" in sys.argv:
+        build_trace(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -154,7 +154,7 @@ class CommunityIndex:
         self.tail_cap, self.n_sinks = tail_cap, n_sinks
         self.n_comm = torch.tensor(list(n_comm), **i32)
         self.size = torch.zeros((G, c_cap), **i32)
-        self.offs = torch.zeros((G, c_cap + 1), **i32)
+        self.offs = torch.zeros((G, c_cap + 4), **i32)  # rows padded to 16 bytes
         self.toks = torch.zeros((G, l_cap), **i32)
         self.label = torch.full((G, l_cap), -1, **i32)
         self.tail_pos = torch.zeros((G, tail_cap), **i32)

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "ckv.h"
+#include "ckv_device.h"
 #include "ckv_internal.h"
 
 using namespace ckv;
@@ -55,7 +56,15 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 1; }
+int32_t ckv_abi_version(void) { return 2; }
+
+#ifdef CKV_PHASE_TRACE
+// Profiling builds only: copy the 64 phase stamps to host memory.
+int32_t ckv_trace_read(unsigned long long *host) {
+    return hipMemcpyFromSymbol(host, HIP_SYMBOL(ckv::g_phase_trace), sizeof(unsigned long long) * 64) ==
+                   hipSuccess ? 0 : -1;
+}
+#endif
 
 const char *ckv_status_str(ckv_status s) {
     switch (s) {

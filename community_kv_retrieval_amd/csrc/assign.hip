@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     __shared__ int s_a, s_newsize;
 
     const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    CKV_TMARK(30);
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
     const int P = p.seq_len[gc.b];
     const int n = p.tok_n[g];
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         }
     }
 
+    CKV_TMARK(31);
     // Lower bound on the kappa-th best key: in each wave, the kappa-th largest
     // of the per-lane maxima (kappa keys of the wave reach it); the largest such
     // bound of the four waves still has kappa keys at or above it.
@@ -150,6 +152,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         }
         __syncthreads();
     }
+    CKV_TMARK(32);
     const bool fast = inreg && tau != 0ull && s_ncand <= 64;  // uniform
 
     int ne = 0;
@@ -184,6 +187,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     if (wave == 0 && lane == 0) s_ne = ne;
     __syncthreads();
     ne = s_ne;
+    CKV_TMARK(33);
 
     const int cap = min(p.l_cap, p.max_pages << p.ps_log2);
     const bool room = P < cap;
@@ -228,6 +232,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     }
     __syncthreads();
 
+    CKV_TMARK(34);
     const T *kn = reinterpret_cast<const T *>(p.k_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
     const T *vn = reinterpret_cast<const T *>(p.v_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
     const int a = s_a;
@@ -246,6 +251,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         for (int i = tid; i < 2 * D; i += 256) row[i] = i < D ? kn[i] : vn[i - D];
     }
 
+    CKV_TMARK(35);
     // The last block advances every sequence with room by one token.  Every
     // block read seq_len before it counts itself in, so the increment cannot
     // race a read; the next kernel sees it across the kernel boundary.
@@ -255,6 +261,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
             if (p.seq_len[bb] < cap) p.seq_len[bb] += 1;
         reset_counter(p.ctr);
     }
+    CKV_TMARK(36);
 }
 
 hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,

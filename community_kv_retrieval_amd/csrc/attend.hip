@@ -73,10 +73,75 @@ __device__ __forceinline__ void block_reduce_nh(float (&v)[NH], float (*red)[NH]
 
 // Merge the nact partial records (accumulator[D], max, sum) of every head into
 // the final output.  Loads are batched so that many are in flight at once.
+// Up to kFastMerge partials: the max and sum of every partial go to LDS while
+// each thread's accumulator entries are loaded in passes of kMergePass, all in
+// the same round trip for the first pass.
+constexpr int kFastMerge = 64;
+constexpr int kMergePass = 32;
+
 template <int D, int NH, int PS>
 __device__ __forceinline__ void merge_partials(const float *P, int nchunk, int nact, float (*s_scale)[256],
                                                float (*s_red)[NH], float *out, float *ml) {
     const int tid = threadIdx.x;
+    constexpr int NP = (NH * D + 255) / 256;  // (head, dim) pairs per thread
+    if (nact <= kFastMerge) {
+        float(*s_m)[kFastMerge] = reinterpret_cast<float(*)[kFastMerge]>(&s_scale[0][0]);
+        float(*s_l)[kFastMerge] = reinterpret_cast<float(*)[kFastMerge]>(&s_scale[0][0] + NH * kFastMerge);
+        for (int i = tid; i < NH * nact; i += 256) {
+            const int h = i / nact, c = i - (i / nact) * nact;
+            s_m[h][c] = ld_dev(P + ((size_t)h * nchunk + c) * PS + D);
+            s_l[h][c] = ld_dev(P + ((size_t)h * nchunk + c) * PS + D + 1);
+        }
+        float o[NP][kMergePass];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int pi = tid + i * 256;
+            const int h = pi / D, d = pi - (pi / D) * D;
+#pragma unroll
+            for (int c = 0; c < kMergePass; ++c)
+                o[i][c] = (pi < NH * D && c < nact) ? ld_dev(P + ((size_t)h * nchunk + c) * PS + d) : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int pi = tid + i * 256;
+            if (pi >= NH * D) break;
+            const int h = pi / D, d = pi - (pi / D) * D;
+            float M = kNegInf;
+            for (int c = 0; c < nact; ++c) M = fmaxf(M, s_m[h][c]);
+            float L = 0.f, O = 0.f;
+#pragma unroll
+            for (int c = 0; c < kMergePass; ++c) {
+                if (c < nact) {
+                    const float mc = s_m[h][c];
+                    const float sc = (mc == kNegInf) ? 0.f : exp2f((mc - M) * kLog2e);
+                    L = fmaf(s_l[h][c], sc, L);
+                    O = fmaf(o[i][c], sc, O);
+                }
+            }
+            for (int c0 = kMergePass; c0 < nact; c0 += kMergePass) {
+                float v[kMergePass];
+#pragma unroll
+                for (int c = 0; c < kMergePass; ++c)
+                    v[c] = (c0 + c < nact) ? ld_dev(P + ((size_t)h * nchunk + c0 + c) * PS + d) : 0.f;
+#pragma unroll
+                for (int c = 0; c < kMergePass; ++c) {
+                    if (c0 + c < nact) {
+                        const float mc = s_m[h][c0 + c];
+                        const float sc = (mc == kNegInf) ? 0.f : exp2f((mc - M) * kLog2e);
+                        L = fmaf(s_l[h][c0 + c], sc, L);
+                        O = fmaf(v[c], sc, O);
+                    }
+                }
+            }
+            out[pi] = O / L;
+            if (ml && d == 0) {
+                ml[h * 2] = M;
+                ml[h * 2 + 1] = L;
+            }
+        }
+        return;
+    }
     float M[NH], L[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) M[h] = kNegInf;
@@ -89,7 +154,6 @@ __device__ __forceinline__ void merge_partials(const float *P, int nchunk, int n
     }
     block_reduce_nh<NH, true>(M, s_red);
 
-    constexpr int NP = (NH * D + 255) / 256;  // (head, dim) pairs per thread
     float o[NP];
 #pragma unroll
     for (int i = 0; i < NP; ++i) o[i] = 0.f;
@@ -175,6 +239,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     const int l16 = lane & 15, ts = lane >> 4;
     const int unit = blockIdx.x / a.nchunk;
     const int chunk = blockIdx.x - unit * a.nchunk;
+    if constexpr (!DENSE) CKV_TMARK(20);
 
     int b, kh, qh0, n;
     if constexpr (DENSE) {
@@ -219,6 +284,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     }
     __syncthreads();
 
+    if constexpr (!DENSE) CKV_TMARK(21);
     float qr[NH][E];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -294,6 +360,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         }
     }
 
+    if constexpr (!DENSE) CKV_TMARK(22);
     // Merge the four token rows of the wave (lanes l16, l16+16, l16+32, l16+48).
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -353,6 +420,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
             }
         }
     }
+    if constexpr (!DENSE) CKV_TMARK(23);
     if (nact == 1) return;
 
     // The last block of the unit merges every block's partial.
@@ -365,6 +433,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
                               a.out + ((size_t)b * a.Hq + qh0) * D,
                               DENSE ? nullptr : a.ml + (size_t)unit * NH * 2);
     if (tid == 0) reset_counter(&a.ctr[unit]);
+    if constexpr (!DENSE) CKV_TMARK(24);
 }
 
 template <typename T, int D, int NH, bool DENSE>

@@ -4,9 +4,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <climits>
+#include <type_traits>
+
 #include "ckv.h"
 
 namespace ckv {
+
+// Phase tracing for profiling builds (CKV_PHASE_TRACE, single translation
+// unit): thread 0 of block 0 of a kernel stamps the 100 MHz real-time counter
+// into slot `s` of a device array that ckv_trace_read() copies out.  In normal
+// builds the marks compile to nothing.
+#ifdef CKV_PHASE_TRACE
+__device__ unsigned long long g_phase_trace[64];
+#define CKV_TMARK(s)                                                   \
+    do {                                                               \
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)    \
+            ::ckv::g_phase_trace[(s)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
+#else
+#define CKV_TMARK(s) \
+    do {             \
+    } while (0)
+#endif
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -121,6 +141,36 @@ __device__ __forceinline__ unsigned long long wave_ext_u64(unsigned long long x)
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long x) { return wave_ext_u64<true>(x); }
 __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long x) { return wave_ext_u64<false>(x); }
 
+// Wave-wide 32-bit reductions with the same DPP butterfly (all lanes active).
+template <typename F>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x, F op) {
+    auto dpp = [](uint32_t v, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, decltype(ctrl)::value, 0xF, 0xF, true);
+    };
+    x = op(x, dpp(x, std::integral_constant<int, kQuadSwap1>{}));
+    x = op(x, dpp(x, std::integral_constant<int, kQuadSwap2>{}));
+    x = op(x, dpp(x, std::integral_constant<int, kRowHalfMirror>{}));
+    x = op(x, dpp(x, std::integral_constant<int, kRowMirror>{}));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+__device__ __forceinline__ float wave_min_f(float x) {
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+    return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
 // Order-preserving map of a float32 onto uint32 (larger float, larger code).
 __device__ __forceinline__ uint32_t ordered_bits(float s) {
     const uint32_t u = __float_as_uint(s);
@@ -162,30 +212,63 @@ __device__ __forceinline__ void softmax_scales(float m1, float m2, float &M, flo
 
 // Block-wide exclusive scan of one int per thread (blockDim.x = NT, NT % 64 == 0).
 // `scratch` needs NT/64 + 1 ints of shared memory.  Returns the exclusive prefix;
-// *total receives the block sum.  Contains two barriers.
+// *total receives the block sum.  Contains two barriers; callers separate two
+// scans sharing `scratch` with a barrier.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *total) {
+    constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
+        const int y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
     }
     if (lane == 63) scratch[wave] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int acc = 0;
-        for (int w = 0; w < NT / 64; ++w) {
-            int t = scratch[w];
-            scratch[w] = acc;
-            acc += t;
+    if (wave == 0) {  // scan of the wave totals
+        const int t = lane < NW ? scratch[lane] : 0;
+        int ti = t;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) {
+            const int y = __shfl_up(ti, o, 64);
+            if (lane >= o) ti += y;
         }
-        scratch[NT / 64] = acc;
+        if (lane < NW) scratch[lane] = ti - t;
+        if (lane == NW - 1) scratch[NW] = ti;
     }
     __syncthreads();
-    *total = scratch[NT / 64];
+    *total = scratch[NW];
     return scratch[wave] + x - v;
+}
+
+// Block-wide inclusive prefix maximum of one int per thread (same shape and
+// barriers as block_exclusive_scan).
+template <int NT>
+__device__ __forceinline__ int block_inclusive_max(int v, int *scratch) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x = max(x, y);
+    }
+    if (lane == 63) scratch[wave] = x;
+    __syncthreads();
+    if (wave == 0) {  // exclusive max-scan of the wave results
+        const int t = lane < NW ? scratch[lane] : INT_MIN;
+        int ti = t;
+#pragma unroll
+        for (int o = 1; o < NW; o <<= 1) {
+            const int y = __shfl_up(ti, o, 64);
+            if (lane >= o) ti = max(ti, y);
+        }
+        const int ex = __shfl_up(ti, 1, 64);
+        if (lane < NW) scratch[lane] = lane == 0 ? INT_MIN : ex;
+    }
+    __syncthreads();
+    return max(scratch[wave], x);
 }
 
 // Coordinates of graph g: sequence, kv head, first query head, query heads.

@@ -25,6 +25,9 @@ inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 constexpr int part_stride(int d) { return ((d + 2 + 31) / 32) * 32; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Row stride of the base CSR offsets (c_cap + 1 used, padded for 16-byte rows).
+__host__ __device__ inline int offs_stride(int c_cap) { return c_cap + 4; }
+
 inline int group_of(const ckv_kv *kv) { return kv->n_q_heads / kv->n_kv_heads; }
 inline int heads_per_graph(const ckv_kv *kv, const ckv_index *idx) {
     return idx->mode == CKV_MODE_PER_HEAD ? 1 : group_of(kv);

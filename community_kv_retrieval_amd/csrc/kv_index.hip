@@ -107,7 +107,7 @@ __global__ __launch_bounds__(1024) void build_scan_kernel(BuildParams p) {
     }
     int total;
     int run = block_exclusive_scan<1024>(loc, scratch, &total);
-    int32_t *offs = p.offs + (size_t)g * (p.c_cap + 1);
+    int32_t *offs = p.offs + (size_t)g * offs_stride(p.c_cap);
     int32_t *cur = p.cursor + (size_t)g * p.c_cap;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
     __shared__ int buf[kSortMax];
     const int g = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
     if (c >= min(p.n_comm[g], p.c_cap)) return;
-    const int32_t *offs = p.offs + (size_t)g * (p.c_cap + 1);
+    const int32_t *offs = p.offs + (size_t)g * offs_stride(p.c_cap);
     const int o = offs[c], s = offs[c + 1] - o;
     if (s <= 0) return;
     int32_t *mem = p.toks + (size_t)g * p.l_cap + o;

@@ -30,6 +30,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     __shared__ double s_q[D];
     __shared__ double s_part[4][256];
     const int g = blockIdx.y, c0 = blockIdx.x * 256;
+    CKV_TMARK(0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nc = min(p.n_comm[g], p.c_cap);
     float *out = p.scores + (size_t)g * p.c_cap + c0;
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     const double s = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
     const bool ok = c < nc && p.size[(size_t)g * p.c_cap + c] > 0;
     out[tid] = ok ? (float)s : kNegInf;
+    CKV_TMARK(1);
 }
 
 hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, float *scores,

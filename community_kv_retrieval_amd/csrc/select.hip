@@ -1,27 +1,29 @@
 // Budgeted community retrieval (the CommunityKV page, Figure 1 panel (3):
 // retrieve a candidate subset of communities under a token budget).
 //
-// One 1024-thread block per graph.  Every community becomes a 64-bit key,
-// (order-preserving bits of its float32 score) << 32 | (~id), so a larger key
-// means a better rank and ties of the score fall to the lower id.  The taken
-// set is the longest prefix of the ranking that fits the budget, i.e. every key
-// above the key of the first community that overflows it.
+// One 1024-thread block per graph; thread t owns the EPT consecutive
+// communities t*EPT ... .  Communities rank by float32 score, higher first,
+// ties to the lower id; as one number that is the 64-bit key
+// (order-preserving bits of the score) << 32 | (~id).  The taken set is the
+// longest prefix of the ranking that fits the budget, i.e. every key above the
+// key of the first community that overflows it (the cut).
 //
-// The cut is found in two steps.  First a token-weighted histogram over 1024
-// equal-width score bins between the lowest and highest score (a monotone map
-// of the score, so bins keep the ranking) and one block scan from the top bin
-// give the bin holding the cut; every community above it is taken.  Then the
-// few communities of that bin are sorted by key in one wave (bitonic network)
-// and walked until the budget overflows.  When the scores are degenerate (all
-// equal, or more than 64 in the cut bin) a most-significant-digit radix select
-// over the keys with token-weighted digit histograms finds the same cut.  The
-// community cap (max_comm) is the same radix select with unit weights.
+// The whole graph runs on one CU, so the passes over every community use
+// 32-bit arithmetic only.  The cut is found in two steps: a token-weighted
+// histogram over 1024 equal-width score bins between the lowest and highest
+// score (a monotone map of the score, so bins keep the ranking), walked from
+// the top by one wave, gives the bin holding the cut; every community above it
+// is taken.  The few communities of that bin get their 64-bit keys, one wave
+// sorts them (bitonic network) and walks them until the budget overflows.
+// When the scores are degenerate (all equal, or more than 64 in the cut bin) a
+// most-significant-digit radix select over the 64-bit keys, with
+// token-weighted digit histograms, finds the same cut.  The community cap
+// (max_comm) is the same radix select with unit weights.
 //
 // Then the taken ids are compacted in ascending id order with block scans, and
 // the attended token list is written: sinks, the base members of every taken
-// community, then the taken communities' tail members.  Sizes, scores and tail
-// entries are read at the start with 16-byte loads; CSR offsets only for the
-// taken communities.
+// community, then the taken communities' tail members.  Sizes, scores, CSR
+// offsets and tail entries are read at the start with 16-byte loads.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -29,9 +31,12 @@ namespace ckv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kBins = kSelThreads;
-// Taken communities whose copy runs block-wide out of LDS (more fall back to
-// one thread per community).
-constexpr int kSelLds = 4096;
+// Member slots mapped to their community in LDS (the common case); longer
+// lists binary-search the communities' first slots (up to kSelLds
+// communities), and more communities than that are copied one thread each.
+constexpr int kSelSlots = 4096;
+constexpr int kSelLds = 2048;
+constexpr int kSlotsPerThread = kSelSlots / kSelThreads;
 constexpr int kTailPerThread = 4;  // tail_cap <= 4096
 
 struct SelectParams {
@@ -53,38 +58,59 @@ struct SelectParams {
 };
 
 struct SelShared {
-    int sid[kSelLds];        // taken community
-    int soff[kSelLds];       // its first base member in toks
+    int owner[kSelSlots];    // member slot -> index of its taken community
+    int soff[kSelLds];       // first base member in toks of the k-th taken community
     int spref[kSelLds + 1];  // its first slot in the token list (after the sinks)
     int bw[kBins];           // token weight per score bin
-    uint32_t hw[256];        // radix fallback: token weight per digit
-    uint32_t hn[256];        // radix fallback: candidates per digit
+    uint32_t hw[256];        // radix select: token weight per digit
+    uint32_t hn[256];        // radix select: candidates per digit
     uint32_t bits[CKV_MAX_C_CAP / 32];
     unsigned long long ckey[64];
     int csz[64];
     int ccount;
     int cut_bin, cut_above;
     int scan[kSelThreads / 64 + 1];
-    unsigned long long red_max[kSelThreads / 64];
-    unsigned long long red_min[kSelThreads / 64];
+    float red_lo[kSelThreads / 64], red_hi[kSelThreads / 64];
+    uint32_t red_id[kSelThreads / 64];
     unsigned long long prefix, mask, thr;
     long long rem;
     int done;
 };
 
-__device__ __forceinline__ float key_score(unsigned long long k) {
-    const uint32_t o = (uint32_t)(k >> 32);
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+__device__ __forceinline__ unsigned long long comm_key(float s, int c) {
+    return ((unsigned long long)ordered_bits(s) << 32) | (0xFFFFFFFFu - (uint32_t)c);
 }
 
-// Threshold key of the budget cut by radix select over the keys: the taken
-// communities are those with key > threshold (0 = everything fits).  `unit`
-// counts communities instead of tokens (the community cap).
+// Threshold key of the budget cut by radix select over the 64-bit keys: the
+// taken communities are those with key > threshold (0 = everything fits).
+// `unit` counts communities instead of tokens (the community cap).
 template <int EPT>
-__device__ unsigned long long radix_cut(const unsigned long long (&key)[EPT], const int (&w)[EPT],
-                                        bool unit, long long budget, unsigned long long kmax,
-                                        unsigned long long kmin, SelShared &sh) {
+__device__ unsigned long long radix_cut(const float (&sv)[EPT], const int (&w)[EPT], bool unit,
+                                        long long budget, SelShared &sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    unsigned long long key[EPT];
+    unsigned long long kmax = 0ull, kmin = ~0ull;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        key[j] = w[j] > 0 ? comm_key(sv[j], tid * EPT + j) : 0ull;
+        if (key[j]) {
+            kmax = umax64(kmax, key[j]);
+            kmin = umin64(kmin, key[j]);
+        }
+    }
+    kmax = wave_max_u64(kmax);
+    kmin = wave_min_u64(kmin);
+    if (lane == 0) {
+        sh.ckey[wave] = kmax;
+        sh.ckey[32 + wave] = kmin;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSelThreads / 64; ++i) {
+        kmax = umax64(kmax, sh.ckey[i]);
+        kmin = umin64(kmin, sh.ckey[32 + i]);
+    }
+    __syncthreads();
     const unsigned long long diff = kmax ^ kmin;
     int hi = diff ? 63 - __clzll((long long)diff) : 0;
     unsigned long long mask = ~((2ull << hi) - 1ull);  // bits above hi (0 when hi == 63)
@@ -163,50 +189,70 @@ __device__ unsigned long long radix_cut(const unsigned long long (&key)[EPT], co
 // Budget cut through equal-width score bins (see the file comment).  Returns
 // false, uniformly across the block, when the radix select has to decide.
 template <int EPT>
-__device__ bool value_cut(const unsigned long long (&key)[EPT], const float (&sv)[EPT], const int (&w)[EPT],
-                          int budget, unsigned long long kmax, unsigned long long kmin, SelShared &sh,
-                          unsigned long long &thr) {
+__device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budget, float lo, float hi,
+                          SelShared &sh, unsigned long long &thr) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float hi = key_score(kmax), lo = key_score(kmin);
     const float scale = (float)kBins / (hi - lo);
     if (!(hi > lo) || !(scale < __builtin_huge_valf())) return false;
     sh.bw[tid] = 0;
-    if (tid == 0) {
-        sh.ccount = 0;
-        sh.cut_bin = -1;
-    }
+    if (tid == 0) sh.ccount = 0;
     __syncthreads();
     int bin[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         bin[j] = -1;
-        if (key[j]) {
+        if (w[j] > 0) {
             bin[j] = min(kBins - 1, (int)((sv[j] - lo) * scale));
             atomicAdd(&sh.bw[bin[j]], w[j]);
         }
     }
     __syncthreads();
-    const int rb = kBins - 1 - tid;  // thread t scans bins from the top
-    const int v = sh.bw[rb];
-    int total;
-    const int excl = block_exclusive_scan<kSelThreads>(v, sh.scan, &total);
-    if (total <= budget) {  // every community fits
+    // One wave walks the bins from the top: lane l owns bins
+    // kBins-1-16l .. kBins-16-16l, a prefix over lanes gives each lane the
+    // weight above its bins.
+    if (wave == 0) {
+        int v[16], tot = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            v[k] = sh.bw[kBins - 1 - (lane * 16 + k)];
+            tot += v[k];
+        }
+        int incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        int acc = incl - tot, found = -1, above = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (found < 0 && acc + v[k] > budget) {
+                found = kBins - 1 - (lane * 16 + k);
+                above = acc;
+            }
+            acc += v[k];
+        }
+        const unsigned long long bal = __ballot(found >= 0);
+        const int src = bal ? __ffsll((long long)bal) - 1 : 0;
+        const int fb = __shfl(found, src, 64), fa = __shfl(above, src, 64);
+        if (lane == 0) {
+            sh.cut_bin = bal ? fb : -1;  // -1: every community fits
+            sh.cut_above = fa;
+        }
+    }
+    __syncthreads();
+    const int cb = sh.cut_bin, above = sh.cut_above;
+    if (cb < 0) {
         thr = 0ull;
         __syncthreads();
         return true;
     }
-    if (excl <= budget && budget < excl + v) {
-        sh.cut_bin = rb;
-        sh.cut_above = excl;
-    }
-    __syncthreads();
-    const int cb = sh.cut_bin, above = sh.cut_above;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         if (bin[j] == cb) {
             const int i = atomicAdd(&sh.ccount, 1);
             if (i < 64) {
-                sh.ckey[i] = key[j];
+                sh.ckey[i] = comm_key(sv[j], tid * EPT + j);
                 sh.csz[i] = w[j];
             }
         }
@@ -257,6 +303,7 @@ template <int EPT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     __shared__ SelShared sh;
     const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    CKV_TMARK(10);
     const int C = p.c_cap;
     const int nc = min(p.n_comm[g], C);
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
@@ -264,32 +311,53 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     const int ns = min(p.n_sinks, max(L, 0));
     const float *sc = p.scores + (size_t)g * C;
     const int32_t *sz = p.size + (size_t)g * C;
-    const int32_t *offs = p.offs + (size_t)g * (C + 1);
+    const int32_t *offs = p.offs + (size_t)g * offs_stride(C);
     int32_t *tl = p.tok_list + (size_t)g * p.t_cap;
 
-    // Sizes and scores of this thread's EPT consecutive communities, 16 bytes
-    // per load; the tail entries too.  (CSR offsets are fetched later, for the
-    // taken communities only.)
+    // Sizes, scores and CSR offsets of this thread's EPT consecutive
+    // communities, 16 bytes per load, and the tail entries.
     static_assert(EPT % 4 == 0, "EPT must be a multiple of 4");
-    int s[EPT];
+    int s[EPT], o0[EPT], o1[EPT];
     float sv[EPT];
+    {
+        // c % 4 == 0 and C % 256 == 0: a 16-byte load from c < C stays inside
+        // the row (the offsets row holds C + 4 entries).  Nothing waits for
+        // n_comm: entries at or past it are masked below.
+        int4 s4[EPT / 4], o4[EPT / 4];
+        float4 v4[EPT / 4];
+        int olast = 0;
 #pragma unroll
-    for (int j = 0; j < EPT; j += 4) {
-        const int c = tid * EPT + j;  // c % 4 == 0 and C % 256 == 0: the load stays in the row
-        int4 s4 = make_int4(0, 0, 0, 0);
-        float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c < nc) {
-            s4 = *reinterpret_cast<const int4 *>(sz + c);
-            v4 = *reinterpret_cast<const float4 *>(sc + c);
+        for (int j = 0; j < EPT; j += 4) {
+            const int c = tid * EPT + j;
+            s4[j / 4] = make_int4(0, 0, 0, 0);
+            o4[j / 4] = make_int4(0, 0, 0, 0);
+            v4[j / 4] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (c < C) {
+                s4[j / 4] = *reinterpret_cast<const int4 *>(sz + c);
+                v4[j / 4] = *reinterpret_cast<const float4 *>(sc + c);
+                o4[j / 4] = *reinterpret_cast<const int4 *>(offs + c);
+            }
         }
-        s[j] = c < nc ? s4.x : 0;
-        s[j + 1] = c + 1 < nc ? s4.y : 0;
-        s[j + 2] = c + 2 < nc ? s4.z : 0;
-        s[j + 3] = c + 3 < nc ? s4.w : 0;
-        sv[j] = v4.x;
-        sv[j + 1] = v4.y;
-        sv[j + 2] = v4.z;
-        sv[j + 3] = v4.w;
+        if (tid * EPT + EPT <= C) olast = offs[tid * EPT + EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; j += 4) {
+            const int c = tid * EPT + j;
+            s[j] = c < nc ? s4[j / 4].x : 0;
+            s[j + 1] = c + 1 < nc ? s4[j / 4].y : 0;
+            s[j + 2] = c + 2 < nc ? s4[j / 4].z : 0;
+            s[j + 3] = c + 3 < nc ? s4[j / 4].w : 0;
+            sv[j] = v4[j / 4].x;
+            sv[j + 1] = v4[j / 4].y;
+            sv[j + 2] = v4[j / 4].z;
+            sv[j + 3] = v4[j / 4].w;
+            o0[j] = o4[j / 4].x;
+            o0[j + 1] = o4[j / 4].y;
+            o0[j + 2] = o4[j / 4].z;
+            o0[j + 3] = o4[j / 4].w;
+        }
+#pragma unroll
+        for (int j = 0; j + 1 < EPT; ++j) o1[j] = o0[j + 1];
+        o1[EPT - 1] = olast;
     }
     const int tn = p.tail_len[g];
     int tcomm[kTailPerThread], tpos[kTailPerThread];
@@ -303,55 +371,55 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 
     for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
 
-    unsigned long long key[EPT];
-    unsigned long long kmax = 0ull, kmin = ~0ull;
+    // Score range of the non-empty communities.
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int c = tid * EPT + j;
         if (sv[j] == 0.f) sv[j] = 0.f;  // one key for +0 and -0
-        key[j] = (s[j] > 0) ? (((unsigned long long)ordered_bits(sv[j]) << 32) | (0xFFFFFFFFu - (uint32_t)c)) : 0ull;
-        if (key[j]) {
-            kmax = umax64(kmax, key[j]);
-            kmin = umin64(kmin, key[j]);
+        if (s[j] > 0) {
+            lo = fminf(lo, sv[j]);
+            hi = fmaxf(hi, sv[j]);
         }
     }
-    kmax = wave_max_u64(kmax);
-    kmin = wave_min_u64(kmin);
+    lo = wave_min_f(lo);
+    hi = wave_max_f(hi);
     if (lane == 0) {
-        sh.red_max[wave] = kmax;
-        sh.red_min[wave] = kmin;
+        sh.red_lo[wave] = lo;
+        sh.red_hi[wave] = hi;
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSelThreads / 64; ++i) {
-        kmax = umax64(kmax, sh.red_max[i]);
-        kmin = umin64(kmin, sh.red_min[i]);
+        lo = fminf(lo, sh.red_lo[i]);
+        hi = fmaxf(hi, sh.red_hi[i]);
     }
+    const bool any = hi >= lo;  // uniform: some community is non-empty
+    // Best-ranked community: the lowest id among those scoring hi.
+    uint32_t best = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+        if (s[j] > 0 && sv[j] == hi) best = min(best, (uint32_t)(tid * EPT + j));
+    best = wave_min_u32(best);
+    if (lane == 0) sh.red_id[wave] = best;
     __syncthreads();
+    CKV_TMARK(11);
 
     unsigned long long thr = ~0ull;  // nothing taken when there is no candidate
-    if (kmax != 0ull) {
-        if (!value_cut<EPT>(key, sv, s, p.budget, kmax, kmin, sh, thr))
-            thr = radix_cut<EPT>(key, s, false, (long long)p.budget, kmax, kmin, sh);
-        if (p.max_comm > 0) {
-            const unsigned long long t2 = radix_cut<EPT>(key, s, true, (long long)p.max_comm, kmax, kmin, sh);
-            thr = t2 > thr ? t2 : thr;
-        }
+    if (any) {
+        if (!value_cut<EPT>(sv, s, p.budget, lo, hi, sh, thr)) thr = radix_cut<EPT>(sv, s, false, p.budget, sh);
+        if (p.max_comm > 0) thr = umax64(thr, radix_cut<EPT>(sv, s, true, p.max_comm, sh));
     }
+    CKV_TMARK(12);
 
-    // Compact the taken ids (ascending) and give each its slot in tok_list.
+    // taken <=> key > thr, tested in 32-bit pieces
+    const uint32_t thr_u = (uint32_t)(thr >> 32), thr_id = 0xFFFFFFFFu - (uint32_t)thr;
+    bool taken[EPT];
     int nloc = 0, tokloc = 0;
-    int o0[EPT], o1[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int c = tid * EPT + j;
-        const bool t = key[j] > thr;
-        o0[j] = t ? offs[c] : 0;
-        o1[j] = t ? offs[c + 1] : 0;
-    }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        if (key[j] > thr) {
+        const uint32_t u = ordered_bits(sv[j]), c = (uint32_t)(tid * EPT + j);
+        taken[j] = s[j] > 0 && (u > thr_u || (u == thr_u && c < thr_id));
+        if (taken[j]) {
             ++nloc;
             tokloc += o1[j] - o0[j];
         }
@@ -361,45 +429,76 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     __syncthreads();
     int dst = ns + block_exclusive_scan<kSelThreads>(tokloc, sh.scan, &ntok);
     __syncthreads();
+    CKV_TMARK(13);
     const int32_t *toks = p.toks + (size_t)g * p.l_cap;
-    const bool staged = nsel <= kSelLds;
+    const int mode = nsel > kSelLds ? 2 : (ntok <= kSelSlots ? 0 : 1);  // uniform
+    if (mode == 0)
+        for (int j = tid; j < ntok; j += kSelThreads) sh.owner[j] = -1;
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        if (key[j] > thr) {
+        if (taken[j]) {
             const int c = tid * EPT + j;
+            const int rel = dst - ns, len = o1[j] - o0[j];
             p.sel[(size_t)g * C + kpos] = c;
             atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
-            if (staged) {
-                sh.sid[kpos] = c;
+            if (mode < 2) {
                 sh.soff[kpos] = o0[j];
-                sh.spref[kpos] = dst - ns;
+                sh.spref[kpos] = rel;
+                if (mode == 0 && len > 0) sh.owner[rel] = kpos;  // first slot of the community
             } else {
-                for (int i = o0[j]; i < o1[j]; ++i) tl[dst + i - o0[j]] = toks[i];
+                for (int i = 0; i < len; ++i) tl[dst + i] = toks[o0[j] + i];
             }
-            dst += o1[j] - o0[j];
+            dst += len;
             ++kpos;
         }
     }
-    if (tid == 0 && staged) sh.spref[nsel] = ntok;
+    if (tid == 0 && mode == 1) sh.spref[nsel] = ntok;
     for (int i = tid; i < ns; i += kSelThreads) tl[i] = i;
     __syncthreads();
-    if (staged) {
-        // slot j of the member part belongs to the last taken community whose
-        // first slot is <= j
+    CKV_TMARK(14);
+    if (mode == 0) {
+        // every slot takes the owner of the nearest marked slot at or before it:
+        // an inclusive prefix max over kSlotsPerThread consecutive slots per thread
+        int ow[kSlotsPerThread], run = -1;
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            const int j = tid * kSlotsPerThread + u;
+            ow[u] = j < ntok ? sh.owner[j] : -1;
+            run = max(run, ow[u]);
+            ow[u] = run;
+        }
+        const int before = block_inclusive_max<kSelThreads>(run, sh.scan);
+        const int carry = __shfl_up(before, 1, 64);
+        int prev = (tid & 63) ? carry : -1;
+        if ((tid & 63) == 0 && tid > 0) prev = sh.scan[(tid >> 6)];  // max over earlier waves
+        int v[kSlotsPerThread];
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            const int j = tid * kSlotsPerThread + u;
+            const int k = max(prev, ow[u]);
+            v[u] = j < ntok ? toks[sh.soff[k] + (j - sh.spref[k])] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kSlotsPerThread; ++u) {
+            const int j = tid * kSlotsPerThread + u;
+            if (j < ntok) tl[ns + j] = v[u];
+        }
+    } else if (mode == 1) {
         for (int j0 = 0; j0 < ntok; j0 += 4 * kSelThreads) {
             int v[4], at[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + u * kSelThreads + tid;
                 at[u] = j;
-                if (j < ntok) {
-                    int lo = 0, hi = nsel - 1;
-                    while (lo < hi) {
-                        const int mid = (lo + hi + 1) >> 1;
-                        if (sh.spref[mid] <= j) lo = mid;
-                        else hi = mid - 1;
+                if (j < ntok) {  // the last taken community whose first slot is <= j
+                    int a = 0, b = nsel - 1;
+                    while (a < b) {
+                        const int mid = (a + b + 1) >> 1;
+                        if (sh.spref[mid] <= j) a = mid;
+                        else b = mid - 1;
                     }
-                    v[u] = toks[sh.soff[lo] + (j - sh.spref[lo])];
+                    v[u] = toks[sh.soff[a] + (j - sh.spref[a])];
                 }
             }
 #pragma unroll
@@ -407,6 +506,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
                 if (at[u] < ntok) tl[ns + at[u]] = v[u];
         }
     }
+    CKV_TMARK(15);
 
     // Tail members of taken communities, in tail order.
     int f[kTailPerThread], floc = 0;
@@ -424,10 +524,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         if (f[j]) tl[tdst++] = tpos[j];
 
     if (tid == 0) {
+        uint32_t b = 0xFFFFFFFFu;
+        for (int i = 0; i < kSelThreads / 64; ++i) b = min(b, sh.red_id[i]);
         p.sel_n[g] = nsel;
         p.tok_n[g] = ns + ntok + ntail;
-        p.top[g] = kmax ? (int)(0xFFFFFFFFu - (uint32_t)kmax) : -1;
+        p.top[g] = any ? (int)b : -1;
     }
+    CKV_TMARK(16);
 }
 
 hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *scores, int budget,

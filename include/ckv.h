@@ -109,7 +109,8 @@ typedef struct ckv_index {
     int32_t  n_sinks;    /* leading sink positions, >= 0 */
     int32_t *n_comm;     /* [G] communities in use, <= c_cap (set by the caller before the build) */
     int32_t *size;       /* [G][c_cap] members per community (base + tail) */
-    int32_t *offs;       /* [G][c_cap+1] base CSR offsets into toks */
+    int32_t *offs;       /* [G][c_cap+4] base CSR offsets into toks: entries 0..c_cap used, rows
+                            padded to c_cap+4 so that every row starts 16-byte aligned */
     int32_t *toks;       /* [G][l_cap] base members, grouped by community, ascending position */
     int32_t *label;      /* [G][l_cap] community of every position, -1 = sink / none */
     int32_t *tail_pos;   /* [G][tail_cap] appended positions, in order */

@@ -73,6 +73,15 @@ def test_fewer_candidates_than_kappa():
     PY.run_steps(w, 7, w.steps)
 
 
+@pytest.mark.parametrize("n_ctx,budget", [(14000, 9000), (40000, 1 << 20)])
+def test_long_token_lists(n_ctx, budget):
+    # more member slots than the select kernel maps in LDS, and (second case)
+    # more taken communities than it stages: the fallback copies
+    w = small_per_head(n_ctx=n_ctx, budget=budget, n_kv_heads=2, n_q_heads=8, steps=2)
+    PY.log(f"long token lists n={n_ctx} budget={budget}")
+    PY.run_steps(w, 18, w.steps, check_dense=budget > n_ctx)
+
+
 def test_community_cap():
     w = small_per_head(n_ctx=3000, budget=1 << 20, max_comm=5, steps=3)
     PY.log("max_comm 5")
