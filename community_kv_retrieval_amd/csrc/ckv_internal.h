@@ -13,7 +13,7 @@ namespace ckv {
 // Tokens one gather block attends: 16 tokens per pass of its 256 threads
 // (4 waves x 4 rows of 16 lanes), kGatherU passes per block.
 constexpr int kGatherU = 8;
-constexpr int kGatherTokens = 16 * kGatherU;
+constexpr int kGatherTokens = 16 * kGatherU * 2;
 // The dense baseline walks kDenseIters such spans per block.
 constexpr int kDenseU = 8;
 constexpr int kDenseIters = 8;
