@@ -96,22 +96,48 @@ def main():
     n_comm = np.array(synth.graph_n_comm(w, slices), dtype=np.int64)
     score_bytes = int(n_comm.sum()) * w.head_dim * 4
 
-    # Headline pass: K steps back to back, bracketed by synchronisation.
+    # Eager pass: K steps launched one call at a time from Python.
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
     e0.record()
     for t in range(W, total):
         dec.step(Q[t], KN[t], VN[t])
     e1.record()
     torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / K
+    ref = [x.clone() for x in (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)]
+
+    # Headline pass: the same K steps captured once as one HIP graph (how a
+    # decode loop is launched in serving) and replayed, bracketed by
+    # synchronisation.  The replay must reproduce the eager pass bit for bit.
+    restore()
+    for t in range(W):
+        dec.step(Q[t], KN[t], VN[t])
+    torch.cuda.synchronize()
+    snap_w = (idx.state_dict(), kv.kv.clone(), kv.seq_len.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(W, total):
+            dec.step(Q[t], KN[t], VN[t])
+    idx.load_state_dict(snap_w[0])
+    kv.kv.copy_(snap_w[1])
+    kv.seq_len.copy_(snap_w[2])
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / K
+    got = (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)
+    assert all(torch.equal(a, b) for a, b in zip(ref, got)), "graph replay differs from the eager steps"
+    del graph
     if args.profile:
-        log(f"[bench] profile run: {ms_step * 1e3:.1f} us/step")
+        log(f"[bench] profile run: {ms_step * 1e3:.1f} us/step (graph), {ms_eager * 1e3:.1f} us/step (eager)")
         return
 
     # Breakdown pass: the same steps with an event between the four calls.
@@ -218,6 +244,8 @@ def main():
         "tokens_per_step": round(float(tok[W:].sum(axis=1).mean()), 1),
         "dense_flash_decode": dense,
         "cpu_baseline": cpu,
+        "ms_per_step_eager": round(ms_eager, 5),
+        "launch": "hip_graph",
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(res), flush=True)
