@@ -15,6 +15,7 @@ steps.  Output: one JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -27,6 +28,10 @@ if ROOT not in sys.path:
 
 METRIC = "decode steps/s + gathered-KV HBM GB/s (% roofline) at 128K ctx, budget 4096"
 HBM_PEAK_GBPS = 8000.0
+# HBM traffic of one gather launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# scaled by a plain copy kernel; valid only for the sources it names.
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gather_attend_llama31_8b_128k_pmc.txt")
+GATHER_SOURCES = ("attend.hip", "ckv_device.h", "ckv_internal.h")
 
 
 def log(msg):
@@ -44,6 +49,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile", action="store_true", help="only warm-up + timed steps (for rocprofv3 runs)")
+    ap.add_argument("--eager-only", action="store_true", help="with --profile: no HIP graph (counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB copy kernel 5 times (scale for rocprofv3 byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -57,6 +65,9 @@ def main():
     from community_kv_retrieval_amd import ckv, runner, synth
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     w = synth.preset(args.workload)
     W, K = args.warmup, args.steps
     total = W + K
@@ -109,6 +120,9 @@ def main():
     torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / K
     ref = [x.clone() for x in (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)]
+    if args.profile and args.eager_only:
+        log(f"[bench] profile run (eager only): {ms_eager * 1e3:.1f} us/step")
+        return
 
     # Headline pass: the same K steps captured once as one HIP graph (how a
     # decode loop is launched in serving) and replayed, bracketed by
@@ -140,28 +154,34 @@ def main():
         log(f"[bench] profile run: {ms_step * 1e3:.1f} us/step (graph), {ms_eager * 1e3:.1f} us/step (eager)")
         return
 
-    # Breakdown pass: the same steps with an event between the four calls.
+    # Breakdown pass: the same steps, each of the four kernels stamping its own
+    # start/stop events from its dispatch (ckv_time_next_launch), so these are
+    # kernel execution times on the stream the kernels run on.
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+          for _ in range(K)]
+    for row in ev:  # torch creates the underlying HIP events on first record
+        for a, c in row:
+            a.record()
+            c.record()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     b = buf
     for i, t in enumerate(range(W, total)):
         q = Q[t]
-        ev[i][0].record()
+        ckv.ckv_time_next_launch(*ev[i][0])
         ckv.ckv_score_centroids(kv, idx, q, b.scores)
-        ev[i][1].record()
+        ckv.ckv_time_next_launch(*ev[i][1])
         ckv.ckv_select_communities(kv, idx, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
                                    b.tok_list, b.tok_n)
-        ev[i][2].record()
+        ckv.ckv_time_next_launch(*ev[i][2])
         ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, b.out, b.logits, b.ml, b.ws)
-        ev[i][3].record()
+        ckv.ckv_time_next_launch(*ev[i][3])
         ckv.ckv_assign_update(kv, idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, dec.kappa, KN[t], VN[t],
                               b.edges, b.assign, b.ws)
-        ev[i][4].record()
     torch.cuda.synchronize()
-    dt = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(4)] for i in range(K)]) * 1e3  # us
+    dt = np.array([[a.elapsed_time(c) for a, c in ev[i]] for i in range(K)]) * 1e3  # us
     names = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
     gather_us = dt[:, 2]
     gather_gbps = float(gathered.sum() / (gather_us.sum() * 1e-6) / 1e9)
@@ -210,6 +230,8 @@ def main():
         cpu = cpu_baseline(w, args.seed, slices, steps_in, args.cpu_seconds)
 
     avg_gather = float(gathered.mean())
+    src_hash = gather_source_hash()
+    traffic = measured_traffic(w.name, src_hash)
     res = {
         "metric": METRIC,
         "value": round(1e3 / ms_step, 1),
@@ -231,8 +253,8 @@ def main():
         "gathered_kv_frac_of_hbm": round(gather_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "gather_attend", "achieved": round(gather_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": int(avg_gather),
-                     "avg_launch_us": round(float(gather_us.mean()), 2)},
+                     "traffic": traffic, "bytes_per_launch": int(avg_gather),
+                     "avg_launch_us": round(float(gather_us.mean()), 2), "kernel_sources": src_hash},
         "score_roofline": {"bound": "hbm", "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": round(score_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": score_bytes,
                            "avg_launch_us": round(float(dt[:, 0].mean()), 2)},
@@ -249,6 +271,44 @@ def main():
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(res), flush=True)
+
+
+def gather_source_hash():
+    h = hashlib.sha256()
+    for f in GATHER_SOURCES:
+        with open(os.path.join(ROOT, "community_kv_retrieval_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, src_hash):
+    """Bytes per gather launch from the committed counter summary, or None when
+    it was taken on other kernel sources or another workload."""
+    try:
+        with open(PMC_SUMMARY) as fh:
+            kv = dict(line.split(":", 1) for line in fh.read().splitlines() if ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_sources") != src_hash or kv.get("workload") != workload:
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 256 MiB read and 256 MiB written per launch."""
+    import torch
+    n = (256 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 5 launches of neg over {n * 4} bytes")
 
 
 def cpu_baseline(w, seed, slices, steps_in, seconds):

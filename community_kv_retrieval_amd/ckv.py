@@ -30,7 +30,7 @@ CKV_MAX_KAPPA, CKV_MAX_C_CAP = 32, 16384
 
 EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_centroids",
            "ckv_select_communities", "ckv_gather_attend", "ckv_assign_update", "ckv_dense_attend",
-           "ckv_status_str", "ckv_abi_version")
+           "ckv_time_next_launch", "ckv_status_str", "ckv_abi_version")
 
 
 class CkvError(RuntimeError):
@@ -72,6 +72,7 @@ def _load():
                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]),
         "ckv_dense_attend": (c_int32, [KVP, c_void_p, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_time_next_launch": (c_int32, [c_void_p, c_void_p]),
         "ckv_status_str": (ctypes.c_char_p, [c_int32]),
         "ckv_abi_version": (c_int32, []),
     }
@@ -265,6 +266,17 @@ def ckv_dense_attend(kv: KVStore, q: torch.Tensor, sm_scale: float, out: torch.T
     _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
     _check("ckv_dense_attend", LIB.ckv_dense_attend(ctypes.byref(kv.desc), _ptr(q), float(sm_scale), _ptr(out),
                                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def ckv_time_next_launch(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]):
+    """Arms the next step kernel of this thread to stamp `start`/`stop` from its own dispatch.
+
+    Both events must already exist on the device (torch creates an event on its
+    first record()).  Once the kernel has run, start.elapsed_time(stop) is its
+    execution time in ms.  None, None disarms.
+    """
+    ev = lambda e: None if e is None else c_void_p(e.cuda_event)
+    _check("ckv_time_next_launch", LIB.ckv_time_next_launch(ev(start), ev(stop)))
 
 
 # ---------------------------------------------------------------------------

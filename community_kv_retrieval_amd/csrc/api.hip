@@ -9,6 +9,10 @@
 
 using namespace ckv;
 
+namespace ckv {
+thread_local LaunchTiming g_next_timing;
+}
+
 namespace {
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -57,6 +61,12 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 extern "C" {
 
 int32_t ckv_abi_version(void) { return 2; }
+
+ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
+    if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;
+    g_next_timing = LaunchTiming{(hipEvent_t)start, (hipEvent_t)stop};
+    return CKV_OK;
+}
 
 #ifdef CKV_PHASE_TRACE
 // Profiling builds only: copy the 64 phase stamps to host memory.

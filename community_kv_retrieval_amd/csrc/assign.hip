@@ -307,7 +307,7 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
     const dim3 grid(idx->n_graphs), block(256);
 #define CKV_AS(TT, DD, NN) \
-    if (kv->head_dim == DD && nh == NN) { hipLaunchKernelGGL((assign_kernel<TT, DD, NN>), grid, block, 0, s, p); return hipGetLastError(); }
+    if (kv->head_dim == DD && nh == NN) { CKV_LAUNCH((assign_kernel<TT, DD, NN>), grid, block, s, p); return hipGetLastError(); }
 #define CKV_AS_T(TT) \
     CKV_AS(TT, 64, 1) CKV_AS(TT, 64, 2) CKV_AS(TT, 64, 4) CKV_AS(TT, 64, 8) \
     CKV_AS(TT, 128, 1) CKV_AS(TT, 128, 2) CKV_AS(TT, 128, 4) CKV_AS(TT, 128, 8)

@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
 template <typename T, int D, int NH, bool DENSE>
 static hipError_t launch_t(const AttendParams &p, int units, hipStream_t s) {
     constexpr int U = pick_u<T, D, NH>();
-    hipLaunchKernelGGL((attend_kernel<T, D, NH, U, DENSE>), dim3(units * p.nchunk), dim3(256), 0, s, p);
+    CKV_LAUNCH((attend_kernel<T, D, NH, U, DENSE>), dim3(units * p.nchunk), dim3(256), s, p);
     return hipGetLastError();
 }
 

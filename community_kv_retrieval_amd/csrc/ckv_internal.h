@@ -2,6 +2,7 @@
 // shapes, workspace layout and the per-kernel launchers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -18,6 +19,29 @@ constexpr int kGatherTokens = 16 * kGatherU * 2;
 constexpr int kDenseU = 8;
 constexpr int kDenseIters = 8;
 constexpr int kDenseTokens = 16 * kDenseU * kDenseIters;
+
+// Events armed by ckv_time_next_launch for the next step-kernel launch of
+// this host thread.
+struct LaunchTiming {
+    hipEvent_t start, stop;
+};
+extern thread_local LaunchTiming g_next_timing;
+
+inline LaunchTiming take_timing() {
+    const LaunchTiming t = g_next_timing;
+    g_next_timing = LaunchTiming{nullptr, nullptr};
+    return t;
+}
+
+// Launches one step kernel, with the armed timing events if there are any.
+#define CKV_LAUNCH(kernel, grid, block, stream, ...)                                             \
+    do {                                                                                         \
+        const ::ckv::LaunchTiming t_ = ::ckv::take_timing();                                     \
+        if (t_.start)                                                                            \
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, t_.start, t_.stop, 0, __VA_ARGS__); \
+        else                                                                                     \
+            hipLaunchKernelGGL(kernel, grid, block, 0, stream, __VA_ARGS__);                     \
+    } while (0)
 
 inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 // Floats of one split-K partial record (accumulator, max, sum), padded to whole

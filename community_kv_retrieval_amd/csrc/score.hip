@@ -79,11 +79,11 @@ hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, f
     const dim3 grid(idx->c_cap / 256, idx->n_graphs);
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
     if (kv->head_dim == 128) {
-        if (bf) hipLaunchKernelGGL((score_kernel<bf16_t, 128>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((score_kernel<float, 128>), grid, dim3(256), 0, s, p);
+        if (bf) CKV_LAUNCH((score_kernel<bf16_t, 128>), grid, dim3(256), s, p);
+        else CKV_LAUNCH((score_kernel<float, 128>), grid, dim3(256), s, p);
     } else {
-        if (bf) hipLaunchKernelGGL((score_kernel<bf16_t, 64>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((score_kernel<float, 64>), grid, dim3(256), 0, s, p);
+        if (bf) CKV_LAUNCH((score_kernel<bf16_t, 64>), grid, dim3(256), s, p);
+        else CKV_LAUNCH((score_kernel<float, 64>), grid, dim3(256), s, p);
     }
     return hipGetLastError();
 }

@@ -563,10 +563,10 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *sc
     p.tok_n = tok_n;
     const int ept = ceil_div(idx->c_cap, kSelThreads);
     const dim3 grid(idx->n_graphs), block(kSelThreads);
-    if (ept <= 4) hipLaunchKernelGGL((select_kernel<4>), grid, block, 0, s, p);
-    else if (ept <= 8) hipLaunchKernelGGL((select_kernel<8>), grid, block, 0, s, p);
-    else if (ept <= 12) hipLaunchKernelGGL((select_kernel<12>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((select_kernel<16>), grid, block, 0, s, p);
+    if (ept <= 4) CKV_LAUNCH((select_kernel<4>), grid, block, s, p);
+    else if (ept <= 8) CKV_LAUNCH((select_kernel<8>), grid, block, s, p);
+    else if (ept <= 12) CKV_LAUNCH((select_kernel<12>), grid, block, s, p);
+    else CKV_LAUNCH((select_kernel<16>), grid, block, s, p);
     return hipGetLastError();
 }
 

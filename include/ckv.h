@@ -59,6 +59,8 @@ extern "C" {
 
 struct ihipStream_t;
 typedef struct ihipStream_t *ckv_stream_t; /* a hipStream_t */
+struct ihipEvent_t;
+typedef struct ihipEvent_t *ckv_event_t;   /* a hipEvent_t */
 
 typedef int32_t ckv_status;
 #define CKV_OK             0
@@ -197,6 +199,19 @@ ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32
  * seq_len[b] cached tokens of its kv head.  out[batch][n_q_heads][head_dim]. */
 ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out,
                             void *ws, size_t ws_bytes, ckv_stream_t stream);
+
+/* Kernel timing for profiling harnesses (no part of the method).  Arms the
+ * calling host thread so that the next kernel launched by one of
+ * ckv_score_centroids, ckv_select_communities, ckv_gather_attend,
+ * ckv_assign_update or ckv_dense_attend (each launches exactly one kernel)
+ * has `start` and `stop` recorded by its own dispatch (hipExtLaunchKernel):
+ * hipEventElapsedTime(start, stop) is then that kernel's execution time, with
+ * no marker packets around it.  One-shot: the launch consumes the pair.  A call
+ * that fails validation launches nothing and leaves the pair armed.  Both
+ * events must come from hipEventCreate (timing enabled) on the call's device;
+ * start == stop == NULL disarms.  Not for use under stream capture.
+ * Returns CKV_E_INVALID when exactly one of the two is NULL. */
+ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop);
 
 /* Static description of a status code. */
 const char *ckv_status_str(ckv_status s);

@@ -70,8 +70,9 @@ def test_workspace_bytes():
     a = _ws(kv, idx, 4100)
     dense = _ws(kv, None, 0)
     assert 0 < dense < a
-    # partials for 33 blocks x 32 graphs x 130 floats, the build cursor and the dense region
-    assert a >= dense + 4 * 32 * 33 * 130 + 4 * 32 * 8192
+    # partials of ceil(4100 / 256) = 17 gather blocks x 32 graphs, each 130 floats padded to 160
+    # (whole 128-byte lines), the build cursor and the dense region
+    assert a >= dense + 4 * 32 * 17 * 160 + 4 * 32 * 8192
     assert _ws(kv, idx, 8200) > a
     assert _ws(_kv(head_dim=96), idx, 4100) == 0
     assert _ws(kv, _idx(n_graphs=31), 4100) == 0
@@ -155,3 +156,16 @@ def test_binding_rejects_wrong_tensors():
     store.batch, store.n_q_heads, store.n_kv_heads, store.head_dim, store.dtype = 1, 4, 1, 64, torch.float32
     with pytest.raises(ValueError):
         ckv._need(torch.zeros(3, 64), "q", torch.float32, (1, 4, 64))
+
+
+def test_time_next_launch_arming():
+    f = ckv.LIB.ckv_time_next_launch
+    assert f(FAKE, None) == ckv.CKV_E_INVALID
+    assert f(None, FAKE) == ckv.CKV_E_INVALID
+    assert f(None, None) == ckv.CKV_OK
+    # armed events are only consumed by a launch; validation failures launch nothing
+    assert f(FAKE, FAKE) == ckv.CKV_OK
+    kv, idx = _kv(head_dim=96), _idx()
+    assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == \
+        ckv.CKV_E_UNSUPPORTED
+    assert f(None, None) == ckv.CKV_OK
