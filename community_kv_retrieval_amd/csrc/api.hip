@@ -74,6 +74,17 @@ int32_t ckv_trace_read(unsigned long long *host) {
     return hipMemcpyFromSymbol(host, HIP_SYMBOL(ckv::g_phase_trace), sizeof(unsigned long long) * 64) ==
                    hipSuccess ? 0 : -1;
 }
+
+// Profiling builds only: copy the per-block stamps of the first n blocks
+// (8 per block) to host memory, and clear them on the device.
+int32_t ckv_block_trace_read(unsigned long long *host, int32_t n) {
+    if (n < 0 || n > kBlockTraceBlocks) return -1;
+    const size_t bytes = sizeof(unsigned long long) * 8 * (size_t)n;
+    if (hipMemcpyFromSymbol(host, HIP_SYMBOL(ckv::g_block_trace), bytes) != hipSuccess) return -1;
+    void *dev = nullptr;
+    if (hipGetSymbolAddress(&dev, HIP_SYMBOL(ckv::g_block_trace)) != hipSuccess) return -1;
+    return hipMemset(dev, 0, bytes) == hipSuccess ? 0 : -1;
+}
 #endif
 
 const char *ckv_status_str(ckv_status s) {

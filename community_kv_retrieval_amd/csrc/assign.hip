@@ -10,7 +10,7 @@
 // key (weight bits, then inverted position) so that one unsigned compare
 // ranks it.  The kappa best keys are found without sorting all of them: a
 // lower bound taken from the per-lane maxima leaves a few dozen candidates,
-// which one wave orders exactly with repeated DPP max reductions.  Thread 0
+// each of which finds its exact rank by counting the better ones.  One wave
 // takes the majority label of the edges (lowest id on ties), then the block
 // appends the token to that community: label, tail entry, member count, the
 // exact float64 key sum and the float32 centroid column.  Graphs that own the
@@ -53,213 +53,231 @@ __device__ __forceinline__ unsigned long long edge_key(float w, int pos) {
     return ((unsigned long long)ordered_bits(w) << 32) | (0xFFFFFFFFu - (uint32_t)pos);
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+
 template <typename T, int D, int NH>
 __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
-    __shared__ unsigned long long s_tau[4];
+    constexpr int kIpt = 24;  // candidates per thread held in registers
     __shared__ unsigned long long s_cand[64];
-    __shared__ int s_ncand, s_ne;
+    __shared__ uint32_t s_tau[4];
+    __shared__ int s_ncand, s_ne, s_a;
     __shared__ int s_edges[CKV_MAX_KAPPA];
     __shared__ int s_elab[CKV_MAX_KAPPA];
-    __shared__ int s_a, s_newsize;
 
     const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     CKV_TMARK(30);
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
-    const int P = p.seq_len[gc.b];
-    const int n = p.tok_n[g];
     const int32_t *tl = p.tok_list + (size_t)g * p.t_cap;
-
+    // Everything this block reads first, issued together: nothing here waits
+    // for the token count (the list and the logits are t_cap long; entries at
+    // or past tok_n are masked afterwards).
+    const int n = p.tok_n[g];
+    const int P = p.seq_len[gc.b];
+    const int tn = p.tail_len[g];
+    const int topc = p.top[g];
     float M[NH], Linv[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
-        M[h] = p.ml[((size_t)g * NH + h) * 2];
-        Linv[h] = 1.f / p.ml[((size_t)g * NH + h) * 2 + 1];
+        M[h] = NH > 1 ? p.ml[((size_t)g * NH + h) * 2] : 0.f;
+        Linv[h] = NH > 1 ? 1.f / p.ml[((size_t)g * NH + h) * 2 + 1] : 0.f;
     }
-    auto weight = [&](int j) -> float {
-        if constexpr (NH == 1) {
-            return p.logits[(size_t)g * p.t_cap + j];
-        } else {
-            float w = 0.f;
+    const int jmax = min(p.t_cap, kIpt * 256);
+    int cp[kIpt];
+    float z[kIpt][NH];
 #pragma unroll
-            for (int h = 0; h < NH; ++h)
-                w += exp2f((p.logits[((size_t)g * NH + h) * p.t_cap + j] - M[h]) * kLog2e) * Linv[h];
-            return w;
-        }
-    };
+    for (int i = 0; i < kIpt; ++i) {
+        const int j = tid + i * 256;
+        const bool ok = j < jmax;
+        cp[i] = ok ? tl[j] : -1;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) z[i][h] = ok ? p.logits[((size_t)g * NH + h) * p.t_cap + j] : 0.f;
+    }
+    if (tid == 0) s_ncand = 0;
+
+    // The graph of the group's first query head appends the new key and value
+    // at position P; one wave does it while the others rank the edges.
+    const int cap = min(p.l_cap, p.max_pages << p.ps_log2);
+    const bool room = P < cap;
+    const bool owner = p.mode == CKV_MODE_QUERY_GROUP || (gc.qh0 % (p.Hq / p.Hkv)) == 0;
+    const T *kn = reinterpret_cast<const T *>(p.k_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
+    const T *vn = reinterpret_cast<const T *>(p.v_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
+    if (owner && room && wave == 3) {
+        const int page = p.page_table[(size_t)gc.b * p.max_pages + (P >> p.ps_log2)];
+        T *row = reinterpret_cast<T *>(p.kv) +
+                 ((((size_t)page * p.Hkv + gc.kh) << p.ps_log2) | (size_t)(P & ((1 << p.ps_log2) - 1))) * (2 * D);
+        for (int i = lane; i < 2 * D; i += 64) row[i] = i < D ? kn[i] : vn[i - D];
+    }
 
     // Candidates as 64-bit keys, (order-preserving bits of the weight) << 32 |
     // ~position, so the larger key is the better edge (larger weight, then
-    // lower position).  Up to kIpt per thread stay in registers.
-    constexpr int kIpt = 24;
+    // lower position).  With one head the logit orders the tokens as the
+    // probability does.
+    const bool inreg = n <= kIpt * 256;  // uniform
     unsigned long long ck[kIpt];
-    const bool inreg = n <= kIpt * 256;
-    {
-        int cp[kIpt];
-        float z[kIpt][NH];
 #pragma unroll
-        for (int i = 0; i < kIpt; ++i) {  // issue every load first
-            const int j = tid + i * 256;
-            const bool ok = inreg && j < n;
-            cp[i] = ok ? tl[j] : -1;
+    for (int i = 0; i < kIpt; ++i) {
+        const int j = tid + i * 256;
+        float w;
+        if constexpr (NH == 1) {
+            w = z[i][0];
+        } else {
+            w = 0.f;
 #pragma unroll
-            for (int h = 0; h < NH; ++h) z[i][h] = ok ? p.logits[((size_t)g * NH + h) * p.t_cap + j] : 0.f;
+            for (int h = 0; h < NH; ++h) w += exp2f((z[i][h] - M[h]) * kLog2e) * Linv[h];
         }
-#pragma unroll
-        for (int i = 0; i < kIpt; ++i) {
-            float w;
-            if constexpr (NH == 1) {
-                w = z[i][0];
-            } else {
-                w = 0.f;
-#pragma unroll
-                for (int h = 0; h < NH; ++h) w += exp2f((z[i][h] - M[h]) * kLog2e) * Linv[h];
-            }
-            ck[i] = cp[i] >= p.n_sinks ? edge_key(w, cp[i]) : 0ull;
-        }
+        ck[i] = (inreg && j < n && cp[i] >= p.n_sinks) ? edge_key(w, cp[i]) : 0ull;
     }
-
     CKV_TMARK(31);
-    // Lower bound on the kappa-th best key: in each wave, the kappa-th largest
-    // of the per-lane maxima (kappa keys of the wave reach it); the largest such
-    // bound of the four waves still has kappa keys at or above it.
+
+    // Lower bound on the kappa-th best weight: in each wave, kappa rounds of
+    // the largest remaining per-lane maximum (every round retires at least one
+    // lane, so kappa keys of the wave reach the last value); the largest bound
+    // of the four waves still has kappa keys at or above it.  No wave with
+    // kappa candidates: every candidate is kept.
     const int kappa = p.kappa;
-    unsigned long long tau = 0ull;
     if (inreg) {
-        unsigned long long lm = 0ull;
+        uint32_t lm = 0u;
 #pragma unroll
-        for (int i = 0; i < kIpt; ++i) lm = umax64(lm, ck[i]);
-        unsigned long long tw = 0ull;
+        for (int i = 0; i < kIpt; ++i) lm = max(lm, (uint32_t)(ck[i] >> 32));
+        uint32_t tw = 0u;
         int got = 0;
         for (int r = 0; r < kappa; ++r) {
-            const unsigned long long m = wave_max_u64(lm);
-            if (m == 0ull) break;
-            if (lm == m) lm = 0ull;
+            const uint32_t m = wave_max_u32(lm);
+            if (m == 0u) break;
+            if (lm == m) lm = 0u;
             tw = m;
             ++got;
         }
-        if (lane == 0) s_tau[wave] = got == kappa ? tw : 0ull;
-        if (tid == 0) s_ncand = 0;
+        if (lane == 0) s_tau[wave] = got == kappa ? tw : 0u;
         __syncthreads();
-        tau = umax64(umax64(s_tau[0], s_tau[1]), umax64(s_tau[2], s_tau[3]));
-        if (tau != 0ull) {
+        uint32_t tau = max(max(s_tau[0], s_tau[1]), max(s_tau[2], s_tau[3]));
+        if (tau == 0u) tau = 1u;
 #pragma unroll
-            for (int i = 0; i < kIpt; ++i) {
-                if (ck[i] >= tau) {
-                    const int k = atomicAdd(&s_ncand, 1);
-                    if (k < 64) s_cand[k] = ck[i];
-                }
+        for (int i = 0; i < kIpt; ++i) {
+            if (ck[i] != 0ull && (uint32_t)(ck[i] >> 32) >= tau) {
+                const int k = atomicAdd(&s_ncand, 1);
+                if (k < 64) s_cand[k] = ck[i];
             }
         }
         __syncthreads();
     }
     CKV_TMARK(32);
-    const bool fast = inreg && tau != 0ull && s_ncand <= 64;  // uniform
+    const int ncand = inreg ? s_ncand : 65;
+    const bool fast = ncand <= 64;  // uniform
 
-    int ne = 0;
     if (fast) {
-        if (wave == 0) {  // exact order among the few candidates, one per lane
-            unsigned long long c = lane < s_ncand ? s_cand[lane] : 0ull;
-            for (int r = 0; r < kappa; ++r) {
-                const unsigned long long m = wave_max_u64(c);
-                if (m == 0ull) break;
-                if (c == m) c = 0ull;
-                if (lane == 0) s_edges[r] = (int)(0xFFFFFFFFu - (uint32_t)m);
-                ++ne;
+        if (wave == 0) {
+            // Each candidate counts the better ones: its rank.  Its label load
+            // is in flight meanwhile.
+            const unsigned long long mine = lane < ncand ? s_cand[lane] : 0ull;
+            const int pos = (int)(0xFFFFFFFFu - (uint32_t)mine);
+            const int lab = lane < ncand ? p.label[(size_t)g * p.l_cap + pos] : -1;
+            int rank = 0;
+            for (int k = 0; k < ncand; ++k) rank += s_cand[k] > mine;
+            if (lane < ncand && rank < kappa) {
+                s_edges[rank] = pos;
+                s_elab[rank] = lab;
             }
+            if (lane == 0) s_ne = min(kappa, ncand);
         }
     } else if (wave == 0) {  // long token lists or degenerate weights: rounds over all tokens
         unsigned long long prev = ~0ull;
+        int ne = 0;
         for (int r = 0; r < kappa; ++r) {
             unsigned long long best = 0ull;
             for (int j = lane; j < n; j += 64) {
                 const int pos = tl[j];
                 if (pos < p.n_sinks) continue;
-                const unsigned long long k = edge_key(weight(j), pos);
+                float w;
+                if constexpr (NH == 1) {
+                    w = p.logits[(size_t)g * p.t_cap + j];
+                } else {
+                    w = 0.f;
+#pragma unroll
+                    for (int h = 0; h < NH; ++h)
+                        w += exp2f((p.logits[((size_t)g * NH + h) * p.t_cap + j] - M[h]) * kLog2e) * Linv[h];
+                }
+                const unsigned long long k = edge_key(w, pos);
                 if (k < prev && k > best) best = k;
             }
             best = wave_max_u64(best);
             if (best == 0ull) break;
-            if (lane == 0) s_edges[r] = (int)(0xFFFFFFFFu - (uint32_t)best);
+            const int pos = (int)(0xFFFFFFFFu - (uint32_t)best);
+            if (lane == 0) {
+                s_edges[r] = pos;
+                s_elab[r] = p.label[(size_t)g * p.l_cap + pos];
+            }
             prev = best;
             ++ne;
         }
+        if (lane == 0) s_ne = ne;
     }
-    if (wave == 0 && lane == 0) s_ne = ne;
     __syncthreads();
-    ne = s_ne;
+    const int ne = s_ne;
     CKV_TMARK(33);
 
-    const int cap = min(p.l_cap, p.max_pages << p.ps_log2);
-    const bool room = P < cap;
-    if (tid < ne) s_elab[tid] = p.label[(size_t)g * p.l_cap + s_edges[tid]];
-    const int tn = p.tail_len[g];
-    __syncthreads();
-    if (tid == 0) {
-        int best = -1, bestc = 0;
-        for (int r = 0; r < ne; ++r) {
-            const int c = s_elab[r];
-            if (c < 0) continue;
+    // Majority vote of the edges' labels, lowest id on ties: each edge counts
+    // its label's votes; the largest (votes, ~label) wins.  No labelled edge:
+    // the best-scoring community.
+    if (wave == 0) {
+        unsigned long long key = 0ull;
+        if (lane < ne) {
+            const int c = s_elab[lane];
             int k = 0;
-            for (int r2 = 0; r2 < ne; ++r2) k += (s_elab[r2] == c);
-            if (k > bestc || (k == bestc && c < best)) {
-                best = c;
-                bestc = k;
-            }
+            for (int r = 0; r < ne; ++r) k += s_elab[r] == c;
+            if (c >= 0) key = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)c);
         }
-        const int a = best >= 0 ? best : p.top[g];
-        for (int r = 0; r < p.kappa; ++r) p.edges[(size_t)g * p.kappa + r] = r < ne ? s_edges[r] : -1;
-        p.assign[g] = a;
-        int joined = -1;
-        if (!room) {
-            atomicOr(p.status, CKV_ST_CAPACITY);
-        } else if (a >= 0) {
-            if (tn < p.tail_cap) {
-                p.label[(size_t)g * p.l_cap + P] = a;
-                p.tail_pos[(size_t)g * p.tail_cap + tn] = P;
-                p.tail_comm[(size_t)g * p.tail_cap + tn] = a;
-                p.tail_len[g] = tn + 1;
-                s_newsize = p.size[(size_t)g * p.c_cap + a] + 1;
-                p.size[(size_t)g * p.c_cap + a] = s_newsize;
-                joined = a;
-            } else {
-                atomicOr(p.status, CKV_ST_TAIL_FULL);
-                p.label[(size_t)g * p.l_cap + P] = -1;
-            }
-        } else {
-            p.label[(size_t)g * p.l_cap + P] = -1;
+        key = wave_max_u64(key);
+        const int a = key ? (int)(0xFFFFFFFFu - (uint32_t)key) : topc;
+        if (lane < p.kappa) p.edges[(size_t)g * p.kappa + lane] = lane < ne ? s_edges[lane] : -1;  // kappa <= 32
+        if (lane == 0) {
+            p.assign[g] = a;
+            s_a = a;
         }
-        s_a = joined;
     }
     __syncthreads();
-
     CKV_TMARK(34);
-    const T *kn = reinterpret_cast<const T *>(p.k_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
-    const T *vn = reinterpret_cast<const T *>(p.v_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
+
+    // Append to the winning community: label, tail entry, member count, the
+    // float64 key sum and the float32 centroid column.
     const int a = s_a;
-    if (a >= 0 && tid < D) {
+    const bool join = room && a >= 0 && tn < p.tail_cap;  // uniform
+    int newsize = 0;
+    if (join && tid < D) {
+        newsize = p.size[(size_t)g * p.c_cap + a] + 1;
         const size_t ci = ((size_t)g * p.c_cap + a) * D + tid;
         const double cs = p.csum[ci] + (double)to_f32(kn[tid]);
         p.csum[ci] = cs;
-        p.cent[((size_t)g * D + tid) * p.c_cap + a] = (float)(cs / (double)s_newsize);
+        p.cent[((size_t)g * D + tid) * p.c_cap + a] = (float)(cs / (double)newsize);
     }
-    // The graph of the group's first query head stores the new key and value.
-    const bool owner = p.mode == CKV_MODE_QUERY_GROUP || (gc.qh0 % (p.Hq / p.Hkv)) == 0;
-    if (owner && room) {
-        const int page = p.page_table[(size_t)gc.b * p.max_pages + (P >> p.ps_log2)];
-        T *row = reinterpret_cast<T *>(p.kv) +
-                 ((((size_t)page * p.Hkv + gc.kh) << p.ps_log2) | (size_t)(P & ((1 << p.ps_log2) - 1))) * (2 * D);
-        for (int i = tid; i < 2 * D; i += 256) row[i] = i < D ? kn[i] : vn[i - D];
+    if (tid == 0) {
+        if (!room) {
+            atomicOr(p.status, CKV_ST_CAPACITY);
+        } else if (join) {
+            p.label[(size_t)g * p.l_cap + P] = a;
+            p.tail_pos[(size_t)g * p.tail_cap + tn] = P;
+            p.tail_comm[(size_t)g * p.tail_cap + tn] = a;
+            p.tail_len[g] = tn + 1;
+        } else {
+            if (a >= 0) atomicOr(p.status, CKV_ST_TAIL_FULL);
+            p.label[(size_t)g * p.l_cap + P] = -1;
+        }
     }
-
     CKV_TMARK(35);
+    // Every thread has read the member count above: only now may it change.
     // The last block advances every sequence with room by one token.  Every
     // block read seq_len before it counts itself in, so the increment cannot
     // race a read; the next kernel sees it across the kernel boundary.
     __syncthreads();
-    if (tid == 0 && arrive_last(p.ctr, p.G)) {
-        for (int bb = 0; bb < p.B; ++bb)
-            if (p.seq_len[bb] < cap) p.seq_len[bb] += 1;
-        reset_counter(p.ctr);
+    if (tid == 0) {
+        if (join) p.size[(size_t)g * p.c_cap + a] = newsize;
+        if (arrive_last(p.ctr, p.G)) {
+            for (int bb = 0; bb < p.B; ++bb)
+                if (p.seq_len[bb] < cap) p.seq_len[bb] += 1;
+            reset_counter(p.ctr);
+        }
     }
     CKV_TMARK(36);
 }

@@ -240,6 +240,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     const int unit = blockIdx.x / a.nchunk;
     const int chunk = blockIdx.x - unit * a.nchunk;
     if constexpr (!DENSE) CKV_TMARK(20);
+    if constexpr (!DENSE) CKV_BMARK(0);
 
     int b, kh, qh0, n;
     if constexpr (DENSE) {
@@ -285,6 +286,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     __syncthreads();
 
     if constexpr (!DENSE) CKV_TMARK(21);
+    if constexpr (!DENSE) CKV_BMARK(1);
     float qr[NH][E];
 #pragma unroll
     for (int h = 0; h < NH; ++h)
@@ -361,6 +363,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     }
 
     if constexpr (!DENSE) CKV_TMARK(22);
+    if constexpr (!DENSE) CKV_BMARK(2);
     // Merge the four token rows of the wave (lanes l16, l16+16, l16+32, l16+48).
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -421,6 +424,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         }
     }
     if constexpr (!DENSE) CKV_TMARK(23);
+    if constexpr (!DENSE) CKV_BMARK(3);
     if (nact == 1) return;
 
     // The last block of the unit merges every block's partial.
@@ -428,12 +432,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     __syncthreads();
     if (tid == 0) s_last = arrive_last(&a.ctr[unit], nact);
     __syncthreads();
+    if constexpr (!DENSE) CKV_BMARK(4);
     if (!s_last) return;
     merge_partials<D, NH, PS>(P, a.nchunk, nact, s_scale, s_red,
                               a.out + ((size_t)b * a.Hq + qh0) * D,
                               DENSE ? nullptr : a.ml + (size_t)unit * NH * 2);
     if (tid == 0) reset_counter(&a.ctr[unit]);
     if constexpr (!DENSE) CKV_TMARK(24);
+    if constexpr (!DENSE) CKV_BMARK(5);
 }
 
 template <typename T, int D, int NH, bool DENSE>

@@ -22,8 +22,25 @@ __device__ unsigned long long g_phase_trace[64];
         if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)    \
             ::ckv::g_phase_trace[(s)] = __builtin_amdgcn_s_memrealtime(); \
     } while (0)
+// Per-block stamps of one kernel (slots 0..6 of block blockIdx.x; slot 7 holds
+// the hardware id registers of the wave that stamps).
+constexpr int kBlockTraceBlocks = 16384;
+__device__ unsigned long long g_block_trace[kBlockTraceBlocks * 8];
+#define CKV_BMARK(s)                                                                        \
+    do {                                                                                    \
+        if (threadIdx.x == 0 && blockIdx.x < ::ckv::kBlockTraceBlocks) {                    \
+            ::ckv::g_block_trace[blockIdx.x * 8 + (s)] = __builtin_amdgcn_s_memrealtime();  \
+            if ((s) == 0)                                                                   \
+                ::ckv::g_block_trace[blockIdx.x * 8 + 7] =                                  \
+                    ((unsigned long long)__builtin_amdgcn_s_getreg((31 << 11) | 20) << 32) | \
+                    __builtin_amdgcn_s_getreg((31 << 11) | 4);                              \
+        }                                                                                   \
+    } while (0)
 #else
 #define CKV_TMARK(s) \
+    do {             \
+    } while (0)
+#define CKV_BMARK(s) \
     do {             \
     } while (0)
 #endif
@@ -171,6 +188,20 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
     return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 
+// Wave-wide inclusive prefix sum (lane i gets v_0 + ... + v_i), all lanes
+// active: shifts by 1, 2, 4 and 8 lanes inside each row of 16 (lanes shifted in
+// from outside the row add 0), then row_bcast:15 adds the last lane of rows 0
+// and 2 to rows 1 and 3, and row_bcast:31 adds lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return x;
+}
+
 // Order-preserving map of a float32 onto uint32 (larger float, larger code).
 __device__ __forceinline__ uint32_t ordered_bits(float s) {
     const uint32_t u = __float_as_uint(s);
@@ -240,35 +271,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int *to
     __syncthreads();
     *total = scratch[NW];
     return scratch[wave] + x - v;
-}
-
-// Block-wide inclusive prefix maximum of one int per thread (same shape and
-// barriers as block_exclusive_scan).
-template <int NT>
-__device__ __forceinline__ int block_inclusive_max(int v, int *scratch) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x = max(x, y);
-    }
-    if (lane == 63) scratch[wave] = x;
-    __syncthreads();
-    if (wave == 0) {  // exclusive max-scan of the wave results
-        const int t = lane < NW ? scratch[lane] : INT_MIN;
-        int ti = t;
-#pragma unroll
-        for (int o = 1; o < NW; o <<= 1) {
-            const int y = __shfl_up(ti, o, 64);
-            if (lane >= o) ti = max(ti, y);
-        }
-        const int ex = __shfl_up(ti, 1, 64);
-        if (lane < NW) scratch[lane] = lane == 0 ? INT_MIN : ex;
-    }
-    __syncthreads();
-    return max(scratch[wave], x);
 }
 
 // Coordinates of graph g: sequence, kv head, first query head, query heads.

@@ -1,12 +1,14 @@
 // Budgeted community retrieval (the CommunityKV page, Figure 1 panel (3):
 // retrieve a candidate subset of communities under a token budget).
 //
-// One 1024-thread block per graph; thread t owns the EPT consecutive
-// communities t*EPT ... .  Communities rank by float32 score, higher first,
-// ties to the lower id; as one number that is the 64-bit key
-// (order-preserving bits of the score) << 32 | (~id).  The taken set is the
-// longest prefix of the ranking that fits the budget, i.e. every key above the
-// key of the first community that overflows it (the cut).
+// One 1024-thread block per graph.  The communities are read in slabs of 4096:
+// in slab j thread t owns communities 4096 j + 4 t .. 4096 j + 4 t + 3, so
+// every 16-byte load of a wave covers 1 KB of consecutive memory.
+// Communities rank by float32 score, higher first, ties to the lower id; as
+// one number that is the 64-bit key (order-preserving bits of the score) << 32
+// | (~id).  The taken set is the longest prefix of the ranking that fits the
+// budget, i.e. every key above the key of the first community that overflows
+// it (the cut).
 //
 // The whole graph runs on one CU, so the passes over every community use
 // 32-bit arithmetic only.  The cut is found in two steps: a token-weighted
@@ -20,10 +22,12 @@
 // token-weighted digit histograms, finds the same cut.  The community cap
 // (max_comm) is the same radix select with unit weights.
 //
-// Then the taken ids are compacted in ascending id order with block scans, and
-// the attended token list is written: sinks, the base members of every taken
-// community, then the taken communities' tail members.  Sizes, scores, CSR
-// offsets and tail entries are read at the start with 16-byte loads.
+// Then one block scan over per-slab counts gives every taken community its
+// rank in ascending id order and its first slot in the token list, and every
+// taken tail entry its slot after them.  The list is written as sinks, the base
+// members of every taken community (each slot finds its community by binary
+// search over the communities' first slots), then the taken tail members in
+// tail order.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -31,12 +35,10 @@ namespace ckv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kBins = kSelThreads;
-// Member slots mapped to their community in LDS (the common case); longer
-// lists binary-search the communities' first slots (up to kSelLds
-// communities), and more communities than that are copied one thread each.
-constexpr int kSelSlots = 4096;
-constexpr int kSelLds = 2048;
-constexpr int kSlotsPerThread = kSelSlots / kSelThreads;
+constexpr int kSlab = 4 * kSelThreads;  // communities per slab
+// Taken communities whose first slots are kept in LDS for the binary-search
+// copy; more than that are copied one thread per community.
+constexpr int kSelLds = 4096;
 constexpr int kTailPerThread = 4;  // tail_cap <= 4096
 
 struct SelectParams {
@@ -58,9 +60,8 @@ struct SelectParams {
 };
 
 struct SelShared {
-    int owner[kSelSlots];    // member slot -> index of its taken community
     int soff[kSelLds];       // first base member in toks of the k-th taken community
-    int spref[kSelLds + 1];  // its first slot in the token list (after the sinks)
+    int spref[kSelLds];      // its first slot in the token list (after the sinks)
     int bw[kBins];           // token weight per score bin
     uint32_t hw[256];        // radix select: token weight per digit
     uint32_t hn[256];        // radix select: candidates per digit
@@ -69,7 +70,7 @@ struct SelShared {
     int csz[64];
     int ccount;
     int cut_bin, cut_above;
-    int scan[kSelThreads / 64 + 1];
+    int scan[(kSelThreads / 64 + 1) * 9];
     float red_lo[kSelThreads / 64], red_hi[kSelThreads / 64];
     uint32_t red_id[kSelThreads / 64];
     unsigned long long prefix, mask, thr;
@@ -79,6 +80,40 @@ struct SelShared {
 
 __device__ __forceinline__ unsigned long long comm_key(float s, int c) {
     return ((unsigned long long)ordered_bits(s) << 32) | (0xFFFFFFFFu - (uint32_t)c);
+}
+
+// Community id of element e (0 .. 4 NS - 1) of thread tid.
+__device__ __forceinline__ int slab_id(int tid, int e) { return (e >> 2) * kSlab + 4 * tid + (e & 3); }
+
+// Block-wide exclusive prefix sums of NV ints per thread, in thread order, and
+// their totals (two barriers; `scratch` holds (NT/64 + 1) * NV ints).
+template <int NT, int NV>
+__device__ __forceinline__ void block_scan_multi(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], int *scratch) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) x[k] = wave_incl_scan(v[k]);
+    if (lane == 63) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) scratch[wave * NV + k] = x[k];
+    }
+    __syncthreads();
+    if (wave == 0) {  // scan of the wave totals
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int t = lane < NW ? scratch[lane * NV + k] : 0;
+            const int ti = wave_incl_scan(t);
+            if (lane < NW) scratch[lane * NV + k] = ti - t;
+            if (lane == NW - 1) scratch[NW * NV + k] = ti;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        tot[k] = scratch[NW * NV + k];
+        ex[k] = scratch[wave * NV + k] + x[k] - v[k];
+    }
 }
 
 // Threshold key of the budget cut by radix select over the 64-bit keys: the
@@ -92,7 +127,7 @@ __device__ unsigned long long radix_cut(const float (&sv)[EPT], const int (&w)[E
     unsigned long long kmax = 0ull, kmin = ~0ull;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        key[j] = w[j] > 0 ? comm_key(sv[j], tid * EPT + j) : 0ull;
+        key[j] = w[j] > 0 ? comm_key(sv[j], slab_id(tid, j)) : 0ull;
         if (key[j]) {
             kmax = umax64(kmax, key[j]);
             kmin = umin64(kmin, key[j]);
@@ -186,17 +221,15 @@ __device__ unsigned long long radix_cut(const float (&sv)[EPT], const int (&w)[E
     }
 }
 
-// Budget cut through equal-width score bins (see the file comment).  Returns
-// false, uniformly across the block, when the radix select has to decide.
+// Budget cut through equal-width score bins (see the file comment).  The bin
+// weights and the candidate count must be zero on entry.  Returns false,
+// uniformly across the block, when the radix select has to decide.
 template <int EPT>
 __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budget, float lo, float hi,
                           SelShared &sh, unsigned long long &thr) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float scale = (float)kBins / (hi - lo);
     if (!(hi > lo) || !(scale < __builtin_huge_valf())) return false;
-    sh.bw[tid] = 0;
-    if (tid == 0) sh.ccount = 0;
-    __syncthreads();
     int bin[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
@@ -217,12 +250,7 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
             v[k] = sh.bw[kBins - 1 - (lane * 16 + k)];
             tot += v[k];
         }
-        int incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(tot);
         int acc = incl - tot, found = -1, above = 0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -244,7 +272,6 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
     const int cb = sh.cut_bin, above = sh.cut_above;
     if (cb < 0) {
         thr = 0ull;
-        __syncthreads();
         return true;
     }
 #pragma unroll
@@ -252,7 +279,7 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
         if (bin[j] == cb) {
             const int i = atomicAdd(&sh.ccount, 1);
             if (i < 64) {
-                sh.ckey[i] = comm_key(sv[j], tid * EPT + j);
+                sh.ckey[i] = comm_key(sv[j], slab_id(tid, j));
                 sh.csz[i] = w[j];
             }
         }
@@ -282,25 +309,20 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
                 }
             }
         }
-        int incl = sz;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(sz);
         const unsigned long long bal = __ballot(lane < cnt && above + incl > budget);
         const int first = bal ? __ffsll((long long)bal) - 1 : 0;
         const unsigned long long cut = ~__shfl(nk, first, 64);
         if (lane == 0) sh.thr = cut;
     }
     __syncthreads();
-    thr = sh.thr;
-    __syncthreads();
+    thr = sh.thr;  // sh.thr is written once per kernel: no barrier needed after the read
     return true;
 }
 
-template <int EPT>
+template <int NS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
+    constexpr int EPT = 4 * NS;
     __shared__ SelShared sh;
     const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     CKV_TMARK(10);
@@ -314,50 +336,51 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     const int32_t *offs = p.offs + (size_t)g * offs_stride(C);
     int32_t *tl = p.tok_list + (size_t)g * p.t_cap;
 
-    // Sizes, scores and CSR offsets of this thread's EPT consecutive
-    // communities, 16 bytes per load, and the tail entries.
-    static_assert(EPT % 4 == 0, "EPT must be a multiple of 4");
+    // Sizes, scores and CSR offsets of this thread's four communities of every
+    // slab, 16 bytes per load, and the tail entries.  c0 % 4 == 0 and C % 256
+    // == 0, so a 16-byte load from c0 < C stays inside the row and offs[c0 + 4]
+    // exists (the offsets row holds C + 4 entries).  Entries at or past n_comm
+    // are masked after the loads.
     int s[EPT], o0[EPT], o1[EPT];
     float sv[EPT];
     {
-        // c % 4 == 0 and C % 256 == 0: a 16-byte load from c < C stays inside
-        // the row (the offsets row holds C + 4 entries).  Nothing waits for
-        // n_comm: entries at or past it are masked below.
-        int4 s4[EPT / 4], o4[EPT / 4];
-        float4 v4[EPT / 4];
-        int olast = 0;
+        int4 s4[NS], o4[NS];
+        float4 v4[NS];
+        int on[NS];
 #pragma unroll
-        for (int j = 0; j < EPT; j += 4) {
-            const int c = tid * EPT + j;
-            s4[j / 4] = make_int4(0, 0, 0, 0);
-            o4[j / 4] = make_int4(0, 0, 0, 0);
-            v4[j / 4] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (c < C) {
-                s4[j / 4] = *reinterpret_cast<const int4 *>(sz + c);
-                v4[j / 4] = *reinterpret_cast<const float4 *>(sc + c);
-                o4[j / 4] = *reinterpret_cast<const int4 *>(offs + c);
+        for (int j = 0; j < NS; ++j) {
+            const int c0 = j * kSlab + 4 * tid;
+            s4[j] = make_int4(0, 0, 0, 0);
+            o4[j] = make_int4(0, 0, 0, 0);
+            v4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            on[j] = 0;
+            if (c0 < C) {
+                s4[j] = *reinterpret_cast<const int4 *>(sz + c0);
+                v4[j] = *reinterpret_cast<const float4 *>(sc + c0);
+                o4[j] = *reinterpret_cast<const int4 *>(offs + c0);
+                on[j] = offs[c0 + 4];
             }
         }
-        if (tid * EPT + EPT <= C) olast = offs[tid * EPT + EPT];
 #pragma unroll
-        for (int j = 0; j < EPT; j += 4) {
-            const int c = tid * EPT + j;
-            s[j] = c < nc ? s4[j / 4].x : 0;
-            s[j + 1] = c + 1 < nc ? s4[j / 4].y : 0;
-            s[j + 2] = c + 2 < nc ? s4[j / 4].z : 0;
-            s[j + 3] = c + 3 < nc ? s4[j / 4].w : 0;
-            sv[j] = v4[j / 4].x;
-            sv[j + 1] = v4[j / 4].y;
-            sv[j + 2] = v4[j / 4].z;
-            sv[j + 3] = v4[j / 4].w;
-            o0[j] = o4[j / 4].x;
-            o0[j + 1] = o4[j / 4].y;
-            o0[j + 2] = o4[j / 4].z;
-            o0[j + 3] = o4[j / 4].w;
+        for (int j = 0; j < NS; ++j) {
+            const int c0 = j * kSlab + 4 * tid;
+            s[4 * j] = c0 < nc ? s4[j].x : 0;
+            s[4 * j + 1] = c0 + 1 < nc ? s4[j].y : 0;
+            s[4 * j + 2] = c0 + 2 < nc ? s4[j].z : 0;
+            s[4 * j + 3] = c0 + 3 < nc ? s4[j].w : 0;
+            sv[4 * j] = v4[j].x;
+            sv[4 * j + 1] = v4[j].y;
+            sv[4 * j + 2] = v4[j].z;
+            sv[4 * j + 3] = v4[j].w;
+            o0[4 * j] = o4[j].x;
+            o0[4 * j + 1] = o4[j].y;
+            o0[4 * j + 2] = o4[j].z;
+            o0[4 * j + 3] = o4[j].w;
+            o1[4 * j] = o4[j].y;
+            o1[4 * j + 1] = o4[j].z;
+            o1[4 * j + 2] = o4[j].w;
+            o1[4 * j + 3] = on[j];
         }
-#pragma unroll
-        for (int j = 0; j + 1 < EPT; ++j) o1[j] = o0[j + 1];
-        o1[EPT - 1] = olast;
     }
     const int tn = p.tail_len[g];
     int tcomm[kTailPerThread], tpos[kTailPerThread];
@@ -369,7 +392,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         tpos[j] = in ? p.tail_pos[(size_t)g * p.tail_cap + i] : 0;
     }
 
+    // LDS state the cut starts from, cleared under the first barrier below.
     for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
+    sh.bw[tid] = 0;
+    if (tid == 0) sh.ccount = 0;
 
     // Score range of the non-empty communities.
     float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
@@ -394,14 +420,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         hi = fmaxf(hi, sh.red_hi[i]);
     }
     const bool any = hi >= lo;  // uniform: some community is non-empty
-    // Best-ranked community: the lowest id among those scoring hi.
+    // Best-ranked community: the lowest id among those scoring hi (read by
+    // thread 0 at the end, after several barriers).
     uint32_t best = 0xFFFFFFFFu;
 #pragma unroll
     for (int j = 0; j < EPT; ++j)
-        if (s[j] > 0 && sv[j] == hi) best = min(best, (uint32_t)(tid * EPT + j));
+        if (s[j] > 0 && sv[j] == hi) best = min(best, (uint32_t)slab_id(tid, j));
     best = wave_min_u32(best);
     if (lane == 0) sh.red_id[wave] = best;
-    __syncthreads();
     CKV_TMARK(11);
 
     unsigned long long thr = ~0ull;  // nothing taken when there is no candidate
@@ -414,114 +440,110 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     // taken <=> key > thr, tested in 32-bit pieces
     const uint32_t thr_u = (uint32_t)(thr >> 32), thr_id = 0xFFFFFFFFu - (uint32_t)thr;
     bool taken[EPT];
-    int nloc = 0, tokloc = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const uint32_t u = ordered_bits(sv[j]), c = (uint32_t)(tid * EPT + j);
+        const uint32_t u = ordered_bits(sv[j]), c = (uint32_t)slab_id(tid, j);
         taken[j] = s[j] > 0 && (u > thr_u || (u == thr_u && c < thr_id));
-        if (taken[j]) {
-            ++nloc;
-            tokloc += o1[j] - o0[j];
-        }
+        if (taken[j]) atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
     }
-    int nsel, ntok;
-    int kpos = block_exclusive_scan<kSelThreads>(nloc, sh.scan, &nsel);
     __syncthreads();
-    int dst = ns + block_exclusive_scan<kSelThreads>(tokloc, sh.scan, &ntok);
-    __syncthreads();
-    CKV_TMARK(13);
-    const int32_t *toks = p.toks + (size_t)g * p.l_cap;
-    const int mode = nsel > kSelLds ? 2 : (ntok <= kSelSlots ? 0 : 1);  // uniform
-    if (mode == 0)
-        for (int j = tid; j < ntok; j += kSelThreads) sh.owner[j] = -1;
-    __syncthreads();
+    // Per slab: taken communities and their base members; then taken tail entries.
+    constexpr int NV = 2 * NS + 1;
+    int v[NV], ex[NV], tot[NV];
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        if (taken[j]) {
-            const int c = tid * EPT + j;
-            const int rel = dst - ns, len = o1[j] - o0[j];
-            p.sel[(size_t)g * C + kpos] = c;
-            atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
-            if (mode < 2) {
-                sh.soff[kpos] = o0[j];
-                sh.spref[kpos] = rel;
-                if (mode == 0 && len > 0) sh.owner[rel] = kpos;  // first slot of the community
-            } else {
-                for (int i = 0; i < len; ++i) tl[dst + i] = toks[o0[j] + i];
+    for (int j = 0; j < NS; ++j) {
+        v[j] = 0;
+        v[NS + j] = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (taken[4 * j + k]) {
+                v[j] += 1;
+                v[NS + j] += o1[4 * j + k] - o0[4 * j + k];
             }
-            dst += len;
-            ++kpos;
         }
     }
-    if (tid == 0 && mode == 1) sh.spref[nsel] = ntok;
+    int f[kTailPerThread];
+    v[2 * NS] = 0;
+#pragma unroll
+    for (int j = 0; j < kTailPerThread; ++j) {
+        const int i = tid * kTailPerThread + j;
+        const int c = tcomm[j];
+        f[j] = (i < tn && c >= 0 && c < C && ((sh.bits[c >> 5] >> (c & 31)) & 1u)) ? 1 : 0;
+        v[2 * NS] += f[j];
+    }
+    block_scan_multi<kSelThreads, NV>(v, ex, tot, sh.scan);
+    int nsel = 0, ntok = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        nsel += tot[j];
+        ntok += tot[NS + j];
+    }
+    const int ntail = tot[2 * NS];
+    CKV_TMARK(13);
+
+    const int32_t *toks = p.toks + (size_t)g * p.l_cap;
+    const bool lds_copy = nsel <= kSelLds;  // uniform
+    {
+        int kbase = 0, tbase = 0;
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            int kpos = kbase + ex[j], rel = tbase + ex[NS + j];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = 4 * j + k;
+                if (taken[e]) {
+                    const int len = o1[e] - o0[e];
+                    p.sel[(size_t)g * C + kpos] = slab_id(tid, e);
+                    if (lds_copy) {
+                        sh.soff[kpos] = o0[e];
+                        sh.spref[kpos] = rel;
+                    } else {
+                        for (int i = 0; i < len; ++i) tl[ns + rel + i] = toks[o0[e] + i];
+                    }
+                    rel += len;
+                    ++kpos;
+                }
+            }
+            kbase += tot[j];
+            tbase += tot[NS + j];
+        }
+    }
     for (int i = tid; i < ns; i += kSelThreads) tl[i] = i;
+    // Taken tail members, in tail order, after the base members.
+    {
+        int tdst = ns + ntok + ex[2 * NS];
+#pragma unroll
+        for (int j = 0; j < kTailPerThread; ++j)
+            if (f[j]) tl[tdst++] = tpos[j];
+    }
     __syncthreads();
     CKV_TMARK(14);
-    if (mode == 0) {
-        // every slot takes the owner of the nearest marked slot at or before it:
-        // an inclusive prefix max over kSlotsPerThread consecutive slots per thread
-        int ow[kSlotsPerThread], run = -1;
-#pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
-            const int j = tid * kSlotsPerThread + u;
-            ow[u] = j < ntok ? sh.owner[j] : -1;
-            run = max(run, ow[u]);
-            ow[u] = run;
-        }
-        const int before = block_inclusive_max<kSelThreads>(run, sh.scan);
-        const int carry = __shfl_up(before, 1, 64);
-        int prev = (tid & 63) ? carry : -1;
-        if ((tid & 63) == 0 && tid > 0) prev = sh.scan[(tid >> 6)];  // max over earlier waves
-        int v[kSlotsPerThread];
-#pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
-            const int j = tid * kSlotsPerThread + u;
-            const int k = max(prev, ow[u]);
-            v[u] = j < ntok ? toks[sh.soff[k] + (j - sh.spref[k])] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < kSlotsPerThread; ++u) {
-            const int j = tid * kSlotsPerThread + u;
-            if (j < ntok) tl[ns + j] = v[u];
-        }
-    } else if (mode == 1) {
+    if (lds_copy) {
+        // Slot j belongs to the last taken community whose first slot is <= j.
         for (int j0 = 0; j0 < ntok; j0 += 4 * kSelThreads) {
-            int v[4], at[4];
+            int val[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + u * kSelThreads + tid;
-                at[u] = j;
-                if (j < ntok) {  // the last taken community whose first slot is <= j
+                val[u] = 0;
+                if (j < ntok) {
                     int a = 0, b = nsel - 1;
                     while (a < b) {
                         const int mid = (a + b + 1) >> 1;
                         if (sh.spref[mid] <= j) a = mid;
                         else b = mid - 1;
                     }
-                    v[u] = toks[sh.soff[a] + (j - sh.spref[a])];
+                    val[u] = toks[sh.soff[a] + (j - sh.spref[a])];
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (at[u] < ntok) tl[ns + at[u]] = v[u];
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + u * kSelThreads + tid;
+                if (j < ntok) tl[ns + j] = val[u];
+            }
         }
     }
     CKV_TMARK(15);
-
-    // Tail members of taken communities, in tail order.
-    int f[kTailPerThread], floc = 0;
-#pragma unroll
-    for (int j = 0; j < kTailPerThread; ++j) {
-        const int i = tid * kTailPerThread + j;
-        const int c = tcomm[j];
-        f[j] = (i < tn && c >= 0 && c < C && ((sh.bits[c >> 5] >> (c & 31)) & 1u)) ? 1 : 0;
-        floc += f[j];
-    }
-    int ntail;
-    int tdst = ns + ntok + block_exclusive_scan<kSelThreads>(floc, sh.scan, &ntail);
-#pragma unroll
-    for (int j = 0; j < kTailPerThread; ++j)
-        if (f[j]) tl[tdst++] = tpos[j];
 
     if (tid == 0) {
         uint32_t b = 0xFFFFFFFFu;
@@ -561,12 +583,12 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *sc
     p.top = top;
     p.tok_list = tok_list;
     p.tok_n = tok_n;
-    const int ept = ceil_div(idx->c_cap, kSelThreads);
+    const int ns = ceil_div(idx->c_cap, kSlab);
     const dim3 grid(idx->n_graphs), block(kSelThreads);
-    if (ept <= 4) CKV_LAUNCH((select_kernel<4>), grid, block, s, p);
-    else if (ept <= 8) CKV_LAUNCH((select_kernel<8>), grid, block, s, p);
-    else if (ept <= 12) CKV_LAUNCH((select_kernel<12>), grid, block, s, p);
-    else CKV_LAUNCH((select_kernel<16>), grid, block, s, p);
+    if (ns <= 1) CKV_LAUNCH((select_kernel<1>), grid, block, s, p);
+    else if (ns <= 2) CKV_LAUNCH((select_kernel<2>), grid, block, s, p);
+    else if (ns <= 3) CKV_LAUNCH((select_kernel<3>), grid, block, s, p);
+    else CKV_LAUNCH((select_kernel<4>), grid, block, s, p);
     return hipGetLastError();
 }
 
