@@ -45,6 +45,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama31_8b_128k")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--windows", type=int, default=1,
+                    help="graph windows per step, each on its own stream (1 = one launch per call)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -76,6 +78,7 @@ def main():
     slices = synth.gen_layer(w, args.seed)
     layer = runner.load_layer(w, args.seed, extra=total + 1, slices=slices)
     dec, buf, idx, kv = layer.dec, layer.dec.buf, layer.idx, layer.kv
+    dec.set_windows(args.windows)
     steps_in = [synth.gen_step(w, args.seed, t, slices) for t in range(total)]
     Q = torch.stack([s.q for s in steps_in]).cuda()
     KN = torch.stack([s.k_new for s in steps_in]).cuda()
@@ -248,7 +251,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": w.n_ctx, "budget": w.budget, "kappa": w.kappa,
                    "graphs": "per_query_head" if w.mode == synth.PER_HEAD else "query_group",
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-                   "kv_dtype": w.dtype, "n_graphs": idx.n_graphs, "seed": args.seed},
+                   "kv_dtype": w.dtype, "n_graphs": idx.n_graphs, "seed": args.seed,
+                   "windows": dec.windows},
         "gathered_kv_gbps": round(gather_gbps, 1),
         "gathered_kv_frac_of_hbm": round(gather_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "gather_attend", "achieved": round(gather_gbps, 1),

@@ -12,6 +12,7 @@ header documents.
 """
 from __future__ import annotations
 
+import copy
 import ctypes
 import math
 import os
@@ -51,7 +52,8 @@ class CkvIndex(ctypes.Structure):
                 ("tail_cap", c_int32), ("n_sinks", c_int32),
                 ("n_comm", c_void_p), ("size", c_void_p), ("offs", c_void_p), ("toks", c_void_p),
                 ("label", c_void_p), ("tail_pos", c_void_p), ("tail_comm", c_void_p),
-                ("tail_len", c_void_p), ("csum", c_void_p), ("cent", c_void_p), ("status", c_void_p)]
+                ("tail_len", c_void_p), ("csum", c_void_p), ("cent", c_void_p), ("status", c_void_p),
+                ("win_first", c_int32), ("win_count", c_int32)]
 
 
 def _load():
@@ -170,6 +172,16 @@ class CommunityIndex:
 
     def heads_per_graph(self, kv: KVStore) -> int:
         return 1 if self.mode == CKV_MODE_PER_HEAD else kv.group
+
+    def window(self, first: int, count: int) -> "CommunityIndex":
+        """The same index (shared state), with the four step calls restricted to
+        graphs first .. first + count - 1."""
+        if not (0 <= first and 0 < count and first + count <= self.n_graphs):
+            raise ValueError(f"window [{first}, {first + count}) outside the {self.n_graphs} graphs")
+        v = copy.copy(self)
+        v.desc = CkvIndex.from_buffer_copy(self.desc)
+        v.desc.win_first, v.desc.win_count = first, count
+        return v
 
     STATE = ("size", "offs", "toks", "label", "tail_pos", "tail_comm", "tail_len", "csum", "cent", "status")
 
@@ -305,13 +317,31 @@ class DecodeBuffers:
 
 
 class Decoder:
-    """Runs CommunityKV decode steps for one layer on the current stream."""
+    """Runs CommunityKV decode steps for one layer.
+
+    With windows > 1 a step splits the graphs into that many windows, each run
+    on a stream of its own, window w scoring after window w - 1 has scored: the
+    later windows' bandwidth-bound scoring and gathering then overlap the
+    earlier windows' latency-bound selection and assignment.  The results are
+    the same as with one window (every graph's work is unchanged).
+    """
 
     def __init__(self, kv: KVStore, idx: CommunityIndex, budget: int, max_comm: int, kappa: int,
-                 sm_scale: float, device="cuda"):
+                 sm_scale: float, device="cuda", windows: int = 1):
         self.kv, self.idx = kv, idx
         self.budget, self.max_comm, self.kappa, self.sm_scale = budget, max_comm, kappa, sm_scale
         self.buf = DecodeBuffers(kv, idx, budget, kappa, device)
+        self.set_windows(windows)
+
+    def set_windows(self, windows: int):
+        G = self.idx.n_graphs
+        windows = max(1, min(int(windows), G))
+        self.windows = windows
+        self._views, self._streams = [], []
+        if windows > 1:
+            bounds = [G * w // windows for w in range(windows + 1)]
+            self._views = [self.idx.window(bounds[w], bounds[w + 1] - bounds[w]) for w in range(windows)]
+            self._streams = [torch.cuda.Stream() for _ in range(windows)]
 
     def build(self, labels_in: torch.Tensor, stream=None):
         ckv_index_build(self.kv, self.idx, labels_in, self.buf.ws, stream)
@@ -333,10 +363,34 @@ class Decoder:
                           b.edges, b.assign, b.ws, stream)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
-        self.retrieve(q, stream)
-        self.attend(q, stream)
-        self.update(k_new, v_new, stream)
-        return self.buf.out
+        if self.windows == 1:
+            self.retrieve(q, stream)
+            self.attend(q, stream)
+            self.update(k_new, v_new, stream)
+            return self.buf.out
+        b, kv = self.buf, self.kv
+        cur = torch.cuda.current_stream() if stream is None else stream
+        start = torch.cuda.Event()
+        start.record(cur)
+        prev = None
+        for view, s in zip(self._views, self._streams):
+            s.wait_event(start)
+            if prev is not None:
+                s.wait_event(prev)
+            for t in (q, k_new, v_new):
+                t.record_stream(s)
+            ckv_score_centroids(kv, view, q, b.scores, s)
+            prev = torch.cuda.Event()
+            prev.record(s)
+            ckv_select_communities(kv, view, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
+                                   b.tok_list, b.tok_n, s)
+            ckv_gather_attend(kv, view, q, b.tok_list, b.tok_n, self.sm_scale, b.out, b.logits, b.ml, b.ws, s)
+            ckv_assign_update(kv, view, b.tok_list, b.tok_n, b.logits, b.ml, b.top, self.kappa, k_new, v_new,
+                              b.edges, b.assign, b.ws, s)
+            done = torch.cuda.Event()
+            done.record(s)
+            cur.wait_event(done)
+        return b.out
 
     def dense(self, q: torch.Tensor, out: torch.Tensor, stream=None):
         ckv_dense_attend(self.kv, q, self.sm_scale, out, self.buf.ws, stream)

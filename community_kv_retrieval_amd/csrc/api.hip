@@ -44,6 +44,9 @@ ckv_status check_index(const ckv_kv *kv, const ckv_index *idx) {
     if (!idx->n_comm || !idx->size || !idx->offs || !idx->toks || !idx->label || !idx->tail_pos ||
         !idx->tail_comm || !idx->tail_len || !idx->csum || !idx->cent || !idx->status)
         return CKV_E_INVALID;
+    if (idx->win_count < 0 || idx->win_first < 0) return CKV_E_INVALID;
+    if (idx->win_count == 0 ? idx->win_first != 0 : (long long)idx->win_first + idx->win_count > G)
+        return CKV_E_INVALID;
     return CKV_OK;
 }
 
@@ -60,7 +63,7 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 2; }
+int32_t ckv_abi_version(void) { return 3; }
 
 ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;

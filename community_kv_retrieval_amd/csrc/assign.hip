@@ -26,7 +26,7 @@ struct AssignParams {
     const int32_t *page_table;
     int32_t *seq_len;
     int B, Hq, Hkv, ps_log2, max_pages;
-    int mode, G, c_cap, l_cap, tail_cap, n_sinks, t_cap, kappa;
+    int mode, G, g0, c_cap, l_cap, tail_cap, n_sinks, t_cap, kappa;
     int32_t *size;
     int32_t *label;
     int32_t *tail_pos;
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     __shared__ int s_edges[CKV_MAX_KAPPA];
     __shared__ int s_elab[CKV_MAX_KAPPA];
 
-    const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     CKV_TMARK(30);
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
     const int32_t *tl = p.tok_list + (size_t)g * p.t_cap;
@@ -175,7 +175,13 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
             const int pos = (int)(0xFFFFFFFFu - (uint32_t)mine);
             const int lab = lane < ncand ? p.label[(size_t)g * p.l_cap + pos] : -1;
             int rank = 0;
-            for (int k = 0; k < ncand; ++k) rank += s_cand[k] > mine;
+            for (int k0 = 0; k0 < ncand; k0 += 8) {  // k0 + 7 < 64: reads stay inside s_cand
+                unsigned long long kk[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) kk[u] = s_cand[k0 + u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) rank += (k0 + u < ncand && kk[u] > mine) ? 1 : 0;
+            }
             if (lane < ncand && rank < kappa) {
                 s_edges[rank] = pos;
                 s_elab[rank] = lab;
@@ -226,7 +232,13 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         if (lane < ne) {
             const int c = s_elab[lane];
             int k = 0;
-            for (int r = 0; r < ne; ++r) k += s_elab[r] == c;
+            for (int r0 = 0; r0 < ne; r0 += 8) {  // ne <= 32 = CKV_MAX_KAPPA: reads stay inside s_elab
+                int ll[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) ll[u] = s_elab[min(r0 + u, CKV_MAX_KAPPA - 1)];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) k += (r0 + u < ne && ll[u] == c) ? 1 : 0;
+            }
             if (c >= 0) key = ((unsigned long long)k << 32) | (0xFFFFFFFFu - (uint32_t)c);
         }
         key = wave_max_u64(key);
@@ -296,7 +308,9 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     p.ps_log2 = __builtin_ctz((unsigned)kv->page_size);
     p.max_pages = kv->max_pages;
     p.mode = idx->mode;
-    p.G = idx->n_graphs;
+    p.G = idx->n_graphs;  // arrivals of every window of the step
+    const Window w = window_of(idx);
+    p.g0 = w.first;
     p.c_cap = idx->c_cap;
     p.l_cap = idx->l_cap;
     p.tail_cap = idx->tail_cap;
@@ -323,7 +337,7 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     p.ctr = ctr;
     const int nh = heads_per_graph(kv, idx);
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
-    const dim3 grid(idx->n_graphs), block(256);
+    const dim3 grid(w.count), block(256);
 #define CKV_AS(TT, DD, NN) \
     if (kv->head_dim == DD && nh == NN) { CKV_LAUNCH((assign_kernel<TT, DD, NN>), grid, block, s, p); return hipGetLastError(); }
 #define CKV_AS_T(TT) \

@@ -39,6 +39,7 @@ struct AttendParams {
     float *part;
     int32_t *ctr;
     int nchunk;  // blocks per unit
+    int g0;      // first unit of the launch window
 };
 
 template <typename T, int D, int NH>
@@ -237,8 +238,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, ts = lane >> 4;
-    const int unit = blockIdx.x / a.nchunk;
-    const int chunk = blockIdx.x - unit * a.nchunk;
+    const int lunit = blockIdx.x / a.nchunk;
+    const int chunk = blockIdx.x - lunit * a.nchunk;
+    const int unit = a.g0 + lunit;
     if constexpr (!DENSE) CKV_TMARK(20);
     if constexpr (!DENSE) CKV_BMARK(0);
 
@@ -492,7 +494,9 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
     p.part = part;
     p.ctr = ctr;
     p.nchunk = ceil_div(t_cap, kGatherTokens);
-    return dispatch<false>(kv, heads_per_graph(kv, idx), p, idx->n_graphs, s);
+    const Window w = window_of(idx);
+    p.g0 = w.first;
+    return dispatch<false>(kv, heads_per_graph(kv, idx), p, w.count, s);
 }
 
 hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *part,

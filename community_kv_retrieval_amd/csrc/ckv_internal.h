@@ -52,6 +52,14 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Row stride of the base CSR offsets (c_cap + 1 used, padded for 16-byte rows).
 __host__ __device__ inline int offs_stride(int c_cap) { return c_cap + 4; }
 
+// Graphs a step call processes: [first, first + count).
+struct Window {
+    int first, count;
+};
+inline Window window_of(const ckv_index *idx) {
+    return idx->win_count > 0 ? Window{idx->win_first, idx->win_count} : Window{0, idx->n_graphs};
+}
+
 inline int group_of(const ckv_kv *kv) { return kv->n_q_heads / kv->n_kv_heads; }
 inline int heads_per_graph(const ckv_kv *kv, const ckv_index *idx) {
     return idx->mode == CKV_MODE_PER_HEAD ? 1 : group_of(kv);

@@ -22,14 +22,14 @@ struct ScoreParams {
     const int32_t *size;
     const int32_t *n_comm;
     float *scores;
-    int mode, Hq, Hkv, c_cap;
+    int mode, Hq, Hkv, c_cap, g0;
 };
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     __shared__ double s_q[D];
     __shared__ double s_part[4][256];
-    const int g = blockIdx.y, c0 = blockIdx.x * 256;
+    const int g = p.g0 + blockIdx.y, c0 = blockIdx.x * 256;
     CKV_TMARK(0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nc = min(p.n_comm[g], p.c_cap);
@@ -74,9 +74,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 
 hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, float *scores,
                         hipStream_t s) {
+    const Window w = window_of(idx);
     ScoreParams p{q, idx->cent, idx->size, idx->n_comm, scores, idx->mode, kv->n_q_heads,
-                  kv->n_kv_heads, idx->c_cap};
-    const dim3 grid(idx->c_cap / 256, idx->n_graphs);
+                  kv->n_kv_heads, idx->c_cap, w.first};
+    const dim3 grid(idx->c_cap / 256, w.count);
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
     if (kv->head_dim == 128) {
         if (bf) CKV_LAUNCH((score_kernel<bf16_t, 128>), grid, dim3(256), s, p);

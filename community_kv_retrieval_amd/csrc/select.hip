@@ -51,7 +51,7 @@ struct SelectParams {
     const int32_t *tail_len;
     const int32_t *n_comm;
     const int32_t *seq_len;
-    int mode, Hq, Hkv, c_cap, l_cap, tail_cap, n_sinks, budget, max_comm, t_cap;
+    int mode, Hq, Hkv, c_cap, l_cap, tail_cap, n_sinks, budget, max_comm, t_cap, g0;
     int32_t *sel;
     int32_t *sel_n;
     int32_t *top;
@@ -70,7 +70,7 @@ struct SelShared {
     int csz[64];
     int ccount;
     int cut_bin, cut_above;
-    int scan[(kSelThreads / 64 + 1) * 9];
+    int scan[(kSelThreads / 64) * 9];
     float red_lo[kSelThreads / 64], red_hi[kSelThreads / 64];
     uint32_t red_id[kSelThreads / 64];
     unsigned long long prefix, mask, thr;
@@ -86,10 +86,12 @@ __device__ __forceinline__ unsigned long long comm_key(float s, int c) {
 __device__ __forceinline__ int slab_id(int tid, int e) { return (e >> 2) * kSlab + 4 * tid + (e & 3); }
 
 // Block-wide exclusive prefix sums of NV ints per thread, in thread order, and
-// their totals (two barriers; `scratch` holds (NT/64 + 1) * NV ints).
+// their totals.  One barrier: every wave scans the wave totals itself.
+// `scratch` holds NT/64 * NV ints; the caller puts a barrier between two uses.
 template <int NT, int NV>
 __device__ __forceinline__ void block_scan_multi(const int (&v)[NV], int (&ex)[NV], int (&tot)[NV], int *scratch) {
     constexpr int NW = NT / 64;
+    static_assert(NW <= 64, "one lane per wave total");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x[NV];
 #pragma unroll
@@ -99,20 +101,13 @@ __device__ __forceinline__ void block_scan_multi(const int (&v)[NV], int (&ex)[N
         for (int k = 0; k < NV; ++k) scratch[wave * NV + k] = x[k];
     }
     __syncthreads();
-    if (wave == 0) {  // scan of the wave totals
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int t = lane < NW ? scratch[lane * NV + k] : 0;
-            const int ti = wave_incl_scan(t);
-            if (lane < NW) scratch[lane * NV + k] = ti - t;
-            if (lane == NW - 1) scratch[NW * NV + k] = ti;
-        }
-    }
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
-        tot[k] = scratch[NW * NV + k];
-        ex[k] = scratch[wave * NV + k] + x[k] - v[k];
+        const int t = lane < NW ? scratch[lane * NV + k] : 0;
+        const int ti = wave_incl_scan(t);
+        tot[k] = __builtin_amdgcn_readlane(ti, NW - 1);
+        const int before = wave > 0 ? __builtin_amdgcn_readlane(ti, wave > 0 ? wave - 1 : 0) : 0;
+        ex[k] = before + x[k] - v[k];
     }
 }
 
@@ -240,6 +235,7 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
         }
     }
     __syncthreads();
+    CKV_TMARK(40);
     // One wave walks the bins from the top: lane l owns bins
     // kBins-1-16l .. kBins-16-16l, a prefix over lanes gives each lane the
     // weight above its bins.
@@ -269,6 +265,7 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
         }
     }
     __syncthreads();
+    CKV_TMARK(41);
     const int cb = sh.cut_bin, above = sh.cut_above;
     if (cb < 0) {
         thr = 0ull;
@@ -285,34 +282,32 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
         }
     }
     __syncthreads();
+    CKV_TMARK(42);
     const int cnt = sh.ccount;
     if (cnt > 64) {
         __syncthreads();
         return false;
     }
     if (wave == 0) {
-        // bitonic sort of the complemented keys, ascending = keys descending
-        unsigned long long nk = lane < cnt ? ~sh.ckey[lane] : ~0ull;
-        int sz = lane < cnt ? sh.csz[lane] : 0;
+        // Each candidate of the cut bin sums the token weight of the better
+        // ones; the cut is the best candidate whose inclusive weight overflows.
+        const unsigned long long mine = lane < cnt ? sh.ckey[lane] : 0ull;
+        const int msz = lane < cnt ? sh.csz[lane] : 0;
+        int better = 0;
+        for (int k0 = 0; k0 < cnt; k0 += 8) {  // k0 + 7 < 64: reads stay inside ckey/csz
+            unsigned long long kk[8];
+            int ss[8];
 #pragma unroll
-        for (int k = 2; k <= 64; k <<= 1) {
-#pragma unroll
-            for (int jj = k >> 1; jj > 0; jj >>= 1) {
-                const unsigned long long onk = __shfl_xor(nk, jj, 64);
-                const int osz = __shfl_xor(sz, jj, 64);
-                const bool lower = (lane & jj) == 0;
-                const bool asc = (lane & k) == 0;
-                const bool take = (lower == asc) ? (onk < nk) : (onk > nk);
-                if (take) {
-                    nk = onk;
-                    sz = osz;
-                }
+            for (int u = 0; u < 8; ++u) {
+                kk[u] = sh.ckey[k0 + u];
+                ss[u] = sh.csz[k0 + u];
             }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (k0 + u < cnt && kk[u] > mine) better += ss[u];
         }
-        const int incl = wave_incl_scan(sz);
-        const unsigned long long bal = __ballot(lane < cnt && above + incl > budget);
-        const int first = bal ? __ffsll((long long)bal) - 1 : 0;
-        const unsigned long long cut = ~__shfl(nk, first, 64);
+        const bool over = lane < cnt && above + better + msz > budget;
+        const unsigned long long cut = wave_max_u64(over ? mine : 0ull);
         if (lane == 0) sh.thr = cut;
     }
     __syncthreads();
@@ -324,7 +319,7 @@ template <int NS>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     constexpr int EPT = 4 * NS;
     __shared__ SelShared sh;
-    const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     CKV_TMARK(10);
     const int C = p.c_cap;
     const int nc = min(p.n_comm[g], C);
@@ -447,6 +442,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         if (taken[j]) atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
     }
     __syncthreads();
+    CKV_TMARK(43);
     // Per slab: taken communities and their base members; then taken tail entries.
     constexpr int NV = 2 * NS + 1;
     int v[NV], ex[NV], tot[NV];
@@ -583,8 +579,10 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *sc
     p.top = top;
     p.tok_list = tok_list;
     p.tok_n = tok_n;
+    const Window w = window_of(idx);
+    p.g0 = w.first;
     const int ns = ceil_div(idx->c_cap, kSlab);
-    const dim3 grid(idx->n_graphs), block(kSelThreads);
+    const dim3 grid(w.count), block(kSelThreads);
     if (ns <= 1) CKV_LAUNCH((select_kernel<1>), grid, block, s, p);
     else if (ns <= 2) CKV_LAUNCH((select_kernel<2>), grid, block, s, p);
     else if (ns <= 3) CKV_LAUNCH((select_kernel<3>), grid, block, s, p);

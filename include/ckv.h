@@ -121,6 +121,17 @@ typedef struct ckv_index {
     double  *csum;       /* [G][c_cap][head_dim] exact float64 key sum of every community */
     float   *cent;       /* [G][head_dim][c_cap] centroid = float32(csum / size), transposed */
     int32_t *status;     /* [1] CKV_ST_* bits */
+    /* Launch window of the four step calls (score, select, gather, assign):
+     * they process graphs win_first .. win_first + win_count - 1 only
+     * (win_count = 0: every graph; win_first must then be 0).  Windows let a
+     * caller run disjoint sets of graphs on different streams so that one set's
+     * latency-bound calls overlap another set's bandwidth-bound ones.  Every
+     * array stays indexed by the global graph id, so windows never share a slot.
+     * Within one decode step the ckv_assign_update windows must cover every
+     * graph exactly once: seq_len advances when the last of the G graphs is done.
+     * ckv_index_build and ckv_dense_attend ignore the window. */
+    int32_t  win_first;
+    int32_t  win_count;
 } ckv_index;
 
 /* Bytes of workspace the calls below need for this layer shape and a token

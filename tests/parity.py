@@ -127,23 +127,30 @@ def _edges_ok(r: O.GraphStep, gpu_edges, stats: Stats, where: str) -> bool:
 
 def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None,
               check_state_every: int = 1, layer_kw: Optional[dict] = None, check_dense: bool = False,
-              pair=None) -> Stats:
+              pair=None, windows: int = 1) -> Stats:
+    """Steps the library and the oracle side by side and checks every output.
+    windows > 1 runs each step as the decoder's windowed multi-stream step."""
     layer, orc = pair if pair is not None else make_pair(w, seed, steps, graphs, **(layer_kw or {}))
     dev = layer.kv.kv.device
     dec, buf = layer.dec, layer.dec.buf
+    dec.set_windows(windows)
+    assert not (check_dense and windows > 1), "the dense check runs between the calls of one window"
     check_csr(layer, orc)
     check_index_state(layer, orc, w, full=True)
     stats = Stats()
     for t in range(steps):
         inp = synth.gen_step(w, seed, t, layer.slices)
         q, kn, vn = inp.q.to(dev), inp.k_new.to(dev), inp.v_new.to(dev)
-        dec.retrieve(q)
-        dec.attend(q)
         dense = None
-        if check_dense:
-            dense = torch.empty_like(buf.out)
-            dec.dense(q, dense)
-        dec.update(kn, vn)
+        if windows > 1:
+            dec.step(q, kn, vn)
+        else:
+            dec.retrieve(q)
+            dec.attend(q)
+            if check_dense:
+                dense = torch.empty_like(buf.out)
+                dec.dense(q, dense)
+            dec.update(kn, vn)
         torch.cuda.synchronize()
         H = {k: getattr(buf, k).cpu().numpy() for k in
              ("sel", "sel_n", "top", "tok_list", "tok_n", "out", "logits", "ml", "edges", "assign")}

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ckv.LIB.ckv_abi_version() == 2
+    assert ckv.LIB.ckv_abi_version() == 3
     for code in (0, -1, -2, -3, -4):
         assert ckv.ckv_status_str(code) != "unknown status"
     assert ckv.ckv_status_str(7) == "unknown status"
@@ -101,6 +101,25 @@ def test_kv_validation(kw, code):
 def test_index_validation(kw):
     kv, idx = _kv(), _idx(**kw)
     assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == ckv.CKV_E_INVALID
+
+
+@pytest.mark.parametrize("first,count", [(0, -1), (-1, 4), (1, 0), (30, 3), (32, 1)])
+def test_window_validation(first, count):
+    kv, idx = _kv(), _idx(win_first=first, win_count=count)
+    for f in (ckv.LIB.ckv_score_centroids,):
+        assert f(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == ckv.CKV_E_INVALID
+
+
+def test_window_view_binding():
+    idx = object.__new__(ckv.CommunityIndex)
+    idx.n_graphs = 32
+    idx.desc = ckv.CkvIndex(0, 32, 256, 1000, 16, 4)
+    v = idx.window(8, 8)
+    assert (v.desc.win_first, v.desc.win_count) == (8, 8)
+    assert (idx.desc.win_first, idx.desc.win_count) == (0, 0)
+    for bad in ((0, 0), (-1, 2), (30, 3)):
+        with pytest.raises(ValueError):
+            idx.window(*bad)
 
 
 def test_select_validation():

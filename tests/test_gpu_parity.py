@@ -200,6 +200,52 @@ def test_checkpoint_resume_bit_identical():
         assert torch.equal(getattr(ref.idx, k), getattr(res.idx, k)), k
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("windows", [2, 3])
+def test_windowed_steps_match_oracle(windows):
+    PY.log(f"windowed steps, {windows} windows")
+    st = PY.run_steps(small_per_head(n_ctx=6000, steps=5), 21, 5, windows=windows)
+    assert st.graphs > 0
+    st = PY.run_steps(small_group(batch=3, n_ctx=5000, min_ctx=2000, steps=4), 22, 4, windows=windows)
+    assert st.graphs > 0
+
+
+def cached_rows(store):
+    """K/V of every cached position (slots past seq_len hold no data)."""
+    pt, lens, ps = store.page_table.cpu(), store.seq_len.cpu(), store.kv.shape[2]
+    kv = store.kv.cpu()
+    out = []
+    for b in range(lens.numel()):
+        pos = torch.arange(int(lens[b]))
+        out.append(kv[pt[b, pos // ps].long(), :, pos % ps])
+    return torch.cat(out)
+
+
+@pytest.mark.gpu
+def test_windowed_equals_one_window():
+    w = small_per_head(n_ctx=5000, steps=6)
+    PY.log("windows 1 / 4 / 5 bit-identical")
+    runs = []
+    for windows in (1, 4, 5):
+        layer = runner.load_layer(w, 23, extra=7)
+        layer.dec.set_windows(windows)
+        rec = []
+        for t in range(6):
+            inp = synth.gen_step(w, 23, t, layer.slices)
+            layer.dec.step(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda())
+            b = layer.dec.buf
+            n = b.tok_n.cpu()
+            rec += [x.cpu().clone() for x in (b.out, b.ml, b.edges, b.assign, b.tok_n, b.sel_n, b.top)]
+            rec += [b.tok_list[g, :n[g]].cpu().clone() for g in range(n.numel())]
+            rec += [b.logits[g, :, :n[g]].cpu().clone() for g in range(n.numel())]
+        rec += [getattr(layer.idx, k).cpu().clone() for k in ckv.CommunityIndex.STATE]
+        rec += [layer.kv.seq_len.cpu().clone(), cached_rows(layer.kv)]
+        runs.append(rec)
+    for other in runs[1:]:
+        for x, y in zip(runs[0], other):
+            assert torch.equal(x, y)
+
+
 def test_dense_baseline_matches_oracle():
     w = synth.preset("qwen3_8b_32k").replace(n_ctx=20000, batch=2, min_ctx=9000)
     PY.log("dense baseline")
