@@ -176,7 +176,7 @@ def main():
         ckv.ckv_time_next_launch(*ev[i][0])
         ckv.ckv_score_centroids(kv, idx, q, b.scores)
         ckv.ckv_time_next_launch(*ev[i][1])
-        ckv.ckv_select_communities(kv, idx, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
+        ckv.ckv_select_communities(kv, idx, q, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
                                    b.tok_list, b.tok_n)
         ckv.ckv_time_next_launch(*ev[i][2])
         ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, b.out, b.logits, b.ml, b.ws)

@@ -52,8 +52,8 @@ class CkvIndex(ctypes.Structure):
                 ("tail_cap", c_int32), ("n_sinks", c_int32),
                 ("n_comm", c_void_p), ("size", c_void_p), ("offs", c_void_p), ("toks", c_void_p),
                 ("label", c_void_p), ("tail_pos", c_void_p), ("tail_comm", c_void_p),
-                ("tail_len", c_void_p), ("csum", c_void_p), ("cent", c_void_p), ("status", c_void_p),
-                ("win_first", c_int32), ("win_count", c_int32)]
+                ("tail_len", c_void_p), ("csum", c_void_p), ("cent", c_void_p), ("cq", c_void_p),
+                ("cscale", c_void_p), ("status", c_void_p), ("win_first", c_int32), ("win_count", c_int32)]
 
 
 def _load():
@@ -66,7 +66,7 @@ def _load():
         "ckv_kv_write": (c_int32, [KVP, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "ckv_index_build": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_score_centroids": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p]),
-        "ckv_select_communities": (c_int32, [KVP, IXP, c_void_p, c_int32, c_int32, c_int32, c_void_p,
+        "ckv_select_communities": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
                                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "ckv_gather_attend": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -165,10 +165,13 @@ class CommunityIndex:
         self.tail_len = torch.zeros((G,), **i32)
         self.csum = torch.zeros((G, c_cap, D), dtype=torch.float64, device=device)
         self.cent = torch.zeros((G, D, c_cap), dtype=torch.float32, device=device)
+        self.cq = torch.zeros((G, D, c_cap), dtype=torch.int16, device=device)
+        self.cscale = torch.zeros((G, c_cap), dtype=torch.float32, device=device)
         self.status = torch.zeros((1,), **i32)
         self.desc = CkvIndex(mode, G, c_cap, l_cap, tail_cap, n_sinks, *[
             t.data_ptr() for t in (self.n_comm, self.size, self.offs, self.toks, self.label, self.tail_pos,
-                                   self.tail_comm, self.tail_len, self.csum, self.cent, self.status)])
+                                   self.tail_comm, self.tail_len, self.csum, self.cent, self.cq, self.cscale,
+                                   self.status)])
 
     def heads_per_graph(self, kv: KVStore) -> int:
         return 1 if self.mode == CKV_MODE_PER_HEAD else kv.group
@@ -183,7 +186,8 @@ class CommunityIndex:
         v.desc.win_first, v.desc.win_count = first, count
         return v
 
-    STATE = ("size", "offs", "toks", "label", "tail_pos", "tail_comm", "tail_len", "csum", "cent", "status")
+    STATE = ("size", "offs", "toks", "label", "tail_pos", "tail_comm", "tail_len", "csum", "cent", "cq", "cscale",
+             "status")
 
     def state_dict(self):
         return {k: getattr(self, k).clone() for k in self.STATE + ("n_comm",)}
@@ -222,10 +226,11 @@ def ckv_score_centroids(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, score
                                                           _ptr(scores), _stream(stream)))
 
 
-def ckv_select_communities(kv: KVStore, idx: CommunityIndex, scores: torch.Tensor, budget: int, max_comm: int,
-                           sel: torch.Tensor, sel_n: torch.Tensor, top: torch.Tensor, tok_list: torch.Tensor,
-                           tok_n: torch.Tensor, stream=None):
+def ckv_select_communities(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, scores: torch.Tensor, budget: int,
+                           max_comm: int, sel: torch.Tensor, sel_n: torch.Tensor, top: torch.Tensor,
+                           tok_list: torch.Tensor, tok_n: torch.Tensor, stream=None):
     G = idx.n_graphs
+    _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
     _need(scores, "scores", torch.float32, (G, idx.c_cap))
     _need(sel, "sel", torch.int32, (G, idx.c_cap))
     for name, t in (("sel_n", sel_n), ("top", top), ("tok_n", tok_n)):
@@ -233,7 +238,7 @@ def ckv_select_communities(kv: KVStore, idx: CommunityIndex, scores: torch.Tenso
     t_cap = tok_list.shape[1]
     _need(tok_list, "tok_list", torch.int32, (G, t_cap))
     _check("ckv_select_communities", LIB.ckv_select_communities(
-        ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(scores), budget, max_comm, t_cap, _ptr(sel),
+        ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q), _ptr(scores), budget, max_comm, t_cap, _ptr(sel),
         _ptr(sel_n), _ptr(top), _ptr(tok_list), _ptr(tok_n), _stream(stream)))
 
 
@@ -349,7 +354,7 @@ class Decoder:
     def retrieve(self, q: torch.Tensor, stream=None):
         b = self.buf
         ckv_score_centroids(self.kv, self.idx, q, b.scores, stream)
-        ckv_select_communities(self.kv, self.idx, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
+        ckv_select_communities(self.kv, self.idx, q, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
                                b.tok_list, b.tok_n, stream)
 
     def attend(self, q: torch.Tensor, stream=None):
@@ -382,7 +387,7 @@ class Decoder:
             ckv_score_centroids(kv, view, q, b.scores, s)
             prev = torch.cuda.Event()
             prev.record(s)
-            ckv_select_communities(kv, view, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
+            ckv_select_communities(kv, view, q, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
                                    b.tok_list, b.tok_n, s)
             ckv_gather_attend(kv, view, q, b.tok_list, b.tok_n, self.sm_scale, b.out, b.logits, b.ml, b.ws, s)
             ckv_assign_update(kv, view, b.tok_list, b.tok_n, b.logits, b.ml, b.top, self.kappa, k_new, v_new,

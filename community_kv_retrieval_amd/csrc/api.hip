@@ -42,7 +42,8 @@ ckv_status check_index(const ckv_kv *kv, const ckv_index *idx) {
     if (idx->c_cap < 256 || idx->c_cap % 256 || idx->c_cap > CKV_MAX_C_CAP) return CKV_E_INVALID;
     if (idx->l_cap < 1 || idx->tail_cap < 1 || idx->tail_cap > 4096 || idx->n_sinks < 0) return CKV_E_INVALID;
     if (!idx->n_comm || !idx->size || !idx->offs || !idx->toks || !idx->label || !idx->tail_pos ||
-        !idx->tail_comm || !idx->tail_len || !idx->csum || !idx->cent || !idx->status)
+        !idx->tail_comm || !idx->tail_len || !idx->csum || !idx->cent || !idx->cq || !idx->cscale ||
+        !idx->status)
         return CKV_E_INVALID;
     if (idx->win_count < 0 || idx->win_first < 0) return CKV_E_INVALID;
     if (idx->win_count == 0 ? idx->win_first != 0 : (long long)idx->win_first + idx->win_count > G)
@@ -140,18 +141,18 @@ ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const voi
     return hip_status(launch_score(kv, idx, q, scores, (hipStream_t)stream));
 }
 
-ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const float *scores,
-                                  int32_t budget, int32_t max_comm, int32_t t_cap, int32_t *sel,
-                                  int32_t *sel_n, int32_t *top, int32_t *tok_list, int32_t *tok_n,
-                                  ckv_stream_t stream) {
+ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                                  const float *scores, int32_t budget, int32_t max_comm, int32_t t_cap,
+                                  int32_t *sel, int32_t *sel_n, int32_t *top, int32_t *tok_list,
+                                  int32_t *tok_n, ckv_stream_t stream) {
     ckv_status st = check_kv(kv);
     if (st != CKV_OK) return st;
     if ((st = check_index(kv, idx)) != CKV_OK) return st;
-    if (!scores || !sel || !sel_n || !top || !tok_list || !tok_n) return CKV_E_INVALID;
+    if (!q || !scores || !sel || !sel_n || !top || !tok_list || !tok_n) return CKV_E_INVALID;
     if (budget < 0 || max_comm < 0) return CKV_E_INVALID;
     const long long need = (long long)idx->n_sinks + (budget < idx->l_cap ? budget : idx->l_cap);
     if (t_cap < need) return CKV_E_INVALID;
-    return hip_status(launch_select(kv, idx, scores, budget, max_comm, t_cap, sel, sel_n, top, tok_list,
+    return hip_status(launch_select(kv, idx, q, scores, budget, max_comm, t_cap, sel, sel_n, top, tok_list,
                                     tok_n, (hipStream_t)stream));
 }
 

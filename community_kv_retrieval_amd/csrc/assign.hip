@@ -34,6 +34,8 @@ struct AssignParams {
     int32_t *tail_len;
     double *csum;
     float *cent;
+    int16_t *cq;
+    float *cscale;
     int32_t *status;
     const int32_t *tok_list;
     const int32_t *tok_n;
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     __shared__ int s_ncand, s_ne, s_a;
     __shared__ int s_edges[CKV_MAX_KAPPA];
     __shared__ int s_elab[CKV_MAX_KAPPA];
+    __shared__ float s_max[4];
 
     const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     CKV_TMARK(30);
@@ -257,12 +260,19 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     const int a = s_a;
     const bool join = room && a >= 0 && tn < p.tail_cap;  // uniform
     int newsize = 0;
+    float cv = 0.f;
     if (join && tid < D) {
         newsize = p.size[(size_t)g * p.c_cap + a] + 1;
         const size_t ci = ((size_t)g * p.c_cap + a) * D + tid;
         const double cs = p.csum[ci] + (double)to_f32(kn[tid]);
         p.csum[ci] = cs;
-        p.cent[((size_t)g * D + tid) * p.c_cap + a] = (float)(cs / (double)newsize);
+        cv = (float)(cs / (double)newsize);
+        p.cent[((size_t)g * D + tid) * p.c_cap + a] = cv;
+    }
+    // the screening copy of the column: scale = max |cent| / 32767
+    if (join) {
+        const float m = wave_max_f(fabsf(cv));
+        if (lane == 0) s_max[wave] = m;
     }
     if (tid == 0) {
         if (!room) {
@@ -283,6 +293,11 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     // block read seq_len before it counts itself in, so the increment cannot
     // race a read; the next kernel sees it across the kernel boundary.
     __syncthreads();
+    if (join) {
+        const float scale = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])) / kScreenMax;
+        if (tid < D) p.cq[((size_t)g * D + tid) * p.c_cap + a] = screen_code(cv, scale);
+        if (tid == 0) p.cscale[(size_t)g * p.c_cap + a] = scale;
+    }
     if (tid == 0) {
         if (join) p.size[(size_t)g * p.c_cap + a] = newsize;
         if (arrive_last(p.ctr, p.G)) {
@@ -324,6 +339,8 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     p.tail_len = idx->tail_len;
     p.csum = idx->csum;
     p.cent = idx->cent;
+    p.cq = idx->cq;
+    p.cscale = idx->cscale;
     p.status = idx->status;
     p.tok_list = tok_list;
     p.tok_n = tok_n;

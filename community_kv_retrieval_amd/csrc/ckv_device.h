@@ -36,7 +36,16 @@ __device__ unsigned long long g_block_trace[kBlockTraceBlocks * 8];
                     __builtin_amdgcn_s_getreg((31 << 11) | 4);                              \
         }                                                                                   \
     } while (0)
+// Per-wave stamps of block 0 (slot s of wave w at index 16 s + w).
+#define CKV_WMARK(s)                                                                          \
+    do {                                                                                      \
+        if (blockIdx.x == 0 && blockIdx.y == 0 && (threadIdx.x & 63) == 0)                    \
+            ::ckv::g_block_trace[16 * (s) + (threadIdx.x >> 6)] = __builtin_amdgcn_s_memrealtime(); \
+    } while (0)
 #else
+#define CKV_WMARK(s) \
+    do {             \
+    } while (0)
 #define CKV_TMARK(s) \
     do {             \
     } while (0)
@@ -127,6 +136,24 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ float shfl_xor_f(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// The same butterfly on a float64 (each 32-bit half moved by DPP): every lane
+// of the row ends with the identical row sum.
+template <int CTRL> __device__ __forceinline__ double dpp_d(double x) {
+    const unsigned long long u = __double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double row16_sum_d(double x) {
+    x += dpp_d<kQuadSwap1>(x);
+    x += dpp_d<kQuadSwap2>(x);
+    x += dpp_d<kRowHalfMirror>(x);
+    x += dpp_d<kRowMirror>(x);
+    return x;
+}
+
+
+
 // Wave-wide max of a 64-bit key, in every lane: the DPP butterfly inside each
 // row of 16 lanes, then the four row results read out with readlane.  Call with
 // all 64 lanes active.
@@ -184,6 +211,14 @@ __device__ __forceinline__ float wave_min_f(float x) {
         return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
     }));
 }
+__device__ __forceinline__ float wave_sum_f(float x) {
+    return __uint_as_float(wave_reduce_u32(__float_as_uint(x), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+    return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a + b; });
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
     return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
@@ -200,6 +235,17 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
     x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return x;
+}
+
+// Screening code of one centroid element: round(v / scale) clamped to
+// [-32767, 32767], with scale = max |column| / 32767, so that
+// |v - scale * code| <= scale * (1/2 + 2^-9); a zero scale (all-zero column)
+// gives 0.
+constexpr float kScreenMax = 32767.f;
+__device__ __forceinline__ int16_t screen_code(float v, float scale) {
+    if (!(scale > 0.f)) return 0;
+    const float r = fminf(kScreenMax, fmaxf(-kScreenMax, rintf(v / scale)));
+    return (int16_t)(int)r;
 }
 
 // Order-preserving map of a float32 onto uint32 (larger float, larger code).

@@ -112,7 +112,7 @@ hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int3
                               int32_t *cursor, hipStream_t s);
 hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, float *scores,
                         hipStream_t s);
-hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *scores, int budget,
+hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, const float *scores, int budget,
                          int max_comm, int t_cap, int32_t *sel, int32_t *sel_n, int32_t *top,
                          int32_t *tok_list, int32_t *tok_n, hipStream_t s);
 hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,

@@ -73,6 +73,8 @@ struct BuildParams {
     int32_t *label;
     double *csum;
     float *cent;
+    int16_t *cq;
+    float *cscale;
     int32_t *status;
     int32_t *cursor;
 };
@@ -168,17 +170,28 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
     const int32_t *ptab = p.page_table + (size_t)gc.b * p.max_pages;
     const T *kvb = reinterpret_cast<const T *>(p.kv);
     const int smask = (1 << p.ps_log2) - 1;
-    for (int d = tid; d < D; d += 256) {
+    static_assert(D <= 256, "one thread per dimension");
+    __shared__ float s_max[4];
+    float cv = 0.f;
+    if (tid < D) {
         double acc = 0.0;
         for (int i = 0; i < s; ++i) {
             const int pos = mem[i];
             const int page = ptab[pos >> p.ps_log2];
             const size_t row = (((size_t)page * p.Hkv + gc.kh) << p.ps_log2) | (size_t)(pos & smask);
-            acc += (double)to_f32(kvb[row * 2 * D + d]);
+            acc += (double)to_f32(kvb[row * 2 * D + tid]);
         }
-        p.csum[((size_t)g * p.c_cap + c) * D + d] = acc;
-        p.cent[((size_t)g * D + d) * p.c_cap + c] = (float)(acc / (double)s);
+        p.csum[((size_t)g * p.c_cap + c) * D + tid] = acc;
+        cv = (float)(acc / (double)s);
+        p.cent[((size_t)g * D + tid) * p.c_cap + c] = cv;
     }
+    // screening copy of the column: scale = max |cent| / 32767
+    const float m = wave_max_f(fabsf(cv));
+    if ((tid & 63) == 0) s_max[tid >> 6] = m;
+    __syncthreads();
+    const float scale = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])) / kScreenMax;
+    if (tid < D) p.cq[((size_t)g * D + tid) * p.c_cap + c] = screen_code(cv, scale);
+    if (tid == 0) p.cscale[(size_t)g * p.c_cap + c] = scale;
 }
 
 hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t *labels_in,
@@ -188,6 +201,8 @@ hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int3
     if ((e = fill_u32(idx->size, G * C, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->csum, G * C * D * 2, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->cent, G * C * D, 0u, s)) != hipSuccess) return e;
+    if ((e = fill_u32(idx->cq, G * C * D / 2, 0u, s)) != hipSuccess) return e;  // C % 256 == 0
+    if ((e = fill_u32(idx->cscale, G * C, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->tail_len, G, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->status, 1, 0u, s)) != hipSuccess) return e;
 
@@ -210,6 +225,8 @@ hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int3
     p.toks = idx->toks;
     p.label = idx->label;
     p.csum = idx->csum;
+    p.cq = idx->cq;
+    p.cscale = idx->cscale;
     p.cent = idx->cent;
     p.status = idx->status;
     p.cursor = cursor;

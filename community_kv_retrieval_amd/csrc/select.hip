@@ -4,23 +4,33 @@
 // One 1024-thread block per graph.  The communities are read in slabs of 4096:
 // in slab j thread t owns communities 4096 j + 4 t .. 4096 j + 4 t + 3, so
 // every 16-byte load of a wave covers 1 KB of consecutive memory.
-// Communities rank by float32 score, higher first, ties to the lower id; as
-// one number that is the 64-bit key (order-preserving bits of the score) << 32
-// | (~id).  The taken set is the longest prefix of the ranking that fits the
-// budget, i.e. every key above the key of the first community that overflows
-// it (the cut).
+// Communities rank by their exact score (float32 of the float64 product of
+// the graph's query with the float32 centroid), higher first, ties to the
+// lower id; as one number that is the 64-bit key (order-preserving bits of the
+// score) << 32 | (~id).  The taken set is the longest prefix of the ranking
+// that fits the budget, i.e. every key above the key of the first community
+// that overflows it (the cut).
 //
-// The whole graph runs on one CU, so the passes over every community use
-// 32-bit arithmetic only.  The cut is found in two steps: a token-weighted
-// histogram over 1024 equal-width score bins between the lowest and highest
-// score (a monotone map of the score, so bins keep the ranking), walked from
-// the top by one wave, gives the bin holding the cut; every community above it
-// is taken.  The few communities of that bin get their 64-bit keys, one wave
-// sorts them (bitonic network) and walks them until the budget overflows.
-// When the scores are degenerate (all equal, or more than 64 in the cut bin) a
+// The scores given are screening scores s~ with |s - s~| <= E (the scoring
+// kernel's bound), i.e. every exact score lies in [L, U] = [s~ - E, s~ + E].
+// Two token-weighted histograms over 1024 equal-width bins (a monotone map, so
+// bins keep the order) of U and of L, each walked from the top, give the bin
+// b_h where the U walk overflows the budget and the bin b_l where the L walk
+// does.  Every community whose L bin is above b_h is certainly taken: all
+// communities ranked above it have U at least as high, and those weigh no more
+// than the budget.  Every community whose U bin is below b_l is certainly not:
+// the communities whose L bin reaches b_l all rank above it and overflow the
+// budget.  The communities in between (the band), and those whose U reaches
+// the largest L (the candidates for the best community), get their exact
+// score from the float64 key sums, one 16-lane group per community, and the
+// band is cut with what the certain communities leave of the budget.  When the
+// scores are degenerate, the band does not fit in LDS, or the community cap
+// (max_comm) is set, every exact score is computed, slab by slab, and the cut
+// is found on them directly: a histogram of the exact scores gives the bin
+// holding the cut and the few communities of that bin are ranked exactly; a
 // most-significant-digit radix select over the 64-bit keys, with
-// token-weighted digit histograms, finds the same cut.  The community cap
-// (max_comm) is the same radix select with unit weights.
+// token-weighted digit histograms, finds the same cut when that bin is
+// crowded, and the community cap is the same radix select with unit weights.
 //
 // Then one block scan over per-slab counts gives every taken community its
 // rank in ascending id order and its first slot in the token list, and every
@@ -40,6 +50,16 @@ constexpr int kSlab = 4 * kSelThreads;  // communities per slab
 // copy; more than that are copied one thread per community.
 constexpr int kSelLds = 4096;
 constexpr int kTailPerThread = 4;  // tail_cap <= 4096
+// Communities whose exact score the screened path computes (band and
+// best-community candidates); more than that switches to exact scores for all.
+constexpr int kList = 2048;
+constexpr int kRankCut = 256;  // bands up to this size are cut by counting
+constexpr uint32_t kBand = 1u << 30, kTopCand = 1u << 29;
+// Screening bound factor, in units of cscale * |qbar|_1: 1/2 + 2^-9 for the
+// rounding of the int16 codes, 32767 (D + 1) 2^-24 < 0.252 for the float32
+// accumulation of D <= 128 products |q_d| * 32767 and for rounding qbar to
+// float32, with slack.
+constexpr float kScreenK = 0.76f;
 
 struct SelectParams {
     const float *scores;
@@ -51,6 +71,10 @@ struct SelectParams {
     const int32_t *tail_len;
     const int32_t *n_comm;
     const int32_t *seq_len;
+    const float *cscale;
+    const double *csum;
+    const void *q;
+    int bf16, D;
     int mode, Hq, Hkv, c_cap, l_cap, tail_cap, n_sinks, budget, max_comm, t_cap, g0;
     int32_t *sel;
     int32_t *sel_n;
@@ -60,18 +84,33 @@ struct SelectParams {
 };
 
 struct SelShared {
-    int soff[kSelLds];       // first base member in toks of the k-th taken community
-    int spref[kSelLds];      // its first slot in the token list (after the sinks)
-    int bw[kBins];           // token weight per score bin
-    uint32_t hw[256];        // radix select: token weight per digit
-    uint32_t hn[256];        // radix select: candidates per digit
+    union {
+        struct {
+            int soff[kSelLds];   // first base member in toks of the k-th taken community
+            int spref[kSelLds];  // its first slot in the token list (after the sinks)
+        } cp;
+        struct {
+            unsigned long long key[kList];  // exact key
+            int id[kList];                  // community | kBand | kTopCand
+            int sz[kList];
+        } ls;
+        float exs[kSlab];  // exact scores of one slab
+    } u;
+    int bw[kBins];   // token weight per bin: U (screened), exact score (exact path)
+    int bwl[kBins];  // token weight per bin of L
+    uint32_t hw[256];  // radix select: token weight per digit
+    uint32_t hn[256];  // radix select: candidates per digit
     uint32_t bits[CKV_MAX_C_CAP / 32];
+    double qbar[128];
+    float qabs[128];
     unsigned long long ckey[64];
     int csz[64];
     int ccount;
     int cut_bin, cut_above;
+    int b_h, b_l;
+    unsigned long long topkey, bandthr;
     int scan[(kSelThreads / 64) * 9];
-    float red_lo[kSelThreads / 64], red_hi[kSelThreads / 64];
+    float red_lo[kSelThreads / 64], red_hi[kSelThreads / 64], red_lm[kSelThreads / 64];
     uint32_t red_id[kSelThreads / 64];
     unsigned long long prefix, mask, thr;
     long long rem;
@@ -79,7 +118,14 @@ struct SelShared {
 };
 
 __device__ __forceinline__ unsigned long long comm_key(float s, int c) {
+    if (s == 0.f) s = 0.f;  // one key for +0 and -0
     return ((unsigned long long)ordered_bits(s) << 32) | (0xFFFFFFFFu - (uint32_t)c);
+}
+
+// The float32 score a key was made from.
+__device__ __forceinline__ float key_score(unsigned long long k) {
+    const uint32_t u = (uint32_t)(k >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
 // Community id of element e (0 .. 4 NS - 1) of thread tid.
@@ -111,18 +157,16 @@ __device__ __forceinline__ void block_scan_multi(const int (&v)[NV], int (&ex)[N
     }
 }
 
-// Threshold key of the budget cut by radix select over the 64-bit keys: the
-// taken communities are those with key > threshold (0 = everything fits).
-// `unit` counts communities instead of tokens (the community cap).
-template <int EPT>
-__device__ unsigned long long radix_cut(const float (&sv)[EPT], const int (&w)[EPT], bool unit,
+// Threshold key of a budget cut by radix select over 64-bit keys (0 = no
+// candidate): the taken keys are those > threshold (0 = everything fits).
+// `unit` counts candidates instead of their token weight (the community cap).
+template <int N>
+__device__ unsigned long long radix_cut(const unsigned long long (&key)[N], const int (&w)[N], bool unit,
                                         long long budget, SelShared &sh) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    unsigned long long key[EPT];
     unsigned long long kmax = 0ull, kmin = ~0ull;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        key[j] = w[j] > 0 ? comm_key(sv[j], slab_id(tid, j)) : 0ull;
+    for (int j = 0; j < N; ++j) {
         if (key[j]) {
             kmax = umax64(kmax, key[j]);
             kmin = umin64(kmin, key[j]);
@@ -141,6 +185,7 @@ __device__ unsigned long long radix_cut(const float (&sv)[EPT], const int (&w)[E
         kmin = umin64(kmin, sh.ckey[32 + i]);
     }
     __syncthreads();
+    if (kmax == 0ull) return 0ull;  // uniform: no candidate
     const unsigned long long diff = kmax ^ kmin;
     int hi = diff ? 63 - __clzll((long long)diff) : 0;
     unsigned long long mask = ~((2ull << hi) - 1ull);  // bits above hi (0 when hi == 63)
@@ -155,7 +200,7 @@ __device__ unsigned long long radix_cut(const float (&sv)[EPT], const int (&w)[E
         }
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
+        for (int j = 0; j < N; ++j) {
             if (key[j] && (key[j] & mask) == prefix) {
                 const uint32_t d = (uint32_t)(key[j] >> lo) & dm;
                 atomicAdd(&sh.hw[d], unit ? 1u : (uint32_t)w[j]);
@@ -216,12 +261,20 @@ __device__ unsigned long long radix_cut(const float (&sv)[EPT], const int (&w)[E
     }
 }
 
+// Keys of this thread's communities (0 for empty ones).
+template <int EPT>
+__device__ __forceinline__ void comm_keys(const float (&sv)[EPT], const int (&w)[EPT],
+                                          unsigned long long (&key)[EPT]) {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) key[j] = w[j] > 0 ? comm_key(sv[j], slab_id(threadIdx.x, j)) : 0ull;
+}
+
 // Budget cut through equal-width score bins (see the file comment).  The bin
 // weights and the candidate count must be zero on entry.  Returns false,
 // uniformly across the block, when the radix select has to decide.
-template <int EPT>
+template <int EPT, typename IdF>
 __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budget, float lo, float hi,
-                          SelShared &sh, unsigned long long &thr) {
+                          SelShared &sh, unsigned long long &thr, IdF idf) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float scale = (float)kBins / (hi - lo);
     if (!(hi > lo) || !(scale < __builtin_huge_valf())) return false;
@@ -235,7 +288,6 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
         }
     }
     __syncthreads();
-    CKV_TMARK(40);
     // One wave walks the bins from the top: lane l owns bins
     // kBins-1-16l .. kBins-16-16l, a prefix over lanes gives each lane the
     // weight above its bins.
@@ -265,7 +317,6 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
         }
     }
     __syncthreads();
-    CKV_TMARK(41);
     const int cb = sh.cut_bin, above = sh.cut_above;
     if (cb < 0) {
         thr = 0ull;
@@ -276,13 +327,12 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
         if (bin[j] == cb) {
             const int i = atomicAdd(&sh.ccount, 1);
             if (i < 64) {
-                sh.ckey[i] = comm_key(sv[j], slab_id(tid, j));
+                sh.ckey[i] = comm_key(sv[j], idf(j));
                 sh.csz[i] = w[j];
             }
         }
     }
     __syncthreads();
-    CKV_TMARK(42);
     const int cnt = sh.ccount;
     if (cnt > 64) {
         __syncthreads();
@@ -315,7 +365,56 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
     return true;
 }
 
-template <int NS>
+// Exact score of n communities, one 16-lane group per community, stride 64
+// groups: float32 of the float64 sum over d of qbar_d * float32(csum_d / size),
+// the centroid exactly as the index stores it.  The communities are the list
+// entries (to_list) or the ids slab * 4096 + i of one slab.  Every lane loads
+// its D/16 consecutive sums with vector loads; rows of two communities per
+// group are in flight together.
+template <int D>
+__device__ __forceinline__ void exact_scores(const SelectParams &p, int g, int n, SelShared &sh,
+                                             bool to_list, int slab) {
+    constexpr int E = D / 16;  // doubles per lane
+    const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
+    const int nc = min(p.n_comm[g], p.c_cap);
+    for (int i0 = grp; i0 < n; i0 += 2 * 64) {
+        int cc[2], nn[2];
+        double cs[2][E];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int i = i0 + 64 * r;
+            const bool ok = i < n;
+            if (to_list) {
+                cc[r] = ok ? (sh.u.ls.id[i] & 0xFFFF) : 0;
+                nn[r] = ok ? sh.u.ls.sz[i] : 0;
+            } else {
+                cc[r] = slab * kSlab + (ok ? i : 0);
+                nn[r] = ok && cc[r] < nc ? p.size[(size_t)g * p.c_cap + cc[r]] : 0;
+                if (cc[r] >= p.c_cap) cc[r] = 0;
+            }
+            const double *row = p.csum + ((size_t)g * p.c_cap + cc[r]) * D + l16 * E;
+#pragma unroll
+            for (int e = 0; e < E; ++e) cs[r][e] = row[e];
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            double part = 0.0;
+            if (nn[r] > 0) {
+                const double dn = (double)nn[r];
+#pragma unroll
+                for (int e = 0; e < E; ++e) part = fma(sh.qbar[l16 * E + e], (double)(float)(cs[r][e] / dn), part);
+            }
+            const double S = row16_sum_d(part);
+            const int i = i0 + 64 * r;
+            if (l16 == 0 && i < n) {
+                if (to_list) sh.u.ls.key[i] = comm_key((float)S, cc[r]);
+                else sh.u.exs[i] = nn[r] > 0 ? (float)S : kNegInf;
+            }
+        }
+    }
+}
+
+template <int NS, int D>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     constexpr int EPT = 4 * NS;
     __shared__ SelShared sh;
@@ -329,29 +428,31 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     const float *sc = p.scores + (size_t)g * C;
     const int32_t *sz = p.size + (size_t)g * C;
     const int32_t *offs = p.offs + (size_t)g * offs_stride(C);
+    const float *scl = p.cscale + (size_t)g * C;
     int32_t *tl = p.tok_list + (size_t)g * p.t_cap;
 
-    // Sizes, scores and CSR offsets of this thread's four communities of every
-    // slab, 16 bytes per load, and the tail entries.  c0 % 4 == 0 and C % 256
-    // == 0, so a 16-byte load from c0 < C stays inside the row and offs[c0 + 4]
-    // exists (the offsets row holds C + 4 entries).  Entries at or past n_comm
-    // are masked after the loads.
-    int s[EPT], o0[EPT], o1[EPT];
-    float sv[EPT];
+    // Sizes, screening scores, scales and CSR offsets of this thread's four
+    // communities of every slab, 16 bytes per load, and the tail entries.
+    // c0 % 4 == 0 and C % 256 == 0, so a 16-byte load from c0 < C stays inside
+    // the row and offs[c0 + 4] exists (the offsets row holds C + 4 entries).
+    // Entries at or past n_comm are masked after the loads.
+    int s[EPT], o0[EPT], on[NS];
+    float sv[EPT], se[EPT];
     {
         int4 s4[NS], o4[NS];
-        float4 v4[NS];
-        int on[NS];
+        float4 v4[NS], e4[NS];
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
             const int c0 = j * kSlab + 4 * tid;
             s4[j] = make_int4(0, 0, 0, 0);
             o4[j] = make_int4(0, 0, 0, 0);
             v4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            e4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
             on[j] = 0;
             if (c0 < C) {
                 s4[j] = *reinterpret_cast<const int4 *>(sz + c0);
                 v4[j] = *reinterpret_cast<const float4 *>(sc + c0);
+                e4[j] = *reinterpret_cast<const float4 *>(scl + c0);
                 o4[j] = *reinterpret_cast<const int4 *>(offs + c0);
                 on[j] = offs[c0 + 4];
             }
@@ -367,16 +468,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
             sv[4 * j + 1] = v4[j].y;
             sv[4 * j + 2] = v4[j].z;
             sv[4 * j + 3] = v4[j].w;
+            se[4 * j] = e4[j].x;
+            se[4 * j + 1] = e4[j].y;
+            se[4 * j + 2] = e4[j].z;
+            se[4 * j + 3] = e4[j].w;
             o0[4 * j] = o4[j].x;
             o0[4 * j + 1] = o4[j].y;
             o0[4 * j + 2] = o4[j].z;
             o0[4 * j + 3] = o4[j].w;
-            o1[4 * j] = o4[j].y;
-            o1[4 * j + 1] = o4[j].z;
-            o1[4 * j + 2] = o4[j].w;
-            o1[4 * j + 3] = on[j];
         }
     }
+    // end of the base members of element e: the next element's start
+    auto o1 = [&](int e) { return (e & 3) == 3 ? on[e >> 2] : o0[e + 1]; };
     const int tn = p.tail_len[g];
     int tcomm[kTailPerThread], tpos[kTailPerThread];
 #pragma unroll
@@ -386,62 +489,333 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         tcomm[j] = in ? p.tail_comm[(size_t)g * p.tail_cap + i] : -1;
         tpos[j] = in ? p.tail_pos[(size_t)g * p.tail_cap + i] : 0;
     }
+    // The graph's query: its head's q, or the sum of its group's q (exact in float64).
+    if (tid < p.D) {
+        double a = 0.0;
+        const size_t q0 = ((size_t)gc.b * p.Hq + gc.qh0) * p.D + tid;
+        for (int h = 0; h < gc.nh; ++h) {
+            const size_t qi = q0 + (size_t)h * p.D;
+            a += p.bf16 ? (double)to_f32(reinterpret_cast<const bf16_t *>(p.q)[qi])
+                        : (double)reinterpret_cast<const float *>(p.q)[qi];
+        }
+        sh.qbar[tid] = a;
+        sh.qabs[tid] = fabsf((float)a);
+    }
 
-    // LDS state the cut starts from, cleared under the first barrier below.
+    // LDS state the cuts start from, cleared under the first barrier below.
     for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
     sh.bw[tid] = 0;
-    if (tid == 0) sh.ccount = 0;
+    sh.bwl[tid] = 0;
+    if (tid == 0) {
+        sh.ccount = 0;
+        sh.topkey = 0ull;
+    }
+    __syncthreads();
 
-    // Score range of the non-empty communities.
-    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+    // Interval [L, U] of every exact score: E = cscale * |qbar|_1 * kScreenK
+    // plus 2^-20 |s~| for the float32 roundings of s~, of the exact score and
+    // of U and L themselves.
+    float qn = sh.qabs[lane] * (lane < p.D ? 1.f : 0.f);
+    if (lane + 64 < p.D) qn += sh.qabs[lane + 64];
+    const float kq = wave_sum_f(qn) * kScreenK;
+    float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf(), lmax = -__builtin_huge_valf();
+    auto bound = [&](int j) { return se[j] * kq + fabsf(sv[j]) * 0x1p-20f; };
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        if (sv[j] == 0.f) sv[j] = 0.f;  // one key for +0 and -0
         if (s[j] > 0) {
-            lo = fminf(lo, sv[j]);
-            hi = fmaxf(hi, sv[j]);
+            const float e = bound(j);
+            lo = fminf(lo, sv[j] - e);
+            hi = fmaxf(hi, sv[j] + e);
+            lmax = fmaxf(lmax, sv[j] - e);
         }
     }
     lo = wave_min_f(lo);
     hi = wave_max_f(hi);
+    lmax = wave_max_f(lmax);
     if (lane == 0) {
         sh.red_lo[wave] = lo;
         sh.red_hi[wave] = hi;
+        sh.red_lm[wave] = lmax;
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSelThreads / 64; ++i) {
         lo = fminf(lo, sh.red_lo[i]);
         hi = fmaxf(hi, sh.red_hi[i]);
+        lmax = fmaxf(lmax, sh.red_lm[i]);
     }
     const bool any = hi >= lo;  // uniform: some community is non-empty
-    // Best-ranked community: the lowest id among those scoring hi (read by
-    // thread 0 at the end, after several barriers).
-    uint32_t best = 0xFFFFFFFFu;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j)
-        if (s[j] > 0 && sv[j] == hi) best = min(best, (uint32_t)slab_id(tid, j));
-    best = wave_min_u32(best);
-    if (lane == 0) sh.red_id[wave] = best;
+    const float bscale = (float)kBins / (hi - lo);
+    bool exact_all = p.max_comm > 0 || !(hi > lo) || !(bscale < __builtin_huge_valf());  // uniform
     CKV_TMARK(11);
 
     unsigned long long thr = ~0ull;  // nothing taken when there is no candidate
-    if (any) {
-        if (!value_cut<EPT>(sv, s, p.budget, lo, hi, sh, thr)) thr = radix_cut<EPT>(sv, s, false, p.budget, sh);
-        if (p.max_comm > 0) thr = umax64(thr, radix_cut<EPT>(sv, s, true, p.max_comm, sh));
+    uint32_t cert = 0u;  // bit j: community j of this thread is taken
+    if (any && !exact_all) {
+        // Token-weighted histograms of U and L; the U walk overflows the
+        // budget in bin b_h, the L walk in bin b_l (-1: no overflow).
+        int bb[EPT];        // U bin << 16 | L bin
+        uint32_t tcm = 0u;  // bit j: candidate for the best community
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const float e = bound(j), u = sv[j] + e, l = sv[j] - e;
+            const int bu = min(kBins - 1, (int)((u - lo) * bscale));
+            const int bl = min(kBins - 1, (int)((l - lo) * bscale));
+            bb[j] = (bu << 16) | bl;
+            if (s[j] > 0) {
+                atomicAdd(&sh.bw[bu], s[j]);
+                atomicAdd(&sh.bwl[bl], s[j]);
+                if (u >= lmax) tcm |= 1u << j;
+            }
+        }
+        __syncthreads();
+        CKV_TMARK(50);
+        if (wave < 2) {
+            const int *hist = wave == 0 ? sh.bw : sh.bwl;
+            int v[16], tot = 0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                v[k] = hist[kBins - 1 - (lane * 16 + k)];
+                tot += v[k];
+            }
+            const int incl = wave_incl_scan(tot);
+            int acc = incl - tot, found = -1;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if (found < 0 && acc + v[k] > p.budget) found = kBins - 1 - (lane * 16 + k);
+                acc += v[k];
+            }
+            const unsigned long long bal = __ballot(found >= 0);
+            const int src = bal ? __ffsll((long long)bal) - 1 : 0;
+            const int fb = __shfl(found, src, 64);
+            if (lane == 0) {
+                if (wave == 0) sh.b_h = bal ? fb : -1;
+                else sh.b_l = bal ? fb : -1;
+            }
+        }
+        __syncthreads();
+        CKV_TMARK(51);
+        const int b_h = sh.b_h, b_l = sh.b_l;
+        // Certain, band and best-community candidates; the latter two go to the
+        // list, at places a block scan of the per-thread counts assigns.
+        uint32_t wantm = 0u, bandm = 0u;
+        int v[3] = {0, 0, 0}, ex[3], tot[3];  // list entries, band entries, certain weight
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            if (s[j] <= 0) continue;
+            const bool ce = (bb[j] & 0xFFFF) > b_h;
+            const bool band = !ce && (bb[j] >> 16) >= b_l;
+            const bool tc = (tcm >> j) & 1u;
+            if (ce) {
+                cert |= 1u << j;
+                v[2] += s[j];
+            }
+            if (band) {
+                bandm |= 1u << j;
+                v[1] += 1;
+            }
+            if (band || tc) {
+                wantm |= 1u << j;
+                v[0] += 1;
+            }
+        }
+        block_scan_multi<kSelThreads, 3>(v, ex, tot, sh.scan);
+        CKV_TMARK(52);
+        const int nlist = tot[0];
+        if (nlist > kList) {
+            exact_all = true;  // uniform
+        } else {
+            int i = ex[0];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                if ((wantm >> j) & 1u) {
+                    sh.u.ls.id[i] = slab_id(tid, j) | (((bandm >> j) & 1u) ? (int)kBand : 0) |
+                                    (((tcm >> j) & 1u) ? (int)kTopCand : 0);
+                    sh.u.ls.sz[i] = s[j];
+                    ++i;
+                }
+            }
+            CKV_TMARK(53);
+            __syncthreads();
+            CKV_TMARK(54);
+            exact_scores<D>(p, g, nlist, sh, true, 0);
+            sh.bw[tid] = 0;  // the band cut starts from empty bins
+            if (tid == 0) sh.ccount = 0;
+            __syncthreads();
+            CKV_TMARK(55);
+            // Best community: the largest exact key among the candidates; the
+            // band entries with their exact scores and the band's score range.
+            constexpr int NB = kList / kSelThreads;
+            unsigned long long bk[NB], tk = 0ull;
+            int bwt[NB];
+            float bs[NB], blo = __builtin_huge_valf(), bhi = -__builtin_huge_valf();
+#pragma unroll
+            for (int r = 0; r < NB; ++r) {
+                const int i = tid + r * kSelThreads;
+                const int id = i < nlist ? sh.u.ls.id[i] : 0;
+                const unsigned long long key = i < nlist ? sh.u.ls.key[i] : 0ull;
+                if (id & kTopCand) tk = umax64(tk, key);
+                const bool band = (id & kBand) != 0;
+                bk[r] = band ? key : 0ull;
+                bwt[r] = band ? sh.u.ls.sz[i] : 0;
+                bs[r] = band ? key_score(key) : 0.f;
+                if (band) {
+                    blo = fminf(blo, bs[r]);
+                    bhi = fmaxf(bhi, bs[r]);
+                }
+            }
+            tk = wave_max_u64(tk);
+            blo = wave_min_f(blo);
+            bhi = wave_max_f(bhi);
+            if (lane == 0) {
+                if (tk) atomicMax(&sh.topkey, tk);
+                sh.red_lo[wave] = blo;
+                sh.red_hi[wave] = bhi;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kSelThreads / 64; ++i) {
+                blo = fminf(blo, sh.red_lo[i]);
+                bhi = fmaxf(bhi, sh.red_hi[i]);
+            }
+            // Cut of the band with the budget the certain communities leave.
+            const int rest = p.budget - tot[2];
+            unsigned long long bthr = 0ull;
+            const int nband = tot[1];
+            if (nband > 0 && nband <= 64) {
+                // few band members: wave 0 compacts them into ckey/csz and each
+                // one sums the weight of the better ones; the cut is the best
+                // member whose inclusive weight overflows what is left
+                if (wave == 0) {
+                    int got = 0;
+                    for (int i0 = 0; i0 < nlist; i0 += 64) {
+                        const int i = i0 + lane;
+                        const bool b = i < nlist && (sh.u.ls.id[i] & kBand);
+                        const unsigned long long m = __ballot(b);
+                        if (b) {
+                            const int at = got + __popcll(m & ((1ull << lane) - 1ull));
+                            sh.ckey[at] = sh.u.ls.key[i];
+                            sh.csz[at] = sh.u.ls.sz[i];
+                        }
+                        got += __popcll(m);
+                    }
+                    const unsigned long long mine = lane < nband ? sh.ckey[lane] : 0ull;
+                    const int msz = lane < nband ? sh.csz[lane] : 0;
+                    long long better = 0;
+                    for (int k0 = 0; k0 < nband; k0 += 8) {  // k0 + 7 < 64: inside ckey/csz
+                        unsigned long long kk[8];
+                        int ss[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            kk[u] = sh.ckey[k0 + u];
+                            ss[u] = sh.csz[k0 + u];
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            if (k0 + u < nband && kk[u] > mine) better += ss[u];
+                    }
+                    const bool over = lane < nband && better + msz > rest;
+                    const unsigned long long cut = wave_max_u64(over ? mine : 0ull);
+                    if (lane == 0) sh.bandthr = cut;
+                }
+                __syncthreads();
+                bthr = sh.bandthr;
+            } else if (nband > 64) {  // uniform
+                if (!value_cut<NB>(bs, bwt, rest, blo, bhi, sh, bthr,
+                                   [&](int r) { return (int)(0xFFFFFFFFu - (uint32_t)bk[r]); }))
+                    bthr = radix_cut<NB>(bk, bwt, false, rest, sh);
+            }
+            // band members above the band cut are taken: marked from the list side
+            for (int i = tid; i < nlist; i += kSelThreads) {
+                const int id = sh.u.ls.id[i];
+                if ((id & kBand) && sh.u.ls.key[i] > bthr) {
+                    const int c = id & 0xFFFF;
+                    atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+                }
+            }
+            CKV_TMARK(56);
+        }
+    }
+    if (any && exact_all) {
+        // Exact scores of every community, one slab at a time, then the cut on them.
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            __syncthreads();
+            exact_scores<D>(p, g, min(kSlab, C - j * kSlab), sh, false, j);
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int e = 4 * j + k;
+                if (4 * tid + k < kSlab && j * kSlab + 4 * tid + k < C) sv[e] = sh.u.exs[4 * tid + k];
+            }
+        }
+        // exact range and best community
+        float elo = __builtin_huge_valf(), ehi = -__builtin_huge_valf();
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            if (s[j] > 0) {
+                elo = fminf(elo, sv[j]);
+                ehi = fmaxf(ehi, sv[j]);
+            }
+        }
+        elo = wave_min_f(elo);
+        ehi = wave_max_f(ehi);
+        __syncthreads();
+        sh.bw[tid] = 0;
+        if (tid == 0) sh.ccount = 0;
+        if (lane == 0) {
+            sh.red_lo[wave] = elo;
+            sh.red_hi[wave] = ehi;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSelThreads / 64; ++i) {
+            elo = fminf(elo, sh.red_lo[i]);
+            ehi = fmaxf(ehi, sh.red_hi[i]);
+        }
+        unsigned long long bk = 0ull;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (s[j] > 0) bk = umax64(bk, comm_key(sv[j], slab_id(tid, j)));
+        bk = wave_max_u64(bk);
+        if (lane == 0 && bk) atomicMax(&sh.topkey, bk);
+        if (!value_cut<EPT>(sv, s, p.budget, elo, ehi, sh, thr, [&](int j) { return slab_id(tid, j); })) {
+            unsigned long long keys[EPT];
+            comm_keys<EPT>(sv, s, keys);
+            thr = radix_cut<EPT>(keys, s, false, p.budget, sh);
+        }
+        if (p.max_comm > 0) {
+            unsigned long long keys[EPT];
+            comm_keys<EPT>(sv, s, keys);
+            thr = umax64(thr, radix_cut<EPT>(keys, s, true, p.max_comm, sh));
+        }
+        cert = 0u;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const uint32_t u = ordered_bits(sv[j] == 0.f ? 0.f : sv[j]), c = (uint32_t)slab_id(tid, j);
+            const uint32_t thr_u = (uint32_t)(thr >> 32), thr_id = 0xFFFFFFFFu - (uint32_t)thr;
+            if (s[j] > 0 && (u > thr_u || (u == thr_u && c < thr_id))) cert |= 1u << j;
+        }
+        __syncthreads();
     }
     CKV_TMARK(12);
 
-    // taken <=> key > thr, tested in 32-bit pieces
-    const uint32_t thr_u = (uint32_t)(thr >> 32), thr_id = 0xFFFFFFFFu - (uint32_t)thr;
+    // taken communities: the certain ones mark their bits (band members above
+    // the band cut are marked already); then every owner reads its bits back
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        if (any && s[j] > 0 && ((cert >> j) & 1u)) {
+            const int c = slab_id(tid, j);
+            atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+        }
+    }
+    __syncthreads();
     bool taken[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const uint32_t u = ordered_bits(sv[j]), c = (uint32_t)slab_id(tid, j);
-        taken[j] = s[j] > 0 && (u > thr_u || (u == thr_u && c < thr_id));
-        if (taken[j]) atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+        const int c = slab_id(tid, j);
+        taken[j] = any && s[j] > 0 && ((sh.bits[c >> 5] >> (c & 31)) & 1u);
     }
-    __syncthreads();
     CKV_TMARK(43);
     // Per slab: taken communities and their base members; then taken tail entries.
     constexpr int NV = 2 * NS + 1;
@@ -454,7 +828,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         for (int k = 0; k < 4; ++k) {
             if (taken[4 * j + k]) {
                 v[j] += 1;
-                v[NS + j] += o1[4 * j + k] - o0[4 * j + k];
+                v[NS + j] += o1(4 * j + k) - o0[4 * j + k];
             }
         }
     }
@@ -488,11 +862,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
             for (int k = 0; k < 4; ++k) {
                 const int e = 4 * j + k;
                 if (taken[e]) {
-                    const int len = o1[e] - o0[e];
+                    const int len = o1(e) - o0[e];
                     p.sel[(size_t)g * C + kpos] = slab_id(tid, e);
                     if (lds_copy) {
-                        sh.soff[kpos] = o0[e];
-                        sh.spref[kpos] = rel;
+                        sh.u.cp.soff[kpos] = o0[e];
+                        sh.u.cp.spref[kpos] = rel;
                     } else {
                         for (int i = 0; i < len; ++i) tl[ns + rel + i] = toks[o0[e] + i];
                     }
@@ -526,10 +900,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
                     int a = 0, b = nsel - 1;
                     while (a < b) {
                         const int mid = (a + b + 1) >> 1;
-                        if (sh.spref[mid] <= j) a = mid;
+                        if (sh.u.cp.spref[mid] <= j) a = mid;
                         else b = mid - 1;
                     }
-                    val[u] = toks[sh.soff[a] + (j - sh.spref[a])];
+                    val[u] = toks[sh.u.cp.soff[a] + (j - sh.u.cp.spref[a])];
                 }
             }
 #pragma unroll
@@ -542,16 +916,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     CKV_TMARK(15);
 
     if (tid == 0) {
-        uint32_t b = 0xFFFFFFFFu;
-        for (int i = 0; i < kSelThreads / 64; ++i) b = min(b, sh.red_id[i]);
+        const unsigned long long tk = sh.topkey;
         p.sel_n[g] = nsel;
         p.tok_n[g] = ns + ntok + ntail;
-        p.top[g] = any ? (int)b : -1;
+        p.top[g] = any && tk ? (int)(0xFFFFFFFFu - (uint32_t)tk) : -1;
     }
     CKV_TMARK(16);
 }
 
-hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *scores, int budget,
+hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, const float *scores, int budget,
                          int max_comm, int t_cap, int32_t *sel, int32_t *sel_n, int32_t *top,
                          int32_t *tok_list, int32_t *tok_n, hipStream_t s) {
     SelectParams p{};
@@ -564,6 +937,11 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *sc
     p.tail_len = idx->tail_len;
     p.n_comm = idx->n_comm;
     p.seq_len = kv->seq_len;
+    p.cscale = idx->cscale;
+    p.csum = idx->csum;
+    p.q = q;
+    p.bf16 = kv->dtype == CKV_DTYPE_BF16;
+    p.D = kv->head_dim;
     p.mode = idx->mode;
     p.Hq = kv->n_q_heads;
     p.Hkv = kv->n_kv_heads;
@@ -583,10 +961,14 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const float *sc
     p.g0 = w.first;
     const int ns = ceil_div(idx->c_cap, kSlab);
     const dim3 grid(w.count), block(kSelThreads);
-    if (ns <= 1) CKV_LAUNCH((select_kernel<1>), grid, block, s, p);
-    else if (ns <= 2) CKV_LAUNCH((select_kernel<2>), grid, block, s, p);
-    else if (ns <= 3) CKV_LAUNCH((select_kernel<3>), grid, block, s, p);
-    else CKV_LAUNCH((select_kernel<4>), grid, block, s, p);
+#define CKV_SEL(N, DD)                                                   \
+    if (ns <= N && kv->head_dim == DD) {                                 \
+        CKV_LAUNCH((select_kernel<N, DD>), grid, block, s, p);           \
+        return hipGetLastError();                                        \
+    }
+    CKV_SEL(1, 64) CKV_SEL(2, 64) CKV_SEL(3, 64) CKV_SEL(4, 64)
+    CKV_SEL(1, 128) CKV_SEL(2, 128) CKV_SEL(3, 128) CKV_SEL(4, 128)
+#undef CKV_SEL
     return hipGetLastError();
 }
 

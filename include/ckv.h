@@ -120,6 +120,9 @@ typedef struct ckv_index {
     int32_t *tail_len;   /* [G] */
     double  *csum;       /* [G][c_cap][head_dim] exact float64 key sum of every community */
     float   *cent;       /* [G][head_dim][c_cap] centroid = float32(csum / size), transposed */
+    int16_t *cq;         /* [G][head_dim][c_cap] screening copy of cent: cent ~ cscale * cq,
+                            cq = round(cent / cscale) in [-32767, 32767] */
+    float   *cscale;     /* [G][c_cap] max_d |cent[d]| / 32767 of every community (0: zero column) */
     int32_t *status;     /* [1] CKV_ST_* bits */
     /* Launch window of the four step calls (score, select, gather, assign):
      * they process graphs win_first .. win_first + win_count - 1 only
@@ -155,26 +158,35 @@ ckv_status ckv_kv_write(const ckv_kv *kv, int32_t b, int32_t kv_head, int32_t po
 ckv_status ckv_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t *labels_in,
                            void *ws, size_t ws_bytes, ckv_stream_t stream);
 
-/* Score every community against the query (Figure 1 panel (3): "score the
- * query against community centroids").  q: [batch][n_q_heads][head_dim] of
- * kv->dtype.  The graph's query is its head's q (per head) or the sum of its
- * group's q (query group; the group's summed q.centroid).  scores: [G][c_cap]
- * float32 = float32(sum_d qbar_d * cent_d) accumulated in float64; -inf for
- * empty communities and ids >= n_comm[g]. */
+/* Screening scores of every community against the query (Figure 1 panel (3):
+ * the query is scored against the community centroids).  q:
+ * [batch][n_q_heads][head_dim] of kv->dtype.  The graph's query qbar is its
+ * head's q (per head) or the sum of its group's q (query group; the group's
+ * summed q . centroid).  The exact score of community c is
+ * float32(sum_d qbar_d * cent[d][c]) with the sum in float64; this call writes
+ * scores[G][c_cap] = cscale[c] * sum_d float32(qbar_d) * cq[d][c] (float32),
+ * within cscale[c] * |qbar|_1 * 0.76 + 2^-20 |score| of the exact score, and
+ * -inf for empty communities and ids >= n_comm[g].  ckv_select_communities
+ * resolves the ranking exactly from these bounds. */
 ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const void *q,
                                float *scores, ckv_stream_t stream);
 
-/* Retrieve communities under the token budget (Figure 1 panel (3): "retrieve
- * a candidate subset").  Communities are ranked by score, higher first, ties to
- * the lower id; the longest prefix of that ranking whose member count stays
- * within `budget` (and, if max_comm > 0, holds at most max_comm communities)
- * is taken: the first community that does not fit ends the walk.
+/* Retrieve communities under the token budget (Figure 1 panel (3): a subset
+ * of the communities is retrieved; Tables 2-3: the subset is bounded by a
+ * token budget).  Communities are ranked by their exact score (see
+ * ckv_score_centroids), higher first, ties to the lower id; the longest prefix
+ * of that ranking whose member count stays within `budget` (and, if
+ * max_comm > 0, holds at most max_comm communities) is taken: the first
+ * community that does not fit ends the walk.  `scores` are the screening
+ * scores of ckv_score_centroids for the same q; exact scores are computed here
+ * (from csum and size) for every community whose screening interval leaves its
+ * place relative to the cut open, so the result is that of the exact scores.
  * Outputs per graph: sel[G][c_cap] taken ids ascending, sel_n[G] their count,
  * top[G] the best-ranked non-empty community (-1 if none), tok_list[G][t_cap]
  * the attended positions (sinks first, then members of the taken communities)
  * and tok_n[G] their count.  Requires t_cap >= n_sinks + min(budget, l_cap). */
-ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const float *scores,
-                                  int32_t budget, int32_t max_comm, int32_t t_cap,
+ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                                  const float *scores, int32_t budget, int32_t max_comm, int32_t t_cap,
                                   int32_t *sel, int32_t *sel_n, int32_t *top,
                                   int32_t *tok_list, int32_t *tok_n, ckv_stream_t stream);
 

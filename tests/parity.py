@@ -71,10 +71,25 @@ def check_index_state(layer, orc: O.Oracle, w: synth.Workload, full: bool = Fals
         assert (size[g, C:] == 0).all()
         cent = idx.cent[g, :, :C].t().cpu().numpy()
         np.testing.assert_array_equal(cent, orc.centroids32(g), err_msg=f"centroids g={g}")
+        check_screening_copy(idx, g, C, cent)
         if full:
             np.testing.assert_array_equal(idx.csum[g, :C].cpu().numpy(), st.sums, err_msg=f"csum g={g}")
             n = orc.len[st.b]
             np.testing.assert_array_equal(idx.label[g, :n].cpu().numpy(), st.labels[:n], err_msg=f"label g={g}")
+
+
+def check_screening_copy(idx, g: int, C: int, cent: np.ndarray):
+    """The int16 screening copy of the centroid table: per community
+    scale = max |cent| / 32767 (float32) and code = round(cent / scale),
+    clamped to +-32767 (0 for a zero column), as the library documents it."""
+    scale = idx.cscale[g, :C].cpu().numpy()
+    code = idx.cq[g, :, :C].t().cpu().numpy().astype(np.int32)
+    want_scale = (np.abs(cent).max(axis=1).astype(np.float32) / np.float32(32767)).astype(np.float32)
+    np.testing.assert_array_equal(scale, want_scale, err_msg=f"cscale g={g}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        want = np.clip(np.rint(cent / want_scale[:, None]), -32767, 32767)
+    want = np.where(want_scale[:, None] > 0, want, 0).astype(np.int32)
+    np.testing.assert_array_equal(code, want, err_msg=f"cq g={g}")
 
 
 def check_csr(layer, orc: O.Oracle):

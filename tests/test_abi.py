@@ -55,7 +55,7 @@ def _kv(**kw):
 def _idx(**kw):
     d = dict(mode=ckv.CKV_MODE_PER_HEAD, n_graphs=32, c_cap=8192, l_cap=131200, tail_cap=256, n_sinks=4)
     for f in ("n_comm", "size", "offs", "toks", "label", "tail_pos", "tail_comm", "tail_len", "csum", "cent",
-              "status"):
+              "cq", "cscale", "status"):
         d[f] = FAKE
     d.update(kw)
     return ckv.CkvIndex(**d)
@@ -97,7 +97,7 @@ def test_kv_validation(kw, code):
 
 @pytest.mark.parametrize("kw", [dict(n_graphs=8), dict(c_cap=1000), dict(c_cap=32768), dict(tail_cap=0),
                                 dict(tail_cap=5000), dict(n_sinks=-1), dict(mode=3), dict(cent=None),
-                                dict(status=None), dict(csum=None)])
+                                dict(status=None), dict(csum=None), dict(cq=None), dict(cscale=None)])
 def test_index_validation(kw):
     kv, idx = _kv(), _idx(**kw)
     assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == ckv.CKV_E_INVALID
@@ -125,12 +125,13 @@ def test_window_view_binding():
 def test_select_validation():
     kv, idx = _kv(), _idx()
     f = ckv.LIB.ckv_select_communities
-    args = lambda budget, mc, tcap, sel=FAKE: (ctypes.byref(kv), ctypes.byref(idx), FAKE, budget, mc, tcap, sel,
-                                               FAKE, FAKE, FAKE, FAKE, None)
+    args = lambda budget, mc, tcap, sel=FAKE, q=FAKE: (ctypes.byref(kv), ctypes.byref(idx), q, FAKE, budget, mc,
+                                                       tcap, sel, FAKE, FAKE, FAKE, FAKE, None)
     assert f(*args(4096, 0, 4099)) == ckv.CKV_E_INVALID   # t_cap below sinks + budget
     assert f(*args(-1, 0, 4100)) == ckv.CKV_E_INVALID
     assert f(*args(4096, -2, 4100)) == ckv.CKV_E_INVALID
     assert f(*args(4096, 0, 4100, sel=None)) == ckv.CKV_E_INVALID
+    assert f(*args(4096, 0, 4100, q=None)) == ckv.CKV_E_INVALID
 
 
 def test_gather_assign_dense_workspace_checks():
