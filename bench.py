@@ -108,7 +108,9 @@ def main():
     row_bytes = 2 * w.head_dim * esz  # K row + V row
     gathered = tok[W:].sum(axis=1) * row_bytes  # bytes per timed step
     n_comm = np.array(synth.graph_n_comm(w, slices), dtype=np.int64)
-    score_bytes = int(n_comm.sum()) * w.head_dim * 4
+    # the scoring kernel streams the int16 screening copy of every used
+    # centroid column plus its scale and member count
+    score_bytes = int(n_comm.sum()) * (w.head_dim * 2 + 8)
 
     # Eager pass: K steps launched one call at a time from Python.
     restore()
