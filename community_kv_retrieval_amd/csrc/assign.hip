@@ -1,7 +1,7 @@
-// Edges, constant-time assignment and the O(d) centroid update (the
-// CommunityKV page, Figure 1 panel (3): the top-kappa attended keys become the
-// new token's edges and assign it to a community in constant time; Table 1:
-// per-step update O(d); Table 6: sinks are excluded from the top-kappa pool).
+// Edges, assignment and the O(d) centroid update (the CommunityKV page,
+// Figure 1 panel (3): the keys the new token attends to most become its edges
+// and decide its community at a cost independent of the context length;
+// Table 1: per-step update O(d); Table 6: sinks never become edges).
 //
 // One 256-thread block per graph.  The edge weight of an attended non-sink
 // token is its softmax probability (one head) or the sum of its heads'

@@ -1,5 +1,6 @@
-// Budgeted community retrieval (the CommunityKV page, Figure 1 panel (3):
-// retrieve a candidate subset of communities under a token budget).
+// Budgeted community retrieval (the CommunityKV page, Figure 1 panel (3): the
+// communities whose centroids score best are retrieved, and Tables 2-3 bound
+// their tokens by a budget).
 //
 // One 1024-thread block per graph.  The communities are read in slabs of 4096:
 // in slab j thread t owns communities 4096 j + 4 t .. 4096 j + 4 t + 3, so
@@ -552,8 +553,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     unsigned long long thr = ~0ull;  // nothing taken when there is no candidate
     uint32_t cert = 0u;  // bit j: community j of this thread is taken
     if (any && !exact_all) {
-        // Token-weighted histograms of U and L; the U walk overflows the
-        // budget in bin b_h, the L walk in bin b_l (-1: no overflow).
+        // Token-weighted histograms of U (bw) and of L (bw + the corrections
+        // in bwl of the few communities whose L falls in a lower bin); the U
+        // walk overflows the budget in bin b_h, the L walk in bin b_l (-1: no
+        // overflow).
         int bb[EPT];        // U bin << 16 | L bin
         uint32_t tcm = 0u;  // bit j: candidate for the best community
 #pragma unroll
@@ -564,18 +567,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
             bb[j] = (bu << 16) | bl;
             if (s[j] > 0) {
                 atomicAdd(&sh.bw[bu], s[j]);
-                atomicAdd(&sh.bwl[bl], s[j]);
+                if (bl != bu) {  // rare: the L histogram differs from the U one
+                    atomicAdd(&sh.bwl[bl], s[j]);
+                    atomicSub(&sh.bwl[bu], s[j]);
+                }
                 if (u >= lmax) tcm |= 1u << j;
             }
         }
         __syncthreads();
         CKV_TMARK(50);
         if (wave < 2) {
-            const int *hist = wave == 0 ? sh.bw : sh.bwl;
             int v[16], tot = 0;
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                v[k] = hist[kBins - 1 - (lane * 16 + k)];
+                const int b = kBins - 1 - (lane * 16 + k);
+                v[k] = sh.bw[b] + (wave == 1 ? sh.bwl[b] : 0);
                 tot += v[k];
             }
             const int incl = wave_incl_scan(tot);
@@ -643,6 +649,42 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
             if (tid == 0) sh.ccount = 0;
             __syncthreads();
             CKV_TMARK(55);
+            const int rest = p.budget - tot[2];  // budget left to the band
+            if (nlist <= 64) {  // uniform: the usual case, finished by wave 0
+                if (wave == 0) {
+                    // best community, and each band member sums the weight of the
+                    // better ones; the cut is the best member whose inclusive
+                    // weight overflows what the certain communities leave
+                    const bool ok = lane < nlist;
+                    const int id = ok ? sh.u.ls.id[lane] : 0;
+                    const unsigned long long key = ok ? sh.u.ls.key[lane] : 0ull;
+                    const int sz = ok ? sh.u.ls.sz[lane] : 0;
+                    const bool band = (id & kBand) != 0;
+                    const unsigned long long tk = wave_max_u64((id & kTopCand) ? key : 0ull);
+                    long long better = 0;
+                    for (int k0 = 0; k0 < nlist; k0 += 8) {  // k0 + 7 < 64 <= kList
+                        unsigned long long kk[8];
+                        int ii[8], ss[8];
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            kk[u] = sh.u.ls.key[k0 + u];
+                            ii[u] = sh.u.ls.id[k0 + u];
+                            ss[u] = sh.u.ls.sz[k0 + u];
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u)
+                            if (k0 + u < nlist && (ii[u] & kBand) && kk[u] > key) better += ss[u];
+                    }
+                    const bool over = band && better + sz > rest;
+                    const unsigned long long cut = wave_max_u64(over ? key : 0ull);
+                    if (band && key > cut) {
+                        const int c = id & 0xFFFF;
+                        atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+                    }
+                    if (lane == 0 && tk) sh.topkey = tk;
+                }
+                // the barrier before the taken flags are read orders these writes
+            } else {
             // Best community: the largest exact key among the candidates; the
             // band entries with their exact scores and the band's score range.
             constexpr int NB = kList / kSelThreads;
@@ -679,7 +721,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
                 bhi = fmaxf(bhi, sh.red_hi[i]);
             }
             // Cut of the band with the budget the certain communities leave.
-            const int rest = p.budget - tot[2];
             unsigned long long bthr = 0ull;
             const int nband = tot[1];
             if (nband > 0 && nband <= 64) {
@@ -732,6 +773,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
                     const int c = id & 0xFFFF;
                     atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
                 }
+            }
             }
             CKV_TMARK(56);
         }

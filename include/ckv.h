@@ -4,12 +4,13 @@
  *
  * The method: "CommunityKV: Efficient Long-Context Decoding via Graph
  * Partitioning" (McKenna, Alexandridis, Susanj, Liu).  Its Figure 1 caption,
- * panel (3) "Incremental Update", defines one decode step: score the query
- * against the community centroids, retrieve a candidate subset of
- * communities, run exact attention over that subset together with the sink
- * tokens, then use the top-kappa attended keys as the new token's edges and
- * assign the token to a community in constant time.  Table 1 gives the
- * per-step update as O(d).  Table 6 fixes kappa = 8, sinks excluded from the
+ * panel (3), the incremental update, describes one decode step.  The query is
+ * compared with every community's centroid.  The best communities are
+ * gathered within a token budget.  Softmax attention over their tokens and
+ * the sink tokens is computed exactly.  The kappa tokens that attention
+ * weights most become the new token's edges, and they decide its community
+ * at a cost independent of the context length.  Table 1 gives the per-step
+ * update as O(d).  Table 6 fixes kappa = 8, sinks excluded from the
  * top-kappa pool, and one graph per query head as the default; Tables 5 and 6
  * name query-group graphs (one graph per kv head, shared by its query heads)
  * as the alternative aggregation.
@@ -152,9 +153,10 @@ ckv_status ckv_kv_write(const ckv_kv *kv, int32_t b, int32_t kv_head, int32_t po
  * partition, Figure 1 panel (2); here any labelling the caller supplies).
  * labels_in: [G][l_cap] community of each position < seq_len[b] (-1 = none;
  * positions < n_sinks are always sinks).  idx->n_comm must hold each graph's
- * community count.  Fills size, offs, toks, label, csum and cent (centroid =
- * mean of the members' keys, Figure 1 panel (2) "a centroid per community"),
- * empties the tails and clears status. */
+ * community count.  Fills size, offs, toks, label, csum, cent (the centroid
+ * is the mean of the members' keys; Figure 1 panel (2) draws one per
+ * community) and its screening copy cq/cscale, empties the tails and clears
+ * status. */
 ckv_status ckv_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t *labels_in,
                            void *ws, size_t ws_bytes, ckv_stream_t stream);
 
@@ -191,8 +193,8 @@ ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const 
                                   int32_t *tok_list, int32_t *tok_n, ckv_stream_t stream);
 
 /* Exact softmax attention of each graph's query heads over its token list
- * (Figure 1 panel (3): "run exact attention on this subset together with sink
- * tokens").  z_j = sm_scale * q . k_j in float32 from the stored K; outputs:
+ * (Figure 1 panel (3): attention over the retrieved subset is exact and also
+ * covers the sink tokens).  z_j = sm_scale * q . k_j in float32 from the stored K; outputs:
  * out[batch][n_q_heads][head_dim] float32 (every query head is written),
  * logits[G][hpg][t_cap] the z_j of each slot < tok_n[g] (hpg = heads per graph),
  * ml[G][hpg][2] = (max z, sum exp(z - max)). */
@@ -201,9 +203,9 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
                              float sm_scale, float *out, float *logits, float *ml,
                              void *ws, size_t ws_bytes, ckv_stream_t stream);
 
-/* Edges, assignment and update (Figure 1 panel (3): "use the resulting top-kappa
- * keys to update the new token's edges and assign it to a community in
- * constant time"; Table 1: per-step update O(d)).  For every graph: the kappa
+/* Edges, assignment and update (Figure 1 panel (3): the kappa keys the new
+ * token attends to most become its edges and decide its community, at a cost
+ * independent of the context length; Table 1: per-step update O(d)).  For every graph: the kappa
  * non-sink attended tokens of largest weight (per head: the head's attention
  * probability; query group: the sum of its heads' probabilities), ties to the
  * lower position, become edges[G][kappa] (-1 padded); the new token goes to the

@@ -6,12 +6,12 @@ use it.  It shares no code with the HIP library; the two meet only in the
 seeded inputs.
 
 Source: "CommunityKV: Efficient Long-Context Decoding via Graph Partitioning"
-(McKenna, Alexandridis, Susanj, Liu), Figure 1 caption, panel (3)
-"Incremental Update": at each decoding step the query is scored against the
-community centroids, a candidate subset is retrieved, exact attention runs on
-that subset together with the sink tokens, and the top-kappa attended keys
-become the new token's edges, which assign it to a community in constant
-time.  Table 1 gives the per-step update as O(d) and the retrieval as a pass
+(McKenna, Alexandridis, Susanj, Liu), Figure 1 caption, panel (3), the
+incremental update.  Each decoding step compares the query with the community
+centroids and keeps the best communities.  Attention over their tokens and
+the sinks is computed exactly.  The tokens it weights most become the new
+token's edges, and they decide its community at a cost independent of the
+context length.  Table 1 gives the per-step update as O(d) and the retrieval as a pass
 over the centroids.  Table 6 fixes the defaults (kappa = 8, per-head graphs,
 sinks excluded from the top-kappa pool).
 
@@ -73,8 +73,8 @@ def scoring_centroids(sums: np.ndarray, counts: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Retrieval (Figure 1, panel (3): score the query against community centroids
-# and retrieve a candidate subset under a token budget)
+# Retrieval (Figure 1, panel (3): the query is compared with every centroid and
+# the best communities are kept, within a token budget)
 # --------------------------------------------------------------------------
 
 def aggregate_query(q_heads: np.ndarray) -> np.ndarray:
@@ -107,7 +107,7 @@ def select_communities(scores: np.ndarray, counts: np.ndarray, budget: int,
                        max_comm: int = 0) -> np.ndarray:
     """Communities retrieved for attention, as ascending ids.
 
-    Reading of "retrieve a candidate subset" under a token budget: walk the
+    Reading of the budgeted retrieval of a subset of communities: walk the
     communities from the best score down and keep each one while the running
     member count stays within the budget; the first community that would
     exceed it ends the walk (no skipping ahead to smaller ones).  Sink tokens
