@@ -17,6 +17,8 @@
 // partial records are padded to whole cache lines and written and read with
 // device-scope accesses, and each block waits for its stores before it counts
 // itself in.
+#include <cstdlib>
+
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -38,8 +40,9 @@ struct AttendParams {
     float *ml;
     float *part;
     int32_t *ctr;
-    int nchunk;  // blocks per unit
-    int g0;      // first unit of the launch window
+    int nchunk;     // blocks per unit
+    int per_block;  // tokens per block (gather)
+    int g0;         // first unit of the launch window
 };
 
 template <typename T, int D, int NH>
@@ -224,11 +227,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     using RS = RowSlice<T, D>;
     constexpr int E = RS::E;
     constexpr int SPAN = 16 * U;
-    constexpr int PER_BLOCK = DENSE ? kDenseTokens : kGatherTokens;
-    constexpr int ITERS = PER_BLOCK / SPAN;
+    constexpr int MAX_BLOCK = DENSE ? kDenseTokens : kGatherMaxTokens;
+    const int PER_BLOCK = DENSE ? kDenseTokens : a.per_block;  // a multiple of SPAN, <= MAX_BLOCK
+    const int ITERS = PER_BLOCK / SPAN;
     constexpr int PS = part_stride(D);
 
-    __shared__ uint32_t s_row[PER_BLOCK];
+    __shared__ uint32_t s_row[MAX_BLOCK];
     __shared__ float s_q[NH][D];
     __shared__ float s_wm[4][NH], s_wl[4][NH];
     __shared__ float s_wacc[4][NH][D];
@@ -470,6 +474,18 @@ static hipError_t dispatch(const ckv_kv *kv, int nh, const AttendParams &p, int 
     return hipErrorInvalidValue;
 }
 
+// Tokens per gather block.  256 (two passes of 128) measured best for every
+// workload here: longer spans (512, 1024) pay less per-block staging and
+// split-K but lose more to blocks that share a compute unit.
+// CKV_GATHER_TOKENS = 512 or 1024 overrides it (tuning).
+static int gather_span() {
+    if (const char *e = getenv("CKV_GATHER_TOKENS")) {
+        const int v = atoi(e);
+        if (v == 2 * kGatherTokens || v == kGatherMaxTokens) return v;
+    }
+    return kGatherTokens;
+}
+
 hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
                          const int32_t *tok_list, const int32_t *tok_n, int t_cap, float sm_scale,
                          float *out, float *logits, float *ml, float *part, int32_t *ctr,
@@ -493,7 +509,8 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
     p.ml = ml;
     p.part = part;
     p.ctr = ctr;
-    p.nchunk = ceil_div(t_cap, kGatherTokens);
+    p.per_block = gather_span();
+    p.nchunk = ceil_div(t_cap, p.per_block);
     const Window w = window_of(idx);
     p.g0 = w.first;
     return dispatch<false>(kv, heads_per_graph(kv, idx), p, w.count, s);

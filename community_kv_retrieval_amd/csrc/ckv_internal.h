@@ -12,9 +12,12 @@
 namespace ckv {
 
 // Tokens one gather block attends: 16 tokens per pass of its 256 threads
-// (4 waves x 4 rows of 16 lanes), kGatherU passes per block.
+// (4 waves x 4 rows of 16 lanes), kGatherU passes per iteration.  The smallest
+// block span is kGatherTokens (the workspace holds a partial per such span);
+// larger problems use 2x or 4x longer spans (at most kGatherMaxTokens).
 constexpr int kGatherU = 8;
 constexpr int kGatherTokens = 16 * kGatherU * 2;
+constexpr int kGatherMaxTokens = 4 * kGatherTokens;
 // The dense baseline walks kDenseIters such spans per block.
 constexpr int kDenseU = 8;
 constexpr int kDenseIters = 8;
