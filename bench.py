@@ -50,6 +50,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--recall-steps", type=int, default=16,
+                    help="steps per budget of the attention-mass recall sweep (0: skip)")
     ap.add_argument("--profile", action="store_true", help="only warm-up + timed steps (for rocprofv3 runs)")
     ap.add_argument("--eager-only", action="store_true", help="with --profile: no HIP graph (counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -230,6 +232,29 @@ def main():
         dense = {"us_per_call": round(d_us, 2), "bytes": d_bytes, "gbps": round(d_bytes / (d_us * 1e-6) / 1e9, 1),
                  "frac_of_8tbps": round(d_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
+    # Attention-mass recall (the page's Figure 3 quality proxy): the share of
+    # each head's dense softmax mass that the attended tokens carry, per budget.
+    recall = None
+    if args.recall_steps > 0:
+        recall = {}
+        budget0 = dec.budget
+        dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
+        dout = torch.empty_like(buf.out)
+        for B in [b for b in (128, 512, 1024, 2048, 4096) if b <= budget0]:
+            restore()
+            dec.budget = B
+            vals = []
+            for t in range(min(args.recall_steps, total)):
+                dec.retrieve(Q[t])
+                dec.attend(Q[t])
+                dec.dense(Q[t], dout, ml=dml)
+                vals.append(dec.recall(dml).flatten())
+                dec.update(KN[t], VN[t])
+            v = torch.cat(vals).cpu().numpy()
+            recall[str(B)] = {"mean": round(float(v.mean()), 4), "p10": round(float(np.percentile(v, 10)), 4),
+                              "min": round(float(v.min()), 4)}
+        dec.budget = budget0
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.seed, slices, steps_in, args.cpu_seconds)
@@ -271,6 +296,7 @@ def main():
                          "p90": round(float(np.percentile(cold_us, 90)), 2)},
         "tokens_per_step": round(float(tok[W:].sum(axis=1).mean()), 1),
         "dense_flash_decode": dense,
+        "attention_mass_recall": recall,
         "cpu_baseline": cpu,
         "ms_per_step_eager": round(ms_eager, 5),
         "launch": "hip_graph",

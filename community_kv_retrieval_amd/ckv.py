@@ -73,7 +73,7 @@ def _load():
         "ckv_assign_update": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                         c_void_p]),
-        "ckv_dense_attend": (c_int32, [KVP, c_void_p, c_float, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_dense_attend": (c_int32, [KVP, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_time_next_launch": (c_int32, [c_void_p, c_void_p]),
         "ckv_status_str": (ctypes.c_char_p, [c_int32]),
         "ckv_abi_version": (c_int32, []),
@@ -278,11 +278,14 @@ def ckv_assign_update(kv: KVStore, idx: CommunityIndex, tok_list: torch.Tensor, 
 
 
 def ckv_dense_attend(kv: KVStore, q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor,
-                     stream=None):
+                     stream=None, ml: Optional[torch.Tensor] = None):
     _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
     _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
+    if ml is not None:
+        _need(ml, "ml", torch.float32, (kv.batch, kv.n_q_heads, 2))
     _check("ckv_dense_attend", LIB.ckv_dense_attend(ctypes.byref(kv.desc), _ptr(q), float(sm_scale), _ptr(out),
-                                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                                                    _ptr(ml), _ptr(ws), ws.numel() * ws.element_size(),
+                                                    _stream(stream)))
 
 
 def ckv_time_next_launch(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]):
@@ -397,6 +400,26 @@ class Decoder:
             cur.wait_event(done)
         return b.out
 
-    def dense(self, q: torch.Tensor, out: torch.Tensor, stream=None):
-        ckv_dense_attend(self.kv, q, self.sm_scale, out, self.buf.ws, stream)
+    def dense(self, q: torch.Tensor, out: torch.Tensor, stream=None, ml: Optional[torch.Tensor] = None):
+        ckv_dense_attend(self.kv, q, self.sm_scale, out, self.buf.ws, stream, ml=ml)
         return out
+
+    def recall(self, dense_ml: torch.Tensor) -> torch.Tensor:
+        """Attention-mass recall of the last gather, per graph and head: the
+        share of the dense softmax mass (dense_ml from dense(..., ml=)) that the
+        attended tokens carry, exp(lse_attended - lse_all) (page Figure 3).
+        Host-side arithmetic on kernel outputs (a diagnostic, not a step)."""
+        kv, idx, b = self.kv, self.idx, self.buf
+        G, nh = idx.n_graphs, idx.heads_per_graph(kv)
+        g = torch.arange(G, device=dense_ml.device)
+        if idx.mode == CKV_MODE_PER_HEAD:
+            bb, qh = g // kv.n_q_heads, g % kv.n_q_heads
+            heads = qh[:, None]
+        else:
+            bb, kh = g // kv.n_kv_heads, g % kv.n_kv_heads
+            heads = kh[:, None] * kv.group + torch.arange(nh, device=dense_ml.device)[None, :]
+        d = dense_ml[bb[:, None], heads]  # [G][nh][2]
+        s = b.ml.double()
+        lse_t = s[..., 0] + torch.log(s[..., 1])
+        lse_d = d[..., 0].double() + torch.log(d[..., 1].double())
+        return torch.exp(lse_t - lse_d)

@@ -189,14 +189,14 @@ ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32
                                     edges, assign, (int32_t *)at(ws, L.ctr_assign), (hipStream_t)stream));
 }
 
-ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out, void *ws,
-                            size_t ws_bytes, ckv_stream_t stream) {
+ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
+                            void *ws, size_t ws_bytes, ckv_stream_t stream) {
     ckv_status st = check_kv(kv);
     if (st != CKV_OK) return st;
     if (!q || !out) return CKV_E_INVALID;
     const WsLayout L = ws_layout(kv, nullptr, 0);
     if (!ws || ws_bytes < L.dense_total) return CKV_E_WORKSPACE;
-    return hip_status(launch_dense(kv, q, sm_scale, out, (float *)at(ws, L.part_dense),
+    return hip_status(launch_dense(kv, q, sm_scale, out, ml, (float *)at(ws, L.part_dense),
                                    (int32_t *)at(ws, L.ctr_dense), (hipStream_t)stream));
 }
 

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     const int start = chunk * PER_BLOCK;
     if (n <= 0 && chunk == 0) {  // nothing to attend: zero output, empty softmax state
         for (int i = tid; i < NH * D; i += 256) a.out[((size_t)b * a.Hq + qh0) * D + i] = 0.f;
-        if (!DENSE && tid < NH) {
+        if (a.ml && tid < NH) {
             a.ml[((size_t)unit * NH + tid) * 2] = kNegInf;
             a.ml[((size_t)unit * NH + tid) * 2 + 1] = 0.f;
         }
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         }
         if (nact == 1) {
             a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = o / L;
-            if (!DENSE && d == 0) {
+            if (a.ml && d == 0) {
                 a.ml[((size_t)unit * NH + h) * 2] = M;
                 a.ml[((size_t)unit * NH + h) * 2 + 1] = L;
             }
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     if (!s_last) return;
     merge_partials<D, NH, PS>(P, a.nchunk, nact, s_scale, s_red,
                               a.out + ((size_t)b * a.Hq + qh0) * D,
-                              DENSE ? nullptr : a.ml + (size_t)unit * NH * 2);
+                              a.ml ? a.ml + (size_t)unit * NH * 2 : nullptr);
     if (tid == 0) reset_counter(&a.ctr[unit]);
     if constexpr (!DENSE) CKV_TMARK(24);
     if constexpr (!DENSE) CKV_BMARK(5);
@@ -516,8 +516,8 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
     return dispatch<false>(kv, heads_per_graph(kv, idx), p, w.count, s);
 }
 
-hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *part,
-                        int32_t *ctr, hipStream_t s) {
+hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
+                        float *part, int32_t *ctr, hipStream_t s) {
     AttendParams p{};
     p.kv = kv->kv;
     p.page_table = kv->page_table;
@@ -531,6 +531,7 @@ hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *
     p.mode = CKV_MODE_QUERY_GROUP;
     p.sm_scale = sm_scale;
     p.out = out;
+    p.ml = ml;
     p.part = part;
     p.ctr = ctr;
     p.nchunk = ceil_div(ctx_cap(kv), kDenseTokens);

@@ -122,8 +122,8 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
                          const int32_t *tok_list, const int32_t *tok_n, int t_cap, float sm_scale,
                          float *out, float *logits, float *ml, float *part, int32_t *ctr,
                          hipStream_t s);
-hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *part,
-                        int32_t *ctr, hipStream_t s);
+hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
+                        float *part, int32_t *ctr, hipStream_t s);
 hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
                          const int32_t *tok_n, const float *logits, const float *ml, int t_cap,
                          const int32_t *top, int kappa, const void *k_new, const void *v_new,

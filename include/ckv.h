@@ -221,8 +221,13 @@ ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32
                              int32_t *assign, void *ws, size_t ws_bytes, ckv_stream_t stream);
 
 /* Dense flash-decode baseline: softmax attention of every query head over all
- * seq_len[b] cached tokens of its kv head.  out[batch][n_q_heads][head_dim]. */
-ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out,
+ * seq_len[b] cached tokens of its kv head.  out[batch][n_q_heads][head_dim];
+ * ml (NULL: not written) [batch][n_q_heads][2] = (max z, sum exp(z - max)) of
+ * every head over all its tokens.  With the ml of ckv_gather_attend for the
+ * same q, exp(m_T + log l_T - m - log l) is the share of the dense attention
+ * mass that the attended tokens carry (the page's attention-mass recall,
+ * Figure 3). */
+ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
                             void *ws, size_t ws_bytes, ckv_stream_t stream);
 
 /* Kernel timing for profiling harnesses (no part of the method).  Arms the

@@ -172,6 +172,19 @@ def dense_attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_s
     return out / e.sum(axis=1, keepdims=True)
 
 
+def attention_mass_recall(q_heads: np.ndarray, keys: np.ndarray, positions: np.ndarray,
+                          sm_scale: float) -> np.ndarray:
+    """Share of each head's dense softmax mass over every cached token that
+    the attended positions carry (the page's attention-mass recall, Figure 3):
+    sum over j in positions of softmax_j(sm_scale * q . K^T).  One value per
+    head; 1 when every cached token is attended."""
+    q = np.asarray(q_heads, dtype=np.float64).reshape(-1, np.shape(q_heads)[-1])
+    z = float(sm_scale) * (q @ np.asarray(keys, dtype=np.float64).T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return p[:, np.asarray(positions, dtype=np.int64)].sum(axis=1)
+
+
 # --------------------------------------------------------------------------
 # Incremental update (Figure 1, panel (3); Table 1 "Per-step Update O(d)")
 # --------------------------------------------------------------------------
@@ -356,6 +369,13 @@ class Oracle:
             self.V[(b, kh)][P] = np.asarray(v_new[b][kh], dtype=np.float32)
         for b in {b for (b, _) in self.K}:
             self.len[b] += 1
+
+    def recall(self, gid: int, q, positions) -> np.ndarray:
+        """Attention-mass recall of graph gid's heads for the given attended positions."""
+        st = self.g[gid]
+        n = self.len[st.b]
+        return attention_mass_recall(self.graph_query(gid, q), self.K[(st.b, st.kh)][:n], positions,
+                                     self.w.sm_scale)
 
     def dense(self, q, b: int, kh: int) -> np.ndarray:
         """Dense attention of kv head kh's query heads over all cached tokens of sequence b."""

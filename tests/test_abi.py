@@ -150,7 +150,7 @@ def test_gather_assign_dense_workspace_checks():
     assert a(33, FAKE, need) == ckv.CKV_E_INVALID
     assert a(8, None, need) == ckv.CKV_E_WORKSPACE
     assert a(8, FAKE, need - 1) == ckv.CKV_E_WORKSPACE
-    d = ckv.LIB.ckv_dense_attend(ctypes.byref(kv), FAKE, 1.0, FAKE, FAKE, _ws(kv, None, 0) - 1, None)
+    d = ckv.LIB.ckv_dense_attend(ctypes.byref(kv), FAKE, 1.0, FAKE, None, FAKE, _ws(kv, None, 0) - 1, None)
     assert d == ckv.CKV_E_WORKSPACE
 
 

@@ -260,3 +260,32 @@ def test_dense_baseline_matches_oracle():
             ref = orc.dense(inp.q.float().numpy(), b, kh)
             g = got[b, kh * 4:(kh + 1) * 4]
             assert np.all(np.abs(g - ref) <= PY.ATOL + PY.RTOL * np.abs(ref))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("group", [False, True])
+def test_attention_mass_recall_matches_oracle(group):
+    """The share of dense attention mass the attended tokens carry, from the
+    kernels' (max, sum) outputs, against the oracle's definition."""
+    w = small_group(batch=2, n_ctx=5000, min_ctx=2000, steps=3) if group else small_per_head(n_ctx=6000, steps=3)
+    PY.log(f"recall group={group}")
+    layer, orc = PY.make_pair(w, 31, 3)
+    dec, buf = layer.dec, layer.dec.buf
+    dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
+    dout = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    for t in range(3):
+        inp = synth.gen_step(w, 31, t, layer.slices)
+        q = inp.q.cuda()
+        dec.retrieve(q)
+        dec.attend(q)
+        dec.dense(q, dout, ml=dml)
+        rec = dec.recall(dml).cpu().numpy()
+        tl, tn = buf.tok_list.cpu().numpy(), buf.tok_n.cpu().numpy()
+        qn = inp.q.float().numpy()
+        for g in orc.graph_ids:
+            ref = orc.recall(g, qn, np.sort(tl[g, :tn[g]]))
+            np.testing.assert_allclose(rec[g], ref, rtol=1e-4, atol=1e-7, err_msg=f"step {t} graph {g}")
+            assert np.all(rec[g] <= 1 + 1e-5) and np.all(rec[g] > 0)
+        dec.update(inp.k_new.cuda(), inp.v_new.cuda())
+        torch.cuda.synchronize()
+        orc.append(inp.k_new.float().numpy(), inp.v_new.float().numpy())

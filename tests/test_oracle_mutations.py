@@ -24,7 +24,9 @@ def _pins():
                P.test_attend_matches_torch_sdpa_float64, P.test_dense_chunking_is_exact,
                P.test_attended_positions_brute_force,
                P.test_top_kappa_excludes_sinks_and_takes_all_when_short,
-               P.test_group_weights_explicit_loop, P.test_budget_walk_invariants_on_workload]
+               P.test_group_weights_explicit_loop, P.test_budget_walk_invariants_on_workload,
+               P.test_recall_two_tokens_closed_form, P.test_recall_brute_force_loops,
+               P.test_recall_full_set_is_one_and_complements_add_up]
     checks += [lambda s=s: P.test_select_matches_definition(s) for s in range(40)]
     checks += [lambda s=s: P.test_top_kappa_matches_heap(s) for s in range(20)]
     checks += [lambda s=s: P.test_vote_matches_counter(s) for s in range(20)]
@@ -176,6 +178,17 @@ def m_dense_last_chunk_only(q_heads, keys, values, sm_scale, chunk=1 << 15):
     return _orig["attend"](q_heads, keys[lo:], values[lo:], sm_scale)[0]
 
 
+def m_recall_unnormalised(q_heads, keys, positions, sm_scale):
+    q = np.asarray(q_heads, np.float64).reshape(-1, np.shape(q_heads)[-1])
+    z = float(sm_scale) * (q @ np.asarray(keys, np.float64).T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    return p[:, np.asarray(positions, np.int64)].sum(axis=1)
+
+
+def m_recall_no_scale(q_heads, keys, positions, sm_scale):
+    return _orig["attention_mass_recall"](q_heads, keys, positions, 1.0)
+
+
 MUTANTS = {
     "score_communities": [m_score_sign, m_score_no_empty_mask],
     "select_communities": [m_select_overflow_included, m_select_skip_ahead],
@@ -189,6 +202,7 @@ MUTANTS = {
     "community_means": [m_means_off_by_one],
     "community_sums": [m_sums_skip_first],
     "dense_attend": [m_dense_last_chunk_only],
+    "attention_mass_recall": [m_recall_unnormalised, m_recall_no_scale],
 }
 
 

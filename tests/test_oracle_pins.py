@@ -366,3 +366,39 @@ def test_budget_walk_invariants_on_workload():
         assert taken + st.counts[nxt] > 40
         assert r.scores[r.selected].min() >= r.scores[rest].max()
     assert len(r.positions) == taken + w.n_sinks
+
+
+# --------------------------------------------------------------------------
+# Attention-mass recall (Figure 3): the share of the dense softmax mass that
+# the attended positions carry.
+# --------------------------------------------------------------------------
+
+def test_recall_two_tokens_closed_form():
+    # z = (0, log 3): softmax (1/4, 3/4); attending token 1 alone captures 3/4
+    q = np.array([[1.0, 0.0]])
+    K = np.array([[0.0, 0.0], [np.log(3.0), 0.0]])
+    np.testing.assert_allclose(O.attention_mass_recall(q, K, [1], 1.0), [0.75], rtol=1e-15)
+    np.testing.assert_allclose(O.attention_mass_recall(q, K, [0], 1.0), [0.25], rtol=1e-15)
+
+
+def test_recall_brute_force_loops():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 4))
+    K = rng.standard_normal((7, 4))
+    pos = [1, 4, 6]
+    want = []
+    for h in range(3):
+        w = [math.exp(0.5 * sum(q[h, i] * K[j, i] for i in range(4))) for j in range(7)]
+        want.append(sum(w[j] for j in pos) / sum(w))
+    np.testing.assert_allclose(O.attention_mass_recall(q, K, pos, 0.5), want, rtol=1e-12)
+
+
+def test_recall_full_set_is_one_and_complements_add_up():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 8))
+    K = rng.standard_normal((50, 8)) * 3
+    a = rng.choice(50, size=17, replace=False)
+    b = np.setdiff1d(np.arange(50), a)
+    np.testing.assert_allclose(O.attention_mass_recall(q, K, np.arange(50), 1.0), [1.0, 1.0], rtol=1e-14)
+    np.testing.assert_allclose(O.attention_mass_recall(q, K, a, 1.0) + O.attention_mass_recall(q, K, b, 1.0),
+                               [1.0, 1.0], rtol=1e-14)
