@@ -52,3 +52,59 @@ def load_layer(w: synth.Workload, seed: int, extra: int, layer: int = 0, device:
     dec = ckv.Decoder(kv, idx, w.budget if budget is None else budget, w.max_comm, w.kappa, w.sm_scale, device)
     dec.build(torch.from_numpy(labels).to(device))
     return Layer(kv, idx, dec, slices, lens)
+
+
+@dataclass
+class StackLayer:
+    """One layer of a multi-layer stack, with its step inputs on the device."""
+    kv: ckv.KVStore
+    idx: ckv.CommunityIndex
+    dec: ckv.Decoder
+    parts: list          # parts[b][kh]: host Partition (labels, n_comm; no centres)
+    q: torch.Tensor      # [steps][B][Hq][d]
+    k_new: torch.Tensor  # [steps][B][Hkv][d]
+    v_new: torch.Tensor
+
+
+def load_stack(w: synth.Workload, seed: int, steps: int, device: str = "cuda", page_size: int = 16,
+               layers: Optional[List[int]] = None, log=None) -> List[StackLayer]:
+    """Every layer of workload `w` (or the listed ones) with keys and values
+    drawn on the device, the store sized for n_ctx + steps tokens per sequence,
+    and `steps` decode steps of inputs per layer."""
+    lens = synth.seq_lengths(w, seed)
+    cap = w.n_ctx + max(steps, 1)
+    mode = ckv.CKV_MODE_PER_HEAD if w.mode == synth.PER_HEAD else ckv.CKV_MODE_QUERY_GROUP
+    out = []
+    for layer in (range(w.n_layers) if layers is None else layers):
+        parts = [[synth.gen_partition(w, seed, layer, b, kh, lens[b], with_centers=False)
+                  for kh in range(w.n_kv_heads)] for b in range(w.batch)]
+        n_comm = np.array([[p.n_comm for p in row] for row in parts], dtype=np.int64)
+        offsets = np.concatenate([[0], np.cumsum(n_comm.ravel())[:-1]]).reshape(n_comm.shape)
+        kv = ckv.KVStore(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.torch_dtype, cap, page_size,
+                         device, shuffle_pages=True, seed=seed + 1000 * layer, seq_len=lens)
+        cents = []
+        for b in range(w.batch):
+            for kh in range(w.n_kv_heads):
+                c, k, v = synth.gen_slice_device(w, seed, layer, b, kh, parts[b][kh], device)
+                ckv.ckv_kv_write(kv, b, kh, 0, k, v)
+                cents.append(c)
+                del k, v
+        centers = torch.cat(cents)
+        del cents
+        q, kn, vn = synth.gen_steps_device(w, seed, layer, steps, centers, offsets, n_comm, device)
+        del centers
+        labels = torch.full((w.n_graphs, cap), -1, dtype=torch.int32)
+        for g in range(w.n_graphs):
+            b, kh, _, _ = w.graph_coords(g)
+            lab = parts[b][kh].labels
+            labels[g, :lab.shape[0]] = torch.from_numpy(lab)
+        gn = [int(n_comm[w.graph_coords(g)[0], w.graph_coords(g)[1]]) for g in range(w.n_graphs)]
+        idx = ckv.CommunityIndex(kv, mode, gn, l_cap=cap, tail_cap=max(1, min(4096, steps)),
+                                 n_sinks=w.n_sinks, device=device)
+        dec = ckv.Decoder(kv, idx, w.budget, w.max_comm, w.kappa, w.sm_scale, device)
+        dec.build(labels.to(device))
+        out.append(StackLayer(kv, idx, dec, parts, q, kn, vn))
+        if log is not None:
+            log(f"layer {layer}: {sum(lens)} tokens, {int(n_comm.sum())} communities")
+    torch.cuda.synchronize()
+    return out

@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 # stream tags for SeedSequence spawn keys
-_T_PART, _T_KEY, _T_VAL, _T_STEP, _T_LEN = 1, 2, 3, 4, 5
+_T_PART, _T_KEY, _T_VAL, _T_STEP, _T_LEN, _T_DEV, _T_DEV_STEP = 1, 2, 3, 4, 5, 6, 7
 
 PER_HEAD = "per_head"
 GROUP = "group"
@@ -158,8 +158,10 @@ class Partition:
     n_comm: int
 
 
-def gen_partition(w: Workload, seed: int, layer: int, b: int, kh: int, n: int) -> Partition:
-    """Draw centres and labels for positions 0..n-1 (0..n_sinks-1 are sinks)."""
+def gen_partition(w: Workload, seed: int, layer: int, b: int, kh: int, n: int,
+                  with_centers: bool = True) -> Partition:
+    """Draw centres and labels for positions 0..n-1 (0..n_sinks-1 are sinks).
+    The centres are the last draw, so with_centers=False gives the same labels."""
     r = _rng(seed, _T_PART, layer, b, kh)
     d = w.head_dim
     labels = np.full(n, -1, dtype=np.int32)
@@ -187,7 +189,7 @@ def gen_partition(w: Workload, seed: int, layer: int, b: int, kh: int, n: int) -
     perm = r.permutation(np.arange(w.n_sinks, n, dtype=np.int32))
     lab = np.repeat(np.arange(C, dtype=np.int32), sizes)
     labels[perm] = lab
-    centers = r.standard_normal((C, d), dtype=np.float32)
+    centers = r.standard_normal((C, d), dtype=np.float32) if with_centers else None
     return Partition(centers, labels, C)
 
 
@@ -284,3 +286,58 @@ def gen_step(w: Workload, seed: int, step: int, slices: List[List[Slice]], layer
             kn[b, kh] = (part.centers[cs[0]] + np.float32(w.noise) * kk) * np.float32(w.key_scale)
             vn[b, kh] = r.standard_normal(d, dtype=np.float32)
     return StepInput(_to_storage(q, w), _to_storage(kn, w), _to_storage(vn, w), tgt)
+
+
+# --------------------------------------------------------------------------
+# Device-side streams for the multi-layer workload.  The key, value and centre
+# draws of one slice come from a torch generator on the GPU seeded from the
+# slice's SeedSequence key, so any slice can be regenerated (and copied to
+# the host for the oracle) on its own; the labels use the host partition
+# stream above.
+# --------------------------------------------------------------------------
+
+def torch_generator(seed: int, tag: int, *key: int, device="cuda") -> torch.Generator:
+    ss = np.random.SeedSequence(entropy=seed, spawn_key=(tag,) + tuple(key))
+    g = torch.Generator(device=device)
+    g.manual_seed(int(ss.generate_state(1, dtype=np.uint64)[0] & np.uint64(0x7FFFFFFFFFFFFFFF)))
+    return g
+
+
+def gen_slice_device(w: Workload, seed: int, layer: int, b: int, kh: int, part: Partition, device="cuda"):
+    """Centres [C][d] (float32) and keys, values [n][d] (storage dtype) of one
+    slice, drawn on the device: keys are (centre of the label + noise) *
+    key_scale, sinks pure noise * key_scale, values N(0, I)."""
+    n, d, s = part.labels.shape[0], w.head_dim, w.n_sinks
+    g = torch_generator(seed, _T_DEV, layer, b, kh, device=device)
+    centers = torch.randn((part.n_comm, d), generator=g, device=device)
+    k = torch.randn((n, d), generator=g, device=device)
+    v = torch.randn((n, d), generator=g, device=device)
+    lab = torch.from_numpy(part.labels[s:].astype(np.int64)).to(device)
+    k[s:] = centers[lab] + float(w.noise) * k[s:]
+    k.mul_(float(w.key_scale))
+    return centers, k.to(w.torch_dtype), v.to(w.torch_dtype)
+
+
+def gen_steps_device(w: Workload, seed: int, layer: int, steps: int, centers: torch.Tensor,
+                     offsets: np.ndarray, n_comm: np.ndarray, device="cuda"):
+    """Queries, new keys and new values of `steps` decode steps of one layer,
+    as device tensors [steps][B][Hq][d], [steps][B][Hkv][d], [steps][B][Hkv][d].
+    `centers` holds the layer's centres, slice (b, kh) at rows
+    offsets[b, kh] .. offsets[b, kh] + n_comm[b, kh].  Same rules as gen_step:
+    every query head draws a planted centre of its kv head (the heads of a
+    group share one in group mode), the new key follows the group's first
+    head's centre."""
+    B, Hq, Hkv, d, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    r = _rng(seed, _T_DEV_STEP, layer)
+    u = r.random((steps, B, Hkv, G))
+    if w.mode != PER_HEAD:
+        u[..., 1:] = u[..., :1]
+    cs = np.minimum((u * n_comm[None, :, :, None]).astype(np.int64), n_comm[None, :, :, None] - 1)
+    rows = torch.from_numpy((cs + offsets[None, :, :, None]).reshape(steps, B, Hq)).to(device)
+    g = torch_generator(seed, _T_DEV_STEP, layer, device=device)
+    q = centers[rows] + float(w.noise) * torch.randn((steps, B, Hq, d), generator=g, device=device)
+    first = rows.view(steps, B, Hkv, G)[..., 0]
+    kn = (centers[first] + float(w.noise) * torch.randn((steps, B, Hkv, d), generator=g, device=device)) \
+        * float(w.key_scale)
+    vn = torch.randn((steps, B, Hkv, d), generator=g, device=device)
+    return q.to(w.torch_dtype), kn.to(w.torch_dtype), vn.to(w.torch_dtype)

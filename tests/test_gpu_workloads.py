@@ -31,3 +31,60 @@ def test_llama31_8b_128k_group_b8_sampled():
     PY.log(f"{w.name}: graphs {graphs}, 8 steps")
     st = PY.run_steps(w, 4, 8, graphs=graphs, check_state_every=4)
     PY.log(f"  graphs {st.graphs} near-ties sel {st.near_sel} edges {st.near_edges} max abs {st.max_abs:.2e}")
+
+
+def test_qwen3_8b_stream_36_layers_sampled():
+    """The 36-layer batch-8 stack at full size (about 155 GB of K/V resident),
+    stepped through all layers as the benchmark does; sampled (layer, graph)
+    pairs are checked against the oracle on slices regenerated from the same
+    device streams."""
+    import numpy as np
+    import torch
+
+    from community_kv_retrieval_amd import runner
+    from oracle import ckv_oracle as O
+
+    w = synth.preset("qwen3_8b_stream_36l")
+    steps = 3
+    PY.log(f"{w.name}: building {w.n_layers} layers")
+    stack = runner.load_stack(w, 1, steps)
+    samples = [(0, 0), (17, 37), (35, 63)]
+    orcs = {}
+    for layer, g in samples:
+        b, kh, _, _ = w.graph_coords(g)
+        part = stack[layer].parts[b][kh]
+        _, k, v = synth.gen_slice_device(w, 1, layer, b, kh, part)
+        kvh = {b: {kh: (k.float().cpu().numpy(), v.float().cpu().numpy())}}
+        del k, v
+        orcs[(layer, g)] = O.Oracle(w, kvh, {g: part.labels}, {g: part.n_comm}, graphs=[g], extra=steps + 1)
+    stats = PY.Stats()
+    for t in range(steps):
+        for L in stack:
+            L.dec.step(L.q[t], L.k_new[t], L.v_new[t])
+        torch.cuda.synchronize()
+        for (layer, g), orc in orcs.items():
+            L = stack[layer]
+            buf = L.dec.buf
+            where = f"{w.name} layer {layer} graph {g} step {t}"
+            qn = L.q[t].float().cpu().numpy()
+            st = orc.g[g]
+            r = orc.step_graph(g, qn)
+            gsel = buf.sel[g, :int(buf.sel_n[g])].cpu().numpy()
+            assert int(buf.top[g]) == r.top, where
+            if not PY._selection_ok(r, st.counts, gsel, w.budget, stats, where):
+                r = orc.step_graph(g, qn, force_sel=gsel)
+            tl = buf.tok_list[g, :int(buf.tok_n[g])].cpu().numpy()
+            np.testing.assert_array_equal(np.sort(tl), r.positions, err_msg=where)
+            gout = buf.out[st.b, st.qh0:st.qh0 + st.nh].cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(gout - r.out) <= PY.ATOL + PY.RTOL * np.abs(r.out)), where
+            ge = buf.edges[g].cpu().numpy()
+            ne = int((ge >= 0).sum())
+            if not PY._edges_ok(r, ge[:ne], stats, where):
+                r = orc.step_graph(g, qn, force_sel=gsel, force_edges=ge[:ne])
+            assert int(buf.assign[g]) == r.assign, where
+            orc.apply_update(g, int(buf.assign[g]), L.k_new[t].float().cpu().numpy()[st.b, st.kh])
+            orc.append(L.k_new[t].float().cpu().numpy(), L.v_new[t].float().cpu().numpy())
+            stats.graphs += 1
+    for L in stack:
+        assert int(L.idx.status.item()) == 0
+    PY.log(f"  checked {stats.graphs} graph-steps, near-ties sel {stats.near_sel} edges {stats.near_edges}")
