@@ -186,10 +186,10 @@ def main():
         ckv.ckv_select_communities(kv, idx, q, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
                                    b.tok_list, b.tok_n)
         ckv.ckv_time_next_launch(*ev[i][2])
-        ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, b.out, b.logits, b.ml, b.ws)
+        ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, None, b.logits, None, b.ws)
         ckv.ckv_time_next_launch(*ev[i][3])
         ckv.ckv_assign_update(kv, idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, dec.kappa, KN[t], VN[t],
-                              b.edges, b.assign, b.ws)
+                              b.edges, b.assign, b.ws, out=b.out)
     torch.cuda.synchronize()
     dt = np.array([[a.elapsed_time(c) for a, c in ev[i]] for i in range(K)]) * 1e3  # us
     names = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
@@ -241,6 +241,7 @@ def main():
     if args.recall_steps > 0:
         recall = {}
         budget0 = dec.budget
+        dec.defer = False  # recall reads the gather's ml before the update
         dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
         dout = torch.empty_like(buf.out)
         for B in [b for b in (128, 512, 1024, 2048, 4096) if b <= budget0]:
@@ -257,6 +258,7 @@ def main():
             recall[str(B)] = {"mean": round(float(v.mean()), 4), "p10": round(float(np.percentile(v, 10)), 4),
                               "min": round(float(v.min()), 4)}
         dec.budget = budget0
+        dec.defer = True
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -372,10 +374,10 @@ def bench_stack(args, w):
             ckv.ckv_select_communities(L.kv, L.idx, q, b.scores, L.dec.budget, L.dec.max_comm, b.sel, b.sel_n,
                                        b.top, b.tok_list, b.tok_n)
             ckv.ckv_time_next_launch(*ev[i][li][2])
-            ckv.ckv_gather_attend(L.kv, L.idx, q, b.tok_list, b.tok_n, L.dec.sm_scale, b.out, b.logits, b.ml, b.ws)
+            ckv.ckv_gather_attend(L.kv, L.idx, q, b.tok_list, b.tok_n, L.dec.sm_scale, None, b.logits, None, b.ws)
             ckv.ckv_time_next_launch(*ev[i][li][3])
             ckv.ckv_assign_update(L.kv, L.idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, L.dec.kappa,
-                                  L.k_new[t], L.v_new[t], b.edges, b.assign, b.ws)
+                                  L.k_new[t], L.v_new[t], b.edges, b.assign, b.ws, out=b.out)
             tok.append(b.tok_n.sum())
     torch.cuda.synchronize()
     dt = np.array([[[a.elapsed_time(c) for a, c in ev[i][li]] for li in range(len(stack))]

@@ -71,8 +71,8 @@ def _load():
         "ckv_gather_attend": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_assign_update": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
-                                        c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
-                                        c_void_p]),
+                                        c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_size_t, c_void_p]),
         "ckv_dense_attend": (c_int32, [KVP, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_time_next_launch": (c_int32, [c_void_p, c_void_p]),
         "ckv_status_str": (ctypes.c_char_p, [c_int32]),
@@ -243,15 +243,18 @@ def ckv_select_communities(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, sc
 
 
 def ckv_gather_attend(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, tok_list: torch.Tensor,
-                      tok_n: torch.Tensor, sm_scale: float, out: torch.Tensor, logits: torch.Tensor,
-                      ml: torch.Tensor, ws: torch.Tensor, stream=None):
+                      tok_n: torch.Tensor, sm_scale: float, out: Optional[torch.Tensor], logits: torch.Tensor,
+                      ml: Optional[torch.Tensor], ws: torch.Tensor, stream=None):
+    """out = ml = None defers the combine to the next ckv_assign_update(out=...)."""
     G, nh, t_cap = idx.n_graphs, idx.heads_per_graph(kv), tok_list.shape[1]
     _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
     _need(tok_list, "tok_list", torch.int32, (G, t_cap))
     _need(tok_n, "tok_n", torch.int32, (G,))
-    _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
+    if out is not None:
+        _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
     _need(logits, "logits", torch.float32, (G, nh, t_cap))
-    _need(ml, "ml", torch.float32, (G, nh, 2))
+    if ml is not None:
+        _need(ml, "ml", torch.float32, (G, nh, 2))
     _check("ckv_gather_attend", LIB.ckv_gather_attend(
         ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q), _ptr(tok_list), _ptr(tok_n), t_cap,
         float(sm_scale), _ptr(out), _ptr(logits), _ptr(ml), _ptr(ws), ws.numel() * ws.element_size(),
@@ -259,13 +262,17 @@ def ckv_gather_attend(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, tok_lis
 
 
 def ckv_assign_update(kv: KVStore, idx: CommunityIndex, tok_list: torch.Tensor, tok_n: torch.Tensor,
-                      logits: torch.Tensor, ml: torch.Tensor, top: torch.Tensor, kappa: int,
+                      logits: torch.Tensor, ml: Optional[torch.Tensor], top: torch.Tensor, kappa: int,
                       k_new: torch.Tensor, v_new: torch.Tensor, edges: torch.Tensor, assign: torch.Tensor,
-                      ws: torch.Tensor, stream=None):
+                      ws: torch.Tensor, stream=None, out: Optional[torch.Tensor] = None):
+    """out given: complete a deferred gather first (writes out and, if given, ml)."""
     G, nh, t_cap = idx.n_graphs, idx.heads_per_graph(kv), tok_list.shape[1]
     _need(tok_list, "tok_list", torch.int32, (G, t_cap))
     _need(logits, "logits", torch.float32, (G, nh, t_cap))
-    _need(ml, "ml", torch.float32, (G, nh, 2))
+    if ml is not None:
+        _need(ml, "ml", torch.float32, (G, nh, 2))
+    if out is not None:
+        _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
     for name, t in (("tok_n", tok_n), ("top", top), ("assign", assign)):
         _need(t, name, torch.int32, (G,))
     _need(k_new, "k_new", kv.dtype, (kv.batch, kv.n_kv_heads, kv.head_dim))
@@ -273,7 +280,7 @@ def ckv_assign_update(kv: KVStore, idx: CommunityIndex, tok_list: torch.Tensor, 
     _need(edges, "edges", torch.int32, (G, kappa))
     _check("ckv_assign_update", LIB.ckv_assign_update(
         ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(tok_list), _ptr(tok_n), _ptr(logits), _ptr(ml),
-        t_cap, _ptr(top), kappa, _ptr(k_new), _ptr(v_new), _ptr(edges), _ptr(assign), _ptr(ws),
+        t_cap, _ptr(top), kappa, _ptr(k_new), _ptr(v_new), _ptr(edges), _ptr(assign), _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -327,6 +334,11 @@ class DecodeBuffers:
 class Decoder:
     """Runs CommunityKV decode steps for one layer.
 
+    With defer set (the default) the gather leaves its per-span softmax states
+    in the workspace and the assign call combines them into out and ml, so the
+    combine overlaps the assignment instead of ending the gather; the results
+    are bit-identical to a complete gather's.
+
     With windows > 1 a step splits the graphs into that many windows, each run
     on a stream of its own, window w scoring after window w - 1 has scored: the
     later windows' bandwidth-bound scoring and gathering then overlap the
@@ -335,9 +347,10 @@ class Decoder:
     """
 
     def __init__(self, kv: KVStore, idx: CommunityIndex, budget: int, max_comm: int, kappa: int,
-                 sm_scale: float, device="cuda", windows: int = 1):
+                 sm_scale: float, device="cuda", windows: int = 1, defer: bool = True):
         self.kv, self.idx = kv, idx
         self.budget, self.max_comm, self.kappa, self.sm_scale = budget, max_comm, kappa, sm_scale
+        self.defer = defer
         self.buf = DecodeBuffers(kv, idx, budget, kappa, device)
         self.set_windows(windows)
 
@@ -361,14 +374,16 @@ class Decoder:
                                b.tok_list, b.tok_n, stream)
 
     def attend(self, q: torch.Tensor, stream=None):
+        """With defer set, out and ml are written by the following update()."""
         b = self.buf
-        ckv_gather_attend(self.kv, self.idx, q, b.tok_list, b.tok_n, self.sm_scale, b.out, b.logits, b.ml, b.ws,
+        out, ml = (None, None) if self.defer else (b.out, b.ml)
+        ckv_gather_attend(self.kv, self.idx, q, b.tok_list, b.tok_n, self.sm_scale, out, b.logits, ml, b.ws,
                           stream)
 
     def update(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
         b = self.buf
         ckv_assign_update(self.kv, self.idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, self.kappa, k_new, v_new,
-                          b.edges, b.assign, b.ws, stream)
+                          b.edges, b.assign, b.ws, stream, out=b.out if self.defer else None)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
         if self.windows == 1:
@@ -392,9 +407,10 @@ class Decoder:
             prev.record(s)
             ckv_select_communities(kv, view, q, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
                                    b.tok_list, b.tok_n, s)
-            ckv_gather_attend(kv, view, q, b.tok_list, b.tok_n, self.sm_scale, b.out, b.logits, b.ml, b.ws, s)
+            out, ml = (None, None) if self.defer else (b.out, b.ml)
+            ckv_gather_attend(kv, view, q, b.tok_list, b.tok_n, self.sm_scale, out, b.logits, ml, b.ws, s)
             ckv_assign_update(kv, view, b.tok_list, b.tok_n, b.logits, b.ml, b.top, self.kappa, k_new, v_new,
-                              b.edges, b.assign, b.ws, s)
+                              b.edges, b.assign, b.ws, s, out=b.out if self.defer else None)
             done = torch.cuda.Event()
             done.record(s)
             cur.wait_event(done)
@@ -408,7 +424,8 @@ class Decoder:
         """Attention-mass recall of the last gather, per graph and head: the
         share of the dense softmax mass (dense_ml from dense(..., ml=)) that the
         attended tokens carry, exp(lse_attended - lse_all) (page Figure 3).
-        Host-side arithmetic on kernel outputs (a diagnostic, not a step)."""
+        Host-side arithmetic on kernel outputs (a diagnostic, not a step).
+        Needs a complete gather's ml: with defer set, call it after update()."""
         kv, idx, b = self.kv, self.idx, self.buf
         G, nh = idx.n_graphs, idx.heads_per_graph(kv)
         g = torch.arange(G, device=dense_ml.device)

@@ -64,7 +64,7 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 3; }
+int32_t ckv_abi_version(void) { return 4; }
 
 ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;
@@ -163,7 +163,8 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
     ckv_status st = check_kv(kv);
     if (st != CKV_OK) return st;
     if ((st = check_index(kv, idx)) != CKV_OK) return st;
-    if (!q || !tok_list || !tok_n || !out || !logits || !ml) return CKV_E_INVALID;
+    if (!q || !tok_list || !tok_n || !logits) return CKV_E_INVALID;
+    if ((out == nullptr) != (ml == nullptr)) return CKV_E_INVALID;  // both (complete) or neither (deferred)
     if (t_cap < 1) return CKV_E_INVALID;
     if ((st = check_ws(kv, idx, t_cap, ws, ws_bytes)) != CKV_OK) return st;
     const WsLayout L = ws_layout(kv, idx, t_cap);
@@ -173,20 +174,22 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
 }
 
 ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
-                             const int32_t *tok_n, const float *logits, const float *ml, int32_t t_cap,
+                             const int32_t *tok_n, const float *logits, float *ml, int32_t t_cap,
                              const int32_t *top, int32_t kappa, const void *k_new, const void *v_new,
-                             int32_t *edges, int32_t *assign, void *ws, size_t ws_bytes,
+                             int32_t *edges, int32_t *assign, float *out, void *ws, size_t ws_bytes,
                              ckv_stream_t stream) {
     ckv_status st = check_kv(kv);
     if (st != CKV_OK) return st;
     if ((st = check_index(kv, idx)) != CKV_OK) return st;
-    if (!tok_list || !tok_n || !logits || !ml || !top || !k_new || !v_new || !edges || !assign)
+    if (!tok_list || !tok_n || !logits || !top || !k_new || !v_new || !edges || !assign)
         return CKV_E_INVALID;
+    if (!out && !ml) return CKV_E_INVALID;  // a complete gather's softmax state is read
     if (kappa < 1 || kappa > CKV_MAX_KAPPA || t_cap < 1) return CKV_E_INVALID;
     if ((st = check_ws(kv, idx, t_cap, ws, ws_bytes)) != CKV_OK) return st;
     const WsLayout L = ws_layout(kv, idx, t_cap);
     return hip_status(launch_assign(kv, idx, tok_list, tok_n, logits, ml, t_cap, top, kappa, k_new, v_new,
-                                    edges, assign, (int32_t *)at(ws, L.ctr_assign), (hipStream_t)stream));
+                                    edges, assign, out, (const float *)at(ws, L.part_gather),
+                                    (int32_t *)at(ws, L.ctr_assign), (hipStream_t)stream));
 }
 
 ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,

@@ -18,6 +18,7 @@
 // sequence length.
 #include "ckv_device.h"
 #include "ckv_internal.h"
+#include "combine.h"
 
 namespace ckv {
 
@@ -40,7 +41,10 @@ struct AssignParams {
     const int32_t *tok_list;
     const int32_t *tok_n;
     const float *logits;
-    const float *ml;
+    float *ml;           // read (gather complete) or written (deferred combine)
+    float *out;          // not null: combine the deferred gather's records into out
+    const float *part;   // the gather's partial records
+    int nchunk;          // gather spans per graph (records per head)
     const int32_t *top;
     const void *k_new;
     const void *v_new;
@@ -59,7 +63,15 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     return wave_reduce_u32(x, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
-template <typename T, int D, int NH>
+// How the kernel gets the attention's softmax state.  Complete: the gather
+// wrote ml.  Deferred: the gather left per-span records that this kernel
+// combines (into out and ml); with at most kPreChunks spans and four heads the
+// accumulators are loaded with the first round trip (DeferRegs), otherwise
+// when they are combined (Defer).
+enum AssignMode { kAssignComplete = 0, kAssignDeferRegs = 1, kAssignDefer = 2 };
+constexpr int kPreChunks = 20;
+
+template <typename T, int D, int NH, int MODE>
 __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     constexpr int kIpt = 24;  // candidates per thread held in registers
     __shared__ unsigned long long s_cand[64];
@@ -68,8 +80,13 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     __shared__ int s_edges[CKV_MAX_KAPPA];
     __shared__ int s_elab[CKV_MAX_KAPPA];
     __shared__ float s_max[4];
+    __shared__ CombineLds<NH> s_comb;
+    constexpr int PS = part_stride(D);
 
     const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr bool defer = MODE != kAssignComplete;
+    constexpr bool regs = MODE == kAssignDeferRegs;
+    static_assert(!regs || NH <= 4, "preloaded combine: at most four heads");
     CKV_TMARK(30);
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
     const int32_t *tl = p.tok_list + (size_t)g * p.t_cap;
@@ -81,11 +98,16 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     const int tn = p.tail_len[g];
     const int topc = p.top[g];
     float M[NH], Linv[NH];
+    if constexpr (!defer) {
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        M[h] = NH > 1 ? p.ml[((size_t)g * NH + h) * 2] : 0.f;
-        Linv[h] = NH > 1 ? 1.f / p.ml[((size_t)g * NH + h) * 2 + 1] : 0.f;
+        for (int h = 0; h < NH; ++h) {
+            M[h] = NH > 1 ? p.ml[((size_t)g * NH + h) * 2] : 0.f;
+            Linv[h] = NH > 1 ? 1.f / p.ml[((size_t)g * NH + h) * 2 + 1] : 0.f;
+        }
     }
+    // Deferred gather: nact records per head hold this graph's spans.
+    const float *PR = p.part + (size_t)g * NH * p.nchunk * PS;
+    const int nact = n > 0 ? (n + kGatherTokens - 1) / kGatherTokens : 0;
     const int jmax = min(p.t_cap, kIpt * 256);
     int cp[kIpt];
     float z[kIpt][NH];
@@ -97,20 +119,58 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) z[i][h] = ok ? p.logits[((size_t)g * NH + h) * p.t_cap + j] : 0.f;
     }
+    // DeferRegs: then the records of every span the list can have, with no
+    // condition on any load (clamped addresses), so that the LDS write of the
+    // (max, sum) pairs waits for them and nothing after them: the
+    // accumulators stay in flight until waves 1-3 combine them while wave 0
+    // ranks the edges.
+    float st_m = 0.f, st_l = 0.f;
+    float ov[combine_pairs<D, NH, 192>()][regs ? kPreChunks : 1];
+    if constexpr (regs) {
+        const float *r = PR + (size_t)min(tid, NH * p.nchunk - 1) * PS;  // head / chunk = tid div / mod nchunk
+        st_m = r[D];
+        st_l = r[D + 1];
+        combine_preload_all<D, NH, PS, 192, kPreChunks>(PR, p.nchunk, tid - 64, ov);
+    }
     if (tid == 0) s_ncand = 0;
+    if constexpr (regs) {
+        if (tid < NH * p.nchunk) {
+            const int h = tid / p.nchunk;
+            s_comb.m[h][tid - h * p.nchunk] = st_m;
+            s_comb.l[h][tid - h * p.nchunk] = st_l;
+        }
+    } else if constexpr (defer) {
+        combine_stage<NH, D, PS, false>(PR, p.nchunk, nact, s_comb);
+    }
 
-    // The graph of the group's first query head appends the new key and value
-    // at position P; one wave does it while the others rank the edges.
     const int cap = min(p.l_cap, p.max_pages << p.ps_log2);
     const bool room = P < cap;
     const bool owner = p.mode == CKV_MODE_QUERY_GROUP || (gc.qh0 % (p.Hq / p.Hkv)) == 0;
     const T *kn = reinterpret_cast<const T *>(p.k_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
     const T *vn = reinterpret_cast<const T *>(p.v_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
-    if (owner && room && wave == 3) {
-        const int page = p.page_table[(size_t)gc.b * p.max_pages + (P >> p.ps_log2)];
-        T *row = reinterpret_cast<T *>(p.kv) +
-                 ((((size_t)page * p.Hkv + gc.kh) << p.ps_log2) | (size_t)(P & ((1 << p.ps_log2) - 1))) * (2 * D);
-        for (int i = lane; i < 2 * D; i += 64) row[i] = i < D ? kn[i] : vn[i - D];
+
+    // Deferred gather: every head's softmax state (M, L) from the records, by
+    // the combine's own steps, so the weights below equal those computed from
+    // a complete gather's ml.  The barriers up to the ranking order LDS
+    // traffic only: the accumulator loads above stay in flight.
+    if constexpr (defer) {
+        lds_barrier();
+        if (nact >= 1 && nact <= kCombineLds) combine_heads<NH>(nact, s_comb);
+        lds_barrier();
+        if constexpr (NH > 1) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                float L = 1.f;
+                M[h] = kNegInf;
+                if (nact >= 1 && nact <= kCombineLds) {
+                    M[h] = s_comb.M[h];
+                    L = s_comb.L[h];
+                } else if (nact > kCombineLds) {
+                    head_state_long<D, PS, false>(PR, p.nchunk, nact, h, M[h], L);
+                }
+                Linv[h] = 1.f / L;
+            }
+        }
     }
 
     // Candidates as 64-bit keys, (order-preserving bits of the weight) << 32 |
@@ -154,7 +214,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
             ++got;
         }
         if (lane == 0) s_tau[wave] = got == kappa ? tw : 0u;
-        __syncthreads();
+        lds_barrier();
         uint32_t tau = max(max(s_tau[0], s_tau[1]), max(s_tau[2], s_tau[3]));
         if (tau == 0u) tau = 1u;
 #pragma unroll
@@ -164,7 +224,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
                 if (k < 64) s_cand[k] = ck[i];
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
     CKV_TMARK(32);
     const int ncand = inreg ? s_ncand : 65;
@@ -223,7 +283,25 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         }
         if (lane == 0) s_ne = ne;
     }
-    __syncthreads();
+    // Meanwhile the other three waves combine the deferred gather's records
+    // into the attention output.
+    if constexpr (defer) {
+        if (wave > 0) {
+            float *o = p.out + ((size_t)gc.b * p.Hq + gc.qh0) * D;
+            float *mlg = p.ml ? p.ml + (size_t)g * NH * 2 : nullptr;
+            if (nact == 0) {
+                combine_empty<D, NH, 192>(tid - 64, o, mlg);
+            } else if constexpr (regs) {
+                combine_out_regs<D, NH, 192, kPreChunks>(nact, s_comb, tid - 64, ov, o, mlg);
+            } else {
+                if (nact <= kCombineLds)
+                    combine_out<D, NH, PS, false, 192>(PR, p.nchunk, nact, s_comb, tid - 64, o, mlg);
+                else
+                    combine_out_long<D, NH, PS, false, 192>(PR, p.nchunk, nact, tid - 64, o, mlg);
+            }
+        }
+    }
+    lds_barrier();
     const int ne = s_ne;
     CKV_TMARK(33);
 
@@ -252,8 +330,18 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
             s_a = a;
         }
     }
-    __syncthreads();
+    lds_barrier();
     CKV_TMARK(34);
+
+    // The graph of the group's first query head appends the new key and value
+    // at position P (wave 3, idle in the update below; nothing in this kernel
+    // reads the row).
+    if (owner && room && wave == 3) {
+        const int page = p.page_table[(size_t)gc.b * p.max_pages + (P >> p.ps_log2)];
+        T *row = reinterpret_cast<T *>(p.kv) +
+                 ((((size_t)page * p.Hkv + gc.kh) << p.ps_log2) | (size_t)(P & ((1 << p.ps_log2) - 1))) * (2 * D);
+        for (int i = lane; i < 2 * D; i += 64) row[i] = i < D ? kn[i] : vn[i - D];
+    }
 
     // Append to the winning community: label, tail entry, member count, the
     // float64 key sum and the float32 centroid column.
@@ -310,9 +398,10 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
 }
 
 hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
-                         const int32_t *tok_n, const float *logits, const float *ml, int t_cap,
+                         const int32_t *tok_n, const float *logits, float *ml, int t_cap,
                          const int32_t *top, int kappa, const void *k_new, const void *v_new,
-                         int32_t *edges, int32_t *assign, int32_t *ctr, hipStream_t s) {
+                         int32_t *edges, int32_t *assign, float *out, const float *part, int32_t *ctr,
+                         hipStream_t s) {
     AssignParams p{};
     p.kv = kv->kv;
     p.page_table = kv->page_table;
@@ -346,6 +435,9 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     p.tok_n = tok_n;
     p.logits = logits;
     p.ml = ml;
+    p.out = out;
+    p.part = part;
+    p.nchunk = ceil_div(t_cap, kGatherTokens);
     p.top = top;
     p.k_new = k_new;
     p.v_new = v_new;
@@ -355,8 +447,16 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     const int nh = heads_per_graph(kv, idx);
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
     const dim3 grid(w.count), block(256);
-#define CKV_AS(TT, DD, NN) \
-    if (kv->head_dim == DD && nh == NN) { CKV_LAUNCH((assign_kernel<TT, DD, NN>), grid, block, s, p); return hipGetLastError(); }
+    const int mode = !out ? kAssignComplete : (nh <= 4 && p.nchunk <= kPreChunks) ? kAssignDeferRegs : kAssignDefer;
+#define CKV_AS_M(TT, DD, NN, MM)                                                  \
+    if (kv->head_dim == DD && nh == NN && mode == MM) {                          \
+        CKV_LAUNCH((assign_kernel<TT, DD, NN, MM>), grid, block, s, p);          \
+        return hipGetLastError();                                                \
+    }
+#define CKV_AS(TT, DD, NN)                        \
+    CKV_AS_M(TT, DD, NN, kAssignComplete)         \
+    CKV_AS_M(TT, DD, NN, kAssignDefer)            \
+    CKV_AS_M(TT, DD, NN, (NN <= 4 ? kAssignDeferRegs : kAssignDefer))
 #define CKV_AS_T(TT) \
     CKV_AS(TT, 64, 1) CKV_AS(TT, 64, 2) CKV_AS(TT, 64, 4) CKV_AS(TT, 64, 8) \
     CKV_AS(TT, 128, 1) CKV_AS(TT, 128, 2) CKV_AS(TT, 128, 4) CKV_AS(TT, 128, 8)
@@ -367,6 +467,7 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     }
 #undef CKV_AS_T
 #undef CKV_AS
+#undef CKV_AS_M
     return hipErrorInvalidValue;
 }
 

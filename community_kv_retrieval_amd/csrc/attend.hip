@@ -17,10 +17,9 @@
 // partial records are padded to whole cache lines and written and read with
 // device-scope accesses, and each block waits for its stores before it counts
 // itself in.
-#include <cstdlib>
-
 #include "ckv_device.h"
 #include "ckv_internal.h"
+#include "combine.h"
 
 namespace ckv {
 
@@ -41,8 +40,8 @@ struct AttendParams {
     float *part;
     int32_t *ctr;
     int nchunk;     // blocks per unit
-    int per_block;  // tokens per block (gather)
     int g0;         // first unit of the launch window
+    int units;      // units in the launch
 };
 
 template <typename T, int D, int NH>
@@ -50,205 +49,46 @@ constexpr int pick_u() {
     return (NH >= 8 || RowSlice<T, D>::BYTES == 32) ? 4 : 8;
 }
 
-// Block-wide reduction of NH values per thread (max or sum) over 256 threads;
-// every thread gets the results.  red: [4][NH] shared floats.
-template <int NH, bool MAX>
-__device__ __forceinline__ void block_reduce_nh(float (&v)[NH], float (*red)[NH]) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float y = __shfl_xor(v[h], o, 64);
-            v[h] = MAX ? fmaxf(v[h], y) : v[h] + y;
-        }
-        if (lane == 0) red[wave][h] = v[h];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        float r = red[0][h];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) r = MAX ? fmaxf(r, red[w][h]) : r + red[w][h];
-        v[h] = r;
-    }
-    __syncthreads();
-}
-
-// Merge the nact partial records (accumulator[D], max, sum) of every head into
-// the final output.  Loads are batched so that many are in flight at once.
-// Up to kFastMerge partials: the max and sum of every partial go to LDS while
-// each thread's accumulator entries are loaded in passes of kMergePass, all in
-// the same round trip for the first pass.
-constexpr int kFastMerge = 64;
-constexpr int kMergePass = 32;
-
-template <int D, int NH, int PS>
-__device__ __forceinline__ void merge_partials(const float *P, int nchunk, int nact, float (*s_scale)[256],
-                                               float (*s_red)[NH], float *out, float *ml) {
-    const int tid = threadIdx.x;
-    constexpr int NP = (NH * D + 255) / 256;  // (head, dim) pairs per thread
-    if (nact <= kFastMerge) {
-        float(*s_m)[kFastMerge] = reinterpret_cast<float(*)[kFastMerge]>(&s_scale[0][0]);
-        float(*s_l)[kFastMerge] = reinterpret_cast<float(*)[kFastMerge]>(&s_scale[0][0] + NH * kFastMerge);
-        for (int i = tid; i < NH * nact; i += 256) {
-            const int h = i / nact, c = i - (i / nact) * nact;
-            s_m[h][c] = ld_dev(P + ((size_t)h * nchunk + c) * PS + D);
-            s_l[h][c] = ld_dev(P + ((size_t)h * nchunk + c) * PS + D + 1);
-        }
-        float o[NP][kMergePass];
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int pi = tid + i * 256;
-            const int h = pi / D, d = pi - (pi / D) * D;
-#pragma unroll
-            for (int c = 0; c < kMergePass; ++c)
-                o[i][c] = (pi < NH * D && c < nact) ? ld_dev(P + ((size_t)h * nchunk + c) * PS + d) : 0.f;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int pi = tid + i * 256;
-            if (pi >= NH * D) break;
-            const int h = pi / D, d = pi - (pi / D) * D;
-            float M = kNegInf;
-            for (int c = 0; c < nact; ++c) M = fmaxf(M, s_m[h][c]);
-            float L = 0.f, O = 0.f;
-#pragma unroll
-            for (int c = 0; c < kMergePass; ++c) {
-                if (c < nact) {
-                    const float mc = s_m[h][c];
-                    const float sc = (mc == kNegInf) ? 0.f : exp2f((mc - M) * kLog2e);
-                    L = fmaf(s_l[h][c], sc, L);
-                    O = fmaf(o[i][c], sc, O);
-                }
-            }
-            for (int c0 = kMergePass; c0 < nact; c0 += kMergePass) {
-                float v[kMergePass];
-#pragma unroll
-                for (int c = 0; c < kMergePass; ++c)
-                    v[c] = (c0 + c < nact) ? ld_dev(P + ((size_t)h * nchunk + c0 + c) * PS + d) : 0.f;
-#pragma unroll
-                for (int c = 0; c < kMergePass; ++c) {
-                    if (c0 + c < nact) {
-                        const float mc = s_m[h][c0 + c];
-                        const float sc = (mc == kNegInf) ? 0.f : exp2f((mc - M) * kLog2e);
-                        L = fmaf(s_l[h][c0 + c], sc, L);
-                        O = fmaf(v[c], sc, O);
-                    }
-                }
-            }
-            out[pi] = O / L;
-            if (ml && d == 0) {
-                ml[h * 2] = M;
-                ml[h * 2 + 1] = L;
-            }
-        }
-        return;
-    }
-    float M[NH], L[NH];
-#pragma unroll
-    for (int h = 0; h < NH; ++h) M[h] = kNegInf;
-    for (int c = tid; c < nact; c += 256) {
-        float m[NH];
-#pragma unroll
-        for (int h = 0; h < NH; ++h) m[h] = ld_dev(P + ((size_t)h * nchunk + c) * PS + D);
-#pragma unroll
-        for (int h = 0; h < NH; ++h) M[h] = fmaxf(M[h], m[h]);
-    }
-    block_reduce_nh<NH, true>(M, s_red);
-
-    float o[NP];
-#pragma unroll
-    for (int i = 0; i < NP; ++i) o[i] = 0.f;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) L[h] = 0.f;
-    constexpr int B = 16;
-    for (int c0 = 0; c0 < nact; c0 += 256) {
-        const int tn = min(256, nact - c0);
-        if (tid < tn) {
-            float m[NH], l[NH];
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                m[h] = ld_dev(P + ((size_t)h * nchunk + c0 + tid) * PS + D);
-                l[h] = ld_dev(P + ((size_t)h * nchunk + c0 + tid) * PS + D + 1);
-            }
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                const float sc = (m[h] == kNegInf) ? 0.f : exp2f((m[h] - M[h]) * kLog2e);
-                s_scale[h][tid] = sc;
-                L[h] += l[h] * sc;
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int pi = tid + i * 256;
-            if (pi < NH * D) {
-                const int h = pi / D, d = pi - (pi / D) * D;
-                const float *src = P + ((size_t)h * nchunk + c0) * PS + d;
-                for (int j0 = 0; j0 < tn; j0 += B) {
-                    float v[B];
-#pragma unroll
-                    for (int j = 0; j < B; ++j) v[j] = (j0 + j < tn) ? ld_dev(src + (size_t)(j0 + j) * PS) : 0.f;
-#pragma unroll
-                    for (int j = 0; j < B; ++j)
-                        if (j0 + j < tn) o[i] = fmaf(v[j], s_scale[h][j0 + j], o[i]);
-                }
-            }
-        }
-        __syncthreads();
-    }
-    block_reduce_nh<NH, false>(L, s_red);
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-        const int pi = tid + i * 256;
-        if (pi < NH * D) {
-            const int h = pi / D;
-            float Lh = L[0];
-#pragma unroll
-            for (int hh = 1; hh < NH; ++hh)
-                if (h == hh) Lh = L[hh];
-            out[pi] = o[i] / Lh;
-        }
-    }
-    if (ml) {
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-            if (tid == h) {
-                ml[h * 2] = M[h];
-                ml[h * 2 + 1] = L[h];
-            }
-    }
-}
-
 template <typename T, int D, int NH, int U, bool DENSE>
 __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     using RS = RowSlice<T, D>;
     constexpr int E = RS::E;
     constexpr int SPAN = 16 * U;
-    constexpr int MAX_BLOCK = DENSE ? kDenseTokens : kGatherMaxTokens;
-    const int PER_BLOCK = DENSE ? kDenseTokens : a.per_block;  // a multiple of SPAN, <= MAX_BLOCK
-    const int ITERS = PER_BLOCK / SPAN;
+    constexpr int PER_BLOCK = DENSE ? kDenseTokens : kGatherTokens;
+    constexpr int MAX_BLOCK = PER_BLOCK;
+    constexpr int ITERS = PER_BLOCK / SPAN;
+    static_assert(PER_BLOCK % SPAN == 0, "a block's span is whole passes");
     constexpr int PS = part_stride(D);
+    // Gather with out == nullptr: the combine is deferred to the assign kernel,
+    // every block leaves its partial record and the launch ends there.
+    const bool defer = !DENSE && a.out == nullptr;
 
     __shared__ uint32_t s_row[MAX_BLOCK];
     __shared__ float s_q[NH][D];
     __shared__ float s_wm[4][NH], s_wl[4][NH];
     __shared__ float s_wacc[4][NH][D];
-    __shared__ float s_scale[NH][256];
-    __shared__ float s_red[4][NH];
+    __shared__ CombineLds<NH> s_comb;
     __shared__ int s_last;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, ts = lane >> 4;
-    const int lunit = blockIdx.x / a.nchunk;
-    const int chunk = blockIdx.x - lunit * a.nchunk;
+    // Chunk-major order: chunk c of every unit is dispatched before chunk c+1
+    // of any, so the short last chunks come last and land where a compute unit
+    // already holds two full ones; with a unit count divisible by 8 the blocks
+    // of one unit also share an XCD (workgroups go round-robin over the XCDs).
+    const int chunk = blockIdx.x / a.units;
+    const int lunit = blockIdx.x - chunk * a.units;
     const int unit = a.g0 + lunit;
     if constexpr (!DENSE) CKV_TMARK(20);
     if constexpr (!DENSE) CKV_BMARK(0);
 
     int b, kh, qh0, n;
+    const int start = chunk * PER_BLOCK;
+    // Gather: the span's token positions are loaded together with the list
+    // length (start < t_cap always holds, so the loads stay inside the row;
+    // entries past the length are ignored), one round trip instead of two.
+    constexpr int SLOTS = MAX_BLOCK / 256;
+    int pos_l[SLOTS];
     if constexpr (DENSE) {
         b = unit / a.Hkv;
         kh = unit - b * a.Hkv;
@@ -259,10 +99,16 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         b = gc.b;
         kh = gc.kh;
         qh0 = gc.qh0;
+        const int32_t *tl = a.tok_list + (size_t)unit * a.t_cap + start;
+        const int lim = min(PER_BLOCK, a.t_cap - start);
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int t = tid + i * 256;
+            pos_l[i] = t < lim ? tl[t] : 0;
+        }
         n = a.tok_n[unit];
     }
-    const int start = chunk * PER_BLOCK;
-    if (n <= 0 && chunk == 0) {  // nothing to attend: zero output, empty softmax state
+    if (n <= 0 && chunk == 0 && !defer) {  // nothing to attend: zero output, empty softmax state
         for (int i = tid; i < NH * D; i += 256) a.out[((size_t)b * a.Hq + qh0) * D + i] = 0.f;
         if (a.ml && tid < NH) {
             a.ml[((size_t)unit * NH + tid) * 2] = kNegInf;
@@ -274,15 +120,17 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     const int nact = (n + PER_BLOCK - 1) / PER_BLOCK;
     const int cnt = min(PER_BLOCK, n - start);
 
-    // Stage the row index of every token of the span (rows past the end
-    // repeat the span's first token and are masked below).
+    // Stage the row index of every token of the span (rows past the end read
+    // position 0 of the sequence, which exists whenever the span is not empty,
+    // and are masked below).
     {
         const int32_t *ptab = a.page_table + (size_t)b * a.max_pages;
-        const int32_t *tl = DENSE ? nullptr : a.tok_list + (size_t)unit * a.t_cap + start;
         const uint32_t smask = (1u << a.ps_log2) - 1u;
-        for (int t = tid; t < PER_BLOCK; t += 256) {
-            const int tt = t < cnt ? t : 0;
-            const int pos = DENSE ? start + tt : tl[tt];
+#pragma unroll
+        for (int i = 0; i < SLOTS; ++i) {
+            const int t = tid + i * 256;
+            if (t >= PER_BLOCK) break;
+            const int pos = t < cnt ? (DENSE ? start + t : pos_l[i]) : (DENSE ? start : 0);
             const int page = ptab[pos >> a.ps_log2];
             s_row[t] = ((uint32_t)(page * a.Hkv + kh) << a.ps_log2) | ((uint32_t)pos & smask);
         }
@@ -414,14 +262,20 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
             o += s_wacc[w][h][d] * s;
             L += s_wl[w][h] * s;
         }
-        if (nact == 1) {
+        float *dst = P + ((size_t)h * a.nchunk + chunk) * PS;
+        if (defer) {  // read by a later kernel: plain stores
+            dst[d] = o;
+            if (d == 0) {
+                dst[D] = M;
+                dst[D + 1] = L;
+            }
+        } else if (nact == 1) {
             a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = o / L;
             if (a.ml && d == 0) {
                 a.ml[((size_t)unit * NH + h) * 2] = M;
                 a.ml[((size_t)unit * NH + h) * 2 + 1] = L;
             }
         } else {
-            float *dst = P + ((size_t)h * a.nchunk + chunk) * PS;
             st_dev(dst + d, o);
             if (d == 0) {
                 st_dev(dst + D, M);
@@ -431,18 +285,37 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     }
     if constexpr (!DENSE) CKV_TMARK(23);
     if constexpr (!DENSE) CKV_BMARK(3);
-    if (nact == 1) return;
+    if (nact == 1 || defer) return;
 
-    // The last block of the unit merges every block's partial.
+    // The last block of the unit combines every block's partial.
     stores_done();
     __syncthreads();
     if (tid == 0) s_last = arrive_last(&a.ctr[unit], nact);
     __syncthreads();
     if constexpr (!DENSE) CKV_BMARK(4);
     if (!s_last) return;
-    merge_partials<D, NH, PS>(P, a.nchunk, nact, s_scale, s_red,
-                              a.out + ((size_t)b * a.Hq + qh0) * D,
-                              a.ml ? a.ml + (size_t)unit * NH * 2 : nullptr);
+    {
+        float *o = a.out + ((size_t)b * a.Hq + qh0) * D;
+        float *mlu = a.ml ? a.ml + (size_t)unit * NH * 2 : nullptr;
+        constexpr int NB = kCombineBatch;
+        if (nact <= NB) {  // accumulators and (m, l) in one round trip
+            float v[combine_pairs<D, NH, 256>()][NB];
+            combine_preload<D, NH, PS, true, 256, NB>(P, a.nchunk, nact, tid, v);
+            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
+            __syncthreads();
+            combine_heads<NH>(nact, s_comb);
+            __syncthreads();
+            combine_out_regs<D, NH, 256, NB>(nact, s_comb, tid, v, o, mlu);
+        } else if (nact <= kCombineLds) {
+            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
+            __syncthreads();
+            combine_heads<NH>(nact, s_comb);
+            __syncthreads();
+            combine_out<D, NH, PS, true, 256>(P, a.nchunk, nact, s_comb, tid, o, mlu);
+        } else {
+            combine_out_long<D, NH, PS, true, 256>(P, a.nchunk, nact, tid, o, mlu);
+        }
+    }
     if (tid == 0) reset_counter(&a.ctr[unit]);
     if constexpr (!DENSE) CKV_TMARK(24);
     if constexpr (!DENSE) CKV_BMARK(5);
@@ -451,7 +324,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
 template <typename T, int D, int NH, bool DENSE>
 static hipError_t launch_t(const AttendParams &p, int units, hipStream_t s) {
     constexpr int U = pick_u<T, D, NH>();
-    CKV_LAUNCH((attend_kernel<T, D, NH, U, DENSE>), dim3(units * p.nchunk), dim3(256), s, p);
+    AttendParams pu = p;
+    pu.units = units;
+    CKV_LAUNCH((attend_kernel<T, D, NH, U, DENSE>), dim3(units * p.nchunk), dim3(256), s, pu);
     return hipGetLastError();
 }
 
@@ -472,18 +347,6 @@ static hipError_t dispatch(const ckv_kv *kv, int nh, const AttendParams &p, int 
 #undef CKV_ATT_T
 #undef CKV_ATT
     return hipErrorInvalidValue;
-}
-
-// Tokens per gather block.  256 (two passes of 128) measured best for every
-// workload here: longer spans (512, 1024) pay less per-block staging and
-// split-K but lose more to blocks that share a compute unit.
-// CKV_GATHER_TOKENS = 512 or 1024 overrides it (tuning).
-static int gather_span() {
-    if (const char *e = getenv("CKV_GATHER_TOKENS")) {
-        const int v = atoi(e);
-        if (v == 2 * kGatherTokens || v == kGatherMaxTokens) return v;
-    }
-    return kGatherTokens;
 }
 
 hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
@@ -509,8 +372,7 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
     p.ml = ml;
     p.part = part;
     p.ctr = ctr;
-    p.per_block = gather_span();
-    p.nchunk = ceil_div(t_cap, p.per_block);
+    p.nchunk = ceil_div(t_cap, kGatherTokens);
     const Window w = window_of(idx);
     p.g0 = w.first;
     return dispatch<false>(kv, heads_per_graph(kv, idx), p, w.count, s);

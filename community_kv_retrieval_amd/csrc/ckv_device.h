@@ -272,6 +272,15 @@ __device__ __forceinline__ void stores_done() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): every prior load and store acknowledged
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
+// Block barrier for LDS traffic only: waits for this wave's LDS accesses, not
+// for its global loads still in flight (their registers are waited for where
+// they are used), so loads issued early keep flowing across it.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 // Bump a device-scope counter; true for the block that completes `total`.
 __device__ __forceinline__ bool arrive_last(int32_t *ctr, int total) {
     return __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total - 1;

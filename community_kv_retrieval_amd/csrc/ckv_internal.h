@@ -12,12 +12,11 @@
 namespace ckv {
 
 // Tokens one gather block attends: 16 tokens per pass of its 256 threads
-// (4 waves x 4 rows of 16 lanes), kGatherU passes per iteration.  The smallest
-// block span is kGatherTokens (the workspace holds a partial per such span);
-// larger problems use 2x or 4x longer spans (at most kGatherMaxTokens).
+// (4 waves x 4 rows of 16 lanes), kGatherU passes per iteration, two
+// iterations.  The workspace holds one partial record per head and span, and
+// the assign kernel finds a deferred gather's records by the same span.
 constexpr int kGatherU = 8;
 constexpr int kGatherTokens = 16 * kGatherU * 2;
-constexpr int kGatherMaxTokens = 4 * kGatherTokens;
 // The dense baseline walks kDenseIters such spans per block.
 constexpr int kDenseU = 8;
 constexpr int kDenseIters = 8;
@@ -124,9 +123,12 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
                          hipStream_t s);
 hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
                         float *part, int32_t *ctr, hipStream_t s);
+// out != nullptr: the preceding gather was deferred; the assign kernel
+// combines its partial records (part) into out and, if not null, ml.
 hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
-                         const int32_t *tok_n, const float *logits, const float *ml, int t_cap,
+                         const int32_t *tok_n, const float *logits, float *ml, int t_cap,
                          const int32_t *top, int kappa, const void *k_new, const void *v_new,
-                         int32_t *edges, int32_t *assign, int32_t *ctr, hipStream_t s);
+                         int32_t *edges, int32_t *assign, float *out, const float *part, int32_t *ctr,
+                         hipStream_t s);
 
 }  // namespace ckv

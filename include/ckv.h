@@ -197,7 +197,15 @@ ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const 
  * covers the sink tokens).  z_j = sm_scale * q . k_j in float32 from the stored K; outputs:
  * out[batch][n_q_heads][head_dim] float32 (every query head is written),
  * logits[G][hpg][t_cap] the z_j of each slot < tok_n[g] (hpg = heads per graph),
- * ml[G][hpg][2] = (max z, sum exp(z - max)). */
+ * ml[G][hpg][2] = (max z, sum exp(z - max)).  The list is split into spans of
+ * 256 tokens attended in parallel; their softmax states are combined in span
+ * order (log-sum-exp).
+ * Deferred combine: with out == NULL and ml == NULL the call writes the logits
+ * and leaves the per-span states in ws; the next ckv_assign_update on the same
+ * ws, tok_list, tok_n and t_cap with a non-NULL out then writes out and ml,
+ * bit for bit as this call would have (the combine then overlaps the assign's
+ * own work instead of ending the gather).  Exactly one of out, ml NULL:
+ * CKV_E_INVALID. */
 ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void *q,
                              const int32_t *tok_list, const int32_t *tok_n, int32_t t_cap,
                              float sm_scale, float *out, float *logits, float *ml,
@@ -213,12 +221,18 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
  * edge): assign[G].  Then, at P = seq_len[b]: label[P] = a, P joins a's tail,
  * size[a] += 1, csum[a] += k_new, cent[a] = float32(csum[a] / size[a]); k_new,
  * v_new ([batch][n_kv_heads][head_dim] of kv->dtype) are stored at P, and
- * finally seq_len[b] += 1. */
+ * finally seq_len[b] += 1.
+ * out == NULL: the gather was complete and its ml (required) is read.
+ * out != NULL: the preceding ckv_gather_attend was deferred (out == ml == NULL
+ * there); this call first completes it, writing out[batch][n_q_heads][head_dim]
+ * and, when ml is not NULL, ml[G][hpg][2], from the states left in ws, and
+ * takes the weights from those same states. */
 ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
-                             const int32_t *tok_n, const float *logits, const float *ml,
+                             const int32_t *tok_n, const float *logits, float *ml,
                              int32_t t_cap, const int32_t *top, int32_t kappa,
                              const void *k_new, const void *v_new, int32_t *edges,
-                             int32_t *assign, void *ws, size_t ws_bytes, ckv_stream_t stream);
+                             int32_t *assign, float *out, void *ws, size_t ws_bytes,
+                             ckv_stream_t stream);
 
 /* Dense flash-decode baseline: softmax attention of every query head over all
  * seq_len[b] cached tokens of its kv head.  out[batch][n_q_heads][head_dim];

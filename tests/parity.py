@@ -142,12 +142,14 @@ def _edges_ok(r: O.GraphStep, gpu_edges, stats: Stats, where: str) -> bool:
 
 def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None,
               check_state_every: int = 1, layer_kw: Optional[dict] = None, check_dense: bool = False,
-              pair=None, windows: int = 1) -> Stats:
+              pair=None, windows: int = 1, defer: bool = True) -> Stats:
     """Steps the library and the oracle side by side and checks every output.
-    windows > 1 runs each step as the decoder's windowed multi-stream step."""
+    windows > 1 runs each step as the decoder's windowed multi-stream step;
+    defer=False runs complete gathers (combine inside the gather kernel)."""
     layer, orc = pair if pair is not None else make_pair(w, seed, steps, graphs, **(layer_kw or {}))
     dev = layer.kv.kv.device
     dec, buf = layer.dec, layer.dec.buf
+    dec.defer = defer
     dec.set_windows(windows)
     assert not (check_dense and windows > 1), "the dense check runs between the calls of one window"
     check_csr(layer, orc)

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ckv.LIB.ckv_abi_version() == 3
+    assert ckv.LIB.ckv_abi_version() == 4
     for code in (0, -1, -2, -3, -4):
         assert ckv.ckv_status_str(code) != "unknown status"
     assert ckv.ckv_status_str(7) == "unknown status"
@@ -143,9 +143,15 @@ def test_gather_assign_dense_workspace_checks():
     r = ckv.LIB.ckv_gather_attend(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, 4100, 1.0, FAKE, None, FAKE,
                                   FAKE, need, None)
     assert r == ckv.CKV_E_INVALID
-    a = lambda kappa, ws, nbytes: ckv.LIB.ckv_assign_update(
-        ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, FAKE, 4100, FAKE, kappa, FAKE, FAKE, FAKE, FAKE, ws,
-        nbytes, None)
+    g = lambda out, ml: ckv.LIB.ckv_gather_attend(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, 4100, 1.0,
+                                                 out, FAKE, ml, FAKE, need, None)
+    assert g(FAKE, None) == ckv.CKV_E_INVALID   # out and ml: both (complete) or neither (deferred)
+    assert g(None, FAKE) == ckv.CKV_E_INVALID
+    a = lambda kappa, ws, nbytes, ml=FAKE, out=None: ckv.LIB.ckv_assign_update(
+        ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, ml, 4100, FAKE, kappa, FAKE, FAKE, FAKE, FAKE, out,
+        ws, nbytes, None)
+    assert a(8, FAKE, need, ml=None) == ckv.CKV_E_INVALID   # complete gather: its ml is read
+    assert a(0, FAKE, need, ml=None, out=FAKE) == ckv.CKV_E_INVALID
     assert a(0, FAKE, need) == ckv.CKV_E_INVALID
     assert a(33, FAKE, need) == ckv.CKV_E_INVALID
     assert a(8, None, need) == ckv.CKV_E_WORKSPACE

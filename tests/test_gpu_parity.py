@@ -33,7 +33,7 @@ def small_group(**kw):
 def test_tiny_workload_16_steps(seed):
     w = synth.preset("tiny")
     PY.log(f"tiny seed={seed}")
-    st = PY.run_steps(w, seed, w.steps, check_dense=True)
+    st = PY.run_steps(w, seed, w.steps, check_dense=True, defer=seed == 1)
     PY.log(f"  near-tie selections {st.near_sel}, edges {st.near_edges}, max abs {st.max_abs:.2e}")
     assert st.steps == 16
 
@@ -246,6 +246,43 @@ def test_windowed_equals_one_window():
             assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("case", ["per_head", "group", "per_head_long", "group_windows"])
+def test_deferred_combine_equals_complete(case):
+    """A gather whose combine runs in the assign kernel gives the same bits as
+    a complete gather followed by the assign: outputs, softmax state, edges,
+    assignments and the whole index.  The long case has more spans per graph
+    than the combine stages in LDS."""
+    if case.startswith("group"):
+        w = small_group(batch=2, n_ctx=6000, min_ctx=2000, steps=5)
+    elif case == "per_head_long":
+        w = small_per_head(n_ctx=24000, budget=20000, n_kv_heads=2, n_q_heads=4, steps=3)
+    else:
+        w = small_per_head(n_ctx=7000, steps=5)
+    windows = 3 if case.endswith("windows") else 1
+    PY.log(f"deferred combine vs complete gather: {case}")
+    runs = []
+    for defer in (False, True):
+        layer = runner.load_layer(w, 29, extra=w.steps + 1)
+        layer.dec.defer = defer
+        layer.dec.set_windows(windows)
+        rec = []
+        for t in range(w.steps):
+            inp = synth.gen_step(w, 29, t, layer.slices)
+            layer.dec.step(inp.q.cuda(), inp.k_new.cuda(), inp.v_new.cuda())
+            b = layer.dec.buf
+            n = b.tok_n.cpu()
+            rec += [x.cpu().clone() for x in (b.out, b.ml, b.edges, b.assign, b.tok_n)]
+            rec += [b.logits[g, :, :n[g]].cpu().clone() for g in range(n.numel())]
+        rec += [getattr(layer.idx, k).cpu().clone() for k in ckv.CommunityIndex.STATE]
+        rec += [layer.kv.seq_len.cpu().clone(), cached_rows(layer.kv)]
+        assert int(layer.idx.status.item()) == 0
+        runs.append(rec)
+    if case == "per_head_long":
+        assert int(n.max()) > 64 * 256, "the long case must exceed the staged span count"
+    for x, y in zip(*runs):
+        assert torch.equal(x, y)
+
+
 def test_dense_baseline_matches_oracle():
     w = synth.preset("qwen3_8b_32k").replace(n_ctx=20000, batch=2, min_ctx=9000)
     PY.log("dense baseline")
@@ -271,6 +308,7 @@ def test_attention_mass_recall_matches_oracle(group):
     PY.log(f"recall group={group}")
     layer, orc = PY.make_pair(w, 31, 3)
     dec, buf = layer.dec, layer.dec.buf
+    dec.defer = False  # ml is read before the update
     dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
     dout = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     for t in range(3):
