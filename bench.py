@@ -31,7 +31,7 @@ HBM_PEAK_GBPS = 8000.0
 # HBM traffic of one gather launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
 # scaled by a plain copy kernel; valid only for the sources it names.
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gather_attend_llama31_8b_128k_pmc.txt")
-GATHER_SOURCES = ("attend.hip", "ckv_device.h", "ckv_internal.h")
+GATHER_SOURCES = ("attend.hip", "combine.h", "ckv_device.h", "ckv_internal.h")
 
 
 def log(msg):

@@ -6,17 +6,19 @@
 // Every caller that combines the same records gets the same bits: the gather's
 // own last block, and the assign kernel when the gather was launched with its
 // combine deferred.  Up to kCombineLds chunks: one wave per head reduces M and
-// L over its lanes (lane c holds chunk c) and stages s_c in LDS, then each
-// (head, dim) sums o_c s_c over the chunks in increasing order as one fma
-// chain.  Longer lists (a different, equally fixed order): every (head, dim)
-// walks the chunks itself.
+// L over its lanes (lane c holds chunks c, c + 64, ...; L is each lane's fma
+// chain over its chunks, then a fixed-order wave sum) and stages s_c in LDS,
+// then each (head, dim) sums o_c s_c over the chunks in increasing order as
+// one fma chain.  Longer lists (a different, equally fixed order): every
+// (head, dim) walks the chunks itself.
 #pragma once
 
 #include "ckv_device.h"
 
 namespace ckv {
 
-constexpr int kCombineLds = 64;   // chunks handled by the staged form (one per lane)
+constexpr int kCombineLds = 256;  // chunks handled by the staged form (four per lane)
+constexpr int kCombineLanePass = kCombineLds / 64;
 constexpr int kCombineBatch = 32; // accumulator loads in flight per (head, dim) pair and pass
 
 template <int NH>
@@ -46,14 +48,28 @@ __device__ __forceinline__ float chunk_scale(float m, float M) {
 
 // Step 1 (nact <= kCombineLds): stage every head's (m, l) into LDS.  The
 // caller then synchronises the block (an LDS barrier suffices).
+// All loads are issued before the first LDS write (256-thread block).
 template <int NH, int D, int PS, bool DEV>
 __device__ __forceinline__ void combine_stage(const float *P, int nchunk, int nact, CombineLds<NH> &s) {
     if (nact > kCombineLds) return;
-    for (int i = threadIdx.x; i < NH * nact; i += blockDim.x) {
+    constexpr int IT = (NH * kCombineLds + 255) / 256;
+    float m[IT], l[IT];
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int i = threadIdx.x + k * 256;
         const int h = i / nact, c = i - (i / nact) * nact;
         const float *r = P + ((size_t)h * nchunk + c) * PS;
-        s.m[h][c] = ld_part<DEV>(r + D);
-        s.l[h][c] = ld_part<DEV>(r + D + 1);
+        m[k] = i < NH * nact ? ld_part<DEV>(r + D) : 0.f;
+        l[k] = i < NH * nact ? ld_part<DEV>(r + D + 1) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < IT; ++k) {
+        const int i = threadIdx.x + k * 256;
+        if (i < NH * nact) {
+            const int h = i / nact, c = i - (i / nact) * nact;
+            s.m[h][c] = m[k];
+            s.l[h][c] = l[k];
+        }
     }
 }
 
@@ -64,12 +80,26 @@ template <int NH>
 __device__ __forceinline__ void combine_heads(int nact, CombineLds<NH> &s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int h = wave; h < NH; h += 4) {
-        const bool in = lane < nact;
-        const float m = in ? s.m[h][lane] : kNegInf;
-        const float M = wave_max_f(m);
-        const float sc = in ? chunk_scale(m, M) : 0.f;
-        const float L = wave_sum_f(in ? s.l[h][lane] * sc : 0.f);
-        if (in) s.sc[h][lane] = sc;
+        float m[kCombineLanePass];
+        float Mlane = kNegInf;
+#pragma unroll
+        for (int k = 0; k < kCombineLanePass; ++k) {
+            const int c = lane + 64 * k;
+            m[k] = c < nact ? s.m[h][c] : kNegInf;
+            Mlane = fmaxf(Mlane, m[k]);
+        }
+        const float M = wave_max_f(Mlane);
+        float Llane = 0.f;
+#pragma unroll
+        for (int k = 0; k < kCombineLanePass; ++k) {
+            const int c = lane + 64 * k;
+            if (c < nact) {
+                const float sc = chunk_scale(m[k], M);
+                s.sc[h][c] = sc;
+                Llane = fmaf(s.l[h][c], sc, Llane);
+            }
+        }
+        const float L = wave_sum_f(Llane);
         if (lane == 0) {
             s.M[h] = M;
             s.L[h] = L;
@@ -205,10 +235,26 @@ template <int D, int PS, bool DEV>
 __device__ __forceinline__ void head_state_long(const float *P, int nchunk, int nact, int h, float &M, float &L) {
     const float *r = P + (size_t)h * nchunk * PS;
     M = kNegInf;
-    for (int c = 0; c < nact; ++c) M = fmaxf(M, ld_part<DEV>(r + (size_t)c * PS + D));
+    for (int c0 = 0; c0 < nact; c0 += kCombineBatch) {
+        float mm[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            mm[j] = c0 + j < nact ? ld_part<DEV>(r + (size_t)(c0 + j) * PS + D) : kNegInf;
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) M = fmaxf(M, mm[j]);
+    }
     L = 0.f;
-    for (int c = 0; c < nact; ++c)
-        L = fmaf(ld_part<DEV>(r + (size_t)c * PS + D + 1), chunk_scale(ld_part<DEV>(r + (size_t)c * PS + D), M), L);
+    for (int c0 = 0; c0 < nact; c0 += kCombineBatch) {
+        float mm[kCombineBatch], ll[kCombineBatch];
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j) {
+            mm[j] = c0 + j < nact ? ld_part<DEV>(r + (size_t)(c0 + j) * PS + D) : kNegInf;
+            ll[j] = c0 + j < nact ? ld_part<DEV>(r + (size_t)(c0 + j) * PS + D + 1) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kCombineBatch; ++j)
+            if (c0 + j < nact) L = fmaf(ll[j], chunk_scale(mm[j], M), L);
+    }
 }
 
 template <int D, int NH, int PS, bool DEV, int NT>

@@ -246,16 +246,19 @@ def test_windowed_equals_one_window():
             assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("case", ["per_head", "group", "per_head_long", "group_windows"])
+@pytest.mark.parametrize("case", ["per_head", "group", "per_head_mid", "per_head_long", "group_windows"])
 def test_deferred_combine_equals_complete(case):
     """A gather whose combine runs in the assign kernel gives the same bits as
     a complete gather followed by the assign: outputs, softmax state, edges,
-    assignments and the whole index.  The long case has more spans per graph
-    than the combine stages in LDS."""
+    assignments and the whole index.  The mid case has more spans per graph
+    than a wave has lanes, the long case more than the combine stages in LDS
+    (256 spans of 256 tokens)."""
     if case.startswith("group"):
         w = small_group(batch=2, n_ctx=6000, min_ctx=2000, steps=5)
-    elif case == "per_head_long":
+    elif case == "per_head_mid":
         w = small_per_head(n_ctx=24000, budget=20000, n_kv_heads=2, n_q_heads=4, steps=3)
+    elif case == "per_head_long":
+        w = small_per_head(n_ctx=80000, budget=70000, n_kv_heads=1, n_q_heads=2, steps=2)
     else:
         w = small_per_head(n_ctx=7000, steps=5)
     windows = 3 if case.endswith("windows") else 1
@@ -277,8 +280,10 @@ def test_deferred_combine_equals_complete(case):
         rec += [layer.kv.seq_len.cpu().clone(), cached_rows(layer.kv)]
         assert int(layer.idx.status.item()) == 0
         runs.append(rec)
+    if case == "per_head_mid":
+        assert int(n.max()) > 64 * 256
     if case == "per_head_long":
-        assert int(n.max()) > 64 * 256, "the long case must exceed the staged span count"
+        assert int(n.max()) > 256 * 256, "the long case must exceed the staged span count"
     for x, y in zip(*runs):
         assert torch.equal(x, y)
 
