@@ -47,6 +47,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--windows", type=int, default=1,
                     help="graph windows per step, each on its own stream (1 = one launch per call)")
+    ap.add_argument("--no-defer", action="store_true",
+                    help="complete gathers (combine inside the gather kernel) instead of the deferred combine")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -84,6 +86,7 @@ def main():
     layer = runner.load_layer(w, args.seed, extra=total + 1, slices=slices)
     dec, buf, idx, kv = layer.dec, layer.dec.buf, layer.idx, layer.kv
     dec.set_windows(args.windows)
+    dec.defer = not args.no_defer
     steps_in = [synth.gen_step(w, args.seed, t, slices) for t in range(total)]
     Q = torch.stack([s.q for s in steps_in]).cuda()
     KN = torch.stack([s.k_new for s in steps_in]).cuda()
@@ -186,10 +189,11 @@ def main():
         ckv.ckv_select_communities(kv, idx, q, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
                                    b.tok_list, b.tok_n)
         ckv.ckv_time_next_launch(*ev[i][2])
-        ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, None, b.logits, None, b.ws)
+        out, ml = (None, None) if dec.defer else (b.out, b.ml)
+        ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, out, b.logits, ml, b.ws)
         ckv.ckv_time_next_launch(*ev[i][3])
         ckv.ckv_assign_update(kv, idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, dec.kappa, KN[t], VN[t],
-                              b.edges, b.assign, b.ws, out=b.out)
+                              b.edges, b.assign, b.ws, out=b.out if dec.defer else None)
     torch.cuda.synchronize()
     dt = np.array([[a.elapsed_time(c) for a, c in ev[i]] for i in range(K)]) * 1e3  # us
     names = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
@@ -284,7 +288,7 @@ def main():
                    "graphs": "per_query_head" if w.mode == synth.PER_HEAD else "query_group",
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
                    "kv_dtype": w.dtype, "n_graphs": idx.n_graphs, "seed": args.seed,
-                   "windows": dec.windows},
+                   "windows": dec.windows, "deferred_combine": dec.defer},
         "gathered_kv_gbps": round(gather_gbps, 1),
         "gathered_kv_frac_of_hbm": round(gather_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "gather_attend", "achieved": round(gather_gbps, 1),
