@@ -15,6 +15,10 @@ context length.  Table 1 gives the per-step update as O(d) and the retrieval as 
 over the centroids.  Table 6 fixes the defaults (kappa = 8, per-head graphs,
 sinks excluded from the top-kappa pool).
 
+The same caption's panel (1), the prefill graph construction, is here too:
+every prompt token is linked to the earlier non-sink tokens it attends to
+most (prefill_edges).
+
 Everything is computed in float64 with plain numpy, one graph at a time, in
 the order the caption describes.  Where the page leaves a step open, the
 reading taken is stated at the function that implements it.
@@ -227,6 +231,84 @@ def majority_vote(edge_labels: Sequence[int]) -> int:
 # --------------------------------------------------------------------------
 # Whole-step driver over many graphs
 # --------------------------------------------------------------------------
+
+# --------------------------------------------------------------------------
+# Prefill graph construction (Figure 1, panel (1)): each query is connected to
+# the keys it attends to most, sinks left out of the pool.  It precedes the
+# partition (panel (2)) and the decode path; Table 10 times it as the prefill's
+# fused top-kappa selection.
+# --------------------------------------------------------------------------
+
+def causal_probs(q_heads: np.ndarray, keys: np.ndarray, sm_scale: float) -> np.ndarray:
+    """Causal softmax of every query position over the keys at or before it.
+
+    q_heads: [n][h][d] (the heads of one graph), keys: [n][d].  Returns
+    p [h][n][n] with p[h, i, j] = softmax_j(sm_scale * q[i, h] . k[j]) over
+    j <= i (reading: the prefill attention is the model's causal attention,
+    the token itself included) and 0 for j > i.
+    """
+    q = np.asarray(q_heads, dtype=np.float64)
+    K = np.asarray(keys, dtype=np.float64)
+    n = K.shape[0]
+    z = float(sm_scale) * np.einsum("ihd,jd->hij", q, K)
+    future = np.triu(np.ones((n, n), dtype=bool), k=1)
+    z[:, future] = -np.inf
+    e = np.exp(z - z.max(axis=2, keepdims=True))
+    return e / e.sum(axis=2, keepdims=True)
+
+
+def prefill_edges(q_heads: np.ndarray, keys: np.ndarray, n_sinks: int, kappa: int, sm_scale: float):
+    """Top-kappa edges of every query position of one graph.
+
+    The weight of key j for query i is the graph's attention weight: the
+    head's probability (one head) or the sum of the group's probabilities
+    (query group; as in the decode step).  Candidates are the keys
+    n_sinks <= j < i: sinks never become edges (Table 6) and a token is not
+    its own edge (reading: an edge links two tokens), while the token itself
+    stays in the softmax normaliser.  Ties go to the lower position; fewer
+    than kappa candidates: all of them.
+
+    Returns edges [n][kappa] (int64, -1 padded) and weights [n][kappa]
+    (float64, 0 padded), each row in rank order.
+    """
+    w = causal_probs(q_heads, keys, sm_scale).sum(axis=0)
+    n = w.shape[0]
+    edges = np.full((n, kappa), -1, dtype=np.int64)
+    weights = np.zeros((n, kappa), dtype=np.float64)
+    for i in range(n):
+        cand = np.arange(n_sinks, i)
+        if cand.size == 0:
+            continue
+        wi = w[i, n_sinks:i]
+        order = np.lexsort((cand, -wi))[:kappa]
+        edges[i, :order.size] = cand[order]
+        weights[i, :order.size] = wi[order]
+    return edges, weights
+
+
+def prefill_edges_rows(q_heads_rows: np.ndarray, rows: Sequence[int], keys: np.ndarray, n_sinks: int,
+                       kappa: int, sm_scale: float):
+    """prefill_edges for selected query positions only (long prefixes).
+
+    q_heads_rows: [len(rows)][h][d], the queries of those positions; keys:
+    [>= max(rows) + 1][d].  Same definition, one row at a time.
+    """
+    K = np.asarray(keys, dtype=np.float64)
+    edges = np.full((len(rows), kappa), -1, dtype=np.int64)
+    weights = np.zeros((len(rows), kappa), dtype=np.float64)
+    for r, i in enumerate(rows):
+        z = float(sm_scale) * (np.asarray(q_heads_rows[r], dtype=np.float64) @ K[:i + 1].T)  # [h][i+1]
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        w = (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+        cand = np.arange(n_sinks, i)
+        if cand.size == 0:
+            continue
+        wi = w[n_sinks:i]
+        order = np.lexsort((cand, -wi))[:kappa]
+        edges[r, :order.size] = cand[order]
+        weights[r, :order.size] = wi[order]
+    return edges, weights
+
 
 @dataclass
 class GraphState:

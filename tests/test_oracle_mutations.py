@@ -26,7 +26,10 @@ def _pins():
                P.test_top_kappa_excludes_sinks_and_takes_all_when_short,
                P.test_group_weights_explicit_loop, P.test_budget_walk_invariants_on_workload,
                P.test_recall_two_tokens_closed_form, P.test_recall_brute_force_loops,
-               P.test_recall_full_set_is_one_and_complements_add_up]
+               P.test_recall_full_set_is_one_and_complements_add_up,
+               P.test_prefill_identical_keys_closed_form, P.test_prefill_one_hot_target_closed_form,
+               P.test_prefill_subsets_brute_force, P.test_prefill_per_head_matches_decode_edges,
+               P.test_prefill_invariants_and_rows]
     checks += [lambda s=s: P.test_select_matches_definition(s) for s in range(40)]
     checks += [lambda s=s: P.test_top_kappa_matches_heap(s) for s in range(20)]
     checks += [lambda s=s: P.test_vote_matches_counter(s) for s in range(20)]
@@ -189,7 +192,83 @@ def m_recall_no_scale(q_heads, keys, positions, sm_scale):
     return _orig["attention_mass_recall"](q_heads, keys, positions, 1.0)
 
 
+def _prefill_from(w, n_sinks, kappa, cand_hi=0, tie_sign=1):
+    # top-kappa rows from a weight matrix w [n][n]; candidates [n_sinks, i + cand_hi)
+    n = w.shape[0]
+    edges = np.full((n, kappa), -1, dtype=np.int64)
+    weights = np.zeros((n, kappa))
+    for i in range(n):
+        cand = np.arange(n_sinks, min(i + cand_hi, n))
+        if cand.size == 0:
+            continue
+        wi = w[i, cand]
+        order = np.lexsort((tie_sign * cand, -wi))[:kappa]
+        edges[i, :order.size] = cand[order]
+        weights[i, :order.size] = wi[order]
+    return edges, weights
+
+
+def m_prefill_self_candidate(q_heads, keys, n_sinks, kappa, sm_scale):
+    return _prefill_from(O.causal_probs(q_heads, keys, sm_scale).sum(axis=0), n_sinks, kappa, cand_hi=1)
+
+
+def m_prefill_sinks_in_pool(q_heads, keys, n_sinks, kappa, sm_scale):
+    return _orig["prefill_edges"](q_heads, keys, 0, kappa, sm_scale)
+
+
+def m_prefill_tie_high_pos(q_heads, keys, n_sinks, kappa, sm_scale):
+    return _prefill_from(O.causal_probs(q_heads, keys, sm_scale).sum(axis=0), n_sinks, kappa, tie_sign=-1)
+
+
+def m_prefill_group_max(q_heads, keys, n_sinks, kappa, sm_scale):
+    return _prefill_from(O.causal_probs(q_heads, keys, sm_scale).max(axis=0), n_sinks, kappa)
+
+
+def m_causal_self_excluded(q_heads, keys, sm_scale):
+    q, K = np.asarray(q_heads, np.float64), np.asarray(keys, np.float64)
+    n = K.shape[0]
+    z = float(sm_scale) * np.einsum("ihd,jd->hij", q, K)
+    z[:, np.triu(np.ones((n, n), dtype=bool), k=0)] = -np.inf
+    z[:, 0, 0] = 0.0  # row 0 keeps one term
+    e = np.exp(z - z.max(axis=2, keepdims=True))
+    return e / e.sum(axis=2, keepdims=True)
+
+
+def m_causal_no_mask(q_heads, keys, sm_scale):
+    q, K = np.asarray(q_heads, np.float64), np.asarray(keys, np.float64)
+    z = float(sm_scale) * np.einsum("ihd,jd->hij", q, K)
+    e = np.exp(z - z.max(axis=2, keepdims=True))
+    return e / e.sum(axis=2, keepdims=True)
+
+
+def m_causal_no_scale(q_heads, keys, sm_scale):
+    return _orig["causal_probs"](q_heads, keys, 1.0)
+
+
+def m_prefill_rows_self_excluded(q_heads_rows, rows, keys, n_sinks, kappa, sm_scale):
+    K = np.asarray(keys, np.float64)
+    edges = np.full((len(rows), kappa), -1, dtype=np.int64)
+    weights = np.zeros((len(rows), kappa))
+    for r, i in enumerate(rows):
+        if i == 0:
+            continue
+        z = float(sm_scale) * (np.asarray(q_heads_rows[r], np.float64) @ K[:i].T)
+        e = np.exp(z - z.max(axis=1, keepdims=True))
+        w = (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+        cand = np.arange(n_sinks, i)
+        if cand.size == 0:
+            continue
+        order = np.lexsort((cand, -w[n_sinks:i]))[:kappa]
+        edges[r, :order.size] = cand[order]
+        weights[r, :order.size] = w[n_sinks:i][order]
+    return edges, weights
+
+
 MUTANTS = {
+    "prefill_edges": [m_prefill_self_candidate, m_prefill_sinks_in_pool, m_prefill_tie_high_pos,
+                      m_prefill_group_max],
+    "causal_probs": [m_causal_self_excluded, m_causal_no_mask, m_causal_no_scale],
+    "prefill_edges_rows": [m_prefill_rows_self_excluded],
     "score_communities": [m_score_sign, m_score_no_empty_mask],
     "select_communities": [m_select_overflow_included, m_select_skip_ahead],
     "rank_communities": [m_rank_tie_high_id, m_rank_ascending],

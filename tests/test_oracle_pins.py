@@ -402,3 +402,109 @@ def test_recall_full_set_is_one_and_complements_add_up():
     np.testing.assert_allclose(O.attention_mass_recall(q, K, np.arange(50), 1.0), [1.0, 1.0], rtol=1e-14)
     np.testing.assert_allclose(O.attention_mass_recall(q, K, a, 1.0) + O.attention_mass_recall(q, K, b, 1.0),
                                [1.0, 1.0], rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Prefill graph construction (Figure 1, panel (1))
+# ---------------------------------------------------------------------------
+
+def test_prefill_identical_keys_closed_form():
+    # every key equal: p[i, j] = 1/(i+1) for j <= i, all candidates tie and the
+    # lowest positions win; a group of 3 identical heads sums to 3/(i+1)
+    n, d, s, kappa = 14, 5, 4, 3
+    K = np.tile(np.arange(1.0, d + 1.0), (n, 1))
+    q = np.random.default_rng(1).standard_normal((n, 3, d))
+    q[:, 1:] = q[:, :1]
+    e1, w1 = O.prefill_edges(q[:, :1], K, s, kappa, 0.7)
+    e3, w3 = O.prefill_edges(q, K, s, kappa, 0.7)
+    for i in range(n):
+        k = max(0, min(kappa, i - s))
+        want = list(range(s, s + k)) + [-1] * (kappa - k)
+        assert e1[i].tolist() == want and e3[i].tolist() == want
+        np.testing.assert_allclose(w1[i, :k], 1.0 / (i + 1), rtol=1e-14)
+        np.testing.assert_allclose(w3[i, :k], 3.0 / (i + 1), rtol=1e-14)
+        assert not w1[i, k:].any()
+
+
+def test_prefill_one_hot_target_closed_form():
+    # keys are unit vectors, query i points at one earlier key t(i) with
+    # strength a: z = a at t(i), 0 elsewhere, so p = e^a / (e^a + i) there and
+    # 1 / (e^a + i) at every other key j <= i (the token itself included)
+    n, s, kappa, a = 12, 2, 3, 2.5
+    K = np.eye(n)
+    t = [0, 0, 0, 1, 3, 2, 5, 4, 7, 8, 3, 9]
+    q = np.zeros((n, 1, n))
+    for i in range(n):
+        q[i, 0, t[i]] = a
+    e, w = O.prefill_edges(q, K, s, kappa, 1.0)
+    for i in range(n):
+        hi, lo = math.exp(a) / (math.exp(a) + i), 1.0 / (math.exp(a) + i)
+        cand = list(range(s, i))
+        if t[i] in cand:
+            want = [t[i]] + [j for j in cand if j != t[i]][:kappa - 1]
+            wts = [hi] + [lo] * (len(want) - 1)
+        else:
+            want, wts = cand[:kappa], [lo] * min(kappa, len(cand))
+        assert e[i, :len(want)].tolist() == want and (e[i, len(want):] == -1).all()
+        np.testing.assert_allclose(w[i, :len(want)], wts, rtol=1e-14)
+
+
+def test_prefill_subsets_brute_force():
+    # the edge set is the kappa-subset of the candidates with the largest
+    # weights: checked by enumerating every subset (distinct random weights);
+    # the weights are causal softmax values, whose ratios are exp(z_j - z_k)
+    rng = np.random.default_rng(11)
+    n, d, s, kappa = 9, 3, 2, 3
+    q, K = rng.standard_normal((n, 2, d)), rng.standard_normal((n, d))
+    e, w = O.prefill_edges(q, K, s, kappa, 0.9)
+    P = O.causal_probs(q, K, 0.9)
+    for i in range(n):
+        cand = list(range(s, i))
+        if not cand:
+            assert (e[i] == -1).all()
+            continue
+        W = P[:, i, :].sum(axis=0)
+        best = max(itertools.combinations(cand, min(kappa, len(cand))), key=lambda S: sum(W[j] for j in S))
+        assert set(e[i][e[i] >= 0].tolist()) == set(best)
+        for h in range(2):
+            np.testing.assert_allclose(P[h, i, :i + 1].sum(), 1.0, rtol=1e-14)
+            zi = [0.9 * float(np.dot(q[i, h], K[j])) for j in range(i + 1)]
+            np.testing.assert_allclose(P[h, i, 1:i + 1] / P[h, i, 0],
+                                       [math.exp(z - zi[0]) for z in zi[1:]], rtol=1e-12)
+            assert not P[h, i, i + 1:].any()
+
+
+def test_prefill_per_head_matches_decode_edges():
+    # one head: the edges of query i rank the earlier non-sink keys exactly as
+    # the decode step's top-kappa does over the attended set 0..i-1 (softmax is
+    # monotone in the logit; the normaliser does not change the order)
+    rng = np.random.default_rng(12)
+    n, d, s, kappa = 40, 6, 4, 5
+    q, K = rng.standard_normal((n, 1, d)), rng.standard_normal((n, d))
+    e, _ = O.prefill_edges(q, K, s, kappa, 0.6)
+    for i in range(1, n):
+        _, p, _ = O.attend(q[i], K[:i], K[:i], 0.6)
+        want = O.top_kappa(O.edge_weights(p), np.arange(i), kappa, s)
+        assert e[i, :want.size].tolist() == want.tolist() and (e[i, want.size:] == -1).all()
+
+
+def test_prefill_invariants_and_rows():
+    rng = np.random.default_rng(13)
+    n, d, s, kappa = 64, 8, 4, 6
+    q, K = rng.standard_normal((n, 4, d)), rng.standard_normal((n, d)) * 2
+    e, w = O.prefill_edges(q, K, s, kappa, 0.5)
+    P = O.causal_probs(q, K, 0.5).sum(axis=0)
+    for i in range(n):
+        k = max(0, min(kappa, i - s))
+        got = e[i, :k]
+        assert (e[i, k:] == -1).all() and (w[i, k:] == 0).all()
+        assert ((got >= s) & (got < i)).all() and len(set(got.tolist())) == k
+        assert (np.diff(w[i, :k]) <= 0).all()
+        np.testing.assert_allclose(w[i, :k], P[i, got], rtol=1e-14)
+        if k:
+            rest = np.setdiff1d(np.arange(s, i), got)
+            assert (P[i, rest] <= w[i, k - 1]).all()
+    rows = [0, 5, 31, 63]
+    er, wr = O.prefill_edges_rows(q[rows], rows, K, s, kappa, 0.5)
+    assert (er == e[rows]).all()
+    np.testing.assert_allclose(wr, w[rows], rtol=1e-13, atol=1e-300)
