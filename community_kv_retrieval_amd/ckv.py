@@ -31,6 +31,7 @@ CKV_MAX_KAPPA, CKV_MAX_C_CAP = 32, 16384
 
 EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_centroids",
            "ckv_select_communities", "ckv_gather_attend", "ckv_assign_update", "ckv_dense_attend",
+           "ckv_prefill_workspace_bytes", "ckv_prefill_topk",
            "ckv_time_next_launch", "ckv_status_str", "ckv_abi_version")
 
 
@@ -74,6 +75,9 @@ def _load():
                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_size_t, c_void_p]),
         "ckv_dense_attend": (c_int32, [KVP, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_prefill_workspace_bytes": (c_size_t, [KVP, c_int32, c_int32]),
+        "ckv_prefill_topk": (c_int32, [KVP, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int32, c_float,
+                                       c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_time_next_launch": (c_int32, [c_void_p, c_void_p]),
         "ckv_status_str": (ctypes.c_char_p, [c_int32]),
         "ckv_abi_version": (c_int32, []),
@@ -282,6 +286,28 @@ def ckv_assign_update(kv: KVStore, idx: CommunityIndex, tok_list: torch.Tensor, 
         ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(tok_list), _ptr(tok_n), _ptr(logits), _ptr(ml),
         t_cap, _ptr(top), kappa, _ptr(k_new), _ptr(v_new), _ptr(edges), _ptr(assign), _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def prefill_workspace(kv: KVStore, mode: int, n: int, device="cuda") -> torch.Tensor:
+    nbytes = int(LIB.ckv_prefill_workspace_bytes(ctypes.byref(kv.desc), mode, n))
+    if nbytes == 0:
+        raise ValueError(f"ckv_prefill_workspace_bytes: bad arguments (mode {mode}, n {n})")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def ckv_prefill_topk(kv: KVStore, mode: int, b: int, q: torch.Tensor, n_sinks: int, kappa: int, sm_scale: float,
+                     edges: torch.Tensor, weights: Optional[torch.Tensor], ws: torch.Tensor, stream=None):
+    """Prefill graph of sequence b: q [n][n_q_heads][head_dim], keys = the store's
+    positions 0..n-1; edges [graphs][n][kappa] int32, weights (optional) float32."""
+    n = q.shape[0]
+    graphs = kv.n_q_heads if mode == CKV_MODE_PER_HEAD else kv.n_kv_heads
+    _need(q, "q", kv.dtype, (n, kv.n_q_heads, kv.head_dim))
+    _need(edges, "edges", torch.int32, (graphs, n, kappa))
+    if weights is not None:
+        _need(weights, "weights", torch.float32, (graphs, n, kappa))
+    _check("ckv_prefill_topk", LIB.ckv_prefill_topk(
+        ctypes.byref(kv.desc), mode, b, _ptr(q), n, n_sinks, kappa, float(sm_scale), _ptr(edges), _ptr(weights),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def ckv_dense_attend(kv: KVStore, q: torch.Tensor, sm_scale: float, out: torch.Tensor, ws: torch.Tensor,

@@ -203,4 +203,30 @@ ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, flo
                                    (int32_t *)at(ws, L.ctr_dense), (hipStream_t)stream));
 }
 
+size_t ckv_prefill_workspace_bytes(const ckv_kv *kv, int32_t mode, int32_t n) {
+    if (check_kv(kv) != CKV_OK || n < 1) return 0;
+    if (mode != CKV_MODE_PER_HEAD && mode != CKV_MODE_QUERY_GROUP) return 0;
+    return align256((size_t)4 * kv->n_q_heads * n);
+}
+
+ckv_status ckv_prefill_topk(const ckv_kv *kv, int32_t mode, int32_t b, const void *q, int32_t n,
+                            int32_t n_sinks, int32_t kappa, float sm_scale, int32_t *edges, float *weights,
+                            void *ws, size_t ws_bytes, ckv_stream_t stream) {
+    ckv_status st = check_kv(kv);
+    if (st != CKV_OK) return st;
+    if (kv->dtype != CKV_DTYPE_BF16) return CKV_E_UNSUPPORTED;  // matrix cores take bf16 operands
+    if (mode != CKV_MODE_PER_HEAD && mode != CKV_MODE_QUERY_GROUP) return CKV_E_INVALID;
+    if (!q || !edges || b < 0 || b >= kv->batch) return CKV_E_INVALID;
+    if (n < 1 || (int64_t)n > (int64_t)kv->max_pages * kv->page_size) return CKV_E_INVALID;
+    if (n_sinks < 0 || kappa < 1 || kappa > CKV_MAX_KAPPA || !(sm_scale > 0.f)) return CKV_E_INVALID;
+    if (mode == CKV_MODE_QUERY_GROUP) {
+        const int grp = kv->n_q_heads / kv->n_kv_heads;
+        if (grp > 4 || kappa > 16) return CKV_E_UNSUPPORTED;
+    }
+    const size_t need = ckv_prefill_workspace_bytes(kv, mode, n);
+    if (!ws || ws_bytes < need) return CKV_E_WORKSPACE;
+    return hip_status(launch_prefill(kv, mode, b, q, n, n_sinks, kappa, sm_scale, edges, weights, (float *)ws,
+                                     (hipStream_t)stream));
+}
+
 }  // extern "C"

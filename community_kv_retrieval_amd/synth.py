@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 # stream tags for SeedSequence spawn keys
-_T_PART, _T_KEY, _T_VAL, _T_STEP, _T_LEN, _T_DEV, _T_DEV_STEP = 1, 2, 3, 4, 5, 6, 7
+_T_PART, _T_KEY, _T_VAL, _T_STEP, _T_LEN, _T_DEV, _T_DEV_STEP, _T_PREFILL = 1, 2, 3, 4, 5, 6, 7, 8
 
 PER_HEAD = "per_head"
 GROUP = "group"
@@ -341,3 +341,26 @@ def gen_steps_device(w: Workload, seed: int, layer: int, steps: int, centers: to
         * float(w.key_scale)
     vn = torch.randn((steps, B, Hkv, d), generator=g, device=device)
     return q.to(w.torch_dtype), kn.to(w.torch_dtype), vn.to(w.torch_dtype)
+
+
+def gen_prefill_queries(w: Workload, seed: int, layer: int, b: int, slices_b, n: Optional[int] = None) -> torch.Tensor:
+    """Queries of the prompt positions 0..n-1 of sequence b, [n][Hq][d] in the
+    storage dtype: a head of kv head kh asks at position i for the centre of
+    i's planted community in that slice plus N(0, noise^2) (the decode query
+    rule), a sink position asks N(0, I).  slices_b: gen_layer(...)[b] (or
+    partitions with centres, indexed by kv head)."""
+    G = w.n_q_heads // w.n_kv_heads
+    parts = [getattr(x, "part", x) for x in slices_b]
+    n = parts[0].labels.shape[0] if n is None else n
+    r = _rng(seed, _T_PREFILL, layer, b)
+    out = np.empty((n, w.n_q_heads, w.head_dim), dtype=np.float32)
+    for kh, part in enumerate(parts):
+        lab = part.labels[:n]
+        base = part.centers[np.maximum(lab, 0)]
+        sink = lab < 0
+        for g in range(G):
+            noise = r.standard_normal((n, w.head_dim), dtype=np.float32)
+            q = base + np.float32(w.noise) * noise
+            q[sink] = noise[sink]
+            out[:, kh * G + g] = q
+    return _to_storage(out, w)

@@ -244,11 +244,37 @@ ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32
 ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
                             void *ws, size_t ws_bytes, ckv_stream_t stream);
 
+/* Prefill graph construction (Figure 1 panel (1): during prefill each query is
+ * linked to the keys it attends to most; sinks are left out of the pool, Table 6;
+ * Table 10 times it as the fused top-kappa selection).  For every position
+ * i < n of sequence b and every graph g of the sequence (per head: query head
+ * g, g < n_q_heads; query group: kv head g, g < n_kv_heads) the kappa keys
+ * j with n_sinks <= j < i of largest weight, ties to the lower position,
+ * become edges[g][i][0..kappa) in rank order (-1 padded when fewer).  The
+ * weight of key j is the causal softmax probability of query i over keys
+ * 0..i (the token itself included in the normaliser, not in the pool) with
+ * logits sm_scale * q . k: the head's own (per head) or the sum over the
+ * group's heads (query group).  weights (NULL: not written) [g][i][kappa]
+ * holds those weights, 0 for padding.  Logits are float32 products of the
+ * bf16 operands (matrix cores), the weights float32.
+ * q: [n][n_q_heads][head_dim] bf16 (the prompt's queries); keys: positions
+ * 0..n-1 of sequence b in the store (written beforehand, e.g. by
+ * ckv_kv_write; seq_len is neither read nor changed).  Requires a bf16 store
+ * (else CKV_E_UNSUPPORTED), 1 <= kappa <= 32, sm_scale > 0; query groups need
+ * at most 4 heads per group and kappa <= 16 (else CKV_E_UNSUPPORTED).  ws:
+ * ckv_prefill_workspace_bytes(kv, mode, n) bytes (holds the per-head
+ * log-sum-exp of the group mode). */
+size_t ckv_prefill_workspace_bytes(const ckv_kv *kv, int32_t mode, int32_t n);
+ckv_status ckv_prefill_topk(const ckv_kv *kv, int32_t mode, int32_t b, const void *q, int32_t n,
+                            int32_t n_sinks, int32_t kappa, float sm_scale, int32_t *edges, float *weights,
+                            void *ws, size_t ws_bytes, ckv_stream_t stream);
+
 /* Kernel timing for profiling harnesses (no part of the method).  Arms the
  * calling host thread so that the next kernel launched by one of
  * ckv_score_centroids, ckv_select_communities, ckv_gather_attend,
- * ckv_assign_update or ckv_dense_attend (each launches exactly one kernel)
- * has `start` and `stop` recorded by its own dispatch (hipExtLaunchKernel):
+ * ckv_assign_update, ckv_dense_attend (each launches exactly one kernel) or
+ * ckv_prefill_topk (one kernel per head; the query-group mode launches two and
+ * the pair times the first) has `start` and `stop` recorded by its own dispatch (hipExtLaunchKernel):
  * hipEventElapsedTime(start, stop) is then that kernel's execution time, with
  * no marker packets around it.  One-shot: the launch consumes the pair.  A call
  * that fails validation launches nothing and leaves the pair armed.  Both

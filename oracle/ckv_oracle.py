@@ -286,6 +286,16 @@ def prefill_edges(q_heads: np.ndarray, keys: np.ndarray, n_sinks: int, kappa: in
     return edges, weights
 
 
+def prefill_row_weights(q_heads_row: np.ndarray, i: int, keys: np.ndarray, sm_scale: float) -> np.ndarray:
+    """The graph weight of every key j <= i for query position i: the causal
+    softmax over keys 0..i of each head (q_heads_row: [h][d]), summed over
+    the heads.  Returns [i + 1] float64."""
+    K = np.asarray(keys, dtype=np.float64)[:i + 1]
+    z = float(sm_scale) * (np.asarray(q_heads_row, dtype=np.float64) @ K.T)  # [h][i+1]
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    return (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+
+
 def prefill_edges_rows(q_heads_rows: np.ndarray, rows: Sequence[int], keys: np.ndarray, n_sinks: int,
                        kappa: int, sm_scale: float):
     """prefill_edges for selected query positions only (long prefixes).
@@ -293,13 +303,10 @@ def prefill_edges_rows(q_heads_rows: np.ndarray, rows: Sequence[int], keys: np.n
     q_heads_rows: [len(rows)][h][d], the queries of those positions; keys:
     [>= max(rows) + 1][d].  Same definition, one row at a time.
     """
-    K = np.asarray(keys, dtype=np.float64)
     edges = np.full((len(rows), kappa), -1, dtype=np.int64)
     weights = np.zeros((len(rows), kappa), dtype=np.float64)
     for r, i in enumerate(rows):
-        z = float(sm_scale) * (np.asarray(q_heads_rows[r], dtype=np.float64) @ K[:i + 1].T)  # [h][i+1]
-        e = np.exp(z - z.max(axis=1, keepdims=True))
-        w = (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+        w = prefill_row_weights(q_heads_rows[r], i, keys, sm_scale)
         cand = np.arange(n_sinks, i)
         if cand.size == 0:
             continue

@@ -195,3 +195,28 @@ def test_time_next_launch_arming():
     assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == \
         ckv.CKV_E_UNSUPPORTED
     assert f(None, None) == ckv.CKV_OK
+
+
+def test_prefill_workspace_and_validation():
+    kv = _kv()
+    wsb = lambda mode, n, k=kv: ckv.LIB.ckv_prefill_workspace_bytes(ctypes.byref(k), mode, n)
+    assert wsb(ckv.CKV_MODE_PER_HEAD, 4096) == 4 * 32 * 4096
+    assert wsb(ckv.CKV_MODE_QUERY_GROUP, 100) == 12800  # 4 * 32 * 100 rounded to 256
+    assert wsb(ckv.CKV_MODE_PER_HEAD, 0) == 0 and wsb(7, 10) == 0
+    need = wsb(ckv.CKV_MODE_QUERY_GROUP, 4096)
+    f = ckv.LIB.ckv_prefill_topk
+
+    def call(mode=ckv.CKV_MODE_PER_HEAD, b=0, q=FAKE, n=4096, sinks=4, kappa=8, scale=1.0, edges=FAKE,
+             ws=FAKE, nbytes=need, k=kv):
+        return f(ctypes.byref(k), mode, b, q, n, sinks, kappa, scale, edges, None, ws, nbytes, None)
+    assert call(b=1) == ckv.CKV_E_INVALID                       # sequence out of range
+    assert call(n=0) == ckv.CKV_E_INVALID
+    assert call(n=8200 * 16 + 1) == ckv.CKV_E_INVALID           # past the page table
+    assert call(kappa=0) == ckv.CKV_E_INVALID and call(kappa=33) == ckv.CKV_E_INVALID
+    assert call(sinks=-1) == ckv.CKV_E_INVALID and call(scale=0.0) == ckv.CKV_E_INVALID
+    assert call(q=None) == ckv.CKV_E_INVALID and call(edges=None) == ckv.CKV_E_INVALID
+    assert call(mode=5) == ckv.CKV_E_INVALID
+    assert call(ws=None) == ckv.CKV_E_WORKSPACE and call(nbytes=need - 1) == ckv.CKV_E_WORKSPACE
+    assert call(k=_kv(dtype=ckv.CKV_DTYPE_F32)) == ckv.CKV_E_UNSUPPORTED   # matrix cores: bf16 only
+    assert call(mode=ckv.CKV_MODE_QUERY_GROUP, kappa=17) == ckv.CKV_E_UNSUPPORTED
+    assert call(mode=ckv.CKV_MODE_QUERY_GROUP, k=_kv(n_kv_heads=4)) == ckv.CKV_E_UNSUPPORTED  # 8 heads per group

@@ -264,7 +264,12 @@ def m_prefill_rows_self_excluded(q_heads_rows, rows, keys, n_sinks, kappa, sm_sc
     return edges, weights
 
 
+def m_row_weights_no_scale(q_heads_row, i, keys, sm_scale):
+    return _orig["prefill_row_weights"](q_heads_row, i, keys, 1.0)
+
+
 MUTANTS = {
+    "prefill_row_weights": [m_row_weights_no_scale],
     "prefill_edges": [m_prefill_self_candidate, m_prefill_sinks_in_pool, m_prefill_tie_high_pos,
                       m_prefill_group_max],
     "causal_probs": [m_causal_self_excluded, m_causal_no_mask, m_causal_no_scale],
