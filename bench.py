@@ -55,6 +55,9 @@ def main():
     ap.add_argument("--recall-steps", type=int, default=16,
                     help="steps per budget of the attention-mass recall sweep (0: skip)")
     ap.add_argument("--profile", action="store_true", help="only warm-up + timed steps (for rocprofv3 runs)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill graph-construction leg")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill graph construction of the workload's first sequence (profiling)")
     ap.add_argument("--eager-only", action="store_true", help="with --profile: no HIP graph (counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB copy kernel 5 times (scale for rocprofv3 byte counters)")
@@ -80,6 +83,12 @@ def main():
         return
     W, K = args.warmup, args.steps
     total = W + K
+    if args.prefill_only:
+        slices = synth.gen_layer(w, args.seed)
+        layer = runner.load_layer(w, args.seed, extra=1, slices=slices)
+        print(json.dumps({"prefill_graph": bench_prefill(w, args.seed, layer.kv, slices, reps=args.steps)}),
+              flush=True)
+        return
     log(f"[bench] workload {w.name}: generating")
     t0 = time.time()
     slices = synth.gen_layer(w, args.seed)
@@ -264,6 +273,10 @@ def main():
         dec.budget = budget0
         dec.defer = True
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = bench_prefill(w, args.seed, kv, slices)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.seed, slices, steps_in, args.cpu_seconds)
@@ -306,12 +319,67 @@ def main():
         "tokens_per_step": round(float(tok[W:].sum(axis=1).mean()), 1),
         "dense_flash_decode": dense,
         "attention_mass_recall": recall,
+        "prefill_graph": prefill,
         "cpu_baseline": cpu,
         "ms_per_step_eager": round(ms_eager, 5),
         "launch": "hip_graph",
         "wall_s_timed": round(wall, 4),
     }
     print(json.dumps(res), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(w, seed, kv, slices, reps=3):
+    """Prefill graph construction (top-kappa edges per query, matrix cores) of
+    the first sequence's whole prompt: per head with weights, per head
+    without, and per query group.  Algorithmic work: n(n+1)/2 causal pairs x
+    2 d flop per query head (the group mode's second pass is not counted)."""
+    import numpy as np
+    import torch
+
+    from community_kv_retrieval_amd import ckv, synth
+
+    n = int(slices[0][0].part.labels.shape[0])
+    parts = [slices[0][kh].part for kh in range(w.n_kv_heads)]
+    q = synth.gen_prefill_queries_device(w, seed, 0, 0, parts)
+    flops = n * (n + 1) / 2 * 2 * w.head_dim * w.n_q_heads
+    out = {"workload": w.name, "prompt_tokens": n, "q_heads": w.n_q_heads, "kappa": w.kappa,
+           "algorithmic_tflop": round(flops / 1e12, 3)}
+    for name, mode, with_w in (("per_head", ckv.CKV_MODE_PER_HEAD, True),
+                               ("per_head_edges_only", ckv.CKV_MODE_PER_HEAD, False),
+                               ("query_group", ckv.CKV_MODE_QUERY_GROUP, True)):
+        graphs = w.n_q_heads if mode == ckv.CKV_MODE_PER_HEAD else w.n_kv_heads
+        edges = torch.empty((graphs, n, w.kappa), dtype=torch.int32, device="cuda")
+        weights = torch.empty((graphs, n, w.kappa), dtype=torch.float32, device="cuda") if with_w else None
+        ws = ckv.prefill_workspace(kv, mode, n)
+        ckv.ckv_prefill_topk(kv, mode, 0, q, w.n_sinks, w.kappa, w.sm_scale, edges, weights, ws)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()  # torch creates the underlying HIP events on first record
+            e1.record()
+            torch.cuda.synchronize()
+            if mode == ckv.CKV_MODE_PER_HEAD:  # the call's one kernel, dispatch-stamped
+                ckv.ckv_time_next_launch(e0, e1)
+                ckv.ckv_prefill_topk(kv, mode, 0, q, w.n_sinks, w.kappa, w.sm_scale, edges, weights, ws)
+            else:  # two kernels: events around the call
+                e0.record()
+                ckv.ckv_prefill_topk(kv, mode, 0, q, w.n_sinks, w.kappa, w.sm_scale, edges, weights, ws)
+                e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        t = float(np.median(ms))
+        tf = flops / (t * 1e-3) / 1e12
+        out[name] = {"ms_per_layer": round(t, 3), "tflops": round(tf, 1),
+                     "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del edges, weights, ws
+    out["roofline"] = {"bound": "mfma", "kernel": "prefill_topk (per head, weights)",
+                       "achieved": out["per_head"]["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": out["per_head"]["frac_of_bf16_mfma_peak"], "traffic": None}
+    return out
 
 
 def bench_stack(args, w):

@@ -8,9 +8,11 @@
 // v_mfma_f32_32x32x16_bf16 and multiplies 32-key tiles of K (the A operand,
 // read from LDS) into a 32x32 fp32 tile.  In that tile a lane owns one query
 // column and 16 keys, so everything per query stays in the lane: the scores
-// are scaled into the log2 domain, folded into an online log-sum-exp, and
-// offered to a sorted top-kappa list held in registers; the two lanes that
-// share a query merge their states at the end.  Four waves of a block use the
+// are folded into an online log-sum-exp (base 2, the scale entering the
+// exponent) and offered to a sorted top-kappa list held in registers; the two
+// lanes that share a query merge their states at the end.  Masks are only
+// evaluated on the tiles that touch the diagonal, the sinks or the end of
+// the prompt.  Four waves of a block use the
 // same keys (the heads of one kv head, or four query tiles in group mode), so
 // a 64-key tile is staged once per block in LDS, double-buffered, while the
 // next one loads.  Tiles are walked in increasing key order and a lane's keys
@@ -18,8 +20,8 @@
 // equal scores.
 //
 // Graph weights.  One head: the causal softmax probability of the head (the
-// list ranks the logits, which order the keys the same way; the weight is
-// 2^(s - lse) at the end).  Query group: the sum of the group's head
+// list ranks the raw dot products, which order the keys as the logits do for a
+// positive scale; the weight is 2^(c s - lse) at the end).  Query group: the sum of the group's head
 // probabilities, which needs every head's normaliser first, so a first pass
 // writes the per-head log-sum-exp and a second ranks the summed weights.
 #include "ckv_device.h"
@@ -71,6 +73,23 @@ __device__ __forceinline__ void pf_insert(float (&ls)[KL], int (&lp)[KL], float 
     }
 }
 
+// Insertion of a key visited after every key in the list (a higher
+// position): it ranks above an entry only with a strictly larger score.
+template <int KL>
+__device__ __forceinline__ void pf_insert_later(float (&ls)[KL], int (&lp)[KL], float s, int p) {
+#pragma unroll
+    for (int i = KL - 1; i > 0; --i) {
+        const bool up = s > ls[i - 1];
+        const bool here = s > ls[i];
+        ls[i] = up ? ls[i - 1] : (here ? s : ls[i]);
+        lp[i] = up ? lp[i - 1] : (here ? p : lp[i]);
+    }
+    if (s > ls[0]) {
+        ls[0] = s;
+        lp[0] = p;
+    }
+}
+
 // Key row m of the 32x32 accumulator entry j of lane half `hf`.
 __device__ __forceinline__ int pf_row(int j, int hf) { return (j >> 2) * 8 + hf * 4 + (j & 3); }
 
@@ -96,6 +115,66 @@ __device__ __forceinline__ void pf_rows(const PrefillParams &a, int kh, int kt, 
         const size_t row = (((size_t)pg[i] * a.Hkv + kh) << a.ps_log2) | (size_t)(pos & ((1 << a.ps_log2) - 1));
         v[i] = *reinterpret_cast<const u32x4_t *>(a.kv + row * row_bytes + (c % CPR) * 16);
     }
+}
+
+// 32x32 score tile: the K rows at `arow` (A operand, LDS) times the queries.
+template <int KK>
+__device__ __forceinline__ f32x16_t pf_mfma(const uint8_t *arow, const bf16x8_t (&qb)[KK]) {
+    f32x16_t acc = {};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8_t *>(arow + kk * 32), qb[kk], acc,
+                                                      0, 0, 0);
+    return acc;
+}
+
+// One lane's 16 scores (keys k0 + pf_row(j, hf)) into its log-sum-exp and its
+// top-kappa list.  Per head the scores are the raw dot products (the scale is
+// positive, so they rank the keys as the logits do; the running maximum m2 is
+// kept in the same units and c = sm_scale log2 e enters the exponent as one
+// fma); in group mode they are the summed weights.  MASK: the tile touches the
+// diagonal, the sinks or the end of the prompt (wave-uniform).
+template <int KL, bool LSE, bool TOPK, bool MASK>
+__device__ __forceinline__ void pf_scores_m(const PrefillParams &a, const float (&s)[16], int k0, int qp, int hf,
+                                            float none, float (&ls)[KL], int (&lp)[KL], float &m2, float &l2) {
+    bool att[16], cand[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int kp = k0 + pf_row(j, hf);
+        att[j] = !MASK || (kp <= qp && kp < a.n);
+        cand[j] = !MASK || (kp >= a.n_sinks && kp < qp && qp < a.n);
+    }
+    float tmax = kNegInf, cmax = none;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if constexpr (LSE) tmax = fmaxf(tmax, att[j] ? s[j] : kNegInf);
+        if constexpr (TOPK) cmax = fmaxf(cmax, cand[j] ? s[j] : none);
+    }
+    if constexpr (LSE) {
+        if (tmax > m2) {
+            l2 = m2 == kNegInf ? 0.f : l2 * exp2f((m2 - tmax) * a.c);
+            m2 = tmax;
+        }
+        const float mc = -m2 * a.c;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) l2 += att[j] ? exp2f(fmaf(s[j], a.c, mc)) : 0.f;
+    }
+    if constexpr (TOPK) {
+        if (__builtin_amdgcn_ballot_w64(cmax > ls[KL - 1])) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                if (cand[j] && s[j] > ls[KL - 1]) pf_insert_later<KL>(ls, lp, s[j], k0 + pf_row(j, hf));
+        }
+    }
+}
+
+template <int KL, bool LSE, bool TOPK>
+__device__ __forceinline__ void pf_scores(const PrefillParams &a, const float (&s)[16], int k0, int q0, int qp, int hf,
+                                          float none, float (&ls)[KL], int (&lp)[KL], float &m2, float &l2) {
+    if (k0 + 31 >= q0 || k0 < a.n_sinks || k0 + 31 >= a.n)
+        pf_scores_m<KL, LSE, TOPK, true>(a, s, k0, qp, hf, none, ls, lp, m2, l2);
+    else
+        pf_scores_m<KL, LSE, TOPK, false>(a, s, k0, qp, hf, none, ls, lp, m2, l2);
 }
 
 template <int D, int KL, int VAR, int GH>
@@ -160,93 +239,80 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams a) {
     float m2 = kNegInf, l2 = 0.f;  // online log-sum-exp state (log2 domain)
 
     // Staging: thread t moves chunks t + 256 i (row c / CPR, column c % CPR).
+    // Two register sets alternate, so the rows of tile kt + 2 are in flight
+    // while tile kt is computed (and the page-table entries two tiles further).
     int pgA[NCH], pgB[NCH];
-    u32x4_t stage[NCH];
+    u32x4_t stA[NCH], stB[NCH];
     pf_pages<CPR, NCH>(a, 0, pgA);
-    pf_rows<D, CPR, NCH>(a, kh, 0, pgA, stage);
-    if (nkt > 1) pf_pages<CPR, NCH>(a, 1, pgB);
+    pf_rows<D, CPR, NCH>(a, kh, 0, pgA, stA);
+    if (nkt > 2) pf_pages<CPR, NCH>(a, 2, pgA);
+    if (nkt > 1) {
+        pf_pages<CPR, NCH>(a, 1, pgB);
+        pf_rows<D, CPR, NCH>(a, kh, 1, pgB, stB);
+        if (nkt > 3) pf_pages<CPR, NCH>(a, 3, pgB);
+    }
 
-    for (int kt = 0; kt < nkt; ++kt) {
+    auto key_tile = [&](int kt, u32x4_t (&stg)[NCH], int (&pg)[NCH]) __attribute__((always_inline)) {
         uint8_t *buf = s_k[kt & 1];
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const int c = tid + 256 * i;
-            *reinterpret_cast<u32x4_t *>(buf + (c / CPR) * ROWB + (c % CPR) * 16) = stage[i];
+            *reinterpret_cast<u32x4_t *>(buf + (c / CPR) * ROWB + (c % CPR) * 16) = stg[i];
         }
         __syncthreads();
-        if (kt + 1 < nkt) {
-            pf_rows<D, CPR, NCH>(a, kh, kt + 1, pgB, stage);
-            if (kt + 2 < nkt) pf_pages<CPR, NCH>(a, kt + 2, pgB);
+        if (kt + 2 < nkt) {
+            pf_rows<D, CPR, NCH>(a, kh, kt + 2, pg, stg);
+            if (kt + 4 < nkt) pf_pages<CPR, NCH>(a, kt + 4, pg);
         }
-
+        const int k0 = kt * kPfKeys;
+        if (k0 > qlast) return;  // wave-uniform: past this wave's queries
+        const bool two = k0 + 32 <= qlast;
+        const uint8_t *r0 = buf + qc * ROWB + hf * 16;
+        const uint8_t *r1 = r0 + 32 * ROWB;
+        // Scores of this lane's query against keys k0 + [0, 32) and k0 + [32, 64)
+        // (entry j: key pf_row(j, hf)), log2 domain; both MFMA chains are issued
+        // before the scores of the first are used.
+        float s0[16], s1[16];
+        if constexpr (kGroup) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            const int k0 = kt * kPfKeys + st * 32;
-            if (k0 > qlast) continue;  // wave-uniform: past this wave's queries
-            const uint8_t *arow = buf + (st * 32 + qc) * ROWB + hf * 16;
-            // Scores of this lane's query against keys k0 + pf_row(j, hf), log2 domain.
-            float s[16];
-            if constexpr (kGroup) {
+            for (int j = 0; j < 16; ++j) s0[j] = s1[j] = 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s[j] = 0.f;
+            for (int h = 0; h < NQH; ++h) {
+                const f32x16_t acc0 = pf_mfma<KK>(r0, qb[h]);
+                f32x16_t acc1 = {};
+                if (two) acc1 = pf_mfma<KK>(r1, qb[h]);
 #pragma unroll
-                for (int h = 0; h < NQH; ++h) {
-                    f32x16_t acc = {};
+                for (int j = 0; j < 16; ++j) s0[j] += exp2f(fmaf(acc0[j], a.c, -lse_q[h]));
+                if (two) {
 #pragma unroll
-                    for (int kk = 0; kk < KK; ++kk)
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            *reinterpret_cast<const bf16x8_t *>(arow + kk * 32), qb[h][kk], acc, 0, 0, 0);
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) s[j] += exp2f(acc[j] * a.c - lse_q[h]);
+                    for (int j = 0; j < 16; ++j) s1[j] += exp2f(fmaf(acc1[j], a.c, -lse_q[h]));
                 }
-            } else {
-                f32x16_t acc = {};
-#pragma unroll
-                for (int kk = 0; kk < KK; ++kk)
-                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        *reinterpret_cast<const bf16x8_t *>(arow + kk * 32), qb[0][kk], acc, 0, 0, 0);
-#pragma unroll
-                for (int j = 0; j < 16; ++j) s[j] = acc[j] * a.c;
             }
-            // Masks only near the diagonal, the sinks and the end of the prompt.
-            const bool edge = k0 + 31 >= q0 || k0 < a.n_sinks || k0 + 31 >= a.n;
-            bool att[16], cand[16];
+        } else {
+            const f32x16_t acc0 = pf_mfma<KK>(r0, qb[0]);
+            f32x16_t acc1 = {};
+            if (two) acc1 = pf_mfma<KK>(r1, qb[0]);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int kp = k0 + pf_row(j, hf);
-                att[j] = !edge || (kp <= qp && kp < a.n);
-                cand[j] = !edge || (kp >= a.n_sinks && kp < qp && qp < a.n);
-            }
-            if constexpr (kLse) {
-                float tmax = kNegInf;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) tmax = fmaxf(tmax, att[j] ? s[j] : kNegInf);
-                if (tmax > m2) {
-                    l2 *= exp2f(m2 - tmax);
-                    m2 = tmax;
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) l2 += att[j] ? exp2f(s[j] - m2) : 0.f;
-            }
-            if constexpr (kTopk) {
-                float cmax = kNone;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) cmax = fmaxf(cmax, cand[j] ? s[j] : kNone);
-                if (__builtin_amdgcn_ballot_w64(cmax > ls[KL - 1])) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        if (cand[j] && s[j] > ls[KL - 1]) pf_insert<KL>(ls, lp, s[j], k0 + pf_row(j, hf));
-                }
+                s0[j] = acc0[j];
+                s1[j] = acc1[j];
             }
         }
+        pf_scores<KL, kLse, kTopk>(a, s0, k0, q0, qp, hf, kNone, ls, lp, m2, l2);
+        if (two) pf_scores<KL, kLse, kTopk>(a, s1, k0 + 32, q0, qp, hf, kNone, ls, lp, m2, l2);
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+        key_tile(kt, stA, pgA);
+        if (kt + 1 < nkt) key_tile(kt + 1, stB, pgB);
     }
 
     // The two lanes of each query (qc, qc + 32) merge their states.
     if constexpr (kLse) {
         const float mo = __shfl_xor(m2, 32, 64), lo = __shfl_xor(l2, 32, 64);
         const float M = fmaxf(m2, mo);
-        const float L = (m2 == kNegInf ? 0.f : l2 * exp2f(m2 - M)) + (mo == kNegInf ? 0.f : lo * exp2f(mo - M));
-        m2 = M + log2f(L);  // the query's log-sum-exp, log2 domain
+        const float L = (m2 == kNegInf ? 0.f : l2 * exp2f((m2 - M) * a.c)) +
+                        (mo == kNegInf ? 0.f : lo * exp2f((mo - M) * a.c));
+        m2 = M * a.c + log2f(L);  // the query's log-sum-exp of the logits, log2 domain
     }
     if constexpr (kTopk) {
         float os[KL];
@@ -274,7 +340,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams a) {
             e[i] = has ? lp[i] : -1;
             if (w) {
                 float wt = 0.f;
-                if (has) wt = kGroup ? ls[i] : exp2f(ls[i] - m2);
+                if (has) wt = kGroup ? ls[i] : exp2f(fmaf(ls[i], a.c, -m2));
                 w[i] = wt;
             }
         }

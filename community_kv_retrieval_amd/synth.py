@@ -364,3 +364,22 @@ def gen_prefill_queries(w: Workload, seed: int, layer: int, b: int, slices_b, n:
             q[sink] = noise[sink]
             out[:, kh * G + g] = q
     return _to_storage(out, w)
+
+
+def gen_prefill_queries_device(w: Workload, seed: int, layer: int, b: int, parts, device="cuda") -> torch.Tensor:
+    """gen_prefill_queries' rule drawn on the device (long prompts): [n][Hq][d]
+    in the storage dtype, noise from a torch generator keyed like the host
+    stream.  parts: the sequence's partitions with centres, by kv head."""
+    G = w.n_q_heads // w.n_kv_heads
+    n = parts[0].labels.shape[0]
+    g = torch_generator(seed, _T_PREFILL, layer, b, device=device)
+    out = torch.empty((n, w.n_q_heads, w.head_dim), dtype=w.torch_dtype, device=device)
+    for kh, part in enumerate(parts):
+        lab = torch.from_numpy(part.labels.astype(np.int64)).to(device)
+        cent = torch.from_numpy(part.centers).to(device)
+        base = cent[lab.clamp(min=0)]
+        sink = (lab < 0)[:, None]
+        for h in range(G):
+            noise = torch.randn((n, w.head_dim), generator=g, device=device)
+            out[:, kh * G + h] = torch.where(sink, noise, base + float(w.noise) * noise).to(w.torch_dtype)
+    return out
