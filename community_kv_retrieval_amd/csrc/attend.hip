@@ -49,6 +49,92 @@ constexpr int pick_u() {
     return (NH >= 8 || RowSlice<T, D>::BYTES == 32) ? 4 : 8;
 }
 
+// Block epilogue shared by the gather kernels.  The four waves' softmax states
+// (s_wm, s_wl: max and sum per head; s_wacc: unnormalised accumulators) are
+// merged in a fixed order into the span's record; a deferred gather stops
+// there, a one-span list writes out and ml directly, otherwise the last block
+// of the unit combines every span's record.
+template <int D, int NH, bool DENSE>
+__device__ __forceinline__ void attend_finish(const AttendParams &a, int unit, int b, int qh0, int chunk, int nact,
+                                              bool defer, float (&s_wm)[4][NH], float (&s_wl)[4][NH],
+                                              float (&s_wacc)[4][NH][D], CombineLds<NH> &s_comb, int &s_last) {
+    constexpr int PS = part_stride(D);
+    const int tid = threadIdx.x;
+    __syncthreads();
+
+    // Block result per head: merge the four waves in a fixed order.
+    float *P = a.part + (size_t)unit * NH * a.nchunk * PS;
+    for (int i = tid; i < NH * D; i += 256) {
+        const int h = i / D, d = i - (i / D) * D;
+        float M = s_wm[0][h];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) M = fmaxf(M, s_wm[w][h]);
+        float o = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float s = (s_wm[w][h] == kNegInf) ? 0.f : exp2f((s_wm[w][h] - M) * kLog2e);
+            o += s_wacc[w][h][d] * s;
+            L += s_wl[w][h] * s;
+        }
+        float *dst = P + ((size_t)h * a.nchunk + chunk) * PS;
+        if (defer) {  // read by a later kernel: plain stores
+            dst[d] = o;
+            if (d == 0) {
+                dst[D] = M;
+                dst[D + 1] = L;
+            }
+        } else if (nact == 1) {
+            a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = o / L;
+            if (a.ml && d == 0) {
+                a.ml[((size_t)unit * NH + h) * 2] = M;
+                a.ml[((size_t)unit * NH + h) * 2 + 1] = L;
+            }
+        } else {
+            st_dev(dst + d, o);
+            if (d == 0) {
+                st_dev(dst + D, M);
+                st_dev(dst + D + 1, L);
+            }
+        }
+    }
+    if constexpr (!DENSE) CKV_TMARK(23);
+    if constexpr (!DENSE) CKV_BMARK(3);
+    if (nact == 1 || defer) return;
+
+    // The last block of the unit combines every block's partial.
+    stores_done();
+    __syncthreads();
+    if (tid == 0) s_last = arrive_last(&a.ctr[unit], nact);
+    __syncthreads();
+    if constexpr (!DENSE) CKV_BMARK(4);
+    if (!s_last) return;
+    {
+        float *o = a.out + ((size_t)b * a.Hq + qh0) * D;
+        float *mlu = a.ml ? a.ml + (size_t)unit * NH * 2 : nullptr;
+        constexpr int NB = kCombineBatch;
+        if (nact <= NB) {  // accumulators and (m, l) in one round trip
+            float v[combine_pairs<D, NH, 256>()][NB];
+            combine_preload<D, NH, PS, true, 256, NB>(P, a.nchunk, nact, tid, v);
+            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
+            __syncthreads();
+            combine_heads<NH>(nact, s_comb);
+            __syncthreads();
+            combine_out_regs<D, NH, 256, NB>(nact, s_comb, tid, v, o, mlu);
+        } else if (nact <= kCombineLds) {
+            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
+            __syncthreads();
+            combine_heads<NH>(nact, s_comb);
+            __syncthreads();
+            combine_out<D, NH, PS, true, 256>(P, a.nchunk, nact, s_comb, tid, o, mlu);
+        } else {
+            combine_out_long<D, NH, PS, true, 256>(P, a.nchunk, nact, tid, o, mlu);
+        }
+    }
+    if (tid == 0) reset_counter(&a.ctr[unit]);
+    if constexpr (!DENSE) CKV_TMARK(24);
+    if constexpr (!DENSE) CKV_BMARK(5);
+}
+
 template <typename T, int D, int NH, int U, bool DENSE>
 __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     using RS = RowSlice<T, D>;
@@ -246,79 +332,190 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
             for (int e = 0; e < E; ++e) s_wacc[wave][h][l16 * E + e] = acc[h][e];
         }
     }
-    __syncthreads();
+    attend_finish<D, NH, DENSE>(a, unit, b, qh0, chunk, nact, defer, s_wm, s_wl, s_wacc, s_comb, s_last);
+}
 
-    // Block result per head: merge the four waves in a fixed order.
-    float *P = a.part + (size_t)unit * NH * a.nchunk * PS;
-    for (int i = tid; i < NH * D; i += 256) {
-        const int h = i / D, d = i - (i / D) * D;
-        float M = s_wm[0][h];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) M = fmaxf(M, s_wm[w][h]);
-        float o = 0.f, L = 0.f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float s = (s_wm[w][h] == kNegInf) ? 0.f : exp2f((s_wm[w][h] - M) * kLog2e);
-            o += s_wacc[w][h][d] * s;
-            L += s_wl[w][h] * s;
+// Query groups of four heads (bf16): the q.k products on the matrix cores.
+// v_mfma_f32_16x16x32_bf16 takes 16 gathered tokens as the A operand (K rows,
+// one 16-byte slice per lane) and the four query heads, padded to 16, as the
+// B operand; in the result a lane with l16 = h < 4 holds head h's logits of
+// four tokens.  Those 16 lanes apply the softmax with wave-uniform running
+// (max, sum) per head and pass the probabilities through LDS to the
+// accumulation, which keeps the coalesced layout of the VALU kernel (four
+// token rows of 16 lanes, eight dims of V per lane).  With the statistics
+// uniform over the wave, its four rows add without rescaling.
+typedef __bf16 bf16x8v_t __attribute__((ext_vector_type(8)));
+typedef float f32x4v_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+__global__ __launch_bounds__(256) void attend_group4_kernel(AttendParams a) {
+    constexpr int NH = 4;
+    constexpr int PER_BLOCK = kGatherTokens;
+    constexpr int KS = D / 32;             // k-slices of one 16-token MFMA tile
+    constexpr int WT = PER_BLOCK / 4;      // tokens per wave
+    constexpr int BT = 32;                 // tokens per batch: two 16-token tiles
+    constexpr int E = 8;                   // dims of V per lane
+    static_assert(D == 16 * E, "one 16-lane row covers a V row");
+    const bool defer = a.out == nullptr;
+
+    __shared__ uint32_t s_row[PER_BLOCK];
+    __shared__ float s_wm[4][NH], s_wl[4][NH];
+    __shared__ float s_wacc[4][NH][D];
+    __shared__ __attribute__((aligned(16))) float s_p[4][BT][NH];
+    __shared__ CombineLds<NH> s_comb;
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, ts = lane >> 4;
+    const int chunk = blockIdx.x / a.units;
+    const int lunit = blockIdx.x - chunk * a.units;
+    const int unit = a.g0 + lunit;
+    const GraphCoords gc = graph_coords(unit, a.mode, a.Hq, a.Hkv);
+    const int b = gc.b, kh = gc.kh, qh0 = gc.qh0;
+    const int start = chunk * PER_BLOCK;
+    const int32_t *tl = a.tok_list + (size_t)unit * a.t_cap + start;
+    const int pos_l = tid < min(PER_BLOCK, a.t_cap - start) ? tl[tid] : 0;
+    const int n = a.tok_n[unit];
+    if (n <= 0 && chunk == 0 && !defer) {  // nothing to attend: zero output, empty softmax state
+        for (int i = tid; i < NH * D; i += 256) a.out[((size_t)b * a.Hq + qh0) * D + i] = 0.f;
+        if (a.ml && tid < NH) {
+            a.ml[((size_t)unit * NH + tid) * 2] = kNegInf;
+            a.ml[((size_t)unit * NH + tid) * 2 + 1] = 0.f;
         }
-        float *dst = P + ((size_t)h * a.nchunk + chunk) * PS;
-        if (defer) {  // read by a later kernel: plain stores
-            dst[d] = o;
-            if (d == 0) {
-                dst[D] = M;
-                dst[D + 1] = L;
-            }
-        } else if (nact == 1) {
-            a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = o / L;
-            if (a.ml && d == 0) {
-                a.ml[((size_t)unit * NH + h) * 2] = M;
-                a.ml[((size_t)unit * NH + h) * 2 + 1] = L;
-            }
-        } else {
-            st_dev(dst + d, o);
-            if (d == 0) {
-                st_dev(dst + D, M);
-                st_dev(dst + D + 1, L);
-            }
-        }
+        return;
     }
-    if constexpr (!DENSE) CKV_TMARK(23);
-    if constexpr (!DENSE) CKV_BMARK(3);
-    if (nact == 1 || defer) return;
-
-    // The last block of the unit combines every block's partial.
-    stores_done();
-    __syncthreads();
-    if (tid == 0) s_last = arrive_last(&a.ctr[unit], nact);
-    __syncthreads();
-    if constexpr (!DENSE) CKV_BMARK(4);
-    if (!s_last) return;
+    if (start >= n) return;
+    const int nact = (n + PER_BLOCK - 1) / PER_BLOCK;
+    const int cnt = min(PER_BLOCK, n - start);
     {
-        float *o = a.out + ((size_t)b * a.Hq + qh0) * D;
-        float *mlu = a.ml ? a.ml + (size_t)unit * NH * 2 : nullptr;
-        constexpr int NB = kCombineBatch;
-        if (nact <= NB) {  // accumulators and (m, l) in one round trip
-            float v[combine_pairs<D, NH, 256>()][NB];
-            combine_preload<D, NH, PS, true, 256, NB>(P, a.nchunk, nact, tid, v);
-            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
-            __syncthreads();
-            combine_heads<NH>(nact, s_comb);
-            __syncthreads();
-            combine_out_regs<D, NH, 256, NB>(nact, s_comb, tid, v, o, mlu);
-        } else if (nact <= kCombineLds) {
-            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
-            __syncthreads();
-            combine_heads<NH>(nact, s_comb);
-            __syncthreads();
-            combine_out<D, NH, PS, true, 256>(P, a.nchunk, nact, s_comb, tid, o, mlu);
-        } else {
-            combine_out_long<D, NH, PS, true, 256>(P, a.nchunk, nact, tid, o, mlu);
+        const int32_t *ptab = a.page_table + (size_t)b * a.max_pages;
+        const uint32_t smask = (1u << a.ps_log2) - 1u;
+        const int pos = tid < cnt ? pos_l : 0;  // rows past the end read position 0 (masked)
+        const int page = ptab[pos >> a.ps_log2];
+        s_row[tid] = ((uint32_t)(page * a.Hkv + kh) << a.ps_log2) | ((uint32_t)pos & smask);
+    }
+    // The heads as the B operand: head l16 (< 4), dims 32 s + 8 ts .. + 8.
+    const bf16_t *qp = reinterpret_cast<const bf16_t *>(a.q) + ((size_t)b * a.Hq + qh0 + min(l16, NH - 1)) * D + ts * 8;
+    bf16x8v_t qb[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const bf16x8v_t v = *reinterpret_cast<const bf16x8v_t *>(qp + 32 * s);
+        qb[s] = l16 < NH ? v : bf16x8v_t{};
+    }
+    __syncthreads();
+
+    float m[NH], l[NH], acc[NH][E];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        m[h] = kNegInf;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+    const bf16_t *kvb = reinterpret_cast<const bf16_t *>(a.kv);
+    const float c2 = a.sm_scale;
+    for (int bt = 0; bt < WT; bt += BT) {
+        const int t0 = wave * WT + bt;  // first token of the batch (within the span)
+        if (t0 >= cnt) break;           // wave-uniform
+        // K slices (A operand: token t0 + 16 g + l16, dims 32 s + 8 ts) and V (row ts of pass p).
+        bf16x8v_t ka[2][KS];
+        u32x4v_t vf[BT / 4];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const bf16_t *row = kvb + (size_t)s_row[t0 + 16 * g + l16] * (2 * D) + ts * 8;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) ka[g][s] = *reinterpret_cast<const bf16x8v_t *>(row + 32 * s);
+        }
+#pragma unroll
+        for (int p = 0; p < BT / 4; ++p)
+            vf[p] = *reinterpret_cast<const u32x4v_t *>(kvb + (size_t)s_row[t0 + 4 * p + ts] * (2 * D) + D + l16 * E);
+        f32x4v_t sc[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            sc[g] = f32x4v_t{};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) sc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[g][s], qb[s], sc[g], 0, 0, 0);
+        }
+        // Lane (ts, l16 = h < 4): head h, tokens t0 + 16 g + 4 ts + i.
+        float z[2][4];
+        float bmax = kNegInf;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + 16 * g + 4 * ts + i;
+                z[g][i] = t < cnt ? sc[g][i] * c2 : kNegInf;
+                bmax = fmaxf(bmax, z[g][i]);
+                if (l16 < NH && t < cnt) a.logits[((size_t)unit * NH + l16) * a.t_cap + start + t] = z[g][i];
+            }
+        bmax = fmaxf(bmax, shfl_xor_f(bmax, 16));
+        bmax = fmaxf(bmax, shfl_xor_f(bmax, 32));
+        float mh = kNegInf;  // this lane's head maximum after the update (lanes l16 < 4)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const float mn = fmaxf(m[h], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bmax), h)));
+            const float sh = (m[h] == kNegInf) ? 0.f : exp2f((m[h] - mn) * kLog2e);
+            l[h] *= sh;
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[h][e] *= sh;
+            m[h] = mn;
+            if (l16 == h) mh = mn;
+        }
+        float psum = 0.f;
+        if (l16 < NH) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pr = z[g][i] == kNegInf ? 0.f : exp2f((z[g][i] - mh) * kLog2e);
+                    s_p[wave][16 * g + 4 * ts + i][l16] = pr;
+                    psum += pr;
+                }
+        }
+        psum += shfl_xor_f(psum, 16);
+        psum += shfl_xor_f(psum, 32);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) l[h] += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(psum), h));
+        __builtin_amdgcn_wave_barrier();  // a wave's LDS accesses complete in order: the reads see the writes
+#pragma unroll
+        for (int p = 0; p < BT / 4; ++p) {
+            const float4 pp = *reinterpret_cast<const float4 *>(&s_p[wave][4 * p + ts][0]);
+            const uint32_t w4[4] = {vf[p][0], vf[p][1], vf[p][2], vf[p][3]};
+            float v[E];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = __uint_as_float(w4[k] << 16);
+                v[2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+            }
+            const float ph[NH] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] = fmaf(ph[h], v[e], acc[h][e]);
+        }
+        __builtin_amdgcn_wave_barrier();  // the next batch overwrites s_p only after every lane read it
+    }
+    // The wave's four token rows share (m, l): their accumulators add.
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            acc[h][e] += shfl_xor_f(acc[h][e], 16);
+            acc[h][e] += shfl_xor_f(acc[h][e], 32);
+        }
+    if (ts == 0) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            if (l16 == 0) {
+                s_wm[wave][h] = m[h];
+                s_wl[wave][h] = l[h];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) s_wacc[wave][h][l16 * E + e] = acc[h][e];
         }
     }
-    if (tid == 0) reset_counter(&a.ctr[unit]);
-    if constexpr (!DENSE) CKV_TMARK(24);
-    if constexpr (!DENSE) CKV_BMARK(5);
+    attend_finish<D, NH, false>(a, unit, b, qh0, chunk, nact, defer, s_wm, s_wl, s_wacc, s_comb, s_last);
 }
 
 template <typename T, int D, int NH, bool DENSE>
@@ -375,7 +572,14 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
     p.nchunk = ceil_div(t_cap, kGatherTokens);
     const Window w = window_of(idx);
     p.g0 = w.first;
-    return dispatch<false>(kv, heads_per_graph(kv, idx), p, w.count, s);
+    const int nh = heads_per_graph(kv, idx);
+    if (nh == 4 && kv->head_dim == 128 && kv->dtype == CKV_DTYPE_BF16) {  // query groups of four: matrix cores
+        AttendParams pu = p;
+        pu.units = w.count;
+        CKV_LAUNCH((attend_group4_kernel<128>), dim3(w.count * p.nchunk), dim3(256), s, pu);
+        return hipGetLastError();
+    }
+    return dispatch<false>(kv, nh, p, w.count, s);
 }
 
 hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
