@@ -161,9 +161,33 @@ __device__ __forceinline__ void pf_scores_m(const PrefillParams &a, const float 
     }
     if constexpr (TOPK) {
         if (__builtin_amdgcn_ballot_w64(cmax > ls[KL - 1])) {
+            // Each lane pops its own keys above its list minimum, lowest first
+            // (later keys come later), one per pass: the wave runs as many
+            // passes as its busiest lane has hits.
+            uint32_t hits = 0;
+            const float thr = ls[KL - 1];
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (cand[j] && s[j] > ls[KL - 1]) pf_insert_later<KL>(ls, lp, s[j], k0 + pf_row(j, hf));
+            for (int j = 0; j < 16; ++j) hits |= (cand[j] && s[j] > thr) ? (1u << j) : 0u;
+            while (__builtin_amdgcn_ballot_w64(hits != 0)) {
+                if (hits) {
+                    const uint32_t j = (uint32_t)__builtin_ctz(hits);
+                    hits &= hits - 1;
+                    // s[j] by a tree of bit-masked blends (no indexed access)
+                    uint32_t t8[8], t4[4];
+                    const uint32_t m0 = 0u - (j & 1u), m1 = 0u - ((j >> 1) & 1u);
+                    const uint32_t m2 = 0u - ((j >> 2) & 1u), m3 = 0u - ((j >> 3) & 1u);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t a0 = __float_as_uint(s[2 * i]), a1 = __float_as_uint(s[2 * i + 1]);
+                        t8[i] = a0 ^ ((a0 ^ a1) & m0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) t4[i] = t8[2 * i] ^ ((t8[2 * i] ^ t8[2 * i + 1]) & m1);
+                    const uint32_t t2a = t4[0] ^ ((t4[0] ^ t4[1]) & m2), t2b = t4[2] ^ ((t4[2] ^ t4[3]) & m2);
+                    const float sj = __uint_as_float(t2a ^ ((t2a ^ t2b) & m3));
+                    if (sj > ls[KL - 1]) pf_insert_later<KL>(ls, lp, sj, k0 + pf_row((int)j, hf));
+                }
+            }
         }
     }
 }
