@@ -178,3 +178,30 @@ def test_prefill_32k_sampled_rows(mode):
     assert ((wt >= 0) & (wt <= (1 if mode == ckv.CKV_MODE_PER_HEAD else 4) + 1e-5)).all()
     assert (np.diff(np.where(valid, wt, -1.0), axis=2) <= 1e-7).all()  # rank order
     PY.log(f"  32K mode={mode}: graphs {graphs_all}, near ties {stats['near']}")
+
+
+@pytest.mark.parametrize("mode", [ckv.CKV_MODE_PER_HEAD, ckv.CKV_MODE_QUERY_GROUP])
+def test_prefill_128k_bench_configuration_sampled_rows(mode):
+    # the benchmark's prefill leg as it runs: the 128K layer loaded by the
+    # runner, queries drawn on the device, every graph computed; sampled rows
+    # of sampled graphs against the oracle
+    from community_kv_retrieval_amd import runner
+    w = synth.preset("llama31_8b_128k")
+    slices = synth.gen_layer(w, 1)
+    layer = runner.load_layer(w, 1, extra=1, slices=slices)
+    n = int(slices[0][0].part.labels.shape[0])
+    q = synth.gen_prefill_queries_device(w, 1, 0, 0, [slices[0][kh].part for kh in range(w.n_kv_heads)])
+    PY.log(f"prefill 128K bench configuration mode={mode}")
+    e, wt = _run(layer.kv, mode, 0, q, w.n_sinks, w.kappa, w.sm_scale)
+    rng = np.random.default_rng(9)
+    rows = sorted(set([4, 5, 63, 64, 65536, n - 1] + rng.integers(0, n, size=8).tolist()))
+    qh_all = q[rows].float().cpu().numpy().astype(np.float64)
+    graphs = [0, 17, 31] if mode == ckv.CKV_MODE_PER_HEAD else [0, 6]
+    stats = {"near": 0}
+    for g in graphs:
+        keys = slices[0][_kv_head(w, mode, g)].k.float().numpy().astype(np.float64)
+        qh = qh_all[:, _heads(w, mode, g)]
+        re_, rw = O.prefill_edges_rows(qh, rows, keys, w.n_sinks, w.kappa, w.sm_scale)
+        _check_rows(e[g][rows], wt[g][rows], re_, rw, rows, qh, keys, w.n_sinks, w.sm_scale,
+                    f"128K mode={mode} g={g}", stats)
+    PY.log(f"  128K mode={mode}: near ties {stats['near']}")
