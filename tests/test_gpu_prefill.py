@@ -205,3 +205,33 @@ def test_prefill_128k_bench_configuration_sampled_rows(mode):
         _check_rows(e[g][rows], wt[g][rows], re_, rw, rows, qh, keys, w.n_sinks, w.sm_scale,
                     f"128K mode={mode} g={g}", stats)
     PY.log(f"  128K mode={mode}: near ties {stats['near']}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (16, 2)])
+def test_prefill_per_head_group_sizes(hq, hkv):
+    # one, two and eight query heads per kv head: blocks then hold four query
+    # tiles of one head, two tiles of two heads, or half a group
+    w = _small(n_q_heads=hq, n_kv_heads=hkv, n_ctx=777)
+    kv, slices, lens = _layer(w, 47)
+    q = synth.gen_prefill_queries(w, 47, 0, 1, slices[1])
+    PY.log(f"prefill per head {hq}/{hkv}")
+    _compare_all(w, kv, slices, 1, q, ckv.CKV_MODE_PER_HEAD, w.n_sinks, 8, w.sm_scale)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4)])
+def test_prefill_group_sizes(hq, hkv):
+    w = _small(n_q_heads=hq, n_kv_heads=hkv, n_ctx=650)
+    kv, slices, lens = _layer(w, 48)
+    q = synth.gen_prefill_queries(w, 48, 0, 0, slices[0])
+    PY.log(f"prefill group {hq}/{hkv}")
+    _compare_all(w, kv, slices, 0, q, ckv.CKV_MODE_QUERY_GROUP, w.n_sinks, 8, w.sm_scale)
+
+
+def test_prefill_group_of_eight_is_unsupported():
+    w = _small(n_q_heads=16, n_kv_heads=2, n_ctx=100)
+    kv, slices, lens = _layer(w, 49)
+    q = synth.gen_prefill_queries(w, 49, 0, 0, slices[0]).cuda()
+    edges = torch.empty((2, 100, 8), dtype=torch.int32, device="cuda")
+    ws = ckv.prefill_workspace(kv, ckv.CKV_MODE_QUERY_GROUP, 100)
+    with pytest.raises(ckv.CkvError):
+        ckv.ckv_prefill_topk(kv, ckv.CKV_MODE_QUERY_GROUP, 0, q, 4, 8, 1.0, edges, None, ws)
