@@ -275,7 +275,8 @@ def main():
 
     prefill = None
     if not args.no_prefill:
-        prefill = bench_prefill(w, args.seed, kv, slices)
+        prefill = bench_prefill(w, args.seed, kv, slices,
+                                cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 2)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -331,7 +332,7 @@ def main():
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def bench_prefill(w, seed, kv, slices, reps=3):
+def bench_prefill(w, seed, kv, slices, reps=3, cpu_seconds=0.0):
     """Prefill graph construction (top-kappa edges per query, matrix cores) of
     the first sequence's whole prompt: per head with weights, per head
     without, and per query group.  Algorithmic work: n(n+1)/2 causal pairs x
@@ -376,6 +377,8 @@ def bench_prefill(w, seed, kv, slices, reps=3):
         out[name] = {"ms_per_layer": round(t, 3), "tflops": round(tf, 1),
                      "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
         del edges, weights, ws
+    if cpu_seconds > 0:
+        out["cpu_baseline"] = prefill_cpu_baseline(w, q, slices, cpu_seconds)
     out["roofline"] = {"bound": "mfma", "kernel": "prefill_topk (per head, weights)",
                        "achieved": out["per_head"]["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": out["per_head"]["frac_of_bf16_mfma_peak"], "traffic": None}
@@ -570,6 +573,51 @@ def cpu_baseline(w, seed, slices, steps_in, seconds):
     return {"value": round(n / t_used, 3), "unit": "decode steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {n} decode steps of the same workload, all {w.n_graphs} graphs, float64 numpy "
                       f"({t_used:.1f}s of CPU time; setup not timed)"}
+
+
+def prefill_cpu_baseline(w, q, slices, seconds):
+    """The CPU oracle's prefill graph (prefill_edges_rows, float64 numpy) on a
+    random sample of (position, query head) rows of the same prompt, timed and
+    extrapolated to the whole layer by the number of query-key pairs."""
+    import numpy as np
+
+    from oracle import ckv_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    n = q.shape[0]
+    G = w.n_q_heads // w.n_kv_heads
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.integers(0, n, size=256))
+    qh = q[torch_index(rows)].float().cpu().numpy().astype(np.float64)  # [R][Hq][d]
+    t_used, pairs, done = 0.0, 0, 0
+    for kh in range(w.n_kv_heads):
+        keys = slices[0][kh].k.float().numpy().astype(np.float64)
+        for h in range(kh * G, (kh + 1) * G):
+            for r, i in enumerate(rows):
+                t0 = time.perf_counter()
+                O.prefill_edges_rows(qh[r:r + 1, h:h + 1], [int(i)], keys, w.n_sinks, w.kappa, w.sm_scale)
+                t_used += time.perf_counter() - t0
+                pairs += int(i) + 1
+                done += 1
+                if t_used >= seconds:
+                    break
+            if t_used >= seconds:
+                break
+        if t_used >= seconds:
+            break
+    total_pairs = n * (n + 1) / 2 * w.n_q_heads
+    return {"value": round(t_used * total_pairs / pairs, 1), "unit": "s per layer (extrapolated)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} random (position, query head) rows of the {n}-token prompt, float64 numpy "
+                      f"({t_used:.1f}s of CPU time), scaled by query-key pairs to all {w.n_q_heads} heads"}
+
+
+def torch_index(rows):
+    import torch
+    return torch.as_tensor(rows, dtype=torch.long, device="cuda")
 
 
 if __name__ == "__main__":
