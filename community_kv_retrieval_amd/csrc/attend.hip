@@ -349,7 +349,7 @@ typedef float f32x4v_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
 template <int D>
-__global__ __launch_bounds__(256) void attend_group4_kernel(AttendParams a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void attend_group4_kernel(AttendParams a) {
     constexpr int NH = 4;
     constexpr int PER_BLOCK = kGatherTokens;
     constexpr int KS = D / 32;             // k-slices of one 16-token MFMA tile
@@ -371,6 +371,7 @@ __global__ __launch_bounds__(256) void attend_group4_kernel(AttendParams a) {
     const int chunk = blockIdx.x / a.units;
     const int lunit = blockIdx.x - chunk * a.units;
     const int unit = a.g0 + lunit;
+    CKV_BMARK(0);
     const GraphCoords gc = graph_coords(unit, a.mode, a.Hq, a.Hkv);
     const int b = gc.b, kh = gc.kh, qh0 = gc.qh0;
     const int start = chunk * PER_BLOCK;
@@ -404,6 +405,7 @@ __global__ __launch_bounds__(256) void attend_group4_kernel(AttendParams a) {
         qb[s] = l16 < NH ? v : bf16x8v_t{};
     }
     __syncthreads();
+    CKV_BMARK(1);
 
     float m[NH], l[NH], acc[NH][E];
 #pragma unroll
@@ -496,6 +498,7 @@ __global__ __launch_bounds__(256) void attend_group4_kernel(AttendParams a) {
         }
         __builtin_amdgcn_wave_barrier();  // the next batch overwrites s_p only after every lane read it
     }
+    CKV_BMARK(2);
     // The wave's four token rows share (m, l): their accumulators add.
 #pragma unroll
     for (int h = 0; h < NH; ++h)

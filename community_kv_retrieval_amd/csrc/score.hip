@@ -46,46 +46,52 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     const int g = p.g0 + blockIdx.y, c0 = blockIdx.x * kScoreTile;
     CKV_TMARK(0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nc = min(p.n_comm[g], p.c_cap);
-    float *out = p.scores + (size_t)g * p.c_cap;
-    if (c0 >= nc) {  // the whole tile is unused
-        for (int i = tid; i < kScoreTile; i += 256)
-            if (c0 + i < p.c_cap) out[c0 + i] = kNegInf;
-        return;
-    }
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
-    if (tid < D) {
-        const T *q = reinterpret_cast<const T *>(p.q) + ((size_t)gc.b * p.Hq + gc.qh0) * D + tid;
-        double s = 0.0;
-        for (int h = 0; h < gc.nh; ++h) s += (double)to_f32(q[(size_t)h * D]);
-        s_q[tid] = (float)s;
+    // Every load of the block is issued before any is waited for, the query
+    // first (it is needed first): one round trip instead of three.  c_cap %
+    // 256 == 0, so every tile is whole and inside the table; a tile past the
+    // graph's community count is read and then scored -inf like any unused id.
+    // Query: the graph's heads (at most 8), loaded unconditionally at clamped
+    // addresses so that no load waits for another.
+    constexpr int kMaxHeads = 8;
+    T qv[kMaxHeads];
+    {
+        const T *q = reinterpret_cast<const T *>(p.q) + ((size_t)gc.b * p.Hq + gc.qh0) * D + min(tid, D - 1);
+#pragma unroll
+        for (int h = 0; h < kMaxHeads; ++h) qv[h] = q[(size_t)min(h, gc.nh - 1) * D];
     }
-    __syncthreads();
-
-    // c_cap % 256 == 0: every tile is whole.
     constexpr int DW = D / 4;
-    const int16_t *base = p.cq + (size_t)g * D * p.c_cap + c0 + 4 * lane;
+    const int16_t *base = p.cq + ((size_t)g * D + wave * DW) * p.c_cap + c0 + 4 * lane;
+    int2 v[DW];
+#pragma unroll
+    for (int j = 0; j < DW; ++j) v[j] = *reinterpret_cast<const int2 *>(base + (size_t)j * p.c_cap);
+    const int c = c0 + tid;  // kScoreTile == blockDim: one output per thread
+    const int sz = p.size[(size_t)g * p.c_cap + c];
+    const float scl = p.cscale[(size_t)g * p.c_cap + c];
+    const int nc = min(p.n_comm[g], p.c_cap);
+    if (tid < D) {  // the head sum in float64, heads in order
+        double qs = 0.0;
+#pragma unroll
+        for (int h = 0; h < kMaxHeads; ++h)
+            if (h < gc.nh) qs += (double)to_f32(qv[h]);
+        s_q[tid] = (float)qs;
+    }
+    lds_barrier();
+
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
+#pragma unroll
     for (int j = 0; j < DW; ++j) {
-        const int d = wave * DW + j;
-        const int2 v = *reinterpret_cast<const int2 *>(base + (size_t)d * p.c_cap);
-        const float qq = s_q[d];
-        acc[0] = fmaf(qq, lo16(v.x), acc[0]);
-        acc[1] = fmaf(qq, hi16(v.x), acc[1]);
-        acc[2] = fmaf(qq, lo16(v.y), acc[2]);
-        acc[3] = fmaf(qq, hi16(v.y), acc[3]);
+        const float qq = s_q[wave * DW + j];
+        acc[0] = fmaf(qq, lo16(v[j].x), acc[0]);
+        acc[1] = fmaf(qq, hi16(v[j].x), acc[1]);
+        acc[2] = fmaf(qq, lo16(v[j].y), acc[2]);
+        acc[3] = fmaf(qq, hi16(v[j].y), acc[3]);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) s_part[wave][4 * lane + k] = acc[k];
-    __syncthreads();
-    for (int i = tid; i < kScoreTile; i += 256) {
-        const int c = c0 + i;
-        if (c >= p.c_cap) break;
-        const float sum = ((s_part[0][i] + s_part[1][i]) + s_part[2][i]) + s_part[3][i];
-        const bool ok = c < nc && p.size[(size_t)g * p.c_cap + c] > 0;
-        out[c] = ok ? p.cscale[(size_t)g * p.c_cap + c] * sum : kNegInf;
-    }
+    lds_barrier();
+    const float sum = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
+    p.scores[(size_t)g * p.c_cap + c] = (c < nc && sz > 0) ? scl * sum : kNegInf;
     CKV_TMARK(1);
 }
 

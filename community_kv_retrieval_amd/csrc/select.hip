@@ -931,22 +931,25 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     __syncthreads();
     CKV_TMARK(14);
     if (lds_copy) {
-        // Slot j belongs to the last taken community whose first slot is <= j.
+        // Slot j belongs to the last taken community whose first slot is <= j
+        // (spref ascends from spref[0] = 0): found by binary lifting, the same
+        // power-of-two steps for every slot, so the four searches of a thread
+        // run side by side instead of one after another.
+        const int top_step = nsel > 1 ? 1 << (31 - __builtin_clz(nsel - 1)) : 0;  // uniform
         for (int j0 = 0; j0 < ntok; j0 += 4 * kSelThreads) {
-            int val[4];
+            int val[4], at[4] = {0, 0, 0, 0};
+            for (int step = top_step; step > 0; step >>= 1) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j = j0 + u * kSelThreads + tid;
+                    const int nx = at[u] + step;
+                    if (nx < nsel && sh.u.cp.spref[nx] <= j) at[u] = nx;
+                }
+            }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int j = j0 + u * kSelThreads + tid;
-                val[u] = 0;
-                if (j < ntok) {
-                    int a = 0, b = nsel - 1;
-                    while (a < b) {
-                        const int mid = (a + b + 1) >> 1;
-                        if (sh.u.cp.spref[mid] <= j) a = mid;
-                        else b = mid - 1;
-                    }
-                    val[u] = toks[sh.u.cp.soff[a] + (j - sh.u.cp.spref[a])];
-                }
+                val[u] = j < ntok ? toks[sh.u.cp.soff[at[u]] + (j - sh.u.cp.spref[at[u]])] : 0;
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {

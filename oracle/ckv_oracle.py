@@ -149,10 +149,15 @@ def attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: 
 
     Returns (out [h][d], probs [h][T], logits [h][T]) with
     logits = sm_scale * q . k, probs = softmax(logits) per head, out = probs @ V.
+    With no token at all (no sinks and no community within the budget, a case
+    the page never meets) the output is the empty sum, zero (reading R23).
     """
     q = np.asarray(q_heads, dtype=np.float64).reshape(-1, np.shape(q_heads)[-1])
     K = np.asarray(keys, dtype=np.float64)
     V = np.asarray(values, dtype=np.float64)
+    if K.shape[0] == 0:
+        empty = np.zeros((q.shape[0], 0))
+        return np.zeros((q.shape[0], V.shape[-1])), empty, empty
     z = float(sm_scale) * (q @ K.T)
     m = z.max(axis=1, keepdims=True)
     e = np.exp(z - m)
@@ -200,7 +205,7 @@ def edge_weights(probs: np.ndarray) -> np.ndarray:
     graphs: the sum of the group's per-head probabilities (reading: the group
     graph's edge weight is the summed attention of its heads).
     """
-    return np.asarray(probs, dtype=np.float64).reshape(-1, np.shape(probs)[-1]).sum(axis=0)
+    return np.atleast_2d(np.asarray(probs, dtype=np.float64)).sum(axis=0)
 
 
 def top_kappa(weights: np.ndarray, positions: np.ndarray, kappa: int, n_sinks: int) -> np.ndarray:

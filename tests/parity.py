@@ -140,6 +140,16 @@ def _edges_ok(r: O.GraphStep, gpu_edges, stats: Stats, where: str) -> bool:
     return False
 
 
+def _check_logits(H, g, tl, r, where):
+    slot = {int(p): i for i, p in enumerate(tl)}
+    idxs = np.array([slot[int(p)] for p in r.positions])
+    gl = H["logits"][g][:, idxs]
+    assert np.abs(gl - r.logits).max() <= LOGIT_ATOL * max(1.0, np.abs(r.logits).max()), f"{where}: logits"
+    np.testing.assert_allclose(H["ml"][g][:, 0], r.logits.max(axis=1), atol=LOGIT_ATOL * 20)
+    lsum = np.exp(r.logits - r.logits.max(axis=1, keepdims=True)).sum(axis=1)
+    np.testing.assert_allclose(H["ml"][g][:, 1], lsum, rtol=1e-4)
+
+
 def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None,
               check_state_every: int = 1, layer_kw: Optional[dict] = None, check_dense: bool = False,
               pair=None, windows: int = 1, defer: bool = True) -> Stats:
@@ -199,15 +209,11 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
                 if r.positions.size == orc.len[st.b]:  # every cached token attended: sparse == dense
                     assert np.all(np.abs(gout - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: sparse vs dense"
                     stats.dense_equal += 1
-            # logits of every slot, and the softmax state
-            slot = {int(p): i for i, p in enumerate(tl)}
-            idxs = np.array([slot[int(p)] for p in r.positions])
-            gl = H["logits"][g][:, idxs]
-            assert np.abs(gl - r.logits).max() <= LOGIT_ATOL * max(1.0, np.abs(r.logits).max()), \
-                f"{where}: logits"
-            np.testing.assert_allclose(H["ml"][g][:, 0], r.logits.max(axis=1), atol=LOGIT_ATOL * 20)
-            lsum = np.exp(r.logits - r.logits.max(axis=1, keepdims=True)).sum(axis=1)
-            np.testing.assert_allclose(H["ml"][g][:, 1], lsum, rtol=1e-4)
+            # logits of every slot, and the softmax state (empty: max -inf, sum 0)
+            if r.positions.size == 0:
+                assert np.all(H["ml"][g][:, 0] == -np.inf) and np.all(H["ml"][g][:, 1] == 0), f"{where}: empty ml"
+            else:
+                _check_logits(H, g, tl, r, where)
             ge = H["edges"][g]
             ne = int((ge >= 0).sum())
             assert (ge[ne:] == -1).all()

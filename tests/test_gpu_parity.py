@@ -246,19 +246,25 @@ def test_windowed_equals_one_window():
             assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("case", ["per_head", "group", "per_head_mid", "per_head_long", "group_windows"])
+@pytest.mark.parametrize("case", ["per_head", "group", "per_head_mid", "per_head_long", "group_windows",
+                                  "per_head_windows", "tiny_f32", "per_head_empty"])
 def test_deferred_combine_equals_complete(case):
     """A gather whose combine runs in the assign kernel gives the same bits as
     a complete gather followed by the assign: outputs, softmax state, edges,
     assignments and the whole index.  The mid case has more spans per graph
-    than a wave has lanes, the long case more than the combine stages in LDS
-    (256 spans of 256 tokens)."""
+    than the assign preloads (and than a wave has lanes), the long case more
+    than the combine stages in LDS (256 spans of 256 tokens); the empty case
+    attends nothing (no sinks, no community fits the budget)."""
     if case.startswith("group"):
         w = small_group(batch=2, n_ctx=6000, min_ctx=2000, steps=5)
     elif case == "per_head_mid":
         w = small_per_head(n_ctx=24000, budget=20000, n_kv_heads=2, n_q_heads=4, steps=3)
     elif case == "per_head_long":
         w = small_per_head(n_ctx=80000, budget=70000, n_kv_heads=1, n_q_heads=2, steps=2)
+    elif case == "tiny_f32":
+        w = synth.preset("tiny").replace(steps=6)
+    elif case == "per_head_empty":
+        w = small_per_head(n_ctx=3000, n_sinks=0, budget=1, min_size=2, steps=3)
     else:
         w = small_per_head(n_ctx=7000, steps=5)
     windows = 3 if case.endswith("windows") else 1
@@ -284,8 +290,18 @@ def test_deferred_combine_equals_complete(case):
         assert int(n.max()) > 64 * 256
     if case == "per_head_long":
         assert int(n.max()) > 256 * 256, "the long case must exceed the staged span count"
+    if case == "per_head_empty":
+        assert int(n.max()) == 0
     for x, y in zip(*runs):
         assert torch.equal(x, y)
+
+
+def test_nothing_attended():
+    """No sinks and no community small enough for the budget: every token list
+    is empty; the output is zero and each new token joins the best community."""
+    w = small_per_head(n_ctx=3000, n_sinks=0, budget=1, min_size=2, steps=3)
+    PY.log("empty token lists")
+    PY.run_steps(w, 31, w.steps)
 
 
 def test_dense_baseline_matches_oracle():

@@ -224,6 +224,17 @@ def test_attend_two_tokens_closed_form():
     np.testing.assert_allclose(out[0], p0 * V[0] + (1 - p0) * V[1], rtol=1e-14)
 
 
+def test_attend_empty_set_is_the_empty_sum():
+    """Nothing attended: the output is the empty sum (zero), there is no edge,
+    and the vote falls back (R13/R23)."""
+    q = np.array([[0.7, -1.3, 0.2], [1.0, 0.0, -0.5]])
+    out, p, z = O.attend(q, np.zeros((0, 3)), np.zeros((0, 5)), 0.5)
+    assert out.shape == (2, 5) and not out.any()
+    assert p.shape == (2, 0) and z.shape == (2, 0)
+    assert O.top_kappa(O.edge_weights(p), np.zeros(0, dtype=np.int64), 8, 0).size == 0
+    assert O.majority_vote([]) == -1
+
+
 def test_attend_matches_torch_sdpa_float64():
     r = np.random.default_rng(7)
     q = r.standard_normal((4, 64))
