@@ -490,17 +490,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         tcomm[j] = in ? p.tail_comm[(size_t)g * p.tail_cap + i] : -1;
         tpos[j] = in ? p.tail_pos[(size_t)g * p.tail_cap + i] : 0;
     }
-    // The graph's query: its head's q, or the sum of its group's q (exact in float64).
-    if (tid < p.D) {
-        double a = 0.0;
-        const size_t q0 = ((size_t)gc.b * p.Hq + gc.qh0) * p.D + tid;
-        for (int h = 0; h < gc.nh; ++h) {
-            const size_t qi = q0 + (size_t)h * p.D;
-            a += p.bf16 ? (double)to_f32(reinterpret_cast<const bf16_t *>(p.q)[qi])
-                        : (double)reinterpret_cast<const float *>(p.q)[qi];
+    // The graph's query: its head's q, or the sum of its group's q (exact in
+    // float64).  The (at most 8) heads are loaded unconditionally at clamped
+    // addresses, so they share the round trip of the loads above.
+    {
+        constexpr int kMaxHeads = 8;
+        float qv[kMaxHeads];
+        const size_t q0 = ((size_t)gc.b * p.Hq + gc.qh0) * p.D + min(tid, p.D - 1);
+        if (p.bf16) {
+            const bf16_t *qb = reinterpret_cast<const bf16_t *>(p.q) + q0;
+#pragma unroll
+            for (int h = 0; h < kMaxHeads; ++h) qv[h] = to_f32(qb[(size_t)min(h, gc.nh - 1) * p.D]);
+        } else {
+            const float *qf = reinterpret_cast<const float *>(p.q) + q0;
+#pragma unroll
+            for (int h = 0; h < kMaxHeads; ++h) qv[h] = qf[(size_t)min(h, gc.nh - 1) * p.D];
         }
-        sh.qbar[tid] = a;
-        sh.qabs[tid] = fabsf((float)a);
+        if (tid < p.D) {
+            double a = 0.0;
+#pragma unroll
+            for (int h = 0; h < kMaxHeads; ++h)
+                if (h < gc.nh) a += (double)qv[h];
+            sh.qbar[tid] = a;
+            sh.qabs[tid] = fabsf((float)a);
+        }
     }
 
     // LDS state the cuts start from, cleared under the first barrier below.
