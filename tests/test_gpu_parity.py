@@ -88,6 +88,21 @@ def test_community_cap():
     PY.run_steps(w, 8, w.steps)
 
 
+def test_max_community_capacity():
+    """c_cap at its maximum (16384) over about 550 communities: the selection's
+    four-slab path, and scoring tiles that lie wholly past the community count."""
+    w = small_per_head(n_ctx=9000, steps=3)
+    PY.log("c_cap 16384")
+    PY.run_steps(w, 33, w.steps, layer_kw={"c_cap": ckv.CKV_MAX_C_CAP})
+
+
+def test_largest_kappa():
+    """kappa at its maximum (32) with a budget of many communities."""
+    w = small_per_head(n_ctx=9000, budget=1500, kappa=32, steps=4)
+    PY.log("kappa 32")
+    PY.run_steps(w, 34, w.steps)
+
+
 @pytest.mark.parametrize("dtype,d", [("f32", 128), ("bf16", 64), ("f32", 64)])
 def test_dtypes_and_head_dims(dtype, d):
     w = small_group(dtype=dtype, head_dim=d, key_scale=1.0 / np.sqrt(d), batch=2, n_ctx=3000, min_ctx=0, steps=3)
