@@ -32,7 +32,7 @@ struct ScoreParams {
     const int32_t *size;
     const int32_t *n_comm;
     float *scores;
-    int mode, Hq, Hkv, c_cap, g0;
+    int mode, Hq, Hkv, c_cap, g0, count;  // count: graphs in the launch window
 };
 
 // Signed 16-bit halves of a 32-bit word.
@@ -43,7 +43,13 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     __shared__ float s_q[D];
     __shared__ float s_part[4][kScoreTile];
-    const int g = p.g0 + blockIdx.y, c0 = blockIdx.x * kScoreTile;
+    // Tile-major order: tile t of every graph of the window, then tile t + 1.
+    // Workgroups go round-robin over the eight XCDs, so with a graph count
+    // divisible by 8 all tiles of graph g run on the XCD that the selection
+    // block of g (block g of its launch) runs on, and the scores, sizes and
+    // scales it reads next are in that XCD's L2.
+    const int tile = blockIdx.x / p.count, lg = blockIdx.x - tile * p.count;
+    const int g = p.g0 + lg, c0 = tile * kScoreTile;
     CKV_TMARK(0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
@@ -99,8 +105,8 @@ hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, f
                         hipStream_t s) {
     const Window w = window_of(idx);
     ScoreParams p{q, idx->cq, idx->cscale, idx->size, idx->n_comm, scores, idx->mode, kv->n_q_heads,
-                  kv->n_kv_heads, idx->c_cap, w.first};
-    const dim3 grid(ceil_div(idx->c_cap, kScoreTile), w.count);
+                  kv->n_kv_heads, idx->c_cap, w.first, w.count};
+    const dim3 grid(ceil_div(idx->c_cap, kScoreTile) * w.count);
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
     if (kv->head_dim == 128) {
         if (bf) CKV_LAUNCH((score_kernel<bf16_t, 128>), grid, dim3(256), s, p);
