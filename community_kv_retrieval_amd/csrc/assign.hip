@@ -14,8 +14,9 @@
 // takes the majority label of the edges (lowest id on ties), then the block
 // appends the token to that community: label, tail entry, member count, the
 // exact float64 key sum and the float32 centroid column.  Graphs that own the
-// kv head store the new key and value; the last block to finish advances every
-// sequence length.
+// kv head store the new key and value.  Each block counts itself in as soon as
+// it has read its sequence length; the last to count in advances every
+// sequence length at its end.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 #include "combine.h"
@@ -69,6 +70,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // accumulators are loaded with the first round trip (DeferRegs), otherwise
 // when they are combined (Defer).
 enum AssignMode { kAssignComplete = 0, kAssignDeferRegs = 1, kAssignDefer = 2 };
+constexpr int kLenLds = 64;  // sequences whose lengths the first round trip reads
 constexpr int kPreChunks = 20;
 
 template <typename T, int D, int NH, int MODE>
@@ -81,6 +83,8 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     __shared__ int s_elab[CKV_MAX_KAPPA];
     __shared__ float s_max[4];
     __shared__ CombineLds<NH> s_comb;
+    __shared__ int s_P;                      // the graph's sequence length (position of the new token)
+    __shared__ int s_len[kLenLds];           // every sequence's length, for the advance at the end
     constexpr int PS = part_stride(D);
 
     const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,7 +98,13 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     // for the token count (the list and the logits are t_cap long; entries at
     // or past tok_n are masked afterwards).
     const int n = p.tok_n[g];
-    const int P = p.seq_len[gc.b];
+    // Sequence lengths: wave 0 only (the others take P from LDS below).
+    const bool few = p.B <= kLenLds;  // uniform
+    int P0 = 0, len_l = 0;
+    if (wave == 0) {
+        P0 = p.seq_len[gc.b];
+        if (few) len_l = p.seq_len[min(lane, p.B - 1)];
+    }
     const int tn = p.tail_len[g];
     const int topc = p.top[g];
     float M[NH], Linv[NH];
@@ -143,8 +153,22 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         combine_stage<NH, D, PS, false>(PR, p.nchunk, nact, s_comb);
     }
 
+    // The block counts itself in as soon as wave 0 holds the lengths (the
+    // asm takes them as inputs, so their loads have returned, and no memory
+    // access moves across it): every thread takes P from LDS, so once every
+    // block of the step has counted in, every read of seq_len is done and the
+    // last block may advance the lengths, at its end, without a round trip
+    // there.
+    bool last = false;
+    if (wave == 0) {
+        asm volatile("" ::"v"(P0), "v"(len_l) : "memory");
+        if (few && lane < p.B) s_len[lane] = len_l;
+        if (tid == 0) {
+            s_P = P0;
+            last = arrive_last(p.ctr, p.G);
+        }
+    }
     const int cap = min(p.l_cap, p.max_pages << p.ps_log2);
-    const bool room = P < cap;
     const bool owner = p.mode == CKV_MODE_QUERY_GROUP || (gc.qh0 % (p.Hq / p.Hkv)) == 0;
     const T *kn = reinterpret_cast<const T *>(p.k_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
     const T *vn = reinterpret_cast<const T *>(p.v_new) + ((size_t)gc.b * p.Hkv + gc.kh) * D;
@@ -303,6 +327,8 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     }
     lds_barrier();
     const int ne = s_ne;
+    const int P = s_P;
+    const bool room = P < cap;
     CKV_TMARK(33);
 
     // Majority vote of the edges' labels, lowest id on ties: each edge counts
@@ -377,9 +403,8 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     }
     CKV_TMARK(35);
     // Every thread has read the member count above: only now may it change.
-    // The last block advances every sequence with room by one token.  Every
-    // block read seq_len before it counts itself in, so the increment cannot
-    // race a read; the next kernel sees it across the kernel boundary.
+    // The last block to count in advances every sequence with room by one
+    // token; the next kernel sees it across the kernel boundary.
     __syncthreads();
     if (join) {
         const float scale = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])) / kScreenMax;
@@ -388,9 +413,11 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     }
     if (tid == 0) {
         if (join) p.size[(size_t)g * p.c_cap + a] = newsize;
-        if (arrive_last(p.ctr, p.G)) {
-            for (int bb = 0; bb < p.B; ++bb)
-                if (p.seq_len[bb] < cap) p.seq_len[bb] += 1;
+        if (last) {
+            for (int bb = 0; bb < p.B; ++bb) {
+                const int L0 = few ? s_len[bb] : p.seq_len[bb];
+                if (L0 < cap) p.seq_len[bb] = L0 + 1;
+            }
             reset_counter(p.ctr);
         }
     }
