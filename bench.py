@@ -209,6 +209,7 @@ def main():
     gather_us = dt[:, 2]
     gather_gbps = float(gathered.sum() / (gather_us.sum() * 1e-6) / 1e9)
     score_gbps = float(score_bytes * K / (dt[:, 0].sum() * 1e-6) / 1e9)
+    ceiling = read_ceiling(w, kv, idx, buf, row_bytes, K)
 
     # Cold pass: a 512 MB write between steps evicts the 256 MB MALL; only the
     # step itself is timed.
@@ -308,7 +309,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gather_attend", "achieved": round(gather_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "bytes_per_launch": int(avg_gather),
-                     "avg_launch_us": round(float(gather_us.mean()), 2), "kernel_sources": src_hash},
+                     "avg_launch_us": round(float(gather_us.mean()), 2), "kernel_sources": src_hash,
+                     "read_ceiling_gbps": ceiling["gbps"],
+                     "frac_of_read_ceiling": round(gather_gbps / ceiling["gbps"], 4)},
+        "read_ceiling": ceiling,
         "score_roofline": {"bound": "hbm", "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": round(score_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": score_bytes,
                            "avg_launch_us": round(float(dt[:, 0].mean()), 2)},
@@ -534,6 +538,44 @@ def measured_traffic(workload, src_hash):
         return int(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_ceiling(w, kv, idx, buf, row_bytes, reps):
+    """The practical read rate of the gather's access pattern: ckv_read_rows
+    (the gather's loads, no arithmetic) over the rows the last step's token
+    lists name, timed with dispatch-stamped events like the gather."""
+    import numpy as np
+    import torch
+    from community_kv_retrieval_amd import ckv, synth
+    G, T = buf.tok_list.shape
+    gi = torch.arange(G, device="cuda")[:, None].expand(G, T)
+    mask = torch.arange(T, device="cuda")[None, :] < buf.tok_n[:, None]
+    pos, g = buf.tok_list[mask].long(), gi[mask]
+    if w.mode == synth.PER_HEAD:
+        b, kh = g // w.n_q_heads, (g % w.n_q_heads) // (w.n_q_heads // w.n_kv_heads)
+    else:
+        b, kh = g // w.n_kv_heads, g % w.n_kv_heads
+    ps = kv.page_size
+    page = kv.page_table[b, pos // ps].long()
+    rows = ((page * w.n_kv_heads + kh) * ps + pos % ps).to(torch.int32).contiguous()
+    n = rows.numel()
+    part = torch.zeros(((n + 255) // 256,), dtype=torch.int32, device="cuda")
+    for _ in range(5):
+        ckv.ckv_read_rows(kv, rows, part)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, c in ev:
+        a.record()
+        c.record()
+    torch.cuda.synchronize()
+    for a, c in ev:
+        ckv.ckv_time_next_launch(a, c)
+        ckv.ckv_read_rows(kv, rows, part)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(c) for a, c in ev]) * 1e3
+    gbps = n * row_bytes / (float(us.mean()) * 1e-6) / 1e9
+    return {"kernel": "read_rows", "rows": n, "bytes_per_launch": n * row_bytes,
+            "avg_launch_us": round(float(us.mean()), 2), "gbps": round(gbps, 1),
+            "frac_of_8tbps": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def copy_calibration():

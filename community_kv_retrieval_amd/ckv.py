@@ -31,7 +31,7 @@ CKV_MAX_KAPPA, CKV_MAX_C_CAP = 32, 16384
 
 EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_centroids",
            "ckv_select_communities", "ckv_gather_attend", "ckv_assign_update", "ckv_dense_attend",
-           "ckv_prefill_workspace_bytes", "ckv_prefill_topk",
+           "ckv_prefill_workspace_bytes", "ckv_prefill_topk", "ckv_read_rows",
            "ckv_time_next_launch", "ckv_status_str", "ckv_abi_version")
 
 
@@ -78,6 +78,7 @@ def _load():
         "ckv_prefill_workspace_bytes": (c_size_t, [KVP, c_int32, c_int32]),
         "ckv_prefill_topk": (c_int32, [KVP, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int32, c_float,
                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_read_rows": (c_int32, [KVP, c_void_p, c_int32, c_void_p, c_void_p]),
         "ckv_time_next_launch": (c_int32, [c_void_p, c_void_p]),
         "ckv_status_str": (ctypes.c_char_p, [c_int32]),
         "ckv_abi_version": (c_int32, []),
@@ -319,6 +320,15 @@ def ckv_dense_attend(kv: KVStore, q: torch.Tensor, sm_scale: float, out: torch.T
     _check("ckv_dense_attend", LIB.ckv_dense_attend(ctypes.byref(kv.desc), _ptr(q), float(sm_scale), _ptr(out),
                                                     _ptr(ml), _ptr(ws), ws.numel() * ws.element_size(),
                                                     _stream(stream)))
+
+
+def ckv_read_rows(kv: KVStore, rows: torch.Tensor, part: torch.Tensor, stream=None):
+    """The gather's loads over the given pool rows (a read-ceiling measurement);
+    part[ceil(n/256)] gets per-block XOR checksums of the rows' 32-bit words."""
+    n = rows.numel()
+    _need(rows, "rows", torch.int32, (n,))
+    _need(part, "part", torch.int32, ((n + 255) // 256,))
+    _check("ckv_read_rows", LIB.ckv_read_rows(ctypes.byref(kv.desc), _ptr(rows), n, _ptr(part), _stream(stream)))
 
 
 def ckv_time_next_launch(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]):

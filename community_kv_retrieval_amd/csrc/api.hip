@@ -64,7 +64,7 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 4; }
+int32_t ckv_abi_version(void) { return 5; }
 
 ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;
@@ -201,6 +201,15 @@ ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, flo
     if (!ws || ws_bytes < L.dense_total) return CKV_E_WORKSPACE;
     return hip_status(launch_dense(kv, q, sm_scale, out, ml, (float *)at(ws, L.part_dense),
                                    (int32_t *)at(ws, L.ctr_dense), (hipStream_t)stream));
+}
+
+ckv_status ckv_read_rows(const ckv_kv *kv, const uint32_t *rows, int32_t n, uint32_t *part, ckv_stream_t stream) {
+    ckv_status st = check_kv(kv);
+    if (st != CKV_OK) return st;
+    if (n < 0) return CKV_E_INVALID;
+    if (n == 0) return CKV_OK;  // nothing to read, nothing launched
+    if (!rows || !part) return CKV_E_INVALID;
+    return hip_status(launch_read_rows(kv, rows, n, part, (hipStream_t)stream));
 }
 
 size_t ckv_prefill_workspace_bytes(const ckv_kv *kv, int32_t mode, int32_t n) {

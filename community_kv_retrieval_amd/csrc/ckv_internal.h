@@ -123,6 +123,8 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
                          hipStream_t s);
 hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
                         float *part, int32_t *ctr, hipStream_t s);
+// Read-ceiling measurement: the gather's loads over given rows, XOR checksums.
+hipError_t launch_read_rows(const ckv_kv *kv, const uint32_t *rows, int n, uint32_t *part, hipStream_t s);
 // out != nullptr: the preceding gather was deferred; the assign kernel
 // combines its partial records (part) into out and, if not null, ml.
 hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,

@@ -269,10 +269,22 @@ ckv_status ckv_prefill_topk(const ckv_kv *kv, int32_t mode, int32_t b, const voi
                             int32_t n_sinks, int32_t kappa, float sm_scale, int32_t *edges, float *weights,
                             void *ws, size_t ws_bytes, ckv_stream_t stream);
 
+/* Read ceiling of the gather's access pattern, for measurement (no part of
+ * the method).  Reads the K|V rows rows[0..n) of the store (row id r: token
+ * slot r % page_size of kv head (r / page_size) % n_kv_heads of page
+ * r / (page_size * n_kv_heads), i.e. the record at kv + r * 2 * head_dim
+ * elements) with the gather's loads: 256 rows per block, 16 lanes per row.
+ * part[ceil(n / 256)] (device, uint32) receives, per block of 256 rows, the
+ * XOR of every 32-bit word of those rows, so a caller can check that all bytes
+ * were read.  Row ids at or past n_pages * n_kv_heads * page_size are clamped
+ * to the last row.  n == 0: nothing is launched.  Errors: CKV_E_INVALID for
+ * n < 0 or a NULL rows / part with n > 0. */
+ckv_status ckv_read_rows(const ckv_kv *kv, const uint32_t *rows, int32_t n, uint32_t *part, ckv_stream_t stream);
+
 /* Kernel timing for profiling harnesses (no part of the method).  Arms the
  * calling host thread so that the next kernel launched by one of
  * ckv_score_centroids, ckv_select_communities, ckv_gather_attend,
- * ckv_assign_update, ckv_dense_attend (each launches exactly one kernel) or
+ * ckv_assign_update, ckv_dense_attend, ckv_read_rows (each launches exactly one kernel) or
  * ckv_prefill_topk (one kernel per head; the query-group mode launches two and
  * the pair times the first) has `start` and `stop` recorded by its own dispatch (hipExtLaunchKernel):
  * hipEventElapsedTime(start, stop) is then that kernel's execution time, with

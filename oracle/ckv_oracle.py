@@ -234,7 +234,7 @@ def majority_vote(edge_labels: Sequence[int]) -> int:
 
 
 # --------------------------------------------------------------------------
-# Whole-step driver over many graphs
+# Whole-step loop over many graphs
 # --------------------------------------------------------------------------
 
 # --------------------------------------------------------------------------

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ckv.LIB.ckv_abi_version() == 4
+    assert ckv.LIB.ckv_abi_version() == 5
     for code in (0, -1, -2, -3, -4):
         assert ckv.ckv_status_str(code) != "unknown status"
     assert ckv.ckv_status_str(7) == "unknown status"
@@ -158,6 +158,15 @@ def test_gather_assign_dense_workspace_checks():
     assert a(8, FAKE, need - 1) == ckv.CKV_E_WORKSPACE
     d = ckv.LIB.ckv_dense_attend(ctypes.byref(kv), FAKE, 1.0, FAKE, None, FAKE, _ws(kv, None, 0) - 1, None)
     assert d == ckv.CKV_E_WORKSPACE
+
+
+def test_read_rows_validation():
+    kv = _kv()
+    f = lambda rows, n, part: ckv.LIB.ckv_read_rows(ctypes.byref(kv), rows, n, part, None)
+    assert f(FAKE, -1, FAKE) == ckv.CKV_E_INVALID
+    assert f(None, 4, FAKE) == ckv.CKV_E_INVALID
+    assert f(FAKE, 4, None) == ckv.CKV_E_INVALID
+    assert f(None, 0, None) == ckv.CKV_OK  # nothing to read, nothing launched
 
 
 def test_kv_write_and_build_validation():

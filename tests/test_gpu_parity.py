@@ -319,6 +319,27 @@ def test_nothing_attended():
     PY.run_steps(w, 31, w.steps)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_read_rows_checksum(dtype, d):
+    """The read-ceiling kernel reads every byte of the rows it is given: its
+    per-block XOR of the rows' 32-bit words equals the host's, including a
+    ragged last block and row ids past the store (clamped to its last row)."""
+    w = small_per_head(dtype=dtype, head_dim=d, key_scale=1.0 / np.sqrt(d), n_ctx=3000, steps=1)
+    PY.log(f"read rows {dtype} d={d}")
+    kv = runner.load_layer(w, 41, extra=2).kv
+    n_rows = kv.n_pages * kv.n_kv_heads * kv.page_size
+    n = 256 * 7 + 77
+    rows = torch.randint(0, n_rows, (n,), generator=torch.Generator().manual_seed(5), dtype=torch.int32)
+    rows[:3] = torch.tensor([n_rows - 1, n_rows + 5, 2**31 - 1], dtype=torch.int32)
+    part = torch.zeros(((n + 255) // 256,), dtype=torch.int32, device="cuda")
+    ckv.ckv_read_rows(kv, rows.cuda(), part)
+    torch.cuda.synchronize()
+    words = kv.kv.view(torch.int32).reshape(n_rows, -1).cpu().numpy()
+    r = np.minimum(rows.numpy().astype(np.int64), n_rows - 1)
+    ref = np.array([np.bitwise_xor.reduce(words[r[i:i + 256]].ravel()) for i in range(0, n, 256)], dtype=np.int32)
+    np.testing.assert_array_equal(part.cpu().numpy(), ref)
+
+
 def test_dense_baseline_matches_oracle():
     w = synth.preset("qwen3_8b_32k").replace(n_ctx=20000, batch=2, min_ctx=9000)
     PY.log("dense baseline")
