@@ -44,6 +44,30 @@ struct AttendParams {
     int units;      // units in the launch
 };
 
+// The 32-bit words of a row fragment (bf16: two elements each, low half first).
+template <int B>
+__device__ __forceinline__ void frag_words(const Frag<B> &f, uint32_t (&w)[B / 4]) {
+    if constexpr (B == 8) {
+        w[0] = f.w.x;
+        w[1] = f.w.y;
+    } else if constexpr (B == 16) {
+        w[0] = f.w.x;
+        w[1] = f.w.y;
+        w[2] = f.w.z;
+        w[3] = f.w.w;
+    } else {
+        w[0] = f.w0.x;
+        w[1] = f.w0.y;
+        w[2] = f.w0.z;
+        w[3] = f.w0.w;
+        w[4] = f.w1.x;
+        w[5] = f.w1.y;
+        w[6] = f.w1.z;
+        w[7] = f.w1.w;
+    }
+}
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
 template <typename T, int D, int NH>
 constexpr int pick_u() {
     return (NH >= 8 || RowSlice<T, D>::BYTES == 32) ? 4 : 8;
@@ -232,6 +256,16 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     for (int h = 0; h < NH; ++h)
 #pragma unroll
         for (int e = 0; e < E; ++e) qr[h][e] = s_q[h][l16 * E + e];
+    // bf16: q.k as packed dot products of element pairs (the products are
+    // exact in float32; the pairs' sums round once per pair).  The float32
+    // copy of a bf16 q repacks exactly.
+    constexpr bool kDot2 = std::is_same<T, bf16_t>::value;
+    uint32_t qpk[NH][E / 2];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int i = 0; i < E / 2; ++i)
+            qpk[h][i] = (__float_as_uint(qr[h][2 * i]) >> 16) | (__float_as_uint(qr[h][2 * i + 1]) & 0xFFFF0000u);
 
     float m[NH], l[NH], acc[NH][E];
 #pragma unroll
@@ -257,15 +291,24 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         float z[NH][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float k[E];
-            RS::to_float(kf[u], k);
             const int t = base + u * 16 + wave * 4 + ts;
             const bool valid = t < cnt;
+            float k[E];
+            uint32_t kw[RS::BYTES / 4];
+            if constexpr (kDot2) frag_words(kf[u], kw);
+            else RS::to_float(kf[u], k);
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 float d = 0.f;
+                if constexpr (kDot2) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) d = fmaf(qr[h][e], k[e], d);
+                    for (int i = 0; i < E / 2; ++i)
+                        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, kw[i]),
+                                                            __builtin_bit_cast(bf16x2v_t, qpk[h][i]), d, false);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) d = fmaf(qr[h][e], k[e], d);
+                }
                 d = row16_sum(d);
                 z[h][u] = valid ? d * a.sm_scale : kNegInf;
             }
