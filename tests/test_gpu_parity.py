@@ -88,6 +88,29 @@ def test_community_cap():
     PY.run_steps(w, 8, w.steps)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_random_configuration(seed):
+    """Seeded random mixes of the shape parameters, a few steps each against
+    the oracle: graph mode, storage dtype, head dim, batch with ragged lengths,
+    group size (one, two, four or eight heads per kv head), budget, kappa,
+    sinks, community sizes and page size."""
+    r = np.random.default_rng(1000 + seed)
+    mode = [synth.PER_HEAD, synth.GROUP][int(r.integers(2))]
+    dtype = ["bf16", "f32"][int(r.integers(2))]
+    d = [64, 128][int(r.integers(2))]
+    hkv, grp = int(r.choice([1, 2, 4])), int(r.choice([1, 2, 4, 8]))
+    batch, n_ctx = int(r.integers(1, 4)), int(r.integers(600, 5000))
+    w = synth.preset("qwen3_8b_32k").replace(
+        name=f"random{seed}", batch=batch, n_q_heads=hkv * grp, n_kv_heads=hkv, head_dim=d, dtype=dtype,
+        n_ctx=n_ctx, min_ctx=int(r.integers(0, n_ctx // 2)), n_sinks=int(r.integers(0, 9)), mode=mode,
+        budget=int(r.integers(1, n_ctx)), kappa=int(r.integers(1, 33)), key_scale=1.0 / np.sqrt(d),
+        mean_size=int(r.integers(4, 33)), min_size=1, max_size=64, steps=3)
+    page_size = int(r.choice([1, 4, 16, 64]))
+    PY.log(f"random {seed}: {mode} {dtype} d={d} batch={batch} kv_heads={hkv} group={grp} ctx={n_ctx} "
+           f"budget={w.budget} kappa={w.kappa} sinks={w.n_sinks} mean_size={w.mean_size} page={page_size}")
+    PY.run_steps(w, 50 + seed, w.steps, layer_kw={"page_size": page_size})
+
+
 def test_max_community_capacity():
     """c_cap at its maximum (16384) over about 550 communities: the selection's
     four-slab path, and scoring tiles that lie wholly past the community count."""
