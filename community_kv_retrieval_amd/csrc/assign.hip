@@ -75,7 +75,7 @@ constexpr int kPreChunks = 20;
 
 template <typename T, int D, int NH, int MODE>
 __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
-    constexpr int kIpt = NH >= 4 ? 18 : 24;  // candidates per thread held in registers (fewer with several heads)
+    constexpr int kIpt = 18;  // list entries per thread held in registers (4 608 per graph)
     __shared__ unsigned long long s_cand[64];
     __shared__ uint32_t s_tau[4];
     __shared__ int s_ncand, s_ne, s_a;
