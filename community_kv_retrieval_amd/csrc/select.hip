@@ -129,8 +129,14 @@ __device__ __forceinline__ float key_score(unsigned long long k) {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// Community id of element e (0 .. 4 NS - 1) of thread tid.
-__device__ __forceinline__ int slab_id(int tid, int e) { return (e >> 2) * kSlab + 4 * tid + (e & 3); }
+// Community of element e of thread tid: elements 0 .. 4 NS - 1 are four
+// consecutive communities in each slab of 4096 (slab e / 4); the elements
+// after them are single communities NS * 4096 + x * 1024 + tid (x = e - 4 NS),
+// which cover a capacity just past a whole number of slabs.
+template <int NS>
+__device__ __forceinline__ int slab_id(int tid, int e) {
+    return e < 4 * NS ? (e >> 2) * kSlab + 4 * tid + (e & 3) : NS * kSlab + (e - 4 * NS) * kSelThreads + tid;
+}
 
 // Block-wide exclusive prefix sums of NV ints per thread, in thread order, and
 // their totals.  One barrier: every wave scans the wave totals itself.
@@ -263,11 +269,11 @@ __device__ unsigned long long radix_cut(const unsigned long long (&key)[N], cons
 }
 
 // Keys of this thread's communities (0 for empty ones).
-template <int EPT>
+template <int NS, int EPT>
 __device__ __forceinline__ void comm_keys(const float (&sv)[EPT], const int (&w)[EPT],
                                           unsigned long long (&key)[EPT]) {
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) key[j] = w[j] > 0 ? comm_key(sv[j], slab_id(threadIdx.x, j)) : 0ull;
+    for (int j = 0; j < EPT; ++j) key[j] = w[j] > 0 ? comm_key(sv[j], slab_id<NS>(threadIdx.x, j)) : 0ull;
 }
 
 // Budget cut through equal-width score bins (see the file comment).  The bin
@@ -415,9 +421,10 @@ __device__ __forceinline__ void exact_scores(const SelectParams &p, int g, int n
     }
 }
 
-template <int NS, int D>
+template <int NS, int X, int D>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
-    constexpr int EPT = 4 * NS;
+    constexpr int EPT = 4 * NS + X;
+    constexpr int NGR = NS + X;  // id-ordered groups: the slabs, then the single columns
     __shared__ SelShared sh;
     const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     CKV_TMARK(10);
@@ -479,8 +486,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
             o0[4 * j + 3] = o4[j].w;
         }
     }
+    // The single columns past the slabs: one community each, 4-byte loads, and
+    // the next community's offset for the end of its base members.
+    int onx[X > 0 ? X : 1];
+#pragma unroll
+    for (int x = 0; x < X; ++x) {
+        const int c = NS * kSlab + x * kSelThreads + tid, e = 4 * NS + x;
+        const bool in = c < C;
+        const int sz_c = in ? sz[c] : 0;
+        sv[e] = in ? sc[c] : 0.f;
+        se[e] = in ? scl[c] : 0.f;
+        o0[e] = in ? offs[c] : 0;
+        onx[x] = in ? offs[c + 1] : 0;
+        s[e] = c < nc ? sz_c : 0;
+    }
     // end of the base members of element e: the next element's start
-    auto o1 = [&](int e) { return (e & 3) == 3 ? on[e >> 2] : o0[e + 1]; };
+    auto o1 = [&](int e) { return e >= 4 * NS ? onx[e - 4 * NS] : (e & 3) == 3 ? on[e >> 2] : o0[e + 1]; };
     const int tn = p.tail_len[g];
     int tcomm[kTailPerThread], tpos[kTailPerThread];
 #pragma unroll
@@ -648,7 +669,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 #pragma unroll
             for (int j = 0; j < EPT; ++j) {
                 if ((wantm >> j) & 1u) {
-                    sh.u.ls.id[i] = slab_id(tid, j) | (((bandm >> j) & 1u) ? (int)kBand : 0) |
+                    sh.u.ls.id[i] = slab_id<NS>(tid, j) | (((bandm >> j) & 1u) ? (int)kBand : 0) |
                                     (((tcm >> j) & 1u) ? (int)kTopCand : 0);
                     sh.u.ls.sz[i] = s[j];
                     ++i;
@@ -804,6 +825,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
                 if (4 * tid + k < kSlab && j * kSlab + 4 * tid + k < C) sv[e] = sh.u.exs[4 * tid + k];
             }
         }
+        if constexpr (X > 0) {
+            __syncthreads();
+            exact_scores<D>(p, g, max(0, min(X * kSelThreads, C - NS * kSlab)), sh, false, NS);
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < X; ++x)
+                if (NS * kSlab + x * kSelThreads + tid < C) sv[4 * NS + x] = sh.u.exs[x * kSelThreads + tid];
+        }
         // exact range and best community
         float elo = __builtin_huge_valf(), ehi = -__builtin_huge_valf();
 #pragma unroll
@@ -831,23 +860,23 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         unsigned long long bk = 0ull;
 #pragma unroll
         for (int j = 0; j < EPT; ++j)
-            if (s[j] > 0) bk = umax64(bk, comm_key(sv[j], slab_id(tid, j)));
+            if (s[j] > 0) bk = umax64(bk, comm_key(sv[j], slab_id<NS>(tid, j)));
         bk = wave_max_u64(bk);
         if (lane == 0 && bk) atomicMax(&sh.topkey, bk);
-        if (!value_cut<EPT>(sv, s, p.budget, elo, ehi, sh, thr, [&](int j) { return slab_id(tid, j); })) {
+        if (!value_cut<EPT>(sv, s, p.budget, elo, ehi, sh, thr, [&](int j) { return slab_id<NS>(tid, j); })) {
             unsigned long long keys[EPT];
-            comm_keys<EPT>(sv, s, keys);
+            comm_keys<NS, EPT>(sv, s, keys);
             thr = radix_cut<EPT>(keys, s, false, p.budget, sh);
         }
         if (p.max_comm > 0) {
             unsigned long long keys[EPT];
-            comm_keys<EPT>(sv, s, keys);
+            comm_keys<NS, EPT>(sv, s, keys);
             thr = umax64(thr, radix_cut<EPT>(keys, s, true, p.max_comm, sh));
         }
         cert = 0u;
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
-            const uint32_t u = ordered_bits(sv[j] == 0.f ? 0.f : sv[j]), c = (uint32_t)slab_id(tid, j);
+            const uint32_t u = ordered_bits(sv[j] == 0.f ? 0.f : sv[j]), c = (uint32_t)slab_id<NS>(tid, j);
             const uint32_t thr_u = (uint32_t)(thr >> 32), thr_id = 0xFFFFFFFFu - (uint32_t)thr;
             if (s[j] > 0 && (u > thr_u || (u == thr_u && c < thr_id))) cert |= 1u << j;
         }
@@ -860,7 +889,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         if (any && s[j] > 0 && ((cert >> j) & 1u)) {
-            const int c = slab_id(tid, j);
+            const int c = slab_id<NS>(tid, j);
             atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
         }
     }
@@ -868,42 +897,49 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
     bool taken[EPT];
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const int c = slab_id(tid, j);
+        const int c = slab_id<NS>(tid, j);
         taken[j] = any && s[j] > 0 && ((sh.bits[c >> 5] >> (c & 31)) & 1u);
     }
     CKV_TMARK(43);
     // Per slab: taken communities and their base members; then taken tail entries.
-    constexpr int NV = 2 * NS + 1;
+    constexpr int NV = 2 * NGR + 1;
+    static_assert(NV <= 9, "the scan scratch holds nine values per wave");
     int v[NV], ex[NV], tot[NV];
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         v[j] = 0;
-        v[NS + j] = 0;
+        v[NGR + j] = 0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             if (taken[4 * j + k]) {
                 v[j] += 1;
-                v[NS + j] += o1(4 * j + k) - o0[4 * j + k];
+                v[NGR + j] += o1(4 * j + k) - o0[4 * j + k];
             }
         }
     }
+#pragma unroll
+    for (int x = 0; x < X; ++x) {
+        const int e = 4 * NS + x;
+        v[NS + x] = taken[e] ? 1 : 0;
+        v[NGR + NS + x] = taken[e] ? o1(e) - o0[e] : 0;
+    }
     int f[kTailPerThread];
-    v[2 * NS] = 0;
+    v[2 * NGR] = 0;
 #pragma unroll
     for (int j = 0; j < kTailPerThread; ++j) {
         const int i = tid * kTailPerThread + j;
         const int c = tcomm[j];
         f[j] = (i < tn && c >= 0 && c < C && ((sh.bits[c >> 5] >> (c & 31)) & 1u)) ? 1 : 0;
-        v[2 * NS] += f[j];
+        v[2 * NGR] += f[j];
     }
     block_scan_multi<kSelThreads, NV>(v, ex, tot, sh.scan);
     int nsel = 0, ntok = 0;
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
+    for (int j = 0; j < NGR; ++j) {
         nsel += tot[j];
-        ntok += tot[NS + j];
+        ntok += tot[NGR + j];
     }
-    const int ntail = tot[2 * NS];
+    const int ntail = tot[2 * NGR];
     CKV_TMARK(13);
 
     const int32_t *toks = p.toks + (size_t)g * p.l_cap;
@@ -912,13 +948,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
         int kbase = 0, tbase = 0;
 #pragma unroll
         for (int j = 0; j < NS; ++j) {
-            int kpos = kbase + ex[j], rel = tbase + ex[NS + j];
+            int kpos = kbase + ex[j], rel = tbase + ex[NGR + j];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int e = 4 * j + k;
                 if (taken[e]) {
                     const int len = o1(e) - o0[e];
-                    p.sel[(size_t)g * C + kpos] = slab_id(tid, e);
+                    p.sel[(size_t)g * C + kpos] = slab_id<NS>(tid, e);
                     if (lds_copy) {
                         sh.u.cp.soff[kpos] = o0[e];
                         sh.u.cp.spref[kpos] = rel;
@@ -930,13 +966,29 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectParams p) {
                 }
             }
             kbase += tot[j];
-            tbase += tot[NS + j];
+            tbase += tot[NGR + j];
+        }
+#pragma unroll
+        for (int x = 0; x < X; ++x) {
+            const int e = 4 * NS + x;
+            if (taken[e]) {
+                const int kpos = kbase + ex[NS + x], rel = tbase + ex[NGR + NS + x], len = o1(e) - o0[e];
+                p.sel[(size_t)g * C + kpos] = slab_id<NS>(tid, e);
+                if (lds_copy) {
+                    sh.u.cp.soff[kpos] = o0[e];
+                    sh.u.cp.spref[kpos] = rel;
+                } else {
+                    for (int i = 0; i < len; ++i) tl[ns + rel + i] = toks[o0[e] + i];
+                }
+            }
+            kbase += tot[NS + x];
+            tbase += tot[NGR + NS + x];
         }
     }
     for (int i = tid; i < ns; i += kSelThreads) tl[i] = i;
     // Taken tail members, in tail order, after the base members.
     {
-        int tdst = ns + ntok + ex[2 * NS];
+        int tdst = ns + ntok + ex[2 * NGR];
 #pragma unroll
         for (int j = 0; j < kTailPerThread; ++j)
             if (f[j]) tl[tdst++] = tpos[j];
@@ -1017,15 +1069,21 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, 
     p.tok_n = tok_n;
     const Window w = window_of(idx);
     p.g0 = w.first;
-    const int ns = ceil_div(idx->c_cap, kSlab);
+    // Whole slabs of 4096, and one column of 1024 more when that covers the
+    // rest: 8448 communities take two slabs and a column, not three slabs.
+    const int full = idx->c_cap / kSlab, rest = idx->c_cap - full * kSlab;
+    const int ns = full >= 1 && rest > 0 && rest <= kSelThreads ? full : ceil_div(idx->c_cap, kSlab);
+    const int nx = ns < ceil_div(idx->c_cap, kSlab) ? 1 : 0;
     const dim3 grid(w.count), block(kSelThreads);
-#define CKV_SEL(N, DD)                                                   \
-    if (ns <= N && kv->head_dim == DD) {                                 \
-        CKV_LAUNCH((select_kernel<N, DD>), grid, block, s, p);           \
+#define CKV_SEL(N, XX, DD)                                               \
+    if (ns == N && nx == XX && kv->head_dim == DD) {                     \
+        CKV_LAUNCH((select_kernel<N, XX, DD>), grid, block, s, p);       \
         return hipGetLastError();                                        \
     }
-    CKV_SEL(1, 64) CKV_SEL(2, 64) CKV_SEL(3, 64) CKV_SEL(4, 64)
-    CKV_SEL(1, 128) CKV_SEL(2, 128) CKV_SEL(3, 128) CKV_SEL(4, 128)
+    CKV_SEL(1, 0, 64) CKV_SEL(2, 0, 64) CKV_SEL(3, 0, 64) CKV_SEL(4, 0, 64)
+    CKV_SEL(1, 1, 64) CKV_SEL(2, 1, 64) CKV_SEL(3, 1, 64)
+    CKV_SEL(1, 0, 128) CKV_SEL(2, 0, 128) CKV_SEL(3, 0, 128) CKV_SEL(4, 0, 128)
+    CKV_SEL(1, 1, 128) CKV_SEL(2, 1, 128) CKV_SEL(3, 1, 128)
 #undef CKV_SEL
     return hipGetLastError();
 }
