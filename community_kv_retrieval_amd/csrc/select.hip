@@ -4,7 +4,9 @@
 //
 // One 1024-thread block per graph.  The communities are read in slabs of 4096:
 // in slab j thread t owns communities 4096 j + 4 t .. 4096 j + 4 t + 3, so
-// every 16-byte load of a wave covers 1 KB of consecutive memory.
+// every 16-byte load of a wave covers 1 KB of consecutive memory.  A capacity
+// at most 1024 past whole slabs adds one column instead of a fourth-empty
+// slab: thread t also owns community 4096 NS + t (NS whole slabs).
 // Communities rank by their exact score (float32 of the float64 product of
 // the graph's query with the float32 centroid), higher first, ties to the
 // lower id; as one number that is the 64-bit key (order-preserving bits of the
@@ -33,9 +35,9 @@
 // token-weighted digit histograms, finds the same cut when that bin is
 // crowded, and the community cap is the same radix select with unit weights.
 //
-// Then one block scan over per-slab counts gives every taken community its
-// rank in ascending id order and its first slot in the token list, and every
-// taken tail entry its slot after them.  The list is written as sinks, the base
+// Then one block scan over per-slab (and per-column) counts gives every taken
+// community its rank in ascending id order and its first slot in the token
+// list, and every taken tail entry its slot after them.  The list is written as sinks, the base
 // members of every taken community (each slot finds its community by binary
 // search over the communities' first slots), then the taken tail members in
 // tail order.
@@ -375,7 +377,8 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
 // Exact score of n communities, one 16-lane group per community, stride 64
 // groups: float32 of the float64 sum over d of qbar_d * float32(csum_d / size),
 // the centroid exactly as the index stores it.  The communities are the list
-// entries (to_list) or the ids slab * 4096 + i of one slab.  Every lane loads
+// entries (to_list) or the ids slab * 4096 + i of one slab (or of the column
+// past the last whole slab, i < 1024).  Every lane loads
 // its D/16 consecutive sums with vector loads; rows of two communities per
 // group are in flight together.
 template <int D>
