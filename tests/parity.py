@@ -107,6 +107,25 @@ def check_csr(layer, orc: O.Oracle):
         np.testing.assert_array_equal(toks[g, :order.size], order)
 
 
+def _check_screening(scores, cscale, q_heads, exact, counts, where: str):
+    """The scoring kernel's screening scores against the oracle's exact ones.
+    The int16 copy rounds every centroid entry to within cscale / 2, and the
+    float32 dot product over D dimensions (with the query rounded to float32)
+    adds at most 32767 (D + 1) 2^-24 cscale |qbar|_1; the two float32 roundings
+    of the screening score and the one of the exact score stay under
+    2^-21 |s~|.  The selection's certain-taken / certain-not decisions rest on
+    this bound.  Empty communities and ids at or past the count score -inf."""
+    C, D = counts.size, q_heads.shape[-1]
+    live = counts > 0
+    assert np.all(scores[:C][~live] == -np.inf) and np.all(scores[C:] == -np.inf), f"{where}: dead ids not -inf"
+    qbar = q_heads.astype(np.float64).sum(axis=0).astype(np.float32).astype(np.float64)
+    s = scores[:C][live].astype(np.float64)
+    bound = cscale[:C][live].astype(np.float64) * np.abs(qbar).sum() * (0.5 + 32767 * (D + 1) * 2.0 ** -24) \
+        + np.abs(s) * 2.0 ** -21
+    err = np.abs(s - exact[live].astype(np.float64))
+    assert np.all(err <= bound), f"{where}: screening error {err.max():.3g} beyond its bound"
+
+
 def _selection_ok(r: O.GraphStep, counts, gpu_sel, budget, stats: Stats, where: str) -> bool:
     so, sg = set(r.selected.tolist()), set(int(c) for c in gpu_sel)
     if so == sg:
@@ -168,6 +187,7 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
     for t in range(steps):
         inp = synth.gen_step(w, seed, t, layer.slices)
         q, kn, vn = inp.q.to(dev), inp.k_new.to(dev), inp.v_new.to(dev)
+        cscale = layer.idx.cscale.clone()  # the scales the step scores with (its update changes them)
         dense = None
         if windows > 1:
             dec.step(q, kn, vn)
@@ -180,7 +200,8 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
             dec.update(kn, vn)
         torch.cuda.synchronize()
         H = {k: getattr(buf, k).cpu().numpy() for k in
-             ("sel", "sel_n", "top", "tok_list", "tok_n", "out", "logits", "ml", "edges", "assign")}
+             ("sel", "sel_n", "top", "tok_list", "tok_n", "out", "logits", "ml", "edges", "assign", "scores")}
+        H["cscale"] = cscale.cpu().numpy()
         assert int(layer.idx.status.item()) == 0, f"step {t}: device status {int(layer.idx.status.item())}"
         qn = inp.q.float().numpy()
         for g in orc.graph_ids:
@@ -189,6 +210,8 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
             gsel = H["sel"][g, :H["sel_n"][g]]
             assert (np.diff(gsel) > 0).all(), f"{where}: sel not ascending"
             r = orc.step_graph(g, qn)
+            _check_screening(H["scores"][g], H["cscale"][g], qn[st.b, st.qh0:st.qh0 + st.nh], r.scores, st.counts,
+                             where)
             assert H["top"][g] == r.top, f"{where}: top {H['top'][g]} != {r.top}"
             if not _selection_ok(r, st.counts, gsel, w.budget, stats, where):
                 r = orc.step_graph(g, qn, force_sel=gsel)
