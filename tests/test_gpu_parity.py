@@ -119,24 +119,26 @@ def test_max_community_capacity():
     PY.run_steps(w, 33, w.steps, layer_kw={"c_cap": ckv.CKV_MAX_C_CAP})
 
 
-@pytest.mark.parametrize("n_ctx,c_cap,budget,max_comm,d", [
-    (18000, 4352, 600, 0, 128),     # one slab of 4096 and one column of 1024
-    (35500, 8448, 600, 0, 128),     # two slabs and a column: the 128K capacity
-    (35500, 8448, 600, 40, 128),    # the same, exact scores of every community
-    (35500, 8448, 20000, 0, 128),   # more taken communities than the LDS copy holds
-    (52800, 12544, 900, 0, 64),     # three slabs and a column, d = 64
+@pytest.mark.parametrize("n_ctx,c_cap,budget,max_comm,d,mode", [
+    (18000, 4352, 600, 0, 128, synth.PER_HEAD),    # one slab of 4096 and one column of 1024
+    (18000, 4352, 600, 0, 64, synth.GROUP),        # the same, d = 64, query groups
+    (35500, 8448, 600, 0, 128, synth.PER_HEAD),    # two slabs and a column: the 128K capacity
+    (35500, 8448, 600, 40, 128, synth.PER_HEAD),   # the same, exact scores of every community
+    (35500, 8448, 20000, 0, 128, synth.PER_HEAD),  # more taken communities than the LDS copy holds
+    (35500, 8448, 1200, 0, 64, synth.GROUP),       # two slabs and a column, d = 64, query groups
+    (52800, 12544, 900, 0, 64, synth.PER_HEAD),    # three slabs and a column, d = 64
 ])
-def test_selection_column_past_the_slabs(n_ctx, c_cap, budget, max_comm, d):
+def test_selection_column_past_the_slabs(n_ctx, c_cap, budget, max_comm, d, mode):
     """Capacities just past a whole number of slabs of 4096 communities take
     one column of 1024 more per selection block instead of another slab; the
     community counts here reach into that column."""
     w = small_per_head(n_ctx=n_ctx, budget=budget, max_comm=max_comm, mean_size=4, min_size=2, n_kv_heads=2,
-                       n_q_heads=4, head_dim=d, key_scale=1.0 / np.sqrt(d), steps=3)
+                       n_q_heads=4, head_dim=d, key_scale=1.0 / np.sqrt(d), mode=mode, steps=3)
     layer, orc = PY.make_pair(w, 41, w.steps)
     n_comm = synth.graph_n_comm(w, layer.slices)
     assert layer.idx.c_cap == c_cap, layer.idx.c_cap
     assert max(n_comm) > (c_cap // 4096) * 4096, n_comm
-    PY.log(f"c_cap {c_cap} n_comm {min(n_comm)}..{max(n_comm)} budget {budget} max_comm {max_comm} d {d}")
+    PY.log(f"c_cap {c_cap} n_comm {min(n_comm)}..{max(n_comm)} budget {budget} max_comm {max_comm} d {d} {mode}")
     PY.run_steps(w, 41, w.steps, pair=(layer, orc))
 
 
