@@ -1088,7 +1088,7 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, 
     CKV_SEL(1, 0, 128) CKV_SEL(2, 0, 128) CKV_SEL(3, 0, 128) CKV_SEL(4, 0, 128)
     CKV_SEL(1, 1, 128) CKV_SEL(2, 1, 128) CKV_SEL(3, 1, 128)
 #undef CKV_SEL
-    return hipGetLastError();
+    return hipErrorInvalidValue;  // c_cap and head_dim are validated before: not reached
 }
 
 }  // namespace ckv
