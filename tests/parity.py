@@ -14,7 +14,7 @@ Bars (written here once, used by every GPU test):
 from __future__ import annotations
 
 import sys
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Dict, List, Optional
 
 import numpy as np
@@ -171,10 +171,11 @@ def _check_logits(H, g, tl, r, where):
 
 def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None,
               check_state_every: int = 1, layer_kw: Optional[dict] = None, check_dense: bool = False,
-              pair=None, windows: int = 1, defer: bool = True) -> Stats:
+              pair=None, windows: int = 1, defer: bool = True, q_fn=None) -> Stats:
     """Steps the library and the oracle side by side and checks every output.
     windows > 1 runs each step as the decoder's windowed multi-stream step;
-    defer=False runs complete gathers (combine inside the gather kernel)."""
+    defer=False runs complete gathers (combine inside the gather kernel).
+    q_fn(t, q) -> q replaces step t's queries (both sides see the same ones)."""
     layer, orc = pair if pair is not None else make_pair(w, seed, steps, graphs, **(layer_kw or {}))
     dev = layer.kv.kv.device
     dec, buf = layer.dec, layer.dec.buf
@@ -186,6 +187,8 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
     stats = Stats()
     for t in range(steps):
         inp = synth.gen_step(w, seed, t, layer.slices)
+        if q_fn is not None:
+            inp = replace(inp, q=q_fn(t, inp.q))
         q, kn, vn = inp.q.to(dev), inp.k_new.to(dev), inp.v_new.to(dev)
         cscale = layer.idx.cscale.clone()  # the scales the step scores with (its update changes them)
         dense = None

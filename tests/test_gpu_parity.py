@@ -142,6 +142,22 @@ def test_selection_column_past_the_slabs(n_ctx, c_cap, budget, max_comm, d, mode
     PY.run_steps(w, 41, w.steps, pair=(layer, orc))
 
 
+@pytest.mark.parametrize("mode,n_ctx,mean_size", [(synth.PER_HEAD, 3000, 16), (synth.GROUP, 3000, 16),
+                                                  (synth.PER_HEAD, 18000, 4)])
+def test_zero_query_ties_break_by_id(mode, n_ctx, mean_size):
+    """A zero query scores every non-empty community exactly 0, so the
+    screening range is empty and the selection computes every exact score:
+    the budget then takes the lowest ids, attention is uniform over the
+    attended set, and the edges are its lowest non-sink positions.  Every
+    decision is an exact tie broken the one documented way, so nothing may
+    differ from the oracle, not even inside the tie window.  The last case
+    has a community count past one slab of 4096."""
+    w = small_per_head(mode=mode, n_ctx=n_ctx, mean_size=mean_size, min_size=2, n_kv_heads=2, n_q_heads=4, steps=3)
+    PY.log(f"zero query {mode} n_ctx={n_ctx}")
+    st = PY.run_steps(w, 42, w.steps, q_fn=lambda t, q: torch.zeros_like(q))
+    assert st.near_sel == 0 and st.near_edges == 0, (st.near_sel, st.near_edges)
+
+
 def test_largest_kappa():
     """kappa at its maximum (32) with a budget of many communities."""
     w = small_per_head(n_ctx=9000, budget=1500, kappa=32, steps=4)
