@@ -158,6 +158,19 @@ def test_zero_query_ties_break_by_id(mode, n_ctx, mean_size):
     assert st.near_sel == 0 and st.near_edges == 0, (st.near_sel, st.near_edges)
 
 
+@pytest.mark.parametrize("mode", [synth.PER_HEAD, synth.GROUP])
+def test_peaked_softmax(mode):
+    """Keys scaled 4x: the logits span hundreds, so all but a few tokens'
+    probabilities underflow float32.  The running (max, sum) rescaling and the
+    split-K combine must stay finite and exact to the tolerance, and the group
+    edge weights (sums of probabilities) meet many exact zeros, whose order is
+    the position tie-break."""
+    w = small_per_head(mode=mode, n_ctx=3000, key_scale=4.0, steps=3)
+    PY.log(f"peaked softmax {mode}")
+    st = PY.run_steps(w, 43, w.steps)
+    PY.log(f"  near-tie selections {st.near_sel}, edges {st.near_edges}, max abs {st.max_abs:.2e}")
+
+
 def test_largest_kappa():
     """kappa at its maximum (32) with a budget of many communities."""
     w = small_per_head(n_ctx=9000, budget=1500, kappa=32, steps=4)
