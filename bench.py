@@ -204,30 +204,39 @@ def main():
     # Breakdown pass: the same steps, each of the four kernels stamping its own
     # start/stop events from its dispatch (ckv_time_next_launch), so these are
     # kernel execution times on the stream the kernels run on.
+    b = buf
+
+    def stamp_events():
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+              for _ in range(K)]
+        for row in ev:  # torch creates the underlying HIP events on first record
+            for a, c in row:
+                a.record()
+                c.record()
+        return ev
+
+    def stamped_step(t, row):
+        """One step as its four calls, each stamping row[k] from its dispatch."""
+        q = Q[t]
+        ckv.ckv_time_next_launch(*row[0])
+        ckv.ckv_score_centroids(kv, idx, q, b.scores)
+        ckv.ckv_time_next_launch(*row[1])
+        ckv.ckv_select_communities(kv, idx, q, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
+                                   b.tok_list, b.tok_n)
+        ckv.ckv_time_next_launch(*row[2])
+        out, ml = (None, None) if dec.defer else (b.out, b.ml)
+        ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, out, b.logits, ml, b.ws)
+        ckv.ckv_time_next_launch(*row[3])
+        ckv.ckv_assign_update(kv, idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, dec.kappa, KN[t], VN[t],
+                              b.edges, b.assign, b.ws, out=b.out if dec.defer else None)
+
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
-          for _ in range(K)]
-    for row in ev:  # torch creates the underlying HIP events on first record
-        for a, c in row:
-            a.record()
-            c.record()
+    ev = stamp_events()
     torch.cuda.synchronize()
-    b = buf
     for i, t in enumerate(range(W, total)):
-        q = Q[t]
-        ckv.ckv_time_next_launch(*ev[i][0])
-        ckv.ckv_score_centroids(kv, idx, q, b.scores)
-        ckv.ckv_time_next_launch(*ev[i][1])
-        ckv.ckv_select_communities(kv, idx, q, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
-                                   b.tok_list, b.tok_n)
-        ckv.ckv_time_next_launch(*ev[i][2])
-        out, ml = (None, None) if dec.defer else (b.out, b.ml)
-        ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, out, b.logits, ml, b.ws)
-        ckv.ckv_time_next_launch(*ev[i][3])
-        ckv.ckv_assign_update(kv, idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, dec.kappa, KN[t], VN[t],
-                              b.edges, b.assign, b.ws, out=b.out if dec.defer else None)
+        stamped_step(t, ev[i])
     torch.cuda.synchronize()
     dt = np.array([[a.elapsed_time(c) for a, c in ev[i]] for i in range(K)]) * 1e3  # us
     names = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
@@ -236,15 +245,19 @@ def main():
     score_gbps = float(score_bytes * K / (dt[:, 0].sum() * 1e-6) / 1e9)
     ceiling = read_ceiling(w, kv, idx, buf, row_bytes, K)
 
-    # Cold pass: a 512 MB write between steps evicts the 256 MB MALL; only the
-    # step itself is timed.
+    # Cold passes: a 512 MB read between steps evicts the 256 MB MALL (a read,
+    # so the step does not also pay for writing dirty lines back); only the
+    # step itself is timed.  The first pass times whole steps; the second stamps
+    # each kernel as in the breakdown pass (its extra event calls can slow the
+    # host's launches past the flush, so it does not time whole steps).
+    flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
-    flush = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
     cold = []
     for t in range(W, total):
-        flush.fill_(float(t))
+        flush.amax()
         a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         dec.step(Q[t], KN[t], VN[t])
@@ -252,6 +265,16 @@ def main():
         cold.append((a, c))
     torch.cuda.synchronize()
     cold_us = np.array([a.elapsed_time(c) for a, c in cold]) * 1e3
+    restore()
+    for t in range(W):
+        dec.step(Q[t], KN[t], VN[t])
+    evc = stamp_events()
+    torch.cuda.synchronize()
+    for i, t in enumerate(range(W, total)):
+        flush.amax()
+        stamped_step(t, evc[i])
+    torch.cuda.synchronize()
+    cold_dt = np.array([[a.elapsed_time(c) for a, c in evc[i]] for i in range(K)]) * 1e3  # us
     del flush
 
     # Dense flash-decode over every cached token of the same state.
@@ -345,7 +368,8 @@ def main():
         "breakdown_step_us": round(float(dt.sum(axis=1).mean()), 2),
         "cold_step_us": {"median": round(float(np.median(cold_us)), 2),
                          "p10": round(float(np.percentile(cold_us, 10)), 2),
-                         "p90": round(float(np.percentile(cold_us, 90)), 2)},
+                         "p90": round(float(np.percentile(cold_us, 90)), 2),
+                         "kernels_median": {n: round(float(np.median(cold_dt[:, k])), 2) for k, n in enumerate(names)}},
         "tokens_per_step": round(float(tok[W:].sum(axis=1).mean()), 1),
         "dense_flash_decode": dense,
         "attention_mass_recall": recall,
