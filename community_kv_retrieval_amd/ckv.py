@@ -31,7 +31,7 @@ CKV_MAX_KAPPA, CKV_MAX_C_CAP = 32, 16384
 
 EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_centroids",
            "ckv_select_communities", "ckv_gather_attend", "ckv_assign_update", "ckv_dense_attend",
-           "ckv_prefill_workspace_bytes", "ckv_prefill_topk", "ckv_read_rows",
+           "ckv_attention_recall", "ckv_prefill_workspace_bytes", "ckv_prefill_topk", "ckv_read_rows",
            "ckv_time_next_launch", "ckv_status_str", "ckv_abi_version")
 
 
@@ -75,6 +75,7 @@ def _load():
                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_size_t, c_void_p]),
         "ckv_dense_attend": (c_int32, [KVP, c_void_p, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_attention_recall": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_void_p]),
         "ckv_prefill_workspace_bytes": (c_size_t, [KVP, c_int32, c_int32]),
         "ckv_prefill_topk": (c_int32, [KVP, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int32, c_float,
                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
@@ -322,6 +323,20 @@ def ckv_dense_attend(kv: KVStore, q: torch.Tensor, sm_scale: float, out: torch.T
                                                     _stream(stream)))
 
 
+def ckv_attention_recall(kv: KVStore, idx: CommunityIndex, ml: torch.Tensor, dense_ml: torch.Tensor,
+                         recall: torch.Tensor, stream=None):
+    """recall[G][hpg]: the share of each head's dense softmax mass (dense_ml
+    from ckv_dense_attend) that its graph's attended tokens (ml from the
+    gather) carry."""
+    G, nh = idx.n_graphs, idx.heads_per_graph(kv)
+    _need(ml, "ml", torch.float32, (G, nh, 2))
+    _need(dense_ml, "dense_ml", torch.float32, (kv.batch, kv.n_q_heads, 2))
+    _need(recall, "recall", torch.float32, (G, nh))
+    _check("ckv_attention_recall", LIB.ckv_attention_recall(ctypes.byref(kv.desc), ctypes.byref(idx.desc),
+                                                            _ptr(ml), _ptr(dense_ml), _ptr(recall),
+                                                            _stream(stream)))
+
+
 def ckv_read_rows(kv: KVStore, rows: torch.Tensor, part: torch.Tensor, stream=None):
     """The gather's loads over the given pool rows (a read-ceiling measurement);
     part[ceil(n/256)] gets per-block XOR checksums of the rows' 32-bit words."""
@@ -456,23 +471,13 @@ class Decoder:
         ckv_dense_attend(self.kv, q, self.sm_scale, out, self.buf.ws, stream, ml=ml)
         return out
 
-    def recall(self, dense_ml: torch.Tensor) -> torch.Tensor:
-        """Attention-mass recall of the last gather, per graph and head: the
-        share of the dense softmax mass (dense_ml from dense(..., ml=)) that the
-        attended tokens carry, exp(lse_attended - lse_all) (page Figure 3).
-        Host-side arithmetic on kernel outputs (a diagnostic, not a step).
-        Needs a complete gather's ml: with defer set, call it after update()."""
-        kv, idx, b = self.kv, self.idx, self.buf
-        G, nh = idx.n_graphs, idx.heads_per_graph(kv)
-        g = torch.arange(G, device=dense_ml.device)
-        if idx.mode == CKV_MODE_PER_HEAD:
-            bb, qh = g // kv.n_q_heads, g % kv.n_q_heads
-            heads = qh[:, None]
-        else:
-            bb, kh = g // kv.n_kv_heads, g % kv.n_kv_heads
-            heads = kh[:, None] * kv.group + torch.arange(nh, device=dense_ml.device)[None, :]
-        d = dense_ml[bb[:, None], heads]  # [G][nh][2]
-        s = b.ml.double()
-        lse_t = s[..., 0] + torch.log(s[..., 1])
-        lse_d = d[..., 0].double() + torch.log(d[..., 1].double())
-        return torch.exp(lse_t - lse_d)
+    def recall(self, dense_ml: torch.Tensor, recall: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+        """Attention-mass recall of the last gather, per graph and head
+        (ckv_attention_recall), from dense_ml of dense(..., ml=).  Needs a
+        complete gather's ml: with defer set, call it after update()."""
+        if recall is None:
+            recall = torch.empty((self.idx.n_graphs, self.idx.heads_per_graph(self.kv)), dtype=torch.float32,
+                                 device=dense_ml.device)
+        ckv_attention_recall(self.kv, self.idx, self.buf.ml, dense_ml, recall, stream)
+        return recall

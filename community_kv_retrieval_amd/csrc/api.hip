@@ -64,7 +64,7 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 5; }
+int32_t ckv_abi_version(void) { return 6; }
 
 ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;
@@ -201,6 +201,15 @@ ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, flo
     if (!ws || ws_bytes < L.dense_total) return CKV_E_WORKSPACE;
     return hip_status(launch_dense(kv, q, sm_scale, out, ml, (float *)at(ws, L.part_dense),
                                    (int32_t *)at(ws, L.ctr_dense), (hipStream_t)stream));
+}
+
+ckv_status ckv_attention_recall(const ckv_kv *kv, const ckv_index *idx, const float *ml, const float *dense_ml,
+                                float *recall, ckv_stream_t stream) {
+    ckv_status st = check_kv(kv);
+    if (st != CKV_OK) return st;
+    if ((st = check_index(kv, idx)) != CKV_OK) return st;
+    if (!ml || !dense_ml || !recall) return CKV_E_INVALID;
+    return hip_status(launch_recall(kv, idx, ml, dense_ml, recall, (hipStream_t)stream));
 }
 
 ckv_status ckv_read_rows(const ckv_kv *kv, const uint32_t *rows, int32_t n, uint32_t *part, ckv_stream_t stream) {

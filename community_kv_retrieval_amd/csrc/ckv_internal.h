@@ -133,6 +133,11 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
                          int32_t *edges, int32_t *assign, float *out, const float *part, int32_t *ctr,
                          hipStream_t s);
 
+// Attention-mass recall of every graph's heads from the gather's and the
+// dense baseline's softmax states.
+hipError_t launch_recall(const ckv_kv *kv, const ckv_index *idx, const float *ml, const float *dense_ml,
+                         float *recall, hipStream_t s);
+
 // Prefill graph construction of sequence b's first n positions.  lse: [Hq][n]
 // floats of workspace (query-group mode).
 hipError_t launch_prefill(const ckv_kv *kv, int mode, int b, const void *q, int n, int n_sinks, int kappa,

@@ -238,11 +238,24 @@ ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32
  * seq_len[b] cached tokens of its kv head.  out[batch][n_q_heads][head_dim];
  * ml (NULL: not written) [batch][n_q_heads][2] = (max z, sum exp(z - max)) of
  * every head over all its tokens.  With the ml of ckv_gather_attend for the
- * same q, exp(m_T + log l_T - m - log l) is the share of the dense attention
- * mass that the attended tokens carry (the page's attention-mass recall,
- * Figure 3). */
+ * same q, ckv_attention_recall gives the share of the dense attention mass
+ * that the attended tokens carry (the page's attention-mass recall, Figure 3). */
 ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, float *out, float *ml,
                             void *ws, size_t ws_bytes, ckv_stream_t stream);
+
+/* Attention-mass recall (Figure 3: the share of the full attention mass that
+ * the retrieved tokens capture), for every graph and head:
+ *   recall[G][hpg] = exp(m_T - m) * l_T / l
+ * from (m_T, l_T) = ml[G][hpg][2] of ckv_gather_attend (a complete gather, or
+ * the ml a deferred gather's ckv_assign_update wrote) and (m, l) =
+ * dense_ml[batch][n_q_heads][2] of ckv_dense_attend on the same q and cache
+ * state: the softmax mass of the attended tokens over that of every cached
+ * token.  Evaluated in float64, stored as float32; 0 where the graph attended
+ * nothing (l_T = 0).  All three arrays are device memory.  Processes every
+ * graph (the launch window is ignored).  Errors: CKV_E_INVALID for a NULL
+ * array or a bad descriptor. */
+ckv_status ckv_attention_recall(const ckv_kv *kv, const ckv_index *idx, const float *ml, const float *dense_ml,
+                                float *recall, ckv_stream_t stream);
 
 /* Prefill graph construction (Figure 1 panel (1): during prefill each query is
  * linked to the keys it attends to most; sinks are left out of the pool, Table 6;

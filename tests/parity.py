@@ -22,8 +22,10 @@ import torch
 
 from community_kv_retrieval_amd import ckv, runner, synth
 from oracle import ckv_oracle as O
+from tests import decisions as D
 
-ATOL, RTOL, TIE = 2e-3, 1e-2, 1e-6
+ATOL, RTOL = 2e-3, 1e-2
+TIE = D.TIE
 LOGIT_ATOL = 1e-4
 
 
@@ -126,36 +128,18 @@ def _check_screening(scores, cscale, q_heads, exact, counts, where: str):
     assert np.all(err <= bound), f"{where}: screening error {err.max():.3g} beyond its bound"
 
 
-def _selection_ok(r: O.GraphStep, counts, gpu_sel, budget, stats: Stats, where: str) -> bool:
-    so, sg = set(r.selected.tolist()), set(int(c) for c in gpu_sel)
-    if so == sg:
-        return True
-    ranked = O.rank_communities(r.scores, counts)
-    k = len(so)
-    bound = [float(r.scores[ranked[k - 1]])] if k else []
-    if k < ranked.size:
-        bound.append(float(r.scores[ranked[k]]))
-    for c in so ^ sg:
-        gap = min(abs(float(r.scores[c]) - s) for s in bound) if bound else np.inf
-        assert gap <= TIE, f"{where}: selection differs beyond the tie window (community {c}, gap {gap})"
-        stats.gaps.append(gap)
-    assert int(counts[list(sg)].sum()) <= budget, f"{where}: device selection exceeds the budget"
-    stats.near_sel += 1
-    return False
+def _selection_ok(r: O.GraphStep, counts, gpu_sel, w, stats: Stats, where: str) -> bool:
+    return D.selection_ok(r.scores, counts, r.selected, gpu_sel, w.budget, w.max_comm, where, stats.gaps) or \
+        _count(stats, "near_sel")
 
 
-def _edges_ok(r: O.GraphStep, gpu_edges, stats: Stats, where: str) -> bool:
-    eo, eg = [int(x) for x in r.edges], [int(x) for x in gpu_edges]
-    if set(eo) == set(eg):
-        assert eo == eg or True
-        return True
-    wpos = dict(zip(r.positions.tolist(), r.weights.tolist()))
-    cut = wpos[eo[-1]]
-    for p in set(eo) ^ set(eg):
-        gap = abs(wpos[p] - cut)
-        assert gap <= TIE, f"{where}: edges differ beyond the tie window (position {p}, gap {gap})"
-        stats.gaps.append(gap)
-    stats.near_edges += 1
+def _edges_ok(r: O.GraphStep, gpu_edges, w, stats: Stats, where: str) -> bool:
+    return D.edges_ok(r.positions, r.weights, w.n_sinks, w.kappa, r.edges, gpu_edges, where, stats.gaps) or \
+        _count(stats, "near_edges")
+
+
+def _count(stats: Stats, field_name: str) -> bool:
+    setattr(stats, field_name, getattr(stats, field_name) + 1)
     return False
 
 
@@ -169,23 +153,80 @@ def _check_logits(H, g, tl, r, where):
     np.testing.assert_allclose(H["ml"][g][:, 1], lsum, rtol=1e-4)
 
 
+def snapshot(buf, cscale) -> Dict[str, np.ndarray]:
+    """Host copies of a decoder's step outputs, plus the screening scales the
+    step scored with (taken before its update changed them)."""
+    H = {k: getattr(buf, k).cpu().numpy() for k in
+         ("sel", "sel_n", "top", "tok_list", "tok_n", "out", "logits", "ml", "edges", "assign", "scores")}
+    H["cscale"] = cscale.cpu().numpy()
+    return H
+
+
+def check_graph(H, g: int, orc: O.Oracle, qn: np.ndarray, k_new: np.ndarray, w: synth.Workload, stats: Stats,
+                where: str, dense: Optional[torch.Tensor] = None):
+    """Every output of graph g's step against the oracle's step on the same
+    query, then the oracle applies the device's (checked) assignment.
+    qn: [B][Hq][d] the step's queries; k_new: [B][Hkv][d] the new keys."""
+    st = orc.g[g]
+    gsel = H["sel"][g, :H["sel_n"][g]]
+    assert (np.diff(gsel) > 0).all(), f"{where}: sel not ascending"
+    r = orc.step_graph(g, qn)
+    _check_screening(H["scores"][g], H["cscale"][g], qn[st.b, st.qh0:st.qh0 + st.nh], r.scores, st.counts, where)
+    assert H["top"][g] == r.top, f"{where}: top {H['top'][g]} != {r.top}"
+    if not _selection_ok(r, st.counts, gsel, w, stats, where):
+        r = orc.step_graph(g, qn, force_sel=gsel)
+    tl = H["tok_list"][g, :H["tok_n"][g]]
+    assert tl.size == np.unique(tl).size, f"{where}: duplicate token"
+    np.testing.assert_array_equal(np.sort(tl), r.positions, err_msg=f"{where}: token set")
+    gout = H["out"][st.b, st.qh0:st.qh0 + st.nh].astype(np.float64)
+    err = np.abs(gout - r.out)
+    assert np.all(err <= ATOL + RTOL * np.abs(r.out)), f"{where}: attention max abs err {err.max():.3g}"
+    stats.max_abs = max(stats.max_abs, float(err.max()))
+    stats.max_rel = max(stats.max_rel, float((err / np.maximum(np.abs(r.out), 1e-3)).max()))
+    if dense is not None:
+        grp = w.n_q_heads // w.n_kv_heads
+        dref = orc.dense(qn, st.b, st.kh)[st.qh0 - st.kh * grp:st.qh0 - st.kh * grp + st.nh]
+        dn = dense.cpu().numpy()[st.b, st.qh0:st.qh0 + st.nh]
+        assert np.all(np.abs(dn - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: dense baseline"
+        if r.positions.size == orc.len[st.b]:  # every cached token attended: sparse == dense
+            assert np.all(np.abs(gout - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: sparse vs dense"
+            stats.dense_equal += 1
+    # logits of every slot, and the softmax state (empty: max -inf, sum 0)
+    if r.positions.size == 0:
+        assert np.all(H["ml"][g][:, 0] == -np.inf) and np.all(H["ml"][g][:, 1] == 0), f"{where}: empty ml"
+    else:
+        _check_logits(H, g, tl, r, where)
+    ge = H["edges"][g]
+    ne = int((ge >= 0).sum())
+    assert (ge[ne:] == -1).all(), f"{where}: edges not -1 padded"
+    if not _edges_ok(r, ge[:ne], w, stats, where):
+        r = orc.step_graph(g, qn, force_sel=gsel, force_edges=ge[:ne])
+    assert H["assign"][g] == r.assign, f"{where}: assign {H['assign'][g]} != {r.assign}"
+    orc.apply_update(g, int(H["assign"][g]), k_new[st.b, st.kh])
+    stats.graphs += 1
+    return r
+
+
 def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None,
               check_state_every: int = 1, layer_kw: Optional[dict] = None, check_dense: bool = False,
-              pair=None, windows: int = 1, defer: bool = True, q_fn=None) -> Stats:
+              pair=None, windows: int = 1, defer: bool = True, q_fn=None, first_step: int = 0) -> Stats:
     """Steps the library and the oracle side by side and checks every output.
     windows > 1 runs each step as the decoder's windowed multi-stream step;
     defer=False runs complete gathers (combine inside the gather kernel).
-    q_fn(t, q) -> q replaces step t's queries (both sides see the same ones)."""
+    q_fn(t, q) -> q replaces step t's queries (both sides see the same ones).
+    Steps are numbered first_step .. first_step + steps - 1 (the inputs of
+    step t are drawn for t), continuing a pair that has already run."""
     layer, orc = pair if pair is not None else make_pair(w, seed, steps, graphs, **(layer_kw or {}))
     dev = layer.kv.kv.device
     dec, buf = layer.dec, layer.dec.buf
     dec.defer = defer
     dec.set_windows(windows)
     assert not (check_dense and windows > 1), "the dense check runs between the calls of one window"
-    check_csr(layer, orc)
-    check_index_state(layer, orc, w, full=True)
+    if first_step == 0:
+        check_csr(layer, orc)
+        check_index_state(layer, orc, w, full=True)
     stats = Stats()
-    for t in range(steps):
+    for t in range(first_step, first_step + steps):
         inp = synth.gen_step(w, seed, t, layer.slices)
         if q_fn is not None:
             inp = replace(inp, q=q_fn(t, inp.q))
@@ -202,56 +243,17 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
                 dec.dense(q, dense)
             dec.update(kn, vn)
         torch.cuda.synchronize()
-        H = {k: getattr(buf, k).cpu().numpy() for k in
-             ("sel", "sel_n", "top", "tok_list", "tok_n", "out", "logits", "ml", "edges", "assign", "scores")}
-        H["cscale"] = cscale.cpu().numpy()
+        H = snapshot(buf, cscale)
         assert int(layer.idx.status.item()) == 0, f"step {t}: device status {int(layer.idx.status.item())}"
         qn = inp.q.float().numpy()
+        kn_host = inp.k_new.float().numpy()
         for g in orc.graph_ids:
-            where = f"{w.name} seed={seed} step={t} graph={g}"
-            st = orc.g[g]
-            gsel = H["sel"][g, :H["sel_n"][g]]
-            assert (np.diff(gsel) > 0).all(), f"{where}: sel not ascending"
-            r = orc.step_graph(g, qn)
-            _check_screening(H["scores"][g], H["cscale"][g], qn[st.b, st.qh0:st.qh0 + st.nh], r.scores, st.counts,
-                             where)
-            assert H["top"][g] == r.top, f"{where}: top {H['top'][g]} != {r.top}"
-            if not _selection_ok(r, st.counts, gsel, w.budget, stats, where):
-                r = orc.step_graph(g, qn, force_sel=gsel)
-            tl = H["tok_list"][g, :H["tok_n"][g]]
-            assert tl.size == np.unique(tl).size, f"{where}: duplicate token"
-            np.testing.assert_array_equal(np.sort(tl), r.positions, err_msg=f"{where}: token set")
-            gout = H["out"][st.b, st.qh0:st.qh0 + st.nh].astype(np.float64)
-            err = np.abs(gout - r.out)
-            assert np.all(err <= ATOL + RTOL * np.abs(r.out)), \
-                f"{where}: attention max abs err {err.max():.3g}"
-            stats.max_abs = max(stats.max_abs, float(err.max()))
-            stats.max_rel = max(stats.max_rel, float((err / np.maximum(np.abs(r.out), 1e-3)).max()))
-            if dense is not None:
-                grp = w.n_q_heads // w.n_kv_heads
-                dref = orc.dense(qn, st.b, st.kh)[st.qh0 - st.kh * grp:st.qh0 - st.kh * grp + st.nh]
-                dn = dense.cpu().numpy()[st.b, st.qh0:st.qh0 + st.nh]
-                assert np.all(np.abs(dn - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: dense baseline"
-                if r.positions.size == orc.len[st.b]:  # every cached token attended: sparse == dense
-                    assert np.all(np.abs(gout - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: sparse vs dense"
-                    stats.dense_equal += 1
-            # logits of every slot, and the softmax state (empty: max -inf, sum 0)
-            if r.positions.size == 0:
-                assert np.all(H["ml"][g][:, 0] == -np.inf) and np.all(H["ml"][g][:, 1] == 0), f"{where}: empty ml"
-            else:
-                _check_logits(H, g, tl, r, where)
-            ge = H["edges"][g]
-            ne = int((ge >= 0).sum())
-            assert (ge[ne:] == -1).all()
-            if not _edges_ok(r, ge[:ne], stats, where):
-                r = orc.step_graph(g, qn, force_sel=gsel, force_edges=ge[:ne])
-            assert H["assign"][g] == r.assign, f"{where}: assign {H['assign'][g]} != {r.assign}"
-            orc.apply_update(g, int(H["assign"][g]), inp.k_new.float().numpy()[st.b, st.kh])
-            stats.graphs += 1
-        orc.append(inp.k_new.float().numpy(), inp.v_new.float().numpy())
+            check_graph(H, g, orc, qn, kn_host, w, stats, f"{w.name} seed={seed} step={t} graph={g}", dense)
+        orc.append(kn_host, inp.v_new.float().numpy())
         stats.steps += 1
-        if check_state_every and (t + 1) % check_state_every == 0:
-            check_index_state(layer, orc, w, full=(t + 1 == steps))
+        done = t + 1 - first_step
+        if check_state_every and done % check_state_every == 0:
+            check_index_state(layer, orc, w, full=(done == steps))
     lens = layer.kv.seq_len.cpu().numpy()
     for b in {st.b for st in orc.g.values()}:
         assert lens[b] == orc.len[b]

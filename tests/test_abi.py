@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ckv.LIB.ckv_abi_version() == 5
+    assert ckv.LIB.ckv_abi_version() == 6
     for code in (0, -1, -2, -3, -4):
         assert ckv.ckv_status_str(code) != "unknown status"
     assert ckv.ckv_status_str(7) == "unknown status"
@@ -158,6 +158,16 @@ def test_gather_assign_dense_workspace_checks():
     assert a(8, FAKE, need - 1) == ckv.CKV_E_WORKSPACE
     d = ckv.LIB.ckv_dense_attend(ctypes.byref(kv), FAKE, 1.0, FAKE, None, FAKE, _ws(kv, None, 0) - 1, None)
     assert d == ckv.CKV_E_WORKSPACE
+
+
+def test_attention_recall_validation():
+    kv, idx = _kv(), _idx()
+    f = ckv.LIB.ckv_attention_recall
+    for args in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
+        assert f(ctypes.byref(kv), ctypes.byref(idx), *args, None) == ckv.CKV_E_INVALID
+    assert f(ctypes.byref(kv), ctypes.byref(_idx(n_graphs=31)), FAKE, FAKE, FAKE, None) == ckv.CKV_E_INVALID
+    assert f(ctypes.byref(_kv(head_dim=96)), ctypes.byref(idx), FAKE, FAKE, FAKE, None) == ckv.CKV_E_UNSUPPORTED
+    assert f(None, ctypes.byref(idx), FAKE, FAKE, FAKE, None) == ckv.CKV_E_INVALID
 
 
 def test_read_rows_validation():
