@@ -84,7 +84,7 @@ def selection_ok(scores: np.ndarray, counts: np.ndarray, oracle_sel: Sequence[in
 
 def edges_ok(positions: np.ndarray, weights: np.ndarray, n_sinks: int, kappa: int, oracle_edges: Sequence[int],
              dev_edges: Sequence[int], where: str = "", gaps: Optional[List[float]] = None,
-             tie: float = TIE) -> bool:
+             tie: float = TIE, rel: float = 0.0) -> bool:
     """True when the device's edges equal the oracle's, in rank order; False
     when they differ but are the first kappa of a tie-consistent ranking of the
     pool (the caller then adopts them); AssertionError otherwise.
@@ -92,10 +92,11 @@ def edges_ok(positions: np.ndarray, weights: np.ndarray, n_sinks: int, kappa: in
     The pool is the attended non-sink tokens (Table 6: sinks excluded), ranked
     by weight, higher first.  The device must return exactly min(kappa, |pool|)
     distinct pool tokens, in an order where each may precede the next
-    (weight >= next weight - tie), each of weight >= every unchosen pool
-    token's weight - tie.
+    (weight >= next weight - window), each of weight >= every unchosen pool
+    token's weight - window.
     positions: the attended positions (sinks included); weights: the oracle's
-    float64 graph weight of each; tie: the window (absolute), TIE by default.
+    float64 graph weight of each.  Two weights a, b count as tied when they
+    differ by at most tie + rel * max(a, b) (TIE absolute by default).
     """
     positions = np.asarray(positions)
     w = dict(zip(positions.tolist(), np.asarray(weights, dtype=np.float64).tolist()))
@@ -116,14 +117,15 @@ def edges_ok(positions: np.ndarray, weights: np.ndarray, n_sinks: int, kappa: in
     for i in range(len(eg) - 1):
         j = i + 1 + int(np.argmax(we[i + 1:]))
         inv = we[j] - we[i]
-        assert inv <= tie, (f"{where}: edges out of rank order: position {eg[j]} (rank {j}) outweighs "
-                            f"{eg[i]} (rank {i}) by {inv:.3g}")
+        assert inv <= tie + rel * we[j], (f"{where}: edges out of rank order: position {eg[j]} (rank {j}) "
+                                          f"outweighs {eg[i]} (rank {i}) by {inv:.3g}")
         worst = max(worst, inv)
     chosen = set(eg)
     rest = [p for p in pool if p not in chosen]
     if rest and eg:
-        inv = max(w[p] for p in rest) - min(w[p] for p in eg)
-        assert inv <= tie, f"{where}: an unchosen pool token outweighs a device edge by {inv:.3g}"
+        best_rest = max(w[p] for p in rest)
+        inv = best_rest - min(we)
+        assert inv <= tie + rel * best_rest, f"{where}: an unchosen pool token outweighs a device edge by {inv:.3g}"
         worst = max(worst, inv)
     if gaps is not None:
         gaps.append(worst)
@@ -131,10 +133,14 @@ def edges_ok(positions: np.ndarray, weights: np.ndarray, n_sinks: int, kappa: in
 
 
 # Prefill graph (Figure 1 panel (1)): the logits come from bf16 operands on
-# the matrix cores with float32 accumulation, |dz| <= d 2^-24 sum_i |q_i k_i|
-# (about 8e-5 at d = 128 with these key magnitudes), and a weight
-# exp(z - lse) carries the error of z and of lse: relative <= ~1.7e-4.
-PREFILL_TIE_REL = 2e-4
+# the matrix cores with float32 accumulation, |dz| <= (d - 1) 2^-24
+# sum_i |q_i k_i| (about 6e-5 at d = 128 with these magnitudes, sum |q k| up
+# to ~10), and a weight exp(z - lse) carries the error of z and of lse:
+# relative eps <= ~1.7e-4 per weight (a sum of a group's positive weights keeps
+# that bound).  Two weights can therefore change order when they differ by at
+# most eps (a + b) <= 2 eps max(a, b): the pair window is relative to the
+# larger weight compared.  Each device weight matches the oracle's within eps.
+PREFILL_TIE_REL = 3.5e-4
 PREFILL_WRT, PREFILL_WAT = 2e-4, 1e-9
 
 
@@ -142,8 +148,8 @@ def prefill_row_ok(W: np.ndarray, i: int, n_sinks: int, kappa: int, oracle_row: 
                    dev_weights: Optional[np.ndarray], where: str = "") -> bool:
     """One query position i of the prefill graph: dev_row (kappa entries, -1
     padded) against the oracle's, under the edge rules of edges_ok over the
-    pool n_sinks <= j < i with a window relative to the oracle's kappa-th
-    weight; dev_weights (or None) must match the oracle weight of each chosen
+    pool n_sinks <= j < i with a pair window relative to the larger weight
+    (PREFILL_TIE_REL); dev_weights (or None) must match the oracle weight of each chosen
     edge within PREFILL_WRT / PREFILL_WAT and be 0 past the edges.
     W: the oracle's float64 weight of every key j <= i.
     Returns True when identical, False for an accepted near tie."""
@@ -153,9 +159,8 @@ def prefill_row_ok(W: np.ndarray, i: int, n_sinks: int, kappa: int, oracle_row: 
     assert (o[k:] == -1).all()
     ka = int((a >= 0).sum())
     assert (a[ka:] == -1).all(), f"{where} row {i}: edges not -1 padded"
-    wk = float(W[o[k - 1]]) if k else 0.0
-    same = edges_ok(np.arange(i), W[:i], n_sinks, kappa, o[:k], a[:ka], f"{where} row {i}",
-                    tie=PREFILL_TIE_REL * wk + 1e-12)
+    same = edges_ok(np.arange(i), W[:i], n_sinks, kappa, o[:k], a[:ka], f"{where} row {i}", tie=1e-12,
+                    rel=PREFILL_TIE_REL)
     if dev_weights is not None:
         assert (dev_weights[ka:] == 0).all(), f"{where} row {i}: padding weight"
         np.testing.assert_allclose(dev_weights[:ka], W[a[:ka]], rtol=PREFILL_WRT, atol=PREFILL_WAT,

@@ -254,6 +254,8 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
         done = t + 1 - first_step
         if check_state_every and done % check_state_every == 0:
             check_index_state(layer, orc, w, full=(done == steps))
+        if done % 32 == 0:
+            log(f"  {w.name}: {done} of {steps} steps checked")
     lens = layer.kv.seq_len.cpu().numpy()
     for b in {st.b for st in orc.g.values()}:
         assert lens[b] == orc.len[b]

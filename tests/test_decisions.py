@@ -247,3 +247,19 @@ def test_prefill_rows_identical_and_mistakes():
         wbad[0] *= 1.01
         with pytest.raises(AssertionError):
             D.prefill_row_ok(W, i, sinks, kappa, row, row, wbad)
+
+
+def test_prefill_pair_window_is_relative_to_the_pair():
+    """A swap of two heavy edges 6e-7 apart relatively is a tie; the same
+    absolute gap between light edges is not (window relative to the pair)."""
+    pos = np.arange(10)
+    w = np.array([0.3, 0.2, 0.1, 0.05, 0.0239383, 0.0239382, 0.0100, 2e-5, 1e-5, 1e-5 * (1 - 1e-4)])
+    W = np.r_[w, 0.0]  # weight of the query's own position (never a candidate)
+    orow = np.array([4, 5, 6, 7])
+    i = 10
+    assert D.prefill_row_ok(W, i, 4, 4, orow, orow, None) is True
+    assert D.prefill_row_ok(W, i, 4, 4, orow, np.array([5, 4, 6, 7]), None) is False
+    six = np.array([4, 5, 6, 7, 8, 9])
+    assert D.prefill_row_ok(W, i, 4, 6, six, np.array([4, 5, 6, 7, 9, 8]), None) is False  # 1e-9 of 1e-5
+    with pytest.raises(AssertionError):
+        D.prefill_row_ok(W, i, 4, 6, six, np.array([4, 5, 6, 8, 7, 9]), None)  # 1e-5 of 2e-5
