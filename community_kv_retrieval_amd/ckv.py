@@ -28,9 +28,11 @@ CKV_ST_TAIL_FULL, CKV_ST_CAPACITY, CKV_ST_BAD_LABEL = 1, 2, 4
 CKV_DTYPE_F32, CKV_DTYPE_BF16 = 0, 1
 CKV_MODE_PER_HEAD, CKV_MODE_QUERY_GROUP = 0, 1
 CKV_MAX_KAPPA, CKV_MAX_C_CAP = 32, 16384
+CKV_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_centroids",
-           "ckv_select_communities", "ckv_gather_attend", "ckv_assign_update", "ckv_dense_attend",
+           "ckv_select_communities", "ckv_gather_attend", "ckv_gather_attend_noalloc", "ckv_assign_update",
+           "ckv_dense_attend",
            "ckv_attention_recall", "ckv_prefill_workspace_bytes", "ckv_prefill_topk", "ckv_read_rows",
            "ckv_time_next_launch", "ckv_status_str", "ckv_abi_version")
 
@@ -71,6 +73,8 @@ def _load():
                                              c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
         "ckv_gather_attend": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+        "ckv_gather_attend_noalloc": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_int32, c_float,
+                                                c_void_p, c_void_p, c_void_p, c_void_p]),
         "ckv_assign_update": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_size_t, c_void_p]),
@@ -265,6 +269,22 @@ def ckv_gather_attend(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, tok_lis
         ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q), _ptr(tok_list), _ptr(tok_n), t_cap,
         float(sm_scale), _ptr(out), _ptr(logits), _ptr(ml), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def ckv_gather_attend_noalloc(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, tok_list: torch.Tensor,
+                              tok_n: torch.Tensor, sm_scale: float, out: torch.Tensor, logits: torch.Tensor,
+                              ml: torch.Tensor, stream=None):
+    """ckv_gather_attend (complete) with the library's static scratch instead of a workspace."""
+    G, nh, t_cap = idx.n_graphs, idx.heads_per_graph(kv), tok_list.shape[1]
+    _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
+    _need(tok_list, "tok_list", torch.int32, (G, t_cap))
+    _need(tok_n, "tok_n", torch.int32, (G,))
+    _need(out, "out", torch.float32, (kv.batch, kv.n_q_heads, kv.head_dim))
+    _need(logits, "logits", torch.float32, (G, nh, t_cap))
+    _need(ml, "ml", torch.float32, (G, nh, 2))
+    _check("ckv_gather_attend_noalloc", LIB.ckv_gather_attend_noalloc(
+        ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q), _ptr(tok_list), _ptr(tok_n), t_cap,
+        float(sm_scale), _ptr(out), _ptr(logits), _ptr(ml), _stream(stream)))
 
 
 def ckv_assign_update(kv: KVStore, idx: CommunityIndex, tok_list: torch.Tensor, tok_n: torch.Tensor,

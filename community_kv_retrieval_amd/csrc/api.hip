@@ -173,6 +173,20 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
                                     (hipStream_t)stream));
 }
 
+ckv_status ckv_gather_attend_noalloc(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                                     const int32_t *tok_list, const int32_t *tok_n, int32_t t_cap,
+                                     float sm_scale, float *out, float *logits, float *ml,
+                                     ckv_stream_t stream) {
+    ckv_status st = check_kv(kv);
+    if (st != CKV_OK) return st;
+    if ((st = check_index(kv, idx)) != CKV_OK) return st;
+    if (!q || !tok_list || !tok_n || !logits || !out || !ml) return CKV_E_INVALID;
+    if (t_cap < 1) return CKV_E_INVALID;
+    if (noalloc_gather_bytes(kv, idx, t_cap) > CKV_NOALLOC_SCRATCH_BYTES) return CKV_E_WORKSPACE;
+    return hip_status(launch_gather_noalloc(kv, idx, q, tok_list, tok_n, t_cap, sm_scale, out, logits, ml,
+                                            (hipStream_t)stream));
+}
+
 ckv_status ckv_assign_update(const ckv_kv *kv, const ckv_index *idx, const int32_t *tok_list,
                              const int32_t *tok_n, const float *logits, float *ml, int32_t t_cap,
                              const int32_t *top, int32_t kappa, const void *k_new, const void *v_new,

@@ -133,6 +133,12 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
                          int32_t *edges, int32_t *assign, float *out, const float *part, int32_t *ctr,
                          hipStream_t s);
 
+// The gather with its partials and counters in the library's static scratch.
+size_t noalloc_gather_bytes(const ckv_kv *kv, const ckv_index *idx, int t_cap);
+hipError_t launch_gather_noalloc(const ckv_kv *kv, const ckv_index *idx, const void *q, const int32_t *tok_list,
+                                 const int32_t *tok_n, int t_cap, float sm_scale, float *out, float *logits,
+                                 float *ml, hipStream_t s);
+
 // Attention-mass recall of every graph's heads from the gather's and the
 // dense baseline's softmax states.
 hipError_t launch_recall(const ckv_kv *kv, const ckv_index *idx, const float *ml, const float *dense_ml,

@@ -83,6 +83,8 @@ typedef int32_t ckv_status;
 
 #define CKV_MAX_KAPPA 32
 #define CKV_MAX_C_CAP 16384
+/* Static device scratch of ckv_gather_attend_noalloc (bytes, per GPU). */
+#define CKV_NOALLOC_SCRATCH_BYTES (4u << 20)
 
 /* The paged K/V store of one attention layer (layout above). */
 typedef struct ckv_kv {
@@ -210,6 +212,27 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
                              const int32_t *tok_list, const int32_t *tok_n, int32_t t_cap,
                              float sm_scale, float *out, float *logits, float *ml,
                              void *ws, size_t ws_bytes, ckv_stream_t stream);
+
+/* ckv_gather_attend without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments and results as ckv_gather_attend
+ * in its complete mode (out and ml required, bit-identical outputs), but the
+ * split-K partial records and arrival counters live in a static device array
+ * of the library, CKV_NOALLOC_SCRATCH_BYTES per GPU, held until the process
+ * ends; the call allocates nothing.  The scratch need is 256-aligned
+ * 4 * n_graphs bytes of counters plus 4 * n_graphs * heads_per_graph *
+ * ceil(t_cap / 256) * (32 * ceil((head_dim + 2) / 32)) bytes of records; a
+ * larger need returns CKV_E_WORKSPACE before anything is enqueued.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.  The
+ * stream must belong to the current device.  Each call clears its counters
+ * with a small fill kernel before the gather, so it may be captured and
+ * replayed.  Errors as for ckv_gather_attend; out == NULL or ml == NULL:
+ * CKV_E_INVALID. */
+ckv_status ckv_gather_attend_noalloc(const ckv_kv *kv, const ckv_index *idx, const void *q,
+                                     const int32_t *tok_list, const int32_t *tok_n, int32_t t_cap,
+                                     float sm_scale, float *out, float *logits, float *ml,
+                                     ckv_stream_t stream);
 
 /* Edges, assignment and update (Figure 1 panel (3): the kappa keys the new
  * token attends to most become its edges and decide its community, at a cost

@@ -170,6 +170,24 @@ def test_attention_recall_validation():
     assert f(None, ctypes.byref(idx), FAKE, FAKE, FAKE, None) == ckv.CKV_E_INVALID
 
 
+def test_gather_noalloc_validation():
+    """The no-allocation gather checks its scratch need on the host: too large a
+    shape is CKV_E_WORKSPACE before any device call; out and ml are required."""
+    f = ckv.LIB.ckv_gather_attend_noalloc
+    kv, idx = _kv(), _idx()
+    args = lambda t_cap, out=FAKE, ml=FAKE: (ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, t_cap, 1.0, out,
+                                             FAKE, ml, None)
+    # 32 graphs x 1 head x ceil(t_cap / 256) spans x 160 floats: 4 MiB holds about 204 spans
+    assert f(*args(300_000)) == ckv.CKV_E_WORKSPACE
+    assert f(*args(4100, out=None)) == ckv.CKV_E_INVALID
+    assert f(*args(4100, ml=None)) == ckv.CKV_E_INVALID
+    assert f(*args(0)) == ckv.CKV_E_INVALID
+    gidx = _idx(mode=ckv.CKV_MODE_QUERY_GROUP, n_graphs=64)
+    gkv = _kv(batch=8)
+    big = (ctypes.byref(gkv), ctypes.byref(gidx), FAKE, FAKE, FAKE, 4 * 4100, 1.0, FAKE, FAKE, FAKE, None)
+    assert f(*big) == ckv.CKV_E_WORKSPACE  # 64 graphs x 4 heads x 65 spans: 10.6 MB
+
+
 def test_read_rows_validation():
     kv = _kv()
     f = lambda rows, n, part: ckv.LIB.ckv_read_rows(ctypes.byref(kv), rows, n, part, None)
