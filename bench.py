@@ -219,10 +219,10 @@ def main():
         """One step as its four calls, each stamping row[k] from its dispatch."""
         q = Q[t]
         ckv.ckv_time_next_launch(*row[0])
-        ckv.ckv_score_centroids(kv, idx, q, b.scores)
+        ckv.ckv_score_centroids(kv, idx, q, b.scores, b.ws)
         ckv.ckv_time_next_launch(*row[1])
         ckv.ckv_select_communities(kv, idx, q, b.scores, dec.budget, dec.max_comm, b.sel, b.sel_n, b.top,
-                                   b.tok_list, b.tok_n)
+                                   b.tok_list, b.tok_n, b.ws)
         ckv.ckv_time_next_launch(*row[2])
         out, ml = (None, None) if dec.defer else (b.out, b.ml)
         ckv.ckv_gather_attend(kv, idx, q, b.tok_list, b.tok_n, dec.sm_scale, out, b.logits, ml, b.ws)
@@ -500,10 +500,10 @@ def bench_stack(args, w):
         for li, L in enumerate(stack):
             b, q = L.dec.buf, L.q[t]
             ckv.ckv_time_next_launch(*ev[i][li][0])
-            ckv.ckv_score_centroids(L.kv, L.idx, q, b.scores)
+            ckv.ckv_score_centroids(L.kv, L.idx, q, b.scores, b.ws)
             ckv.ckv_time_next_launch(*ev[i][li][1])
             ckv.ckv_select_communities(L.kv, L.idx, q, b.scores, L.dec.budget, L.dec.max_comm, b.sel, b.sel_n,
-                                       b.top, b.tok_list, b.tok_n)
+                                       b.top, b.tok_list, b.tok_n, b.ws)
             ckv.ckv_time_next_launch(*ev[i][li][2])
             ckv.ckv_gather_attend(L.kv, L.idx, q, b.tok_list, b.tok_n, L.dec.sm_scale, None, b.logits, None, b.ws)
             ckv.ckv_time_next_launch(*ev[i][li][3])

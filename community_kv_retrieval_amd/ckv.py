@@ -68,9 +68,10 @@ def _load():
         "ckv_workspace_bytes": (c_size_t, [KVP, IXP, c_int32]),
         "ckv_kv_write": (c_int32, [KVP, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
         "ckv_index_build": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_size_t, c_void_p]),
-        "ckv_score_centroids": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p]),
+        "ckv_score_centroids": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_select_communities": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p,
-                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+                                             c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                             c_void_p]),
         "ckv_gather_attend": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_int32, c_float, c_void_p,
                                         c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_gather_attend_noalloc": (c_int32, [KVP, IXP, c_void_p, c_void_p, c_void_p, c_int32, c_float,
@@ -229,16 +230,19 @@ def ckv_index_build(kv: KVStore, idx: CommunityIndex, labels_in: torch.Tensor, w
                                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def ckv_score_centroids(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, scores: torch.Tensor, stream=None):
+def ckv_score_centroids(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, scores: torch.Tensor,
+                        ws: torch.Tensor, stream=None):
+    """ws: the workspace the following ckv_select_communities reads the candidates from."""
     _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
     _need(scores, "scores", torch.float32, (idx.n_graphs, idx.c_cap))
     _check("ckv_score_centroids", LIB.ckv_score_centroids(ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q),
-                                                          _ptr(scores), _stream(stream)))
+                                                          _ptr(scores), _ptr(ws), ws.numel() * ws.element_size(),
+                                                          _stream(stream)))
 
 
 def ckv_select_communities(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, scores: torch.Tensor, budget: int,
                            max_comm: int, sel: torch.Tensor, sel_n: torch.Tensor, top: torch.Tensor,
-                           tok_list: torch.Tensor, tok_n: torch.Tensor, stream=None):
+                           tok_list: torch.Tensor, tok_n: torch.Tensor, ws: torch.Tensor, stream=None):
     G = idx.n_graphs
     _need(q, "q", kv.dtype, (kv.batch, kv.n_q_heads, kv.head_dim))
     _need(scores, "scores", torch.float32, (G, idx.c_cap))
@@ -249,7 +253,8 @@ def ckv_select_communities(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, sc
     _need(tok_list, "tok_list", torch.int32, (G, t_cap))
     _check("ckv_select_communities", LIB.ckv_select_communities(
         ctypes.byref(kv.desc), ctypes.byref(idx.desc), _ptr(q), _ptr(scores), budget, max_comm, t_cap, _ptr(sel),
-        _ptr(sel_n), _ptr(top), _ptr(tok_list), _ptr(tok_n), _stream(stream)))
+        _ptr(sel_n), _ptr(top), _ptr(tok_list), _ptr(tok_n), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(stream)))
 
 
 def ckv_gather_attend(kv: KVStore, idx: CommunityIndex, q: torch.Tensor, tok_list: torch.Tensor,
@@ -440,9 +445,9 @@ class Decoder:
 
     def retrieve(self, q: torch.Tensor, stream=None):
         b = self.buf
-        ckv_score_centroids(self.kv, self.idx, q, b.scores, stream)
+        ckv_score_centroids(self.kv, self.idx, q, b.scores, b.ws, stream)
         ckv_select_communities(self.kv, self.idx, q, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
-                               b.tok_list, b.tok_n, stream)
+                               b.tok_list, b.tok_n, b.ws, stream)
 
     def attend(self, q: torch.Tensor, stream=None):
         """With defer set, out and ml are written by the following update()."""
@@ -473,11 +478,11 @@ class Decoder:
                 s.wait_event(prev)
             for t in (q, k_new, v_new):
                 t.record_stream(s)
-            ckv_score_centroids(kv, view, q, b.scores, s)
+            ckv_score_centroids(kv, view, q, b.scores, b.ws, s)
             prev = torch.cuda.Event()
             prev.record(s)
             ckv_select_communities(kv, view, q, b.scores, self.budget, self.max_comm, b.sel, b.sel_n, b.top,
-                                   b.tok_list, b.tok_n, s)
+                                   b.tok_list, b.tok_n, b.ws, s)
             out, ml = (None, None) if self.defer else (b.out, b.ml)
             ckv_gather_attend(kv, view, q, b.tok_list, b.tok_n, self.sm_scale, out, b.logits, ml, b.ws, s)
             ckv_assign_update(kv, view, b.tok_list, b.tok_n, b.logits, b.ml, b.top, self.kappa, k_new, v_new,

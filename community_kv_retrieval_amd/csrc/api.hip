@@ -64,7 +64,7 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 6; }
+int32_t ckv_abi_version(void) { return 7; }
 
 ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;
@@ -133,18 +133,20 @@ ckv_status ckv_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t
 }
 
 ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const void *q, float *scores,
-                               ckv_stream_t stream) {
+                               void *ws, size_t ws_bytes, ckv_stream_t stream) {
     ckv_status st = check_kv(kv);
     if (st != CKV_OK) return st;
     if ((st = check_index(kv, idx)) != CKV_OK) return st;
     if (!q || !scores) return CKV_E_INVALID;
-    return hip_status(launch_score(kv, idx, q, scores, (hipStream_t)stream));
+    const WsLayout L = ws_layout(kv, idx, 0);
+    if (!ws || ws_bytes < L.total) return CKV_E_WORKSPACE;
+    return hip_status(launch_score(kv, idx, q, scores, cand_arrays(ws, L, idx), (hipStream_t)stream));
 }
 
 ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const void *q,
                                   const float *scores, int32_t budget, int32_t max_comm, int32_t t_cap,
                                   int32_t *sel, int32_t *sel_n, int32_t *top, int32_t *tok_list,
-                                  int32_t *tok_n, ckv_stream_t stream) {
+                                  int32_t *tok_n, void *ws, size_t ws_bytes, ckv_stream_t stream) {
     ckv_status st = check_kv(kv);
     if (st != CKV_OK) return st;
     if ((st = check_index(kv, idx)) != CKV_OK) return st;
@@ -152,8 +154,10 @@ ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const 
     if (budget < 0 || max_comm < 0) return CKV_E_INVALID;
     const long long need = (long long)idx->n_sinks + (budget < idx->l_cap ? budget : idx->l_cap);
     if (t_cap < need) return CKV_E_INVALID;
+    const WsLayout L = ws_layout(kv, idx, 0);
+    if (!ws || ws_bytes < L.total) return CKV_E_WORKSPACE;
     return hip_status(launch_select(kv, idx, q, scores, budget, max_comm, t_cap, sel, sel_n, top, tok_list,
-                                    tok_n, (hipStream_t)stream));
+                                    tok_n, cand_arrays(ws, L, idx), (hipStream_t)stream));
 }
 
 ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void *q,

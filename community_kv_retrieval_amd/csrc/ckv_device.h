@@ -36,6 +36,12 @@ __device__ unsigned long long g_block_trace[kBlockTraceBlocks * 8];
                     __builtin_amdgcn_s_getreg((31 << 11) | 4);                              \
         }                                                                                   \
     } while (0)
+// Event counter in slot s of the phase array (profiling builds: e.g. how often
+// a fast path falls back), bumped once per block.
+#define CKV_TCOUNT(s)                                                                 \
+    do {                                                                              \
+        if (threadIdx.x == 0) atomicAdd(&::ckv::g_phase_trace[(s)], 1ull);            \
+    } while (0)
 // Per-wave stamps of block 0 (slot s of wave w at index 16 s + w).
 #define CKV_WMARK(s)                                                                          \
     do {                                                                                      \
@@ -43,6 +49,9 @@ __device__ unsigned long long g_block_trace[kBlockTraceBlocks * 8];
             ::ckv::g_block_trace[16 * (s) + (threadIdx.x >> 6)] = __builtin_amdgcn_s_memrealtime(); \
     } while (0)
 #else
+#define CKV_TCOUNT(s) \
+    do {              \
+    } while (0)
 #define CKV_WMARK(s) \
     do {             \
     } while (0)
@@ -246,6 +255,17 @@ __device__ __forceinline__ int16_t screen_code(float v, float scale) {
     if (!(scale > 0.f)) return 0;
     const float r = fminf(kScreenMax, fmaxf(-kScreenMax, rintf(v / scale)));
     return (int16_t)(int)r;
+}
+
+// Screening bound factor, in units of cscale * |qbar|_1: 1/2 + 2^-9 for the
+// rounding of the int16 codes, 32767 (D + 1) 2^-24 < 0.252 for the float32
+// accumulation of D <= 128 products |q_d| * 32767 and for rounding qbar to
+// float32, with slack.  A screening score s~ then lies within
+// E = cscale * |qbar|_1 * kScreenK + 2^-20 |s~| of the exact score (the last
+// term for the float32 roundings of s~, of the exact score and of s~ +- E).
+constexpr float kScreenK = 0.76f;
+__device__ __forceinline__ float screen_bound(float s, float cscale, float kq) {
+    return cscale * kq + fabsf(s) * 0x1p-20f;
 }
 
 // Order-preserving map of a float32 onto uint32 (larger float, larger code).

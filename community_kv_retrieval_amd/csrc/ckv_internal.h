@@ -75,10 +75,32 @@ struct WsLayout {
     size_t ctr_dense, part_dense;              // dense baseline
     size_t dense_total;                        // bytes the dense baseline needs
     size_t ctr_gather, ctr_assign;             // int32 counters (byte offsets)
+    size_t cand, cand_end;                     // selection candidates (scoring -> selection)
     size_t part_gather;                        // float partials
     size_t build_cursor;                       // int32 [G][c_cap]
     size_t total;
 };
+
+// Selection candidates.  The scoring kernel keeps, of every wave's 64
+// communities, the kCandPerWave of largest upper screening bound U, and the
+// largest U it leaves out (at 128K about 2 communities per wave matter to the
+// cut, so 15 are left out of the candidates only in degenerate cases); the selection works on those unless a left-out
+// community could matter.  Per graph: (c_cap / 256) tiles x 4 waves x
+// kCandPerWave records of (id, U, L, size, first base member, base members),
+// id -1 for an empty slot, and one left-out maximum per wave.
+constexpr int kCandPerWave = 15;
+inline int cand_per_graph(int c_cap) { return c_cap / 256 * 4 * kCandPerWave; }
+struct CandArrays {
+    int32_t *id;
+    float *u, *l;
+    int32_t *sz, *o0, *len;
+    float *ex;  // [G][ncand / kCandPerWave]
+    int ncand;  // per graph
+};
+inline size_t cand_bytes(const ckv_index *idx) {
+    const size_t n = (size_t)idx->n_graphs * cand_per_graph(idx->c_cap);
+    return 6 * 4 * n + 4 * (n / kCandPerWave);
+}
 
 // idx == nullptr: only the dense baseline's part.
 inline WsLayout ws_layout(const ckv_kv *kv, const ckv_index *idx, int t_cap) {
@@ -99,6 +121,9 @@ inline WsLayout ws_layout(const ckv_kv *kv, const ckv_index *idx, int t_cap) {
     L.ctr_gather = off;
     L.ctr_assign = off + 4 * G;
     off = align256(off + 4 * G + 4);
+    L.cand = off;
+    off += align256(cand_bytes(idx));
+    L.cand_end = off;
     L.part_gather = off;
     off += align256(4 * G * heads_per_graph(kv, idx) * (size_t)ceil_div(t_cap > 0 ? t_cap : 1, kGatherTokens) * D2);
     L.build_cursor = off;
@@ -107,16 +132,31 @@ inline WsLayout ws_layout(const ckv_kv *kv, const ckv_index *idx, int t_cap) {
     return L;
 }
 
+inline CandArrays cand_arrays(void *ws, const WsLayout &L, const ckv_index *idx) {
+    CandArrays c;
+    c.ncand = cand_per_graph(idx->c_cap);
+    const size_t n = (size_t)idx->n_graphs * c.ncand;
+    char *b = static_cast<char *>(ws) + L.cand;
+    c.id = reinterpret_cast<int32_t *>(b);
+    c.u = reinterpret_cast<float *>(c.id + n);
+    c.l = c.u + n;
+    c.sz = reinterpret_cast<int32_t *>(c.l + n);
+    c.o0 = c.sz + n;
+    c.len = c.o0 + n;
+    c.ex = reinterpret_cast<float *>(c.len + n);
+    return c;
+}
+
 // Launchers (each returns the hipError_t of its launches).
 hipError_t launch_kv_write(const ckv_kv *kv, int b, int kh, int pos0, int n, const void *k,
                            const void *v, hipStream_t s);
 hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t *labels_in,
                               int32_t *cursor, hipStream_t s);
 hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, float *scores,
-                        hipStream_t s);
+                        const CandArrays &cand, hipStream_t s);
 hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, const float *scores, int budget,
                          int max_comm, int t_cap, int32_t *sel, int32_t *sel_n, int32_t *top,
-                         int32_t *tok_list, int32_t *tok_n, hipStream_t s);
+                         int32_t *tok_list, int32_t *tok_n, const CandArrays &cand, hipStream_t s);
 hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
                          const int32_t *tok_list, const int32_t *tok_n, int t_cap, float sm_scale,
                          float *out, float *logits, float *ml, float *part, int32_t *ctr,

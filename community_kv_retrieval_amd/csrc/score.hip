@@ -18,6 +18,11 @@
 // instruction reads 512 consecutive bytes of one dimension's row.  The four
 // waves of a block split the dimensions and add their partial sums in a fixed
 // order.  Empty communities and ids >= n_comm score -inf.
+//
+// Each wave also hands the selection its candidates: of its 64 communities,
+// the kCandPerWave with the largest upper bound U = s~ + E of the exact score
+// (E the screening bound), with their bounds, sizes and base-member ranges,
+// and the largest U among the ones it leaves out.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -31,7 +36,9 @@ struct ScoreParams {
     const float *cscale;
     const int32_t *size;
     const int32_t *n_comm;
+    const int32_t *offs;
     float *scores;
+    CandArrays cand;
     int mode, Hq, Hkv, c_cap, g0, count;  // count: graphs in the launch window
 };
 
@@ -75,6 +82,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     const int sz = p.size[(size_t)g * p.c_cap + c];
     const float scl = p.cscale[(size_t)g * p.c_cap + c];
     const int nc = min(p.n_comm[g], p.c_cap);
+    // base members of c: offs[c] .. offs[c + 1] (the offsets row holds c_cap + 4 entries)
+    const int32_t *orow = p.offs + (size_t)g * offs_stride(p.c_cap) + c;
+    const int m0 = orow[0], m1 = orow[1];
     if (tid < D) {  // the head sum in float64, heads in order
         double qs = 0.0;
 #pragma unroll
@@ -97,15 +107,54 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     for (int k = 0; k < 4; ++k) s_part[wave][4 * lane + k] = acc[k];
     lds_barrier();
     const float sum = ((s_part[0][tid] + s_part[1][tid]) + s_part[2][tid]) + s_part[3][tid];
-    p.scores[(size_t)g * p.c_cap + c] = (c < nc && sz > 0) ? scl * sum : kNegInf;
+    const bool live = c < nc && sz > 0;
+    const float sv = live ? scl * sum : kNegInf;
+    p.scores[(size_t)g * p.c_cap + c] = sv;
+
+    // Selection candidates of this wave's 64 communities: the kCandPerWave of
+    // largest U = s~ + E (ties: lower lane), and the largest U left out.  The
+    // kCandPerWave-th largest key is found bit by bit from the top (a count of
+    // the lanes at or above each trial threshold), so no sort is needed.
+    float qa = fabsf(s_q[lane]);
+    if constexpr (D > 64) qa += fabsf(s_q[lane + 64]);
+    const float kq = wave_sum_f(qa) * kScreenK;
+    const float e = screen_bound(sv, scl, kq);
+    const float up = sv + e, lw = sv - e;
+    const uint32_t key = live ? ordered_bits(up) : 0u;
+    uint32_t thr = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = thr | (1u << bit);
+        const unsigned long long m = __ballot(key >= t);  // counted as two 32-bit halves: a scalar compare
+        if (__builtin_popcount((uint32_t)m) + __builtin_popcount((uint32_t)(m >> 32)) >= kCandPerWave) thr = t;
+    }
+    const bool gt = live && key > thr, eq = live && key == thr;
+    const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;  // lanes under this one
+    const int ngt = __popcll(__ballot(gt));
+    const bool take = gt || (eq && __popcll(__ballot(eq) & below) < kCandPerWave - ngt);
+    const unsigned long long mt = __ballot(take);
+    const int ntake = __popcll(mt);
+    const float exv = wave_max_f(live && !take ? up : kNegInf);
+    const int nw = p.cand.ncand / kCandPerWave;  // waves per graph
+    const size_t cbase = (size_t)g * p.cand.ncand + ((size_t)tile * 4 + wave) * kCandPerWave;
+    if (take) {
+        const size_t k = cbase + __popcll(mt & below);
+        p.cand.id[k] = c;
+        p.cand.u[k] = up;
+        p.cand.l[k] = lw;
+        p.cand.sz[k] = sz;
+        p.cand.o0[k] = m0;
+        p.cand.len[k] = m1 - m0;
+    }
+    if (lane >= ntake && lane < kCandPerWave) p.cand.id[cbase + lane] = -1;
+    if (lane == 0) p.cand.ex[(size_t)g * nw + tile * 4 + wave] = exv;
     CKV_TMARK(1);
 }
 
 hipError_t launch_score(const ckv_kv *kv, const ckv_index *idx, const void *q, float *scores,
-                        hipStream_t s) {
+                        const CandArrays &cand, hipStream_t s) {
     const Window w = window_of(idx);
-    ScoreParams p{q, idx->cq, idx->cscale, idx->size, idx->n_comm, scores, idx->mode, kv->n_q_heads,
-                  kv->n_kv_heads, idx->c_cap, w.first, w.count};
+    ScoreParams p{q, idx->cq, idx->cscale, idx->size, idx->n_comm, idx->offs, scores, cand, idx->mode,
+                  kv->n_q_heads, kv->n_kv_heads, idx->c_cap, w.first, w.count};
     const dim3 grid(ceil_div(idx->c_cap, kScoreTile) * w.count);
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
     if (kv->head_dim == 128) {

@@ -171,9 +171,13 @@ ckv_status ckv_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t
  * scores[G][c_cap] = cscale[c] * sum_d float32(qbar_d) * cq[d][c] (float32),
  * within cscale[c] * |qbar|_1 * 0.76 + 2^-20 |score| of the exact score, and
  * -inf for empty communities and ids >= n_comm[g].  ckv_select_communities
- * resolves the ranking exactly from these bounds. */
+ * resolves the ranking exactly from these bounds.  It also leaves in ws the
+ * selection's candidates (of every 64 consecutive communities the 16 of
+ * largest upper bound, and the largest bound left out), which the next
+ * ckv_select_communities on the same ws reads: ws must hold at least
+ * ckv_workspace_bytes(kv, idx, 0) bytes (CKV_E_WORKSPACE otherwise). */
 ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const void *q,
-                               float *scores, ckv_stream_t stream);
+                               float *scores, void *ws, size_t ws_bytes, ckv_stream_t stream);
 
 /* Retrieve communities under the token budget (Figure 1 panel (3): a subset
  * of the communities is retrieved; Tables 2-3: the subset is bounded by a
@@ -188,11 +192,17 @@ ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const voi
  * Outputs per graph: sel[G][c_cap] taken ids ascending, sel_n[G] their count,
  * top[G] the best-ranked non-empty community (-1 if none), tok_list[G][t_cap]
  * the attended positions (sinks first, then members of the taken communities)
- * and tok_n[G] their count.  Requires t_cap >= n_sinks + min(budget, l_cap). */
+ * and tok_n[G] their count.  Requires t_cap >= n_sinks + min(budget, l_cap).
+ * ws: the workspace the preceding ckv_score_centroids for the same q wrote its
+ * candidates to (at least ckv_workspace_bytes(kv, idx, 0) bytes).  The
+ * selection works on the candidates when they provably hold every community
+ * the result depends on, and on every community otherwise; the result is the
+ * same either way. */
 ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const void *q,
                                   const float *scores, int32_t budget, int32_t max_comm, int32_t t_cap,
                                   int32_t *sel, int32_t *sel_n, int32_t *top,
-                                  int32_t *tok_list, int32_t *tok_n, ckv_stream_t stream);
+                                  int32_t *tok_list, int32_t *tok_n, void *ws, size_t ws_bytes,
+                                  ckv_stream_t stream);
 
 /* Exact softmax attention of each graph's query heads over its token list
  * (Figure 1 panel (3): attention over the retrieved subset is exact and also

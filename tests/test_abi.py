@@ -36,13 +36,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ckv.LIB.ckv_abi_version() == 6
+    assert ckv.LIB.ckv_abi_version() == 7
     for code in (0, -1, -2, -3, -4):
         assert ckv.ckv_status_str(code) != "unknown status"
     assert ckv.ckv_status_str(7) == "unknown status"
 
 
 FAKE = 0x10000  # never dereferenced: validation fails or succeeds before any device call
+BIG = 1 << 40  # a workspace size large enough for any shape here
 
 
 def _kv(**kw):
@@ -91,7 +92,7 @@ def test_workspace_bytes():
 ])
 def test_kv_validation(kw, code):
     kv, idx = _kv(**kw), _idx()
-    r = ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None)
+    r = ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, BIG, None)
     assert r == code
 
 
@@ -100,14 +101,14 @@ def test_kv_validation(kw, code):
                                 dict(status=None), dict(csum=None), dict(cq=None), dict(cscale=None)])
 def test_index_validation(kw):
     kv, idx = _kv(), _idx(**kw)
-    assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == ckv.CKV_E_INVALID
+    assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, BIG, None) == ckv.CKV_E_INVALID
 
 
 @pytest.mark.parametrize("first,count", [(0, -1), (-1, 4), (1, 0), (30, 3), (32, 1)])
 def test_window_validation(first, count):
     kv, idx = _kv(), _idx(win_first=first, win_count=count)
     for f in (ckv.LIB.ckv_score_centroids,):
-        assert f(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == ckv.CKV_E_INVALID
+        assert f(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, BIG, None) == ckv.CKV_E_INVALID
 
 
 def test_window_view_binding():
@@ -126,12 +127,27 @@ def test_select_validation():
     kv, idx = _kv(), _idx()
     f = ckv.LIB.ckv_select_communities
     args = lambda budget, mc, tcap, sel=FAKE, q=FAKE: (ctypes.byref(kv), ctypes.byref(idx), q, FAKE, budget, mc,
-                                                       tcap, sel, FAKE, FAKE, FAKE, FAKE, None)
+                                                       tcap, sel, FAKE, FAKE, FAKE, FAKE, FAKE, BIG, None)
     assert f(*args(4096, 0, 4099)) == ckv.CKV_E_INVALID   # t_cap below sinks + budget
     assert f(*args(-1, 0, 4100)) == ckv.CKV_E_INVALID
     assert f(*args(4096, -2, 4100)) == ckv.CKV_E_INVALID
     assert f(*args(4096, 0, 4100, sel=None)) == ckv.CKV_E_INVALID
     assert f(*args(4096, 0, 4100, q=None)) == ckv.CKV_E_INVALID
+
+
+def test_score_select_need_the_candidate_workspace():
+    """Scoring leaves the selection's candidates in the workspace: both calls
+    refuse a workspace smaller than ckv_workspace_bytes(kv, idx, 0)."""
+    kv, idx = _kv(), _idx()
+    need = _ws(kv, idx, 0)
+    score = lambda ws, nb: ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, ws, nb, None)
+    sel = lambda ws, nb: ckv.LIB.ckv_select_communities(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, 4096, 0,
+                                                        4100, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nb, None)
+    for f in (score, sel):
+        assert f(None, need) == ckv.CKV_E_WORKSPACE
+        assert f(FAKE, need - 1) == ckv.CKV_E_WORKSPACE
+    # 32 graphs x 33 tiles x 64 candidates of 24 bytes, one left-out maximum per 16
+    assert need >= _ws(kv, None, 0) + 32 * 8192 // 256 * 64 * 24
 
 
 def test_gather_assign_dense_workspace_checks():
@@ -229,7 +245,7 @@ def test_time_next_launch_arming():
     # armed events are only consumed by a launch; validation failures launch nothing
     assert f(FAKE, FAKE) == ckv.CKV_OK
     kv, idx = _kv(head_dim=96), _idx()
-    assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, None) == \
+    assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, BIG, None) == \
         ckv.CKV_E_UNSUPPORTED
     assert f(None, None) == ckv.CKV_OK
 
