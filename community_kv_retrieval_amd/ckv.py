@@ -176,7 +176,7 @@ class CommunityIndex:
         self.tail_len = torch.zeros((G,), **i32)
         self.csum = torch.zeros((G, c_cap, D), dtype=torch.float64, device=device)
         self.cent = torch.zeros((G, D, c_cap), dtype=torch.float32, device=device)
-        self.cq = torch.zeros((G, D, c_cap), dtype=torch.int16, device=device)
+        self.cq = torch.zeros((G, c_cap // 256, D, 256), dtype=torch.int16, device=device)  # tile-major
         self.cscale = torch.zeros((G, c_cap), dtype=torch.float32, device=device)
         self.status = torch.zeros((1,), **i32)
         self.desc = CkvIndex(mode, G, c_cap, l_cap, tail_cap, n_sinks, *[

@@ -408,7 +408,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
     __syncthreads();
     if (join) {
         const float scale = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])) / kScreenMax;
-        if (tid < D) p.cq[((size_t)g * D + tid) * p.c_cap + a] = screen_code(cv, scale);
+        if (tid < D) p.cq[cq_offset(g, tid, a, D, p.c_cap)] = screen_code(cv, scale);
         if (tid == 0) p.cscale[(size_t)g * p.c_cap + a] = scale;
     }
     if (tid == 0) {

@@ -268,6 +268,13 @@ __device__ __forceinline__ float screen_bound(float s, float cscale, float kq) {
     return cscale * kq + fabsf(s) * 0x1p-20f;
 }
 
+// Element (graph g, dim d, community c) of the int16 screening copy, stored
+// tile-major: [graph][c_cap / 256][dim][256], so the 256 communities a scoring
+// block reads are one contiguous 256 * D * 2-byte region.
+__device__ __forceinline__ size_t cq_offset(int g, int d, int c, int D, int c_cap) {
+    return (((size_t)g * (c_cap >> 8) + (c >> 8)) * D + d) * 256 + (c & 255);
+}
+
 // Order-preserving map of a float32 onto uint32 (larger float, larger code).
 __device__ __forceinline__ uint32_t ordered_bits(float s) {
     const uint32_t u = __float_as_uint(s);

@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
     if ((tid & 63) == 0) s_max[tid >> 6] = m;
     __syncthreads();
     const float scale = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3])) / kScreenMax;
-    if (tid < D) p.cq[((size_t)g * D + tid) * p.c_cap + c] = screen_code(cv, scale);
+    if (tid < D) p.cq[cq_offset(g, tid, c, D, p.c_cap)] = screen_code(cv, scale);
     if (tid == 0) p.cscale[(size_t)g * p.c_cap + c] = scale;
 }
 

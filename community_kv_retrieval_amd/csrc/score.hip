@@ -13,9 +13,10 @@
 //
 // The screening copy is half the float32 table and streamed once from HBM, so
 // the kernel is bandwidth-bound and runs on the vector units, not the matrix
-// cores.  The table is stored transposed, [graph][dim][community], so lane j of
-// a wave owns communities 4j..4j+3 of a 256-wide tile and every wave
-// instruction reads 512 consecutive bytes of one dimension's row.  The four
+// cores.  The table is stored transposed and tile-major, [graph][tile of 256
+// communities][dim][256], so lane j of a wave owns communities 4j..4j+3 of a
+// tile, every wave instruction reads 512 consecutive bytes of one dimension's
+// row, and a block streams one contiguous region.  The four
 // waves of a block split the dimensions and add their partial sums in a fixed
 // order.  Empty communities and ids >= n_comm score -inf.
 //
@@ -74,10 +75,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
         for (int h = 0; h < kMaxHeads; ++h) qv[h] = q[(size_t)min(h, gc.nh - 1) * D];
     }
     constexpr int DW = D / 4;
-    const int16_t *base = p.cq + ((size_t)g * D + wave * DW) * p.c_cap + c0 + 4 * lane;
+    const int16_t *base = p.cq + cq_offset(g, wave * DW, c0, D, p.c_cap) + 4 * lane;
     int2 v[DW];
 #pragma unroll
-    for (int j = 0; j < DW; ++j) v[j] = *reinterpret_cast<const int2 *>(base + (size_t)j * p.c_cap);
+    for (int j = 0; j < DW; ++j) v[j] = *reinterpret_cast<const int2 *>(base + (size_t)j * 256);
     const int c = c0 + tid;  // kScoreTile == blockDim: one output per thread
     const int sz = p.size[(size_t)g * p.c_cap + c];
     const float scl = p.cscale[(size_t)g * p.c_cap + c];

@@ -81,11 +81,13 @@ def check_index_state(layer, orc: O.Oracle, w: synth.Workload, full: bool = Fals
 
 
 def check_screening_copy(idx, g: int, C: int, cent: np.ndarray):
-    """The int16 screening copy of the centroid table: per community
-    scale = max |cent| / 32767 (float32) and code = round(cent / scale),
-    clamped to +-32767 (0 for a zero column), as the library documents it."""
+    """The int16 screening copy of the centroid table (stored tile-major,
+    [c_cap / 256][D][256] per graph): per community scale = max |cent| / 32767
+    (float32) and code = round(cent / scale), clamped to +-32767 (0 for a zero
+    column), as the library documents it."""
     scale = idx.cscale[g, :C].cpu().numpy()
-    code = idx.cq[g, :, :C].t().cpu().numpy().astype(np.int32)
+    D = idx.cq.shape[2]
+    code = idx.cq[g].permute(1, 0, 2).reshape(D, -1)[:, :C].t().cpu().numpy().astype(np.int32)
     want_scale = (np.abs(cent).max(axis=1).astype(np.float32) / np.float32(32767)).astype(np.float32)
     np.testing.assert_array_equal(scale, want_scale, err_msg=f"cscale g={g}")
     with np.errstate(divide="ignore", invalid="ignore"):

@@ -82,6 +82,20 @@ def test_long_token_lists(n_ctx, budget):
     PY.run_steps(w, 18, w.steps, check_dense=budget > n_ctx)
 
 
+@pytest.mark.parametrize("mode", [synth.PER_HEAD, synth.GROUP])
+@pytest.mark.parametrize("budget", [2500, 4200])
+def test_selection_beyond_the_candidates(mode, budget):
+    """Budgets near half of a 9000-token context: about half of every group of
+    64 communities bears on the cut, more than the 15 candidates the scoring
+    kernel keeps per group, so the selection falls back from the candidates to
+    every community (with the cut still inside the walk: the L walk overflows);
+    a budget of 2500 mixes groups that fit in their candidates and groups
+    that do not."""
+    w = small_per_head(mode=mode, n_ctx=9000, budget=budget, steps=3)
+    PY.log(f"selection beyond the candidates {mode} budget {budget}")
+    PY.run_steps(w, 9, w.steps)
+
+
 def test_community_cap():
     w = small_per_head(n_ctx=3000, budget=1 << 20, max_comm=5, steps=3)
     PY.log("max_comm 5")
