@@ -52,6 +52,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-group", action="store_true", help="skip the batch-8 query-group leg")
     ap.add_argument("--recall-steps", type=int, default=16,
                     help="steps per budget of the attention-mass recall sweep (0: skip)")
     ap.add_argument("--profile", action="store_true", help="only warm-up + timed steps (for rocprofv3 runs)")
@@ -102,6 +103,7 @@ def main():
     VN = torch.stack([s.v_new for s in steps_in]).cuda()
     torch.cuda.synchronize()
     log(f"[bench] setup {time.time() - t0:.1f}s; G={idx.n_graphs} c_cap={idx.c_cap} t_cap={buf.t_cap}")
+    aux = aux_memory(kv, idx)
 
     snap = (idx.state_dict(), kv.kv.clone(), kv.seq_len.clone())
 
@@ -111,8 +113,158 @@ def main():
         kv.seq_len.copy_(snap[2])
         torch.cuda.synchronize()
 
-    # Accounting pass: tokens gathered per step (results are deterministic,
-    # so the timed passes below gather exactly these).
+    if args.profile:
+        passes = time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=True, eager_only=args.eager_only)
+        return
+    L = time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore)
+    gathered, score_bytes, row_bytes = L["gathered"], L["score_bytes"], L["row_bytes"]
+    ref = L["ref"]
+
+    # Host-input pass: the same steps launched eagerly, each step's query and
+    # new key/value rows first copied from pinned host memory (a caller that
+    # holds them on the host).  Compare with the eager rate; never the headline.
+    restore()
+    Qh, KNh, VNh = (torch.empty(x.shape, dtype=x.dtype, pin_memory=True) for x in (Q, KN, VN))
+    for hx, dx in ((Qh, Q), (KNh, KN), (VNh, VN)):
+        hx.copy_(dx)
+    qd, knd, vnd = torch.empty_like(Q[0]), torch.empty_like(KN[0]), torch.empty_like(VN[0])
+    for t in range(W):
+        dec.step(Q[t], KN[t], VN[t])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(W, total):
+        qd.copy_(Qh[t], non_blocking=True)
+        knd.copy_(KNh[t], non_blocking=True)
+        vnd.copy_(VNh[t], non_blocking=True)
+        dec.step(qd, knd, vnd)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_host = e0.elapsed_time(e1) / K
+    got = (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)
+    assert all(torch.equal(a, b) for a, b in zip(ref, got)), "host-input steps differ from the eager steps"
+    host_bytes = int(Q[0].numel() * Q.element_size() + 2 * KN[0].numel() * KN.element_size())
+    del Qh, KNh, VNh
+
+    ceiling = read_ceiling(w, kv, idx, buf, row_bytes, K)
+    dense = None if args.no_dense else dense_baseline(w, dec, kv, Q[W], restore)
+
+    # Attention-mass recall (the page's Figure 3 quality proxy): the share of
+    # each head's dense softmax mass that the attended tokens carry, per budget.
+    recall = None
+    if args.recall_steps > 0:
+        recall = {}
+        budget0 = dec.budget
+        dec.defer = False  # recall reads the gather's ml before the update
+        dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
+        dout = torch.empty_like(buf.out)
+        for B in [b for b in (128, 512, 1024, 2048, 4096) if b <= budget0]:
+            restore()
+            dec.budget = B
+            vals = []
+            for t in range(min(args.recall_steps, total)):
+                dec.retrieve(Q[t])
+                dec.attend(Q[t])
+                dec.dense(Q[t], dout, ml=dml)
+                vals.append(dec.recall(dml).flatten())
+                dec.update(KN[t], VN[t])
+            v = torch.cat(vals).cpu().numpy()
+            recall[str(B)] = {"mean": round(float(v.mean()), 4), "p10": round(float(np.percentile(v, 10)), 4),
+                              "min": round(float(v.min()), 4)}
+        dec.budget = budget0
+        dec.defer = not args.no_defer
+
+    prefill = None
+    if not args.no_prefill:
+        prefill = bench_prefill(w, args.seed, kv, slices,
+                                cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.seed, slices, steps_in, args.cpu_seconds)
+    del layer, dec, buf, idx, kv, snap, Q, KN, VN
+    torch.cuda.empty_cache()
+
+    group = None
+    if not args.no_group and w.name == "llama31_8b_128k":
+        group = bench_group(args, synth.preset("llama31_8b_128k_group_b8"), W, K)
+
+    src_hash = gather_source_hash()
+    traffic = measured_traffic(w.name, src_hash)
+    cold_step_us = float(L["cold_us"].mean())
+    res = {
+        "metric": METRIC,
+        "value": round(1e6 / cold_step_us, 1),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(cold_step_us * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "ctx": w.n_ctx, "budget": w.budget, "kappa": w.kappa,
+                   "graphs": "per_query_head" if w.mode == synth.PER_HEAD else "query_group",
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "kv_dtype": w.dtype, "n_graphs": L["n_graphs"], "seed": args.seed,
+                   "windows": args.windows, "deferred_combine": not args.no_defer},
+        "timing": "each of the K steps timed alone after a 512 MB read that evicts the 256 MB MALL (cold); "
+                  "'warm' is the same K steps replayed back to back as one HIP graph",
+        "step_us": L["step_us"],
+        "warm": {"steps_per_s": round(1e3 / L["ms_warm"], 1), "ms_per_step": round(L["ms_warm"], 5),
+                 "ms_per_step_eager": round(L["ms_eager"], 5), "launch": "hip_graph"},
+        "gathered_kv_gbps": L["gather"]["cold"]["gbps"],
+        "gathered_kv_frac_of_hbm": L["gather"]["cold"]["frac"],
+        "roofline": {"bound": "hbm", "kernel": "gather_attend", "achieved": L["gather"]["cold"]["gbps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": L["gather"]["cold"]["frac"],
+                     "traffic": traffic, "bytes_per_launch": int(gathered.mean()),
+                     "avg_launch_us": L["gather"]["cold"]["avg_launch_us"], "kernel_sources": src_hash,
+                     "mall": "flushed", "warm": L["gather"]["warm"],
+                     "read_ceiling_gbps": ceiling["gbps"],
+                     "frac_of_read_ceiling_warm": round(L["gather"]["warm"]["gbps"] / ceiling["gbps"], 4)},
+        "read_ceiling": ceiling,
+        "score_roofline": {"bound": "hbm", "kernel": "score_centroids", "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "bytes_per_launch": score_bytes, "cold": L["score"]["cold"], "warm": L["score"]["warm"]},
+        "breakdown_us": L["breakdown_cold"],
+        "breakdown_us_warm": L["breakdown_warm"],
+        "tokens_per_step": round(float(L["tok"][W:].sum(axis=1).mean()), 1),
+        "aux_memory": aux,
+        "dense_flash_decode": dense,
+        "attention_mass_recall": recall,
+        "prefill_graph": prefill,
+        "group_b8": group,
+        "cpu_baseline": cpu,
+        "host_inputs": {"ms_per_step": round(ms_host, 5), "steps_per_s": round(1e3 / ms_host, 1),
+                        "bytes_per_step": host_bytes,
+                        "how": "eager launches; q, k_new and v_new copied from pinned host memory before each step"},
+        "launch": "eager per step (cold); hip_graph (warm)",
+        "wall_s_timed": L["wall_s"],
+    }
+    if dense is not None:
+        res["dense_flash_decode"]["dense_over_sparse_step_cold"] = round(dense["us_per_call"] / cold_step_us, 3)
+        res["dense_flash_decode"]["dense_over_sparse_step_warm"] = round(dense["us_per_call"] / (L["ms_warm"] * 1e3), 3)
+    print(json.dumps(res), flush=True)
+
+
+STEP_KERNELS = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
+
+
+def time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=False, eager_only=False):
+    """Every timing pass of one layer over steps W .. W + K - 1 (after W
+    untimed warm-up steps, from the same restored state each time):
+    accounting (tokens gathered per step), eager, the K steps captured as one
+    HIP graph and replayed (warm; must equal the eager pass bit for bit),
+    each kernel stamped from its own dispatch (warm), and the cold passes
+    (a 512 MB read before every step evicts the 256 MB MALL: whole steps, and
+    per kernel)."""
+    import numpy as np
+    import torch
+
+    from community_kv_retrieval_amd import ckv
+    total = W + K
+    buf = dec.buf
     restore()
     tok = []
     for t in range(total):
@@ -124,7 +276,7 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     row_bytes = 2 * w.head_dim * esz  # K row + V row
     gathered = tok[W:].sum(axis=1) * row_bytes  # bytes per timed step
-    n_comm = np.array(synth.graph_n_comm(w, slices), dtype=np.int64)
+    n_comm = np.array(idx.n_comm.cpu().numpy(), dtype=np.int64)
     # the scoring kernel streams the int16 screening copy of every used
     # centroid column plus its scale and member count
     score_bytes = int(n_comm.sum()) * (w.head_dim * 2 + 8)
@@ -142,13 +294,12 @@ def main():
     torch.cuda.synchronize()
     ms_eager = e0.elapsed_time(e1) / K
     ref = [x.clone() for x in (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)]
-    if args.profile and args.eager_only:
+    if profile and eager_only:
         log(f"[bench] profile run (eager only): {ms_eager * 1e3:.1f} us/step")
-        return
+        return None
 
-    # Headline pass: the same K steps captured once as one HIP graph (how a
-    # decode loop is launched in serving) and replayed, bracketed by
-    # synchronisation.  The replay must reproduce the eager pass bit for bit.
+    # Warm pass: the same K steps captured once as one HIP graph and replayed,
+    # bracketed by synchronisation; it must reproduce the eager pass bit for bit.
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
@@ -161,49 +312,20 @@ def main():
     idx.load_state_dict(snap_w[0])
     kv.kv.copy_(snap_w[1])
     kv.seq_len.copy_(snap_w[2])
+    del snap_w
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     e0.record()
     graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = e0.elapsed_time(e1) / K
+    ms_warm = e0.elapsed_time(e1) / K
     got = (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)
     assert all(torch.equal(a, b) for a, b in zip(ref, got)), "graph replay differs from the eager steps"
     del graph
-    if args.profile:
-        log(f"[bench] profile run: {ms_step * 1e3:.1f} us/step (graph), {ms_eager * 1e3:.1f} us/step (eager)")
-        return
+    if profile:
+        log(f"[bench] profile run: {ms_warm * 1e3:.1f} us/step (graph), {ms_eager * 1e3:.1f} us/step (eager)")
+        return None
 
-    # Host-input pass: the same steps launched eagerly, each step's query and
-    # new key/value rows first copied from pinned host memory (a caller that
-    # holds them on the host).  Compare with ms_eager; never the headline.
-    restore()
-    Qh, KNh, VNh = (torch.empty(x.shape, dtype=x.dtype, pin_memory=True) for x in (Q, KN, VN))
-    for hx, dx in ((Qh, Q), (KNh, KN), (VNh, VN)):
-        hx.copy_(dx)
-    qd, knd, vnd = torch.empty_like(Q[0]), torch.empty_like(KN[0]), torch.empty_like(VN[0])
-    for t in range(W):
-        dec.step(Q[t], KN[t], VN[t])
-    torch.cuda.synchronize()
-    e0.record()
-    for t in range(W, total):
-        qd.copy_(Qh[t], non_blocking=True)
-        knd.copy_(KNh[t], non_blocking=True)
-        vnd.copy_(VNh[t], non_blocking=True)
-        dec.step(qd, knd, vnd)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_host = e0.elapsed_time(e1) / K
-    got = (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)
-    assert all(torch.equal(a, b) for a, b in zip(ref, got)), "host-input steps differ from the eager steps"
-    host_bytes = int(Q[0].numel() * Q.element_size() + 2 * KN[0].numel() * KN.element_size())
-    del Qh, KNh, VNh
-
-    # Breakdown pass: the same steps, each of the four kernels stamping its own
-    # start/stop events from its dispatch (ckv_time_next_launch), so these are
-    # kernel execution times on the stream the kernels run on.
     b = buf
 
     def stamp_events():
@@ -230,6 +352,8 @@ def main():
         ckv.ckv_assign_update(kv, idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, dec.kappa, KN[t], VN[t],
                               b.edges, b.assign, b.ws, out=b.out if dec.defer else None)
 
+    # Warm per-kernel pass: each kernel stamps its own start/stop from its
+    # dispatch (ckv_time_next_launch), on the stream it runs on.
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
@@ -239,22 +363,18 @@ def main():
         stamped_step(t, ev[i])
     torch.cuda.synchronize()
     dt = np.array([[a.elapsed_time(c) for a, c in ev[i]] for i in range(K)]) * 1e3  # us
-    names = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
-    gather_us = dt[:, 2]
-    gather_gbps = float(gathered.sum() / (gather_us.sum() * 1e-6) / 1e9)
-    score_gbps = float(score_bytes * K / (dt[:, 0].sum() * 1e-6) / 1e9)
-    ceiling = read_ceiling(w, kv, idx, buf, row_bytes, K)
 
     # Cold passes: a 512 MB read between steps evicts the 256 MB MALL (a read,
     # so the step does not also pay for writing dirty lines back); only the
-    # step itself is timed.  The first pass times whole steps; the second stamps
-    # each kernel as in the breakdown pass (its extra event calls can slow the
-    # host's launches past the flush, so it does not time whole steps).
+    # step itself is timed.  The first pass times whole steps (the headline);
+    # the second stamps each kernel (its extra event calls can slow the host's
+    # launches past the flush, so it does not time whole steps).
     flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
     cold = []
     for t in range(W, total):
         flush.amax()
@@ -264,7 +384,10 @@ def main():
         c.record()
         cold.append((a, c))
     torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
     cold_us = np.array([a.elapsed_time(c) for a, c in cold]) * 1e3
+    got = (buf.out, buf.edges, buf.assign, idx.cent, idx.size, idx.tail_len, kv.seq_len)
+    assert all(torch.equal(a, b) for a, b in zip(ref, got)), "cold steps differ from the eager steps"
     restore()
     for t in range(W):
         dec.step(Q[t], KN[t], VN[t])
@@ -277,112 +400,102 @@ def main():
     cold_dt = np.array([[a.elapsed_time(c) for a, c in evc[i]] for i in range(K)]) * 1e3  # us
     del flush
 
-    # Dense flash-decode over every cached token of the same state.
-    dense = None
-    if not args.no_dense:
-        restore()
-        out = torch.empty_like(buf.out)
-        for _ in range(3):
-            dec.dense(Q[W], out)
-        torch.cuda.synchronize()
-        reps = 20
-        a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            dec.dense(Q[W], out)
-        c.record()
-        torch.cuda.synchronize()
-        d_us = a.elapsed_time(c) / reps * 1e3
-        d_bytes = int(kv.seq_len.sum().item()) * w.n_kv_heads * row_bytes
-        dense = {"us_per_call": round(d_us, 2), "bytes": d_bytes, "gbps": round(d_bytes / (d_us * 1e-6) / 1e9, 1),
-                 "frac_of_8tbps": round(d_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    def kernel_rate(times_us, nbytes):
+        gbps = float(nbytes / (times_us.sum() * 1e-6) / 1e9)
+        return {"gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "avg_launch_us": round(float(times_us.mean()), 2)}
 
-    # Attention-mass recall (the page's Figure 3 quality proxy): the share of
-    # each head's dense softmax mass that the attended tokens carry, per budget.
-    recall = None
-    if args.recall_steps > 0:
-        recall = {}
-        budget0 = dec.budget
-        dec.defer = False  # recall reads the gather's ml before the update
-        dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
-        dout = torch.empty_like(buf.out)
-        for B in [b for b in (128, 512, 1024, 2048, 4096) if b <= budget0]:
-            restore()
-            dec.budget = B
-            vals = []
-            for t in range(min(args.recall_steps, total)):
-                dec.retrieve(Q[t])
-                dec.attend(Q[t])
-                dec.dense(Q[t], dout, ml=dml)
-                vals.append(dec.recall(dml).flatten())
-                dec.update(KN[t], VN[t])
-            v = torch.cat(vals).cpu().numpy()
-            recall[str(B)] = {"mean": round(float(v.mean()), 4), "p10": round(float(np.percentile(v, 10)), 4),
-                              "min": round(float(v.min()), 4)}
-        dec.budget = budget0
-        dec.defer = True
-
-    prefill = None
-    if not args.no_prefill:
-        prefill = bench_prefill(w, args.seed, kv, slices,
-                                cpu_seconds=0.0 if args.no_cpu_baseline else args.cpu_seconds / 2)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.seed, slices, steps_in, args.cpu_seconds)
-
-    avg_gather = float(gathered.mean())
-    src_hash = gather_source_hash()
-    traffic = measured_traffic(w.name, src_hash)
-    res = {
-        "metric": METRIC,
-        "value": round(1e3 / ms_step, 1),
-        "unit": "decode steps/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "ctx": w.n_ctx, "budget": w.budget, "kappa": w.kappa,
-                   "graphs": "per_query_head" if w.mode == synth.PER_HEAD else "query_group",
-                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-                   "kv_dtype": w.dtype, "n_graphs": idx.n_graphs, "seed": args.seed,
-                   "windows": dec.windows, "deferred_combine": dec.defer},
-        "gathered_kv_gbps": round(gather_gbps, 1),
-        "gathered_kv_frac_of_hbm": round(gather_gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "gather_attend", "achieved": round(gather_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "bytes_per_launch": int(avg_gather),
-                     "avg_launch_us": round(float(gather_us.mean()), 2), "kernel_sources": src_hash,
-                     "read_ceiling_gbps": ceiling["gbps"],
-                     "frac_of_read_ceiling": round(gather_gbps / ceiling["gbps"], 4)},
-        "read_ceiling": ceiling,
-        "score_roofline": {"bound": "hbm", "achieved": round(score_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": round(score_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": score_bytes,
-                           "avg_launch_us": round(float(dt[:, 0].mean()), 2)},
-        "breakdown_us": {n: round(float(dt[:, j].mean()), 2) for j, n in enumerate(names)},
-        "breakdown_step_us": round(float(dt.sum(axis=1).mean()), 2),
-        "cold_step_us": {"median": round(float(np.median(cold_us)), 2),
-                         "p10": round(float(np.percentile(cold_us, 10)), 2),
-                         "p90": round(float(np.percentile(cold_us, 90)), 2),
-                         "kernels_median": {n: round(float(np.median(cold_dt[:, k])), 2) for k, n in enumerate(names)}},
-        "tokens_per_step": round(float(tok[W:].sum(axis=1).mean()), 1),
-        "dense_flash_decode": dense,
-        "attention_mass_recall": recall,
-        "prefill_graph": prefill,
-        "cpu_baseline": cpu,
-        "ms_per_step_eager": round(ms_eager, 5),
-        "host_inputs": {"ms_per_step": round(ms_host, 5), "steps_per_s": round(1e3 / ms_host, 1),
-                        "bytes_per_step": host_bytes,
-                        "how": "eager launches; q, k_new and v_new copied from pinned host memory before each step"},
-        "launch": "hip_graph",
-        "wall_s_timed": round(wall, 4),
+    return {
+        "tok": tok, "gathered": gathered, "score_bytes": score_bytes, "row_bytes": row_bytes, "ref": ref,
+        "n_graphs": idx.n_graphs, "ms_eager": ms_eager, "ms_warm": ms_warm, "cold_us": cold_us,
+        "wall_s": round(wall, 4),
+        "step_us": {"cold_mean": round(float(cold_us.mean()), 2), "cold_median": round(float(np.median(cold_us)), 2),
+                    "cold_p10": round(float(np.percentile(cold_us, 10)), 2),
+                    "cold_p90": round(float(np.percentile(cold_us, 90)), 2), "warm": round(ms_warm * 1e3, 2)},
+        "breakdown_cold": {n: round(float(cold_dt[:, j].mean()), 2) for j, n in enumerate(STEP_KERNELS)},
+        "breakdown_warm": {n: round(float(dt[:, j].mean()), 2) for j, n in enumerate(STEP_KERNELS)},
+        "gather": {"cold": kernel_rate(cold_dt[:, 2], gathered.sum()), "warm": kernel_rate(dt[:, 2], gathered.sum())},
+        "score": {"cold": kernel_rate(cold_dt[:, 0], score_bytes * K), "warm": kernel_rate(dt[:, 0], score_bytes * K)},
     }
-    print(json.dumps(res), flush=True)
+
+
+def aux_memory(kv, idx):
+    """Bytes of the community index (everything the method keeps beside the
+    K/V cache) against the K/V bytes of the cached tokens, as the page's
+    Table 5 reports auxiliary memory against the KV cache."""
+    parts = {k: int(getattr(idx, k).numel() * getattr(idx, k).element_size())
+             for k in idx.STATE + ("n_comm",) if k != "status"}
+    kv_filled = int(kv.seq_len.sum().item()) * kv.n_kv_heads * 2 * kv.head_dim * kv.kv.element_size()
+    kv_alloc = int(kv.kv.numel() * kv.kv.element_size())
+    total = sum(parts.values())
+    return {"index_bytes": total, "kv_bytes_cached": kv_filled, "kv_bytes_allocated": kv_alloc,
+            "aux_over_kv": round(total / kv_filled, 4), "parts": parts}
+
+
+def dense_baseline(w, dec, kv, q, restore, reps=20):
+    """Dense flash-decode over every cached token of the same state."""
+    import torch
+    restore()
+    out = torch.empty_like(dec.buf.out)
+    for _ in range(3):
+        dec.dense(q, out)
+    torch.cuda.synchronize()
+    a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dec.dense(q, out)
+    c.record()
+    torch.cuda.synchronize()
+    d_us = a.elapsed_time(c) / reps * 1e3
+    row_bytes = 2 * w.head_dim * (2 if w.dtype == "bf16" else 4)
+    d_bytes = int(kv.seq_len.sum().item()) * w.n_kv_heads * row_bytes
+    return {"us_per_call": round(d_us, 2), "bytes": d_bytes, "gbps": round(d_bytes / (d_us * 1e-6) / 1e9, 1),
+            "frac_of_8tbps": round(d_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def bench_group(args, w, W, K):
+    """The batch-8 query-group layer (one graph per kv head, the group's four
+    query heads share its selection): keys, values and step inputs drawn on
+    the device with the recipe of the host generator, then every timing pass
+    of time_layer, the gather roofline, auxiliary memory and the dense
+    baseline."""
+    import torch
+
+    from community_kv_retrieval_amd import runner
+    t0 = time.time()
+    L0 = runner.load_stack(w, args.seed, W + K, layers=[0])[0]
+    dec, kv, idx = L0.dec, L0.kv, L0.idx
+    dec.defer = not args.no_defer
+    log(f"[bench] group leg {w.name}: setup {time.time() - t0:.1f}s; G={idx.n_graphs}")
+    aux = aux_memory(kv, idx)
+    snap = (idx.state_dict(), kv.kv.clone(), kv.seq_len.clone())
+
+    def restore():
+        idx.load_state_dict(snap[0])
+        kv.kv.copy_(snap[1])
+        kv.seq_len.copy_(snap[2])
+        torch.cuda.synchronize()
+
+    L = time_layer(w, dec, kv, idx, L0.q, L0.k_new, L0.v_new, W, K, restore)
+    dense = None if args.no_dense else dense_baseline(w, dec, kv, L0.q[W], restore, reps=5)
+    cold_step_us = float(L["cold_us"].mean())
+    out = {"workload": w.name, "batch": w.batch, "ctx": w.n_ctx, "budget": w.budget, "graphs": "query_group",
+           "n_graphs": idx.n_graphs, "data": "synthetic, drawn on the device",
+           "steps_per_s": round(1e6 / cold_step_us, 1), "tokens_per_s": round(1e6 / cold_step_us * w.batch, 1),
+           "step_us": L["step_us"], "warm_steps_per_s": round(1e3 / L["ms_warm"], 1),
+           "breakdown_us": L["breakdown_cold"], "breakdown_us_warm": L["breakdown_warm"],
+           "gathered_bytes_per_step": int(L["gathered"].mean()),
+           "gather_roofline": {"bound": "hbm", "kernel": "gather_attend (matrix-core group kernel)",
+                               "peak": HBM_PEAK_GBPS, "unit": "GB/s", "cold": L["gather"]["cold"],
+                               "warm": L["gather"]["warm"]},
+           "score_roofline": {"bytes_per_launch": L["score_bytes"], "cold": L["score"]["cold"],
+                              "warm": L["score"]["warm"]},
+           "aux_memory": aux, "dense_flash_decode": dense}
+    if dense is not None:
+        out["dense_flash_decode"]["dense_over_sparse_step_cold"] = round(dense["us_per_call"] / cold_step_us, 3)
+    del L0, dec, kv, idx, snap
+    torch.cuda.empty_cache()
+    return out
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
