@@ -61,6 +61,7 @@ class Workload:
     max_size: int = 64
     n_layers: int = 1
     min_ctx: int = 0           # > 0: per-sequence lengths uniform in [min_ctx, n_ctx]
+    cent_budget: int = 0       # centroid entries of next-ranked communities (Table 6; 0 = none)
 
     @property
     def group(self) -> int:

@@ -15,6 +15,10 @@ context length.  Table 1 gives the per-step update as O(d) and the retrieval as 
 over the centroids.  Table 6 fixes the defaults (kappa = 8, per-head graphs,
 sinks excluded from the top-kappa pool).
 
+Table 6 also ablates a centroid budget: the attention then takes, besides the
+exact tokens, the centroids of the next-ranked communities (centroid_communities,
+attend_with_centroids).
+
 The same caption's panel (1), the prefill graph construction, is here too:
 every prompt token is linked to the earlier non-sink tokens it attends to
 most (prefill_edges).
@@ -140,6 +144,25 @@ def attended_positions(labels: np.ndarray, n_sinks: int, selected: np.ndarray) -
     return np.union1d(sinks, members)
 
 
+def centroid_communities(scores: np.ndarray, counts: np.ndarray, selected: np.ndarray,
+                         n_cent: int) -> np.ndarray:
+    """Communities whose centroid the attention takes besides the exact tokens
+    (Table 6, "Centroid Budget": 0, 4, 16, 64 or 256; 0, the default, takes
+    none), as ascending ids.
+
+    Reading (the page gives only the budget values): the n_cent best-ranked
+    non-empty communities that the budget walk did not take, in the ranking of
+    rank_communities; all of them when fewer are left.  After a plain walk
+    these are the ranks just past the taken prefix, starting with the
+    community that ended the walk.
+    """
+    if n_cent <= 0:
+        return np.zeros(0, dtype=np.int64)
+    taken = {int(c) for c in np.asarray(selected)}
+    rest = [int(c) for c in rank_communities(scores, counts) if int(c) not in taken]
+    return np.array(sorted(rest[:n_cent]), dtype=np.int64)
+
+
 # --------------------------------------------------------------------------
 # Exact attention on the subset (Figure 1, panel (3))
 # --------------------------------------------------------------------------
@@ -163,6 +186,40 @@ def attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: 
     e = np.exp(z - m)
     p = e / e.sum(axis=1, keepdims=True)
     return p @ V, p, z
+
+
+def attend_with_centroids(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                          cent_keys: np.ndarray, cent_values: np.ndarray, cent_counts: np.ndarray,
+                          sm_scale: float):
+    """Softmax attention over the attended tokens and the centroid entries of
+    the centroid budget (Table 6).
+
+    Reading: a centroid entry stands for its n members as if every member's
+    key were the centroid mu, so it enters the softmax as one term of logit
+    sm_scale * q . mu + ln n (the mass n exp(sm_scale q . mu)) with the
+    members' mean value as its value.  It is not a token: it never becomes an
+    edge, but its mass is in the normaliser of every token's probability.
+    cent_keys: [N][d] the stored (float32) centroids; cent_values: [N][d] the
+    mean member values; cent_counts: [N] member counts (> 0).
+    Returns (out [h][d], token probs [h][T], token logits [h][T],
+    centroid probs [h][N], centroid logits [h][N]).
+    """
+    q = np.asarray(q_heads, dtype=np.float64).reshape(-1, np.shape(q_heads)[-1])
+    K = np.asarray(keys, dtype=np.float64).reshape(-1, q.shape[1])
+    V = np.asarray(values, dtype=np.float64).reshape(-1, q.shape[1])
+    MU = np.asarray(cent_keys, dtype=np.float64).reshape(-1, q.shape[1])
+    NU = np.asarray(cent_values, dtype=np.float64).reshape(-1, q.shape[1])
+    n = np.asarray(cent_counts, dtype=np.float64)
+    T = K.shape[0]
+    zt = float(sm_scale) * (q @ K.T)
+    zc = float(sm_scale) * (q @ MU.T) + np.log(n)[None, :]
+    z = np.concatenate([zt, zc], axis=1)
+    if z.shape[1] == 0:
+        return np.zeros((q.shape[0], V.shape[1])), zt, zt, zc, zc
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    out = p[:, :T] @ V + p[:, T:] @ NU
+    return out, p[:, :T], zt, p[:, T:], zc
 
 
 def dense_attend(q_heads: np.ndarray, keys: np.ndarray, values: np.ndarray, sm_scale: float,
@@ -333,6 +390,7 @@ class GraphState:
     labels: np.ndarray       # [cap] int64, -1 = sink / not yet cached
     sums: np.ndarray         # [C][d] float64
     counts: np.ndarray       # [C] int64
+    vsums: np.ndarray        # [C][d] float64 exact value sums (the centroid entries' values)
 
 
 @dataclass
@@ -347,13 +405,16 @@ class GraphStep:
     edges: np.ndarray
     assign: int
     top: int                 # best-scoring community
+    cent: np.ndarray = field(default_factory=lambda: np.zeros(0, dtype=np.int64))  # centroid entries
+    cent_logits: np.ndarray = field(default_factory=lambda: np.zeros((0, 0)))      # [nh][len(cent)]
 
 
 class Oracle:
     """Decode-step oracle for a set of graphs of one layer.
 
     shape: any object with batch, n_q_heads, n_kv_heads, head_dim, n_sinks,
-    mode ("per_head" | "group"), budget, max_comm, kappa, sm_scale.
+    mode ("per_head" | "group"), budget, max_comm, kappa, sm_scale, and
+    optionally cent_budget (default 0).
     kv[b][kh] = (keys [n_b][d], values [n_b][d]) as float32-representable
     arrays (bf16 and fp32 storage both read exactly).
     graphs: which graphs to track (default: all).
@@ -390,7 +451,8 @@ class Oracle:
             lab = np.full(n + extra, -1, dtype=np.int64)
             lab[:n] = labels[gid]
             sums, counts = community_sums(self.K[(b, kh)][:n], lab[:n], n_comm[gid])
-            self.g[gid] = GraphState(b, kh, qh0, nh, lab, sums, counts)
+            vsums, _ = community_sums(self.V[(b, kh)][:n], lab[:n], n_comm[gid])
+            self.g[gid] = GraphState(b, kh, qh0, nh, lab, sums, counts, vsums)
 
     # -- pieces a checker may call on their own -----------------------------
     def centroids32(self, gid: int) -> np.ndarray:
@@ -401,8 +463,11 @@ class Oracle:
         st = self.g[gid]
         return np.asarray(q[st.b, st.qh0:st.qh0 + st.nh], dtype=np.float64)
 
-    def step_graph(self, gid: int, q: np.ndarray, force_sel=None, force_edges=None) -> GraphStep:
-        """Retrieval, attention and edge choice for one graph (no state change)."""
+    def step_graph(self, gid: int, q: np.ndarray, force_sel=None, force_edges=None,
+                   force_cent=None) -> GraphStep:
+        """Retrieval, attention and edge choice for one graph (no state change).
+        With a centroid budget (shape.cent_budget > 0) the attention also takes
+        the centroid entries of centroid_communities."""
         w, st = self.w, self.g[gid]
         n = self.len[st.b]
         qh = self.graph_query(gid, q)
@@ -415,7 +480,17 @@ class Oracle:
         pos = attended_positions(st.labels[:n], w.n_sinks, sel)
         K = self.K[(st.b, st.kh)][pos]
         V = self.V[(st.b, st.kh)][pos]
-        out, p, z = attend(qh, K, V, w.sm_scale)
+        cent = centroid_communities(scores, st.counts, sel, getattr(w, "cent_budget", 0))
+        if force_cent is not None:
+            cent = np.array(sorted(int(c) for c in force_cent), dtype=np.int64)
+        zc = np.zeros((qh.shape[0], 0))
+        if cent.size:
+            nc = st.counts[cent]
+            out, p, z, _, zc = attend_with_centroids(qh, K, V, self.centroids32(gid)[cent],
+                                                     st.vsums[cent] / nc[:, None].astype(np.float64), nc,
+                                                     w.sm_scale)
+        else:
+            out, p, z = attend(qh, K, V, w.sm_scale)
         wts = edge_weights(p)
         edges = top_kappa(wts, pos, w.kappa, w.n_sinks)
         if force_edges is not None:
@@ -423,17 +498,20 @@ class Oracle:
         a = majority_vote(st.labels[edges])
         if a < 0:
             a = top  # no attended non-sink token: fall back to the best-scoring community
-        return GraphStep(scores, sel, pos, out, p, z, wts, edges, a, top)
+        return GraphStep(scores, sel, pos, out, p, z, wts, edges, a, top, cent, zc)
 
-    def apply_update(self, gid: int, assign: int, k_new: np.ndarray):
+    def apply_update(self, gid: int, assign: int, k_new: np.ndarray, v_new: Optional[np.ndarray] = None):
         """label[P] = a, member count and key sum of a grow by the new token
-        (so the centroid becomes the running mean (n*mu + k)/(n + 1))."""
+        (so the centroid becomes the running mean (n*mu + k)/(n + 1)); the
+        value sum grows by its value."""
         st = self.g[gid]
         P = self.len[st.b]
         if assign < 0:
             return
         st.labels[P] = assign
         st.sums[assign] += np.asarray(k_new, dtype=np.float64)
+        if v_new is not None:
+            st.vsums[assign] += np.asarray(v_new, dtype=np.float64)
         st.counts[assign] += 1
 
     def step(self, q, k_new, v_new, force_sel: Optional[Dict[int, Sequence[int]]] = None,
@@ -450,7 +528,7 @@ class Oracle:
             res[gid] = self.step_graph(gid, q, (force_sel or {}).get(gid), (force_edges or {}).get(gid))
         for gid in self.graph_ids:
             st = self.g[gid]
-            self.apply_update(gid, res[gid].assign, k_new[st.b][st.kh])
+            self.apply_update(gid, res[gid].assign, k_new[st.b][st.kh], v_new[st.b][st.kh])
         self.append(k_new, v_new)
         return res
 

@@ -132,6 +132,47 @@ def edges_ok(positions: np.ndarray, weights: np.ndarray, n_sinks: int, kappa: in
     return False
 
 
+def centroids_ok(scores: np.ndarray, counts: np.ndarray, selected: Sequence[int], oracle_cent: Sequence[int],
+                 dev_cent: Sequence[int], n_cent: int, where: str = "", gaps: Optional[List[float]] = None) -> bool:
+    """The communities whose centroids a step attends (Table 6's centroid
+    budget, read as the n_cent best-ranked non-empty communities the budget
+    walk did not take).  True when the device's set equals the oracle's;
+    False when it differs but is the head of a tie-consistent ranking of the
+    communities outside the selection (the caller then adopts it);
+    AssertionError otherwise.  The device must return exactly
+    min(n_cent, non-empty communities outside the selection) distinct such
+    communities, each scoring at least every other outsider's score - TIE.
+    selected: the selection the step used (the device's, once accepted)."""
+    so = sorted(int(c) for c in oracle_cent)
+    sg = [int(c) for c in dev_cent]
+    assert len(set(sg)) == len(sg), f"{where}: duplicate centroid community {sg}"
+    sg = sorted(sg)
+    counts = np.asarray(counts)
+    C = counts.size
+    live = counts > 0
+    taken = np.zeros(C, dtype=bool)
+    taken[[int(c) for c in selected]] = True
+    outside = np.nonzero(live & ~taken)[0]
+    want = min(max(n_cent, 0), outside.size)
+    assert len(sg) == want, f"{where}: device attends {len(sg)} centroids, expected {want}"
+    if so == sg:
+        return True
+    s = np.asarray(scores, dtype=np.float64)[:C]
+    for c in sg:
+        assert 0 <= c < C and live[c] and not taken[c], \
+            f"{where}: centroid community {c} is empty, out of range or already selected"
+    chosen = np.zeros(C, dtype=bool)
+    chosen[sg] = True
+    rest = np.nonzero(live & ~taken & ~chosen)[0]
+    if rest.size and sg:
+        inv = float(s[rest].max() - s[sg].min())
+        assert inv <= TIE, (f"{where}: community {int(rest[np.argmax(s[rest])])} outranks centroid community "
+                            f"{sg[int(np.argmin(s[sg]))]} by {inv:.3g}")
+        if gaps is not None:
+            gaps.append(max(inv, 0.0))
+    return False
+
+
 # Prefill graph (Figure 1 panel (1)): the logits come from bf16 operands on
 # the matrix cores with float32 accumulation, |dz| <= (d - 1) 2^-24
 # sum_i |q_i k_i| (about 6e-5 at d = 128 with these magnitudes, sum |q k| up

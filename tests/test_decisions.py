@@ -263,3 +263,48 @@ def test_prefill_pair_window_is_relative_to_the_pair():
     assert D.prefill_row_ok(W, i, 4, 6, six, np.array([4, 5, 6, 7, 9, 8]), None) is False  # 1e-9 of 1e-5
     with pytest.raises(AssertionError):
         D.prefill_row_ok(W, i, 4, 6, six, np.array([4, 5, 6, 8, 7, 9]), None)  # 1e-5 of 2e-5
+
+
+# --- centroid budget ---------------------------------------------------------
+
+def _cent(scores, counts, sel, n):
+    s = np.asarray(scores, dtype=np.float32)
+    c = np.asarray(counts, dtype=np.int64)
+    return s, c, O.centroid_communities(s, c, np.asarray(sel, dtype=np.int64), n)
+
+
+def test_identical_centroids_pass():
+    s, c, co = _cent([5, 4, 3, 2, 1], [1] * 5, [0, 1], 2)
+    assert co.tolist() == [2, 3]
+    assert D.centroids_ok(s, c, [0, 1], co, [3, 2], 2) is True
+
+
+@pytest.mark.parametrize("dev", [
+    [2],           # one too few
+    [2, 3, 4],     # one too many
+    [2, 4],        # the second replaced by a worse one
+    [1, 2],        # a selected community
+    [2, 2],        # duplicate
+    [2, 9],        # out of range
+    [3, 4],        # the walk's stopper left out
+])
+def test_centroid_mistakes_rejected(dev):
+    s, c, co = _cent([5, 4, 3, 2, 1], [1] * 5, [0, 1], 2)
+    with pytest.raises(AssertionError):
+        D.centroids_ok(s, c, [0, 1], co, dev, 2)
+
+
+def test_centroid_near_tie_accepted_and_empty_rejected():
+    s, c, co = _cent([5, 4, 3, 2 - 4e-7, 2, -np.inf], [1, 1, 1, 1, 1, 0], [0, 1], 2)
+    assert co.tolist() == [2, 4]
+    assert D.centroids_ok(s, c, [0, 1], co, [2, 3], 2) is False
+    with pytest.raises(AssertionError):
+        D.centroids_ok(s, c, [0, 1], co, [2, 5], 2)
+
+
+def test_centroid_all_left_taken_when_short():
+    s, c, co = _cent([5, 4, 3], [1, 1, 1], [0], 8)
+    assert co.tolist() == [1, 2]
+    assert D.centroids_ok(s, c, [0], co, [1, 2], 8) is True
+    with pytest.raises(AssertionError):
+        D.centroids_ok(s, c, [0], co, [1], 8)

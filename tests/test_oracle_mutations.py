@@ -29,7 +29,12 @@ def _pins():
                P.test_recall_full_set_is_one_and_complements_add_up,
                P.test_prefill_identical_keys_closed_form, P.test_prefill_one_hot_target_closed_form,
                P.test_prefill_subsets_brute_force, P.test_prefill_per_head_matches_decode_edges,
-               P.test_prefill_invariants_and_rows]
+               P.test_prefill_invariants_and_rows, P.test_centroid_entry_two_term_closed_form,
+               P.test_centroid_budget_past_the_walk_on_workload]
+    checks += [lambda a=a: P.test_centroid_communities_hand_cases(*a) for a in P.CENT_HAND_CASES]
+    checks += [lambda b=b, h=h: P.test_centroid_entries_equal_attention_over_identical_members(b, h)
+               for b in (1, 3, 64) for h in (1, 4)]
+    checks += [lambda m=m: P.test_value_sums_stay_member_sums(m) for m in ("per_head", "group")]
     checks += [lambda s=s: P.test_select_matches_definition(s) for s in range(40)]
     checks += [lambda s=s: P.test_top_kappa_matches_heap(s) for s in range(20)]
     checks += [lambda s=s: P.test_vote_matches_counter(s) for s in range(20)]
@@ -268,7 +273,51 @@ def m_row_weights_no_scale(q_heads_row, i, keys, sm_scale):
     return _orig["prefill_row_weights"](q_heads_row, i, keys, 1.0)
 
 
+def m_cent_includes_taken(scores, counts, selected, n_cent):
+    return _orig["centroid_communities"](scores, counts, np.zeros(0, dtype=np.int64), n_cent)
+
+
+def m_cent_lowest_ranked(scores, counts, selected, n_cent):
+    if n_cent <= 0:
+        return np.zeros(0, dtype=np.int64)
+    taken = {int(c) for c in selected}
+    rest = [int(c) for c in O.rank_communities(scores, counts) if int(c) not in taken]
+    return np.array(sorted(rest[::-1][:n_cent]), dtype=np.int64)
+
+
+def m_cent_skip_stopper(scores, counts, selected, n_cent):
+    if n_cent <= 0:
+        return np.zeros(0, dtype=np.int64)
+    taken = {int(c) for c in selected}
+    rest = [int(c) for c in O.rank_communities(scores, counts) if int(c) not in taken]
+    return np.array(sorted(rest[1:n_cent + 1]), dtype=np.int64)
+
+
+def m_cent_one_short(scores, counts, selected, n_cent):
+    return _orig["centroid_communities"](scores, counts, selected, n_cent)[:max(n_cent - 1, 0)]
+
+
+def m_cent_no_count(q, K, V, MU, NU, n, sm_scale):
+    return _orig["attend_with_centroids"](q, K, V, MU, NU, np.ones_like(np.asarray(n)), sm_scale)
+
+
+def m_cent_value_sum(q, K, V, MU, NU, n, sm_scale):
+    nn = np.asarray(n, dtype=np.float64).reshape(-1, 1)
+    return _orig["attend_with_centroids"](q, K, V, MU, np.asarray(NU) * nn, n, sm_scale)
+
+
+def m_cent_unscaled(q, K, V, MU, NU, n, sm_scale):
+    return _orig["attend_with_centroids"](q, K, V, np.asarray(MU) / sm_scale, NU, n, sm_scale)
+
+
+def m_cent_token_only_norm(q, K, V, MU, NU, n, sm_scale):
+    out, p, z, pc, zc = _orig["attend_with_centroids"](q, K, V, MU, NU, n, sm_scale)
+    return out, p / p.sum(axis=1, keepdims=True), z, pc, zc
+
+
 MUTANTS = {
+    "centroid_communities": [m_cent_includes_taken, m_cent_lowest_ranked, m_cent_skip_stopper, m_cent_one_short],
+    "attend_with_centroids": [m_cent_no_count, m_cent_value_sum, m_cent_unscaled, m_cent_token_only_norm],
     "prefill_row_weights": [m_row_weights_no_scale],
     "prefill_edges": [m_prefill_self_candidate, m_prefill_sinks_in_pool, m_prefill_tie_high_pos,
                       m_prefill_group_max],
@@ -297,7 +346,7 @@ def test_pins_catch_mutant(monkeypatch, name, mutant):
 
 
 def test_apply_update_mutant_caught(monkeypatch):
-    def bad(self, gid, assign, k_new):  # overwrite instead of accumulate
+    def bad(self, gid, assign, k_new, v_new=None):  # overwrite instead of accumulate
         st = self.g[gid]
         P_ = self.len[st.b]
         if assign < 0:
@@ -306,13 +355,26 @@ def test_apply_update_mutant_caught(monkeypatch):
         st.sums[assign] = np.asarray(k_new, np.float64) * st.counts[assign]
         st.counts[assign] += 1
     monkeypatch.setattr(O.Oracle, "apply_update", bad)
+    assert _count_failures() > 0
+
+
+def test_value_sum_update_mutant_caught(monkeypatch):
+    orig = O.Oracle.apply_update
+
+    def bad(self, gid, assign, k_new, v_new=None):  # the value sum is left as it was
+        orig(self, gid, assign, k_new, None)
+    monkeypatch.setattr(O.Oracle, "apply_update", bad)
+    assert _count_failures() > 0
+
+
+def _count_failures():
     failed = 0
     for chk in _pins():
         try:
             chk()
         except Exception:
             failed += 1
-    assert failed > 0
+    return failed
 
 
 def test_unmutated_oracle_passes_every_pin():

@@ -519,3 +519,123 @@ def test_prefill_invariants_and_rows():
     er, wr = O.prefill_edges_rows(q[rows], rows, K, s, kappa, 0.5)
     assert (er == e[rows]).all()
     np.testing.assert_allclose(wr, w[rows], rtol=1e-13, atol=1e-300)
+
+
+# --------------------------------------------------------------------------
+# Centroid budget (Table 6): the attention also takes the centroids of the
+# next-ranked communities, each standing for its members.
+# --------------------------------------------------------------------------
+
+CENT_HAND_CASES = [
+    ([5, 4, 3, 2, 1], [2, 2, 2, 2, 2], [0, 1], 2, [2, 3]),   # the walk's stopper comes first
+    ([5, 4, 3, 2, 1], [2, 2, 2, 2, 2], [0, 1], 10, [2, 3, 4]),  # fewer left than the budget
+    ([3, 3, 3, 1], [1, 0, 1, 1], [], 2, [0, 2]),            # equal scores: lower id; empty skipped
+    ([5, 4, 3, 2], [1, 1, 1, 1], [1], 2, [0, 2]),           # a selection that is not a prefix
+    ([1, 9, 9, 9], [1, 1, 1, 1], [0], 2, [1, 2]),
+    ([5, 4, 3], [1, 1, 1], [0], 0, []),                     # budget 0: none
+    ([5, 4, 3], [1, 1, 1], [0, 1, 2], 4, []),               # everything taken already
+]
+
+
+@pytest.mark.parametrize("scores,counts,sel,n,expect", CENT_HAND_CASES)
+def test_centroid_communities_hand_cases(scores, counts, sel, n, expect):
+    s = np.array(scores, dtype=np.float32)
+    c = np.array(counts)
+    s[c == 0] = -np.inf
+    np.testing.assert_array_equal(O.centroid_communities(s, c, np.array(sel, dtype=np.int64), n), expect)
+
+
+def test_centroid_entry_two_term_closed_form():
+    # one token (logit 0, value e0) and one centroid entry of n members:
+    # weights 1 : n e^(q.mu), so out = (e0 + n e^(q.mu) nu) / (1 + n e^(q.mu))
+    q = np.array([[1.0, 0.0]])
+    K, V = np.zeros((1, 2)), np.array([[1.0, 0.0]])
+    out, p, z, pc, zc = O.attend_with_centroids(q, K, V, np.zeros((1, 2)), np.array([[0.0, 1.0]]),
+                                                np.array([3]), 1.0)
+    np.testing.assert_allclose(out, [[0.25, 0.75]], rtol=1e-15)
+    np.testing.assert_allclose(p, [[0.25]], rtol=1e-15)
+    np.testing.assert_allclose(pc, [[0.75]], rtol=1e-15)
+    np.testing.assert_allclose(zc, [[np.log(3.0)]], rtol=1e-15)
+    out, p, z, pc, zc = O.attend_with_centroids(q, K, V, np.array([[np.log(2.0), 0.0]]),
+                                                np.array([[0.0, 1.0]]), np.array([1]), 1.0)
+    np.testing.assert_allclose(out, [[1 / 3, 2 / 3]], rtol=1e-15)
+    # the softmax scale multiplies q . mu but not ln n
+    out, p, z, pc, zc = O.attend_with_centroids(q, K, V, np.array([[np.log(2.0), 0.0]]),
+                                                np.array([[0.0, 1.0]]), np.array([2]), 2.0)
+    np.testing.assert_allclose(pc, [[8 / 9]], rtol=1e-15)  # mass 2 * e^(2 ln 2) = 8 against 1
+
+
+def _same_key_oracle(cent_budget, budget, nh, seed):
+    """Every community's members share one key (multiples of 1/8: the float32
+    centroid is that key exactly), values random."""
+    rng = np.random.default_rng(seed)
+    d, C, n_sinks = 4, 12, 2
+    sizes = rng.integers(1, 6, C)
+    labels = np.concatenate([np.full(n_sinks, -1), rng.permutation(np.repeat(np.arange(C), sizes))])
+    centres = rng.integers(-8, 9, (C, d)) / 8.0
+    K = np.zeros((labels.size, d), dtype=np.float32)
+    K[:n_sinks] = rng.integers(-8, 9, (n_sinks, d)) / 8.0
+    K[n_sinks:] = centres[labels[n_sinks:]]
+    V = rng.standard_normal((labels.size, d)).astype(np.float32)
+    shape = SimpleNamespace(batch=1, n_q_heads=nh, n_kv_heads=1, head_dim=d, n_sinks=n_sinks,
+                            mode="per_head" if nh == 1 else "group", budget=budget, max_comm=0,
+                            kappa=3, sm_scale=0.9, cent_budget=cent_budget)
+    orc = O.Oracle(shape, [[(K, V)]], {0: labels}, {0: C}, extra=4)
+    return orc, K, V, labels, rng
+
+
+@pytest.mark.parametrize("cent_budget", [1, 3, 64])
+@pytest.mark.parametrize("nh", [1, 4])
+def test_centroid_entries_equal_attention_over_identical_members(cent_budget, nh):
+    """With identical member keys a centroid entry is exact: the step equals
+    full softmax attention (torch, float64) over the attended tokens and every
+    member of the centroid communities, token probabilities included."""
+    for seed in range(6):
+        orc, K, V, labels, rng = _same_key_oracle(cent_budget, 9, nh, seed)
+        q = rng.standard_normal((1, nh, 4))
+        r = orc.step_graph(0, q)
+        assert r.cent.size == min(cent_budget, int((orc.g[0].counts > 0).sum()) - r.selected.size)
+        members = np.nonzero(np.isin(labels, r.cent))[0]
+        assert not np.intersect1d(members, r.positions).size
+        full = np.concatenate([r.positions, members])
+        qt = torch.tensor(q[0])
+        Kt, Vt = torch.tensor(K[full], dtype=torch.float64), torch.tensor(V[full], dtype=torch.float64)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt[None], Kt[None], Vt[None], scale=0.9)[0]
+        np.testing.assert_allclose(r.out, ref.numpy(), rtol=1e-12, atol=1e-14)
+        probs = torch.softmax(0.9 * qt @ Kt.T, dim=-1).numpy()
+        np.testing.assert_allclose(r.probs, probs[:, :r.positions.size], rtol=1e-12, atol=1e-15)
+        # edges come from the attended tokens only
+        assert np.isin(r.edges, r.positions).all()
+
+
+def test_centroid_budget_past_the_walk_on_workload():
+    """After a plain walk the centroid communities are the next ranks: the
+    taken set and them together are the head of the ranking, and the first of
+    them is the community that ended the walk."""
+    from community_kv_retrieval_amd import synth
+    w, sl, orc = _tiny_oracle("per_head", budget=40)
+    w = w.replace(cent_budget=5)
+    orc.w = w
+    inp = synth.gen_step(w, 11, 0, sl)
+    r = orc.step_graph(0, inp.q.float().numpy())
+    st = orc.g[0]
+    ranked = [c for c in sorted(range(st.counts.size), key=lambda c: (-float(r.scores[c]), c)) if st.counts[c] > 0]
+    k = r.selected.size
+    assert sorted(ranked[:k]) == list(r.selected)
+    assert sorted(ranked[k:k + 5]) == list(r.cent)
+    assert int(st.counts[r.selected].sum()) + int(st.counts[ranked[k]]) > 40
+
+
+@pytest.mark.parametrize("mode", ["per_head", "group"])
+def test_value_sums_stay_member_sums(mode):
+    from community_kv_retrieval_amd import synth
+    w, sl, orc = _tiny_oracle(mode)
+    orc.w = w.replace(cent_budget=4)
+    for t in range(5):
+        inp = synth.gen_step(w, 11, t, sl)
+        orc.step(inp.q.float().numpy(), inp.k_new.float().numpy(), inp.v_new.float().numpy())
+        for g, st in orc.g.items():
+            n = orc.len[st.b]
+            V = orc.V[(st.b, st.kh)][:n].astype(np.float64)
+            for c in range(st.counts.size):
+                np.testing.assert_allclose(st.vsums[c], V[st.labels[:n] == c].sum(axis=0), rtol=1e-13, atol=1e-13)
