@@ -53,6 +53,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-group", action="store_true", help="skip the batch-8 query-group leg")
+    ap.add_argument("--no-centroid", action="store_true", help="skip the centroid-budget leg")
+    ap.add_argument("--centroid-only", type=int, default=0,
+                    help="with --profile: only the centroid-budget layer at this budget (for rocprofv3 runs)")
     ap.add_argument("--recall-steps", type=int, default=16,
                     help="steps per budget of the attention-mass recall sweep (0: skip)")
     ap.add_argument("--profile", action="store_true", help="only warm-up + timed steps (for rocprofv3 runs)")
@@ -79,6 +82,9 @@ def main():
         copy_calibration()
         return
     w = synth.preset(args.workload)
+    if args.centroid_only > 0:
+        bench_centroid(args, w, args.warmup, args.steps, budgets=(args.centroid_only,), profile=True)
+        return
     if w.n_layers > 1:
         bench_stack(args, w)
         return
@@ -188,6 +194,9 @@ def main():
     group = None
     if not args.no_group and w.name == "llama31_8b_128k":
         group = bench_group(args, synth.preset("llama31_8b_128k_group_b8"), W, K)
+    centroid = None
+    if not args.no_centroid and w.name == "llama31_8b_128k":
+        centroid = bench_centroid(args, w, W, K)
 
     src_hash = gather_source_hash()
     traffic = measured_traffic(w.name, src_hash)
@@ -235,6 +244,7 @@ def main():
         "attention_mass_recall": recall,
         "prefill_graph": prefill,
         "group_b8": group,
+        "centroid_budget": centroid,
         "cpu_baseline": cpu,
         "host_inputs": {"ms_per_step": round(ms_host, 5), "steps_per_s": round(1e3 / ms_host, 1),
                         "bytes_per_step": host_bytes,
@@ -493,6 +503,57 @@ def bench_group(args, w, W, K):
            "aux_memory": aux, "dense_flash_decode": dense}
     if dense is not None:
         out["dense_flash_decode"]["dense_over_sparse_step_cold"] = round(dense["us_per_call"] / cold_step_us, 3)
+    del L0, dec, kv, idx, snap
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_centroid(args, w, W, K, budgets=(0, 16, 256), profile=False):
+    """The centroid budget of the page's Table 6 on this workload's layer
+    (drawn on the device): every timing pass of time_layer at each budget
+    (0 = off, the same layer and steps), the step's cost over budget 0, and the
+    bytes the centroid-term kernel reads (a float64 key sum and value sum per
+    centroid term)."""
+    import torch
+
+    from community_kv_retrieval_amd import runner
+    t0 = time.time()
+    wc = w.replace(cent_budget=max(budgets))
+    L0 = runner.load_stack(wc, args.seed, W + K, layers=[0])[0]
+    dec, kv, idx = L0.dec, L0.kv, L0.idx
+    dec.defer = not args.no_defer
+    log(f"[bench] centroid leg {w.name}: setup {time.time() - t0:.1f}s; G={idx.n_graphs}")
+    snap = (idx.state_dict(), kv.kv.clone(), kv.seq_len.clone())
+
+    def restore():
+        idx.load_state_dict(snap[0])
+        kv.kv.copy_(snap[1])
+        kv.seq_len.copy_(snap[2])
+        torch.cuda.synchronize()
+
+    out = {"workload": w.name, "budget": w.budget, "n_graphs": idx.n_graphs, "data": "synthetic, drawn on the device",
+           "reading": "next-ranked communities after the selection, one softmax term each (key: stored centroid, "
+                      "value: mean member value, logit: scale * q . mu + ln n)",
+           "value_sum_bytes": int(idx.vsum.numel() * 8), "by_budget": {}}
+    for n in budgets:
+        idx.desc.cent_budget = n
+        L = time_layer(wc, dec, kv, idx, L0.q, L0.k_new, L0.v_new, W, K, restore, profile=profile,
+                       eager_only=args.eager_only)
+        if profile:
+            continue
+        cold = float(L["cold_us"].mean())
+        out["by_budget"][str(n)] = {
+            "steps_per_s": round(1e6 / cold, 1), "step_us": L["step_us"], "breakdown_us": L["breakdown_cold"],
+            "centroid_terms_per_step": idx.n_graphs * n,
+            "centroid_kernel_bytes_per_step": idx.n_graphs * n * 2 * w.head_dim * 8}
+    if not profile and "0" in out["by_budget"]:
+        base = out["by_budget"]["0"]["step_us"]
+        for n in budgets:
+            if n:
+                st = out["by_budget"][str(n)]["step_us"]
+                out["by_budget"][str(n)]["extra_us_over_budget_0"] = {
+                    "cold": round(st["cold_mean"] - base["cold_mean"], 2), "warm": round(st["warm"] - base["warm"], 2)}
+    idx.desc.cent_budget = max(budgets)
     del L0, dec, kv, idx, snap
     torch.cuda.empty_cache()
     return out

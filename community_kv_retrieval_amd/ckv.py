@@ -27,7 +27,7 @@ CKV_OK, CKV_E_INVALID, CKV_E_UNSUPPORTED, CKV_E_WORKSPACE, CKV_E_HIP = 0, -1, -2
 CKV_ST_TAIL_FULL, CKV_ST_CAPACITY, CKV_ST_BAD_LABEL = 1, 2, 4
 CKV_DTYPE_F32, CKV_DTYPE_BF16 = 0, 1
 CKV_MODE_PER_HEAD, CKV_MODE_QUERY_GROUP = 0, 1
-CKV_MAX_KAPPA, CKV_MAX_C_CAP = 32, 16384
+CKV_MAX_KAPPA, CKV_MAX_C_CAP, CKV_MAX_CENT = 32, 16384, 256
 CKV_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_centroids",
@@ -56,7 +56,8 @@ class CkvIndex(ctypes.Structure):
                 ("n_comm", c_void_p), ("size", c_void_p), ("offs", c_void_p), ("toks", c_void_p),
                 ("label", c_void_p), ("tail_pos", c_void_p), ("tail_comm", c_void_p),
                 ("tail_len", c_void_p), ("csum", c_void_p), ("cent", c_void_p), ("cq", c_void_p),
-                ("cscale", c_void_p), ("status", c_void_p), ("win_first", c_int32), ("win_count", c_int32)]
+                ("cscale", c_void_p), ("status", c_void_p), ("win_first", c_int32), ("win_count", c_int32),
+                ("cent_budget", c_int32), ("cent_sel", c_void_p), ("cent_n", c_void_p), ("vsum", c_void_p)]
 
 
 def _load():
@@ -158,7 +159,7 @@ class CommunityIndex:
     """Community state of every graph of one layer (ckv_index)."""
 
     def __init__(self, kv: KVStore, mode: int, n_comm: Sequence[int], l_cap: int, tail_cap: int,
-                 n_sinks: int, c_cap: Optional[int] = None, device="cuda"):
+                 n_sinks: int, c_cap: Optional[int] = None, device="cuda", cent_budget: int = 0):
         G = kv.batch * (kv.n_q_heads if mode == CKV_MODE_PER_HEAD else kv.n_kv_heads)
         if c_cap is None:
             c_cap = max(256, 256 * math.ceil(max(n_comm) / 256))
@@ -179,10 +180,17 @@ class CommunityIndex:
         self.cq = torch.zeros((G, c_cap // 256, D, 256), dtype=torch.int16, device=device)  # tile-major
         self.cscale = torch.zeros((G, c_cap), dtype=torch.float32, device=device)
         self.status = torch.zeros((1,), **i32)
+        # centroid budget (Table 6): the chosen communities per graph and the value sums
+        self.cent_budget = cent_budget
+        nb = max(cent_budget, 1)
+        self.cent_sel = torch.zeros((G, nb), **i32) if cent_budget > 0 else None
+        self.cent_n = torch.zeros((G,), **i32) if cent_budget > 0 else None
+        self.vsum = torch.zeros((G, c_cap, D), dtype=torch.float64, device=device) if cent_budget > 0 else None
         self.desc = CkvIndex(mode, G, c_cap, l_cap, tail_cap, n_sinks, *[
             t.data_ptr() for t in (self.n_comm, self.size, self.offs, self.toks, self.label, self.tail_pos,
                                    self.tail_comm, self.tail_len, self.csum, self.cent, self.cq, self.cscale,
-                                   self.status)])
+                                   self.status)], 0, 0, cent_budget, _ptr(self.cent_sel), _ptr(self.cent_n),
+            _ptr(self.vsum))
 
     def heads_per_graph(self, kv: KVStore) -> int:
         return 1 if self.mode == CKV_MODE_PER_HEAD else kv.group
@@ -200,11 +208,14 @@ class CommunityIndex:
     STATE = ("size", "offs", "toks", "label", "tail_pos", "tail_comm", "tail_len", "csum", "cent", "cq", "cscale",
              "status")
 
+    def _state_keys(self):
+        return self.STATE + ("n_comm",) + (("vsum", "cent_sel", "cent_n") if self.cent_budget > 0 else ())
+
     def state_dict(self):
-        return {k: getattr(self, k).clone() for k in self.STATE + ("n_comm",)}
+        return {k: getattr(self, k).clone() for k in self._state_keys()}
 
     def load_state_dict(self, sd):
-        for k in self.STATE + ("n_comm",):
+        for k in self._state_keys():
             getattr(self, k).copy_(sd[k])
 
 
@@ -391,7 +402,7 @@ class DecodeBuffers:
 
     def __init__(self, kv: KVStore, idx: CommunityIndex, budget: int, kappa: int, device="cuda"):
         G, nh = idx.n_graphs, idx.heads_per_graph(kv)
-        self.t_cap = idx.n_sinks + min(budget, idx.l_cap)
+        self.t_cap = max(1, idx.n_sinks + min(budget, idx.l_cap))  # the calls take t_cap >= 1
         i32 = dict(dtype=torch.int32, device=device)
         self.scores = torch.empty((G, idx.c_cap), dtype=torch.float32, device=device)
         self.sel = torch.empty((G, idx.c_cap), **i32)

@@ -45,6 +45,8 @@ ckv_status check_index(const ckv_kv *kv, const ckv_index *idx) {
         !idx->tail_comm || !idx->tail_len || !idx->csum || !idx->cent || !idx->cq || !idx->cscale ||
         !idx->status)
         return CKV_E_INVALID;
+    if (idx->cent_budget < 0 || idx->cent_budget > CKV_MAX_CENT) return CKV_E_INVALID;
+    if (idx->cent_budget > 0 && (!idx->cent_sel || !idx->cent_n || !idx->vsum)) return CKV_E_INVALID;
     if (idx->win_count < 0 || idx->win_first < 0) return CKV_E_INVALID;
     if (idx->win_count == 0 ? idx->win_first != 0 : (long long)idx->win_first + idx->win_count > G)
         return CKV_E_INVALID;
@@ -64,7 +66,7 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 8; }
+int32_t ckv_abi_version(void) { return 9; }
 
 ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;
@@ -156,8 +158,11 @@ ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const 
     if (t_cap < need) return CKV_E_INVALID;
     const WsLayout L = ws_layout(kv, idx, 0);
     if (!ws || ws_bytes < L.total) return CKV_E_WORKSPACE;
-    return hip_status(launch_select(kv, idx, q, scores, budget, max_comm, t_cap, sel, sel_n, top, tok_list,
-                                    tok_n, cand_arrays(ws, L, idx), (hipStream_t)stream));
+    hipError_t e = launch_select(kv, idx, q, scores, budget, max_comm, t_cap, sel, sel_n, top, tok_list, tok_n,
+                                 cand_arrays(ws, L, idx), (hipStream_t)stream);
+    if (e == hipSuccess && idx->cent_budget > 0)
+        e = launch_centroid_select(kv, idx, q, scores, sel, sel_n, (hipStream_t)stream);
+    return hip_status(e);
 }
 
 ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void *q,

@@ -45,7 +45,9 @@ struct AssignParams {
     float *ml;           // read (gather complete) or written (deferred combine)
     float *out;          // not null: combine the deferred gather's records into out
     const float *part;   // the gather's partial records
-    int nchunk;          // gather spans per graph (records per head)
+    int nchunk;          // gather record slots per graph and head
+    const int32_t *cent_n;  // centroid budget: centroid terms per graph (their record follows the spans')
+    double *vsum;        // centroid budget: value sums (else null)
     const int32_t *top;
     const void *k_new;
     const void *v_new;
@@ -115,9 +117,11 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
             Linv[h] = NH > 1 ? 1.f / p.ml[((size_t)g * NH + h) * 2 + 1] : 0.f;
         }
     }
-    // Deferred gather: nact records per head hold this graph's spans.
+    // Deferred gather: nact records per head hold this graph's spans, and
+    // with centroid terms one more after them.
     const float *PR = p.part + (size_t)g * NH * p.nchunk * PS;
-    const int nact = n > 0 ? (n + kGatherTokens - 1) / kGatherTokens : 0;
+    const int nact = (n > 0 ? (n + kGatherTokens - 1) / kGatherTokens : 0) +
+                     ((defer && p.cent_n && p.cent_n[g] > 0) ? 1 : 0);
     const int jmax = min(p.t_cap, kIpt * 256);
     int cp[kIpt];
     float z[kIpt][NH];
@@ -380,6 +384,7 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         const size_t ci = ((size_t)g * p.c_cap + a) * D + tid;
         const double cs = p.csum[ci] + (double)to_f32(kn[tid]);
         p.csum[ci] = cs;
+        if (p.vsum) p.vsum[ci] += (double)to_f32(vn[tid]);
         cv = (float)(cs / (double)newsize);
         p.cent[((size_t)g * D + tid) * p.c_cap + a] = cv;
     }
@@ -464,7 +469,9 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
     p.ml = ml;
     p.out = out;
     p.part = part;
-    p.nchunk = ceil_div(t_cap, kGatherTokens);
+    p.nchunk = gather_slots(idx, t_cap);
+    p.cent_n = idx->cent_budget > 0 ? idx->cent_n : nullptr;
+    p.vsum = idx->cent_budget > 0 ? idx->vsum : nullptr;
     p.top = top;
     p.k_new = k_new;
     p.v_new = v_new;

@@ -39,7 +39,8 @@ struct AttendParams {
     float *ml;
     float *part;
     int32_t *ctr;
-    int nchunk;     // blocks per unit
+    const int32_t *cent_n;  // gather with a centroid budget: centroid terms per graph (else null)
+    int nchunk;     // record slots per unit and head
     int g0;         // first unit of the launch window
     int units;      // units in the launch
 };
@@ -73,14 +74,47 @@ constexpr int pick_u() {
     return (NH >= 8 || RowSlice<T, D>::BYTES == 32) ? 4 : 8;
 }
 
+// Combine of the unit's first nrec records into out and ml (the last block of
+// the unit, or the first block of a unit whose only record is its centroid
+// terms'), then the reset of the unit's arrival counter.
+template <int D, int NH, bool DENSE>
+__device__ __forceinline__ void attend_combine(const AttendParams &a, int unit, int b, int qh0, int nrec,
+                                               CombineLds<NH> &s_comb) {
+    constexpr int PS = part_stride(D);
+    const int tid = threadIdx.x;
+    const float *P = a.part + (size_t)unit * NH * a.nchunk * PS;
+    float *o = a.out + ((size_t)b * a.Hq + qh0) * D;
+    float *mlu = a.ml ? a.ml + (size_t)unit * NH * 2 : nullptr;
+    constexpr int NB = kCombineBatch;
+    if (nrec <= NB) {  // accumulators and (m, l) in one round trip
+        float v[combine_pairs<D, NH, 256>()][NB];
+        combine_preload<D, NH, PS, true, 256, NB>(P, a.nchunk, nrec, tid, v);
+        combine_stage<NH, D, PS, true>(P, a.nchunk, nrec, s_comb);
+        __syncthreads();
+        combine_heads<NH>(nrec, s_comb);
+        __syncthreads();
+        combine_out_regs<D, NH, 256, NB>(nrec, s_comb, tid, v, o, mlu);
+    } else if (nrec <= kCombineLds) {
+        combine_stage<NH, D, PS, true>(P, a.nchunk, nrec, s_comb);
+        __syncthreads();
+        combine_heads<NH>(nrec, s_comb);
+        __syncthreads();
+        combine_out<D, NH, PS, true, 256>(P, a.nchunk, nrec, s_comb, tid, o, mlu);
+    } else {
+        combine_out_long<D, NH, PS, true, 256>(P, a.nchunk, nrec, tid, o, mlu);
+    }
+    if (tid == 0) reset_counter(&a.ctr[unit]);
+}
+
 // Block epilogue shared by the gather kernels.  The four waves' softmax states
 // (s_wm, s_wl: max and sum per head; s_wacc: unnormalised accumulators) are
 // merged in a fixed order into the span's record; a deferred gather stops
-// there, a one-span list writes out and ml directly, otherwise the last block
-// of the unit combines every span's record.
+// there, a one-span list without centroid terms writes out and ml directly,
+// otherwise the last of the unit's nact span blocks combines every span's
+// record and, with ncent = 1, the centroid terms' record after them.
 template <int D, int NH, bool DENSE>
 __device__ __forceinline__ void attend_finish(const AttendParams &a, int unit, int b, int qh0, int chunk, int nact,
-                                              bool defer, float (&s_wm)[4][NH], float (&s_wl)[4][NH],
+                                              int ncent, bool defer, float (&s_wm)[4][NH], float (&s_wl)[4][NH],
                                               float (&s_wacc)[4][NH][D], CombineLds<NH> &s_comb, int &s_last) {
     constexpr int PS = part_stride(D);
     const int tid = threadIdx.x;
@@ -107,7 +141,7 @@ __device__ __forceinline__ void attend_finish(const AttendParams &a, int unit, i
                 dst[D] = M;
                 dst[D + 1] = L;
             }
-        } else if (nact == 1) {
+        } else if (nact + ncent == 1) {
             a.out[((size_t)b * a.Hq + qh0 + h) * D + d] = o / L;
             if (a.ml && d == 0) {
                 a.ml[((size_t)unit * NH + h) * 2] = M;
@@ -123,7 +157,7 @@ __device__ __forceinline__ void attend_finish(const AttendParams &a, int unit, i
     }
     if constexpr (!DENSE) CKV_TMARK(23);
     if constexpr (!DENSE) CKV_BMARK(3);
-    if (nact == 1 || defer) return;
+    if (nact + ncent == 1 || defer) return;
 
     // The last block of the unit combines every block's partial.
     stores_done();
@@ -132,29 +166,7 @@ __device__ __forceinline__ void attend_finish(const AttendParams &a, int unit, i
     __syncthreads();
     if constexpr (!DENSE) CKV_BMARK(4);
     if (!s_last) return;
-    {
-        float *o = a.out + ((size_t)b * a.Hq + qh0) * D;
-        float *mlu = a.ml ? a.ml + (size_t)unit * NH * 2 : nullptr;
-        constexpr int NB = kCombineBatch;
-        if (nact <= NB) {  // accumulators and (m, l) in one round trip
-            float v[combine_pairs<D, NH, 256>()][NB];
-            combine_preload<D, NH, PS, true, 256, NB>(P, a.nchunk, nact, tid, v);
-            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
-            __syncthreads();
-            combine_heads<NH>(nact, s_comb);
-            __syncthreads();
-            combine_out_regs<D, NH, 256, NB>(nact, s_comb, tid, v, o, mlu);
-        } else if (nact <= kCombineLds) {
-            combine_stage<NH, D, PS, true>(P, a.nchunk, nact, s_comb);
-            __syncthreads();
-            combine_heads<NH>(nact, s_comb);
-            __syncthreads();
-            combine_out<D, NH, PS, true, 256>(P, a.nchunk, nact, s_comb, tid, o, mlu);
-        } else {
-            combine_out_long<D, NH, PS, true, 256>(P, a.nchunk, nact, tid, o, mlu);
-        }
-    }
-    if (tid == 0) reset_counter(&a.ctr[unit]);
+    attend_combine<D, NH, DENSE>(a, unit, b, qh0, nact + ncent, s_comb);
     if constexpr (!DENSE) CKV_TMARK(24);
     if constexpr (!DENSE) CKV_BMARK(5);
 }
@@ -218,7 +230,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         }
         n = a.tok_n[unit];
     }
-    if (n <= 0 && chunk == 0 && !defer) {  // nothing to attend: zero output, empty softmax state
+    const int ncent = (!DENSE && a.cent_n && a.cent_n[unit] > 0) ? 1 : 0;
+    if (n <= 0 && chunk == 0 && !defer) {
+        if (ncent) {  // centroid terms only: their record is the unit's whole state
+            attend_combine<D, NH, DENSE>(a, unit, b, qh0, 1, s_comb);
+            return;
+        }
+        // nothing to attend: zero output, empty softmax state
         for (int i = tid; i < NH * D; i += 256) a.out[((size_t)b * a.Hq + qh0) * D + i] = 0.f;
         if (a.ml && tid < NH) {
             a.ml[((size_t)unit * NH + tid) * 2] = kNegInf;
@@ -375,7 +393,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
             for (int e = 0; e < E; ++e) s_wacc[wave][h][l16 * E + e] = acc[h][e];
         }
     }
-    attend_finish<D, NH, DENSE>(a, unit, b, qh0, chunk, nact, defer, s_wm, s_wl, s_wacc, s_comb, s_last);
+    attend_finish<D, NH, DENSE>(a, unit, b, qh0, chunk, nact, ncent, defer, s_wm, s_wl, s_wacc, s_comb, s_last);
 }
 
 // Query groups of four heads (bf16): the q.k products on the matrix cores.
@@ -421,7 +439,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     const int32_t *tl = a.tok_list + (size_t)unit * a.t_cap + start;
     const int pos_l = tid < min(PER_BLOCK, a.t_cap - start) ? tl[tid] : 0;
     const int n = a.tok_n[unit];
-    if (n <= 0 && chunk == 0 && !defer) {  // nothing to attend: zero output, empty softmax state
+    const int ncent = (a.cent_n && a.cent_n[unit] > 0) ? 1 : 0;
+    if (n <= 0 && chunk == 0 && !defer) {
+        if (ncent) {  // centroid terms only: their record is the unit's whole state
+            attend_combine<D, NH, false>(a, unit, b, qh0, 1, s_comb);
+            return;
+        }
+        // nothing to attend: zero output, empty softmax state
         for (int i = tid; i < NH * D; i += 256) a.out[((size_t)b * a.Hq + qh0) * D + i] = 0.f;
         if (a.ml && tid < NH) {
             a.ml[((size_t)unit * NH + tid) * 2] = kNegInf;
@@ -561,7 +585,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
             for (int e = 0; e < E; ++e) s_wacc[wave][h][l16 * E + e] = acc[h][e];
         }
     }
-    attend_finish<D, NH, false>(a, unit, b, qh0, chunk, nact, defer, s_wm, s_wl, s_wacc, s_comb, s_last);
+    attend_finish<D, NH, false>(a, unit, b, qh0, chunk, nact, ncent, defer, s_wm, s_wl, s_wacc, s_comb, s_last);
 }
 
 template <typename T, int D, int NH, bool DENSE>
@@ -569,7 +593,8 @@ static hipError_t launch_t(const AttendParams &p, int units, hipStream_t s) {
     constexpr int U = pick_u<T, D, NH>();
     AttendParams pu = p;
     pu.units = units;
-    CKV_LAUNCH((attend_kernel<T, D, NH, U, DENSE>), dim3(units * p.nchunk), dim3(256), s, pu);
+    const int nspan = p.nchunk - (p.cent_n ? 1 : 0);  // one block per span (the last slot is the centroids')
+    CKV_LAUNCH((attend_kernel<T, D, NH, U, DENSE>), dim3(units * nspan), dim3(256), s, pu);
     return hipGetLastError();
 }
 
@@ -615,14 +640,19 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
     p.ml = ml;
     p.part = part;
     p.ctr = ctr;
-    p.nchunk = ceil_div(t_cap, kGatherTokens);
+    p.nchunk = gather_slots(idx, t_cap);
     const Window w = window_of(idx);
     p.g0 = w.first;
     const int nh = heads_per_graph(kv, idx);
+    if (idx->cent_budget > 0) {  // the centroid terms' records first (no timing events: they stay armed)
+        p.cent_n = idx->cent_n;
+        const hipError_t e = launch_centroid_attend(kv, idx, q, tok_n, sm_scale, part, p.nchunk, s);
+        if (e != hipSuccess) return e;
+    }
     if (nh == 4 && kv->head_dim == 128 && kv->dtype == CKV_DTYPE_BF16) {  // query groups of four: matrix cores
         AttendParams pu = p;
         pu.units = w.count;
-        CKV_LAUNCH((attend_group4_kernel<128>), dim3(w.count * p.nchunk), dim3(256), s, pu);
+        CKV_LAUNCH((attend_group4_kernel<128>), dim3(w.count * (p.nchunk - (p.cent_n ? 1 : 0))), dim3(256), s, pu);
         return hipGetLastError();
     }
     return dispatch<false>(kv, nh, p, w.count, s);

@@ -54,6 +54,13 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Row stride of the base CSR offsets (c_cap + 1 used, padded for 16-byte rows).
 __host__ __device__ inline int offs_stride(int c_cap) { return c_cap + 4; }
 
+// Partial-record slots per graph and head of the gather: one per span of the
+// longest list, and with a centroid budget one more, for the centroid terms
+// (written at the slot right after the graph's last span).
+inline int gather_slots(const ckv_index *idx, int t_cap) {
+    return ceil_div(t_cap > 0 ? t_cap : 1, kGatherTokens) + (idx->cent_budget > 0 ? 1 : 0);
+}
+
 // Graphs a step call processes: [first, first + count).
 struct Window {
     int first, count;
@@ -125,7 +132,7 @@ inline WsLayout ws_layout(const ckv_kv *kv, const ckv_index *idx, int t_cap) {
     off += align256(cand_bytes(idx));
     L.cand_end = off;
     L.part_gather = off;
-    off += align256(4 * G * heads_per_graph(kv, idx) * (size_t)ceil_div(t_cap > 0 ? t_cap : 1, kGatherTokens) * D2);
+    off += align256(4 * G * heads_per_graph(kv, idx) * (size_t)gather_slots(idx, t_cap) * D2);
     L.build_cursor = off;
     off += align256(4 * G * (size_t)idx->c_cap);
     L.total = off;
@@ -172,6 +179,14 @@ hipError_t launch_assign(const ckv_kv *kv, const ckv_index *idx, const int32_t *
                          const int32_t *top, int kappa, const void *k_new, const void *v_new,
                          int32_t *edges, int32_t *assign, float *out, const float *part, int32_t *ctr,
                          hipStream_t s);
+
+// Centroid budget: the communities whose centroids each graph's step attends
+// (after the selection), and the softmax state of those centroid terms (into
+// the gather's record slot after the graph's last span, before the gather).
+hipError_t launch_centroid_select(const ckv_kv *kv, const ckv_index *idx, const void *q, const float *scores,
+                                  const int32_t *sel, const int32_t *sel_n, hipStream_t s);
+hipError_t launch_centroid_attend(const ckv_kv *kv, const ckv_index *idx, const void *q, const int32_t *tok_n,
+                                  float sm_scale, float *part, int nslots, hipStream_t s);
 
 // The gather with its partials and counters in the library's static scratch.
 size_t noalloc_gather_bytes(const ckv_kv *kv, const ckv_index *idx, int t_cap);

@@ -72,6 +72,7 @@ struct BuildParams {
     int32_t *toks;
     int32_t *label;
     double *csum;
+    double *vsum;  // centroid budget: value sums (else null)
     float *cent;
     int16_t *cq;
     float *cscale;
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
     const int32_t *ptab = p.page_table + (size_t)gc.b * p.max_pages;
     const T *kvb = reinterpret_cast<const T *>(p.kv);
     const int smask = (1 << p.ps_log2) - 1;
-    static_assert(D <= 256, "one thread per dimension");
+    static_assert(2 * D <= 256, "one thread per dimension of the key sum and of the value sum");
     __shared__ float s_max[4];
     float cv = 0.f;
     if (tid < D) {
@@ -184,6 +185,16 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
         p.csum[((size_t)g * p.c_cap + c) * D + tid] = acc;
         cv = (float)(acc / (double)s);
         p.cent[((size_t)g * D + tid) * p.c_cap + c] = cv;
+    } else if (p.vsum && tid < 2 * D) {  // value sums, in the same member order
+        const int e = tid - D;
+        double acc = 0.0;
+        for (int i = 0; i < s; ++i) {
+            const int pos = mem[i];
+            const int page = ptab[pos >> p.ps_log2];
+            const size_t row = (((size_t)page * p.Hkv + gc.kh) << p.ps_log2) | (size_t)(pos & smask);
+            acc += (double)to_f32(kvb[row * 2 * D + D + e]);
+        }
+        p.vsum[((size_t)g * p.c_cap + c) * D + e] = acc;
     }
     // screening copy of the column: scale = max |cent| / 32767
     const float m = wave_max_f(fabsf(cv));
@@ -200,6 +211,7 @@ hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int3
     hipError_t e;
     if ((e = fill_u32(idx->size, G * C, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->csum, G * C * D * 2, 0u, s)) != hipSuccess) return e;
+    if (idx->cent_budget > 0 && (e = fill_u32(idx->vsum, G * C * D * 2, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->cent, G * C * D, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->cq, G * C * D / 2, 0u, s)) != hipSuccess) return e;  // C % 256 == 0
     if ((e = fill_u32(idx->cscale, G * C, 0u, s)) != hipSuccess) return e;
@@ -225,6 +237,7 @@ hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int3
     p.toks = idx->toks;
     p.label = idx->label;
     p.csum = idx->csum;
+    p.vsum = idx->cent_budget > 0 ? idx->vsum : nullptr;
     p.cq = idx->cq;
     p.cscale = idx->cscale;
     p.cent = idx->cent;

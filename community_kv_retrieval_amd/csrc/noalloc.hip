@@ -52,12 +52,12 @@ __global__ void zero_i32_kernel(int32_t *p, int n) {
 }  // namespace
 
 // Bytes of scratch a gather of this shape uses: the arrival counters of every
-// graph, then one partial record per graph, head and span (as in the
+// graph, then one partial record per graph, head and record slot (as in the
 // workspace).
 size_t noalloc_gather_bytes(const ckv_kv *kv, const ckv_index *idx, int t_cap) {
     const size_t G = (size_t)idx->n_graphs;
     const size_t ctr = align256(4 * G);
-    const size_t part = align256(4 * G * heads_per_graph(kv, idx) * (size_t)ceil_div(t_cap, kGatherTokens) *
+    const size_t part = align256(4 * G * heads_per_graph(kv, idx) * (size_t)gather_slots(idx, t_cap) *
                                  (size_t)part_stride(kv->head_dim));
     return ctr + part;
 }

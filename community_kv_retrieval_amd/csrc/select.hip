@@ -79,6 +79,9 @@ struct SelectParams {
     int32_t *tok_list;
     int32_t *tok_n;
     CandArrays cand;  // from the scoring kernel (cand.ncand == 0: none)
+    int cent_budget;  // centroid selection only
+    int32_t *cent_sel;
+    int32_t *cent_n;
 };
 
 struct SelShared {
@@ -1423,6 +1426,196 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, 
     CKV_SEL_D(64) CKV_SEL_D(128)
 #undef CKV_SEL_D
 #undef CKV_SEL
+    return hipErrorInvalidValue;  // c_cap and head_dim are validated before: not reached
+}
+
+// ---------------------------------------------------------------------------
+// Centroid budget (the CommunityKV page, Table 6, "Centroid Budget"): the N =
+// cent_budget best-ranked non-empty communities that the selection did not
+// take, as ascending ids in cent_sel[g][0 .. cent_n[g]).  One 1024-thread
+// block per graph; thread t owns communities t, t + 1024, ...  The ranking is
+// the selection's (exact score, then lower id), decided from the screening
+// intervals [L, U] the same way: the N-th largest L among the outsiders (a
+// radix select with unit weights) is a score that N of them reach, so an
+// outsider whose U is below it cannot be among the N, and only the others
+// (typically N and a few) get their exact score; a second radix select over
+// those exact keys takes the best N.  When more than kList outsiders are
+// left, every exact score is computed, slab by slab, instead.  Fewer than N
+// outsiders: all of them.
+template <int D, int EPT>
+__global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectParams p) {
+    __shared__ SelShared sh;
+    const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int C = p.c_cap, N = p.cent_budget;
+    const int nc = min(p.n_comm[g], C);
+    const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
+    float sv[EPT], scl[EPT];
+    int sz[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int c = tid + j * kSelThreads;
+        const bool ok = c < nc;
+        sv[j] = ok ? p.scores[(size_t)g * C + c] : kNegInf;
+        scl[j] = ok ? p.cscale[(size_t)g * C + c] : 0.f;
+        sz[j] = ok ? p.size[(size_t)g * C + c] : 0;
+    }
+    const int ntaken = p.sel_n[g];
+    load_qbar(p, gc, sh);
+    for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
+    if (tid == 0) sh.ccount = 0;
+    __syncthreads();
+    for (int i = tid; i < ntaken; i += kSelThreads) {
+        const int c = p.sel[(size_t)g * C + i];
+        atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+    }
+    float qn = sh.qabs[lane] * (lane < p.D ? 1.f : 0.f);
+    if (lane + 64 < p.D) qn += sh.qabs[lane + 64];
+    const float kq = wave_sum_f(qn) * kScreenK;
+    __syncthreads();
+
+    // Outsiders (non-empty, not taken) and their screening intervals.
+    uint32_t outs = 0u;
+    float up[EPT];
+    unsigned long long key[EPT];
+    int w0[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const int c = tid + j * kSelThreads;
+        const bool o = sz[j] > 0 && !((sh.bits[c >> 5] >> (c & 31)) & 1u);
+        const float e = screen_bound(sv[j], scl[j], kq);
+        outs |= (o ? 1u : 0u) << j;
+        up[j] = sv[j] + e;
+        key[j] = o ? comm_key(sv[j] - e, c) : 0ull;
+        w0[j] = 0;
+    }
+    // The N-th largest L (0: at most N - 1 outsiders, every one is chosen).
+    const unsigned long long tl = radix_cut<EPT>(key, w0, true, (long long)N - 1, sh);
+    // From here sh.bits marks the chosen communities.
+    for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
+    __syncthreads();
+    if (tl == 0ull) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int c = tid + j * kSelThreads;
+            if ((outs >> j) & 1u) atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+        }
+    } else {
+        // radix_cut's threshold is an upper end of the cut key's digit range
+        // (keys above it are the N - 1 larger ones): the N-th largest L is the
+        // largest key at or below it.
+        unsigned long long kc = 0ull;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (key[j] <= tl) kc = umax64(kc, key[j]);
+        kc = wave_max_u64(kc);
+        if (lane == 0) sh.ckey[tid >> 6] = kc;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSelThreads / 64; ++i) kc = umax64(kc, sh.ckey[i]);
+        const float ln = key_score(kc);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            if (((outs >> j) & 1u) && up[j] >= ln) {
+                const int slot = atomicAdd(&sh.ccount, 1);
+                if (slot < kList) {
+                    sh.u.ls.id[slot] = tid + j * kSelThreads;
+                    sh.u.ls.sz[slot] = sz[j];
+                }
+            }
+        }
+        __syncthreads();
+        const int ncand = sh.ccount;
+        if (ncand <= kList) {
+            exact_scores<D>(p, g, ncand, sh, true, 0);
+            __syncthreads();
+            constexpr int LPT = kList / kSelThreads;
+            unsigned long long k2[LPT];
+            int w2[LPT];
+#pragma unroll
+            for (int i = 0; i < LPT; ++i) {
+                const int e = tid + i * kSelThreads;
+                k2[i] = e < ncand ? sh.u.ls.key[e] : 0ull;
+                w2[i] = 0;
+            }
+            const unsigned long long t2 = radix_cut<LPT>(k2, w2, true, N, sh);
+#pragma unroll
+            for (int i = 0; i < LPT; ++i) {
+                if (k2[i] && (t2 == 0ull || k2[i] > t2)) {
+                    const int c = (int)(0xFFFFFFFFu - (uint32_t)k2[i]);
+                    atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+                }
+            }
+        } else {  // too many to list: every exact score, slab by slab
+            float ex[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) ex[j] = kNegInf;
+            for (int sl = 0; sl * kSlab < C; ++sl) {
+                const int n = min(kSlab, C - sl * kSlab);
+                exact_scores<D>(p, g, n, sh, false, sl);
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < EPT; ++j) {
+                    const int i = tid + j * kSelThreads - sl * kSlab;
+                    if (i >= 0 && i < n) ex[j] = sh.u.exs[i];
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                key[j] = ((outs >> j) & 1u) ? comm_key(ex[j], tid + j * kSelThreads) : 0ull;
+            const unsigned long long t2 = radix_cut<EPT>(key, w0, true, N, sh);
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                if (key[j] && (t2 == 0ull || key[j] > t2)) {
+                    const int c = tid + j * kSelThreads;
+                    atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // Ascending ids: word w of the bitmap (thread w) writes its communities
+    // after those of the words before it.
+    const uint32_t word = tid < C / 32 ? sh.bits[tid] : 0u;
+    int total;
+    int k = block_exclusive_scan<kSelThreads>(__popc(word), sh.scan, &total);
+    for (uint32_t m = word; m; m &= m - 1u) p.cent_sel[(size_t)g * N + k++] = tid * 32 + __ffs(m) - 1;
+    if (tid == 0) p.cent_n[g] = total;
+}
+
+hipError_t launch_centroid_select(const ckv_kv *kv, const ckv_index *idx, const void *q, const float *scores,
+                                  const int32_t *sel, const int32_t *sel_n, hipStream_t s) {
+    SelectParams p{};
+    p.scores = scores;
+    p.size = idx->size;
+    p.n_comm = idx->n_comm;
+    p.cscale = idx->cscale;
+    p.csum = idx->csum;
+    p.q = q;
+    p.bf16 = kv->dtype == CKV_DTYPE_BF16;
+    p.D = kv->head_dim;
+    p.mode = idx->mode;
+    p.Hq = kv->n_q_heads;
+    p.Hkv = kv->n_kv_heads;
+    p.c_cap = idx->c_cap;
+    p.sel = const_cast<int32_t *>(sel);
+    p.sel_n = const_cast<int32_t *>(sel_n);
+    p.cent_budget = idx->cent_budget;
+    p.cent_sel = idx->cent_sel;
+    p.cent_n = idx->cent_n;
+    const Window w = window_of(idx);
+    p.g0 = w.first;
+    const int ept = ceil_div(idx->c_cap, kSelThreads);
+    const dim3 grid(w.count), block(kSelThreads);
+#define CKV_CSEL(E, DD)                                                                   \
+    if (ept <= E && kv->head_dim == DD) {                                                 \
+        hipLaunchKernelGGL((centroid_select_kernel<DD, E>), grid, block, 0, s, p);       \
+        return hipGetLastError();                                                         \
+    }
+#define CKV_CSEL_D(DD) CKV_CSEL(1, DD) CKV_CSEL(2, DD) CKV_CSEL(4, DD) CKV_CSEL(8, DD) CKV_CSEL(16, DD)
+    CKV_CSEL_D(64) CKV_CSEL_D(128)
+#undef CKV_CSEL_D
+#undef CKV_CSEL
     return hipErrorInvalidValue;  // c_cap and head_dim are validated before: not reached
 }
 

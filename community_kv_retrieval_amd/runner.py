@@ -48,7 +48,7 @@ def load_layer(w: synth.Workload, seed: int, extra: int, layer: int = 0, device:
     if tail_cap is None:
         tail_cap = max(1, min(4096, extra))
     idx = ckv.CommunityIndex(kv, mode, n_comm, l_cap=cap, tail_cap=tail_cap,
-                             n_sinks=w.n_sinks, c_cap=c_cap, device=device)
+                             n_sinks=w.n_sinks, c_cap=c_cap, device=device, cent_budget=w.cent_budget)
     dec = ckv.Decoder(kv, idx, w.budget if budget is None else budget, w.max_comm, w.kappa, w.sm_scale, device)
     dec.build(torch.from_numpy(labels).to(device))
     return Layer(kv, idx, dec, slices, lens)
@@ -100,7 +100,7 @@ def load_stack(w: synth.Workload, seed: int, steps: int, device: str = "cuda", p
             labels[g, :lab.shape[0]] = torch.from_numpy(lab)
         gn = [int(n_comm[w.graph_coords(g)[0], w.graph_coords(g)[1]]) for g in range(w.n_graphs)]
         idx = ckv.CommunityIndex(kv, mode, gn, l_cap=cap, tail_cap=max(1, min(4096, steps)),
-                                 n_sinks=w.n_sinks, device=device)
+                                 n_sinks=w.n_sinks, device=device, cent_budget=w.cent_budget)
         dec = ckv.Decoder(kv, idx, w.budget, w.max_comm, w.kappa, w.sm_scale, device)
         dec.build(labels.to(device))
         out.append(StackLayer(kv, idx, dec, parts, q, kn, vn))

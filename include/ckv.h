@@ -83,6 +83,7 @@ typedef int32_t ckv_status;
 
 #define CKV_MAX_KAPPA 32
 #define CKV_MAX_C_CAP 16384
+#define CKV_MAX_CENT  256   /* largest centroid budget (Table 6 ablates 0, 4, 16, 64, 256) */
 /* Static device scratch of ckv_gather_attend_noalloc (bytes, per GPU). */
 #define CKV_NOALLOC_SCRATCH_BYTES (4u << 20)
 
@@ -140,6 +141,21 @@ typedef struct ckv_index {
      * ckv_index_build and ckv_dense_attend ignore the window. */
     int32_t  win_first;
     int32_t  win_count;
+    /* Centroid budget (Table 6, "Centroid Budget"; 0, the default, turns it
+     * off and the four arrays below may be NULL).  With cent_budget = N in
+     * 1 .. CKV_MAX_CENT the attention of each step also takes the centroids of
+     * the N best-ranked non-empty communities that the selection did not take
+     * (all of them when fewer are left): each is one softmax term with key
+     * mu_c = float32(csum[c] / size[c]) (the stored centroid), value
+     * float32(vsum[c] / size[c]) (the members' mean value) and logit
+     * sm_scale * q . mu_c + ln size[c], i.e. the mass of size[c] tokens whose
+     * key is the centroid.  Centroid terms never become edges, but their mass
+     * is part of the normaliser of every token's probability (and of ml). */
+    int32_t  cent_budget;
+    int32_t *cent_sel;   /* [G][cent_budget] those communities, ascending ids (ckv_select_communities) */
+    int32_t *cent_n;     /* [G] their count */
+    double  *vsum;       /* [G][c_cap][head_dim] exact float64 value sum of every community
+                            (ckv_index_build, ckv_assign_update) */
 } ckv_index;
 
 /* Bytes of workspace the calls below need for this layer shape and a token
@@ -160,7 +176,7 @@ ckv_status ckv_kv_write(const ckv_kv *kv, int32_t b, int32_t kv_head, int32_t po
  * community count.  Fills size, offs, toks, label, csum, cent (the centroid
  * is the mean of the members' keys; Figure 1 panel (2) draws one per
  * community) and its screening copy cq/cscale, empties the tails and clears
- * status. */
+ * status.  With a centroid budget it also fills vsum, the members' value sums. */
 ckv_status ckv_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t *labels_in,
                            void *ws, size_t ws_bytes, ckv_stream_t stream);
 
@@ -199,7 +215,9 @@ ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const voi
  * candidates to (at least ckv_workspace_bytes(kv, idx, 0) bytes).  The
  * selection works on the candidates when they provably hold every community
  * the result depends on, and on every community otherwise; the result is the
- * same either way. */
+ * same either way.  With idx->cent_budget > 0 a second kernel then writes
+ * idx->cent_sel and idx->cent_n: the cent_budget best-ranked non-empty
+ * communities outside sel, ranked by exact score as above. */
 ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const void *q,
                                   const float *scores, int32_t budget, int32_t max_comm, int32_t t_cap,
                                   int32_t *sel, int32_t *sel_n, int32_t *top,
@@ -219,7 +237,12 @@ ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const 
  * ws, tok_list, tok_n and t_cap with a non-NULL out then writes out and ml,
  * bit for bit as this call would have (the combine then overlaps the assign's
  * own work instead of ending the gather).  Exactly one of out, ml NULL:
- * CKV_E_INVALID. */
+ * CKV_E_INVALID.
+ * With idx->cent_budget > 0 the call first attends each graph's centroid
+ * terms (idx->cent_sel, idx->cent_n) in a kernel of its own, which leaves one
+ * more softmax state per head after the spans' (ceil(t_cap / 256) + 1 states
+ * per head in all); the combine takes it last, and out and ml cover tokens
+ * and centroid terms alike. */
 ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void *q,
                              const int32_t *tok_list, const int32_t *tok_n, int32_t t_cap,
                              float sm_scale, float *out, float *logits, float *ml,
@@ -233,7 +256,8 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
  * of the library, CKV_NOALLOC_SCRATCH_BYTES per GPU, held until the process
  * ends; the call allocates nothing.  The scratch need is 256-aligned
  * 4 * n_graphs bytes of counters plus 4 * n_graphs * heads_per_graph *
- * ceil(t_cap / 256) * (32 * ceil((head_dim + 2) / 32)) bytes of records; a
+ * nspan * (32 * ceil((head_dim + 2) / 32)) bytes of records, nspan =
+ * ceil(t_cap / 256), plus one with a centroid budget; a
  * larger need returns CKV_E_WORKSPACE before anything is enqueued.  Every call
  * on one GPU shares that GPU's array: calls that overlap on one GPU (other
  * streams, other host threads) race and must be ordered by the caller.  The
@@ -254,7 +278,8 @@ ckv_status ckv_gather_attend_noalloc(const ckv_kv *kv, const ckv_index *idx, con
  * lower position, become edges[G][kappa] (-1 padded); the new token goes to the
  * community holding most edges, ties to the lowest id (top[g] if there is no
  * edge): assign[G].  Then, at P = seq_len[b]: label[P] = a, P joins a's tail,
- * size[a] += 1, csum[a] += k_new, cent[a] = float32(csum[a] / size[a]); k_new,
+ * size[a] += 1, csum[a] += k_new, cent[a] = float32(csum[a] / size[a]) (and
+ * vsum[a] += v_new with a centroid budget); k_new,
  * v_new ([batch][n_kv_heads][head_dim] of kv->dtype) are stored at P, and
  * finally seq_len[b] += 1.
  * out == NULL: the gather was complete and its ml (required) is read.
@@ -332,7 +357,9 @@ ckv_status ckv_read_rows(const ckv_kv *kv, const uint32_t *rows, int32_t n, uint
 /* Kernel timing for profiling harnesses (no part of the method).  Arms the
  * calling host thread so that the next kernel launched by one of
  * ckv_score_centroids, ckv_select_communities, ckv_gather_attend,
- * ckv_assign_update, ckv_dense_attend, ckv_read_rows (each launches exactly one kernel) or
+ * ckv_assign_update, ckv_dense_attend, ckv_read_rows (each launches exactly one
+ * kernel without a centroid budget; with one, select and gather time their
+ * main kernel, not the centroid kernel) or
  * ckv_prefill_topk (one kernel per head; the query-group mode launches two and
  * the pair times the first) has `start` and `stop` recorded by its own dispatch (hipExtLaunchKernel):
  * hipEventElapsedTime(start, stop) is then that kernel's execution time, with

@@ -43,6 +43,9 @@ class Stats:
     max_abs: float = 0.0
     max_rel: float = 0.0
     dense_equal: int = 0
+    near_cent: int = 0
+    cent_terms: int = 0
+    cent_visible: int = 0   # graphs whose output the centroid terms move beyond the output tolerance
     gaps: List[float] = field(default_factory=list)
 
 
@@ -76,6 +79,8 @@ def check_index_state(layer, orc: O.Oracle, w: synth.Workload, full: bool = Fals
         check_screening_copy(idx, g, C, cent)
         if full:
             np.testing.assert_array_equal(idx.csum[g, :C].cpu().numpy(), st.sums, err_msg=f"csum g={g}")
+            if idx.cent_budget > 0:
+                np.testing.assert_array_equal(idx.vsum[g, :C].cpu().numpy(), st.vsums, err_msg=f"vsum g={g}")
             n = orc.len[st.b]
             np.testing.assert_array_equal(idx.label[g, :n].cpu().numpy(), st.labels[:n], err_msg=f"label g={g}")
 
@@ -146,29 +151,38 @@ def _count(stats: Stats, field_name: str) -> bool:
 
 
 def _check_logits(H, g, tl, r, where):
-    slot = {int(p): i for i, p in enumerate(tl)}
-    idxs = np.array([slot[int(p)] for p in r.positions])
-    gl = H["logits"][g][:, idxs]
-    assert np.abs(gl - r.logits).max() <= LOGIT_ATOL * max(1.0, np.abs(r.logits).max()), f"{where}: logits"
-    np.testing.assert_allclose(H["ml"][g][:, 0], r.logits.max(axis=1), atol=LOGIT_ATOL * 20)
-    lsum = np.exp(r.logits - r.logits.max(axis=1, keepdims=True)).sum(axis=1)
-    np.testing.assert_allclose(H["ml"][g][:, 1], lsum, rtol=1e-4)
+    """Token logits of every slot, and the softmax state (max, sum) over the
+    tokens and the centroid terms of a centroid budget."""
+    if r.positions.size:
+        slot = {int(p): i for i, p in enumerate(tl)}
+        idxs = np.array([slot[int(p)] for p in r.positions])
+        gl = H["logits"][g][:, idxs]
+        assert np.abs(gl - r.logits).max() <= LOGIT_ATOL * max(1.0, np.abs(r.logits).max()), f"{where}: logits"
+    z = np.concatenate([r.logits, r.cent_logits], axis=1) if r.cent.size else r.logits
+    np.testing.assert_allclose(H["ml"][g][:, 0], z.max(axis=1), atol=LOGIT_ATOL * 20, err_msg=f"{where}: ml max")
+    lsum = np.exp(z - z.max(axis=1, keepdims=True)).sum(axis=1)
+    np.testing.assert_allclose(H["ml"][g][:, 1], lsum, rtol=1e-4, err_msg=f"{where}: ml sum")
 
 
-def snapshot(buf, cscale) -> Dict[str, np.ndarray]:
+def snapshot(buf, cscale, idx=None) -> Dict[str, np.ndarray]:
     """Host copies of a decoder's step outputs, plus the screening scales the
-    step scored with (taken before its update changed them)."""
+    step scored with (taken before its update changed them) and, with a
+    centroid budget, the index's centroid communities of the step."""
     H = {k: getattr(buf, k).cpu().numpy() for k in
          ("sel", "sel_n", "top", "tok_list", "tok_n", "out", "logits", "ml", "edges", "assign", "scores")}
     H["cscale"] = cscale.cpu().numpy()
+    if idx is not None and idx.cent_budget > 0:
+        H["cent_sel"] = idx.cent_sel.cpu().numpy()
+        H["cent_n"] = idx.cent_n.cpu().numpy()
     return H
 
 
 def check_graph(H, g: int, orc: O.Oracle, qn: np.ndarray, k_new: np.ndarray, w: synth.Workload, stats: Stats,
-                where: str, dense: Optional[torch.Tensor] = None):
+                where: str, dense: Optional[torch.Tensor] = None, v_new: Optional[np.ndarray] = None):
     """Every output of graph g's step against the oracle's step on the same
     query, then the oracle applies the device's (checked) assignment.
-    qn: [B][Hq][d] the step's queries; k_new: [B][Hkv][d] the new keys."""
+    qn: [B][Hq][d] the step's queries; k_new, v_new: [B][Hkv][d] the new keys
+    and values (v_new: for the value sums of a centroid budget)."""
     st = orc.g[g]
     gsel = H["sel"][g, :H["sel_n"][g]]
     assert (np.diff(gsel) > 0).all(), f"{where}: sel not ascending"
@@ -177,12 +191,24 @@ def check_graph(H, g: int, orc: O.Oracle, qn: np.ndarray, k_new: np.ndarray, w: 
     assert H["top"][g] == r.top, f"{where}: top {H['top'][g]} != {r.top}"
     if not _selection_ok(r, st.counts, gsel, w, stats, where):
         r = orc.step_graph(g, qn, force_sel=gsel)
+    gcent = None
+    if w.cent_budget > 0:
+        gcent = H["cent_sel"][g, :H["cent_n"][g]]
+        assert (np.diff(gcent) > 0).all(), f"{where}: centroid communities not ascending"
+        if not D.centroids_ok(r.scores, st.counts, gsel, r.cent, gcent, w.cent_budget, where, stats.gaps):
+            stats.near_cent += 1
+            r = orc.step_graph(g, qn, force_sel=gsel, force_cent=gcent)
+        stats.cent_terms += int(gcent.size)
     tl = H["tok_list"][g, :H["tok_n"][g]]
     assert tl.size == np.unique(tl).size, f"{where}: duplicate token"
     np.testing.assert_array_equal(np.sort(tl), r.positions, err_msg=f"{where}: token set")
     gout = H["out"][st.b, st.qh0:st.qh0 + st.nh].astype(np.float64)
     err = np.abs(gout - r.out)
     assert np.all(err <= ATOL + RTOL * np.abs(r.out)), f"{where}: attention max abs err {err.max():.3g}"
+    if r.cent.size:  # would the check above see the centroid terms?  (the test's power)
+        r0 = orc.step_graph(g, qn, force_sel=gsel, force_cent=[])
+        if np.any(np.abs(r0.out - r.out) > ATOL + RTOL * np.abs(r.out)):
+            stats.cent_visible += 1
     stats.max_abs = max(stats.max_abs, float(err.max()))
     stats.max_rel = max(stats.max_rel, float((err / np.maximum(np.abs(r.out), 1e-3)).max()))
     if dense is not None:
@@ -194,7 +220,7 @@ def check_graph(H, g: int, orc: O.Oracle, qn: np.ndarray, k_new: np.ndarray, w: 
             assert np.all(np.abs(gout - dref) <= ATOL + RTOL * np.abs(dref)), f"{where}: sparse vs dense"
             stats.dense_equal += 1
     # logits of every slot, and the softmax state (empty: max -inf, sum 0)
-    if r.positions.size == 0:
+    if r.positions.size == 0 and r.cent.size == 0:
         assert np.all(H["ml"][g][:, 0] == -np.inf) and np.all(H["ml"][g][:, 1] == 0), f"{where}: empty ml"
     else:
         _check_logits(H, g, tl, r, where)
@@ -202,9 +228,9 @@ def check_graph(H, g: int, orc: O.Oracle, qn: np.ndarray, k_new: np.ndarray, w: 
     ne = int((ge >= 0).sum())
     assert (ge[ne:] == -1).all(), f"{where}: edges not -1 padded"
     if not _edges_ok(r, ge[:ne], w, stats, where):
-        r = orc.step_graph(g, qn, force_sel=gsel, force_edges=ge[:ne])
+        r = orc.step_graph(g, qn, force_sel=gsel, force_edges=ge[:ne], force_cent=gcent)
     assert H["assign"][g] == r.assign, f"{where}: assign {H['assign'][g]} != {r.assign}"
-    orc.apply_update(g, int(H["assign"][g]), k_new[st.b, st.kh])
+    orc.apply_update(g, int(H["assign"][g]), k_new[st.b, st.kh], None if v_new is None else v_new[st.b, st.kh])
     stats.graphs += 1
     return r
 
@@ -245,13 +271,15 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
                 dec.dense(q, dense)
             dec.update(kn, vn)
         torch.cuda.synchronize()
-        H = snapshot(buf, cscale)
+        H = snapshot(buf, cscale, layer.idx)
         assert int(layer.idx.status.item()) == 0, f"step {t}: device status {int(layer.idx.status.item())}"
         qn = inp.q.float().numpy()
         kn_host = inp.k_new.float().numpy()
+        vn_host = inp.v_new.float().numpy()
         for g in orc.graph_ids:
-            check_graph(H, g, orc, qn, kn_host, w, stats, f"{w.name} seed={seed} step={t} graph={g}", dense)
-        orc.append(kn_host, inp.v_new.float().numpy())
+            check_graph(H, g, orc, qn, kn_host, w, stats, f"{w.name} seed={seed} step={t} graph={g}", dense,
+                        vn_host)
+        orc.append(kn_host, vn_host)
         stats.steps += 1
         done = t + 1 - first_step
         if check_state_every and done % check_state_every == 0:

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ckv.LIB.ckv_abi_version() == 8
+    assert ckv.LIB.ckv_abi_version() == 9
     for code in (0, -1, -2, -3, -4):
         assert ckv.ckv_status_str(code) != "unknown status"
     assert ckv.ckv_status_str(7) == "unknown status"
@@ -102,6 +102,28 @@ def test_kv_validation(kw, code):
 def test_index_validation(kw):
     kv, idx = _kv(), _idx(**kw)
     assert ckv.LIB.ckv_score_centroids(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, BIG, None) == ckv.CKV_E_INVALID
+
+
+@pytest.mark.parametrize("kw", [dict(cent_budget=-1), dict(cent_budget=257),
+                                dict(cent_budget=4),  # arrays missing
+                                dict(cent_budget=4, cent_sel=FAKE, cent_n=FAKE),  # no value sums
+                                dict(cent_budget=4, cent_sel=FAKE, vsum=FAKE),
+                                dict(cent_budget=4, cent_n=FAKE, vsum=FAKE)])
+def test_centroid_budget_validation(kw):
+    kv, idx = _kv(), _idx(**kw)
+    for f in (ckv.LIB.ckv_score_centroids,):
+        assert f(ctypes.byref(kv), ctypes.byref(idx), FAKE, FAKE, FAKE, BIG, None) == ckv.CKV_E_INVALID
+    assert _ws(kv, idx, 4100) == 0
+
+
+def test_centroid_budget_adds_one_record_slot():
+    """With a centroid budget every graph and head has one more partial record
+    (the centroid terms'), after its spans: 17 + 1 slots for t_cap 4100."""
+    kv = _kv()
+    off = _idx()
+    on = _idx(cent_budget=16, cent_sel=FAKE, cent_n=FAKE, vsum=FAKE)
+    assert _ws(kv, on, 4100) - _ws(kv, off, 4100) == 4 * 32 * 160
+    assert ckv.CKV_MAX_CENT == 256
 
 
 @pytest.mark.parametrize("first,count", [(0, -1), (-1, 4), (1, 0), (30, 3), (32, 1)])

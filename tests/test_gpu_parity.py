@@ -473,3 +473,71 @@ def test_attention_mass_recall_matches_oracle(group):
         dec.update(inp.k_new.cuda(), inp.v_new.cuda())
         torch.cuda.synchronize()
         orc.append(inp.k_new.float().numpy(), inp.v_new.float().numpy())
+
+
+# ---------------------------------------------------------------------------
+# Centroid budget (Table 6): the step also attends the centroids of the
+# next-ranked communities after the selection, each as one softmax term.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [synth.PER_HEAD, synth.GROUP])
+@pytest.mark.parametrize("cent_budget,defer", [(4, True), (64, False), (256, True)])
+def test_centroid_budget(mode, cent_budget, defer):
+    """The centroid communities (a tie-consistent continuation of the ranking
+    past the selection), the attention output over tokens and centroid terms,
+    the softmax state, the edges and the value sums, every step; complete and
+    deferred gathers, per-head and query-group (matrix-core) gathers.  The
+    queries are scaled by 0.3, which flattens the softmax so that the centroid
+    terms move every graph's output by many times the output tolerance (the
+    harness counts the graphs where they do)."""
+    w = small_per_head(mode=mode, n_ctx=9000, budget=600, steps=4, cent_budget=cent_budget)
+    PY.log(f"centroid budget {cent_budget} {mode} defer={defer}")
+    st = PY.run_steps(w, 21, w.steps, defer=defer, q_fn=lambda t, q: q * 0.3)
+    PY.log(f"  centroid terms {st.cent_terms}, near-tie sets {st.near_cent}, visible in {st.cent_visible} "
+           f"of {st.graphs} graphs, max abs {st.max_abs:.2e}")
+    assert st.cent_terms >= st.graphs * cent_budget
+    assert st.cent_visible >= st.graphs // 2, (st.cent_visible, st.graphs)
+
+
+@pytest.mark.parametrize("mode", [synth.PER_HEAD, synth.GROUP])
+def test_centroid_terms_only(mode):
+    """No sinks and a zero budget: the token list is empty and the centroid
+    terms are the whole attention (complete and deferred gathers)."""
+    for defer in (False, True):
+        w = small_per_head(mode=mode, n_ctx=2000, budget=0, n_sinks=0, steps=2, cent_budget=16)
+        PY.log(f"centroid terms only {mode} defer={defer}")
+        st = PY.run_steps(w, 22, w.steps, defer=defer)
+        assert st.cent_terms == st.graphs * 16
+
+
+def test_centroid_budget_past_the_communities():
+    """A budget larger than the communities the selection leaves: every one of
+    them is attended as a centroid term."""
+    w = small_per_head(n_ctx=1500, budget=300, steps=3, cent_budget=256)
+    PY.log("centroid budget past the communities")
+    PY.run_steps(w, 23, w.steps)
+
+
+def test_centroid_budget_long_lists_and_windows():
+    """Token lists of more spans than the assign kernel preloads (its
+    deferred combine reads the centroid record after 36 span records), and the
+    windowed multi-stream step."""
+    w = small_per_head(n_ctx=14000, budget=9000, n_kv_heads=2, n_q_heads=8, steps=2, cent_budget=64)
+    PY.log("centroid budget, long lists")
+    PY.run_steps(w, 24, w.steps)
+    w = small_group(steps=3, cent_budget=16)
+    PY.log("centroid budget, two windows")
+    PY.run_steps(w, 25, w.steps, windows=2)
+
+
+@pytest.mark.parametrize("n_ctx,mean_size", [(3000, 16), (40000, 8)])
+def test_centroid_budget_zero_query(n_ctx, mean_size):
+    """A zero query ties every community at score 0: the centroid communities
+    are the lowest ids past the selection, decided without any tie window.
+    The second case leaves more than 2048 outsiders within the screening
+    range, so the centroid selection computes every exact score."""
+    w = small_per_head(n_ctx=n_ctx, mean_size=mean_size, min_size=2, n_kv_heads=2, n_q_heads=4, steps=2,
+                       cent_budget=256)
+    PY.log(f"centroid budget, zero query, n_ctx={n_ctx}")
+    st = PY.run_steps(w, 26, w.steps, q_fn=lambda t, q: torch.zeros_like(q))
+    assert st.near_sel == 0 and st.near_cent == 0 and st.near_edges == 0

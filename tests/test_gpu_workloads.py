@@ -92,3 +92,16 @@ def test_qwen3_8b_stream_36_layers_sampled():
     for L in stack:
         assert int(L.idx.status.item()) == 0
     _report(w, stats)
+
+
+@pytest.mark.parametrize("name,cent_budget", [("llama31_8b_128k", 64), ("llama31_8b_128k_group_b8", 256)])
+def test_centroid_budget_full_size(name, cent_budget):
+    """Table 6's centroid budget at the 128K workloads' full size, on every
+    graph for 24 steps: the centroid communities, the output over tokens and
+    centroid terms, the softmax state, edges and value sums."""
+    w = synth.preset(name).replace(cent_budget=cent_budget)
+    PY.log(f"{w.name}: centroid budget {cent_budget}, 24 steps on all {w.n_graphs} graphs, seed {BENCH_SEED}")
+    st = PY.run_steps(w, BENCH_SEED, 24, check_state_every=12)
+    _report(w, st)
+    PY.log(f"  centroid terms {st.cent_terms}, near-tie sets {st.near_cent}, visible in {st.cent_visible} graphs")
+    assert st.cent_terms >= st.graphs * cent_budget
