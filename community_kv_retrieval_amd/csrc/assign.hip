@@ -46,7 +46,7 @@ struct AssignParams {
     float *out;          // not null: combine the deferred gather's records into out
     const float *part;   // the gather's partial records
     int nchunk;          // gather record slots per graph and head
-    const int32_t *cent_n;  // centroid budget: centroid terms per graph (their record follows the spans')
+    const int32_t *cent_n;  // centroid budget: centroid terms per graph (their records follow the spans')
     double *vsum;        // centroid budget: value sums (else null)
     const int32_t *top;
     const void *k_new;
@@ -118,10 +118,10 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         }
     }
     // Deferred gather: nact records per head hold this graph's spans, and
-    // with centroid terms one more after them.
+    // then its centroid terms' records.
     const float *PR = p.part + (size_t)g * NH * p.nchunk * PS;
     const int nact = (n > 0 ? (n + kGatherTokens - 1) / kGatherTokens : 0) +
-                     ((defer && p.cent_n && p.cent_n[g] > 0) ? 1 : 0);
+                     ((defer && p.cent_n) ? cent_records(p.cent_n[g]) : 0);
     const int jmax = min(p.t_cap, kIpt * 256);
     int cp[kIpt];
     float z[kIpt][NH];

@@ -40,6 +40,7 @@ struct AttendParams {
     float *part;
     int32_t *ctr;
     const int32_t *cent_n;  // gather with a centroid budget: centroid terms per graph (else null)
+    int cent_slots;         // record slots of the centroid terms per graph and head
     int nchunk;     // record slots per unit and head
     int g0;         // first unit of the launch window
     int units;      // units in the launch
@@ -75,7 +76,7 @@ constexpr int pick_u() {
 }
 
 // Combine of the unit's first nrec records into out and ml (the last block of
-// the unit, or the first block of a unit whose only record is its centroid
+// the unit, or the first block of a unit whose only records are its centroid
 // terms'), then the reset of the unit's arrival counter.
 template <int D, int NH, bool DENSE>
 __device__ __forceinline__ void attend_combine(const AttendParams &a, int unit, int b, int qh0, int nrec,
@@ -111,7 +112,7 @@ __device__ __forceinline__ void attend_combine(const AttendParams &a, int unit, 
 // merged in a fixed order into the span's record; a deferred gather stops
 // there, a one-span list without centroid terms writes out and ml directly,
 // otherwise the last of the unit's nact span blocks combines every span's
-// record and, with ncent = 1, the centroid terms' record after them.
+// record and the ncent records of the centroid terms after them.
 template <int D, int NH, bool DENSE>
 __device__ __forceinline__ void attend_finish(const AttendParams &a, int unit, int b, int qh0, int chunk, int nact,
                                               int ncent, bool defer, float (&s_wm)[4][NH], float (&s_wl)[4][NH],
@@ -230,10 +231,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         }
         n = a.tok_n[unit];
     }
-    const int ncent = (!DENSE && a.cent_n && a.cent_n[unit] > 0) ? 1 : 0;
+    const int ncent = (!DENSE && a.cent_n) ? cent_records(a.cent_n[unit]) : 0;
     if (n <= 0 && chunk == 0 && !defer) {
-        if (ncent) {  // centroid terms only: their record is the unit's whole state
-            attend_combine<D, NH, DENSE>(a, unit, b, qh0, 1, s_comb);
+        if (ncent) {  // centroid terms only: their records are the unit's whole state
+            attend_combine<D, NH, DENSE>(a, unit, b, qh0, ncent, s_comb);
             return;
         }
         // nothing to attend: zero output, empty softmax state
@@ -439,10 +440,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
     const int32_t *tl = a.tok_list + (size_t)unit * a.t_cap + start;
     const int pos_l = tid < min(PER_BLOCK, a.t_cap - start) ? tl[tid] : 0;
     const int n = a.tok_n[unit];
-    const int ncent = (a.cent_n && a.cent_n[unit] > 0) ? 1 : 0;
+    const int ncent = a.cent_n ? cent_records(a.cent_n[unit]) : 0;
     if (n <= 0 && chunk == 0 && !defer) {
-        if (ncent) {  // centroid terms only: their record is the unit's whole state
-            attend_combine<D, NH, false>(a, unit, b, qh0, 1, s_comb);
+        if (ncent) {  // centroid terms only: their records are the unit's whole state
+            attend_combine<D, NH, false>(a, unit, b, qh0, ncent, s_comb);
             return;
         }
         // nothing to attend: zero output, empty softmax state
@@ -593,7 +594,7 @@ static hipError_t launch_t(const AttendParams &p, int units, hipStream_t s) {
     constexpr int U = pick_u<T, D, NH>();
     AttendParams pu = p;
     pu.units = units;
-    const int nspan = p.nchunk - (p.cent_n ? 1 : 0);  // one block per span (the last slot is the centroids')
+    const int nspan = p.nchunk - p.cent_slots;  // one block per span (the slots after them are the centroids')
     CKV_LAUNCH((attend_kernel<T, D, NH, U, DENSE>), dim3(units * nspan), dim3(256), s, pu);
     return hipGetLastError();
 }
@@ -646,13 +647,14 @@ hipError_t launch_gather(const ckv_kv *kv, const ckv_index *idx, const void *q,
     const int nh = heads_per_graph(kv, idx);
     if (idx->cent_budget > 0) {  // the centroid terms' records first (no timing events: they stay armed)
         p.cent_n = idx->cent_n;
+        p.cent_slots = cent_records(idx->cent_budget);
         const hipError_t e = launch_centroid_attend(kv, idx, q, tok_n, sm_scale, part, p.nchunk, s);
         if (e != hipSuccess) return e;
     }
     if (nh == 4 && kv->head_dim == 128 && kv->dtype == CKV_DTYPE_BF16) {  // query groups of four: matrix cores
         AttendParams pu = p;
         pu.units = w.count;
-        CKV_LAUNCH((attend_group4_kernel<128>), dim3(w.count * (p.nchunk - (p.cent_n ? 1 : 0))), dim3(256), s, pu);
+        CKV_LAUNCH((attend_group4_kernel<128>), dim3(w.count * (p.nchunk - p.cent_slots)), dim3(256), s, pu);
         return hipGetLastError();
     }
     return dispatch<false>(kv, nh, p, w.count, s);

@@ -5,15 +5,15 @@
 // float32(vsum / n), the members' mean value; logit sm_scale * q . mu + ln n
 // (the mass of n tokens whose key is the centroid).
 //
-// One 256-thread block per graph, laid out like a gather block: 16-lane rows,
-// row r of the block taking centroids r, r + 16, ...; lane l16 of a row holds
-// dimensions [l16 E, l16 E + E) of mu and of the value (E = D / 16), loaded
-// as float64 sums and divided once.  Each row keeps an online softmax state
-// per head; the four rows of a wave merge with lane shuffles, the four waves
-// in a fixed order through LDS.  The result is one more partial record of the
-// gather, written to the slot right after the graph's spans (ceil(tok_n /
-// 256)), which the gather's combine, or the assign kernel's for a deferred
-// gather, takes after the spans' records.
+// One 256-thread block per graph and group of kCentPerRecord (16) terms, laid
+// out like a gather block: 16-lane rows, row r taking the group's term r;
+// lane l16 of a row holds dimensions [l16 E, l16 E + E) of mu and of the
+// value (E = D / 16), loaded as float64 sums and divided once.  The four rows
+// of a wave merge their softmax states with lane shuffles, the four waves in
+// a fixed order through LDS.  Each block's result is one more partial record
+// of the gather: group j of a graph goes to the slot ceil(tok_n / 256) + j,
+// right after the graph's spans, and the gather's combine (or the assign
+// kernel's, for a deferred gather) takes those records after the spans'.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -29,7 +29,7 @@ struct CentParams {
     const int32_t *tok_n;
     float *part;
     float sm_scale;
-    int mode, Hq, Hkv, c_cap, N, nslots, g0;
+    int mode, Hq, Hkv, c_cap, N, nslots, g0, count;
 };
 
 template <typename T, int D, int NH>
@@ -40,10 +40,12 @@ __global__ __launch_bounds__(256) void centroid_attend_kernel(CentParams p) {
     __shared__ float s_q[NH][D];
     __shared__ float s_wm[4][NH], s_wl[4][NH];
     __shared__ float s_wacc[4][NH][D];
-    const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // Group-major order: group j of every graph of the window before group j + 1.
+    const int grp = blockIdx.x / p.count, g = p.g0 + (blockIdx.x - grp * p.count);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = tid >> 4, l16 = tid & 15;
     const int nce = p.cent_n[g];
-    if (nce <= 0) return;  // uniform: no centroid terms, no record
+    if (grp * kCentPerRecord >= nce) return;  // uniform: no terms in this group, no record
     const int n = p.tok_n[g];
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
     const T *qp = reinterpret_cast<const T *>(p.q) + ((size_t)gc.b * p.Hq + gc.qh0) * D;
@@ -63,8 +65,10 @@ __global__ __launch_bounds__(256) void centroid_attend_kernel(CentParams p) {
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
-    for (int i = row; i < nce; i += kRows) {
-        const int c = p.cent_sel[(size_t)g * p.N + i];
+    static_assert(kRows == kCentPerRecord, "one term per row");
+    const int term = grp * kCentPerRecord + row;
+    if (term < nce) {
+        const int c = p.cent_sel[(size_t)g * p.N + term];
         const int cnt = p.size[(size_t)g * p.c_cap + c];
         const size_t off = ((size_t)g * p.c_cap + c) * D + l16 * E;
         double kd[E], vd[E];
@@ -126,9 +130,10 @@ __global__ __launch_bounds__(256) void centroid_attend_kernel(CentParams p) {
         }
     }
     __syncthreads();
-    // The four waves in a fixed order; the record goes to the slot after the
-    // graph's last span (n <= t_cap, so the slot is below nslots).
-    const int slot = n > 0 ? (n + kGatherTokens - 1) / kGatherTokens : 0;
+    // The four waves in a fixed order; the record goes to slot ceil(n / 256) +
+    // grp, after the graph's spans (n <= t_cap and grp < cent_records(N), so
+    // the slot is below nslots).
+    const int slot = (n > 0 ? (n + kGatherTokens - 1) / kGatherTokens : 0) + grp;
     float *P = p.part + (size_t)g * NH * p.nslots * PS;
     for (int i = tid; i < NH * D; i += 256) {
         const int h = i / D, d = i - (i / D) * D;
@@ -171,9 +176,10 @@ hipError_t launch_centroid_attend(const ckv_kv *kv, const ckv_index *idx, const 
     p.nslots = nslots;
     const Window w = window_of(idx);
     p.g0 = w.first;
+    p.count = w.count;
     const int nh = heads_per_graph(kv, idx);
     const bool bf = kv->dtype == CKV_DTYPE_BF16;
-    const dim3 grid(w.count), block(256);
+    const dim3 grid(w.count * cent_records(idx->cent_budget)), block(256);
 #define CKV_CENT(TT, DD, NN)                                                          \
     if (kv->head_dim == DD && nh == NN) {                                             \
         hipLaunchKernelGGL((centroid_attend_kernel<TT, DD, NN>), grid, block, 0, s, p); \

@@ -54,11 +54,16 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Row stride of the base CSR offsets (c_cap + 1 used, padded for 16-byte rows).
 __host__ __device__ inline int offs_stride(int c_cap) { return c_cap + 4; }
 
+// Centroid terms per partial record: the centroid-term kernel attends each
+// group of kCentPerRecord of a graph's centroid terms in one block.
+constexpr int kCentPerRecord = 16;
+__host__ __device__ inline int cent_records(int n_cent) { return (n_cent + kCentPerRecord - 1) / kCentPerRecord; }
+
 // Partial-record slots per graph and head of the gather: one per span of the
-// longest list, and with a centroid budget one more, for the centroid terms
-// (written at the slot right after the graph's last span).
+// longest list, and with a centroid budget one per kCentPerRecord centroid
+// terms (written at the slots right after the graph's last span).
 inline int gather_slots(const ckv_index *idx, int t_cap) {
-    return ceil_div(t_cap > 0 ? t_cap : 1, kGatherTokens) + (idx->cent_budget > 0 ? 1 : 0);
+    return ceil_div(t_cap > 0 ? t_cap : 1, kGatherTokens) + cent_records(idx->cent_budget);
 }
 
 // Graphs a step call processes: [first, first + count).

@@ -1435,17 +1435,22 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, 
 // take, as ascending ids in cent_sel[g][0 .. cent_n[g]).  One 1024-thread
 // block per graph; thread t owns communities t, t + 1024, ...  The ranking is
 // the selection's (exact score, then lower id), decided from the screening
-// intervals [L, U] the same way: the N-th largest L among the outsiders (a
-// radix select with unit weights) is a score that N of them reach, so an
-// outsider whose U is below it cannot be among the N, and only the others
-// (typically N and a few) get their exact score; a second radix select over
-// those exact keys takes the best N.  When more than kList outsiders are
-// left, every exact score is computed, slab by slab, instead.  Fewer than N
-// outsiders: all of them.
+// intervals [L, U] the same way.  A unit-weight histogram of the outsiders'
+// L over 1024 equal-width bins of their score range (a monotone map), walked
+// from the top, gives the bin b holding the N-th largest L: N outsiders reach
+// a score in bin b or above, so an outsider whose U falls in a lower bin
+// cannot be among the N.  The others (typically N and a few) get their exact
+// score from the float64 sums and are ranked exactly: each counts the exact
+// keys above its own (a radix select for longer lists).  When more than
+// kList outsiders reach bin b, every outsider's exact score is computed, slab
+// by slab, and a radix select takes the best N.  Fewer than N + 1 outsiders:
+// all of them.
+constexpr int kCentRankMax = 512;  // candidates ranked by counting; more: radix select
+
 template <int D, int EPT>
 __global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectParams p) {
     __shared__ SelShared sh;
-    const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int g = p.g0 + blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int C = p.c_cap, N = p.cent_budget;
     const int nc = min(p.n_comm[g], C);
     const GraphCoords gc = graph_coords(g, p.mode, p.Hq, p.Hkv);
@@ -1462,6 +1467,7 @@ __global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectPara
     const int ntaken = p.sel_n[g];
     load_qbar(p, gc, sh);
     for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
+    sh.bw[tid] = 0;  // kBins == kSelThreads
     if (tid == 0) sh.ccount = 0;
     __syncthreads();
     for (int i = tid; i < ntaken; i += kSelThreads) {
@@ -1473,49 +1479,88 @@ __global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectPara
     const float kq = wave_sum_f(qn) * kScreenK;
     __syncthreads();
 
-    // Outsiders (non-empty, not taken) and their screening intervals.
+    // Outsiders (non-empty, not taken), their intervals, count and range.
     uint32_t outs = 0u;
-    float up[EPT];
-    unsigned long long key[EPT];
-    int w0[EPT];
+    float lw[EPT], up[EPT];
+    float blo = -kNegInf, bhi = kNegInf;
+    int nout = 0;
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
         const int c = tid + j * kSelThreads;
         const bool o = sz[j] > 0 && !((sh.bits[c >> 5] >> (c & 31)) & 1u);
         const float e = screen_bound(sv[j], scl[j], kq);
         outs |= (o ? 1u : 0u) << j;
+        lw[j] = sv[j] - e;
         up[j] = sv[j] + e;
-        key[j] = o ? comm_key(sv[j] - e, c) : 0ull;
-        w0[j] = 0;
+        if (o) {
+            blo = fminf(blo, lw[j]);
+            bhi = fmaxf(bhi, up[j]);
+            ++nout;
+        }
     }
-    // The N-th largest L (0: at most N - 1 outsiders, every one is chosen).
-    const unsigned long long tl = radix_cut<EPT>(key, w0, true, (long long)N - 1, sh);
+    blo = wave_min_f(blo);
+    bhi = wave_max_f(bhi);
+    nout = (int)wave_sum_f((float)nout);  // at most 64 * EPT: exact in float32
+    if (lane == 0) {
+        sh.red_lo[wave] = blo;
+        sh.red_hi[wave] = bhi;
+        sh.red_lm[wave] = (float)nout;
+    }
+    __syncthreads();
+    nout = 0;
+#pragma unroll
+    for (int i = 0; i < kSelThreads / 64; ++i) {
+        blo = fminf(blo, sh.red_lo[i]);
+        bhi = fmaxf(bhi, sh.red_hi[i]);
+        nout += (int)sh.red_lm[i];
+    }
     // From here sh.bits marks the chosen communities.
     for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
     __syncthreads();
-    if (tl == 0ull) {
+
+    if (nout <= N) {  // uniform: every outsider
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
             const int c = tid + j * kSelThreads;
             if ((outs >> j) & 1u) atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
         }
     } else {
-        // radix_cut's threshold is an upper end of the cut key's digit range
-        // (keys above it are the N - 1 larger ones): the N-th largest L is the
-        // largest key at or below it.
-        unsigned long long kc = 0ull;
+        // bin(x) = floor((x - lo) * 1024 / (hi - lo)), clamped: monotone in x.
+        const float bscale = bhi > blo ? (float)kBins / (bhi - blo) : 0.f;
+        auto bin = [&](float x) { return min(max((int)((x - blo) * bscale), 0), kBins - 1); };
 #pragma unroll
         for (int j = 0; j < EPT; ++j)
-            if (key[j] <= tl) kc = umax64(kc, key[j]);
-        kc = wave_max_u64(kc);
-        if (lane == 0) sh.ckey[tid >> 6] = kc;
+            if ((outs >> j) & 1u) atomicAdd(&sh.bw[bin(lw[j])], 1);
         __syncthreads();
+        if (wave == 0) {  // the highest bin b with at least N lower bounds at or above it
+            int h[kBins / 64], tot = 0;
 #pragma unroll
-        for (int i = 0; i < kSelThreads / 64; ++i) kc = umax64(kc, sh.ckey[i]);
-        const float ln = key_score(kc);
+            for (int i = 0; i < kBins / 64; ++i) {
+                h[i] = sh.bw[(kBins / 64) * lane + i];
+                tot += h[i];
+            }
+            int suf = tot;  // this lane and every higher lane
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_down(suf, o, 64);
+                if (lane + o < 64) suf += y;
+            }
+            int acc = suf - tot, found = -1;
+#pragma unroll
+            for (int i = kBins / 64 - 1; i >= 0; --i) {
+                acc += h[i];
+                if (found < 0 && acc >= N) found = (kBins / 64) * lane + i;
+            }
+            const unsigned long long bal = __ballot(found >= 0);
+            const int src = bal ? 63 - __clzll((long long)bal) : 0;
+            const int fb = __shfl(found, src, 64);
+            if (lane == 0) sh.cut_bin = fb;
+        }
+        __syncthreads();
+        const int bcut = sh.cut_bin;  // >= 0: nout > N lower bounds are in the histogram
 #pragma unroll
         for (int j = 0; j < EPT; ++j) {
-            if (((outs >> j) & 1u) && up[j] >= ln) {
+            if (((outs >> j) & 1u) && bin(up[j]) >= bcut) {
                 const int slot = atomicAdd(&sh.ccount, 1);
                 if (slot < kList) {
                     sh.u.ls.id[slot] = tid + j * kSelThreads;
@@ -1530,19 +1575,32 @@ __global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectPara
             __syncthreads();
             constexpr int LPT = kList / kSelThreads;
             unsigned long long k2[LPT];
-            int w2[LPT];
 #pragma unroll
             for (int i = 0; i < LPT; ++i) {
                 const int e = tid + i * kSelThreads;
                 k2[i] = e < ncand ? sh.u.ls.key[e] : 0ull;
-                w2[i] = 0;
             }
-            const unsigned long long t2 = radix_cut<LPT>(k2, w2, true, N, sh);
-#pragma unroll
-            for (int i = 0; i < LPT; ++i) {
-                if (k2[i] && (t2 == 0ull || k2[i] > t2)) {
-                    const int c = (int)(0xFFFFFFFFu - (uint32_t)k2[i]);
+            unsigned long long t2 = 0ull;  // taken: keys above t2
+            if (ncand <= kCentRankMax) {
+                // rank of each key among the candidates' (keys are distinct)
+                const unsigned long long mine = k2[0];
+                int above = 0;
+                for (int e = 0; e < ncand; ++e) above += sh.u.ls.key[e] > mine ? 1 : 0;
+                if (tid < ncand && above < N) {
+                    const int c = (int)(0xFFFFFFFFu - (uint32_t)mine);
                     atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+                }
+            } else {
+                int w2[LPT];
+#pragma unroll
+                for (int i = 0; i < LPT; ++i) w2[i] = 0;
+                t2 = radix_cut<LPT>(k2, w2, true, N, sh);
+#pragma unroll
+                for (int i = 0; i < LPT; ++i) {
+                    if (k2[i] && (t2 == 0ull || k2[i] > t2)) {
+                        const int c = (int)(0xFFFFFFFFu - (uint32_t)k2[i]);
+                        atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
+                    }
                 }
             }
         } else {  // too many to list: every exact score, slab by slab
@@ -1560,9 +1618,13 @@ __global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectPara
                 }
                 __syncthreads();
             }
+            unsigned long long key[EPT];
+            int w0[EPT];
 #pragma unroll
-            for (int j = 0; j < EPT; ++j)
+            for (int j = 0; j < EPT; ++j) {
                 key[j] = ((outs >> j) & 1u) ? comm_key(ex[j], tid + j * kSelThreads) : 0ull;
+                w0[j] = 0;
+            }
             const unsigned long long t2 = radix_cut<EPT>(key, w0, true, N, sh);
 #pragma unroll
             for (int j = 0; j < EPT; ++j) {
@@ -1612,7 +1674,7 @@ hipError_t launch_centroid_select(const ckv_kv *kv, const ckv_index *idx, const 
         hipLaunchKernelGGL((centroid_select_kernel<DD, E>), grid, block, 0, s, p);       \
         return hipGetLastError();                                                         \
     }
-#define CKV_CSEL_D(DD) CKV_CSEL(1, DD) CKV_CSEL(2, DD) CKV_CSEL(4, DD) CKV_CSEL(8, DD) CKV_CSEL(16, DD)
+#define CKV_CSEL_D(DD) CKV_CSEL(1, DD) CKV_CSEL(2, DD) CKV_CSEL(4, DD) CKV_CSEL(8, DD) CKV_CSEL(12, DD) CKV_CSEL(16, DD)
     CKV_CSEL_D(64) CKV_CSEL_D(128)
 #undef CKV_CSEL_D
 #undef CKV_CSEL

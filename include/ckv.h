@@ -240,9 +240,10 @@ ckv_status ckv_select_communities(const ckv_kv *kv, const ckv_index *idx, const 
  * CKV_E_INVALID.
  * With idx->cent_budget > 0 the call first attends each graph's centroid
  * terms (idx->cent_sel, idx->cent_n) in a kernel of its own, which leaves one
- * more softmax state per head after the spans' (ceil(t_cap / 256) + 1 states
- * per head in all); the combine takes it last, and out and ml cover tokens
- * and centroid terms alike. */
+ * more softmax state per head for every 16 terms, after the spans' (up to
+ * ceil(t_cap / 256) + ceil(cent_budget / 16) states per head in all); the
+ * combine takes them last, and out and ml cover tokens and centroid terms
+ * alike. */
 ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void *q,
                              const int32_t *tok_list, const int32_t *tok_n, int32_t t_cap,
                              float sm_scale, float *out, float *logits, float *ml,
@@ -257,7 +258,7 @@ ckv_status ckv_gather_attend(const ckv_kv *kv, const ckv_index *idx, const void 
  * ends; the call allocates nothing.  The scratch need is 256-aligned
  * 4 * n_graphs bytes of counters plus 4 * n_graphs * heads_per_graph *
  * nspan * (32 * ceil((head_dim + 2) / 32)) bytes of records, nspan =
- * ceil(t_cap / 256), plus one with a centroid budget; a
+ * ceil(t_cap / 256) + ceil(cent_budget / 16); a
  * larger need returns CKV_E_WORKSPACE before anything is enqueued.  Every call
  * on one GPU shares that GPU's array: calls that overlap on one GPU (other
  * streams, other host threads) race and must be ordered by the caller.  The

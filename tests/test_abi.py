@@ -116,13 +116,14 @@ def test_centroid_budget_validation(kw):
     assert _ws(kv, idx, 4100) == 0
 
 
-def test_centroid_budget_adds_one_record_slot():
+@pytest.mark.parametrize("budget,slots", [(1, 1), (16, 1), (17, 2), (256, 16)])
+def test_centroid_budget_adds_record_slots(budget, slots):
     """With a centroid budget every graph and head has one more partial record
-    (the centroid terms'), after its spans: 17 + 1 slots for t_cap 4100."""
+    per 16 centroid terms, after its spans (17 spans for t_cap 4100)."""
     kv = _kv()
     off = _idx()
-    on = _idx(cent_budget=16, cent_sel=FAKE, cent_n=FAKE, vsum=FAKE)
-    assert _ws(kv, on, 4100) - _ws(kv, off, 4100) == 4 * 32 * 160
+    on = _idx(cent_budget=budget, cent_sel=FAKE, cent_n=FAKE, vsum=FAKE)
+    assert _ws(kv, on, 4100) - _ws(kv, off, 4100) == 4 * 32 * 160 * slots
     assert ckv.CKV_MAX_CENT == 256
 
 
