@@ -459,8 +459,22 @@ def dense_baseline(w, dec, kv, q, restore, reps=20):
     d_us = a.elapsed_time(c) / reps * 1e3
     row_bytes = 2 * w.head_dim * (2 if w.dtype == "bf16" else 4)
     d_bytes = int(kv.seq_len.sum().item()) * w.n_kv_heads * row_bytes
-    return {"us_per_call": round(d_us, 2), "bytes": d_bytes, "gbps": round(d_bytes / (d_us * 1e-6) / 1e9, 1),
-            "frac_of_8tbps": round(d_bytes / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    # The read ceiling of the same rows (every cached token of every kv head,
+    # in the dense kernel's order) with the gather's loads and no arithmetic.
+    ps = kv.page_size
+    rows = []
+    for b in range(w.batch):
+        pos = torch.arange(int(kv.seq_len[b].item()), device="cuda")
+        page = kv.page_table[b, pos // ps].long()
+        for kh in range(w.n_kv_heads):
+            rows.append((page * w.n_kv_heads + kh) * ps + pos % ps)
+    rows = torch.cat(rows).to(torch.int32).contiguous()
+    ceiling = rows_read_rate(kv, rows, row_bytes, reps)
+    del rows
+    gbps = d_bytes / (d_us * 1e-6) / 1e9
+    return {"us_per_call": round(d_us, 2), "bytes": d_bytes, "gbps": round(gbps, 1),
+            "frac_of_8tbps": round(gbps / HBM_PEAK_GBPS, 4), "read_ceiling": ceiling,
+            "frac_of_read_ceiling": round(gbps / ceiling["gbps"], 4)}
 
 
 def bench_group(args, w, W, K):
@@ -770,9 +784,8 @@ def read_ceiling(w, kv, idx, buf, row_bytes, reps):
     """The practical read rate of the gather's access pattern: ckv_read_rows
     (the gather's loads, no arithmetic) over the rows the last step's token
     lists name, timed with dispatch-stamped events like the gather."""
-    import numpy as np
     import torch
-    from community_kv_retrieval_amd import ckv, synth
+    from community_kv_retrieval_amd import synth
     G, T = buf.tok_list.shape
     gi = torch.arange(G, device="cuda")[:, None].expand(G, T)
     mask = torch.arange(T, device="cuda")[None, :] < buf.tok_n[:, None]
@@ -784,6 +797,14 @@ def read_ceiling(w, kv, idx, buf, row_bytes, reps):
     ps = kv.page_size
     page = kv.page_table[b, pos // ps].long()
     rows = ((page * w.n_kv_heads + kh) * ps + pos % ps).to(torch.int32).contiguous()
+    return rows_read_rate(kv, rows, row_bytes, reps)
+
+
+def rows_read_rate(kv, rows, row_bytes, reps):
+    """ckv_read_rows over the given row ids, timed with dispatch-stamped events."""
+    import numpy as np
+    import torch
+    from community_kv_retrieval_amd import ckv
     n = rows.numel()
     part = torch.zeros(((n + 255) // 256,), dtype=torch.int32, device="cuda")
     for _ in range(5):

@@ -19,7 +19,7 @@ constexpr int kGatherU = 8;
 constexpr int kGatherTokens = 16 * kGatherU * 2;
 // The dense baseline walks kDenseIters such spans per block.
 constexpr int kDenseU = 8;
-constexpr int kDenseIters = 8;
+constexpr int kDenseIters = 16;
 constexpr int kDenseTokens = 16 * kDenseU * kDenseIters;
 
 // Events armed by ckv_time_next_launch for the next step-kernel launch of

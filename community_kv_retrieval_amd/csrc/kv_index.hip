@@ -7,8 +7,9 @@
 // keys with its float32 mean (the centroid) stored transposed for the scoring
 // kernel.  Steps: clear, count (atomic increments), one block scan per graph,
 // scatter (atomic cursors), then one block per community that sorts its
-// members by position (so the CSR does not depend on atomic order) and sums
-// their keys in that order.
+// members by position (so the CSR does not depend on atomic order: a rank
+// sort in LDS, or for communities of more than 2048 members an ordered pass
+// over the labels) and sums their keys in that order.
 #include "ckv_device.h"
 #include "ckv_internal.h"
 
@@ -154,16 +155,20 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
             for (int j = 0; j < s; ++j) r += buf[j] < x;
             mem[r] = x;
         }
-    } else if (tid == 0) {  // large community: insertion sort by one thread
-        for (int i = 1; i < s; ++i) {
-            const int x = mem[i];
-            int j = i - 1;
-            while (j >= 0 && mem[j] > x) {
-                mem[j + 1] = mem[j];
-                --j;
-            }
-            mem[j + 1] = x;
-        }
+    } else {
+        // Large community: its members are exactly the positions labelled c,
+        // so one ordered pass over the graph's labels lists them ascending.
+        // Thread t counts its run of positions, a block scan gives each run
+        // its first slot, and the run writes its members in order.
+        const int32_t *lab = p.label + (size_t)g * p.l_cap;
+        const int per = (p.l_cap + 255) / 256;
+        const int q0 = min(tid * per, p.l_cap), q1 = min(q0 + per, p.l_cap);
+        int cnt = 0;
+        for (int q = q0; q < q1; ++q) cnt += lab[q] == c ? 1 : 0;
+        int total;
+        int k = block_exclusive_scan<256>(cnt, buf, &total);
+        for (int q = q0; q < q1; ++q)
+            if (lab[q] == c) mem[k++] = q;
     }
     __syncthreads();
     __threadfence_block();

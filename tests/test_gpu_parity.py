@@ -541,3 +541,19 @@ def test_centroid_budget_zero_query(n_ctx, mean_size):
     PY.log(f"centroid budget, zero query, n_ctx={n_ctx}")
     st = PY.run_steps(w, 26, w.steps, q_fn=lambda t, q: torch.zeros_like(q))
     assert st.near_sel == 0 and st.near_cent == 0 and st.near_edges == 0
+
+
+@pytest.mark.parametrize("budget", [5000, 1 << 20])
+def test_large_communities(budget):
+    """Communities of 2500 to 9000 members, more than the 2048 the index
+    build sorts in LDS: the build lists them by its ordered pass over the
+    labels.  The CSR (ascending members), the key sums and the centroids are
+    checked bit-exact after the build, then the steps as usual (the full
+    budget takes every community: equal to dense attention)."""
+    w = small_per_head(n_ctx=30000, mean_size=5000, min_size=2500, max_size=9000, n_kv_heads=2, n_q_heads=4,
+                       steps=2, budget=budget)
+    layer, orc = PY.make_pair(w, 61, w.steps)
+    sizes = [int(st.counts.max()) for st in orc.g.values()]
+    assert min(sizes) > 2048, sizes
+    PY.log(f"large communities: largest per graph {sizes}, budget {budget}")
+    PY.run_steps(w, 61, w.steps, pair=(layer, orc), check_dense=budget > w.n_ctx)
