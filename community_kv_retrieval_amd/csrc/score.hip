@@ -74,6 +74,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 #pragma unroll
         for (int h = 0; h < kMaxHeads; ++h) qv[h] = q[(size_t)min(h, gc.nh - 1) * D];
     }
+    __builtin_amdgcn_sched_barrier(0);  // the query loads issue first
     constexpr int DW = D / 4;
     const int16_t *base = p.cq + cq_offset(g, wave * DW, c0, D, p.c_cap) + 4 * lane;
     int2 v[DW];
@@ -86,13 +87,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     // base members of c: offs[c] .. offs[c + 1] (the offsets row holds c_cap + 4 entries)
     const int32_t *orow = p.offs + (size_t)g * offs_stride(p.c_cap) + c;
     const int m0 = orow[0], m1 = orow[1];
-    if (tid < D) {  // the head sum in float64, heads in order
-        double qs = 0.0;
+    // The head sum in float64, heads in order, by every thread (threads past
+    // D repeat the last dimension): kept unconditional, so that the query
+    // loads stay ahead of the code loads and the sum waits for them alone.
+    double qs = 0.0;
 #pragma unroll
-        for (int h = 0; h < kMaxHeads; ++h)
-            if (h < gc.nh) qs += (double)to_f32(qv[h]);
-        s_q[tid] = (float)qs;
-    }
+    for (int h = 0; h < kMaxHeads; ++h)
+        if (h < gc.nh) qs += (double)to_f32(qv[h]);
+    if (tid < D) s_q[tid] = (float)qs;
     lds_barrier();
 
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
