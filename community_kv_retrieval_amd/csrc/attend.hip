@@ -42,6 +42,7 @@ struct AttendParams {
     const int32_t *cent_n;  // gather with a centroid budget: centroid terms per graph (else null)
     int cent_slots;         // record slots of the centroid terms per graph and head
     int nchunk;     // record slots per unit and head
+    int dense_tokens;  // dense baseline: tokens per block (a multiple of the pass span)
     int g0;         // first unit of the launch window
     int units;      // units in the launch
 };
@@ -177,10 +178,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     using RS = RowSlice<T, D>;
     constexpr int E = RS::E;
     constexpr int SPAN = 16 * U;
-    constexpr int PER_BLOCK = DENSE ? kDenseTokens : kGatherTokens;
-    constexpr int MAX_BLOCK = PER_BLOCK;
-    constexpr int ITERS = PER_BLOCK / SPAN;
-    static_assert(PER_BLOCK % SPAN == 0, "a block's span is whole passes");
+    constexpr int MAX_BLOCK = DENSE ? kDenseTokensMax : kGatherTokens;
+    constexpr int ITERS = MAX_BLOCK / SPAN;
+    static_assert(MAX_BLOCK % SPAN == 0 && kDenseTokensMin % SPAN == 0, "a block's span is whole passes");
+    const int per_block = DENSE ? a.dense_tokens : kGatherTokens;
     constexpr int PS = part_stride(D);
     // Gather with out == nullptr: the combine is deferred to the assign kernel,
     // every block leaves its partial record and the launch ends there.
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
     if constexpr (!DENSE) CKV_BMARK(0);
 
     int b, kh, qh0, n;
-    const int start = chunk * PER_BLOCK;
+    const int start = chunk * per_block;
     // Gather: the span's token positions are loaded together with the list
     // length (start < t_cap always holds, so the loads stay inside the row;
     // entries past the length are ignored), one round trip instead of two.
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         kh = gc.kh;
         qh0 = gc.qh0;
         const int32_t *tl = a.tok_list + (size_t)unit * a.t_cap + start;
-        const int lim = min(PER_BLOCK, a.t_cap - start);
+        const int lim = min(per_block, a.t_cap - start);
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const int t = tid + i * 256;
@@ -246,8 +247,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
         return;
     }
     if (start >= n) return;
-    const int nact = (n + PER_BLOCK - 1) / PER_BLOCK;
-    const int cnt = min(PER_BLOCK, n - start);
+    const int nact = (n + per_block - 1) / per_block;
+    const int cnt = min(per_block, n - start);
 
     // Stage the row index of every token of the span (rows past the end read
     // position 0 of the sequence, which exists whenever the span is not empty,
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttendParams a) {
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const int t = tid + i * 256;
-            if (t >= PER_BLOCK) break;
+            if (t >= per_block) break;
             const int pos = t < cnt ? (DENSE ? start + t : pos_l[i]) : (DENSE ? start : 0);
             const int page = ptab[pos >> a.ps_log2];
             s_row[t] = ((uint32_t)(page * a.Hkv + kh) << a.ps_log2) | ((uint32_t)pos & smask);
@@ -678,7 +679,8 @@ hipError_t launch_dense(const ckv_kv *kv, const void *q, float sm_scale, float *
     p.ml = ml;
     p.part = part;
     p.ctr = ctr;
-    p.nchunk = ceil_div(ctx_cap(kv), kDenseTokens);
+    p.dense_tokens = dense_tokens(kv);
+    p.nchunk = ceil_div(ctx_cap(kv), p.dense_tokens);
     return dispatch<true>(kv, group_of(kv), p, kv->batch * kv->n_kv_heads, s);
 }
 

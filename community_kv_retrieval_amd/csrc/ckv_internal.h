@@ -17,10 +17,10 @@ namespace ckv {
 // the assign kernel finds a deferred gather's records by the same span.
 constexpr int kGatherU = 8;
 constexpr int kGatherTokens = 16 * kGatherU * 2;
-// The dense baseline walks kDenseIters such spans per block.
-constexpr int kDenseU = 8;
-constexpr int kDenseIters = 16;
-constexpr int kDenseTokens = 16 * kDenseU * kDenseIters;
+// The dense baseline: each block walks up to kDenseTokensMax consecutive
+// tokens of one (sequence, kv head); dense_tokens() picks the span at launch.
+constexpr int kDenseTokensMax = 2048;
+constexpr int kDenseTokensMin = 512;
 
 // Events armed by ckv_time_next_launch for the next step-kernel launch of
 // this host thread.
@@ -80,6 +80,17 @@ inline int heads_per_graph(const ckv_kv *kv, const ckv_index *idx) {
 }
 inline int ctx_cap(const ckv_kv *kv) { return kv->max_pages * kv->page_size; }
 
+// Tokens per dense-baseline block: the longest of 2048, 1024 and 512 that
+// still gives at least two blocks per CU (512 blocks) over the store's
+// capacity, else 512.  Long spans amortise a block's start and records; short
+// contexts need the blocks to fill the chip.
+inline int dense_tokens(const ckv_kv *kv) {
+    const long units = (long)kv->batch * kv->n_kv_heads;
+    for (int t = kDenseTokensMax; t > kDenseTokensMin; t /= 2)
+        if (units * ceil_div(ctx_cap(kv), t) >= 512) return t;
+    return kDenseTokensMin;
+}
+
 // Workspace layout.  The dense baseline's region comes first and depends only
 // on the K/V shape, so one workspace serves the dense baseline and the sparse
 // path alike.  Counters are self-resetting.
@@ -123,7 +134,7 @@ inline WsLayout ws_layout(const ckv_kv *kv, const ckv_index *idx, int t_cap) {
     L.ctr_dense = off;
     off = align256(off + 4 * units_dense);
     L.part_dense = off;
-    off += align256(4 * units_dense * group_of(kv) * (size_t)ceil_div(ctx_cap(kv), kDenseTokens) * D2);
+    off += align256(4 * units_dense * group_of(kv) * (size_t)ceil_div(ctx_cap(kv), dense_tokens(kv)) * D2);
     L.dense_total = off;
     if (!idx) {
         L.total = off;
