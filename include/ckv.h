@@ -312,8 +312,10 @@ ckv_status ckv_dense_attend(const ckv_kv *kv, const void *q, float sm_scale, flo
  * dense_ml[batch][n_q_heads][2] of ckv_dense_attend on the same q and cache
  * state: the softmax mass of the attended tokens over that of every cached
  * token.  Evaluated in float64, stored as float32; 0 where the graph attended
- * nothing (l_T = 0).  All three arrays are device memory.  Processes every
- * graph (the launch window is ignored).  Errors: CKV_E_INVALID for a NULL
+ * nothing (l_T = 0).  With a centroid budget the gather's ml also holds the
+ * centroid terms' mass, so the value is then the share of the attended
+ * tokens and the centroid terms together.  All three arrays are device
+ * memory.  Processes every graph (the launch window is ignored).  Errors: CKV_E_INVALID for a NULL
  * array or a bad descriptor. */
 ckv_status ckv_attention_recall(const ckv_kv *kv, const ckv_index *idx, const float *ml, const float *dense_ml,
                                 float *recall, ckv_stream_t stream);
