@@ -56,6 +56,16 @@ def test_noalloc_gather_matches_workspace_gather_twice():
     assert g2 < g1 and t2 < t1
 
 
+def test_noalloc_gather_with_centroid_terms():
+    """With a centroid budget both gathers first write the centroid terms'
+    records (into the static scratch or the workspace) and combine them after
+    the spans: still bit-identical."""
+    w = synth.preset("qwen3_8b_32k").replace(name="noalloc_cent", n_ctx=6000, n_q_heads=8, n_kv_heads=2,
+                                             budget=600, cent_budget=64)
+    PY.log("noalloc with centroid terms (8 graphs, budget 64)")
+    _compare(w, 64)
+
+
 def test_noalloc_rejects_oversized_shape():
     """A shape whose records exceed the static scratch is refused on the host."""
     w = synth.preset("qwen3_8b_32k").replace(name="noalloc_reject", n_ctx=1000, n_q_heads=8, n_kv_heads=2,
