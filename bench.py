@@ -289,9 +289,9 @@ def time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=False, eager_o
     row_bytes = 2 * w.head_dim * esz  # K row + V row
     gathered = tok[W:].sum(axis=1) * row_bytes  # bytes per timed step
     n_comm = np.array(idx.n_comm.cpu().numpy(), dtype=np.int64)
-    # the scoring kernel streams the int16 screening copy of every used
+    # the scoring kernel streams the int8 screening copy of every used
     # centroid column plus its scale and member count
-    score_bytes = int(n_comm.sum()) * (w.head_dim * 2 + 8)
+    score_bytes = int(n_comm.sum()) * (w.head_dim + 8)
 
     # Eager pass: K steps launched one call at a time from Python.
     restore()

@@ -176,8 +176,8 @@ class CommunityIndex:
         self.tail_comm = torch.zeros((G, tail_cap), **i32)
         self.tail_len = torch.zeros((G,), **i32)
         self.csum = torch.zeros((G, c_cap, D), dtype=torch.float64, device=device)
-        self.cent = torch.zeros((G, D, c_cap), dtype=torch.float32, device=device)
-        self.cq = torch.zeros((G, c_cap // 256, D, 256), dtype=torch.int16, device=device)  # tile-major
+        self.cent = torch.zeros((G, c_cap, D), dtype=torch.float32, device=device)
+        self.cq = torch.zeros((G, c_cap // 256, D, 256), dtype=torch.int8, device=device)  # tile-major
         self.cscale = torch.zeros((G, c_cap), dtype=torch.float32, device=device)
         self.status = torch.zeros((1,), **i32)
         # centroid budget (Table 6): the chosen communities per graph and the value sums

@@ -36,7 +36,7 @@ struct AssignParams {
     int32_t *tail_len;
     double *csum;
     float *cent;
-    int16_t *cq;
+    int8_t *cq;
     float *cscale;
     int32_t *status;
     const int32_t *tok_list;
@@ -386,9 +386,9 @@ __global__ __launch_bounds__(256) void assign_kernel(AssignParams p) {
         p.csum[ci] = cs;
         if (p.vsum) p.vsum[ci] += (double)to_f32(vn[tid]);
         cv = (float)(cs / (double)newsize);
-        p.cent[((size_t)g * D + tid) * p.c_cap + a] = cv;
+        p.cent[((size_t)g * p.c_cap + a) * D + tid] = cv;
     }
-    // the screening copy of the column: scale = max |cent| / 32767
+    // the screening copy of the column: scale = max |cent| / 127
     if (join) {
         const float m = wave_max_f(fabsf(cv));
         if (lane == 0) s_max[wave] = m;

@@ -1,14 +1,15 @@
 // Centroid terms of the centroid budget (the CommunityKV page, Table 6,
 // "Centroid Budget").  Each community that the centroid selection chose
 // enters the attention as one softmax term standing for its n members: key
-// mu = float32(csum / n), the centroid exactly as the index stores it; value
+// mu = the stored float32 centroid row (float32(csum / n)); value
 // float32(vsum / n), the members' mean value; logit sm_scale * q . mu + ln n
 // (the mass of n tokens whose key is the centroid).
 //
 // One 256-thread block per graph and group of kCentPerRecord (16) terms, laid
 // out like a gather block: 16-lane rows, row r taking the group's term r;
-// lane l16 of a row holds dimensions [l16 E, l16 E + E) of mu and of the
-// value (E = D / 16), loaded as float64 sums and divided once.  The four rows
+// lane l16 of a row holds dimensions [l16 E, l16 E + E) of mu (from the
+// centroid row) and of the value (E = D / 16; the float64 value sum divided
+// once).  The four rows
 // of a wave merge their softmax states with lane shuffles, the four waves in
 // a fixed order through LDS.  Each block's result is one more partial record
 // of the gather: group j of a graph goes to the slot ceil(tok_n / 256) + j,
@@ -21,7 +22,7 @@ namespace ckv {
 
 struct CentParams {
     const void *q;
-    const double *csum;
+    const float *cent;
     const double *vsum;
     const int32_t *size;
     const int32_t *cent_sel;
@@ -71,20 +72,18 @@ __global__ __launch_bounds__(256) void centroid_attend_kernel(CentParams p) {
         const int c = p.cent_sel[(size_t)g * p.N + term];
         const int cnt = p.size[(size_t)g * p.c_cap + c];
         const size_t off = ((size_t)g * p.c_cap + c) * D + l16 * E;
-        double kd[E], vd[E];
+        float mu[E];
+        double vd[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            kd[e] = p.csum[off + e];
+            mu[e] = p.cent[off + e];
             vd[e] = p.vsum[off + e];
         }
         const double dn = (double)cnt;
         const float lnn = logf((float)cnt);
-        float mu[E], nu[E];
+        float nu[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            mu[e] = (float)(kd[e] / dn);
-            nu[e] = (float)(vd[e] / dn);
-        }
+        for (int e = 0; e < E; ++e) nu[e] = (float)(vd[e] / dn);
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             float d = 0.f;
@@ -160,7 +159,7 @@ hipError_t launch_centroid_attend(const ckv_kv *kv, const ckv_index *idx, const 
                                   float sm_scale, float *part, int nslots, hipStream_t s) {
     CentParams p{};
     p.q = q;
-    p.csum = idx->csum;
+    p.cent = idx->cent;
     p.vsum = idx->vsum;
     p.size = idx->size;
     p.cent_sel = idx->cent_sel;

@@ -247,30 +247,31 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 }
 
 // Screening code of one centroid element: round(v / scale) clamped to
-// [-32767, 32767], with scale = max |column| / 32767, so that
-// |v - scale * code| <= scale * (1/2 + 2^-9); a zero scale (all-zero column)
+// [-127, 127], with scale = max |column| / 127, so that
+// |v - scale * code| <= scale * (1/2 + 2^-17); a zero scale (all-zero column)
 // gives 0.
-constexpr float kScreenMax = 32767.f;
-__device__ __forceinline__ int16_t screen_code(float v, float scale) {
+constexpr float kScreenMax = 127.f;
+__device__ __forceinline__ int8_t screen_code(float v, float scale) {
     if (!(scale > 0.f)) return 0;
     const float r = fminf(kScreenMax, fmaxf(-kScreenMax, rintf(v / scale)));
-    return (int16_t)(int)r;
+    return (int8_t)(int)r;
 }
 
-// Screening bound factor, in units of cscale * |qbar|_1: 1/2 + 2^-9 for the
-// rounding of the int16 codes, 32767 (D + 1) 2^-24 < 0.252 for the float32
-// accumulation of D <= 128 products |q_d| * 32767 and for rounding qbar to
-// float32, with slack.  A screening score s~ then lies within
-// E = cscale * |qbar|_1 * kScreenK + 2^-20 |s~| of the exact score (the last
-// term for the float32 roundings of s~, of the exact score and of s~ +- E).
-constexpr float kScreenK = 0.76f;
+// Screening bound factor, in units of cscale * |qbar|_1: 1/2 + 2^-17 for the
+// rounding of the int8 codes, (D + 4) * 127 * 2^-24 < 0.001 for the float32
+// accumulation of D <= 128 products |q_d| * 127 (four partial sums added in
+// order) and for rounding qbar to float32, with slack.  A screening score s~
+// then lies within E = cscale * |qbar|_1 * kScreenK + 2^-20 |s~| of the exact
+// score (the last term for the float32 roundings of s~, of the exact score and
+// of s~ +- E).
+constexpr float kScreenK = 0.51f;
 __device__ __forceinline__ float screen_bound(float s, float cscale, float kq) {
     return cscale * kq + fabsf(s) * 0x1p-20f;
 }
 
-// Element (graph g, dim d, community c) of the int16 screening copy, stored
+// Element (graph g, dim d, community c) of the int8 screening copy, stored
 // tile-major: [graph][c_cap / 256][dim][256], so the 256 communities a scoring
-// block reads are one contiguous 256 * D * 2-byte region.
+// block reads are one contiguous 256 * D-byte region.
 __device__ __forceinline__ size_t cq_offset(int g, int d, int c, int D, int c_cap) {
     return (((size_t)g * (c_cap >> 8) + (c >> 8)) * D + d) * 256 + (c & 255);
 }

@@ -4,9 +4,10 @@
 // (2): communities of the prefill token graph, each with a centroid) into the
 // decode-time index: member counts, a community-ordered CSR of positions, the
 // per-position labels, and per community the exact float64 sum of the members'
-// keys with its float32 mean (the centroid) stored transposed for the scoring
-// kernel.  Steps: clear, count (atomic increments), one block scan per graph,
-// scatter (atomic cursors), then one block per community that sorts its
+// keys with its float32 mean (the centroid), one row per community, and the
+// int8 screening copy of that row for the scoring kernel.  Steps: clear,
+// count (atomic increments), one block scan per graph, scatter (atomic
+// cursors), then one block per community that sorts its
 // members by position (so the CSR does not depend on atomic order: a rank
 // sort in LDS, or for communities of more than 2048 members an ordered pass
 // over the labels) and sums their keys in that order.
@@ -75,7 +76,7 @@ struct BuildParams {
     double *csum;
     double *vsum;  // centroid budget: value sums (else null)
     float *cent;
-    int16_t *cq;
+    int8_t *cq;
     float *cscale;
     int32_t *status;
     int32_t *cursor;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
         }
         p.csum[((size_t)g * p.c_cap + c) * D + tid] = acc;
         cv = (float)(acc / (double)s);
-        p.cent[((size_t)g * D + tid) * p.c_cap + c] = cv;
+        p.cent[((size_t)g * p.c_cap + c) * D + tid] = cv;
     } else if (p.vsum && tid < 2 * D) {  // value sums, in the same member order
         const int e = tid - D;
         double acc = 0.0;
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256) void build_finish_kernel(BuildParams p) {
         }
         p.vsum[((size_t)g * p.c_cap + c) * D + e] = acc;
     }
-    // screening copy of the column: scale = max |cent| / 32767
+    // screening copy of the column: scale = max |cent| / 127
     const float m = wave_max_f(fabsf(cv));
     if ((tid & 63) == 0) s_max[tid >> 6] = m;
     __syncthreads();
@@ -218,7 +219,7 @@ hipError_t launch_index_build(const ckv_kv *kv, const ckv_index *idx, const int3
     if ((e = fill_u32(idx->csum, G * C * D * 2, 0u, s)) != hipSuccess) return e;
     if (idx->cent_budget > 0 && (e = fill_u32(idx->vsum, G * C * D * 2, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->cent, G * C * D, 0u, s)) != hipSuccess) return e;
-    if ((e = fill_u32(idx->cq, G * C * D / 2, 0u, s)) != hipSuccess) return e;  // C % 256 == 0
+    if ((e = fill_u32(idx->cq, G * C * D / 4, 0u, s)) != hipSuccess) return e;  // C % 256 == 0
     if ((e = fill_u32(idx->cscale, G * C, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->tail_len, G, 0u, s)) != hipSuccess) return e;
     if ((e = fill_u32(idx->status, 1, 0u, s)) != hipSuccess) return e;

@@ -2,21 +2,21 @@
 // against the community centroids; Table 1: retrieval is one pass over the
 // centroids).
 //
-// This kernel computes screening scores from the int16 copy of the centroid
+// This kernel computes screening scores from the int8 copy of the centroid
 // table: s~[c] = cscale[c] * sum_d qbar_d * cq[d][c], with qbar rounded to
 // float32 and a float32 sum.  Against the exact score (float64 sum of qbar_d
 // times the float32 centroid, rounded to float32) the error is at most
-// cscale[c] * |qbar|_1 * (1/2 + 32767 (D + 1) 2^-24 + ...) plus a few float32
+// cscale[c] * |qbar|_1 * (1/2 + (D + 4) 127 2^-24 + ...) plus a few float32
 // roundings of s~; the selection kernel turns that bound into intervals and
 // computes the exact score of every community whose interval touches its
 // budget cut, so the selection is the one the exact scores give.
 //
-// The screening copy is half the float32 table and streamed once from HBM, so
-// the kernel is bandwidth-bound and runs on the vector units, not the matrix
-// cores.  The table is stored transposed and tile-major, [graph][tile of 256
-// communities][dim][256], so lane j of a wave owns communities 4j..4j+3 of a
-// tile, every wave instruction reads 512 consecutive bytes of one dimension's
-// row, and a block streams one contiguous region.  The four
+// The screening copy is a quarter of the float32 table and streamed once from
+// HBM, so the kernel is bandwidth-bound and runs on the vector units, not the
+// matrix cores.  The table is stored transposed and tile-major, [graph][tile
+// of 256 communities][dim][256], so lane j of a wave owns communities 4j..4j+3
+// of a tile, every wave instruction reads 256 consecutive bytes of one
+// dimension's row, and a block streams one contiguous region.  The four
 // waves of a block split the dimensions and add their partial sums in a fixed
 // order.  Empty communities and ids >= n_comm score -inf.
 //
@@ -33,7 +33,7 @@ constexpr int kScoreTile = 256;  // communities per block
 
 struct ScoreParams {
     const void *q;
-    const int16_t *cq;
+    const int8_t *cq;
     const float *cscale;
     const int32_t *size;
     const int32_t *n_comm;
@@ -43,9 +43,11 @@ struct ScoreParams {
     int mode, Hq, Hkv, c_cap, g0, count;  // count: graphs in the launch window
 };
 
-// Signed 16-bit halves of a 32-bit word.
-__device__ __forceinline__ float lo16(int w) { return (float)(int16_t)w; }
-__device__ __forceinline__ float hi16(int w) { return (float)(w >> 16); }
+// Signed byte k of a 32-bit word.
+template <int K>
+__device__ __forceinline__ float byte8(int w) {
+    return (float)((w << (24 - 8 * K)) >> 24);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
@@ -76,10 +78,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);  // the query loads issue first
     constexpr int DW = D / 4;
-    const int16_t *base = p.cq + cq_offset(g, wave * DW, c0, D, p.c_cap) + 4 * lane;
-    int2 v[DW];
+    const int8_t *base = p.cq + cq_offset(g, wave * DW, c0, D, p.c_cap) + 4 * lane;
+    int v[DW];
 #pragma unroll
-    for (int j = 0; j < DW; ++j) v[j] = *reinterpret_cast<const int2 *>(base + (size_t)j * 256);
+    for (int j = 0; j < DW; ++j) v[j] = *reinterpret_cast<const int *>(base + (size_t)j * 256);
     const int c = c0 + tid;  // kScoreTile == blockDim: one output per thread
     const int sz = p.size[(size_t)g * p.c_cap + c];
     const float scl = p.cscale[(size_t)g * p.c_cap + c];
@@ -101,10 +103,10 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
 #pragma unroll
     for (int j = 0; j < DW; ++j) {
         const float qq = s_q[wave * DW + j];
-        acc[0] = fmaf(qq, lo16(v[j].x), acc[0]);
-        acc[1] = fmaf(qq, hi16(v[j].x), acc[1]);
-        acc[2] = fmaf(qq, lo16(v[j].y), acc[2]);
-        acc[3] = fmaf(qq, hi16(v[j].y), acc[3]);
+        acc[0] = fmaf(qq, byte8<0>(v[j]), acc[0]);
+        acc[1] = fmaf(qq, byte8<1>(v[j]), acc[1]);
+        acc[2] = fmaf(qq, byte8<2>(v[j]), acc[2]);
+        acc[3] = fmaf(qq, byte8<3>(v[j]), acc[3]);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) s_part[wave][4 * lane + k] = acc[k];

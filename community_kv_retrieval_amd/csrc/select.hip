@@ -25,7 +25,7 @@
 // the communities whose L bin reaches b_l all rank above it and overflow the
 // budget.  The communities in between (the band), and those whose U reaches
 // the largest L (the candidates for the best community), get their exact
-// score from the float64 key sums, one 16-lane group per community, and the
+// score from the float32 centroid rows, one 16-lane group per community, and the
 // band is cut with what the certain communities leave of the budget.  When the
 // scores are degenerate, the band does not fit in LDS, or the community cap
 // (max_comm) is set, every exact score is computed, slab by slab, and the cut
@@ -69,7 +69,7 @@ struct SelectParams {
     const int32_t *n_comm;
     const int32_t *seq_len;
     const float *cscale;
-    const double *csum;
+    const float *cent;  // float32 centroid rows (the exact scores' operand)
     const void *q;
     int bf16, D;
     int mode, Hq, Hkv, c_cap, l_cap, tail_cap, n_sinks, budget, max_comm, t_cap, g0;
@@ -377,23 +377,24 @@ __device__ bool value_cut(const float (&sv)[EPT], const int (&w)[EPT], int budge
 }
 
 // Exact score of n communities, one 16-lane group per community, stride 64
-// groups: float32 of the float64 sum over d of qbar_d * float32(csum_d / size),
-// the centroid exactly as the index stores it.  The communities are the list
-// entries (to_list) or the ids slab * 4096 + i of one slab (or of the column
-// past the last whole slab, i < 1024).  Every lane loads
-// its D/16 consecutive sums with vector loads; rows of two communities per
-// group are in flight together.
+// groups: float32 of the float64 sum over d of qbar_d * cent[c][d], the
+// float32 centroid row exactly as the index stores it (float32(csum / size)).
+// The communities are the list entries (to_list) or the ids slab * 4096 + i of
+// one slab (or of the column past the last whole slab, i < 1024).  Every lane
+// loads its D/16 consecutive floats with 16-byte loads; the rows of four
+// communities per group are in flight together.
 template <int D>
 __device__ __forceinline__ void exact_scores(const SelectParams &p, int g, int n, SelShared &sh,
                                              bool to_list, int slab) {
-    constexpr int E = D / 16;  // doubles per lane
+    constexpr int E = D / 16;  // floats per lane
+    constexpr int R = 4;       // rows per group in flight
     const int tid = threadIdx.x, grp = tid >> 4, l16 = tid & 15;
     const int nc = min(p.n_comm[g], p.c_cap);
-    for (int i0 = grp; i0 < n; i0 += 2 * 64) {
-        int cc[2], nn[2];
-        double cs[2][E];
+    for (int i0 = grp; i0 < n; i0 += R * 64) {
+        int cc[R], nn[R];
+        float cs[R][E];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < R; ++r) {
             const int i = i0 + 64 * r;
             const bool ok = i < n;
             if (to_list) {
@@ -404,17 +405,22 @@ __device__ __forceinline__ void exact_scores(const SelectParams &p, int g, int n
                 nn[r] = ok && cc[r] < nc ? p.size[(size_t)g * p.c_cap + cc[r]] : 0;
                 if (cc[r] >= p.c_cap) cc[r] = 0;
             }
-            const double *row = p.csum + ((size_t)g * p.c_cap + cc[r]) * D + l16 * E;
+            const float *row = p.cent + ((size_t)g * p.c_cap + cc[r]) * D + l16 * E;
 #pragma unroll
-            for (int e = 0; e < E; ++e) cs[r][e] = row[e];
+            for (int e = 0; e < E; e += 4) {
+                const float4 f = *reinterpret_cast<const float4 *>(row + e);
+                cs[r][e] = f.x;
+                cs[r][e + 1] = f.y;
+                cs[r][e + 2] = f.z;
+                cs[r][e + 3] = f.w;
+            }
         }
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        for (int r = 0; r < R; ++r) {
             double part = 0.0;
             if (nn[r] > 0) {
-                const double dn = (double)nn[r];
 #pragma unroll
-                for (int e = 0; e < E; ++e) part = fma(sh.qbar[l16 * E + e], (double)(float)(cs[r][e] / dn), part);
+                for (int e = 0; e < E; ++e) part = fma(sh.qbar[l16 * E + e], (double)cs[r][e], part);
             }
             const double S = row16_sum_d(part);
             const int i = i0 + 64 * r;
@@ -1385,7 +1391,7 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, 
     p.n_comm = idx->n_comm;
     p.seq_len = kv->seq_len;
     p.cscale = idx->cscale;
-    p.csum = idx->csum;
+    p.cent = idx->cent;
     p.q = q;
     p.bf16 = kv->dtype == CKV_DTYPE_BF16;
     p.D = kv->head_dim;
@@ -1440,7 +1446,7 @@ hipError_t launch_select(const ckv_kv *kv, const ckv_index *idx, const void *q, 
 // from the top, gives the bin b holding the N-th largest L: N outsiders reach
 // a score in bin b or above, so an outsider whose U falls in a lower bin
 // cannot be among the N.  The others (typically N and a few) get their exact
-// score from the float64 sums and are ranked exactly: each counts the exact
+// score from the centroid rows and are ranked exactly: each counts the exact
 // keys above its own (a radix select for longer lists).  When more than
 // kList outsiders reach bin b, every outsider's exact score is computed, slab
 // by slab, and a radix select takes the best N.  Fewer than N + 1 outsiders:
@@ -1652,7 +1658,7 @@ hipError_t launch_centroid_select(const ckv_kv *kv, const ckv_index *idx, const 
     p.size = idx->size;
     p.n_comm = idx->n_comm;
     p.cscale = idx->cscale;
-    p.csum = idx->csum;
+    p.cent = idx->cent;
     p.q = q;
     p.bf16 = kv->dtype == CKV_DTYPE_BF16;
     p.D = kv->head_dim;

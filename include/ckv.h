@@ -123,12 +123,12 @@ typedef struct ckv_index {
     int32_t *tail_comm;  /* [G][tail_cap] their communities */
     int32_t *tail_len;   /* [G] */
     double  *csum;       /* [G][c_cap][head_dim] exact float64 key sum of every community */
-    float   *cent;       /* [G][head_dim][c_cap] centroid = float32(csum / size), transposed */
-    int16_t *cq;         /* [G][c_cap / 256][head_dim][256] screening copy of cent, tile-major
+    float   *cent;       /* [G][c_cap][head_dim] centroid = float32(csum / size), one row per community */
+    int8_t  *cq;         /* [G][c_cap / 256][head_dim][256] screening copy of cent, tile-major
                             (element (g, d, c) at ((g * c_cap/256 + c/256) * head_dim + d) * 256
                             + c % 256): cent ~ cscale * cq, cq = round(cent / cscale) in
-                            [-32767, 32767] */
-    float   *cscale;     /* [G][c_cap] max_d |cent[d]| / 32767 of every community (0: zero column) */
+                            [-127, 127] */
+    float   *cscale;     /* [G][c_cap] max_d |cent[d]| / 127 of every community (0: zero column) */
     int32_t *status;     /* [1] CKV_ST_* bits */
     /* Launch window of the four step calls (score, select, gather, assign):
      * they process graphs win_first .. win_first + win_count - 1 only
@@ -187,7 +187,7 @@ ckv_status ckv_index_build(const ckv_kv *kv, const ckv_index *idx, const int32_t
  * summed q . centroid).  The exact score of community c is
  * float32(sum_d qbar_d * cent[d][c]) with the sum in float64; this call writes
  * scores[G][c_cap] = cscale[c] * sum_d float32(qbar_d) * cq(d, c) (float32),
- * within cscale[c] * |qbar|_1 * 0.76 + 2^-20 |score| of the exact score, and
+ * within cscale[c] * |qbar|_1 * 0.51 + 2^-20 |score| of the exact score, and
  * -inf for empty communities and ids >= n_comm[g].  ckv_select_communities
  * resolves the ranking exactly from these bounds.  It also leaves in ws the
  * selection's candidates (of every 64 consecutive communities the 16 of

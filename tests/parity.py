@@ -27,6 +27,16 @@ from tests import decisions as D
 ATOL, RTOL = 2e-3, 1e-2
 TIE = D.TIE
 LOGIT_ATOL = 1e-4
+# The int8 screening copy (as the library documents it): codes in [-SCREEN_MAX, SCREEN_MAX]
+SCREEN_MAX = 127
+
+
+def screen_factor(D: int) -> float:
+    """Bound factor of a screening score, in units of cscale * |qbar|_1: half a
+    code for the rounding of the codes, plus (D + 4) SCREEN_MAX 2^-24 for the
+    float32 accumulation of D products of |q_d| with codes up to SCREEN_MAX and
+    the float32 rounding of qbar."""
+    return 0.5 + (D + 4) * SCREEN_MAX * 2.0 ** -24
 
 
 def log(msg: str):
@@ -74,7 +84,7 @@ def check_index_state(layer, orc: O.Oracle, w: synth.Workload, full: bool = Fals
         C = st.counts.size
         np.testing.assert_array_equal(size[g, :C], st.counts, err_msg=f"size g={g}")
         assert (size[g, C:] == 0).all()
-        cent = idx.cent[g, :, :C].t().cpu().numpy()
+        cent = idx.cent[g, :C].cpu().numpy()
         np.testing.assert_array_equal(cent, orc.centroids32(g), err_msg=f"centroids g={g}")
         check_screening_copy(idx, g, C, cent)
         if full:
@@ -86,17 +96,17 @@ def check_index_state(layer, orc: O.Oracle, w: synth.Workload, full: bool = Fals
 
 
 def check_screening_copy(idx, g: int, C: int, cent: np.ndarray):
-    """The int16 screening copy of the centroid table (stored tile-major,
-    [c_cap / 256][D][256] per graph): per community scale = max |cent| / 32767
-    (float32) and code = round(cent / scale), clamped to +-32767 (0 for a zero
+    """The int8 screening copy of the centroid table (stored tile-major,
+    [c_cap / 256][D][256] per graph): per community scale = max |cent| / 127
+    (float32) and code = round(cent / scale), clamped to +-127 (0 for a zero
     column), as the library documents it."""
     scale = idx.cscale[g, :C].cpu().numpy()
     D = idx.cq.shape[2]
     code = idx.cq[g].permute(1, 0, 2).reshape(D, -1)[:, :C].t().cpu().numpy().astype(np.int32)
-    want_scale = (np.abs(cent).max(axis=1).astype(np.float32) / np.float32(32767)).astype(np.float32)
+    want_scale = (np.abs(cent).max(axis=1).astype(np.float32) / np.float32(SCREEN_MAX)).astype(np.float32)
     np.testing.assert_array_equal(scale, want_scale, err_msg=f"cscale g={g}")
     with np.errstate(divide="ignore", invalid="ignore"):
-        want = np.clip(np.rint(cent / want_scale[:, None]), -32767, 32767)
+        want = np.clip(np.rint(cent / want_scale[:, None]), -SCREEN_MAX, SCREEN_MAX)
     want = np.where(want_scale[:, None] > 0, want, 0).astype(np.int32)
     np.testing.assert_array_equal(code, want, err_msg=f"cq g={g}")
 
@@ -118,9 +128,9 @@ def check_csr(layer, orc: O.Oracle):
 
 def _check_screening(scores, cscale, q_heads, exact, counts, where: str):
     """The scoring kernel's screening scores against the oracle's exact ones.
-    The int16 copy rounds every centroid entry to within cscale / 2, and the
+    The int8 copy rounds every centroid entry to within cscale / 2, and the
     float32 dot product over D dimensions (with the query rounded to float32)
-    adds at most 32767 (D + 1) 2^-24 cscale |qbar|_1; the two float32 roundings
+    adds at most 127 (D + 4) 2^-24 cscale |qbar|_1 (screen_factor); the two float32 roundings
     of the screening score and the one of the exact score stay under
     2^-21 |s~|.  The selection's certain-taken / certain-not decisions rest on
     this bound.  Empty communities and ids at or past the count score -inf."""
@@ -129,7 +139,7 @@ def _check_screening(scores, cscale, q_heads, exact, counts, where: str):
     assert np.all(scores[:C][~live] == -np.inf) and np.all(scores[C:] == -np.inf), f"{where}: dead ids not -inf"
     qbar = q_heads.astype(np.float64).sum(axis=0).astype(np.float32).astype(np.float64)
     s = scores[:C][live].astype(np.float64)
-    bound = cscale[:C][live].astype(np.float64) * np.abs(qbar).sum() * (0.5 + 32767 * (D + 1) * 2.0 ** -24) \
+    bound = cscale[:C][live].astype(np.float64) * np.abs(qbar).sum() * screen_factor(D) \
         + np.abs(s) * 2.0 ** -21
     err = np.abs(s - exact[live].astype(np.float64))
     assert np.all(err <= bound), f"{where}: screening error {err.max():.3g} beyond its bound"

@@ -1,8 +1,8 @@
 """The screening bound the GPU parity runner checks every step, pinned on the CPU.
 
-The scoring kernel streams an int16 copy of the centroid table (per community
-scale = max |centroid| / 32767, code = round(centroid / scale)); the selection
-treats every exact score as lying within cscale * |qbar|_1 * (1/2 + 32767 (D + 1)
+The scoring kernel streams an int8 copy of the centroid table (per community
+scale = max |centroid| / 127, code = round(centroid / scale)); the selection
+treats every exact score as lying within cscale * |qbar|_1 * (1/2 + 127 (D + 4)
 2^-24) plus a few float32 roundings of the screening score.  Here a plain numpy
 screening score, built from that definition, must satisfy the runner's check
 against the oracle's exact scores, and planted mistakes must fail it, so the
@@ -16,9 +16,9 @@ from tests import parity as PY
 
 
 def _screening(cent32, q_heads, counts, drop_scale=False, drop_head=False):
-    scale = (np.abs(cent32).max(axis=1).astype(np.float32) / np.float32(32767)).astype(np.float32)
+    scale = (np.abs(cent32).max(axis=1).astype(np.float32) / np.float32(PY.SCREEN_MAX)).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
-        code = np.clip(np.rint(cent32 / scale[:, None]), -32767, 32767)
+        code = np.clip(np.rint(cent32 / scale[:, None]), -PY.SCREEN_MAX, PY.SCREEN_MAX)
     code = np.where(scale[:, None] > 0, code, 0).astype(np.float32)
     heads = q_heads[:1] if drop_head else q_heads
     qbar = heads.astype(np.float64).sum(axis=0).astype(np.float32)
@@ -62,7 +62,7 @@ def test_bound_is_not_vacuous():
     # a score moved just past its bound
     qbar = q_heads.astype(np.float64).sum(axis=0).astype(np.float32).astype(np.float64)
     c = int(live[live != 5][0])
-    e = float(scale[c]) * np.abs(qbar).sum() * (0.5 + 32767 * 129 * 2.0 ** -24) + abs(float(s[c])) * 2.0 ** -21
+    e = float(scale[c]) * np.abs(qbar).sum() * PY.screen_factor(128) + abs(float(s[c])) * 2.0 ** -21
     moved = s.copy()
     moved[c] = np.float32(float(exact[c]) + 1.5 * e)
     with pytest.raises(AssertionError, match="beyond its bound"):
