@@ -561,7 +561,7 @@ def bench_centroid(args, w, W, K, budgets=(0, 16, 256), profile=False):
         out["by_budget"][str(n)] = {
             "steps_per_s": round(1e6 / cold, 1), "step_us": L["step_us"], "breakdown_us": L["breakdown_cold"],
             "centroid_terms_per_step": idx.n_graphs * n,
-            "centroid_kernel_bytes_per_step": idx.n_graphs * n * 2 * w.head_dim * 8}
+            "centroid_kernel_bytes_per_step": idx.n_graphs * n * 12 * w.head_dim}  # fp32 row + fp64 value sum
     if not profile and "0" in out["by_budget"]:
         base = out["by_budget"]["0"]["step_us"]
         for n in budgets:

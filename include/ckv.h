@@ -205,8 +205,9 @@ ckv_status ckv_score_centroids(const ckv_kv *kv, const ckv_index *idx, const voi
  * max_comm > 0, holds at most max_comm communities) is taken: the first
  * community that does not fit ends the walk.  `scores` are the screening
  * scores of ckv_score_centroids for the same q; exact scores are computed here
- * (from csum and size) for every community whose screening interval leaves its
- * place relative to the cut open, so the result is that of the exact scores.
+ * (from the centroid rows idx->cent) for every community whose screening
+ * interval leaves its place relative to the cut open, so the result is that of
+ * the exact scores.
  * Outputs per graph: sel[G][c_cap] taken ids ascending, sel_n[G] their count,
  * top[G] the best-ranked non-empty community (-1 if none), tok_list[G][t_cap]
  * the attended positions (sinks first, then members of the taken communities)
