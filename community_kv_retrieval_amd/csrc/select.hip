@@ -85,7 +85,7 @@ struct SelectParams {
 };
 
 struct SelShared {
-    union {
+    union __attribute__((aligned(16))) {
         struct {
             int soff[kSelLds];   // first base member in toks of the k-th taken community
             int spref[kSelLds];  // its first slot in the token list (after the sinks)
@@ -1473,7 +1473,8 @@ __global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectPara
     const int ntaken = p.sel_n[g];
     load_qbar(p, gc, sh);
     for (int i = tid; i < C / 32; i += kSelThreads) sh.bits[i] = 0u;
-    sh.bw[tid] = 0;  // kBins == kSelThreads
+    sh.bw[tid] = 0;   // kBins == kSelThreads
+    sh.bwl[tid] = 0;  // rank counts of the listed candidates
     if (tid == 0) sh.ccount = 0;
     __syncthreads();
     for (int i = tid; i < ntaken; i += kSelThreads) {
@@ -1588,12 +1589,28 @@ __global__ __launch_bounds__(kSelThreads) void centroid_select_kernel(SelectPara
             }
             unsigned long long t2 = 0ull;  // taken: keys above t2
             if (ncand <= kCentRankMax) {
-                // rank of each key among the candidates' (keys are distinct)
-                const unsigned long long mine = k2[0];
-                int above = 0;
-                for (int e = 0; e < ncand; ++e) above += sh.u.ls.key[e] > mine ? 1 : 0;
-                if (tid < ncand && above < N) {
-                    const int c = (int)(0xFFFFFFFFu - (uint32_t)mine);
+                // Rank of each key among the candidates' (keys are distinct):
+                // candidate e is counted by 1024 / P2 threads (P2 = ncand
+                // rounded up to a power of two), each over its own slice of
+                // the keys, two keys per 16-byte read; the partial counts
+                // meet in sh.bwl.
+                const int p2 = ncand <= 1 ? 1 : 1 << (32 - __builtin_clz(ncand - 1));
+                const int e = tid & (p2 - 1), parts = kSelThreads / p2;
+                const int chunk = ((ncand + parts - 1) / parts + 1) & ~1;
+                const int k0 = (tid / p2) * chunk, k1 = min(k0 + chunk, ncand);
+                if (e < ncand && k0 < k1) {
+                    const unsigned long long mine = sh.u.ls.key[e];
+                    int above = 0;
+                    for (int k = k0; k < k1; k += 2) {  // k0 even: 16-byte aligned pairs inside key[kList]
+                        const ulonglong2 kk = *reinterpret_cast<const ulonglong2 *>(&sh.u.ls.key[k]);
+                        above += kk.x > mine ? 1 : 0;
+                        above += (k + 1 < k1 && kk.y > mine) ? 1 : 0;
+                    }
+                    atomicAdd(&sh.bwl[e], above);
+                }
+                __syncthreads();
+                if (tid < ncand && sh.bwl[tid] < N) {
+                    const int c = (int)(0xFFFFFFFFu - (uint32_t)k2[0]);
                     atomicOr(&sh.bits[c >> 5], 1u << (c & 31));
                 }
             } else {

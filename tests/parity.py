@@ -56,6 +56,7 @@ class Stats:
     near_cent: int = 0
     cent_terms: int = 0
     cent_visible: int = 0   # graphs whose output the centroid terms move beyond the output tolerance
+    band_min: int = 0       # largest lower bound of a selection's band seen (_band_lower_bound)
     gaps: List[float] = field(default_factory=list)
 
 
@@ -145,6 +146,27 @@ def _check_screening(scores, cscale, q_heads, exact, counts, where: str):
     assert np.all(err <= bound), f"{where}: screening error {err.max():.3g} beyond its bound"
 
 
+def _band_lower_bound(r: O.GraphStep, counts, cscale, q_heads) -> int:
+    """Live communities whose screening interval holds the exact score of the
+    walk's stopper (the best-ranked live community not taken).  Their upper
+    bounds reach the cut and their lower bounds do not clear it, so each of them
+    is in the selection's band of undecided communities however the score bins
+    fall: the count is a lower bound of the band's size (0 when every live
+    community is taken)."""
+    C, D = counts.size, q_heads.shape[-1]
+    live = counts > 0
+    out = live.copy()
+    out[np.asarray(r.selected, dtype=np.int64)] = False
+    if not out.any():
+        return 0
+    s = r.scores[:C].astype(np.float64)
+    ids = np.flatnonzero(out)
+    stop = ids[np.lexsort((ids, -s[ids]))[0]]  # highest score, then lowest id
+    qbar = q_heads.astype(np.float64).sum(axis=0).astype(np.float32).astype(np.float64)
+    E = cscale[:C].astype(np.float64) * np.abs(qbar).sum() * screen_factor(D)
+    return int((live & (np.abs(s - s[stop]) <= E)).sum())
+
+
 def _selection_ok(r: O.GraphStep, counts, gpu_sel, w, stats: Stats, where: str) -> bool:
     return D.selection_ok(r.scores, counts, r.selected, gpu_sel, w.budget, w.max_comm, where, stats.gaps) or \
         _count(stats, "near_sel")
@@ -198,6 +220,9 @@ def check_graph(H, g: int, orc: O.Oracle, qn: np.ndarray, k_new: np.ndarray, w: 
     assert (np.diff(gsel) > 0).all(), f"{where}: sel not ascending"
     r = orc.step_graph(g, qn)
     _check_screening(H["scores"][g], H["cscale"][g], qn[st.b, st.qh0:st.qh0 + st.nh], r.scores, st.counts, where)
+    if w.max_comm == 0:
+        stats.band_min = max(stats.band_min, _band_lower_bound(r, st.counts, H["cscale"][g],
+                                                               qn[st.b, st.qh0:st.qh0 + st.nh]))
     assert H["top"][g] == r.top, f"{where}: top {H['top'][g]} != {r.top}"
     if not _selection_ok(r, st.counts, gsel, w, stats, where):
         r = orc.step_graph(g, qn, force_sel=gsel)

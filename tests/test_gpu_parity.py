@@ -96,6 +96,20 @@ def test_selection_beyond_the_candidates(mode, budget):
     PY.run_steps(w, 9, w.steps)
 
 
+@pytest.mark.parametrize("budget,mean_size,max_size", [(30000, 6, 24), (8000, 5, 20)])
+def test_long_band(budget, mean_size, max_size):
+    """About 10 000 small communities over 60 000 tokens: more than 512
+    communities' screening intervals hold the score where the walk stops (a
+    lower bound of the band, counted on the host), so the selection cuts a band
+    of hundreds of members through its score bins, with crowded cut bins left
+    to the radix select."""
+    w = small_per_head(n_ctx=60000, n_q_heads=8, n_kv_heads=2, budget=budget, mean_size=mean_size, min_size=1,
+                       max_size=max_size, steps=2)
+    PY.log(f"long band: budget {budget}, mean community size {mean_size}")
+    stats = PY.run_steps(w, 19, w.steps)
+    assert stats.band_min > 512, f"band lower bound {stats.band_min}: the long-band cut was not reached"
+
+
 def test_community_cap():
     w = small_per_head(n_ctx=3000, budget=1 << 20, max_comm=5, steps=3)
     PY.log("max_comm 5")
