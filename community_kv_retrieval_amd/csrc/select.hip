@@ -103,7 +103,7 @@ struct SelShared {
     uint32_t hw[256];  // radix select: token weight per digit
     uint32_t hn[256];  // radix select: candidates per digit
     uint32_t bits[CKV_MAX_C_CAP / 32];
-    double qbar[128];
+    double qbar[128];  // interleaved for the exact scores: dimension l * (D / 16) + e at [e * 16 + l]
     float qabs[128];
     unsigned long long ckey[64];
     int csz[64];
@@ -420,7 +420,7 @@ __device__ __forceinline__ void exact_scores(const SelectParams &p, int g, int n
             double part = 0.0;
             if (nn[r] > 0) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) part = fma(sh.qbar[l16 * E + e], (double)cs[r][e], part);
+                for (int e = 0; e < E; ++e) part = fma(sh.qbar[e * 16 + l16], (double)cs[r][e], part);
             }
             const double S = row16_sum_d(part);
             const int i = i0 + 64 * r;
@@ -455,7 +455,9 @@ __device__ __forceinline__ void load_qbar(const SelectParams &p, const GraphCoor
 #pragma unroll
         for (int h = 0; h < kMaxHeads; ++h)
             if (h < gc.nh) a += (double)qv[h];
-        sh.qbar[tid] = a;
+        // dimension d = 16-lane group lane l * (D / 16) + e at [e][l]: the
+        // exact scores' reads of one e by 16 lanes are 128 contiguous bytes
+        sh.qbar[(tid % (p.D / 16)) * 16 + tid / (p.D / 16)] = a;
         sh.qabs[tid] = fabsf((float)a);
     }
 }
