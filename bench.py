@@ -60,6 +60,8 @@ def main():
                     help="steps per budget of the attention-mass recall sweep (0: skip)")
     ap.add_argument("--profile", action="store_true", help="only warm-up + timed steps (for rocprofv3 runs)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill graph-construction leg")
+    ap.add_argument("--no-refresh", action="store_true", help="skip the refresh-vs-incremental leg")
+    ap.add_argument("--refresh-only", action="store_true", help="only the refresh-vs-incremental leg")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill graph construction of the workload's first sequence (profiling)")
     ap.add_argument("--eager-only", action="store_true", help="with --profile: no HIP graph (counter runs)")
@@ -90,6 +92,9 @@ def main():
         return
     W, K = args.warmup, args.steps
     total = W + K
+    if args.refresh_only:
+        print(json.dumps({"refresh_vs_incremental": bench_refresh(args, synth.preset("qwen3_8b_32k"))}), flush=True)
+        return
     if args.prefill_only:
         slices = synth.gen_layer(w, args.seed)
         layer = runner.load_layer(w, args.seed, extra=1, slices=slices)
@@ -198,6 +203,10 @@ def main():
     if not args.no_centroid and w.name == "llama31_8b_128k":
         centroid = bench_centroid(args, w, W, K)
 
+    refresh = None
+    if not args.no_refresh and w.name == "llama31_8b_128k":
+        refresh = bench_refresh(args, synth.preset("qwen3_8b_32k"))
+
     src_hash = gather_source_hash()
     traffic = measured_traffic(w.name, src_hash)
     cold_step_us = float(L["cold_us"].mean())
@@ -247,6 +256,7 @@ def main():
         "prefill_graph": prefill,
         "group_b8": group,
         "centroid_budget": centroid,
+        "refresh_vs_incremental": refresh,
         "cpu_baseline": cpu,
         "host_inputs": {"ms_per_step": round(ms_host, 5), "steps_per_s": round(1e3 / ms_host, 1),
                         "bytes_per_step": host_bytes,
@@ -622,12 +632,129 @@ def bench_prefill(w, seed, kv, slices, reps=3, cpu_seconds=0.0):
         tf = flops / (t * 1e-3) / 1e12
         out[name] = {"ms_per_layer": round(t, 3), "tflops": round(tf, 1),
                      "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+        if name == "per_head":
+            out["leiden"] = leiden_timing(w, edges, n)
         del edges, weights, ws
     if cpu_seconds > 0:
         out["cpu_baseline"] = prefill_cpu_baseline(w, q, slices, cpu_seconds)
     out["roofline"] = {"bound": "mfma", "kernel": "prefill_topk (per head, weights)",
                        "achieved": out["per_head"]["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                        "frac": out["per_head"]["frac_of_bf16_mfma_peak"], "traffic": None}
+    return out
+
+
+def leiden_timing(w, edges, n, reps=2):
+    """Leiden partition (Figure 1 panel (2); ckv_leiden_partition, host threads)
+    of the prompt's per-head graphs from the prefill edges just computed."""
+    import time
+
+    import numpy as np
+
+    from community_kv_retrieval_amd import ckv
+
+    e = edges.cpu().numpy()
+    n_tok = np.full(e.shape[0], n, dtype=np.int32)
+    secs = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        _, n_comm, q = ckv.ckv_leiden_partition(n_tok, w.n_sinks, e, (1, 1), 0)
+        secs.append(time.perf_counter() - t0)
+    return {"graphs": int(e.shape[0]), "tokens_per_graph": int(n), "gamma": 1, "host_threads": os.cpu_count(),
+            "s_per_layer": round(min(secs), 4), "communities_mean": round(float(n_comm.mean()), 1),
+            "community_size_mean": round(float((n - w.n_sinks) / n_comm.mean()), 1),
+            "modularity_mean": round(float(q.mean()), 4),
+            "context": "the page's Table 10 lists 0.37-0.45 s of exposed Leiden time per prefill (its hardware)"}
+
+
+def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1)):
+    """Refresh against incremental assignment (Tables 8 and 9) on a decode
+    stream that drifts to topics the prompt never had: both runs start from
+    the Leiden partition of the prompt's graph (prefill top-kappa edges,
+    ckv_prefill_topk); "incremental" only assigns new tokens, "refresh" also
+    re-partitions the grown graph every `interval` steps.  Reported per run:
+    attention-mass recall and the output's relative error against dense
+    attention over every cached token (all heads, and the heads whose query is
+    a drift topic), the modularity of the partition on the grown graph, and
+    the cost of each refresh (host Leiden + index rebuild, wall clock)."""
+    import time
+
+    import numpy as np
+    import torch
+
+    from community_kv_retrieval_amd import ckv, runner, synth
+
+    w = base.replace(name=base.name + "_drift", drift_topics=16, drift_rate=0.5)
+    slices = synth.gen_layer(w, args.seed)
+    steps_in = [synth.gen_step(w, args.seed, t, slices) for t in range(steps)]
+    Q = torch.stack([s.q for s in steps_in]).cuda()
+    KN = torch.stack([s.k_new for s in steps_in]).cuda()
+    VN = torch.stack([s.v_new for s in steps_in]).cuda()
+    drift = np.stack([s.target for s in steps_in])[:, 0] < 0          # [steps][Hq] (batch 1)
+    parts = [slices[0][kh].part for kh in range(w.n_kv_heads)]
+    qp = synth.gen_prefill_queries_device(w, args.seed, 0, 0, parts)
+    n = int(qp.shape[0])
+    mode = ckv.CKV_MODE_PER_HEAD if w.mode == synth.PER_HEAD else ckv.CKV_MODE_QUERY_GROUP
+    out = {"workload": w.name, "ctx": w.n_ctx, "budget": w.budget, "steps": steps, "refresh_every": interval,
+           "gamma": gamma[0] / gamma[1], "drift_topics_per_kv_head": w.drift_topics, "drift_rate": w.drift_rate,
+           "quality": "synthetic stand-in for the page's NLL/KL/top-1 (no model): recall and output error "
+                      "against dense attention"}
+    for name, do_refresh in (("incremental", False), ("refresh", True)):
+        layer = runner.load_layer(w, args.seed, extra=steps + 1, slices=slices)
+        dec, kv = layer.dec, layer.kv
+        dec.defer = False
+        table = ckv.EdgeTable(kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
+        graphs = w.n_q_heads if mode == ckv.CKV_MODE_PER_HEAD else w.n_kv_heads
+        pe = torch.empty((graphs, n, w.kappa), dtype=torch.int32, device="cuda")
+        ws = ckv.prefill_workspace(kv, mode, n)
+        ckv.ckv_prefill_topk(kv, mode, 0, qp, w.n_sinks, w.kappa, w.sm_scale, pe, None, ws)
+        table.put_prefill(0, pe)
+        del pe, ws
+        t0 = time.perf_counter()
+        q_init = dec.refresh(table, gamma)
+        torch.cuda.synchronize()
+        init_ms = (time.perf_counter() - t0) * 1e3
+        dec.edge_table = table
+        dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
+        dout = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        rec, err, qual, ref_ms, ncomm = [], [], [], [], []
+        for t in range(steps):
+            dec.retrieve(Q[t])
+            dec.attend(Q[t])
+            dec.dense(Q[t], dout, ml=dml)
+            rec.append(dec.recall(dml).flatten())
+            d = torch.linalg.vector_norm(dec.buf.out - dout, dim=-1) / torch.linalg.vector_norm(dout, dim=-1)
+            err.append(d.flatten())
+            dec.update(KN[t], VN[t])
+            if (t + 1) % interval == 0:
+                if do_refresh and t + 1 < steps:
+                    torch.cuda.synchronize()
+                    t0 = time.perf_counter()
+                    qv = dec.refresh(table, gamma)
+                    torch.cuda.synchronize()
+                    ref_ms.append(round((time.perf_counter() - t0) * 1e3, 1))
+                else:
+                    idx = dec.idx
+                    lens = kv.seq_len.cpu().numpy()
+                    n_tok = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
+                    qv = ckv.ckv_partition_quality(n_tok, idx.n_sinks, table.e[:, :idx.l_cap].cpu().numpy(),
+                                                   np.ascontiguousarray(idx.label.cpu().numpy()), gamma)
+                qual.append(round(float(np.mean(qv)), 4))
+                ncomm.append(round(float(dec.idx.n_comm.float().mean()), 1))
+        R = torch.stack(rec).cpu().numpy()            # [steps][G * hpg] = [steps][Hq] per head
+        E = torch.stack(err).cpu().numpy()
+        win = [round(float(R[i:i + interval].mean()), 4) for i in range(0, steps, interval)]
+        out[name] = {"recall_mean": round(float(R.mean()), 4), "recall_drift_heads": round(float(R[drift].mean()), 4),
+                     "recall_prompt_topic_heads": round(float(R[~drift].mean()), 4),
+                     "recall_by_window": win,
+                     "out_rel_err_mean": round(float(E.mean()), 4),
+                     "out_rel_err_drift_heads": round(float(E[drift].mean()), 4),
+                     "modularity_by_window": qual, "communities_by_window": ncomm,
+                     "initial_partition": {"modularity_mean": round(float(np.mean(q_init)), 4), "ms": round(init_ms, 1)}}
+        if do_refresh:
+            out[name]["refresh_ms"] = ref_ms
+            out[name]["refresh_ms_per_step_amortised"] = round(float(np.mean(ref_ms)) / interval, 3) if ref_ms else None
+        del layer, dec, kv, table
+        torch.cuda.empty_cache()
     return out
 
 

@@ -31,9 +31,17 @@ FLAGS = [
 ]
 
 
+# host-only sources (no device code): the system C++ compiler
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-pthread", "-I", INCLUDE, "-I", CSRC]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -43,12 +51,12 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -63,12 +71,13 @@ def build_trace(verbose: bool = False) -> str:
     one translation unit into _build/libckv_trace.so.  Not the product library."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    hosts = sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
     unity = os.path.join(BUILD, "ckv_trace_all.hip")
     with open(unity, "w") as f:
         for src in srcs:
             f.write(f'#include "{src}"\n')
     out = os.path.join(BUILD, "libckv_trace.so")
-    cmd = [HIPCC, *FLAGS, "-DCKV_PHASE_TRACE", "-shared", unity, "-o", out]
+    cmd = [HIPCC, *FLAGS, "-DCKV_PHASE_TRACE", "-shared", "-pthread", unity, "-x", "c++", *hosts, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"trace build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -34,6 +34,7 @@ EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_
            "ckv_select_communities", "ckv_gather_attend", "ckv_gather_attend_noalloc", "ckv_assign_update",
            "ckv_dense_attend",
            "ckv_attention_recall", "ckv_prefill_workspace_bytes", "ckv_prefill_topk", "ckv_read_rows",
+           "ckv_leiden_partition", "ckv_partition_quality",
            "ckv_time_next_launch", "ckv_status_str", "ckv_abi_version")
 
 
@@ -86,6 +87,10 @@ def _load():
         "ckv_prefill_topk": (c_int32, [KVP, c_int32, c_int32, c_void_p, c_int32, c_int32, c_int32, c_float,
                                        c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "ckv_read_rows": (c_int32, [KVP, c_void_p, c_int32, c_void_p, c_void_p]),
+        "ckv_leiden_partition": (c_int32, [c_int32, c_void_p, c_int32, c_void_p, ctypes.c_int64, c_int32,
+                                           ctypes.c_int64, ctypes.c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
+        "ckv_partition_quality": (c_int32, [c_int32, c_void_p, c_int32, c_void_p, ctypes.c_int64, c_int32,
+                                            ctypes.c_int64, ctypes.c_int64, c_int32, c_void_p, c_void_p]),
         "ckv_time_next_launch": (c_int32, [c_void_p, c_void_p]),
         "ckv_status_str": (ctypes.c_char_p, [c_int32]),
         "ckv_abi_version": (c_int32, []),
@@ -382,6 +387,45 @@ def ckv_read_rows(kv: KVStore, rows: torch.Tensor, part: torch.Tensor, stream=No
     _check("ckv_read_rows", LIB.ckv_read_rows(ctypes.byref(kv.desc), _ptr(rows), n, _ptr(part), _stream(stream)))
 
 
+def _host_i32(a, name: str, shape) -> "np.ndarray":
+    import numpy as np
+    if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous and a.shape == tuple(shape)):
+        raise ValueError(f"{name}: expected a C-contiguous int32 host array of shape {tuple(shape)}")
+    return a
+
+
+def ckv_leiden_partition(n_tokens, n_sinks: int, edges, gamma=(1, 1), n_threads: int = 0):
+    """Leiden partition of every graph's token graph (host call).
+
+    n_tokens: int32 [G]; edges: int32 [G][row_stride][kappa] host array.
+    Returns (labels int32 [G][row_stride], n_comm int32 [G], quality float64 [G])."""
+    import numpy as np
+    G, stride, kappa = edges.shape if edges.ndim == 3 else (0, 0, 0)
+    _host_i32(edges, "edges", (G, stride, kappa))
+    _host_i32(n_tokens, "n_tokens", (G,))
+    labels = np.empty((G, stride), dtype=np.int32)
+    n_comm = np.empty((G,), dtype=np.int32)
+    quality = np.empty((G,), dtype=np.float64)
+    _check("ckv_leiden_partition", LIB.ckv_leiden_partition(
+        G, n_tokens.ctypes.data, n_sinks, edges.ctypes.data, stride, kappa, int(gamma[0]), int(gamma[1]),
+        n_threads, labels.ctypes.data, n_comm.ctypes.data, quality.ctypes.data))
+    return labels, n_comm, quality
+
+
+def ckv_partition_quality(n_tokens, n_sinks: int, edges, labels, gamma=(1, 1), n_threads: int = 0):
+    """Modularity of given labels on every graph's token graph (host call)."""
+    import numpy as np
+    G, stride, kappa = edges.shape if edges.ndim == 3 else (0, 0, 0)
+    _host_i32(edges, "edges", (G, stride, kappa))
+    _host_i32(n_tokens, "n_tokens", (G,))
+    _host_i32(labels, "labels", (G, stride))
+    quality = np.empty((G,), dtype=np.float64)
+    _check("ckv_partition_quality", LIB.ckv_partition_quality(
+        G, n_tokens.ctypes.data, n_sinks, edges.ctypes.data, stride, kappa, int(gamma[0]), int(gamma[1]),
+        n_threads, labels.ctypes.data, quality.ctypes.data))
+    return quality
+
+
 def ckv_time_next_launch(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]):
     """Arms the next step kernel of this thread to stamp `start`/`stop` from its own dispatch.
 
@@ -418,6 +462,34 @@ class DecodeBuffers:
         self.ws = torch.zeros((ckv_workspace_bytes(kv, idx, self.t_cap),), dtype=torch.uint8, device=device)
 
 
+class EdgeTable:
+    """The token graph of one layer as edge rows: e[g][i][0..kappa) = token i's
+    edges in graph g (-1 = none), prompt rows from ckv_prefill_topk, decoded
+    rows from each step's ckv_assign_update (Figure 1, panels (1) and (3)).
+    Device memory; ckv_leiden_partition reads a host copy of it."""
+
+    def __init__(self, kv: KVStore, mode: int, cap: int, kappa: int, device="cuda"):
+        self.mode, self.kappa, self.cap = mode, kappa, cap
+        per = kv.n_q_heads if mode == CKV_MODE_PER_HEAD else kv.n_kv_heads
+        self.per_seq = per
+        self.n_graphs = kv.batch * per
+        self.e = torch.full((self.n_graphs, cap, kappa), -1, dtype=torch.int32, device=device)
+        # sequence of every graph, to find the row a step's new token takes
+        self.graph_seq = torch.arange(self.n_graphs, device=device) // per
+
+    def put_prefill(self, b: int, edges: torch.Tensor):
+        """Rows 0..n-1 of sequence b's graphs from ckv_prefill_topk's edges
+        [graphs of the sequence][n][kappa]."""
+        _need(edges, "edges", torch.int32, (self.per_seq, edges.shape[1], self.kappa))
+        self.e[b * self.per_seq:(b + 1) * self.per_seq, :edges.shape[1]] = edges
+
+    def put_step(self, edges: torch.Tensor, pos: torch.Tensor):
+        """Row pos[seq of g] of every graph g from a step's edges [G][kappa];
+        pos: the sequences' lengths before the step (the new tokens' positions)."""
+        rows = pos.long()[self.graph_seq]
+        self.e[torch.arange(self.n_graphs, device=self.e.device), rows] = edges
+
+
 class Decoder:
     """Runs CommunityKV decode steps for one layer.
 
@@ -438,8 +510,37 @@ class Decoder:
         self.kv, self.idx = kv, idx
         self.budget, self.max_comm, self.kappa, self.sm_scale = budget, max_comm, kappa, sm_scale
         self.defer = defer
+        self.device = device
         self.buf = DecodeBuffers(kv, idx, budget, kappa, device)
         self.set_windows(windows)
+        # when set, every update() records the step's edges in the table (the
+        # graph a refresh partitions); windowed steps do not record
+        self.edge_table: Optional[EdgeTable] = None
+
+    def refresh(self, table: "EdgeTable", gamma=(1, 1), n_threads: int = 0, c_cap: Optional[int] = None):
+        """Re-partition every graph's token graph (prompt and decoded rows of
+        `table`) with ckv_leiden_partition and rebuild the index from the new
+        labels with ckv_index_build ("Refresh" in Tables 8 and 9, against the
+        incremental assignment of every step).  Replaces self.idx and the step
+        buffers; returns the partitions' modularity [G] (float64, host)."""
+        import numpy as np
+        idx = self.idx
+        if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap < idx.l_cap:
+            raise ValueError("edge table does not match the index")
+        lens = self.kv.seq_len.cpu().numpy()
+        n_tok = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
+        edges = table.e[:, :idx.l_cap].cpu().numpy()
+        labels, n_comm, quality = ckv_leiden_partition(n_tok, idx.n_sinks, edges, gamma, n_threads)
+        if int(n_comm.max(initial=0)) > CKV_MAX_C_CAP:
+            raise ValueError(f"{int(n_comm.max())} communities exceed the index's limit {CKV_MAX_C_CAP}")
+        new = CommunityIndex(self.kv, idx.mode, [max(1, int(c)) for c in n_comm], idx.l_cap, idx.tail_cap,
+                             idx.n_sinks, c_cap=c_cap, device=self.device, cent_budget=idx.cent_budget)
+        new.n_comm.copy_(torch.from_numpy(n_comm))
+        self.idx = new
+        self.buf = DecodeBuffers(self.kv, new, self.budget, self.kappa, self.device)
+        self.set_windows(self.windows)
+        self.build(torch.from_numpy(labels).to(self.device))
+        return quality
 
     def set_windows(self, windows: int):
         G = self.idx.n_graphs
@@ -469,8 +570,11 @@ class Decoder:
 
     def update(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
         b = self.buf
+        pos = self.kv.seq_len.clone() if self.edge_table is not None else None
         ckv_assign_update(self.kv, self.idx, b.tok_list, b.tok_n, b.logits, b.ml, b.top, self.kappa, k_new, v_new,
                           b.edges, b.assign, b.ws, stream, out=b.out if self.defer else None)
+        if self.edge_table is not None:
+            self.edge_table.put_step(b.edges, pos)
 
     def step(self, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
         if self.windows == 1:

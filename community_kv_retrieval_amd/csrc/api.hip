@@ -66,7 +66,7 @@ char *at(void *ws, size_t off) { return static_cast<char *>(ws) + off; }
 
 extern "C" {
 
-int32_t ckv_abi_version(void) { return 10; }
+int32_t ckv_abi_version(void) { return 11; }
 
 ckv_status ckv_time_next_launch(ckv_event_t start, ckv_event_t stop) {
     if ((start == nullptr) != (stop == nullptr)) return CKV_E_INVALID;

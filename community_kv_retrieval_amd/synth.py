@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 # stream tags for SeedSequence spawn keys
-_T_PART, _T_KEY, _T_VAL, _T_STEP, _T_LEN, _T_DEV, _T_DEV_STEP, _T_PREFILL = 1, 2, 3, 4, 5, 6, 7, 8
+_T_PART, _T_KEY, _T_VAL, _T_STEP, _T_LEN, _T_DEV, _T_DEV_STEP, _T_PREFILL, _T_DRIFT = 1, 2, 3, 4, 5, 6, 7, 8, 9
 
 PER_HEAD = "per_head"
 GROUP = "group"
@@ -62,6 +62,8 @@ class Workload:
     n_layers: int = 1
     min_ctx: int = 0           # > 0: per-sequence lengths uniform in [min_ctx, n_ctx]
     cent_budget: int = 0       # centroid entries of next-ranked communities (Table 6; 0 = none)
+    drift_topics: int = 0      # > 0: decode steps also draw from this many centres absent from the prompt
+    drift_rate: float = 0.0    # chance that a head's decode query (and the new key) takes such a centre
 
     @property
     def group(self) -> int:
@@ -267,6 +269,8 @@ def gen_step(w: Workload, seed: int, step: int, slices: List[List[Slice]], layer
     the group's first query head, scaled like the prefill keys.
     """
     B, Hq, Hkv, d, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    if w.drift_topics > 0:
+        return _gen_step_drift(w, seed, step, slices, layer)
     q = np.empty((B, Hq, d), dtype=np.float32)
     kn = np.empty((B, Hkv, d), dtype=np.float32)
     vn = np.empty((B, Hkv, d), dtype=np.float32)
@@ -285,6 +289,43 @@ def gen_step(w: Workload, seed: int, step: int, slices: List[List[Slice]], layer
                 tgt[b, kh * G + j] = cs[j]
             kk = r.standard_normal(d, dtype=np.float32)
             kn[b, kh] = (part.centers[cs[0]] + np.float32(w.noise) * kk) * np.float32(w.key_scale)
+            vn[b, kh] = r.standard_normal(d, dtype=np.float32)
+    return StepInput(_to_storage(q, w), _to_storage(kn, w), _to_storage(vn, w), tgt)
+
+
+def drift_centers(w: Workload, seed: int, layer: int, b: int, kh: int) -> np.ndarray:
+    """The drift_topics centres of one slice that the prompt never uses [T][d]."""
+    return _rng(seed, _T_DRIFT, layer, b, kh).standard_normal((w.drift_topics, w.head_dim), dtype=np.float32)
+
+
+def _gen_step_drift(w: Workload, seed: int, step: int, slices, layer: int) -> StepInput:
+    """gen_step with topic drift: each head's centre is, with chance
+    drift_rate, one of the slice's drift centres (target -1 - topic), else a
+    planted community's.  The new key follows the group's first head, so the
+    cache grows with tokens of topics the prompt's partition has no community
+    for: the case a re-partition (Tables 8 and 9, "Refresh") addresses."""
+    B, Hq, Hkv, d, G = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.group
+    q = np.empty((B, Hq, d), dtype=np.float32)
+    kn = np.empty((B, Hkv, d), dtype=np.float32)
+    vn = np.empty((B, Hkv, d), dtype=np.float32)
+    tgt = np.empty((B, Hq), dtype=np.int32)
+    for b in range(B):
+        for kh in range(Hkv):
+            part = slices[b][kh].part
+            extra = drift_centers(w, seed, layer, b, kh)
+            r = _rng(seed, _T_STEP, layer, b, kh, step)
+            nh = G if w.mode == PER_HEAD else 1
+            drift = r.random(nh) < w.drift_rate
+            cs = np.where(drift, -1 - r.integers(0, w.drift_topics, size=nh), r.integers(0, part.n_comm, size=nh))
+            if w.mode != PER_HEAD:
+                cs = np.repeat(cs, G)
+            qn = r.standard_normal((G, d), dtype=np.float32)
+            cen = [extra[-1 - c] if c < 0 else part.centers[c] for c in cs]
+            for j in range(G):
+                q[b, kh * G + j] = cen[j] + np.float32(w.noise) * qn[j]
+                tgt[b, kh * G + j] = cs[j]
+            kk = r.standard_normal(d, dtype=np.float32)
+            kn[b, kh] = (cen[0] + np.float32(w.noise) * kk) * np.float32(w.key_scale)
             vn[b, kh] = r.standard_normal(d, dtype=np.float32)
     return StepInput(_to_storage(q, w), _to_storage(kn, w), _to_storage(vn, w), tgt)
 

@@ -346,6 +346,53 @@ ckv_status ckv_prefill_topk(const ckv_kv *kv, int32_t mode, int32_t b, const voi
                             int32_t n_sinks, int32_t kappa, float sm_scale, int32_t *edges, float *weights,
                             void *ws, size_t ws_bytes, ckv_stream_t stream);
 
+/* Leiden partition of token graphs (Figure 1 panel (2): the prefill graph is
+ * partitioned with the Leiden algorithm; Figure 2: a resolution parameter
+ * gamma sets the community size; Tables 8 and 9: re-partitioning the grown
+ * graph, "Refresh", against incremental assignment).  HOST call: every
+ * pointer below is host memory, and nothing is enqueued on a GPU; Figure 4
+ * runs the partitioning beside the GPU, asynchronously, which a caller gets
+ * by running this call on a thread of its own.
+ *
+ * Graph g (0 <= g < n_graphs) has n_tokens[g] tokens.  Row i of
+ * edges[g][row_stride][kappa] (int32) lists token i's edges (-1 = none), as
+ * ckv_prefill_topk writes them for prompt tokens and ckv_assign_update for
+ * decoded ones; rows >= n_tokens[g] are not read.  The graph's nodes are the
+ * tokens n_sinks .. n_tokens[g]-1; each listed edge i -> j adds one to the
+ * weight between i and j (so 1 or 2).  An edge to a sink, to itself or to a
+ * token >= n_tokens[g] is an error.
+ *
+ * Quality is modularity at resolution gamma_num / gamma_den; every decision
+ * compares exact integers.  The algorithm (Traag, Waltman and van Eck, Sci.
+ * Rep. 9, 5233, 2019): fast local moving, refinement into well-connected
+ * sub-communities, aggregation, until every community of a level is one node;
+ * its random choices are fixed (queue in token order; the best community wins,
+ * staying on ties, the lower id among equal ones; a new community only when
+ * strictly better; refinement takes the best strictly positive merge), so the
+ * result depends on the graph alone.
+ *
+ * Outputs: labels[g][row_stride] = community of each token, numbered 0, 1, ...
+ * in order of first token, -1 for sinks and rows >= n_tokens[g]; n_comm[g];
+ * quality[g] (NULL: not written) = modularity Q of the result.  n_threads
+ * host threads share the graphs (0: one per hardware thread).
+ * Errors (CKV_E_INVALID, outputs then undefined): n_graphs < 0, NULL arrays,
+ * kappa outside 1..32, n_tokens[g] outside 0..row_stride, gamma_num < 0,
+ * gamma_den <= 0, a bad edge, or a graph so large that (2m)^2 * 4 *
+ * max(gamma_num, gamma_den) reaches 2^62. */
+ckv_status ckv_leiden_partition(int32_t n_graphs, const int32_t *n_tokens, int32_t n_sinks, const int32_t *edges,
+                                int64_t row_stride, int32_t kappa, int64_t gamma_num, int64_t gamma_den,
+                                int32_t n_threads, int32_t *labels, int32_t *n_comm, double *quality);
+
+/* Modularity Q (Figure 3, left) of given labels on the same token graphs as
+ * ckv_leiden_partition (HOST call, host pointers, same edge rules): labels of
+ * tokens n_sinks .. n_tokens[g]-1 must lie in 0 .. n_tokens[g]-n_sinks-1 (any
+ * numbering, e.g. the labels an index holds after incremental assignment);
+ * quality[g] is written.  Q = 0 for a graph without edges.  Errors as above,
+ * plus CKV_E_INVALID for a label out of range. */
+ckv_status ckv_partition_quality(int32_t n_graphs, const int32_t *n_tokens, int32_t n_sinks, const int32_t *edges,
+                                 int64_t row_stride, int32_t kappa, int64_t gamma_num, int64_t gamma_den,
+                                 int32_t n_threads, const int32_t *labels, double *quality);
+
 /* Read ceiling of the gather's access pattern, for measurement (no part of
  * the method).  Reads the K|V rows rows[0..n) of the store (row id r: token
  * slot r % page_size of kv head (r / page_size) % n_kv_heads of page

@@ -542,6 +542,19 @@ class Oracle:
         for b in {b for (b, _) in self.K}:
             self.len[b] += 1
 
+    def repartition(self, gid: int, labels: np.ndarray, n_comm: int):
+        """Replace graph gid's partition by `labels` (one per cached position,
+        -1 for sinks) as a re-partition does ("Refresh", Tables 8 and 9): the
+        community state is rebuilt from scratch, each centroid the mean of its
+        members' keys (Figure 1, panel (2)), the value sums likewise."""
+        st = self.g[gid]
+        n = self.len[st.b]
+        lab = np.full(st.labels.shape[0], -1, dtype=np.int64)
+        lab[:n] = np.asarray(labels, dtype=np.int64)[:n]
+        sums, counts = community_sums(self.K[(st.b, st.kh)][:n], lab[:n], n_comm)
+        vsums, _ = community_sums(self.V[(st.b, st.kh)][:n], lab[:n], n_comm)
+        st.labels, st.sums, st.counts, st.vsums = lab, sums, counts, vsums
+
     def recall(self, gid: int, q, positions) -> np.ndarray:
         """Attention-mass recall of graph gid's heads for the given attended positions."""
         st = self.g[gid]

@@ -272,13 +272,16 @@ def check_graph(H, g: int, orc: O.Oracle, qn: np.ndarray, k_new: np.ndarray, w: 
 
 def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[int]] = None,
               check_state_every: int = 1, layer_kw: Optional[dict] = None, check_dense: bool = False,
-              pair=None, windows: int = 1, defer: bool = True, q_fn=None, first_step: int = 0) -> Stats:
+              pair=None, windows: int = 1, defer: bool = True, q_fn=None, first_step: int = 0,
+              edge_log: Optional[Dict] = None) -> Stats:
     """Steps the library and the oracle side by side and checks every output.
     windows > 1 runs each step as the decoder's windowed multi-stream step;
     defer=False runs complete gathers (combine inside the gather kernel).
     q_fn(t, q) -> q replaces step t's queries (both sides see the same ones).
     Steps are numbered first_step .. first_step + steps - 1 (the inputs of
-    step t are drawn for t), continuing a pair that has already run."""
+    step t are drawn for t), continuing a pair that has already run.
+    edge_log (a dict) receives edge_log[(t, g)] = the oracle's edges of graph
+    g at step t (after adopting an accepted near tie)."""
     layer, orc = pair if pair is not None else make_pair(w, seed, steps, graphs, **(layer_kw or {}))
     dev = layer.kv.kv.device
     dec, buf = layer.dec, layer.dec.buf
@@ -312,8 +315,10 @@ def run_steps(w: synth.Workload, seed: int, steps: int, graphs: Optional[List[in
         kn_host = inp.k_new.float().numpy()
         vn_host = inp.v_new.float().numpy()
         for g in orc.graph_ids:
-            check_graph(H, g, orc, qn, kn_host, w, stats, f"{w.name} seed={seed} step={t} graph={g}", dense,
-                        vn_host)
+            r = check_graph(H, g, orc, qn, kn_host, w, stats, f"{w.name} seed={seed} step={t} graph={g}", dense,
+                            vn_host)
+            if edge_log is not None:
+                edge_log[(t, g)] = np.asarray(r.edges, dtype=np.int64)
         orc.append(kn_host, vn_host)
         stats.steps += 1
         done = t + 1 - first_step

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert ckv.LIB.ckv_abi_version() == 10
+    assert ckv.LIB.ckv_abi_version() == 11
     for code in (0, -1, -2, -3, -4):
         assert ckv.ckv_status_str(code) != "unknown status"
     assert ckv.ckv_status_str(7) == "unknown status"

@@ -1,0 +1,118 @@
+"""Refresh (re-partitioning the grown token graph, Tables 8 and 9 of the
+CommunityKV page) on the GPU against the oracle.
+
+The whole cycle of Figure 1 at a small size: the prompt's graph (panel (1),
+ckv_prefill_topk, checked row by row, near ties adopted by the oracle), its
+Leiden partition (panel (2), ckv_leiden_partition on the library side,
+oracle/leiden_oracle.py on the other: labels bit-identical), the index built
+from it (CSR, sums, centroids and screening copy bit-exact), decode steps with
+every output checked (panel (3)), each step's edges appended to the graph,
+then a refresh: the grown graph partitioned again on both sides, labels and
+index compared again, and more checked steps on the new partition.
+"""
+import numpy as np
+import pytest
+import torch
+
+from community_kv_retrieval_amd import ckv, synth
+from oracle import ckv_oracle as O
+from oracle import leiden_oracle as LO
+from tests import decisions as D
+from tests import parity as PY
+
+pytestmark = pytest.mark.gpu
+
+
+def _workload(mode):
+    return synth.preset("qwen3_8b_32k").replace(
+        name=f"refresh_{mode}", n_ctx=1536, n_q_heads=8, n_kv_heads=2, budget=256, steps=48,
+        mode=synth.PER_HEAD if mode == "per_head" else synth.GROUP)
+
+
+def _prefill(layer, w, seed, orc_rows):
+    """Device prefill graph of sequence 0, each row checked against the
+    oracle's; the oracle keeps its own rows except where it adopts a near tie."""
+    mode = ckv.CKV_MODE_PER_HEAD if w.mode == synth.PER_HEAD else ckv.CKV_MODE_QUERY_GROUP
+    qp = synth.gen_prefill_queries(w, seed, 0, 0, layer.slices[0])
+    n = qp.shape[0]
+    graphs = w.n_q_heads if mode == ckv.CKV_MODE_PER_HEAD else w.n_kv_heads
+    edges = torch.empty((graphs, n, w.kappa), dtype=torch.int32, device="cuda")
+    ws = ckv.prefill_workspace(layer.kv, mode, n)
+    ckv.ckv_prefill_topk(layer.kv, mode, 0, qp.cuda(), w.n_sinks, w.kappa, w.sm_scale, edges, None, ws)
+    torch.cuda.synchronize()
+    got = edges.cpu().numpy()
+    qf = qp.float().numpy().astype(np.float64)
+    near = 0
+    for g in range(graphs):
+        _, kh, qh0, nh = w.graph_coords(g)
+        keys = layer.slices[0][kh].k.float().numpy().astype(np.float64)
+        ref, _ = O.prefill_edges(qf[:, qh0:qh0 + nh], keys, w.n_sinks, w.kappa, w.sm_scale)
+        for i in range(n):
+            if np.array_equal(ref[i], got[g, i]):
+                continue
+            W = O.prefill_row_weights(qf[i, qh0:qh0 + nh], i, keys, w.sm_scale)
+            assert not D.prefill_row_ok(W, i, w.n_sinks, w.kappa, ref[i], got[g, i], None, f"prefill g={g}")
+            ref[i] = got[g, i]
+            near += 1
+        orc_rows[g] = {i: ref[i] for i in range(n)}
+    return edges, near
+
+
+def _oracle_partition(orc, w, orc_rows, g):
+    st = orc.g[g]
+    n = orc.len[st.b]
+    rows = np.full((n, w.kappa), -1, dtype=np.int64)
+    for i, r in orc_rows[g].items():
+        rows[i, :r.size] = r
+    lab, nc = LO.partition_tokens(rows, n, w.n_sinks)
+    q = LO.modularity(LO.token_graph(rows, n, w.n_sinks), lab[w.n_sinks:].tolist())
+    return lab, nc, q, rows
+
+
+def _refresh_both(layer, orc, w, orc_rows, where):
+    dec = layer.dec
+    quality = dec.refresh(dec.edge_table)
+    layer.idx = dec.idx
+    torch.cuda.synchronize()
+    table = dec.edge_table.e.cpu().numpy()
+    label = dec.idx.label.cpu().numpy()
+    n_comm = dec.idx.n_comm.cpu().numpy()
+    for g in orc.graph_ids:
+        lab, nc, q, rows = _oracle_partition(orc, w, orc_rows, g)
+        n = lab.size
+        np.testing.assert_array_equal(table[g, :n], rows, err_msg=f"{where}: edge rows g={g}")
+        np.testing.assert_array_equal(label[g, :n], lab, err_msg=f"{where}: labels g={g}")
+        assert n_comm[g] == nc, f"{where}: n_comm g={g}"
+        assert quality[g] == pytest.approx(q, abs=1e-12), f"{where}: modularity g={g}"
+        orc.repartition(g, lab, nc)
+    PY.check_csr(layer, orc)
+    PY.check_index_state(layer, orc, w, full=True)
+    return n_comm
+
+
+@pytest.mark.parametrize("mode", ["per_head", "group"])
+def test_refresh_cycle_matches_oracle(mode):
+    w = _workload(mode)
+    seed = 5
+    steps_a, steps_b = 24, 24
+    PY.log(f"refresh cycle, {mode}: seed {seed}, {w.n_ctx} tokens, {w.n_graphs} graphs")
+    layer, orc = PY.make_pair(w, seed, steps_a + steps_b + 1)
+    dec = layer.dec
+    table = ckv.EdgeTable(layer.kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
+    dec.edge_table = table
+    orc_rows = {}
+    edges, near = _prefill(layer, w, seed, orc_rows)
+    table.put_prefill(0, edges)
+    PY.log(f"  prefill graph checked ({near} near ties adopted)")
+    nc0 = _refresh_both(layer, orc, w, orc_rows, "initial partition")
+    PY.log(f"  initial Leiden partition: {nc0.tolist()} communities")
+    log = {}
+    st = PY.run_steps(w, seed, steps_a, pair=(layer, orc), edge_log=log)
+    for (t, g), e in log.items():
+        orc_rows[g][orc.len[orc.g[g].b] - steps_a + t] = e
+    nc1 = _refresh_both(layer, orc, w, orc_rows, "refresh")
+    PY.log(f"  refresh after {steps_a} steps: {nc1.tolist()} communities")
+    log.clear()
+    st2 = PY.run_steps(w, seed, steps_b, pair=(layer, orc), first_step=steps_a, edge_log=log)
+    assert st.steps == steps_a and st2.steps == steps_b
+    PY.log(f"  {steps_a + steps_b} steps checked around the refresh (max abs {max(st.max_abs, st2.max_abs):.2e})")
