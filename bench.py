@@ -93,7 +93,8 @@ def main():
     W, K = args.warmup, args.steps
     total = W + K
     if args.refresh_only:
-        print(json.dumps({"refresh_vs_incremental": bench_refresh(args, synth.preset("qwen3_8b_32k"))}), flush=True)
+        print(json.dumps({"refresh_vs_incremental": bench_refresh(args, synth.preset("qwen3_8b_32k"), **REFRESH_LEG)}),
+              flush=True)
         return
     if args.prefill_only:
         slices = synth.gen_layer(w, args.seed)
@@ -205,7 +206,7 @@ def main():
 
     refresh = None
     if not args.no_refresh and w.name == "llama31_8b_128k":
-        refresh = bench_refresh(args, synth.preset("qwen3_8b_32k"))
+        refresh = bench_refresh(args, synth.preset("qwen3_8b_32k"), **REFRESH_LEG)
 
     src_hash = gather_source_hash()
     traffic = measured_traffic(w.name, src_hash)
@@ -643,6 +644,13 @@ def bench_prefill(w, seed, kv, slices, reps=3, cpu_seconds=0.0):
     return out
 
 
+# The refresh leg: per-head graphs of the 32K layer, resolution 512 (Leiden's
+# communities then average about 14 tokens at this size, near the planted 16;
+# modularity's community count grows like sqrt(n) at a fixed resolution),
+# 1024 drifting steps, a re-partition every 256.
+REFRESH_LEG = dict(steps=1024, interval=256, gamma=(512, 1))
+
+
 def leiden_timing(w, edges, n, reps=2):
     """Leiden partition (Figure 1 panel (2); ckv_leiden_partition, host threads)
     of the prompt's per-head graphs from the prefill edges just computed."""
@@ -666,7 +674,7 @@ def leiden_timing(w, edges, n, reps=2):
             "context": "the page's Table 10 lists 0.37-0.45 s of exposed Leiden time per prefill (its hardware)"}
 
 
-def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1)):
+def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topics=16, drift_rate=0.5):
     """Refresh against incremental assignment (Tables 8 and 9) on a decode
     stream that drifts to topics the prompt never had: both runs start from
     the Leiden partition of the prompt's graph (prefill top-kappa edges,
@@ -683,7 +691,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1)):
 
     from community_kv_retrieval_amd import ckv, runner, synth
 
-    w = base.replace(name=base.name + "_drift", drift_topics=16, drift_rate=0.5)
+    w = base.replace(name=base.name + "_drift", drift_topics=drift_topics, drift_rate=drift_rate)
     slices = synth.gen_layer(w, args.seed)
     steps_in = [synth.gen_step(w, args.seed, t, slices) for t in range(steps)]
     Q = torch.stack([s.q for s in steps_in]).cuda()
