@@ -724,7 +724,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
         dec.edge_table = table
         dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
         dout = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
-        rec, err, qual, ref_ms, ncomm = [], [], [], [], []
+        rec, err, qual, ref_ms, ncomm, phases = [], [], [], [], [], []
         for t in range(steps):
             dec.retrieve(Q[t])
             dec.attend(Q[t])
@@ -737,9 +737,11 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
                 if do_refresh and t + 1 < steps:
                     torch.cuda.synchronize()
                     t0 = time.perf_counter()
-                    qv = dec.refresh(table, gamma)
+                    tm = {}
+                    qv = dec.refresh(table, gamma, timings=tm)
                     torch.cuda.synchronize()
                     ref_ms.append(round((time.perf_counter() - t0) * 1e3, 1))
+                    phases.append({k: round(v, 1) for k, v in tm.items()})
                 else:
                     idx = dec.idx
                     lens = kv.seq_len.cpu().numpy()
@@ -760,6 +762,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
                      "initial_partition": {"modularity_mean": round(float(np.mean(q_init)), 4), "ms": round(init_ms, 1)}}
         if do_refresh:
             out[name]["refresh_ms"] = ref_ms
+            out[name]["refresh_phases_ms"] = phases
             out[name]["refresh_ms_per_step_amortised"] = round(float(np.mean(ref_ms)) / interval, 3) if ref_ms else None
         del layer, dec, kv, table
         torch.cuda.empty_cache()

@@ -517,20 +517,29 @@ class Decoder:
         # graph a refresh partitions); windowed steps do not record
         self.edge_table: Optional[EdgeTable] = None
 
-    def refresh(self, table: "EdgeTable", gamma=(1, 1), n_threads: int = 0, c_cap: Optional[int] = None):
+    def refresh(self, table: "EdgeTable", gamma=(1, 1), n_threads: int = 0, c_cap: Optional[int] = None,
+                timings: Optional[dict] = None):
         """Re-partition every graph's token graph (prompt and decoded rows of
         `table`) with ckv_leiden_partition and rebuild the index from the new
         labels with ckv_index_build ("Refresh" in Tables 8 and 9, against the
         incremental assignment of every step).  Replaces self.idx and the step
-        buffers; returns the partitions' modularity [G] (float64, host)."""
+        buffers; returns the partitions' modularity [G] (float64, host).
+        timings (a dict) receives the wall-clock ms of the three phases:
+        copy (edge rows to the host), partition (the library's Leiden) and
+        build (new index and ckv_index_build, synchronised)."""
+        import time
+
         import numpy as np
+        t0 = time.perf_counter()
         idx = self.idx
         if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap < idx.l_cap:
             raise ValueError("edge table does not match the index")
         lens = self.kv.seq_len.cpu().numpy()
         n_tok = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
         edges = table.e[:, :idx.l_cap].cpu().numpy()
+        t1 = time.perf_counter()
         labels, n_comm, quality = ckv_leiden_partition(n_tok, idx.n_sinks, edges, gamma, n_threads)
+        t2 = time.perf_counter()
         if int(n_comm.max(initial=0)) > CKV_MAX_C_CAP:
             raise ValueError(f"{int(n_comm.max())} communities exceed the index's limit {CKV_MAX_C_CAP}")
         new = CommunityIndex(self.kv, idx.mode, [max(1, int(c)) for c in n_comm], idx.l_cap, idx.tail_cap,
@@ -540,6 +549,10 @@ class Decoder:
         self.buf = DecodeBuffers(self.kv, new, self.budget, self.kappa, self.device)
         self.set_windows(self.windows)
         self.build(torch.from_numpy(labels).to(self.device))
+        if timings is not None:
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            timings.update(copy=(t1 - t0) * 1e3, partition=(t2 - t1) * 1e3, build=(t3 - t2) * 1e3)
         return quality
 
     def set_windows(self, windows: int):
