@@ -20,7 +20,8 @@
  *  - All pointers inside the descriptors and all array arguments are DEVICE
  *    pointers (memory the caller allocated on the GPU the stream belongs to),
  *    except the descriptors themselves, which are host structs read during
- *    the call only.
+ *    the call only, and the two host calls ckv_leiden_partition and
+ *    ckv_partition_quality, whose arrays are host memory.
  *  - The library allocates, frees and synchronises nothing.  Every call only
  *    validates its arguments on the host and enqueues kernels on `stream`
  *    (NULL = the null stream); it returns before the work runs.  Buffers must
