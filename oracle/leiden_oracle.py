@@ -321,3 +321,30 @@ def partition_tokens(edge_rows: np.ndarray, n_tokens: int, n_sinks: int, gnum: i
     out = np.full(n_tokens, -1, dtype=np.int64)
     out[n_sinks:] = lab
     return out, (max(lab) + 1 if lab else 0)
+
+
+# --------------------------------------------------------------------------
+# Tokens decoded while a partition was computed (Figure 4: the partitioning
+# runs beside the model; Figure 1 panel (3): a new token joins by its edges)
+# --------------------------------------------------------------------------
+
+def extend_by_vote(labels: np.ndarray, n_comm: int, edge_rows: np.ndarray, first: int, stop: int):
+    """Labels of tokens first .. stop - 1, in order, from the partition of the
+    tokens before them: each joins the community most of its edges' targets
+    are in (ties to the lower id), as a decode step assigns a new token; a
+    token none of whose edges has a community starts one of its own (as the
+    partition places a node without edges).  labels: [>= stop] int64, filled
+    below `first`; returns (labels, n_comm) with rows first .. stop - 1 set."""
+    out = np.array(labels, dtype=np.int64, copy=True)
+    for i in range(first, stop):
+        votes: Dict[int, int] = {}
+        for j in np.asarray(edge_rows[i]).tolist():
+            if j >= 0 and out[j] >= 0:
+                votes[int(out[j])] = votes.get(int(out[j]), 0) + 1
+        if votes:
+            best = max(votes.values())
+            out[i] = min(c for c, v in votes.items() if v == best)
+        else:
+            out[i] = n_comm
+            n_comm += 1
+    return out, n_comm

@@ -24,7 +24,8 @@ def _pins():
               P.test_aggregate_hand_example, P.test_guarantees_on_random_graphs,
               P.test_guarantees_on_token_graphs, P.test_no_edges_and_degenerate_graphs,
               P.test_move_nodes_hand_trace, P.test_move_nodes_to_an_empty_community,
-              P.test_quality_with_self_loops_against_definition, P.test_refine_skips_a_node_not_well_connected]
+              P.test_quality_with_self_loops_against_definition, P.test_refine_skips_a_node_not_well_connected,
+              P.test_extend_by_vote_hand_example, P.test_extend_by_vote_matches_partition_of_isolated_growth]
     checks += [lambda a=a: P.test_quality_closed_form_ring_of_cliques(*a) for a in ((30, 5), (8, 4), (3, 6))]
     checks += [lambda nm=nm: P.test_brute_force_optimum(nm) for nm in sorted(P.STRUCTURED)]
     return checks
@@ -52,6 +53,11 @@ MUTANTS = [
     ("leiden", "empty = list(range(n_comm, len(adj)))", "empty = []"),                  # no free ids past level 0
     ("leiden", "if len(set(ref)) == len(adj):", "if True:"),                            # stops after level 0
     ("first_token_order", "seen[c] = len(seen)", "seen[c] = -len(seen) - 1"),
+    ("extend_by_vote", "out[i] = min(c for c, v in votes.items() if v == best)",
+     "out[i] = max(c for c, v in votes.items() if v == best)"),                     # ties to the higher id
+    ("extend_by_vote", "if j >= 0 and out[j] >= 0:", "if j >= 0:"),                # unlabelled targets vote
+    ("extend_by_vote", "out[i] = n_comm\n", "out[i] = 0\n"),                        # no new community
+
 ]
 
 

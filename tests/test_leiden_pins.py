@@ -382,3 +382,41 @@ def test_no_edges_and_degenerate_graphs():
     assert L.leiden(adj) == [0, 1, 1, 2]
     lab, nc = L.partition_tokens(np.full((4, 2), -1), 4, 4)
     assert lab.tolist() == [-1] * 4 and nc == 0
+
+
+# -- tokens decoded during a partition: joined by the vote of their edges ---------------
+
+def test_extend_by_vote_hand_example():
+    # tokens 0-1 sinks, 2-5 partitioned as [0, -, 1, 1] (token 3 in no
+    # community, as a full tail leaves a token); then
+    #  6 -> 2, 4, 5: communities 0, 1, 1 -> 1
+    #  7 -> 2, 4: one vote each -> 0 (lower id)
+    #  8 -> 6, 7, 3: communities 1, 0 and none: one vote each -> 0
+    #  9 -> no edges -> a new community 2; 10 -> 9, 9 -> 2
+    rows = np.full((11, 3), -1)
+    rows[6] = [2, 4, 5]
+    rows[7, :2] = [2, 4]
+    rows[8] = [6, 7, 3]
+    rows[10, :2] = [9, 9]
+    lab = np.array([-1, -1, 0, -1, 1, 1] + [-1] * 5)
+    out, nc = L.extend_by_vote(lab, 2, rows, 6, 11)
+    assert out.tolist() == [-1, -1, 0, -1, 1, 1, 1, 0, 0, 2, 2] and nc == 3
+    assert lab[6] == -1  # the input is not changed
+
+
+def test_extend_by_vote_matches_partition_of_isolated_growth():
+    # a new token whose edges all point into one community joins it, so
+    # extending a partition by tokens linked to one clique each keeps the
+    # cliques (checked against the Leiden result of the whole graph)
+    rows = np.full((40, 4), -1)
+    for c in range(4):                      # four 8-cliques over tokens 4..35
+        mem = [4 + c + 4 * i for i in range(8)]
+        for a in range(1, 8):
+            rows[mem[a], :min(a, 4)] = mem[max(0, a - 4):a][::-1][:4]
+    for t in range(36, 40):                 # four late tokens, one per clique
+        rows[t, :3] = [4 + (t - 36) + 4 * i for i in (0, 3, 5)]
+    full, nc_full = L.partition_tokens(rows, 40, 4)
+    part, nc = L.partition_tokens(rows[:36], 36, 4)
+    lab = np.concatenate([part, np.full(4, -1)])
+    ext, nc2 = L.extend_by_vote(lab, nc, rows, 36, 40)
+    assert nc2 == nc and np.array_equal(ext, full)
