@@ -706,7 +706,8 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
            "gamma": gamma[0] / gamma[1], "drift_topics_per_kv_head": w.drift_topics, "drift_rate": w.drift_rate,
            "quality": "synthetic stand-in for the page's NLL/KL/top-1 (no model): recall and output error "
                       "against dense attention"}
-    for name, do_refresh in (("incremental", False), ("refresh", True)):
+    for name in ("incremental", "refresh", "refresh_async"):
+        do_refresh = name != "incremental"
         layer = runner.load_layer(w, args.seed, extra=steps + 1, slices=slices)
         dec, kv = layer.dec, layer.kv
         dec.defer = False
@@ -725,6 +726,16 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
         dml = torch.empty((w.batch, w.n_q_heads, 2), dtype=torch.float32, device="cuda")
         dout = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
         rec, err, qual, ref_ms, ncomm, phases = [], [], [], [], [], []
+        pend, pend_t, lags = None, 0, []
+        threads = max(1, (os.cpu_count() or 4) - 2)   # leave cores to the thread launching steps
+
+        def apply_pending(t):
+            tm = {}
+            dec.refresh_apply(pend, table, timings=tm)
+            ref_ms.append(round(tm["snapshot"] + tm["wait"] + tm["place"] + tm["build"], 1))
+            phases.append({k: round(v, 1) for k, v in tm.items()})
+            lags.append(t - pend_t)
+
         for t in range(steps):
             dec.retrieve(Q[t])
             dec.attend(Q[t])
@@ -733,8 +744,22 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
             d = torch.linalg.vector_norm(dec.buf.out - dout, dim=-1) / torch.linalg.vector_norm(dout, dim=-1)
             err.append(d.flatten())
             dec.update(KN[t], VN[t])
+            if pend is not None and pend.done():
+                apply_pending(t + 1)
+                pend = None
             if (t + 1) % interval == 0:
-                if do_refresh and t + 1 < steps:
+                if name == "refresh_async":
+                    if pend is not None:
+                        apply_pending(t + 1)
+                        pend = None
+                    if t + 1 < steps:
+                        pend, pend_t = dec.refresh_async(table, gamma, n_threads=threads), t + 1
+                    idx = dec.idx
+                    lens = kv.seq_len.cpu().numpy()
+                    n_tok = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
+                    qv = ckv.ckv_partition_quality(n_tok, idx.n_sinks, table.e[:, :idx.l_cap].cpu().numpy(),
+                                                   np.ascontiguousarray(idx.label.cpu().numpy()), gamma)
+                elif do_refresh and t + 1 < steps:
                     torch.cuda.synchronize()
                     t0 = time.perf_counter()
                     tm = {}
@@ -764,6 +789,11 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
             out[name]["refresh_ms"] = ref_ms
             out[name]["refresh_phases_ms"] = phases
             out[name]["refresh_ms_per_step_amortised"] = round(float(np.mean(ref_ms)) / interval, 3) if ref_ms else None
+        if name == "refresh_async":
+            out[name]["how"] = ("partition of a snapshot on host threads while steps go on; applied at the first "
+                                "step after it is ready, the tokens decoded meanwhile placed by the vote of their "
+                                "edges; refresh_ms is the time the step loop spent on it (snapshot, wait, place, build)")
+            out[name]["applied_after_steps"] = lags
         del layer, dec, kv, table
         torch.cuda.empty_cache()
     return out

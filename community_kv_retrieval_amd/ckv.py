@@ -34,7 +34,7 @@ EXPORTS = ("ckv_workspace_bytes", "ckv_kv_write", "ckv_index_build", "ckv_score_
            "ckv_select_communities", "ckv_gather_attend", "ckv_gather_attend_noalloc", "ckv_assign_update",
            "ckv_dense_attend",
            "ckv_attention_recall", "ckv_prefill_workspace_bytes", "ckv_prefill_topk", "ckv_read_rows",
-           "ckv_leiden_partition", "ckv_partition_quality",
+           "ckv_leiden_partition", "ckv_partition_quality", "ckv_extend_partition",
            "ckv_time_next_launch", "ckv_status_str", "ckv_abi_version")
 
 
@@ -91,6 +91,8 @@ def _load():
                                            ctypes.c_int64, ctypes.c_int64, c_int32, c_void_p, c_void_p, c_void_p]),
         "ckv_partition_quality": (c_int32, [c_int32, c_void_p, c_int32, c_void_p, ctypes.c_int64, c_int32,
                                             ctypes.c_int64, ctypes.c_int64, c_int32, c_void_p, c_void_p]),
+        "ckv_extend_partition": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, ctypes.c_int64, c_int32,
+                                           c_void_p, c_void_p]),
         "ckv_time_next_launch": (c_int32, [c_void_p, c_void_p]),
         "ckv_status_str": (ctypes.c_char_p, [c_int32]),
         "ckv_abi_version": (c_int32, []),
@@ -426,6 +428,23 @@ def ckv_partition_quality(n_tokens, n_sinks: int, edges, labels, gamma=(1, 1), n
     return quality
 
 
+def ckv_extend_partition(first, n_tokens, edges, labels, n_comm):
+    """Tokens first[g] .. n_tokens[g]-1 join the partition by the vote of
+    their edges (host call; labels [G][row_stride] and n_comm [G] int32 are
+    updated in place)."""
+    import numpy as np
+    G, stride, kappa = edges.shape if edges.ndim == 3 else (0, 0, 0)
+    _host_i32(edges, "edges", (G, stride, kappa))
+    _host_i32(first, "first", (G,))
+    _host_i32(n_tokens, "n_tokens", (G,))
+    _host_i32(labels, "labels", (G, stride))
+    _host_i32(n_comm, "n_comm", (G,))
+    _check("ckv_extend_partition", LIB.ckv_extend_partition(
+        G, first.ctypes.data, n_tokens.ctypes.data, edges.ctypes.data, stride, kappa, labels.ctypes.data,
+        n_comm.ctypes.data))
+    return labels, n_comm
+
+
 def ckv_time_next_launch(start: Optional["torch.cuda.Event"], stop: Optional["torch.cuda.Event"]):
     """Arms the next step kernel of this thread to stamp `start`/`stop` from its own dispatch.
 
@@ -490,6 +509,20 @@ class EdgeTable:
         self.e[torch.arange(self.n_graphs, device=self.e.device), rows] = edges
 
 
+class PendingRefresh:
+    """A partition being computed on host threads (Decoder.refresh_async)."""
+
+    def __init__(self, n_tok, rows: int, gamma):
+        self.n_tok, self.rows, self.gamma = n_tok, rows, gamma
+        self.thread = None
+        self.result = None
+        self.error: Optional[BaseException] = None
+        self.snapshot_ms = 0.0
+
+    def done(self) -> bool:
+        return self.thread is not None and not self.thread.is_alive()
+
+
 class Decoder:
     """Runs CommunityKV decode steps for one layer.
 
@@ -517,6 +550,101 @@ class Decoder:
         # graph a refresh partitions); windowed steps do not record
         self.edge_table: Optional[EdgeTable] = None
 
+    def refresh_async(self, table: "EdgeTable", gamma=(1, 1), n_threads: int = 0) -> PendingRefresh:
+        """Start a refresh beside the decode steps (Figure 4 runs the
+        partitioning beside the model): the edge rows of the tokens cached now
+        are copied to pinned host memory on a stream of their own and a host
+        thread partitions them with ckv_leiden_partition, while steps go on.
+        refresh_apply() then places the tokens decoded meanwhile by the vote
+        of their edges (ckv_extend_partition) and rebuilds the index."""
+        import threading
+        import time
+
+        import numpy as np
+        t0 = time.perf_counter()
+        idx = self.idx
+        if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap < idx.l_cap:
+            raise ValueError("edge table does not match the index")
+        lens = self.kv.seq_len.cpu().numpy()
+        n_tok = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
+        rows = int(n_tok.max(initial=0))
+        host = torch.empty((idx.n_graphs, rows, table.kappa), dtype=torch.int32, pin_memory=True)
+        ready = torch.cuda.Event()
+        ready.record()
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            side.wait_event(ready)
+            host.copy_(table.e[:, :rows], non_blocking=True)
+            copied = torch.cuda.Event()
+            copied.record(side)
+        pend = PendingRefresh(n_tok, rows, gamma)
+
+        def work():
+            try:
+                copied.synchronize()
+                pend.result = ckv_leiden_partition(n_tok, idx.n_sinks, host.numpy(), gamma, n_threads)
+            except BaseException as e:  # handed to refresh_apply
+                pend.error = e
+
+        pend.thread = threading.Thread(target=work, name="ckv-leiden", daemon=True)
+        pend.thread.start()
+        pend.snapshot_ms = (time.perf_counter() - t0) * 1e3
+        return pend
+
+    def refresh_apply(self, pend: PendingRefresh, table: "EdgeTable", c_cap: Optional[int] = None,
+                      timings: Optional[dict] = None):
+        """Finish a refresh_async: wait for the partition, let every token
+        decoded since the snapshot join it by the vote of its edges, and
+        rebuild the index from the result (replaces self.idx and the step
+        buffers).  Returns the modularity [G] of the snapshot's partition.
+        timings receives the ms spent waiting, placing the new tokens and
+        building."""
+        import time
+
+        import numpy as np
+        t0 = time.perf_counter()
+        pend.thread.join()
+        t1 = time.perf_counter()
+        if pend.error is not None:
+            raise pend.error
+        labels0, n_comm, quality = pend.result
+        idx = self.idx
+        lens = self.kv.seq_len.cpu().numpy()
+        n_now = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
+        rows = int(n_now.max(initial=0))
+        lo = int(pend.n_tok.min(initial=0))
+        G = idx.n_graphs
+        edges = np.empty((G, rows, table.kappa), dtype=np.int32)   # rows below lo are not read
+        edges[:, lo:rows] = table.e[:, lo:rows].cpu().numpy()
+        labels = np.full((G, idx.l_cap), -1, dtype=np.int32)
+        labels[:, :pend.rows] = labels0
+        lab = np.ascontiguousarray(labels[:, :rows])
+        n_comm = np.ascontiguousarray(n_comm, dtype=np.int32)
+        ckv_extend_partition(pend.n_tok, n_now, edges, lab, n_comm)
+        labels[:, :rows] = lab
+        t2 = time.perf_counter()
+        self._rebuild(labels, n_comm, c_cap)
+        if timings is not None:
+            torch.cuda.synchronize()
+            t3 = time.perf_counter()
+            timings.update(wait=(t1 - t0) * 1e3, place=(t2 - t1) * 1e3, build=(t3 - t2) * 1e3,
+                           snapshot=pend.snapshot_ms)
+        return quality
+
+    def _rebuild(self, labels, n_comm, c_cap: Optional[int]):
+        """New index with n_comm communities per graph, built from labels
+        [G][l_cap] (host int32) by ckv_index_build."""
+        idx = self.idx
+        if int(n_comm.max(initial=0)) > CKV_MAX_C_CAP:
+            raise ValueError(f"{int(n_comm.max())} communities exceed the index's limit {CKV_MAX_C_CAP}")
+        new = CommunityIndex(self.kv, idx.mode, [max(1, int(c)) for c in n_comm], idx.l_cap, idx.tail_cap,
+                             idx.n_sinks, c_cap=c_cap, device=self.device, cent_budget=idx.cent_budget)
+        new.n_comm.copy_(torch.from_numpy(n_comm))
+        self.idx = new
+        self.buf = DecodeBuffers(self.kv, new, self.budget, self.kappa, self.device)
+        self.set_windows(self.windows)
+        self.build(torch.from_numpy(labels).to(self.device))
+
     def refresh(self, table: "EdgeTable", gamma=(1, 1), n_threads: int = 0, c_cap: Optional[int] = None,
                 timings: Optional[dict] = None):
         """Re-partition every graph's token graph (prompt and decoded rows of
@@ -540,15 +668,7 @@ class Decoder:
         t1 = time.perf_counter()
         labels, n_comm, quality = ckv_leiden_partition(n_tok, idx.n_sinks, edges, gamma, n_threads)
         t2 = time.perf_counter()
-        if int(n_comm.max(initial=0)) > CKV_MAX_C_CAP:
-            raise ValueError(f"{int(n_comm.max())} communities exceed the index's limit {CKV_MAX_C_CAP}")
-        new = CommunityIndex(self.kv, idx.mode, [max(1, int(c)) for c in n_comm], idx.l_cap, idx.tail_cap,
-                             idx.n_sinks, c_cap=c_cap, device=self.device, cent_budget=idx.cent_budget)
-        new.n_comm.copy_(torch.from_numpy(n_comm))
-        self.idx = new
-        self.buf = DecodeBuffers(self.kv, new, self.budget, self.kappa, self.device)
-        self.set_windows(self.windows)
-        self.build(torch.from_numpy(labels).to(self.device))
+        self._rebuild(labels, n_comm, c_cap)
         if timings is not None:
             torch.cuda.synchronize()
             t3 = time.perf_counter()

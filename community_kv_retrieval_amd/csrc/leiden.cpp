@@ -486,3 +486,56 @@ extern "C" ckv_status ckv_partition_quality(int32_t n_graphs, const int32_t *n_t
         if (s != CKV_OK) return s;
     return CKV_OK;
 }
+
+// Tokens first[g] .. n_tokens[g]-1, in order, join the partition of the tokens
+// before them by the vote of their edges (the most common community among the
+// labelled targets, ties to the lower id); a token with no labelled target
+// starts a community of its own.  Figure 4 runs the partitioning beside the
+// model, so the tokens decoded meanwhile are placed by the rule of Figure 1
+// panel (3).
+extern "C" ckv_status ckv_extend_partition(int32_t n_graphs, const int32_t *first, const int32_t *n_tokens,
+                                           const int32_t *edges, int64_t row_stride, int32_t kappa,
+                                           int32_t *labels, int32_t *n_comm) {
+    if (n_graphs < 0 || kappa < 1 || kappa > CKV_MAX_KAPPA) return CKV_E_INVALID;
+    if (n_graphs > 0 && (!first || !n_tokens || !edges || !labels || !n_comm)) return CKV_E_INVALID;
+    for (int32_t g = 0; g < n_graphs; ++g)
+        if (first[g] < 0 || first[g] > n_tokens[g] || n_tokens[g] > row_stride || n_comm[g] < 0) return CKV_E_INVALID;
+    for (int32_t g = 0; g < n_graphs; ++g) {
+        const int32_t *rows = edges + size_t(g) * size_t(row_stride) * size_t(kappa);
+        for (int32_t i = first[g]; i < n_tokens[g]; ++i)
+            for (int32_t e = 0; e < kappa; ++e) {
+                const int32_t j = rows[size_t(i) * kappa + e];
+                if (j >= i) return CKV_E_INVALID;  // edges point to earlier tokens
+            }
+    }
+    for (int32_t g = 0; g < n_graphs; ++g) {
+        const int32_t *rows = edges + size_t(g) * size_t(row_stride) * size_t(kappa);
+        int32_t *lab = labels + size_t(g) * size_t(row_stride);
+        int32_t c_n = n_comm[g];
+        int32_t cand[CKV_MAX_KAPPA], cnt[CKV_MAX_KAPPA];
+        for (int32_t i = first[g]; i < n_tokens[g]; ++i) {
+            int32_t m = 0;
+            for (int32_t e = 0; e < kappa; ++e) {
+                const int32_t j = rows[size_t(i) * kappa + e];
+                if (j < 0 || lab[j] < 0) continue;
+                int32_t k = 0;
+                while (k < m && cand[k] != lab[j]) ++k;
+                if (k == m) {
+                    cand[m] = lab[j];
+                    cnt[m++] = 0;
+                }
+                cnt[k]++;
+            }
+            if (m == 0) {
+                lab[i] = c_n++;
+                continue;
+            }
+            int32_t best = 0;
+            for (int32_t k = 1; k < m; ++k)
+                if (cnt[k] > cnt[best] || (cnt[k] == cnt[best] && cand[k] < cand[best])) best = k;
+            lab[i] = cand[best];
+        }
+        n_comm[g] = c_n;
+    }
+    return CKV_OK;
+}

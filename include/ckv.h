@@ -384,6 +384,21 @@ ckv_status ckv_leiden_partition(int32_t n_graphs, const int32_t *n_tokens, int32
                                 int64_t row_stride, int32_t kappa, int64_t gamma_num, int64_t gamma_den,
                                 int32_t n_threads, int32_t *labels, int32_t *n_comm, double *quality);
 
+/* Tokens decoded while a partition was computed join it (HOST call, host
+ * pointers; Figure 4 runs the partitioning beside the model, Figure 1 panel
+ * (3) places a new token by its edges).  For every graph g, tokens
+ * first[g] .. n_tokens[g]-1 of labels[g][row_stride] are set in increasing
+ * order: each joins the community most of its edges' targets (rows of
+ * edges[g][row_stride][kappa], as for ckv_leiden_partition) are in, ties to
+ * the lower id, targets without a community (-1) not voting; a token with no
+ * such target starts community n_comm[g], which then grows by one.  labels
+ * below first[g] are read, not written; n_comm[g] is read and updated.
+ * Errors (CKV_E_INVALID, nothing written): n_graphs < 0, NULL arrays, kappa
+ * outside 1..32, first[g] outside 0..n_tokens[g], n_tokens[g] > row_stride,
+ * n_comm[g] < 0, or an edge of a token to itself or a later token. */
+ckv_status ckv_extend_partition(int32_t n_graphs, const int32_t *first, const int32_t *n_tokens, const int32_t *edges,
+                                int64_t row_stride, int32_t kappa, int32_t *labels, int32_t *n_comm);
+
 /* Modularity Q (Figure 3, left) of given labels on the same token graphs as
  * ckv_leiden_partition (HOST call, host pointers, same edge rules): labels of
  * tokens n_sinks .. n_tokens[g]-1 must lie in 0 .. n_tokens[g]-n_sinks-1 (any

@@ -116,3 +116,56 @@ def test_refresh_cycle_matches_oracle(mode):
     st2 = PY.run_steps(w, seed, steps_b, pair=(layer, orc), first_step=steps_a, edge_log=log)
     assert st.steps == steps_a and st2.steps == steps_b
     PY.log(f"  {steps_a + steps_b} steps checked around the refresh (max abs {max(st.max_abs, st2.max_abs):.2e})")
+
+
+@pytest.mark.parametrize("mode", ["per_head", "group"])
+def test_async_refresh_matches_oracle(mode):
+    """refresh_async after 16 steps, 12 more steps while the host partitions
+    the snapshot, then refresh_apply: the tokens decoded meanwhile join the new
+    partition by the vote of their edges, on both sides; 12 checked steps on
+    the result."""
+    w = _workload(mode)
+    seed = 9
+    PY.log(f"async refresh, {mode}: seed {seed}, {w.n_ctx} tokens, {w.n_graphs} graphs")
+    layer, orc = PY.make_pair(w, seed, 41)
+    dec = layer.dec
+    table = ckv.EdgeTable(layer.kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
+    dec.edge_table = table
+    orc_rows = {}
+    edges, near = _prefill(layer, w, seed, orc_rows)
+    table.put_prefill(0, edges)
+    _refresh_both(layer, orc, w, orc_rows, "initial partition")
+    log = {}
+    PY.run_steps(w, seed, 16, pair=(layer, orc), edge_log=log)
+    n0 = {g: orc.len[orc.g[g].b] for g in orc.graph_ids}
+    for (t, g), e in log.items():
+        orc_rows[g][n0[g] - 16 + t] = e
+    pend = dec.refresh_async(table, n_threads=2)
+    snap = {g: _oracle_partition(orc, w, orc_rows, g) for g in orc.graph_ids}   # (labels, n_comm, Q, rows)
+    log.clear()
+    PY.run_steps(w, seed, 12, pair=(layer, orc), first_step=16, edge_log=log)
+    for (t, g), e in log.items():
+        orc_rows[g][n0[g] + t - 16] = e
+    tm = {}
+    quality = dec.refresh_apply(pend, table, timings=tm)
+    layer.idx = dec.idx
+    torch.cuda.synchronize()
+    label = dec.idx.label.cpu().numpy()
+    n_comm = dec.idx.n_comm.cpu().numpy()
+    for g in orc.graph_ids:
+        lab0, nc0, q0, _ = snap[g]
+        n1 = orc.len[orc.g[g].b]
+        rows = np.full((n1, w.kappa), -1, dtype=np.int64)
+        for i, r in orc_rows[g].items():
+            rows[i, :r.size] = r
+        lab = np.concatenate([lab0, np.full(n1 - lab0.size, -1, dtype=np.int64)])
+        lab, nc = LO.extend_by_vote(lab, nc0, rows, lab0.size, n1)
+        np.testing.assert_array_equal(label[g, :n1], lab, err_msg=f"async labels g={g}")
+        assert n_comm[g] == nc and quality[g] == pytest.approx(q0, abs=1e-12)
+        orc.repartition(g, lab, nc)
+    PY.check_csr(layer, orc)
+    PY.check_index_state(layer, orc, w, full=True)
+    st = PY.run_steps(w, seed, 12, pair=(layer, orc), first_step=28)
+    assert st.steps == 12
+    PY.log(f"  async refresh applied 12 steps after its snapshot ({tm['wait']:.1f} ms waited, "
+           f"{tm['place']:.1f} ms placing, {tm['build']:.1f} ms building); 40 steps checked")

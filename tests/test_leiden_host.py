@@ -124,3 +124,36 @@ def test_host_leiden_rejects_bad_input(bad):
     with pytest.raises(ckv.CkvError) as ei:
         ckv.ckv_leiden_partition(n_tok, 4, e, gamma)
     assert ei.value.code == ckv.CKV_E_INVALID
+
+
+def test_host_extend_partition_matches_oracle():
+    rng = np.random.default_rng(31)
+    tables, firsts, ref = [], [], []
+    for g in range(3):
+        n = 700 + 50 * g
+        t = prefill_like_rows(rng, n, 4, 8, 30)
+        first = 500 + 20 * g
+        lab, nc = L.partition_tokens(t[:first], first, 4)
+        lab = np.concatenate([lab, np.full(n - first, -1)])
+        if g == 1:
+            lab[10] = -1            # a token without a community: its edges do not vote
+        if g == 2:
+            t[first + 3] = -1       # a token without edges starts a community
+        want, nc2 = L.extend_by_vote(lab, nc, t, first, n)
+        tables.append(t)
+        firsts.append(first)
+        ref.append((lab, nc, want, nc2))
+    n_tok, edges = _pack(tables, 900)
+    labels = np.full((3, 900), -1, dtype=np.int32)
+    n_comm = np.zeros(3, dtype=np.int32)
+    for g, (lab, nc, _, _) in enumerate(ref):
+        labels[g, :lab.size] = lab
+        n_comm[g] = nc
+    ckv.ckv_extend_partition(np.array(firsts, dtype=np.int32), n_tok, edges, labels, n_comm)
+    for g, (_, _, want, nc2) in enumerate(ref):
+        assert np.array_equal(labels[g, :want.size], want.astype(np.int32))
+        assert n_comm[g] == nc2
+    bad = edges.copy()
+    bad[0, 600, 0] = 650           # an edge to a later token
+    with pytest.raises(ckv.CkvError):
+        ckv.ckv_extend_partition(np.array(firsts, dtype=np.int32), n_tok, bad, labels.copy(), n_comm.copy())
