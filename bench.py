@@ -732,7 +732,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
         def apply_pending(t):
             tm = {}
             dec.refresh_apply(pend, table, timings=tm)
-            ref_ms.append(round(tm["snapshot"] + tm["wait"] + tm["place"] + tm["build"], 1))
+            ref_ms.append(round(tm["snapshot"] + tm["wait"] + tm["place"] + tm["build"], 1))  # not the drain
             phases.append({k: round(v, 1) for k, v in tm.items()})
             lags.append(t - pend_t)
 
@@ -744,7 +744,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
             d = torch.linalg.vector_norm(dec.buf.out - dout, dim=-1) / torch.linalg.vector_norm(dout, dim=-1)
             err.append(d.flatten())
             dec.update(KN[t], VN[t])
-            if pend is not None and pend.done():
+            if pend is not None and (pend.done() or t + 1 - pend_t >= interval // 2):
                 apply_pending(t + 1)
                 pend = None
             if (t + 1) % interval == 0:
@@ -791,8 +791,10 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
             out[name]["refresh_ms_per_step_amortised"] = round(float(np.mean(ref_ms)) / interval, 3) if ref_ms else None
         if name == "refresh_async":
             out[name]["how"] = ("partition of a snapshot on host threads while steps go on; applied at the first "
-                                "step after it is ready, the tokens decoded meanwhile placed by the vote of their "
-                                "edges; refresh_ms is the time the step loop spent on it (snapshot, wait, place, build)")
+                                "step after it is ready, at most interval/2 steps after the snapshot (then waiting "
+                                "for it), the tokens decoded meanwhile placed by the vote of their edges; refresh_ms "
+                                "is the time the step loop spent on it (snapshot, wait, place, build; not the drain "
+                                "of the steps already queued on the GPU)")
             out[name]["applied_after_steps"] = lags
         del layer, dec, kv, table
         torch.cuda.empty_cache()

@@ -496,6 +496,12 @@ class EdgeTable:
         # sequence of every graph, to find the row a step's new token takes
         self.graph_seq = torch.arange(self.n_graphs, device=device) // per
 
+    def pinned(self) -> torch.Tensor:
+        """A pinned host buffer shaped like the table (allocated once)."""
+        if getattr(self, "_pinned", None) is None:
+            self._pinned = torch.empty((self.n_graphs, self.cap, self.kappa), dtype=torch.int32, pin_memory=True)
+        return self._pinned
+
     def put_prefill(self, b: int, edges: torch.Tensor):
         """Rows 0..n-1 of sequence b's graphs from ckv_prefill_topk's edges
         [graphs of the sequence][n][kappa]."""
@@ -561,20 +567,21 @@ class Decoder:
         import time
 
         import numpy as np
-        t0 = time.perf_counter()
         idx = self.idx
-        if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap < idx.l_cap:
+        if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap != idx.l_cap:
             raise ValueError("edge table does not match the index")
+        torch.cuda.current_stream().synchronize()   # the steps queued so far
+        t0 = time.perf_counter()
         lens = self.kv.seq_len.cpu().numpy()
         n_tok = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
         rows = int(n_tok.max(initial=0))
-        host = torch.empty((idx.n_graphs, rows, table.kappa), dtype=torch.int32, pin_memory=True)
+        host = table.pinned()          # rows >= n_tok[g] are not read
         ready = torch.cuda.Event()
         ready.record()
         side = torch.cuda.Stream()
         with torch.cuda.stream(side):
             side.wait_event(ready)
-            host.copy_(table.e[:, :rows], non_blocking=True)
+            host.copy_(table.e, non_blocking=True)   # contiguous both sides: one DMA, no staging
             copied = torch.cuda.Event()
             copied.record(side)
         pend = PendingRefresh(n_tok, rows, gamma)
@@ -609,26 +616,22 @@ class Decoder:
             raise pend.error
         labels0, n_comm, quality = pend.result
         idx = self.idx
+        torch.cuda.current_stream().synchronize()   # the steps queued so far (their edge rows)
+        t_drain = time.perf_counter()
         lens = self.kv.seq_len.cpu().numpy()
         n_now = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
         rows = int(n_now.max(initial=0))
         lo = int(pend.n_tok.min(initial=0))
-        G = idx.n_graphs
-        edges = np.empty((G, rows, table.kappa), dtype=np.int32)   # rows below lo are not read
-        edges[:, lo:rows] = table.e[:, lo:rows].cpu().numpy()
-        labels = np.full((G, idx.l_cap), -1, dtype=np.int32)
-        labels[:, :pend.rows] = labels0
-        lab = np.ascontiguousarray(labels[:, :rows])
-        n_comm = np.ascontiguousarray(n_comm, dtype=np.int32)
-        ckv_extend_partition(pend.n_tok, n_now, edges, lab, n_comm)
-        labels[:, :rows] = lab
+        host = table.pinned().numpy()   # rows below the snapshot's lengths hold the snapshot already
+        host[:, lo:rows] = table.e[:, lo:rows].contiguous().cpu().numpy()
+        ckv_extend_partition(pend.n_tok, n_now, host, labels0, n_comm)   # labels0: [G][cap]
         t2 = time.perf_counter()
-        self._rebuild(labels, n_comm, c_cap)
+        self._rebuild(labels0, n_comm, c_cap)
         if timings is not None:
             torch.cuda.synchronize()
             t3 = time.perf_counter()
-            timings.update(wait=(t1 - t0) * 1e3, place=(t2 - t1) * 1e3, build=(t3 - t2) * 1e3,
-                           snapshot=pend.snapshot_ms)
+            timings.update(wait=(t1 - t0) * 1e3, drain=(t_drain - t1) * 1e3, place=(t2 - t_drain) * 1e3,
+                           build=(t3 - t2) * 1e3, snapshot=pend.snapshot_ms)
         return quality
 
     def _rebuild(self, labels, n_comm, c_cap: Optional[int]):
@@ -660,11 +663,11 @@ class Decoder:
         import numpy as np
         t0 = time.perf_counter()
         idx = self.idx
-        if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap < idx.l_cap:
+        if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap != idx.l_cap:
             raise ValueError("edge table does not match the index")
         lens = self.kv.seq_len.cpu().numpy()
         n_tok = lens[table.graph_seq.cpu().numpy()].astype(np.int32)
-        edges = table.e[:, :idx.l_cap].cpu().numpy()
+        edges = table.e.cpu().numpy()
         t1 = time.perf_counter()
         labels, n_comm, quality = ckv_leiden_partition(n_tok, idx.n_sinks, edges, gamma, n_threads)
         t2 = time.perf_counter()
