@@ -65,6 +65,8 @@ def main():
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill graph construction of the workload's first sequence (profiling)")
     ap.add_argument("--eager-only", action="store_true", help="with --profile: no HIP graph (counter runs)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="with --profile: only eager steps, each after the MALL flush (cold kernel averages)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB copy kernel 5 times (scale for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -126,7 +128,8 @@ def main():
         torch.cuda.synchronize()
 
     if args.profile:
-        passes = time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=True, eager_only=args.eager_only)
+        passes = time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=True, eager_only=args.eager_only,
+                            cold_only=args.cold_only)
         return
     L = time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore)
     gathered, score_bytes, row_bytes = L["gathered"], L["score_bytes"], L["row_bytes"]
@@ -274,7 +277,7 @@ def main():
 STEP_KERNELS = ["score_centroids", "select_communities", "gather_attend", "assign_update"]
 
 
-def time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=False, eager_only=False):
+def time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=False, eager_only=False, cold_only=False):
     """Every timing pass of one layer over steps W .. W + K - 1 (after W
     untimed warm-up steps, from the same restored state each time):
     accounting (tokens gathered per step), eager, the K steps captured as one
@@ -288,6 +291,18 @@ def time_layer(w, dec, kv, idx, Q, KN, VN, W, K, restore, profile=False, eager_o
     from community_kv_retrieval_amd import ckv
     total = W + K
     buf = dec.buf
+    if profile and cold_only:
+        # For a profiler: every launch of every step kernel follows the 512 MB
+        # read that evicts the MALL (as in the cold passes), so a kernel's
+        # average over all its dispatches is its cold time.
+        flush = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+        restore()
+        for t in range(total):
+            flush.amax()
+            dec.step(Q[t], KN[t], VN[t])
+        torch.cuda.synchronize()
+        log(f"[bench] cold profile run: {total} steps, each after a MALL flush")
+        return None
     restore()
     tok = []
     for t in range(total):
