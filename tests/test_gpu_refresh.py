@@ -29,33 +29,41 @@ def _workload(mode):
         mode=synth.PER_HEAD if mode == "per_head" else synth.GROUP)
 
 
-def _prefill(layer, w, seed, orc_rows):
-    """Device prefill graph of sequence 0, each row checked against the
-    oracle's; the oracle keeps its own rows except where it adopts a near tie."""
+def _prefill(layer, w, seed, orc_rows, table=None):
+    """Device prefill graph of every sequence, each row checked against the
+    oracle's; the oracle keeps its own rows except where it adopts a near tie.
+    With a table, the device rows go into it.  Returns (edges of sequence 0,
+    near ties adopted)."""
     mode = ckv.CKV_MODE_PER_HEAD if w.mode == synth.PER_HEAD else ckv.CKV_MODE_QUERY_GROUP
-    qp = synth.gen_prefill_queries(w, seed, 0, 0, layer.slices[0])
-    n = qp.shape[0]
-    graphs = w.n_q_heads if mode == ckv.CKV_MODE_PER_HEAD else w.n_kv_heads
-    edges = torch.empty((graphs, n, w.kappa), dtype=torch.int32, device="cuda")
-    ws = ckv.prefill_workspace(layer.kv, mode, n)
-    ckv.ckv_prefill_topk(layer.kv, mode, 0, qp.cuda(), w.n_sinks, w.kappa, w.sm_scale, edges, None, ws)
-    torch.cuda.synchronize()
-    got = edges.cpu().numpy()
-    qf = qp.float().numpy().astype(np.float64)
-    near = 0
-    for g in range(graphs):
-        _, kh, qh0, nh = w.graph_coords(g)
-        keys = layer.slices[0][kh].k.float().numpy().astype(np.float64)
-        ref, _ = O.prefill_edges(qf[:, qh0:qh0 + nh], keys, w.n_sinks, w.kappa, w.sm_scale)
-        for i in range(n):
-            if np.array_equal(ref[i], got[g, i]):
-                continue
-            W = O.prefill_row_weights(qf[i, qh0:qh0 + nh], i, keys, w.sm_scale)
-            assert not D.prefill_row_ok(W, i, w.n_sinks, w.kappa, ref[i], got[g, i], None, f"prefill g={g}")
-            ref[i] = got[g, i]
-            near += 1
-        orc_rows[g] = {i: ref[i] for i in range(n)}
-    return edges, near
+    per = w.n_q_heads if mode == ckv.CKV_MODE_PER_HEAD else w.n_kv_heads
+    near, first = 0, None
+    for b in range(w.batch):
+        qp = synth.gen_prefill_queries(w, seed, 0, b, layer.slices[b])
+        n = qp.shape[0]
+        edges = torch.empty((per, n, w.kappa), dtype=torch.int32, device="cuda")
+        ws = ckv.prefill_workspace(layer.kv, mode, n)
+        ckv.ckv_prefill_topk(layer.kv, mode, b, qp.cuda(), w.n_sinks, w.kappa, w.sm_scale, edges, None, ws)
+        torch.cuda.synchronize()
+        if table is not None:
+            table.put_prefill(b, edges)
+        got = edges.cpu().numpy()
+        qf = qp.float().numpy().astype(np.float64)
+        for j in range(per):
+            g = b * per + j
+            _, kh, qh, nh = w.graph_coords(g)      # qh: the first head within sequence b
+            keys = layer.slices[b][kh].k.float().numpy().astype(np.float64)
+            ref, _ = O.prefill_edges(qf[:, qh:qh + nh], keys, w.n_sinks, w.kappa, w.sm_scale)
+            for i in range(n):
+                if np.array_equal(ref[i], got[j, i]):
+                    continue
+                W = O.prefill_row_weights(qf[i, qh:qh + nh], i, keys, w.sm_scale)
+                assert not D.prefill_row_ok(W, i, w.n_sinks, w.kappa, ref[i], got[j, i], None, f"prefill g={g}")
+                ref[i] = got[j, i]
+                near += 1
+            orc_rows[g] = {i: ref[i] for i in range(n)}
+        if first is None:
+            first = edges
+    return first, near
 
 
 def _oracle_partition(orc, w, orc_rows, g):
@@ -101,8 +109,7 @@ def test_refresh_cycle_matches_oracle(mode):
     table = ckv.EdgeTable(layer.kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
     dec.edge_table = table
     orc_rows = {}
-    edges, near = _prefill(layer, w, seed, orc_rows)
-    table.put_prefill(0, edges)
+    edges, near = _prefill(layer, w, seed, orc_rows, table)
     PY.log(f"  prefill graph checked ({near} near ties adopted)")
     nc0 = _refresh_both(layer, orc, w, orc_rows, "initial partition")
     PY.log(f"  initial Leiden partition: {nc0.tolist()} communities")
@@ -132,8 +139,7 @@ def test_async_refresh_matches_oracle(mode):
     table = ckv.EdgeTable(layer.kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
     dec.edge_table = table
     orc_rows = {}
-    edges, near = _prefill(layer, w, seed, orc_rows)
-    table.put_prefill(0, edges)
+    _prefill(layer, w, seed, orc_rows, table)
     _refresh_both(layer, orc, w, orc_rows, "initial partition")
     log = {}
     PY.run_steps(w, seed, 16, pair=(layer, orc), edge_log=log)
@@ -169,3 +175,54 @@ def test_async_refresh_matches_oracle(mode):
     assert st.steps == 12
     PY.log(f"  async refresh applied 12 steps after its snapshot ({tm['wait']:.1f} ms waited, "
            f"{tm['place']:.1f} ms placing, {tm['build']:.1f} ms building); 40 steps checked")
+
+
+def test_refresh_ragged_batch():
+    """Two sequences of different lengths (per-head graphs): every graph's
+    rows, positions and partition are its own sequence's; a synchronous and
+    then an asynchronous refresh, each checked against the oracle."""
+    w = _workload("per_head").replace(name="refresh_ragged", batch=2, min_ctx=900, n_ctx=1400, n_q_heads=4,
+                                      n_kv_heads=1)
+    seed = 4
+    layer, orc = PY.make_pair(w, seed, 41)
+    lens = layer.kv.seq_len.cpu().numpy()
+    assert lens[0] != lens[1], "the two sequences must differ in length"
+    PY.log(f"refresh, ragged batch: lengths {lens.tolist()}, {w.n_graphs} graphs")
+    dec = layer.dec
+    table = ckv.EdgeTable(layer.kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
+    dec.edge_table = table
+    orc_rows = {}
+    _prefill(layer, w, seed, orc_rows, table)
+    _refresh_both(layer, orc, w, orc_rows, "initial partition")
+    log = {}
+    PY.run_steps(w, seed, 12, pair=(layer, orc), edge_log=log)
+    for (t, g), e in log.items():
+        orc_rows[g][orc.len[orc.g[g].b] - 12 + t] = e
+    _refresh_both(layer, orc, w, orc_rows, "refresh")
+    log.clear()
+    PY.run_steps(w, seed, 8, pair=(layer, orc), first_step=12, edge_log=log)
+    for (t, g), e in log.items():
+        orc_rows[g][orc.len[orc.g[g].b] - 20 + t] = e
+    pend = dec.refresh_async(table, n_threads=2)
+    snap = {g: _oracle_partition(orc, w, orc_rows, g) for g in orc.graph_ids}
+    log.clear()
+    PY.run_steps(w, seed, 8, pair=(layer, orc), first_step=20, edge_log=log)
+    for (t, g), e in log.items():
+        orc_rows[g][orc.len[orc.g[g].b] - 28 + t] = e
+    dec.refresh_apply(pend, table)
+    layer.idx = dec.idx
+    label = dec.idx.label.cpu().numpy()
+    for g in orc.graph_ids:
+        lab0, nc0, _, _ = snap[g]
+        n1 = orc.len[orc.g[g].b]
+        rows = np.full((n1, w.kappa), -1, dtype=np.int64)
+        for i, r in orc_rows[g].items():
+            rows[i, :r.size] = r
+        lab = np.concatenate([lab0, np.full(n1 - lab0.size, -1, dtype=np.int64)])
+        lab, nc = LO.extend_by_vote(lab, nc0, rows, lab0.size, n1)
+        np.testing.assert_array_equal(label[g, :n1], lab, err_msg=f"async labels g={g}")
+        orc.repartition(g, lab, nc)
+    PY.check_csr(layer, orc)
+    PY.check_index_state(layer, orc, w, full=True)
+    PY.run_steps(w, seed, 8, pair=(layer, orc), first_step=28)
+    PY.log("  36 steps checked around a refresh and an asynchronous refresh")
