@@ -552,8 +552,8 @@ class Decoder:
         self.device = device
         self.buf = DecodeBuffers(kv, idx, budget, kappa, device)
         self.set_windows(windows)
-        # when set, every update() records the step's edges in the table (the
-        # graph a refresh partitions); windowed steps do not record
+        # when set, every step records its edges in the table (the graph a
+        # refresh partitions)
         self.edge_table: Optional[EdgeTable] = None
 
     def refresh_async(self, table: "EdgeTable", gamma=(1, 1), n_threads: int = 0) -> PendingRefresh:
@@ -720,6 +720,10 @@ class Decoder:
             return self.buf.out
         b, kv = self.buf, self.kv
         cur = torch.cuda.current_stream() if stream is None else stream
+        pos = None
+        if self.edge_table is not None:
+            with torch.cuda.stream(cur):
+                pos = kv.seq_len.clone()   # the new tokens' positions, before any window appends
         start = torch.cuda.Event()
         start.record(cur)
         prev = None
@@ -741,6 +745,9 @@ class Decoder:
             done = torch.cuda.Event()
             done.record(s)
             cur.wait_event(done)
+        if pos is not None:
+            with torch.cuda.stream(cur):
+                self.edge_table.put_step(b.edges, pos)
         return b.out
 
     def dense(self, q: torch.Tensor, out: torch.Tensor, stream=None, ml: Optional[torch.Tensor] = None):

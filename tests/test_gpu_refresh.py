@@ -226,3 +226,22 @@ def test_refresh_ragged_batch():
     PY.check_index_state(layer, orc, w, full=True)
     PY.run_steps(w, seed, 8, pair=(layer, orc), first_step=28)
     PY.log("  36 steps checked around a refresh and an asynchronous refresh")
+
+
+def test_windowed_steps_record_their_edges():
+    """Steps split into two graph windows on separate streams record the same
+    edge rows (checked against the oracle's by the refresh that follows)."""
+    w = _workload("per_head")
+    seed = 12
+    layer, orc = PY.make_pair(w, seed, 17)
+    dec = layer.dec
+    table = ckv.EdgeTable(layer.kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
+    dec.edge_table = table
+    orc_rows = {}
+    _prefill(layer, w, seed, orc_rows, table)
+    _refresh_both(layer, orc, w, orc_rows, "initial partition")
+    log = {}
+    PY.run_steps(w, seed, 16, pair=(layer, orc), edge_log=log, windows=2)
+    for (t, g), e in log.items():
+        orc_rows[g][orc.len[orc.g[g].b] - 16 + t] = e
+    _refresh_both(layer, orc, w, orc_rows, "refresh after windowed steps")
