@@ -570,6 +570,8 @@ class Decoder:
         idx = self.idx
         if table.mode != idx.mode or table.n_graphs != idx.n_graphs or table.cap != idx.l_cap:
             raise ValueError("edge table does not match the index")
+        if getattr(table, "_pending", None) is not None:
+            raise RuntimeError("a refresh of this edge table is still pending: refresh_apply it first")
         torch.cuda.current_stream().synchronize()   # the steps queued so far
         t0 = time.perf_counter()
         lens = self.kv.seq_len.cpu().numpy()
@@ -594,6 +596,7 @@ class Decoder:
                 pend.error = e
 
         pend.thread = threading.Thread(target=work, name="ckv-leiden", daemon=True)
+        table._pending = pend   # the pinned snapshot is in use until refresh_apply
         pend.thread.start()
         pend.snapshot_ms = (time.perf_counter() - t0) * 1e3
         return pend
@@ -612,6 +615,8 @@ class Decoder:
         t0 = time.perf_counter()
         pend.thread.join()
         t1 = time.perf_counter()
+        if getattr(table, "_pending", None) is pend:
+            table._pending = None
         if pend.error is not None:
             raise pend.error
         labels0, n_comm, quality = pend.result
