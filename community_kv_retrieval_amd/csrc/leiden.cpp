@@ -41,11 +41,14 @@ using i64 = int64_t;
 
 // Undirected graph in CSR form: row v lists (neighbour, weight) in increasing
 // neighbour order, a self-loop (aggregate levels) as the entry (v, w).
+// Weights, degrees and community totals are at most 2m < 2^30 (the entry
+// points refuse larger graphs), so they are held in int32; every product is
+// taken in int64.
 struct Graph {
     int32_t n = 0;
     std::vector<i64> off;
     std::vector<int32_t> nbr;
-    std::vector<i64> w;
+    std::vector<int32_t> w;
 };
 
 // Level-0 graph of tokens n_sinks .. n_tok-1 (node i = token n_sinks + i): every
@@ -55,13 +58,17 @@ bool token_graph(const int32_t *rows, int32_t kappa, int32_t n_tok, int32_t n_si
     const int32_t n = std::max(0, n_tok - n_sinks);
     g.n = n;
     std::vector<i64> cnt(size_t(n) + 1, 0);
+    std::vector<int32_t> outdeg(size_t(n), 0);
+    bool backward = true;  // every edge to an earlier token (rows from top-kappa selections)
     for (int32_t i = n_sinks; i < n_tok; ++i)
         for (int32_t e = 0; e < kappa; ++e) {
             const int32_t j = rows[size_t(i) * kappa + e];
             if (j < 0) continue;
             if (j < n_sinks || j >= n_tok || j == i) return false;
+            backward = backward && j < i;
             cnt[i - n_sinks + 1]++;
             cnt[j - n_sinks + 1]++;
+            outdeg[i - n_sinks]++;
         }
     for (int32_t v = 0; v < n; ++v) cnt[v + 1] += cnt[v];
     std::vector<int32_t> raw(static_cast<size_t>(cnt[n]));
@@ -80,7 +87,11 @@ bool token_graph(const int32_t *rows, int32_t kappa, int32_t n_tok, int32_t n_si
     g.nbr.reserve(raw.size());
     g.w.reserve(raw.size());
     for (int32_t v = 0; v < n; ++v) {
-        std::sort(raw.begin() + cnt[v], raw.begin() + cnt[v + 1]);
+        // With backward edges only, v's list is its own row's targets (all
+        // below v, filled first) followed by the tokens that name v (all
+        // above v, filled in increasing order): only the first part needs
+        // sorting.
+        std::sort(raw.begin() + cnt[v], raw.begin() + (backward ? cnt[v] + outdeg[v] : cnt[v + 1]));
         for (i64 e = cnt[v]; e < cnt[v + 1]; ++e) {
             if (!g.nbr.empty() && i64(g.nbr.size()) > g.off[v] && g.nbr.back() == raw[e]) {
                 g.w.back() += 1;
@@ -94,8 +105,8 @@ bool token_graph(const int32_t *rows, int32_t kappa, int32_t n_tok, int32_t n_si
     return true;
 }
 
-std::vector<i64> degrees(const Graph &g) {
-    std::vector<i64> k(g.n, 0);
+std::vector<int32_t> degrees(const Graph &g) {
+    std::vector<int32_t> k(g.n, 0);
     for (int32_t v = 0; v < g.n; ++v)
         for (i64 e = g.off[v]; e < g.off[v + 1]; ++e) k[v] += g.w[e];
     return k;
@@ -110,10 +121,10 @@ struct Params {
 // Fast local moving.  The value of community C for node v (v left out of
 // every community) is A(v, C) * 2m * den - num * k_v * K_C; v goes to the
 // community of largest value.
-void move_nodes(const Graph &g, const std::vector<i64> &k, const Params &P, std::vector<int32_t> &comm,
+void move_nodes(const Graph &g, const std::vector<int32_t> &k, const Params &P, std::vector<int32_t> &comm,
                 MinHeap &empty) {
     const int32_t n = g.n;
-    std::vector<i64> Kc(n, 0), to(n, 0);
+    std::vector<int32_t> Kc(n, 0), to(n, 0);
     std::vector<int32_t> size(n, 0), touched;
     std::vector<uint8_t> queued(n, 1), mark(n, 0);
     for (int32_t v = 0; v < n; ++v) {
@@ -143,10 +154,10 @@ void move_nodes(const Graph &g, const std::vector<i64> &k, const Params &P, std:
         }
         const i64 kv = k[v];
         int32_t best = D;
-        i64 best_s = to[D] * P.two_m * P.gden - P.gnum * kv * (Kc[D] - kv);
+        i64 best_s = i64(to[D]) * P.two_m * P.gden - P.gnum * kv * (Kc[D] - kv);
         for (int32_t c : touched) {
             if (c == D) continue;
-            const i64 s = to[c] * P.two_m * P.gden - P.gnum * kv * Kc[c];
+            const i64 s = i64(to[c]) * P.two_m * P.gden - P.gnum * kv * Kc[c];
             if (s > best_s || (s == best_s && best != D && c < best)) {
                 best = c;
                 best_s = s;
@@ -182,11 +193,11 @@ void move_nodes(const Graph &g, const std::vector<i64> &k, const Params &P, std:
 // community R inside S, itself well-connected to S, of largest strictly
 // positive value A(v, R) * 2m * den - num * k_v * K_R.  Refined ids are node
 // indices.
-std::vector<int32_t> refine(const Graph &g, const std::vector<i64> &k, const Params &P,
+std::vector<int32_t> refine(const Graph &g, const std::vector<int32_t> &k, const Params &P,
                             const std::vector<int32_t> &comm) {
     const int32_t n = g.n;
     std::vector<int32_t> ref(n), size(n, 1), touched;
-    std::vector<i64> Kr(k), ext(n, 0), inside(n, 0), to(n, 0);
+    std::vector<int32_t> Kr(k), ext(n, 0), inside(n, 0), to(n, 0);
     std::vector<uint8_t> mark(n, 0);
     for (int32_t v = 0; v < n; ++v) ref[v] = v;
     // nodes grouped by community, increasing node order inside each
@@ -204,7 +215,7 @@ std::vector<int32_t> refine(const Graph &g, const std::vector<i64> &k, const Par
         for (int32_t i = s0; i < s1; ++i) {
             const int32_t v = order[i];
             KS += k[v];
-            i64 in = 0;
+            int32_t in = 0;
             for (i64 e = g.off[v]; e < g.off[v + 1]; ++e)
                 if (g.nbr[e] != v && comm[g.nbr[e]] == C) in += g.w[e];
             inside[v] = in;
@@ -213,7 +224,7 @@ std::vector<int32_t> refine(const Graph &g, const std::vector<i64> &k, const Par
         for (int32_t i = s0; i < s1; ++i) {
             const int32_t v = order[i];
             const i64 kv = k[v];
-            if (inside[v] * P.two_m * P.gden < P.gnum * kv * (KS - kv)) continue;
+            if (i64(inside[v]) * P.two_m * P.gden < P.gnum * kv * (KS - kv)) continue;
             if (size[ref[v]] != 1) continue;
             touched.clear();
             for (i64 e = g.off[v]; e < g.off[v + 1]; ++e) {
@@ -230,14 +241,14 @@ std::vector<int32_t> refine(const Graph &g, const std::vector<i64> &k, const Par
             i64 best_g = 0;
             for (int32_t r : touched) {
                 if (r == ref[v]) continue;
-                if (ext[r] * P.two_m * P.gden < P.gnum * Kr[r] * (KS - Kr[r])) continue;
-                const i64 gain = to[r] * P.two_m * P.gden - P.gnum * kv * Kr[r];
+                if (i64(ext[r]) * P.two_m * P.gden < P.gnum * Kr[r] * (KS - Kr[r])) continue;
+                const i64 gain = i64(to[r]) * P.two_m * P.gden - P.gnum * kv * Kr[r];
                 if (gain > best_g || (gain == best_g && best >= 0 && r < best)) {
                     best = r;
                     best_g = gain;
                 }
             }
-            const i64 to_best = best >= 0 ? to[best] : 0;
+            const int32_t to_best = best >= 0 ? to[best] : 0;
             for (int32_t r : touched) {
                 to[r] = 0;
                 mark[r] = 0;
@@ -294,7 +305,7 @@ void aggregate(const Graph &g, const std::vector<int32_t> &ref, const std::vecto
     out.off.assign(size_t(na) + 1, 0);
     out.nbr.clear();
     out.w.clear();
-    std::vector<i64> acc(na, 0);
+    std::vector<int32_t> acc(na, 0);
     std::vector<uint8_t> mark(na, 0);
     std::vector<int32_t> touched;
     for (int32_t a = 0; a < na; ++a) {
@@ -325,9 +336,9 @@ void aggregate(const Graph &g, const std::vector<int32_t> &ref, const std::vecto
 // Returns the number of communities.
 int32_t leiden(const Graph &g0, i64 gnum, i64 gden, int32_t *labels) {
     const int32_t n0 = g0.n;
-    std::vector<i64> k = degrees(g0);
+    std::vector<int32_t> k = degrees(g0);
     i64 two_m = 0;
-    for (i64 x : k) two_m += x;
+    for (int32_t x : k) two_m += x;
     std::vector<int32_t> node_of(n0);
     for (int32_t i = 0; i < n0; ++i) node_of[i] = i;
     std::vector<int32_t> comm(node_of);
@@ -376,9 +387,9 @@ int32_t leiden(const Graph &g0, i64 gnum, i64 gden, int32_t *labels) {
 
 // Modularity of token labels (level-0 nodes) at resolution num/den.
 double quality(const Graph &g, const int32_t *lab, i64 gnum, i64 gden) {
-    std::vector<i64> k = degrees(g);
+    std::vector<int32_t> k = degrees(g);
     i64 two_m = 0;
-    for (i64 x : k) two_m += x;
+    for (int32_t x : k) two_m += x;
     if (two_m == 0) return 0.0;
     std::vector<i64> E(g.n, 0), K(g.n, 0);
     for (int32_t v = 0; v < g.n; ++v) {
@@ -397,7 +408,7 @@ double quality(const Graph &g, const int32_t *lab, i64 gnum, i64 gden) {
 // (2m)^2 * max(num, den) * 4.
 i64 total_weight(const Graph &g) {
     i64 t = 0;
-    for (i64 x : g.w) t += x;
+    for (int32_t x : g.w) t += x;
     return t;
 }
 
