@@ -494,7 +494,8 @@ class EdgeTable:
         self.n_graphs = kv.batch * per
         self.e = torch.full((self.n_graphs, cap, kappa), -1, dtype=torch.int32, device=device)
         # sequence of every graph, to find the row a step's new token takes
-        self.graph_seq = torch.arange(self.n_graphs, device=device) // per
+        self._gidx = torch.arange(self.n_graphs, device=device)
+        self.graph_seq = self._gidx // per
 
     def pinned(self) -> torch.Tensor:
         """A pinned host buffer shaped like the table (allocated once)."""
@@ -512,7 +513,11 @@ class EdgeTable:
         """Row pos[seq of g] of every graph g from a step's edges [G][kappa];
         pos: the sequences' lengths before the step (the new tokens' positions)."""
         rows = pos.long()[self.graph_seq]
-        self.e[torch.arange(self.n_graphs, device=self.e.device), rows] = edges
+        # a sequence at the table's capacity stores no new token (the step
+        # reports it in the index status): its row is left as it was
+        ok = rows < self.cap
+        rows = rows.clamp(max=self.cap - 1)
+        self.e[self._gidx, rows] = torch.where(ok[:, None], edges, self.e[self._gidx, rows])
 
 
 class PendingRefresh:
