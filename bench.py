@@ -666,6 +666,15 @@ def bench_prefill(w, seed, kv, slices, reps=3, cpu_seconds=0.0):
 REFRESH_LEG = dict(steps=1024, interval=256, gamma=(512, 1))
 
 
+def host_threads() -> int:
+    """Host threads for the library's Leiden: the job's CPU share as the
+    environment states it (OMP_NUM_THREADS), else the visible cores, at most 16."""
+    try:
+        return max(1, int(os.environ["OMP_NUM_THREADS"]))
+    except (KeyError, ValueError):
+        return max(1, min(16, os.cpu_count() or 1))
+
+
 def leiden_timing(w, edges, n, reps=2):
     """Leiden partition (Figure 1 panel (2); ckv_leiden_partition, host threads)
     of the prompt's per-head graphs from the prefill edges just computed."""
@@ -680,9 +689,9 @@ def leiden_timing(w, edges, n, reps=2):
     secs = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        _, n_comm, q = ckv.ckv_leiden_partition(n_tok, w.n_sinks, e, (1, 1), 0)
+        _, n_comm, q = ckv.ckv_leiden_partition(n_tok, w.n_sinks, e, (1, 1), host_threads())
         secs.append(time.perf_counter() - t0)
-    return {"graphs": int(e.shape[0]), "tokens_per_graph": int(n), "gamma": 1, "host_threads": os.cpu_count(),
+    return {"graphs": int(e.shape[0]), "tokens_per_graph": int(n), "gamma": 1, "host_threads": host_threads(),
             "s_per_layer": round(min(secs), 4), "communities_mean": round(float(n_comm.mean()), 1),
             "community_size_mean": round(float((n - w.n_sinks) / n_comm.mean()), 1),
             "modularity_mean": round(float(q.mean()), 4),
@@ -734,7 +743,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
         table.put_prefill(0, pe)
         del pe, ws
         t0 = time.perf_counter()
-        q_init = dec.refresh(table, gamma)
+        q_init = dec.refresh(table, gamma, n_threads=host_threads())
         torch.cuda.synchronize()
         init_ms = (time.perf_counter() - t0) * 1e3
         dec.edge_table = table
@@ -742,7 +751,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
         dout = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
         rec, err, qual, ref_ms, ncomm, phases = [], [], [], [], [], []
         pend, pend_t, lags = None, 0, []
-        threads = max(1, (os.cpu_count() or 4) - 2)   # leave cores to the thread launching steps
+        threads = max(1, host_threads() - 2)   # leave cores to the thread launching steps
 
         def apply_pending(t):
             tm = {}
@@ -778,7 +787,7 @@ def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topic
                     torch.cuda.synchronize()
                     t0 = time.perf_counter()
                     tm = {}
-                    qv = dec.refresh(table, gamma, timings=tm)
+                    qv = dec.refresh(table, gamma, n_threads=host_threads(), timings=tm)
                     torch.cuda.synchronize()
                     ref_ms.append(round((time.perf_counter() - t0) * 1e3, 1))
                     phases.append({k: round(v, 1) for k, v in tm.items()})
