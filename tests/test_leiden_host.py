@@ -157,3 +157,17 @@ def test_host_extend_partition_matches_oracle():
     bad[0, 600, 0] = 650           # an edge to a later token
     with pytest.raises(ckv.CkvError):
         ckv.ckv_extend_partition(np.array(firsts, dtype=np.int32), n_tok, bad, labels.copy(), n_comm.copy())
+
+
+@pytest.mark.parametrize("gamma", [(1, 1), (512, 1)])
+def test_host_leiden_full_size_prompt_graph(gamma):
+    """A graph of the benchmark's prompt length (131 072 tokens, kappa 8,
+    communities of about 16 planted tokens plus stray edges): the library's
+    labels equal the oracle's at the resolution of the prefill timing (1) and
+    of the refresh leg (512); several aggregation levels run at this size."""
+    rng = np.random.default_rng(2026)
+    n = 131072
+    rows = prefill_like_rows(rng, n, 4, 8, n // 16, p_other=0.3)
+    ref, nc = L.partition_tokens(rows, n, 4, *gamma)
+    labels, n_comm, _ = ckv.ckv_leiden_partition(np.array([n], dtype=np.int32), 4, rows[None].copy(), gamma, 4)
+    assert n_comm[0] == nc and np.array_equal(labels[0], ref.astype(np.int32))
