@@ -66,27 +66,27 @@ def _prefill(layer, w, seed, orc_rows, table=None):
     return first, near
 
 
-def _oracle_partition(orc, w, orc_rows, g):
+def _oracle_partition(orc, w, orc_rows, g, gamma=(1, 1)):
     st = orc.g[g]
     n = orc.len[st.b]
     rows = np.full((n, w.kappa), -1, dtype=np.int64)
     for i, r in orc_rows[g].items():
         rows[i, :r.size] = r
-    lab, nc = LO.partition_tokens(rows, n, w.n_sinks)
-    q = LO.modularity(LO.token_graph(rows, n, w.n_sinks), lab[w.n_sinks:].tolist())
+    lab, nc = LO.partition_tokens(rows, n, w.n_sinks, *gamma)
+    q = LO.modularity(LO.token_graph(rows, n, w.n_sinks), lab[w.n_sinks:].tolist(), *gamma)
     return lab, nc, q, rows
 
 
-def _refresh_both(layer, orc, w, orc_rows, where):
+def _refresh_both(layer, orc, w, orc_rows, where, gamma=(1, 1)):
     dec = layer.dec
-    quality = dec.refresh(dec.edge_table)
+    quality = dec.refresh(dec.edge_table, gamma)
     layer.idx = dec.idx
     torch.cuda.synchronize()
     table = dec.edge_table.e.cpu().numpy()
     label = dec.idx.label.cpu().numpy()
     n_comm = dec.idx.n_comm.cpu().numpy()
     for g in orc.graph_ids:
-        lab, nc, q, rows = _oracle_partition(orc, w, orc_rows, g)
+        lab, nc, q, rows = _oracle_partition(orc, w, orc_rows, g, gamma)
         n = lab.size
         np.testing.assert_array_equal(table[g, :n], rows, err_msg=f"{where}: edge rows g={g}")
         np.testing.assert_array_equal(label[g, :n], lab, err_msg=f"{where}: labels g={g}")
@@ -245,3 +245,40 @@ def test_windowed_steps_record_their_edges():
     for (t, g), e in log.items():
         orc_rows[g][orc.len[orc.g[g].b] - 16 + t] = e
     _refresh_both(layer, orc, w, orc_rows, "refresh after windowed steps")
+
+
+# (graph mode, query heads per kv head, batch, prompt length, kappa, resolution, budget)
+RANDOM_CONFIGS = [
+    ("per_head", 4, 2, 700, 8, (8, 1), 256),
+    ("group", 1, 2, 900, 5, (1, 1), 512),
+    ("per_head", 2, 1, 820, 12, (3, 2), 64),
+    ("group", 4, 2, 560, 3, (64, 1), 128),
+]
+
+
+@pytest.mark.parametrize("seed", range(len(RANDOM_CONFIGS)))
+def test_refresh_random_configurations(seed):
+    """Mixed shapes: graph mode, a batch with ragged lengths, heads per kv
+    head, kappa, budget, resolution and a drifting decode stream; the prompt
+    graph, its partition, 8 steps, a refresh and 4 more steps, all against the
+    oracle."""
+    mode, group, batch, n_ctx, kappa, gamma, budget = RANDOM_CONFIGS[seed]
+    w = synth.preset("qwen3_8b_32k").replace(
+        name=f"refresh_mix_{seed}", batch=batch, n_ctx=n_ctx, min_ctx=n_ctx // 2 if batch > 1 else 0,
+        n_q_heads=2 * group, n_kv_heads=2, kappa=kappa, budget=budget, steps=13,
+        mode=synth.PER_HEAD if mode == "per_head" else synth.GROUP, drift_topics=4, drift_rate=0.5)
+    PY.log(f"refresh mix {seed}: {mode}, batch {batch}, {2 * group} q heads, kappa {kappa}, gamma {gamma}, "
+           f"budget {w.budget}, ctx {n_ctx}")
+    layer, orc = PY.make_pair(w, seed, 14)
+    dec = layer.dec
+    table = ckv.EdgeTable(layer.kv, dec.idx.mode, dec.idx.l_cap, w.kappa)
+    dec.edge_table = table
+    orc_rows = {}
+    _prefill(layer, w, seed, orc_rows, table)
+    _refresh_both(layer, orc, w, orc_rows, "initial partition", gamma)
+    log = {}
+    PY.run_steps(w, seed, 8, pair=(layer, orc), edge_log=log)
+    for (t, g), e in log.items():
+        orc_rows[g][orc.len[orc.g[g].b] - 8 + t] = e
+    _refresh_both(layer, orc, w, orc_rows, "refresh", gamma)
+    PY.run_steps(w, seed, 4, pair=(layer, orc), first_step=8)
