@@ -649,7 +649,7 @@ def bench_prefill(w, seed, kv, slices, reps=3, cpu_seconds=0.0):
         out[name] = {"ms_per_layer": round(t, 3), "tflops": round(tf, 1),
                      "frac_of_bf16_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
         if name == "per_head":
-            out["leiden"] = leiden_timing(w, edges, n)
+            out["leiden"] = leiden_timing(w, edges, n, oracle=cpu_seconds > 0)
         del edges, weights, ws
     if cpu_seconds > 0:
         out["cpu_baseline"] = prefill_cpu_baseline(w, q, slices, cpu_seconds)
@@ -675,9 +675,11 @@ def host_threads() -> int:
         return max(1, min(16, os.cpu_count() or 1))
 
 
-def leiden_timing(w, edges, n, reps=2):
+def leiden_timing(w, edges, n, reps=2, oracle=False):
     """Leiden partition (Figure 1 panel (2); ckv_leiden_partition, host threads)
-    of the prompt's per-head graphs from the prefill edges just computed."""
+    of the prompt's per-head graphs from the prefill edges just computed; with
+    oracle set, the CPU oracle's Leiden timed on the first graph beside it
+    (a baseline, one graph, one thread)."""
     import time
 
     import numpy as np
@@ -695,7 +697,29 @@ def leiden_timing(w, edges, n, reps=2):
             "s_per_layer": round(min(secs), 4), "communities_mean": round(float(n_comm.mean()), 1),
             "community_size_mean": round(float((n - w.n_sinks) / n_comm.mean()), 1),
             "modularity_mean": round(float(q.mean()), 4),
-            "context": "the page's Table 10 lists 0.37-0.45 s of exposed Leiden time per prefill (its hardware)"}
+            "context": "the page's Table 10 lists 0.37-0.45 s of exposed Leiden time per prefill (its hardware)",
+            **(leiden_oracle_baseline(w, e[0], n) if oracle else {})}
+
+
+def leiden_oracle_baseline(w, rows, n):
+    """The oracle's Leiden (pure Python, one thread) on one graph, against the
+    library's on the same graph with one thread."""
+    import time
+
+    import numpy as np
+
+    from community_kv_retrieval_amd import ckv
+    from oracle import leiden_oracle as LO
+    t0 = time.perf_counter()
+    LO.partition_tokens(rows, n, w.n_sinks)
+    t_orc = time.perf_counter() - t0
+    one = np.ascontiguousarray(rows[None])
+    t0 = time.perf_counter()
+    ckv.ckv_leiden_partition(np.array([n], dtype=np.int32), w.n_sinks, one, (1, 1), 1)
+    t_lib = time.perf_counter() - t0
+    return {"cpu_baseline": {"kind": "oracle", "value": round(t_orc, 3), "unit": "s per graph", "cores": 1,
+                             "sample": f"Leiden of the first head's {n}-token prompt graph, pure Python"},
+            "library_s_per_graph_one_thread": round(t_lib, 4)}
 
 
 def bench_refresh(args, base, steps=512, interval=128, gamma=(1, 1), drift_topics=16, drift_rate=0.5):
