@@ -77,7 +77,8 @@ def build_trace(verbose: bool = False) -> str:
         for src in srcs:
             f.write(f'#include "{src}"\n')
     out = os.path.join(BUILD, "libckv_trace.so")
-    cmd = [HIPCC, *FLAGS, "-DCKV_PHASE_TRACE", "-shared", "-pthread", unity, "-x", "c++", *hosts, "-o", out]
+    host_objs = [_compile(h) for h in hosts]
+    cmd = [HIPCC, *FLAGS, "-DCKV_PHASE_TRACE", "-shared", "-pthread", unity, "-x", "none", *host_objs, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"trace build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
