@@ -171,3 +171,22 @@ def test_host_leiden_full_size_prompt_graph(gamma):
     ref, nc = L.partition_tokens(rows, n, 4, *gamma)
     labels, n_comm, _ = ckv.ckv_leiden_partition(np.array([n], dtype=np.int32), 4, rows[None].copy(), gamma, 4)
     assert n_comm[0] == nc and np.array_equal(labels[0], ref.astype(np.int32))
+
+
+def test_host_leiden_resolution_extremes_and_overflow_guard():
+    rng = np.random.default_rng(41)
+    t = prefill_like_rows(rng, 600, 4, 8, 30)
+    n_tok, edges = _pack([t], 600)
+    # a resolution far above every gain: no merge pays, every token alone
+    labels, n_comm, _ = ckv.ckv_leiden_partition(n_tok, 4, edges, (10 ** 6, 1))
+    assert n_comm[0] == 596 and labels[0, 4:].tolist() == list(range(596))
+    ref, nc = L.partition_tokens(t, 600, 4, 10 ** 6, 1)
+    assert nc == 596
+    # resolution 0: the connected components
+    labels0, n0, _ = ckv.ckv_leiden_partition(n_tok, 4, edges, (0, 1))
+    ref0, nc0 = L.partition_tokens(t, 600, 4, 0, 1)
+    assert n0[0] == nc0 and np.array_equal(labels0[0], ref0.astype(np.int32))
+    # products that could leave int64 are refused: (2m)^2 * 4 * max(num, den) >= 2^62
+    with pytest.raises(ckv.CkvError) as ei:
+        ckv.ckv_leiden_partition(n_tok, 4, edges, (1 << 44, 1))
+    assert ei.value.code == ckv.CKV_E_INVALID
