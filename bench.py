@@ -95,7 +95,9 @@ def main():
     W, K = args.warmup, args.steps
     total = W + K
     if args.refresh_only:
-        print(json.dumps({"refresh_vs_incremental": bench_refresh(args, synth.preset("qwen3_8b_32k"), **REFRESH_LEG)}),
+        print(json.dumps({"refresh_vs_incremental": bench_refresh(args, synth.preset("qwen3_8b_32k"), **REFRESH_LEG),
+                          "refresh_vs_incremental_128k": bench_refresh(args, synth.preset("llama31_8b_128k"),
+                                                                       **REFRESH_LEG_128K)}),
               flush=True)
         return
     if args.prefill_only:
@@ -207,9 +209,10 @@ def main():
     if not args.no_centroid and w.name == "llama31_8b_128k":
         centroid = bench_centroid(args, w, W, K)
 
-    refresh = None
+    refresh = refresh_128k = None
     if not args.no_refresh and w.name == "llama31_8b_128k":
         refresh = bench_refresh(args, synth.preset("qwen3_8b_32k"), **REFRESH_LEG)
+        refresh_128k = bench_refresh(args, synth.preset("llama31_8b_128k"), **REFRESH_LEG_128K)
 
     src_hash = gather_source_hash()
     traffic = measured_traffic(w.name, src_hash)
@@ -261,6 +264,7 @@ def main():
         "group_b8": group,
         "centroid_budget": centroid,
         "refresh_vs_incremental": refresh,
+        "refresh_vs_incremental_128k": refresh_128k,
         "cpu_baseline": cpu,
         "host_inputs": {"ms_per_step": round(ms_host, 5), "steps_per_s": round(1e3 / ms_host, 1),
                         "bytes_per_step": host_bytes,
@@ -664,6 +668,9 @@ def bench_prefill(w, seed, kv, slices, reps=3, cpu_seconds=0.0):
 # modularity's community count grows like sqrt(n) at a fixed resolution),
 # 1024 drifting steps, a re-partition every 256.
 REFRESH_LEG = dict(steps=1024, interval=256, gamma=(512, 1))
+# The same at the headline's length (131 072 tokens): a resolution four times
+# higher keeps the communities near the same size.
+REFRESH_LEG_128K = dict(steps=1024, interval=256, gamma=(2048, 1))
 
 
 def host_threads() -> int:
